@@ -1,0 +1,153 @@
+"""Seeded synthetic inputs for the Transformer-XL relative attention forward.
+
+This module is shared by the GPU library's tests/bench and by the CPU oracle's
+tests. It holds no arithmetic of the method itself: it only draws random
+numbers, rounds them to the storage precision, and describes the five
+workload shapes.
+
+Workloads (value recipe, applied to every one):
+  * hidden states h and memory N(0, 1);
+  * projection weights W_q, W_k, W_v, W_r (each [n_head*d_head, d_model]) and
+    W_o ([d_model, n_head*d_head]) N(0, 0.02) -- the nn.Linear [out, in]
+    layout, so a projection is y = x @ W^T;
+  * global biases u, v ([n_head, d_head]) N(0, 0.02);
+  * the optional per-head scalar bias table beta ([2*bias_clamp+1, n_head])
+    N(0, 0.02).
+Draws are float32 from numpy.random.default_rng(seed) in the order
+h, mem, W_q, W_k, W_v, W_r, W_o, u, v, beta; bf16 workloads round every draw
+once to bfloat16 (round to nearest even) and both sides consume those bits.
+"""
+from __future__ import annotations
+
+import dataclasses
+import numpy as np
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    d_model: int
+    n_head: int
+    d_head: int
+    qlen: int
+    mlen: int
+    clamp_len: int = -1     # < 0: no clamp of the relative distance
+    bias_clamp: int = -1    # < 0: no scalar bias table
+    dtype: str = "bf16"     # "f32" or "bf16"
+    segments: int = 1       # > 1: segment-recurrent run with FIFO memory
+    seed: int = 0
+
+    @property
+    def klen(self) -> int:
+        return self.qlen + self.mlen
+
+    def n_valid_pairs(self, mlen: int | None = None) -> int:
+        """Causal (query, key) pairs per (batch, head): query i sees j <= mlen+i."""
+        m = self.mlen if mlen is None else mlen
+        q = self.qlen
+        return q * m + q * (q + 1) // 2
+
+
+# The five workloads: tiny fp32, base-like, large-like (the throughput
+# target, qlen = mlen = 384), long-memory evaluation, and the 4-segment
+# recurrent run with a +-128 scalar bias table.
+WORKLOADS = {
+    "tiny_f32": Workload("tiny_f32", 1, 16, 2, 8, 8, 8, clamp_len=16, dtype="f32", seed=0),
+    "base_bf16": Workload("base_bf16", 32, 512, 8, 64, 128, 128, seed=1),
+    "large_bf16": Workload("large_bf16", 8, 1024, 16, 64, 384, 384, seed=2),
+    "longmem_bf16": Workload("longmem_bf16", 4, 512, 8, 64, 64, 1600, clamp_len=1000, seed=3),
+    "segments_bf16": Workload("segments_bf16", 4, 1024, 16, 64, 512, 512, bias_clamp=128,
+                              segments=4, seed=4),
+}
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); return the uint16 bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bits to float32."""
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+class Tensor:
+    """One input: the exact stored values (float64 view) and the storage bits."""
+
+    def __init__(self, f32: np.ndarray, dtype: str):
+        self.dtype = dtype
+        if dtype == "bf16":
+            self.bits = bf16_bits(f32)
+            self.f32 = bf16_to_f32(self.bits)
+        elif dtype == "f32":
+            self.f32 = np.ascontiguousarray(f32, dtype=np.float32)
+            self.bits = self.f32
+        else:
+            raise ValueError(dtype)
+        self.f64 = self.f32.astype(np.float64)
+
+    @property
+    def shape(self):
+        return self.f32.shape
+
+
+def _normal(rng, shape, std):
+    return (rng.standard_normal(size=shape, dtype=np.float32) * np.float32(std)).astype(np.float32)
+
+
+def layer_inputs(w: Workload, *, batch: int | None = None, qlen: int | None = None,
+                 mlen: int | None = None, seed: int | None = None) -> dict:
+    """Draw one layer call's inputs. Sizes default to the workload's.
+
+    For a segment-recurrent workload, 'h' is the whole input stream
+    [batch, segments*qlen, d_model] and 'mem' is empty (the run starts with
+    no memory).
+    """
+    B = w.batch if batch is None else batch
+    q = w.qlen if qlen is None else qlen
+    m = w.mlen if mlen is None else mlen
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    HD = w.n_head * w.d_head
+    D = w.d_model
+    if w.segments > 1:
+        h = _normal(rng, (B, w.segments * q, D), 1.0)
+        mem = np.zeros((B, 0, D), np.float32)
+    else:
+        h = _normal(rng, (B, q, D), 1.0)
+        mem = _normal(rng, (B, m, D), 1.0)
+    out = {
+        "h": h, "mem": mem,
+        "w_q": _normal(rng, (HD, D), 0.02),
+        "w_k": _normal(rng, (HD, D), 0.02),
+        "w_v": _normal(rng, (HD, D), 0.02),
+        "w_r": _normal(rng, (HD, D), 0.02),
+        "w_o": _normal(rng, (D, HD), 0.02),
+        "u": _normal(rng, (w.n_head, w.d_head), 0.02),
+        "v": _normal(rng, (w.n_head, w.d_head), 0.02),
+    }
+    if w.bias_clamp >= 0:
+        out["beta"] = _normal(rng, (2 * w.bias_clamp + 1, w.n_head), 0.02)
+    return {k: Tensor(a, w.dtype) for k, a in out.items()}
+
+
+def core_inputs(*, batch: int, n_head: int, d_head: int, qlen: int, mlen: int, n_rows: int,
+                dtype: str, seed: int, bias_clamp: int = -1) -> dict:
+    """Inputs for the attention core alone: head-major q, k, v, a projected
+    relative table r ([n_head, n_rows, d_head], row n <-> distance n) and the
+    biases u, v. Magnitudes are those of projected N(0,1) activations."""
+    rng = np.random.default_rng(seed)
+    k_len = qlen + mlen
+    out = {
+        "q": _normal(rng, (batch, n_head, qlen, d_head), 0.6),
+        "k": _normal(rng, (batch, n_head, k_len, d_head), 0.6),
+        "v": _normal(rng, (batch, n_head, k_len, d_head), 0.6),
+        "r": _normal(rng, (n_head, n_rows, d_head), 0.6),
+        "u": _normal(rng, (n_head, d_head), 0.3),
+        "vb": _normal(rng, (n_head, d_head), 0.3),
+    }
+    if bias_clamp >= 0:
+        out["beta"] = _normal(rng, (2 * bias_clamp + 1, n_head), 0.3)
+    return {k: Tensor(a, dtype) for k, a in out.items()}
