@@ -1,0 +1,201 @@
+/*
+ * xl_rel.h -- C ABI of libxlrel.so: the Transformer-XL relative multi-head
+ * attention forward over [cached memory ; current segment] on AMD MI355X
+ * (gfx950).
+ *
+ * The method (pages by title/host and section):
+ *  - score of query i and key j, for one head:
+ *      A_rel(i,j) = q_i.k_j + q_i.r_{i-j} + u.k_j + v.r_{i-j}
+ *    (qidao123.com thread-401555 "Transformer-XL cross-window RPE" §3;
+ *     felixzhao.cn article 118 "Transformer-XL 和相对位置编码" §2.3.2;
+ *     2kiu.com/news/5253360 TransformerXL relative-position tutorial §2.2),
+ *    computed here in the folded form (q_i+u).k_j + (q_i+v).r_{i-j};
+ *  - r_delta = R_delta W_r^T with the sinusoid R_delta (thread-401555 §2,
+ *    felixzhao.cn §2.3.2), distances clamped to [-C, C] (2kiu.com §2.4);
+ *  - queries from the segment, keys/values over [memory ; segment], memory
+ *    first (felixzhao.cn §2.3.1; intelliparadigm.com 2238855
+ *    "Transformer-XL架构解析" §2.1); causal mask after the whole sum
+ *    (2kiu.com §4.2), softmax, P.V, output projection (2kiu.com §3.1);
+ *  - optional per-head scalar bias b_{clamp(i-j, +-k)} added after scaling
+ *    (jsqmd.com 1364567 "Transformer偏置型相对位置编码" §2.2, §3.1-§3.4);
+ *  - FIFO memory update: the newest states push out the oldest
+ *    (intelliparadigm.com §1.1), memory is a detached copy (felixzhao.cn
+ *    §2.3.1).
+ *
+ * Conventions for every entry point
+ *  - All tensors are dense, row-major, on the device of the current HIP
+ *    device, owned by the caller. The library allocates no device memory:
+ *    scratch space comes from the caller's workspace.
+ *  - 'stream' is a hipStream_t (NULL: the null stream). Work is enqueued
+ *    asynchronously; device-side results are valid once the stream reaches
+ *    that point. Host-side outputs (status, FIFO bookkeeping) are final on
+ *    return.
+ *  - Arguments are validated on the host before anything is enqueued; on
+ *    error nothing is launched and a status code is returned, with a
+ *    human-readable reason available from xl_last_error() (per thread).
+ *  - No output may alias an input.
+ *  - Weight layout is nn.Linear's [out_features, in_features]: a projection
+ *    is y = x W^T.
+ */
+#ifndef XL_REL_H
+#define XL_REL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+    XL_OK = 0,
+    XL_NULL_ARG = 1,             /* a required pointer is NULL */
+    XL_BAD_SHAPE = 2,            /* sizes inconsistent or out of range */
+    XL_UNSUPPORTED = 3,          /* valid but outside the supported envelope */
+    XL_WORKSPACE_TOO_SMALL = 4,  /* ws_bytes below xl_rel_attn_workspace_size() */
+    XL_HIP_ERROR = 5             /* a HIP launch/runtime call failed */
+};
+
+/* Element types. */
+enum { XL_F32 = 0, XL_BF16 = 1 };
+
+/* Human-readable name of a status code (static string). */
+const char* xl_status_string(int status);
+/* Detail of the last error on the calling thread ("" if none). */
+const char* xl_last_error(void);
+
+/*
+ * Sinusoidal relative embedding (thread-401555 §2; felixzhao.cn §2.3.2).
+ * Row n (0 <= n < n_rows) of out [n_rows, d_model] is R_delta for
+ * delta = delta0 + n, first clamped to [-clamp_len, clamp_len] when
+ * clamp_len >= 0 (2kiu.com §2.4):
+ *     R_delta[2t]   = sin(delta * base^(-2t/d_model))
+ *     R_delta[2t+1] = cos(delta * base^(-2t/d_model)),  t < d_model/2.
+ * Computed in fp64 and rounded once (to nearest even) to out_dtype.
+ * d_model must be even and positive; base > 0 (0 selects 10000);
+ * n_rows >= 0 (0 launches nothing). delta0 may be negative: delta0 = -2,
+ * n_rows = 1, d_model = 4 gives approximately [-0.909, -0.416, -0.020,
+ * 0.999], the example the page works through.
+ */
+int xl_relpos_embed(int64_t delta0, int64_t n_rows, int64_t d_model, int64_t clamp_len,
+                    double base, int out_dtype, void* out, void* stream);
+
+/* Shape and numerics of one relative-attention layer call. */
+typedef struct {
+    int64_t batch;       /* B >= 1 */
+    int64_t d_model;     /* D: even; multiple of 8 for bf16, of 4 for f32 */
+    int64_t n_head;      /* H >= 1 */
+    int64_t d_head;      /* 64 (bf16) or 8 (f32) */
+    int64_t qlen;        /* segment length, >= 1 */
+    int64_t mlen;        /* memory length, >= 0 (ignored by xl_segment_step) */
+    int64_t clamp_len;   /* < 0: no clamp; else distances clamp to [-C, C] */
+    int64_t bias_clamp;  /* < 0: no scalar bias table; else table has 2k+1 rows */
+    double base;         /* sinusoid base; 0 selects 10000 */
+    float scale;         /* score scale; 0 selects 1/sqrt(d_head) */
+    int32_t dtype;       /* XL_BF16 (d_head 64) or XL_F32 (d_head 8): h, mem,
+                            weights, u, v, bias table and every intermediate */
+    int32_t out_dtype;   /* XL_F32 or XL_BF16 for the layer output */
+} xl_attn_desc;
+
+/* Weights of one layer; all device pointers in desc->dtype. */
+typedef struct {
+    const void* w_q;         /* [H*d_head, D] */
+    const void* w_k;         /* [H*d_head, D] */
+    const void* w_v;         /* [H*d_head, D] */
+    const void* w_r;         /* [H*d_head, D]  position projection W_{k,R} */
+    const void* w_o;         /* [D, H*d_head] */
+    const void* u;           /* [H, d_head]  content bias */
+    const void* v;           /* [H, d_head]  position bias */
+    const void* bias_table;  /* [2*bias_clamp+1, H] or NULL when bias_clamp < 0 */
+} xl_attn_weights;
+
+/*
+ * Workspace layout of xl_rel_attn_fwd / xl_segment_step: byte offsets
+ * (from the workspace base, each 256-byte aligned) of the intermediates the
+ * call leaves behind, in desc->dtype:
+ *   qu, qv  [B, H, qlen, d_head]  s*(q+u), s*(q+v)   (s = scale)
+ *   k       [B, H, klen, d_head]  keys over [memory ; segment]
+ *   vt      [B, H, d_head, ldv]   values, transposed; columns >= klen unused
+ *   rel     [n_rel, D]            sinusoid rows R_n, n = 0..n_rel-1
+ *   r       [H, n_rel, d_head]    projected table r_n = R_n W_r^T
+ *   attn    [B, qlen, H*d_head]   attention output before W_o
+ * with klen = mlen + qlen and n_rel = min(klen, clamp_len + 1) (klen when
+ * there is no clamp).
+ */
+typedef struct {
+    size_t qu, qv, k, vt, rel, r, attn;
+    size_t total;            /* == xl_rel_attn_workspace_size() */
+    int64_t klen, ldv, n_rel;
+} xl_ws_layout;
+
+/* Workspace bytes needed by xl_rel_attn_fwd for desc (0 on invalid desc). */
+size_t xl_rel_attn_workspace_size(const xl_attn_desc* desc);
+/* Fill *layout for desc. Returns a status code. */
+int xl_rel_attn_workspace_layout(const xl_attn_desc* desc, xl_ws_layout* layout);
+
+/*
+ * One relative-attention layer forward (the whole hot path):
+ *   h   [B, qlen, D]  current segment (desc->dtype)
+ *   mem [B, mlen, D]  cached memory, oldest first; NULL iff mlen == 0
+ *   out [B, qlen, D]  (desc->out_dtype)
+ * Steps: sinusoid rows -> r = R W_r^T -> q-projection with s*(q+u), s*(q+v)
+ * -> k/v projection of [mem ; h] -> fused relative attention -> W_o.
+ * ws must hold xl_rel_attn_workspace_size(desc) bytes, 256-byte aligned.
+ */
+int xl_rel_attn_fwd(const xl_attn_desc* desc, const xl_attn_weights* w,
+                    const void* h, const void* mem, void* out,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The fused attention kernel alone (score, rel-shift, mask, softmax, P.V),
+ * on projected operands in desc->dtype, laid out as in xl_ws_layout:
+ *   qu, qv [B, H, qlen, d_head]; k [B, H, klen, d_head];
+ *   vt [B, H, d_head, ldv] (ldv >= klen, multiple of 8);
+ *   r [H, n_rel, d_head] with row n the projection of distance n, n_rel at
+ *     least min(klen, clamp_len + 1) (klen without a clamp); a distance
+ *     delta uses row min(delta, C) (C = clamp_len, or klen - 1 unclamped);
+ *   bias_table [2*bias_clamp+1, H] or NULL;
+ *   attn [B, qlen, H*d_head] output (desc->dtype).
+ * The scale is already folded into qu and qv (desc->scale is not used).
+ * desc->d_model, base, out_dtype are ignored.
+ */
+int xl_rel_attn_core(const xl_attn_desc* desc, const void* qu, const void* qv,
+                     const void* k, const void* vt, int64_t ldv, const void* r,
+                     int64_t n_rel, const void* bias_table, void* attn, void* stream);
+
+/* Caller-owned FIFO memory of one layer: a ring of mlen_max rows per
+ * batch element. Logical row t (0 = oldest, t < len) of batch b is at
+ * buf[b, (head + t) % mlen_max, :]. */
+typedef struct {
+    void* buf;          /* [B, mlen_max, D] in desc->dtype */
+    int64_t mlen_max;   /* >= 1 */
+    int64_t len;        /* rows in use, 0 <= len <= mlen_max */
+    int64_t head;       /* physical row of the oldest entry, 0 <= head < mlen_max */
+} xl_mem_fifo;
+
+/*
+ * One segment of a segment-recurrent run (felixzhao.cn §2.3.1,
+ * intelliparadigm.com §1.1): the layer forward of h over
+ * [memory ; h] with mlen = fifo->len (desc->mlen is ignored), then the FIFO
+ * update: the memory becomes the last min(len + qlen, mlen_max) rows of
+ * [memory ; h] (the layer *input* states, copied). h must not alias
+ * fifo->buf. On success fifo->len and fifo->head are updated on return;
+ * the ring contents are written on 'stream' after the layer has read them.
+ * ws: xl_rel_attn_workspace_size() of desc with mlen = fifo->len.
+ */
+int xl_segment_step(const xl_attn_desc* desc, const xl_attn_weights* w, const void* h,
+                    xl_mem_fifo* fifo, void* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Timing hook: when both are non-NULL, hipEvent_t handles ev_begin/ev_end are
+ * recorded on the launch stream immediately before and after the fused
+ * attention kernel of the next calls of xl_rel_attn_fwd, xl_segment_step and
+ * xl_rel_attn_core on this thread. NULL, NULL switches it off.
+ */
+int xl_set_core_events(void* ev_begin, void* ev_end);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* XL_REL_H */

@@ -1,0 +1,159 @@
+"""The C ABI on the CPU: the library loads, exports every entry point the
+header declares, and rejects invalid arguments on the host before anything is
+launched (no GPU needed: every call below fails validation)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import transformer_xl_relative_amd as xl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "xl_rel.h")
+
+FAKE = [0x7F0000000000 + i * 0x100000000 for i in range(16)]   # distinct, never dereferenced
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(xl_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_expected_entry_points():
+    fns = header_functions()
+    for f in ("xl_relpos_embed", "xl_rel_attn_fwd", "xl_rel_attn_core", "xl_segment_step"):
+        assert f in fns
+    assert set(fns) == set(xl.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = xl.lib()
+    for f in header_functions():
+        assert hasattr(lib, f), f
+    nm = subprocess.run(["nm", "-D", "--defined-only", xl.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r" T (xl_\w+)", nm))
+    assert set(header_functions()) <= exported
+
+
+def test_status_strings():
+    lib = xl.lib()
+    assert lib.xl_status_string(0) == b"ok"
+    assert lib.xl_status_string(4) == b"workspace too small"
+    assert lib.xl_status_string(99) == b"unknown status"
+
+
+def _desc(**over):
+    kw = dict(batch=2, d_model=512, n_head=8, d_head=64, qlen=128, mlen=128, dtype=xl.XL_BF16)
+    kw.update(over)
+    return xl.make_desc(**kw)
+
+
+def _weights(bias=False):
+    return xl.xl_attn_weights(*FAKE[:7], FAKE[7] if bias else None)
+
+
+def _fwd(desc, w=None, h=FAKE[8], mem=FAKE[9], out=FAKE[10], ws=FAKE[11], ws_bytes=1 << 40):
+    w = _weights() if w is None else w
+    return xl.lib().xl_rel_attn_fwd(ctypes.byref(desc) if desc is not None else None, ctypes.byref(w), h, mem, out,
+                                    ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(d_head=32), xl.XL_UNSUPPORTED),
+    (dict(dtype=xl.XL_F32), xl.XL_UNSUPPORTED),          # f32 supports d_head 8 only
+    (dict(d_model=511), xl.XL_BAD_SHAPE),
+    (dict(d_model=20), xl.XL_UNSUPPORTED),               # bf16 needs a multiple of 8
+    (dict(qlen=0), xl.XL_BAD_SHAPE),
+    (dict(batch=0), xl.XL_BAD_SHAPE),
+    (dict(mlen=-1), xl.XL_BAD_SHAPE),
+    (dict(dtype=7), xl.XL_BAD_SHAPE),
+    (dict(out_dtype=9), xl.XL_BAD_SHAPE),
+    (dict(base=-1.0), xl.XL_BAD_SHAPE),
+    (dict(scale=float("inf")), xl.XL_BAD_SHAPE),
+    (dict(qlen=1 << 30), xl.XL_UNSUPPORTED),
+])
+def test_fwd_rejects_bad_descriptors(over, status):
+    assert _fwd(_desc(**over)) == status
+    assert xl.lib().xl_last_error() != b""
+
+
+def test_fwd_rejects_null_and_alias_and_small_workspace():
+    lib = xl.lib()
+    assert _fwd(None) == xl.XL_NULL_ARG
+    assert _fwd(_desc(), mem=None) == xl.XL_NULL_ARG                       # mlen > 0 needs mem
+    assert _fwd(_desc(bias_clamp=16)) == xl.XL_NULL_ARG                    # table missing
+    w = _weights()
+    w.w_o = None
+    assert _fwd(_desc(), w=w) == xl.XL_NULL_ARG
+    assert _fwd(_desc(), out=FAKE[8]) == xl.XL_BAD_SHAPE                   # out aliases h
+    d = _desc()
+    need = xl.xl_rel_attn_workspace_size(d)
+    assert _fwd(d, ws_bytes=need - 1) == xl.XL_WORKSPACE_TOO_SMALL
+    assert b"needs" in lib.xl_last_error()
+    assert _fwd(d, ws=FAKE[11] + 8, ws_bytes=need + 8) == xl.XL_UNSUPPORTED  # misaligned workspace
+
+
+def test_workspace_size_formula():
+    for kw in (dict(), dict(clamp_len=100), dict(mlen=0, qlen=37), dict(dtype=xl.XL_F32, d_head=8, d_model=16)):
+        d = _desc(**kw)
+        lay = xl.xl_rel_attn_workspace_layout(d)
+        B, H, dh, q, m, D = d.batch, d.n_head, d.d_head, d.qlen, d.mlen, d.d_model
+        es = 2 if d.dtype == xl.XL_BF16 else 4
+        klen = q + m
+        ldv = (klen + 63) // 64 * 64
+        n_rel = klen if d.clamp_len < 0 else min(klen, d.clamp_len + 1)
+        a = lambda x: (x + 255) // 256 * 256
+        sizes = [B * H * q * dh, B * H * q * dh, B * H * klen * dh, B * H * dh * ldv, n_rel * D, H * n_rel * dh,
+                 B * q * H * dh]
+        assert lay.total == sum(a(s * es) for s in sizes)
+        assert (lay.klen, lay.ldv, lay.n_rel) == (klen, ldv, n_rel)
+        assert xl.xl_rel_attn_workspace_size(d) == lay.total
+        offs = [lay.qu, lay.qv, lay.k, lay.vt, lay.rel, lay.r, lay.attn]
+        assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert xl.xl_rel_attn_workspace_size(_desc(d_head=16)) == 0
+
+
+def test_core_rejects_bad_arguments():
+    lib = xl.lib()
+    d = _desc()
+    klen = d.qlen + d.mlen
+    call = lambda ldv, n_rel, bias=None, desc=d: lib.xl_rel_attn_core(ctypes.byref(desc), *FAKE[:4], ldv, FAKE[5],
+                                                                      n_rel, bias, FAKE[6], None)
+    assert call(klen - 8, klen) == xl.XL_BAD_SHAPE            # ldv < klen
+    assert call(klen + 4, klen) == xl.XL_BAD_SHAPE            # ldv not a multiple of 8
+    assert call(klen, klen - 1) == xl.XL_BAD_SHAPE            # r too short
+    assert call(klen, klen, desc=_desc(bias_clamp=4)) == xl.XL_NULL_ARG
+    assert lib.xl_rel_attn_core(ctypes.byref(d), None, *FAKE[1:4], klen, FAKE[5], klen, None, FAKE[6],
+                                None) == xl.XL_NULL_ARG
+
+
+def test_segment_step_rejects_bad_fifo():
+    lib = xl.lib()
+    d = _desc(mlen=0)
+    w = _weights()
+    step = lambda fifo, h=FAKE[8]: lib.xl_segment_step(ctypes.byref(d), ctypes.byref(w), h,
+                                                       ctypes.byref(fifo) if fifo is not None else None,
+                                                       FAKE[10], FAKE[11], 1 << 40, None)
+    assert step(None) == xl.XL_NULL_ARG
+    assert step(xl.xl_mem_fifo(None, 128, 0, 0)) == xl.XL_NULL_ARG
+    assert step(xl.xl_mem_fifo(FAKE[12], 128, 129, 0)) == xl.XL_BAD_SHAPE     # len > mlen_max
+    assert step(xl.xl_mem_fifo(FAKE[12], 128, 0, 128)) == xl.XL_BAD_SHAPE     # head out of range
+    assert step(xl.xl_mem_fifo(FAKE[12], 0, 0, 0)) == xl.XL_BAD_SHAPE
+    assert step(xl.xl_mem_fifo(FAKE[12], 128, 10, 3), h=FAKE[12] + 64) == xl.XL_BAD_SHAPE  # h inside the ring
+    f = xl.xl_mem_fifo(FAKE[12], 128, 10, 3)
+    assert lib.xl_segment_step(ctypes.byref(d), ctypes.byref(w), FAKE[8], ctypes.byref(f), FAKE[10], FAKE[11],
+                               16, None) == xl.XL_WORKSPACE_TOO_SMALL
+    assert (f.len, f.head) == (10, 3)                                           # untouched on error
+
+
+def test_relpos_rejects_bad_arguments():
+    lib = xl.lib()
+    assert lib.xl_relpos_embed(0, 4, 7, -1, 10000.0, xl.XL_F32, FAKE[0], None) == xl.XL_BAD_SHAPE
+    assert lib.xl_relpos_embed(0, -1, 8, -1, 10000.0, xl.XL_F32, FAKE[0], None) == xl.XL_BAD_SHAPE
+    assert lib.xl_relpos_embed(0, 4, 8, -1, -2.0, xl.XL_F32, FAKE[0], None) == xl.XL_BAD_SHAPE
+    assert lib.xl_relpos_embed(0, 4, 8, -1, 10000.0, 5, FAKE[0], None) == xl.XL_BAD_SHAPE
+    assert lib.xl_relpos_embed(0, 4, 8, -1, 10000.0, xl.XL_F32, None, None) == xl.XL_NULL_ARG
+    assert lib.xl_relpos_embed(0, 0, 8, -1, 10000.0, xl.XL_F32, None, None) == xl.XL_OK   # nothing to do

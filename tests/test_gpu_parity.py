@@ -1,0 +1,274 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 CPU oracle.
+
+Sizes: reduced batches the oracle finishes in seconds (several query/key tiles
+and ragged tails), the full workload sizes in the benchmark's launch
+configuration compared on sampled batch elements, and edge cases. Tolerances:
+bf16 inputs with fp32 accumulation |g-o| <= 1e-2 + 2e-2|o|; the fp32 workload
+|g-o| <= 1e-5 (|o| + max|o|).
+"""
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+import xl_inputs
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+W = xl_inputs.WORKLOADS
+
+
+@pytest.fixture(scope="module")
+def T():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import transformer_xl_relative_amd as xl
+    xl.lib()
+    return torch
+
+
+def _run_layer(T, w, t, *, batch, qlen, mlen, out_f32=True):
+    import transformer_xl_relative_amd as xl
+    L = gu.Layer(w, t, batch=batch, qlen=qlen, mlen=mlen, out_f32=out_f32)
+    h = gu.dev(t["h"])
+    mem = gu.dev(t["mem"]) if mlen > 0 else None
+    xl.xl_rel_attn_fwd(L.desc, L.weights, h, mem, L.out, L.ws)
+    T.cuda.synchronize()
+    return L
+
+
+# --- relative embedding ---------------------------------------------------------
+
+def test_relpos_worked_example(T):
+    import transformer_xl_relative_amd as xl
+    out = T.empty((1, 4), dtype=T.float32, device="cuda")
+    xl.xl_relpos_embed(-2, 1, 4, -1, 10000.0, out)
+    T.cuda.synchronize()
+    got = out.cpu().numpy()[0]
+    assert np.all(np.abs(got - np.array([-0.909, -0.416, -0.020, 0.999])) < 1e-3), got
+
+
+@pytest.mark.parametrize("delta0,n,D,clamp", [(-40, 81, 64, -1), (0, 1664, 512, 1000), (-7, 300, 1024, 128),
+                                              (0, 768, 1024, -1), (3, 5, 16, 16)])
+def test_relpos_vs_oracle(T, delta0, n, D, clamp):
+    import transformer_xl_relative_amd as xl
+    ref = oracle.relpos_embed(delta0, n, D, clamp)
+    o32 = T.empty((n, D), dtype=T.float32, device="cuda")
+    obf = T.empty((n, D), dtype=T.bfloat16, device="cuda")
+    xl.xl_relpos_embed(delta0, n, D, clamp, 10000.0, o32)
+    xl.xl_relpos_embed(delta0, n, D, clamp, 10000.0, obf)
+    T.cuda.synchronize()
+    g32 = o32.cpu().numpy().astype(np.float64)
+    # fp64 evaluation rounded once: within half an ulp of float32 (device and host
+    # libm may differ in the last fp64 bit, hence the small slack)
+    assert np.all(np.abs(g32 - ref) <= 2.0 ** -24 * np.abs(ref) * (1 + 1e-6) + 1e-45)
+    gbf = gu.host64(obf)
+    # bfloat16 keeps 8 significant bits: half an ulp is at most 2^-8 relative
+    assert np.all(np.abs(gbf - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-30)
+    # exactly the nearest bfloat16 of the oracle value except at rounding ties of libm differences
+    want = xl_inputs.bf16_to_f32(xl_inputs.bf16_bits(ref.astype(np.float32))).astype(np.float64)
+    assert np.mean(gbf != want) < 1e-3
+
+
+# --- whole layer at reduced batch: output and every intermediate ---------------------
+
+def _check_intermediates(T, L, w, t, batch, qlen, mlen):
+    lay = L.layout
+    H, dh, D = w.n_head, w.d_head, w.d_model
+    s = 1.0 / np.sqrt(dh)
+    h = t["h"].f64[:batch, :qlen]
+    mem = t["mem"].f64[:batch, :mlen]
+    x = np.concatenate([mem, h], axis=1)
+    klen = qlen + mlen
+    q = oracle.linear(h, t["w_q"].f64).reshape(batch, qlen, H, dh).transpose(0, 2, 1, 3)
+    k = oracle.linear(x, t["w_k"].f64).reshape(batch, klen, H, dh).transpose(0, 2, 1, 3)
+    v = oracle.linear(x, t["w_v"].f64).reshape(batch, klen, H, dh).transpose(0, 2, 1, 3)
+    R = oracle.relpos_embed(0, lay.n_rel, D)
+    r = oracle.linear(R, t["w_r"].f64).reshape(lay.n_rel, H, dh).transpose(1, 0, 2)
+    u, vb = t["u"].f64, t["v"].f64
+    gu.compare("qu", gu.host64(L.ws_view(lay.qu, (batch, H, qlen, dh))), s * (q + u[None, :, None, :]), dtype=w.dtype)
+    gu.compare("qv", gu.host64(L.ws_view(lay.qv, (batch, H, qlen, dh))), s * (q + vb[None, :, None, :]), dtype=w.dtype)
+    gu.compare("k", gu.host64(L.ws_view(lay.k, (batch, H, klen, dh))), k, dtype=w.dtype)
+    vt = gu.host64(L.ws_view(lay.vt, (batch, H, dh, lay.ldv)))[..., :klen]
+    gu.compare("vt", vt, v.transpose(0, 1, 3, 2), dtype=w.dtype)
+    gu.compare("rel", gu.host64(L.ws_view(lay.rel, (lay.n_rel, D))), R, dtype=w.dtype)
+    gu.compare("r", gu.host64(L.ws_view(lay.r, (H, lay.n_rel, dh))), r, dtype=w.dtype)
+
+
+@pytest.mark.parametrize("name,batch,qlen,mlen", [
+    ("tiny_f32", 1, 8, 8),
+    ("base_bf16", 2, 128, 128),
+    ("large_bf16", 1, 384, 384),
+    ("longmem_bf16", 1, 64, 1600),
+])
+def test_layer_reduced(T, name, batch, qlen, mlen):
+    w = W[name]
+    t = xl_inputs.layer_inputs(w, batch=batch, qlen=qlen, mlen=mlen)
+    L = _run_layer(T, w, t, batch=batch, qlen=qlen, mlen=mlen)
+    ref = gu.oracle_layer(t, w, t["h"].f64, t["mem"].f64)
+    gu.compare(f"{name} out", gu.host64(L.out), ref, dtype=w.dtype)
+    _check_intermediates(T, L, w, t, batch, qlen, mlen)
+
+
+def test_layer_bf16_output(T):
+    w = W["base_bf16"]
+    t = xl_inputs.layer_inputs(w, batch=1, qlen=96, mlen=40)
+    L = _run_layer(T, w, t, batch=1, qlen=96, mlen=40, out_f32=False)
+    ref = gu.oracle_layer(t, w, t["h"].f64, t["mem"].f64)
+    gu.compare("bf16 out", gu.host64(L.out), ref, dtype="bf16")
+
+
+# --- full workload sizes, sampled batch elements ------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny_f32", "base_bf16", "large_bf16", "longmem_bf16"])
+def test_layer_full_size_sampled(T, name):
+    w = W[name]
+    t = xl_inputs.layer_inputs(w)
+    L = _run_layer(T, w, t, batch=w.batch, qlen=w.qlen, mlen=w.mlen)
+    out = gu.host64(L.out)
+    bsel = sorted({0, w.batch - 1})
+    ref = gu.oracle_layer(t, w, t["h"].f64, t["mem"].f64, bsel=bsel)
+    gu.compare(f"{name} full (batches {bsel})", out[bsel], ref, dtype=w.dtype)
+
+
+# --- edge cases -------------------------------------------------------------------------------
+
+EDGE = [
+    # (label, dtype workload, qlen, mlen, clamp_len, bias_clamp)
+    ("q1_m0", "base_bf16", 1, 0, -1, -1),
+    ("q1_m1600", "longmem_bf16", 1, 1600, 1000, -1),
+    ("ragged_q37_m91", "base_bf16", 37, 91, -1, -1),
+    ("klen_lt_tile", "base_bf16", 5, 3, -1, -1),
+    ("two_qtiles_ragged", "base_bf16", 200, 17, -1, -1),
+    ("mlen0_q130", "base_bf16", 130, 0, -1, -1),
+    ("clamp0", "base_bf16", 40, 30, 0, -1),
+    ("clamp3", "base_bf16", 40, 30, 3, -1),
+    ("clamp_klen_minus1", "base_bf16", 40, 30, 69, -1),
+    ("bias_on", "base_bf16", 70, 50, -1, 16),
+    ("bias_and_clamp", "base_bf16", 70, 50, 20, 8),
+    ("f32_ragged", "tiny_f32", 13, 29, 5, -1),
+    ("f32_bias", "tiny_f32", 9, 4, -1, 3),
+]
+
+
+@pytest.mark.parametrize("label,base,qlen,mlen,clamp,bias", EDGE, ids=[e[0] for e in EDGE])
+def test_edge_cases(T, label, base, qlen, mlen, clamp, bias):
+    import dataclasses
+    w = dataclasses.replace(W[base], clamp_len=clamp, bias_clamp=bias, seed=zlib.crc32(label.encode()) % 1000)
+    t = xl_inputs.layer_inputs(w, batch=2, qlen=qlen, mlen=mlen)
+    L = _run_layer(T, w, t, batch=2, qlen=qlen, mlen=mlen)
+    ref = gu.oracle_layer(t, w, t["h"].f64, t["mem"].f64)
+    gu.compare(label, gu.host64(L.out), ref, dtype=w.dtype)
+
+
+def test_split_invariance_gpu(T):
+    # the output of a position does not depend on where the memory/segment split falls
+    import dataclasses
+    w = dataclasses.replace(W["base_bf16"], seed=77)
+    t = xl_inputs.layer_inputs(w, batch=1, qlen=100, mlen=60)
+    X = np.concatenate([t["mem"].f32, t["h"].f32], axis=1)
+    outs = []
+    for m in (60, 61):
+        t2 = dict(t)
+        t2["mem"] = xl_inputs.Tensor(X[:, :m], "bf16")
+        t2["h"] = xl_inputs.Tensor(X[:, m:], "bf16")
+        L = _run_layer(T, w, t2, batch=1, qlen=160 - m, mlen=m)
+        outs.append(gu.host64(L.out))
+    np.testing.assert_allclose(outs[0][:, 1:], outs[1], rtol=2e-2, atol=1e-2)
+
+
+# --- the fused attention kernel alone ----------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,B,H,qlen,mlen,clamp,bias", [
+    ("bf16", 2, 3, 200, 75, -1, -1),
+    ("bf16", 1, 2, 64, 1600, 1000, -1),
+    ("bf16", 2, 2, 129, 128, -1, 128),
+    ("f32", 2, 2, 20, 11, 7, -1),
+])
+def test_core_alone(T, dtype, B, H, qlen, mlen, clamp, bias):
+    import transformer_xl_relative_amd as xl
+    dh = 64 if dtype == "bf16" else 8
+    klen = qlen + mlen
+    n_rel = klen if clamp < 0 else min(klen, clamp + 1)
+    ci = xl_inputs.core_inputs(batch=B, n_head=H, d_head=dh, qlen=qlen, mlen=mlen, n_rows=n_rel, dtype=dtype,
+                               seed=B * 100 + qlen, bias_clamp=bias)
+    s = 1.0 / np.sqrt(dh)
+    # operands in the kernel's layout: folded query biases, transposed values
+    qu = xl_inputs.Tensor((s * (ci["q"].f64 + ci["u"].f64[None, :, None, :])).astype(np.float32), dtype)
+    qv = xl_inputs.Tensor((s * (ci["q"].f64 + ci["vb"].f64[None, :, None, :])).astype(np.float32), dtype)
+    ldv = (klen + 7) // 8 * 8 + 8
+    vt = np.zeros((B, H, dh, ldv), np.float32)
+    vt[..., :klen] = ci["v"].f32.transpose(0, 1, 3, 2)
+    vt = xl_inputs.Tensor(vt, dtype)
+    desc = xl.make_desc(batch=B, d_model=2, n_head=H, d_head=dh, qlen=qlen, mlen=mlen, clamp_len=clamp,
+                        bias_clamp=bias, dtype=xl.XL_BF16 if dtype == "bf16" else xl.XL_F32)
+    attn = T.empty((B, qlen, H * dh), dtype=T.bfloat16 if dtype == "bf16" else T.float32, device="cuda")
+    beta = gu.dev(ci["beta"]) if bias >= 0 else None
+    xl.xl_rel_attn_core(desc, gu.dev(qu), gu.dev(qv), gu.dev(ci["k"]), gu.dev(vt), ldv, gu.dev(ci["r"]), n_rel,
+                        beta, attn)
+    T.cuda.synchronize()
+    ref = oracle.rel_attn_core(ci["q"].f64, ci["k"].f64, ci["v"].f64, ci["r"].f64, ci["u"].f64, ci["vb"].f64,
+                               scale=s, clamp_len=clamp, beta=ci["beta"].f64 if bias >= 0 else None,
+                               bias_clamp=bias)
+    gu.compare("core", gu.host64(attn), ref, dtype=dtype)
+
+
+# --- segment-recurrent run with the FIFO memory -------------------------------------------------
+
+def _segment_run_gpu(T, w, t, *, batch, qlen, n_seg, mlen_max, head0=0):
+    import transformer_xl_relative_amd as xl
+    stream = t["h"]
+    D = w.d_model
+    dt = xl.XL_BF16 if w.dtype == "bf16" else xl.XL_F32
+    tdt = T.bfloat16 if w.dtype == "bf16" else T.float32
+    L = gu.Layer(w, t, batch=batch, qlen=qlen, mlen=mlen_max)   # workspace for the largest memory
+    ring = T.zeros((batch, mlen_max, D), dtype=tdt, device="cuda")
+    fifo = xl.xl_mem_fifo(ring.data_ptr(), mlen_max, 0, head0)
+    hs = gu.dev(stream)
+    outs, mems = [], []
+    for s in range(n_seg):
+        h = hs[:, s * qlen:(s + 1) * qlen].contiguous()
+        out = T.empty((batch, qlen, D), dtype=T.float32, device="cuda")
+        desc = xl.make_desc(batch=batch, d_model=D, n_head=w.n_head, d_head=w.d_head, qlen=qlen, mlen=0,
+                            clamp_len=w.clamp_len, bias_clamp=w.bias_clamp, dtype=dt, out_dtype=xl.XL_F32)
+        xl.xl_segment_step(desc, L.weights, h, fifo, out, L.ws)
+        T.cuda.synchronize()
+        outs.append(gu.host64(out))
+        # logical memory order from the ring
+        idx = [(fifo.head + i) % mlen_max for i in range(fifo.len)]
+        mems.append(ring[:, idx].clone())
+        assert fifo.len == min((s + 1) * qlen, mlen_max)
+    return outs, mems
+
+
+@pytest.mark.parametrize("qlen,n_seg,mlen_max,head0", [(128, 4, 128, 0), (96, 4, 200, 0), (64, 3, 50, 7),
+                                                       (40, 5, 100, 99)])
+def test_segment_run_reduced(T, qlen, n_seg, mlen_max, head0):
+    import dataclasses
+    w = dataclasses.replace(W["segments_bf16"], qlen=qlen, mlen=mlen_max, segments=n_seg)
+    t = xl_inputs.layer_inputs(w, batch=1, qlen=qlen)
+    outs, mems = _segment_run_gpu(T, w, t, batch=1, qlen=qlen, n_seg=n_seg, mlen_max=mlen_max, head0=head0)
+    wts = {k: t[k].f64 for k in ("w_q", "w_k", "w_v", "w_r", "w_o", "u", "v", "beta")}
+    routs, rmems = oracle.segment_run(t["h"].f64, n_seg, qlen, mlen_max, wts, n_head=w.n_head, d_head=w.d_head,
+                                      clamp_len=w.clamp_len, bias_clamp=w.bias_clamp)
+    for s in range(n_seg):
+        gu.compare(f"segment {s}", outs[s], routs[s], dtype="bf16")
+        # the memory holds copies of the input states: bit-exact
+        want = xl_inputs.bf16_bits(rmems[s].astype(np.float32))
+        assert np.array_equal(gu.bits_u16(mems[s]), want), f"memory after segment {s} differs"
+
+
+def test_segment_run_full_size_sampled(T):
+    w = W["segments_bf16"]
+    t = xl_inputs.layer_inputs(w)
+    outs, mems = _segment_run_gpu(T, w, t, batch=w.batch, qlen=w.qlen, n_seg=w.segments, mlen_max=w.mlen)
+    wts = {k: t[k].f64 for k in ("w_q", "w_k", "w_v", "w_r", "w_o", "u", "v", "beta")}
+    routs, rmems = oracle.segment_run(t["h"].f64[:1], w.segments, w.qlen, w.mlen, wts, n_head=w.n_head,
+                                      d_head=w.d_head, clamp_len=w.clamp_len, bias_clamp=w.bias_clamp)
+    for s in range(w.segments):
+        gu.compare(f"segment {s} (batch 0)", outs[s][:1], routs[s], dtype="bf16")
+        want = xl_inputs.bf16_bits(rmems[s].astype(np.float32))
+        assert np.array_equal(gu.bits_u16(mems[s][:1]), want)

@@ -1,0 +1,187 @@
+"""Python binding of libxlrel.so, the MI355X (gfx950) Transformer-XL relative
+attention forward. Argument marshalling only: every step of the computation
+runs in the library's HIP kernels. PyTorch supplies device memory and streams.
+
+The names mirror the C ABI in include/xl_rel.h.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libxlrel.so")
+
+XL_OK, XL_NULL_ARG, XL_BAD_SHAPE, XL_UNSUPPORTED, XL_WORKSPACE_TOO_SMALL, XL_HIP_ERROR = range(6)
+XL_F32, XL_BF16 = 0, 1
+
+_i64 = ctypes.c_int64
+_p = ctypes.c_void_p
+
+
+class xl_attn_desc(ctypes.Structure):
+    _fields_ = [("batch", _i64), ("d_model", _i64), ("n_head", _i64), ("d_head", _i64),
+                ("qlen", _i64), ("mlen", _i64), ("clamp_len", _i64), ("bias_clamp", _i64),
+                ("base", ctypes.c_double), ("scale", ctypes.c_float),
+                ("dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32)]
+
+
+class xl_attn_weights(ctypes.Structure):
+    _fields_ = [(n, _p) for n in ("w_q", "w_k", "w_v", "w_r", "w_o", "u", "v", "bias_table")]
+
+
+class xl_ws_layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in ("qu", "qv", "k", "vt", "rel", "r", "attn", "total")] + \
+               [("klen", _i64), ("ldv", _i64), ("n_rel", _i64)]
+
+
+class xl_mem_fifo(ctypes.Structure):
+    _fields_ = [("buf", _p), ("mlen_max", _i64), ("len", _i64), ("head", _i64)]
+
+
+class XLError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+_STATUS = {0: "XL_OK", 1: "XL_NULL_ARG", 2: "XL_BAD_SHAPE", 3: "XL_UNSUPPORTED",
+           4: "XL_WORKSPACE_TOO_SMALL", 5: "XL_HIP_ERROR"}
+
+_lib = None
+
+EXPORTS = ("xl_status_string", "xl_last_error", "xl_relpos_embed", "xl_rel_attn_workspace_size",
+           "xl_rel_attn_workspace_layout", "xl_rel_attn_fwd", "xl_rel_attn_core", "xl_segment_step",
+           "xl_set_core_events")
+
+
+def lib():
+    """Load libxlrel.so. Fails loudly when it has not been built: there is no
+    fallback implementation."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`"
+                              " (or transformer_xl_relative_amd/build.py)")
+        # One HIP runtime per process: PyTorch ships its own libamdhip64 and
+        # loads it under its own file name, so it must be loaded before this
+        # library, whose dependency then binds to that same runtime. Loading
+        # /opt/rocm's runtime first would leave two runtimes in the process.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
+        L = ctypes.CDLL(LIB_PATH)
+        L.xl_status_string.argtypes = [ctypes.c_int]
+        L.xl_status_string.restype = ctypes.c_char_p
+        L.xl_last_error.argtypes = []
+        L.xl_last_error.restype = ctypes.c_char_p
+        L.xl_relpos_embed.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_double, ctypes.c_int, _p, _p]
+        L.xl_rel_attn_workspace_size.argtypes = [ctypes.POINTER(xl_attn_desc)]
+        L.xl_rel_attn_workspace_size.restype = ctypes.c_size_t
+        L.xl_rel_attn_workspace_layout.argtypes = [ctypes.POINTER(xl_attn_desc), ctypes.POINTER(xl_ws_layout)]
+        L.xl_rel_attn_fwd.argtypes = [ctypes.POINTER(xl_attn_desc), ctypes.POINTER(xl_attn_weights), _p, _p, _p,
+                                      _p, ctypes.c_size_t, _p]
+        L.xl_rel_attn_core.argtypes = [ctypes.POINTER(xl_attn_desc), _p, _p, _p, _p, _i64, _p, _i64, _p, _p, _p]
+        L.xl_segment_step.argtypes = [ctypes.POINTER(xl_attn_desc), ctypes.POINTER(xl_attn_weights), _p,
+                                      ctypes.POINTER(xl_mem_fifo), _p, _p, ctypes.c_size_t, _p]
+        L.xl_set_core_events.argtypes = [_p, _p]
+        for f in ("xl_relpos_embed", "xl_rel_attn_workspace_layout", "xl_rel_attn_fwd", "xl_rel_attn_core",
+                  "xl_segment_step", "xl_set_core_events"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != XL_OK:
+        raise XLError(status, lib().xl_last_error().decode())
+
+
+def _ptr(t) -> Optional[int]:
+    """Device address of a tensor (None stays NULL; ints pass through)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libxlrel must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def make_desc(*, batch, d_model, n_head, d_head, qlen, mlen=0, clamp_len=-1, bias_clamp=-1, base=10000.0,
+              scale=0.0, dtype=XL_BF16, out_dtype=None) -> xl_attn_desc:
+    return xl_attn_desc(batch, d_model, n_head, d_head, qlen, mlen, clamp_len, bias_clamp, base, scale,
+                        dtype, dtype if out_dtype is None else out_dtype)
+
+
+@dataclasses.dataclass
+class Weights:
+    """Layer weights as device tensors ([out, in] projection layout)."""
+    w_q: object
+    w_k: object
+    w_v: object
+    w_r: object
+    w_o: object
+    u: object
+    v: object
+    bias_table: object = None
+
+    def c(self) -> xl_attn_weights:
+        return xl_attn_weights(*[_ptr(getattr(self, f)) for f in
+                                 ("w_q", "w_k", "w_v", "w_r", "w_o", "u", "v", "bias_table")])
+
+
+def xl_relpos_embed(delta0: int, n_rows: int, d_model: int, clamp_len: int, base: float, out, stream=None):
+    dt = XL_BF16 if str(out.dtype) == "torch.bfloat16" else XL_F32
+    _check(lib().xl_relpos_embed(delta0, n_rows, d_model, clamp_len, base, dt, _ptr(out), _stream(stream)))
+    return out
+
+
+def xl_rel_attn_workspace_size(desc: xl_attn_desc) -> int:
+    return lib().xl_rel_attn_workspace_size(ctypes.byref(desc))
+
+
+def xl_rel_attn_workspace_layout(desc: xl_attn_desc) -> xl_ws_layout:
+    lay = xl_ws_layout()
+    _check(lib().xl_rel_attn_workspace_layout(ctypes.byref(desc), ctypes.byref(lay)))
+    return lay
+
+
+def xl_rel_attn_fwd(desc: xl_attn_desc, weights: Weights, h, mem, out, ws, stream=None):
+    cw = weights.c() if isinstance(weights, Weights) else weights
+    _check(lib().xl_rel_attn_fwd(ctypes.byref(desc), ctypes.byref(cw), _ptr(h), _ptr(mem), _ptr(out), _ptr(ws),
+                                 ws.numel() * ws.element_size(), _stream(stream)))
+    return out
+
+
+def xl_rel_attn_core(desc: xl_attn_desc, qu, qv, k, vt, ldv: int, r, n_rel: int, bias_table, attn, stream=None):
+    _check(lib().xl_rel_attn_core(ctypes.byref(desc), _ptr(qu), _ptr(qv), _ptr(k), _ptr(vt), ldv, _ptr(r), n_rel,
+                                  _ptr(bias_table), _ptr(attn), _stream(stream)))
+    return attn
+
+
+def xl_segment_step(desc: xl_attn_desc, weights: Weights, h, fifo: xl_mem_fifo, out, ws, stream=None):
+    cw = weights.c() if isinstance(weights, Weights) else weights
+    _check(lib().xl_segment_step(ctypes.byref(desc), ctypes.byref(cw), _ptr(h), ctypes.byref(fifo), _ptr(out),
+                                 _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return out
+
+
+def xl_set_core_events(ev_begin, ev_end):
+    """Record two torch.cuda.Event (or raw hipEvent_t) around the next fused
+    attention launches on this thread; None, None turns it off."""
+    b = ev_begin.cuda_event if hasattr(ev_begin, "cuda_event") else ev_begin
+    e = ev_end.cuda_event if hasattr(ev_end, "cuda_event") else ev_end
+    _check(lib().xl_set_core_events(b, e))

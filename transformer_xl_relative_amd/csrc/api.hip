@@ -1,0 +1,332 @@
+// api.hip -- C ABI of libxlrel: host-side validation, workspace layout and the
+// launch sequence of the relative attention layer. Declarations and the
+// contract of every entry point are in include/xl_rel.h.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/xl_rel.h"
+#include "xl_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+thread_local void* g_ev_begin = nullptr;
+thread_local void* g_ev_end = nullptr;
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(XL_HIP_ERROR, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kI32 = 2147483647;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+size_t esize(int dt) { return dt == XL_BF16 ? 2 : 4; }
+
+// Validate the shape part of a descriptor (mlen given separately).
+int check_desc(const xl_attn_desc* d, int64_t mlen, bool need_dmodel) {
+    if (!d) return fail(XL_NULL_ARG, "desc is NULL");
+    if (d->batch < 1 || d->n_head < 1 || d->qlen < 1 || mlen < 0)
+        return fail(XL_BAD_SHAPE, "batch, n_head, qlen must be >= 1 and mlen >= 0 (got %lld, %lld, %lld, %lld)",
+                    (long long)d->batch, (long long)d->n_head, (long long)d->qlen, (long long)mlen);
+    if (d->dtype != XL_BF16 && d->dtype != XL_F32) return fail(XL_BAD_SHAPE, "dtype must be XL_F32 or XL_BF16");
+    if (!((d->dtype == XL_BF16 && d->d_head == 64) || (d->dtype == XL_F32 && d->d_head == 8)))
+        return fail(XL_UNSUPPORTED, "supported (dtype, d_head): (bf16, 64), (f32, 8); got (%d, %lld)", (int)d->dtype,
+                    (long long)d->d_head);
+    if (need_dmodel) {
+        if (d->d_model < 2 || (d->d_model & 1)) return fail(XL_BAD_SHAPE, "d_model must be even and >= 2");
+        const int64_t mult = d->dtype == XL_BF16 ? 8 : 4;
+        if (d->d_model % mult) return fail(XL_UNSUPPORTED, "d_model must be a multiple of %lld", (long long)mult);
+        if (d->out_dtype != XL_BF16 && d->out_dtype != XL_F32) return fail(XL_BAD_SHAPE, "bad out_dtype");
+        if (d->d_model > 65536) return fail(XL_UNSUPPORTED, "d_model above 65536");
+        if (!(d->base == 0.0 || (d->base > 0.0 && isfinite(d->base)))) return fail(XL_BAD_SHAPE, "base must be > 0");
+        if (!isfinite(d->scale)) return fail(XL_BAD_SHAPE, "scale must be finite");
+    }
+    if (d->bias_clamp > 65535) return fail(XL_UNSUPPORTED, "bias_clamp above 65535");
+    const int64_t klen = mlen + d->qlen;
+    const int64_t hd = d->n_head * d->d_head;
+    // every element count a kernel indexes with 32-bit arithmetic must fit
+    if (klen > kI32 / 64 || d->batch * klen > kI32 / 2 || hd > 65536 || d->batch * d->n_head > kI32 / 64 ||
+        (double)d->batch * d->n_head * klen * d->d_head > 9.0e15)
+        return fail(XL_UNSUPPORTED, "problem too large for this build");
+    if (d->batch * d->n_head * ((d->qlen + 127) / 128) > kI32) return fail(XL_UNSUPPORTED, "grid too large");
+    return XL_OK;
+}
+
+int64_t n_rel_of(const xl_attn_desc* d, int64_t klen) {
+    return d->clamp_len < 0 ? klen : (klen < d->clamp_len + 1 ? klen : d->clamp_len + 1);
+}
+
+void fill_layout(const xl_attn_desc* d, int64_t mlen, xl_ws_layout* L) {
+    const size_t es = esize(d->dtype);
+    const int64_t B = d->batch, H = d->n_head, dh = d->d_head, q = d->qlen, D = d->d_model;
+    const int64_t klen = mlen + q;
+    const int64_t ldv = (klen + 63) / 64 * 64;
+    const int64_t n_rel = n_rel_of(d, klen);
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
+    L->qu = take((size_t)(B * H * q * dh) * es);
+    L->qv = take((size_t)(B * H * q * dh) * es);
+    L->k = take((size_t)(B * H * klen * dh) * es);
+    L->vt = take((size_t)(B * H * dh * ldv) * es);
+    L->rel = take((size_t)(n_rel * D) * es);
+    L->r = take((size_t)(H * n_rel * dh) * es);
+    L->attn = take((size_t)(B * q * H * dh) * es);
+    L->total = off;
+    L->klen = klen;
+    L->ldv = ldv;
+    L->n_rel = n_rel;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const char* pa = (const char*)a;
+    const char* pb = (const char*)b;
+    return pa < pb + nb && pb < pa + na;
+}
+
+int run_core(const xl::AttnArgs& a, bool bf16, int dh, hipStream_t s) {
+    if (g_ev_begin && g_ev_end) {
+        hipError_t e = hipEventRecord((hipEvent_t)g_ev_begin, s);
+        if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    }
+    hipError_t e = xl::launch_attn(a, bf16, dh, s);
+    if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+    if (g_ev_begin && g_ev_end) {
+        e = hipEventRecord((hipEvent_t)g_ev_end, s);
+        if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    }
+    return XL_OK;
+}
+
+// The layer forward on a memory that is either a plain [B, mlen, D] tensor
+// (ring_len == mlen, ring_head == 0) or a FIFO ring.
+int layer_forward(const xl_attn_desc* d, const xl_attn_weights* w, const void* h, const void* mem, int64_t mlen,
+                  int64_t ring_len, int64_t ring_head, void* out, void* ws, size_t ws_bytes, hipStream_t s) {
+    xl_ws_layout L;
+    fill_layout(d, mlen, &L);
+    if (ws_bytes < L.total)
+        return fail(XL_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", ws_bytes, L.total);
+    if (((uintptr_t)ws) % kAlign) return fail(XL_UNSUPPORTED, "workspace must be 256-byte aligned");
+    const bool bf = d->dtype == XL_BF16;
+    const int64_t B = d->batch, H = d->n_head, dh = d->d_head, q = d->qlen, D = d->d_model, HD = H * dh;
+    const int64_t klen = L.klen;
+    const float scale = d->scale == 0.f ? (float)(1.0 / sqrt((double)dh)) : d->scale;
+    const double base = d->base == 0.0 ? 10000.0 : d->base;
+    char* W = (char*)ws;
+    hipError_t e;
+
+    // 1. sinusoid rows R_n, n < n_rel (a distance uses row min(delta, n_rel-1))
+    e = xl::launch_relpos(0, L.n_rel, D, -1, base, bf ? 1 : 0, W + L.rel, s);
+    if (e != hipSuccess) return hip_fail(e, "relpos launch");
+
+    xl::GemmArgs g;
+    memset(&g, 0, sizeof g);
+    g.H = (int)H;
+    g.dh = (int)dh;
+    g.scale = scale;
+    // 2. r = R W_r^T -> [H, n_rel, dh]
+    g.M = (int)L.n_rel; g.N = (int)HD; g.K = (int)D;
+    g.a0 = W + L.rel; g.lda = D; g.a_seq = 0;
+    g.b = w->w_r; g.epi = xl::EPI_R; g.out0 = W + L.r; g.seq = (int)L.n_rel;
+    if ((e = xl::launch_gemm(g, bf, s)) != hipSuccess) return hip_fail(e, "r projection launch");
+    // 3. q projection with the folded biases -> qu, qv
+    g.M = (int)(B * q); g.N = (int)HD; g.K = (int)D;
+    g.a0 = h; g.lda = D; g.a_seq = 0;
+    g.b = w->w_q; g.epi = xl::EPI_Q; g.out0 = W + L.qu; g.out1 = W + L.qv; g.bias0 = w->u; g.bias1 = w->v;
+    g.seq = (int)q;
+    if ((e = xl::launch_gemm(g, bf, s)) != hipSuccess) return hip_fail(e, "q projection launch");
+    // 4. k, v projections over [memory ; segment]
+    g.M = (int)(B * klen); g.N = (int)HD; g.K = (int)D;
+    g.a0 = mlen ? mem : h; g.a1 = h; g.lda = D;
+    g.a0_bstride = ring_len * D; g.a1_bstride = q * D;
+    g.a_seq = (int)klen; g.a_split = (int)mlen; g.ring_len = (int)(ring_len > 0 ? ring_len : 1);
+    g.ring_head = (int)ring_head;
+    g.seq = (int)klen; g.ldv = (int)L.ldv;
+    g.b = w->w_k; g.epi = xl::EPI_K; g.out0 = W + L.k; g.out1 = nullptr;
+    if ((e = xl::launch_gemm(g, bf, s)) != hipSuccess) return hip_fail(e, "k projection launch");
+    g.b = w->w_v; g.epi = xl::EPI_VT; g.out0 = W + L.vt;
+    if ((e = xl::launch_gemm(g, bf, s)) != hipSuccess) return hip_fail(e, "v projection launch");
+    // 5. fused relative attention
+    xl::AttnArgs a;
+    a.qu = W + L.qu; a.qv = W + L.qv; a.k = W + L.k; a.vt = W + L.vt; a.r = W + L.r;
+    a.bias = d->bias_clamp >= 0 ? w->bias_table : nullptr;
+    a.out = W + L.attn;
+    a.B = (int)B; a.H = (int)H; a.qlen = (int)q; a.mlen = (int)mlen; a.klen = (int)klen;
+    a.ldv = (int)L.ldv; a.n_rel = (int)L.n_rel; a.r_rows = (int)L.n_rel; a.bias_clamp = (int)(d->bias_clamp >= 0 ? d->bias_clamp : 0);
+    int st = run_core(a, bf, (int)dh, s);
+    if (st != XL_OK) return st;
+    // 6. output projection
+    memset(&g, 0, sizeof g);
+    g.M = (int)(B * q); g.N = (int)D; g.K = (int)HD;
+    g.a0 = W + L.attn; g.lda = HD; g.a_seq = 0;
+    g.b = w->w_o; g.epi = xl::EPI_OUT; g.out0 = out; g.out_bf16 = d->out_dtype == XL_BF16;
+    g.H = (int)H; g.dh = (int)dh;
+    if ((e = xl::launch_gemm(g, bf, s)) != hipSuccess) return hip_fail(e, "output projection launch");
+    return XL_OK;
+}
+
+int check_weights(const xl_attn_desc* d, const xl_attn_weights* w) {
+    if (!w) return fail(XL_NULL_ARG, "weights is NULL");
+    if (!w->w_q || !w->w_k || !w->w_v || !w->w_r || !w->w_o || !w->u || !w->v)
+        return fail(XL_NULL_ARG, "a weight pointer is NULL");
+    if (d->bias_clamp >= 0 && !w->bias_table) return fail(XL_NULL_ARG, "bias_clamp >= 0 but bias_table is NULL");
+    return XL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* xl_status_string(int status) {
+    switch (status) {
+        case XL_OK: return "ok";
+        case XL_NULL_ARG: return "null argument";
+        case XL_BAD_SHAPE: return "bad shape";
+        case XL_UNSUPPORTED: return "unsupported";
+        case XL_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case XL_HIP_ERROR: return "HIP error";
+        default: return "unknown status";
+    }
+}
+
+const char* xl_last_error(void) { return g_last_error.c_str(); }
+
+int xl_set_core_events(void* ev_begin, void* ev_end) {
+    g_ev_begin = ev_begin;
+    g_ev_end = ev_end;
+    return XL_OK;
+}
+
+int xl_relpos_embed(int64_t delta0, int64_t n_rows, int64_t d_model, int64_t clamp_len, double base, int out_dtype,
+                    void* out, void* stream) {
+    g_last_error.clear();
+    if (n_rows < 0 || d_model < 2 || (d_model & 1)) return fail(XL_BAD_SHAPE, "n_rows >= 0 and even d_model >= 2 required");
+    if (out_dtype != XL_F32 && out_dtype != XL_BF16) return fail(XL_BAD_SHAPE, "bad out_dtype");
+    if (base == 0.0) base = 10000.0;
+    if (!(base > 0.0) || !isfinite(base)) return fail(XL_BAD_SHAPE, "base must be > 0");
+    if (n_rows > kI32 || d_model > kI32 || n_rows * (d_model / 2) > ((int64_t)1 << 40))
+        return fail(XL_UNSUPPORTED, "table too large");
+    if (n_rows == 0) return XL_OK;
+    if (!out) return fail(XL_NULL_ARG, "out is NULL");
+    if (((uintptr_t)out) % 8) return fail(XL_UNSUPPORTED, "out must be 8-byte aligned");
+    hipError_t e = xl::launch_relpos(delta0, n_rows, d_model, clamp_len, base, out_dtype == XL_BF16, out,
+                                     (hipStream_t)stream);
+    return e == hipSuccess ? XL_OK : hip_fail(e, "relpos launch");
+}
+
+size_t xl_rel_attn_workspace_size(const xl_attn_desc* desc) {
+    if (check_desc(desc, desc ? desc->mlen : 0, true) != XL_OK) return 0;
+    xl_ws_layout L;
+    fill_layout(desc, desc->mlen, &L);
+    return L.total;
+}
+
+int xl_rel_attn_workspace_layout(const xl_attn_desc* desc, xl_ws_layout* layout) {
+    g_last_error.clear();
+    int st = check_desc(desc, desc ? desc->mlen : 0, true);
+    if (st != XL_OK) return st;
+    if (!layout) return fail(XL_NULL_ARG, "layout is NULL");
+    fill_layout(desc, desc->mlen, layout);
+    return XL_OK;
+}
+
+int xl_rel_attn_fwd(const xl_attn_desc* desc, const xl_attn_weights* w, const void* h, const void* mem, void* out,
+                    void* ws, size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    int st = check_desc(desc, desc ? desc->mlen : 0, true);
+    if (st != XL_OK) return st;
+    if ((st = check_weights(desc, w)) != XL_OK) return st;
+    if (!h || !out || !ws) return fail(XL_NULL_ARG, "h, out and ws must be non-NULL");
+    if (desc->mlen > 0 && !mem) return fail(XL_NULL_ARG, "mem is NULL with mlen > 0");
+    const size_t es = esize(desc->dtype);
+    const size_t out_bytes = (size_t)(desc->batch * desc->qlen * desc->d_model) * esize(desc->out_dtype);
+    const size_t h_bytes = (size_t)(desc->batch * desc->qlen * desc->d_model) * es;
+    if (overlaps(out, out_bytes, h, h_bytes) ||
+        (desc->mlen > 0 && overlaps(out, out_bytes, mem, (size_t)(desc->batch * desc->mlen * desc->d_model) * es)) ||
+        overlaps(out, out_bytes, ws, ws_bytes))
+        return fail(XL_BAD_SHAPE, "out aliases an input or the workspace");
+    return layer_forward(desc, w, h, mem, desc->mlen, desc->mlen, 0, out, ws, ws_bytes, (hipStream_t)stream);
+}
+
+int xl_rel_attn_core(const xl_attn_desc* desc, const void* qu, const void* qv, const void* k, const void* vt,
+                     int64_t ldv, const void* r, int64_t n_rel, const void* bias_table, void* attn, void* stream) {
+    g_last_error.clear();
+    int st = check_desc(desc, desc ? desc->mlen : 0, false);
+    if (st != XL_OK) return st;
+    if (!qu || !qv || !k || !vt || !r || !attn) return fail(XL_NULL_ARG, "a core operand is NULL");
+    const int64_t klen = desc->mlen + desc->qlen;
+    if (ldv < klen || ldv % 8) return fail(XL_BAD_SHAPE, "ldv must be >= klen and a multiple of 8");
+    if (ldv > kI32 / 64) return fail(XL_UNSUPPORTED, "ldv too large");
+    const int64_t need = n_rel_of(desc, klen);
+    if (n_rel < need) return fail(XL_BAD_SHAPE, "r has %lld rows, needs %lld", (long long)n_rel, (long long)need);
+    if (n_rel > kI32 / 64) return fail(XL_UNSUPPORTED, "r has too many rows");
+    if (desc->bias_clamp >= 0 && !bias_table) return fail(XL_NULL_ARG, "bias_clamp >= 0 but bias_table is NULL");
+    xl::AttnArgs a;
+    a.qu = qu; a.qv = qv; a.k = k; a.vt = vt; a.r = r;
+    a.bias = desc->bias_clamp >= 0 ? bias_table : nullptr;
+    a.out = attn;
+    a.B = (int)desc->batch; a.H = (int)desc->n_head; a.qlen = (int)desc->qlen; a.mlen = (int)desc->mlen;
+    a.klen = (int)klen; a.ldv = (int)ldv; a.n_rel = (int)need; a.r_rows = (int)n_rel;
+    a.bias_clamp = (int)(desc->bias_clamp >= 0 ? desc->bias_clamp : 0);
+    return run_core(a, desc->dtype == XL_BF16, (int)desc->d_head, (hipStream_t)stream);
+}
+
+int xl_segment_step(const xl_attn_desc* desc, const xl_attn_weights* w, const void* h, xl_mem_fifo* fifo, void* out,
+                    void* ws, size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    if (!fifo) return fail(XL_NULL_ARG, "fifo is NULL");
+    if (!fifo->buf) return fail(XL_NULL_ARG, "fifo->buf is NULL");
+    if (fifo->mlen_max < 1 || fifo->len < 0 || fifo->len > fifo->mlen_max || fifo->head < 0 ||
+        fifo->head >= fifo->mlen_max)
+        return fail(XL_BAD_SHAPE, "fifo state invalid (mlen_max %lld, len %lld, head %lld)", (long long)fifo->mlen_max,
+                    (long long)fifo->len, (long long)fifo->head);
+    int st = check_desc(desc, fifo->len, true);
+    if (st != XL_OK) return st;
+    if (fifo->mlen_max > kI32 / 64) return fail(XL_UNSUPPORTED, "mlen_max too large");
+    if ((st = check_weights(desc, w)) != XL_OK) return st;
+    if (!h || !out || !ws) return fail(XL_NULL_ARG, "h, out and ws must be non-NULL");
+    const size_t es = esize(desc->dtype);
+    const size_t h_bytes = (size_t)(desc->batch * desc->qlen * desc->d_model) * es;
+    const size_t ring_bytes = (size_t)(desc->batch * fifo->mlen_max * desc->d_model) * es;
+    const size_t out_bytes = (size_t)(desc->batch * desc->qlen * desc->d_model) * esize(desc->out_dtype);
+    if (overlaps(h, h_bytes, fifo->buf, ring_bytes)) return fail(XL_BAD_SHAPE, "h aliases fifo->buf");
+    if (overlaps(out, out_bytes, fifo->buf, ring_bytes) || overlaps(out, out_bytes, h, h_bytes) ||
+        overlaps(out, out_bytes, ws, ws_bytes))
+        return fail(XL_BAD_SHAPE, "out aliases an input, the memory or the workspace");
+    xl_attn_desc d = *desc;
+    d.mlen = fifo->len;
+    hipStream_t s = (hipStream_t)stream;
+    st = layer_forward(&d, w, h, fifo->buf, fifo->len, fifo->mlen_max, fifo->head, out, ws, ws_bytes, s);
+    if (st != XL_OK) return st;
+    // FIFO update: row t of h lands at ring row (head + len + t) % mlen_max;
+    // only the last min(qlen, mlen_max) rows survive, so only those are written.
+    const int64_t M = fifo->mlen_max, q = desc->qlen;
+    const int64_t n_w = q < M ? q : M;
+    const int64_t src0 = q - n_w;
+    const int64_t dst0 = (fifo->head + fifo->len + src0) % M;
+    hipError_t e = xl::launch_fifo_write(h, q, fifo->buf, M, dst0, src0, n_w, desc->batch,
+                                         desc->d_model * (int64_t)es, s);
+    if (e != hipSuccess) return hip_fail(e, "fifo write launch");
+    const int64_t new_len = fifo->len + q < M ? fifo->len + q : M;
+    fifo->head = (fifo->head + fifo->len + q - new_len) % M;
+    fifo->len = new_len;
+    return XL_OK;
+}
+
+}  // extern "C"

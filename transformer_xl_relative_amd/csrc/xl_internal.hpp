@@ -1,0 +1,68 @@
+// xl_internal.hpp -- launchers shared between the C-ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace xl {
+
+hipError_t launch_relpos(int64_t delta0, int64_t n_rows, int64_t d_model, int64_t clamp_len,
+                         double base, int out_bf16, void* out, hipStream_t s);
+
+// Epilogues of the projection GEMM C = A B^T (A rows: activations, B rows: weights).
+enum EpiKind : int {
+    EPI_Q = 0,    // qu/qv [B,H,seq,dh] = scale*(C + u), scale*(C + v)
+    EPI_K = 1,    // k [B,H,seq,dh]
+    EPI_VT = 2,   // vt [B,H,dh,ldv]
+    EPI_R = 3,    // r [H, seq, dh] (seq = n_rel rows)
+    EPI_OUT = 4,  // out [M, N] row-major, f32 or bf16
+};
+
+struct GemmArgs {
+    int M, N, K;
+    // A-operand rows. Row m of a "concat" problem (a_seq > 0) is token j = m % a_seq
+    // of batch b = m / a_seq: j < a_split comes from the ring a0 (row
+    // (ring_head + j) % ring_len of batch b), otherwise row j - a_split of a1.
+    // With a_seq == 0 row m is a0 + m * lda.
+    const void* a0;
+    const void* a1;
+    int64_t lda;             // elements between consecutive rows
+    int64_t a0_bstride;      // elements between batches of a0
+    int64_t a1_bstride;      // elements between batches of a1
+    int a_seq, a_split, ring_len, ring_head;
+    const void* b;           // [N, K]
+    // epilogue
+    int epi;
+    void* out0;
+    void* out1;
+    const void* bias0;       // u for EPI_Q
+    const void* bias1;       // v for EPI_Q
+    float scale;
+    int H, dh, seq, ldv;
+    int out_bf16;            // EPI_OUT: 1 bf16, 0 f32
+};
+
+hipError_t launch_gemm(const GemmArgs& g, bool bf16, hipStream_t s);
+
+struct AttnArgs {
+    const void* qu;
+    const void* qv;
+    const void* k;
+    const void* vt;
+    const void* r;
+    const void* bias;     // [2*bias_clamp+1, H] or nullptr
+    void* out;            // [B, qlen, H*dh]
+    int B, H, qlen, mlen, klen, ldv;
+    int n_rel;            // distance delta uses row min(delta, n_rel - 1)
+    int r_rows;           // rows per head in r (>= n_rel)
+    int bias_clamp;
+};
+
+hipError_t launch_attn(const AttnArgs& a, bool bf16, int dh, hipStream_t s);
+
+// FIFO write: copies rows h[b, src0 + t, :] (t < n) to ring row
+// (dst0 + t) % ring_len of batch b.
+hipError_t launch_fifo_write(const void* h, int64_t qlen, void* ring, int64_t ring_len, int64_t dst0,
+                             int64_t src0, int64_t n, int64_t B, int64_t row_bytes, hipStream_t s);
+
+}  // namespace xl
