@@ -1,0 +1,179 @@
+"""Benchmark of the Transformer-XL relative attention hot path on one MI355X.
+
+One step = one xl_segment_step of the large-like workload (batch 8, d_model
+1024, 16 heads of 64, qlen = mlen = 384, causal over [memory ; segment]): the
+sinusoid rows, the R/Q/K/V projections, the fused relative attention, the
+output projection and the FIFO memory update, on synthetic seeded inputs that
+are resident in HBM before the timed region starts. The memory FIFO is full,
+so every step attends over 384 memory rows + 384 segment rows.
+
+Prints one JSON line: the layer's algorithmic TFLOP/s (value), the fused
+attention kernel's roofline against the bf16 MFMA peak (kernel time from HIP
+events recorded around its launch in every timed step), and the CPU oracle
+timed on a bounded sample of the same workload.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+HBM_PEAK_GBS = 8000.0
+
+
+def layer_flops(w, mlen):
+    """Algorithmic FLOPs of one layer step: projections + fused attention."""
+    B, D, H, dh, q = w.batch, w.d_model, w.n_head, w.d_head, w.qlen
+    HD = H * dh
+    klen = q + mlen
+    n_rel = klen if w.clamp_len < 0 else min(klen, w.clamp_len + 1)
+    attn = 6.0 * dh * B * H * w.n_valid_pairs(mlen)          # (q+u).k, (q+v).r, P.V
+    proj = 2.0 * D * HD * (n_rel + B * q + 2 * B * klen + B * q)   # r, q, k+v, o
+    return attn + proj, attn
+
+
+def attn_min_bytes(w, mlen):
+    """Algorithmic HBM bytes of the fused attention: qu, qv, k, v, r read once, output written."""
+    B, H, dh, q = w.batch, w.n_head, w.d_head, w.qlen
+    klen = q + mlen
+    n_rel = klen if w.clamp_len < 0 else min(klen, w.clamp_len + 1)
+    es = 2
+    return es * (2 * B * H * q * dh + 2 * B * H * klen * dh + H * n_rel * dh + B * q * H * dh)
+
+
+def cpu_baseline(w, t, min_seconds=10.0):
+    """The oracle (as it stands) on a bounded sample: whole layer forwards of
+    single batch elements of the same workload, repeated until min_seconds."""
+    import oracle
+    n, t0 = 0, time.perf_counter()
+    while True:
+        b = n % w.batch
+        oracle.rel_attn_fwd(t["h"].f64[b:b + 1], t["mem"].f64[b:b + 1], t["w_q"].f64, t["w_k"].f64,
+                            t["w_v"].f64, t["w_r"].f64, t["w_o"].f64, t["u"].f64, t["v"].f64,
+                            n_head=w.n_head, d_head=w.d_head, clamp_len=w.clamp_len,
+                            beta=t["beta"].f64 if "beta" in t else None, bias_clamp=w.bias_clamp)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    flops, _ = layer_flops(w, w.mlen)
+    per_elem = flops / w.batch
+    return {"value": round(per_elem * n / el / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{n} full-layer forwards of one batch element (of {w.batch}) of {w.name}, "
+                      f"fp64, {el:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="large_bf16")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the relative attention forward is "
+              "built and measured on a single MI355X; see the sharding notes in DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import transformer_xl_relative_amd as xl
+    import xl_inputs
+    from tests import gpu_util as gu
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    w = xl_inputs.WORKLOADS[args.workload]
+    if w.dtype != "bf16":
+        raise SystemExit("bench.py measures the bf16 workloads")
+    t = xl_inputs.layer_inputs(w) if w.segments == 1 else None
+    if t is None:
+        # segment workload: bench one steady-state segment (full memory)
+        t = xl_inputs.layer_inputs(dataclass_replace(w, segments=1))
+    D = w.d_model
+    L = gu.Layer(w, t, batch=w.batch, qlen=w.qlen, mlen=w.mlen, out_f32=False)
+    h = gu.dev(t["h"])
+    ring = gu.dev(t["mem"]).contiguous()
+    fifo = xl.xl_mem_fifo(ring.data_ptr(), w.mlen, w.mlen, 0)   # full memory, oldest row first
+    desc = xl.make_desc(batch=w.batch, d_model=D, n_head=w.n_head, d_head=w.d_head, qlen=w.qlen, mlen=0,
+                        clamp_len=w.clamp_len, bias_clamp=w.bias_clamp, dtype=xl.XL_BF16, out_dtype=xl.XL_BF16)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        xl.xl_segment_step(desc, L.weights, h, fifo, L.out, L.ws, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [(xl.HipEvent(), xl.HipEvent()) for _ in range(K)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(K):
+        xl.xl_set_core_events(*evs[i])
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    xl.xl_set_core_events(None, None)
+    gpu_ms = e0.elapsed_time(e1)
+    ms_per_step = gpu_ms / K
+    core_ms = np.array([a.elapsed_ms(b) for a, b in evs])
+    core_avg_ms = float(core_ms.mean())
+    assert fifo.len == w.mlen
+
+    flops, attn_flops = layer_flops(w, w.mlen)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = attn_flops / (core_avg_ms * 1e-3) / 1e12
+    traffic = None
+    res = {
+        "metric": "rel-attn fwd TFLOP/s (4-term+rel_shift) and % bf16 MFMA peak, 1 GPU",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations and memory, N(0,0.02) weights; resident in HBM)",
+        "config": {"workload": f"{w.name}: one segment step (sinusoid, R/Q/K/V projections, fused relative "
+                               f"attention, output projection, FIFO update), batch {w.batch}, d_model {D}, "
+                               f"{w.n_head} heads x {w.d_head}, qlen {w.qlen}, mlen {w.mlen}, causal",
+                   "batch": w.batch, "qlen": w.qlen, "mlen": w.mlen, "d_model": D, "n_head": w.n_head,
+                   "d_head": w.d_head, "clamp_len": w.clamp_len, "bias_clamp": w.bias_clamp},
+        "roofline": {"kernel": "attn_kernel (fused relative attention)", "bound": "mfma",
+                     "achieved": round(achieved, 3), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                     "algorithmic_flops": attn_flops, "avg_kernel_us": round(core_avg_ms * 1e3, 3),
+                     "algorithmic_bytes": attn_min_bytes(w, w.mlen)},
+        "layer_flops_per_step": flops,
+        "wall_s_timed_region": round(wall, 4),
+    }
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(w, t)
+        res["gpu_over_cpu"] = round(value / res["cpu_baseline"]["value"], 1)
+    print(json.dumps(res), flush=True)
+
+
+def dataclass_replace(w, **kw):
+    import dataclasses
+    return dataclasses.replace(w, **kw)
+
+
+if __name__ == "__main__":
+    main()

@@ -32,6 +32,8 @@ def _load():
         lib.orc_rel_attn_core.argtypes = [_i64] * 5 + [_p, _p, _i64, _i64, _dbl] + [_p] * 4 + [_i64, _i64] + [_p] * 6
         lib.orc_rel_attn_fwd.argtypes = [_i64] * 8 + [_dbl, _dbl] + [_p] * 15
         lib.orc_fifo_update.argtypes = [_i64, _i64, _i64, _i64, _p, _i64, _p, _p, ctypes.POINTER(_i64)]
+        lib.orc_num_threads.argtypes = []
+        lib.orc_num_threads.restype = ctypes.c_int
         for f in ("orc_relpos_embed", "orc_linear", "orc_rel_attn_core", "orc_rel_attn_fwd", "orc_fifo_update"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
@@ -57,6 +59,11 @@ class OracleError(RuntimeError):
 def _check(status, what):
     if status != 0:
         raise OracleError(f"{what} returned status {status}")
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle uses."""
+    return int(_load().orc_num_threads())
 
 
 def relpos_embed(delta0: int, n_rows: int, d_model: int, clamp_len: int = -1, base: float = 10000.0):

@@ -310,3 +310,15 @@ int orc_fifo_update(int64_t B, int64_t D, int64_t mlen_max, int64_t mem_len, con
     *new_len = keep;
     return ORC_OK;
 }
+
+/* Number of OpenMP threads the oracle's parallel loops use (1 without OpenMP). */
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+int orc_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

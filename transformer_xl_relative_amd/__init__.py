@@ -185,3 +185,47 @@ def xl_set_core_events(ev_begin, ev_end):
     b = ev_begin.cuda_event if hasattr(ev_begin, "cuda_event") else ev_begin
     e = ev_end.cuda_event if hasattr(ev_end, "cuda_event") else ev_end
     _check(lib().xl_set_core_events(b, e))
+
+
+class HipEvent:
+    """A raw hipEvent_t of the process's HIP runtime (the one torch loaded), for
+    timing with xl_set_core_events: hipEventCreate / hipEventElapsedTime."""
+    _rt = None
+
+    @classmethod
+    def _runtime(cls):
+        if cls._rt is None:
+            lib()   # torch first, then the runtime libxlrel is bound to
+            rt = ctypes.CDLL("libamdhip64.so.7")
+            rt.hipEventCreate.argtypes = [ctypes.POINTER(_p)]
+            rt.hipEventDestroy.argtypes = [_p]
+            rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), _p, _p]
+            rt.hipEventRecord.argtypes = [_p, _p]
+            cls._rt = rt
+        return cls._rt
+
+    def __init__(self):
+        self.handle = _p()
+        st = self._runtime().hipEventCreate(ctypes.byref(self.handle))
+        if st != 0:
+            raise XLError(XL_HIP_ERROR, f"hipEventCreate failed ({st})")
+
+    @property
+    def cuda_event(self):
+        return self.handle.value
+
+    def record(self, stream=None):
+        st = self._runtime().hipEventRecord(self.handle, _stream(stream))
+        if st != 0:
+            raise XLError(XL_HIP_ERROR, f"hipEventRecord failed ({st})")
+
+    def elapsed_ms(self, end: "HipEvent") -> float:
+        ms = ctypes.c_float()
+        st = self._runtime().hipEventElapsedTime(ctypes.byref(ms), self.handle, end.handle)
+        if st != 0:
+            raise XLError(XL_HIP_ERROR, f"hipEventElapsedTime failed ({st})")
+        return ms.value
+
+    def __del__(self):
+        if self._rt is not None and self.handle:
+            self._rt.hipEventDestroy(self.handle)
