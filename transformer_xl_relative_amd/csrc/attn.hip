@@ -7,102 +7,127 @@
 //   with qu = scale*(q+u), qv = scale*(q+v), delta = mlen + i - j,
 //   masked to -inf for j > mlen + i (2kiu.com §4.2), softmax over j, o = P.V.
 //
-// Work decomposition: one workgroup = (batch, head, 128 queries); 4 waves of
-// 32 queries; keys stream in steps of 32.
+// Work decomposition: one workgroup = (batch, head, NW*32 queries); a wave
+// owns 32 queries; keys stream in steps of 32. Workgroups are issued
+// longest-first (query tiles near the end of the segment see more keys).
 //
 // MFMA layout: every product is computed transposed (keys / distances on the
 // MFMA rows, queries on the columns), so a lane owns one query and the
-// softmax reductions stay inside the lane (plus one swap between the two
-// half-waves).
+// softmax reductions stay inside the lane plus one swap of the half-waves.
 //
-// Relative shift: the position term of query i and key j only depends on
-// delta. Each step a wave multiplies its 32 queries by the 32 band rows of
-// the distances that enter its window (one 32x32 MFMA block), and writes the
-// result into a per-wave LDS ring indexed by absolute key (j mod 64). Reading
-// the ring at the step's keys is then an aligned, contiguous LDS read, and it
-// initialises the accumulator of the content product, so the four terms are
-// summed by the MFMA itself. Every band row is multiplied once per query: the
-// position product costs the same as the content product, and the L x L
-// position matrix is never formed.
+// Relative shift: the position term of query i and key j depends on delta
+// only. A "block" is the 32x32 product of a wave's 32 queries with 32
+// consecutive band rows of r (descending distance). Block beta holds, for
+// query ii of the wave, the position terms of keys 32*beta - 31 + ii ..
+// 32*beta + ii. Blocks are written into a per-wave LDS ring indexed by
+// absolute key (j mod 64, each row rotated against bank conflicts); step s
+// reads its 32 keys from the ring (blocks s and s+1) as the initial value of
+// the content product's accumulator, so the MFMA sums the four terms.
+// Software pipeline: during step s a wave issues the content product of step
+// s+1 and the position block for step s+2's window (block s+3), which the
+// MFMA unit runs while the VALU does the softmax of step s. Each band row is
+// multiplied once
+// per query: the position product costs what the content product costs, and
+// the L x L position matrix is never formed.
 //
-// Data movement: K (row-major) and V^T tiles are staged through two LDS
-// stages (one barrier per step); band rows of r go straight from L2 into the
-// MFMA operand registers one step ahead; qu/qv stay in registers.
+// Data movement: K (row-major) tiles are staged two steps ahead and V^T tiles
+// one step ahead through two LDS buffers each (one barrier per step); band
+// rows of r go from L2 straight into the MFMA operand registers one block
+// ahead; qu/qv stay in registers.
 #include "xl_common.hpp"
 #include "xl_internal.hpp"
+
+#include <type_traits>
+
+#ifndef XL_ATTN_WAVES
+#define XL_ATTN_WAVES 4
+#endif
 
 namespace xl {
 namespace {
 
-constexpr int NW = 4;            // waves per workgroup
 constexpr int WQ = 32;           // queries per wave
-constexpr int BQ = NW * WQ;      // queries per workgroup
 constexpr int BKY = 32;          // keys per step
-constexpr int RING = 64;         // key slots per query in the ring
-constexpr int RSTR = 68;         // floats per query row of the ring (4 pad)
+constexpr int RING = 64;         // key slots per query in the ring (floats, 256 B per row)
 constexpr float LOG2E = 1.4426950408889634f;
-constexpr float RESCALE_TH = 5.5451774444795623f;   // 8 * ln 2: rescale only when the max grows by 2^8
+constexpr float RESCALE_TH = 5.5451774444795623f;   // 8 ln 2: rescale only when the max grows by 2^8
 
-template <typename T, int DH>
+template <typename T, int DH, int NW>
 struct AttnLds {
-    static constexpr int KROW = DH * (int)sizeof(T) + 16;
+    static constexpr int KROW = DH * (int)sizeof(T) + 16;     // padded key row
     static constexpr int KTILE = BKY * KROW;
-    static constexpr int VROW = BKY * (int)sizeof(T) + 8;
+    static constexpr int VROW = BKY * (int)sizeof(T) + 8;     // padded row of V^T
     static constexpr int VTILE = DH * VROW;
     static constexpr int OFF_K = 0;
     static constexpr int OFF_V = 2 * KTILE;
-    static constexpr int OFF_RING = ((OFF_V + 2 * VTILE) + 15) / 16 * 16;
-    static constexpr int TOTAL = OFF_RING + NW * WQ * RSTR * 4;
+    static constexpr int OFF_RING = ((OFF_V + 2 * VTILE) + 255) / 256 * 256;
+    static constexpr int TOTAL = OFF_RING + NW * WQ * RING * 4;
 };
 
-template <typename T, int DH>
-__global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
-    using L = AttnLds<T, DH>;
+// Lanes l and l^32 exchange a value; the two results of the swap hold one
+// value of each half in every lane.
+__device__ __forceinline__ float halves_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <typename T, int DH, int NW, bool HAS_BIAS>
+__global__ void __launch_bounds__(NW * 64) attn_kernel(AttnArgs a) {
+    using L = AttnLds<T, DH, NW>;
     constexpr bool BF = Elem<T>::kBf16;
+    constexpr int NT = NW * 64;
+    constexpr int BQ = NW * WQ;
     constexpr int EPC = 16 / (int)sizeof(T);          // elements per 16-byte chunk
     constexpr int NKC = BF ? DH / 16 : DH / 2;        // MFMA k-steps over d_head
     static_assert(NKC >= 1, "d_head too small");
     using OpT = typename std::conditional<BF, bf16x8, float>::type;
-    extern __shared__ __attribute__((aligned(16))) char smem[];
+    extern __shared__ __attribute__((aligned(256))) char smem[];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: per-wave values live in SGPRs
     const int l32 = lane & 31, hf = lane >> 5;
 
-    // ---- workgroup -> (batch, head, query tile); the longest tiles go first
+    // ---- work item: all heads' last query tiles first
+    // (integer division runs on the vector unit; readfirstlane returns the
+    // wave-uniform results to scalar registers so that branches on them are
+    // scalar branches)
+    const int nbh = a.B * a.H;
     const int nqt = (a.qlen + BQ - 1) / BQ;
-    const int bh = blockIdx.x / nqt;
-    const int qt = nqt - 1 - (int)(blockIdx.x - bh * nqt);
-    const int b = bh / a.H, h = bh - b * a.H;
+    const int qt = __builtin_amdgcn_readfirstlane(nqt - 1 - (int)(blockIdx.x / nbh));
+    const int bh = __builtin_amdgcn_readfirstlane((int)(blockIdx.x % nbh));
+    const int h = __builtin_amdgcn_readfirstlane(bh % a.H);
+    const int b = __builtin_amdgcn_readfirstlane(bh / a.H);
     const int i0 = qt * BQ;
     const int iw = i0 + wave * WQ;                     // first query of this wave
     const int qend = min(i0 + BQ, a.qlen);
-    const int kend = a.mlen + qend;                    // keys [0, kend) are visible to someone
-    const int nsteps = (kend + BKY - 1) / BKY;
+    const int kend = a.mlen + qend;                    // keys [0, kend) are visible to some query
+    const int nsteps = __builtin_amdgcn_readfirstlane((kend + BKY - 1) / BKY);
     const int wlast = iw < a.qlen ? a.mlen + min(iw + WQ, a.qlen) - 1 : -1;
-    const int wsteps = wlast >= 0 ? wlast / BKY + 1 : 0;   // steps with a visible key for this wave
+    const int wsteps = __builtin_amdgcn_readfirstlane(wlast >= 0 ? wlast / BKY + 1 : 0);   // steps with a visible key for this wave
 
     const T* kbase = (const T*)a.k + (int64_t)bh * a.klen * DH;
     const T* vtbase = (const T*)a.vt + (int64_t)bh * DH * a.ldv;
     const T* rbase = (const T*)a.r + (int64_t)h * a.r_rows * DH;
-    const bool has_bias = a.bias != nullptr;
-    const T* bias = (const T*)a.bias;
 
     // ---- query operands (MFMA B operand): lane owns query iw + l32
     const int iq = iw + l32;
     const bool qok = iq < a.qlen;
     OpT quB[NKC], qvB[NKC];
     {
-        const T* qu = (const T*)a.qu + ((int64_t)bh * a.qlen + (qok ? iq : 0)) * DH;
-        const T* qv = (const T*)a.qv + ((int64_t)bh * a.qlen + (qok ? iq : 0)) * DH;
+        const int64_t row = ((int64_t)bh * a.qlen + (qok ? iq : a.qlen - 1)) * DH;
+        const T* qu = (const T*)a.qu + row;
+        const T* qv = (const T*)a.qv + row;
         for (int kc = 0; kc < NKC; ++kc) {
             if constexpr (BF) {
-                const int off = 16 * kc + 8 * hf;
-                quB[kc] = qok ? as_bf16x8(*(const u32x4*)(qu + off)) : as_bf16x8((u32x4){0, 0, 0, 0});
-                qvB[kc] = qok ? as_bf16x8(*(const u32x4*)(qv + off)) : as_bf16x8((u32x4){0, 0, 0, 0});
+                quB[kc] = as_bf16x8(*(const u32x4*)(qu + 16 * kc + 8 * hf));
+                qvB[kc] = as_bf16x8(*(const u32x4*)(qv + 16 * kc + 8 * hf));
             } else {
-                const int off = 2 * kc + hf;
-                quB[kc] = qok ? Elem<T>::to_f(qu[off]) : 0.f;
-                qvB[kc] = qok ? Elem<T>::to_f(qv[off]) : 0.f;
+                quB[kc] = Elem<T>::to_f(qu[2 * kc + hf]);
+                qvB[kc] = Elem<T>::to_f(qv[2 * kc + hf]);
             }
         }
     }
@@ -113,71 +138,127 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
     OpT band[NKC];
     auto load_band = [&](int beta) {
         int d = dtop - BKY * beta - l32;
-        d = d < 0 ? 0 : (d >= a.n_rel ? a.n_rel - 1 : d);
+        d = max(0, min(d, a.n_rel - 1));
         const T* row = rbase + (int64_t)d * DH;
         for (int kc = 0; kc < NKC; ++kc) {
             if constexpr (BF) band[kc] = as_bf16x8(*(const u32x4*)(row + 16 * kc + 8 * hf));
             else band[kc] = Elem<T>::to_f(row[2 * kc + hf]);
         }
     };
-
-    float* ring = (float*)(smem + L::OFF_RING) + (wave * WQ + l32) * RSTR;   // this lane's query row
-    // position block -> ring: register r <-> slot c = acc_row(r, hf) <-> key
-    // j = l32 - (WQ-1) + 32*beta + c (absolute), stored at j mod 64
-    auto pos_block = [&](int beta) {
+    auto pos_product = [&](int beta) {
         f32x16 g;
-        if (has_bias) {
+        if constexpr (HAS_BIAS) {
+            const T* bias = (const T*)a.bias;
             const int dblk = dtop - BKY * beta;
             for (int r = 0; r < 16; ++r) {
-                int d = dblk - acc_row(r, hf);
-                d = d < 0 ? 0 : (d > a.bias_clamp ? a.bias_clamp : d);
-                g[r] = Elem<T>::to_f(bias[(int64_t)(d + a.bias_clamp) * a.H + h]);
+                const int d = max(0, min(dblk - acc_row(r, hf), a.bias_clamp));
+                g[r] = Elem<T>::to_f(bias[(d + a.bias_clamp) * a.H + h]);
             }
         } else {
             for (int r = 0; r < 16; ++r) g[r] = 0.f;
         }
         for (int kc = 0; kc < NKC; ++kc) g = mfma32(band[kc], qvB[kc], g);
-        const int jb = l32 - (WQ - 1) + BKY * beta;
-        for (int r = 0; r < 16; ++r) ring[(jb + acc_row(r, hf)) & (RING - 1)] = g[r];
+        return g;
     };
 
-    // ---- K / V^T tile staging (global -> registers -> LDS)
+    // ---- ring addresses. Logical slot p of query row ii lives at float
+    // (p + 4 ii) mod 64 of a 256-byte row: groups of 4 consecutive slots stay
+    // contiguous and aligned, the writes of one register (32 consecutive
+    // slots over the lanes) and the 16-byte reads of one group (8 rows) hit
+    // distinct banks, and moving a slot by 32 (the other parity of a block or
+    // a step) is address ^ 128.
+    const uint32_t ring_row = (uint32_t)L::OFF_RING + (uint32_t)(wave * WQ + l32) * (RING * 4);
+    uint32_t waddr[16];          // block of even index: register r -> byte address of its key slot
+    for (int r = 0; r < 16; ++r) {
+        const int p = (l32 - (WQ - 1) + acc_row(r, hf)) & (RING - 1);
+        waddr[r] = ring_row + (uint32_t)(((p + 4 * l32) & (RING - 1)) << 2);
+    }
+    uint32_t rq[4];              // even step: 16-byte index of the 4 groups of 4 consecutive keys
+    for (int g = 0; g < 4; ++g) rq[g] = (ring_row >> 4) + (uint32_t)((((8 * g + 4 * hf) + 4 * l32) & (RING - 1)) >> 2);
+    auto ring_write = [&](const f32x16& g, int parity) {
+        const uint32_t flip = (uint32_t)parity << 7;
+        for (int r = 0; r < 16; ++r) *(float*)(smem + (waddr[r] ^ flip)) = g[r];
+    };
+    auto ring_read = [&](int parity) {
+        const uint32_t flip = (uint32_t)parity << 3;   // 128 bytes in 16-byte units
+        const f32x4* base = (const f32x4*)smem;
+        f32x16 acc;
+        for (int g = 0; g < 4; ++g) {
+            const f32x4 t4 = base[rq[g] ^ flip];
+            acc[4 * g] = t4[0]; acc[4 * g + 1] = t4[1]; acc[4 * g + 2] = t4[2]; acc[4 * g + 3] = t4[3];
+        }
+        return acc;
+    };
+    // content product of a step (its K tile in LDS buffer kbuf) on top of its position terms
+    auto content = [&](f32x16 acc, int kbuf) {
+        const char* kt = smem + L::OFF_K + kbuf * L::KTILE + l32 * L::KROW;
+        for (int kc = 0; kc < NKC; ++kc) {
+            OpT ka;
+            if constexpr (BF) ka = as_bf16x8(*(const u32x4*)(kt + (2 * kc + hf) * 16));
+            else ka = *(const float*)(kt + (2 * kc + hf) * 4);
+            acc = mfma32(ka, quB[kc], acc);
+        }
+        return acc;
+    };
+
+    // ---- K / V^T tile staging (global -> registers -> LDS). K of step s is
+    // needed one step early (the content product runs a step ahead), so K
+    // tiles are staged two steps ahead and V^T tiles one step ahead.
     constexpr int KCPR = DH * (int)sizeof(T) / 16;     // 16-byte chunks per key row
     constexpr int KCH = BKY * KCPR;                    // chunks per K tile
     constexpr int VCPR = BKY * (int)sizeof(T) / 16;    // chunks per V^T row
     constexpr int VCH = DH * VCPR;
-    static_assert(KCH <= 256 && VCH <= 256, "tile larger than one chunk per thread");
-    u32x4 kreg = {0, 0, 0, 0}, vreg = {0, 0, 0, 0};
-    auto stage_load = [&](int s) {
+    constexpr int KPT = (KCH + NT - 1) / NT, VPT = (VCH + NT - 1) / NT;
+    u32x4 kreg[KPT], vreg[VPT];
+    auto load_k = [&](int s) {
         const int j0 = s * BKY;
-        if (tid < KCH) {
-            const int jr = tid / KCPR, c = tid - jr * KCPR;
-            const int j = j0 + jr;
-            kreg = j < a.klen ? *(const u32x4*)(kbase + (int64_t)j * DH + c * EPC) : (u32x4){0, 0, 0, 0};
-        }
-        if (tid < VCH) {
-            const int d = tid / VCPR, c = tid - d * VCPR;
-            const int j = j0 + c * EPC;
-            const T* src = vtbase + (int64_t)d * a.ldv + j;
-            if (j + EPC <= a.klen) {
-                vreg = *(const u32x4*)src;
-            } else {
-                T tmp[EPC];
-                for (int e = 0; e < EPC; ++e) tmp[e] = (j + e < a.klen) ? src[e] : (T)0;
-                vreg = __builtin_bit_cast(u32x4, tmp);
+        for (int t = 0; t < KPT; ++t) {
+            const int c = tid + t * NT;
+            if (KCH % NT == 0 || c < KCH) {
+                const int jr = c / KCPR, cc = c - jr * KCPR;
+                const int j = min(j0 + jr, a.klen - 1);        // rows past the end are masked keys
+                kreg[t] = *(const u32x4*)(kbase + (int64_t)j * DH + cc * EPC);
             }
         }
     };
-    auto stage_store = [&](int buf) {
-        if (tid < KCH) {
-            const int jr = tid / KCPR, c = tid - jr * KCPR;
-            *(u32x4*)(smem + L::OFF_K + buf * L::KTILE + jr * L::KROW + c * 16) = kreg;
+    auto store_k = [&](int buf) {
+        for (int t = 0; t < KPT; ++t) {
+            const int c = tid + t * NT;
+            if (KCH % NT == 0 || c < KCH) {
+                const int jr = c / KCPR, cc = c - jr * KCPR;
+                *(u32x4*)(smem + L::OFF_K + buf * L::KTILE + jr * L::KROW + cc * 16) = kreg[t];
+            }
         }
-        if (tid < VCH) {
-            const int d = tid / VCPR, c = tid - d * VCPR;
-            char* dst = smem + L::OFF_V + buf * L::VTILE + d * L::VROW + c * 16;
-            *(u32x2*)dst = (u32x2){vreg[0], vreg[1]};
-            *(u32x2*)(dst + 8) = (u32x2){vreg[2], vreg[3]};
+    };
+    auto load_v = [&](int s) {
+        const int j0 = s * BKY;
+        const bool tail = j0 + BKY > a.klen;
+        for (int t = 0; t < VPT; ++t) {
+            const int c = tid + t * NT;
+            if (VCH % NT == 0 || c < VCH) {
+                const int d = c / VCPR, cc = c - d * VCPR;
+                const int j = j0 + cc * EPC;
+                const T* src = vtbase + (int64_t)d * a.ldv + j;
+                if (!tail) {
+                    vreg[t] = *(const u32x4*)src;
+                } else {
+                    // the last tile: values of keys >= klen are zero (their weight is 0)
+                    T tmp[EPC];
+                    for (int e = 0; e < EPC; ++e) tmp[e] = (j + e < a.klen) ? src[e] : (T)0;
+                    vreg[t] = __builtin_bit_cast(u32x4, tmp);
+                }
+            }
+        }
+    };
+    auto store_v = [&](int buf) {
+        for (int t = 0; t < VPT; ++t) {
+            const int c = tid + t * NT;
+            if (VCH % NT == 0 || c < VCH) {
+                const int d = c / VCPR, cc = c - d * VCPR;
+                char* dst = smem + L::OFF_V + buf * L::VTILE + d * L::VROW + cc * 16;
+                *(u32x2*)dst = (u32x2){vreg[t][0], vreg[t][1]};
+                *(u32x2*)(dst + 8) = (u32x2){vreg[t][2], vreg[t][3]};
+            }
         }
     };
 
@@ -188,47 +269,60 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
         for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
-    stage_load(0);
-    stage_store(0);
+    // prologue: K of steps 0 and 1, V of step 0; blocks 0..2; content of step 0
+    load_k(0);
+    store_k(0);
+    if (nsteps > 1) {
+        load_k(1);
+        store_k(1);
+    }
+    load_v(0);
+    store_v(0);
+    f32x16 scur;
     if (wsteps > 0) {
         load_band(0);
-        pos_block(0);
+        ring_write(pos_product(0), 0);
         load_band(1);
+        ring_write(pos_product(1), 1);
+        if (wsteps > 1) load_band(2);
+    }
+    __syncthreads();
+    if (wsteps > 0) {
+        scur = content(ring_read(0), 0);
+        if (wsteps > 1) {
+            ring_write(pos_product(2), 0);     // block 2 replaces block 0, already read
+            if (wsteps > 2) load_band(3);
+        }
     }
     __syncthreads();
 
     for (int s = 0; s < nsteps; ++s) {
         const int j0 = s * BKY;
-        const bool more = s + 1 < nsteps;
-        if (more) stage_load(s + 1);
+        const int par = s & 1;
+        if (s + 2 < nsteps) load_k(s + 2);
+        if (s + 1 < nsteps) load_v(s + 1);
         if (s < wsteps) {
-            // position block for the distances entering at this step
-            pos_block(s + 1);
-            if (s + 1 < wsteps) load_band(s + 2);
-            // relative-shifted position term of this step's keys -> accumulator
-            f32x16 sacc;
-            for (int gq = 0; gq < 4; ++gq) {
-                const f32x4 t4 = *(const f32x4*)(ring + ((j0 + 8 * gq + 4 * hf) & (RING - 1)));
-                sacc[4 * gq] = t4[0]; sacc[4 * gq + 1] = t4[1]; sacc[4 * gq + 2] = t4[2]; sacc[4 * gq + 3] = t4[3];
+            // the next step's scores: its position terms (blocks s+1, s+2) and content product
+            f32x16 snext, gnext;
+            const bool have_next = s + 1 < wsteps;
+            const bool want_block = s + 2 < wsteps;          // block s+3, read at step s+1
+            if (have_next) snext = content(ring_read(par ^ 1), par ^ 1);
+            if (want_block) {
+                gnext = pos_product(s + 3);
+                if (s + 3 < wsteps) load_band(s + 4);
             }
-            // content term
-            const char* kt = smem + L::OFF_K + (s & 1) * L::KTILE + l32 * L::KROW;
-            for (int kc = 0; kc < NKC; ++kc) {
-                OpT ka;
-                if constexpr (BF) ka = as_bf16x8(*(const u32x4*)(kt + (2 * kc + hf) * 16));
-                else ka = *(const float*)(kt + (2 * kc + hf) * 4);
-                sacc = mfma32(ka, quB[kc], sacc);
-            }
-            // causal mask: key j0 + jj is hidden from query iw + l32 when j > mlen + i
+            // causal mask of this step: key j0 + jj is hidden from query iw + l32 when j > mlen + i
             if (j0 + BKY - 1 > a.mlen + iw) {
                 const int lim = a.mlen + iw + l32 - j0;
                 for (int r = 0; r < 16; ++r)
-                    if (acc_row(r, hf) > lim) sacc[r] = -INFINITY;
+                    if (acc_row(r, hf) > lim) scur[r] = -INFINITY;
             }
-            // online softmax with lazy rescaling
-            float mx = sacc[0];
-            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            // online softmax with lazy rescaling: the exponentials are taken
+            // against the running maximum, which moves (rescaling the running
+            // sums) only when some row's maximum grew by more than 2^8
+            float mx = fmaxf(fmaxf(scur[0], scur[1]), fmaxf(scur[2], scur[3]));
+            for (int r = 4; r < 16; r += 2) mx = fmaxf(mx, fmaxf(scur[r], scur[r + 1]));
+            mx = halves_max(mx);
             if (__any(mx > m_run + RESCALE_TH)) {
                 const float mnew = fmaxf(m_run, mx);
                 const float alpha = __builtin_amdgcn_exp2f((m_run - mnew) * LOG2E);
@@ -239,18 +333,24 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
             }
             const float mb = m_run * LOG2E;
             float p[16];
-            float psum = 0.f;
-            for (int r = 0; r < 16; ++r) {
-                p[r] = __builtin_amdgcn_exp2f(fmaf(sacc[r], LOG2E, -mb));
-                psum += p[r];
-            }
-            l_run += psum;
+            for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(scur[r], LOG2E, -mb));
+            if (want_block) ring_write(gnext, par ^ 1);      // block s+3 replaces block s+1, already read
             // O^T += V^T P^T
-            const char* vt = smem + L::OFF_V + (s & 1) * L::VTILE;
+            const char* vt = smem + L::OFF_V + par * L::VTILE;
             if constexpr (BF) {
                 bf16x8 pb[2];
                 for (int kc = 0; kc < 2; ++kc)
                     for (int e = 0; e < 8; ++e) pb[kc][e] = (__bf16)p[8 * kc + e];
+                // the row sum uses the same rounded weights as P.V
+                typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+                const bf16x2v one = {(__bf16)1.0f, (__bf16)1.0f};
+                float psum = 0.f;
+                for (int kc = 0; kc < 2; ++kc)
+                    for (int e = 0; e < 8; e += 2) {
+                        const bf16x2v pr = {pb[kc][e], pb[kc][e + 1]};
+                        psum = __builtin_amdgcn_fdot2_f32_bf16(pr, one, psum, false);
+                    }
+                l_run += psum;
                 for (int t = 0; t < NDT; ++t) {
                     const char* vrow = vt + (32 * t + l32) * L::VROW;
                     for (int kc = 0; kc < 2; ++kc) {
@@ -261,6 +361,9 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
                     }
                 }
             } else {
+                float psum = 0.f;
+                for (int r = 0; r < 16; ++r) psum += p[r];
+                l_run += psum;
                 const bool drow = l32 < DH;
                 const float* vrow = (const float*)(vt + (drow ? l32 : 0) * L::VROW);
                 for (int r = 0; r < 16; ++r) {
@@ -268,13 +371,15 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
                     o[0] = mfma32(va, p[r], o[0]);
                 }
             }
+            if (have_next) scur = snext;
         }
-        if (more) stage_store((s + 1) & 1);
+        if (s + 2 < nsteps) store_k(par);          // K of step s+2 replaces K of step s
+        if (s + 1 < nsteps) store_v(par ^ 1);      // V of step s+1 replaces V of step s-1
         __syncthreads();
     }
 
     // ---- epilogue: o / l, heads concatenated
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const float l_tot = halves_sum(l_run);
     if (!qok || wsteps == 0) return;
     const float inv = 1.f / l_tot;
     T* orow = (T*)a.out + ((int64_t)b * a.qlen + iq) * ((int64_t)a.H * DH) + (int64_t)h * DH;
@@ -289,29 +394,36 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs a) {
         }
 }
 
-template <typename T, int DH>
+template <typename T, int DH, int NW, bool HAS_BIAS>
 hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
-    using L = AttnLds<T, DH>;
+    using L = AttnLds<T, DH, NW>;
     static bool attr_set = false;
     if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)attn_kernel<T, DH>,
+        hipError_t e = hipFuncSetAttribute((const void*)attn_kernel<T, DH, NW, HAS_BIAS>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, L::TOTAL);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
+    constexpr int BQ = NW * WQ;
     const int nqt = (a.qlen + BQ - 1) / BQ;
     const int64_t grid = (int64_t)a.B * a.H * nqt;
     if (grid <= 0) return hipSuccess;
     (void)hipGetLastError();   // drop a stale error of an earlier runtime call
-    hipLaunchKernelGGL((attn_kernel<T, DH>), dim3((unsigned)grid), dim3(256), L::TOTAL, s, a);
+    hipLaunchKernelGGL((attn_kernel<T, DH, NW, HAS_BIAS>), dim3((unsigned)grid), dim3(NW * 64), L::TOTAL, s, a);
     return hipGetLastError();
+}
+
+template <typename T, int DH>
+hipError_t launch_dt(const AttnArgs& a, hipStream_t s) {
+    constexpr int NW = XL_ATTN_WAVES;
+    return a.bias ? launch_t<T, DH, NW, true>(a, s) : launch_t<T, DH, NW, false>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_attn(const AttnArgs& a, bool bf16, int dh, hipStream_t s) {
-    if (bf16 && dh == 64) return launch_t<bf16_t, 64>(a, s);
-    if (!bf16 && dh == 8) return launch_t<float, 8>(a, s);
+    if (bf16 && dh == 64) return launch_dt<bf16_t, 64>(a, s);
+    if (!bf16 && dh == 8) return launch_dt<float, 8>(a, s);
     return hipErrorInvalidValue;
 }
 
