@@ -84,8 +84,8 @@ int xl_relpos_embed(int64_t delta0, int64_t n_rows, int64_t d_model, int64_t cla
 /* Shape and numerics of one relative-attention layer call. */
 typedef struct {
     int64_t batch;       /* B >= 1 */
-    int64_t d_model;     /* D: even; multiple of 8 for bf16, of 4 for f32 */
-    int64_t n_head;      /* H >= 1 */
+    int64_t d_model;     /* D: multiple of 32 for bf16, of 16 for f32 */
+    int64_t n_head;      /* H >= 1; H*d_head a multiple of 32 (bf16) / 16 (f32) */
     int64_t d_head;      /* 64 (bf16) or 8 (f32) */
     int64_t qlen;        /* segment length, >= 1 */
     int64_t mlen;        /* memory length, >= 0 (ignored by xl_segment_step) */

@@ -65,7 +65,7 @@ def _fwd(desc, w=None, h=FAKE[8], mem=FAKE[9], out=FAKE[10], ws=FAKE[11], ws_byt
     (dict(d_head=32), xl.XL_UNSUPPORTED),
     (dict(dtype=xl.XL_F32), xl.XL_UNSUPPORTED),          # f32 supports d_head 8 only
     (dict(d_model=511), xl.XL_BAD_SHAPE),
-    (dict(d_model=20), xl.XL_UNSUPPORTED),               # bf16 needs a multiple of 8
+    (dict(d_model=40), xl.XL_UNSUPPORTED),               # bf16 needs a multiple of 32
     (dict(qlen=0), xl.XL_BAD_SHAPE),
     (dict(batch=0), xl.XL_BAD_SHAPE),
     (dict(mlen=-1), xl.XL_BAD_SHAPE),

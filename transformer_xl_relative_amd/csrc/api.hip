@@ -51,8 +51,11 @@ int check_desc(const xl_attn_desc* d, int64_t mlen, bool need_dmodel) {
                     (long long)d->d_head);
     if (need_dmodel) {
         if (d->d_model < 2 || (d->d_model & 1)) return fail(XL_BAD_SHAPE, "d_model must be even and >= 2");
-        const int64_t mult = d->dtype == XL_BF16 ? 8 : 4;
+        // the projection GEMMs advance K in whole 64-byte stages
+        const int64_t mult = d->dtype == XL_BF16 ? 32 : 16;
         if (d->d_model % mult) return fail(XL_UNSUPPORTED, "d_model must be a multiple of %lld", (long long)mult);
+        if ((d->n_head * d->d_head) % mult)
+            return fail(XL_UNSUPPORTED, "n_head * d_head must be a multiple of %lld", (long long)mult);
         if (d->out_dtype != XL_BF16 && d->out_dtype != XL_F32) return fail(XL_BAD_SHAPE, "bad out_dtype");
         if (d->d_model > 65536) return fail(XL_UNSUPPORTED, "d_model above 65536");
         if (!(d->base == 0.0 || (d->base > 0.0 && isfinite(d->base)))) return fail(XL_BAD_SHAPE, "base must be > 0");
@@ -135,33 +138,58 @@ int layer_forward(const xl_attn_desc* d, const xl_attn_weights* w, const void* h
     e = xl::launch_relpos(0, L.n_rel, D, -1, base, bf ? 1 : 0, W + L.rel, s);
     if (e != hipSuccess) return hip_fail(e, "relpos launch");
 
-    xl::GemmArgs g;
-    memset(&g, 0, sizeof g);
-    g.H = (int)H;
-    g.dh = (int)dh;
-    g.scale = scale;
-    // 2. r = R W_r^T -> [H, n_rel, dh]
-    g.M = (int)L.n_rel; g.N = (int)HD; g.K = (int)D;
-    g.a0 = W + L.rel; g.lda = D; g.a_seq = 0;
-    g.b = w->w_r; g.epi = xl::EPI_R; g.out0 = W + L.r; g.seq = (int)L.n_rel;
-    if ((e = xl::launch_gemm(g, bf, s)) != hipSuccess) return hip_fail(e, "r projection launch");
-    // 3. q projection with the folded biases -> qu, qv
-    g.M = (int)(B * q); g.N = (int)HD; g.K = (int)D;
-    g.a0 = h; g.lda = D; g.a_seq = 0;
-    g.b = w->w_q; g.epi = xl::EPI_Q; g.out0 = W + L.qu; g.out1 = W + L.qv; g.bias0 = w->u; g.bias1 = w->v;
-    g.seq = (int)q;
-    if ((e = xl::launch_gemm(g, bf, s)) != hipSuccess) return hip_fail(e, "q projection launch");
-    // 4. k, v projections over [memory ; segment]
-    g.M = (int)(B * klen); g.N = (int)HD; g.K = (int)D;
-    g.a0 = mlen ? mem : h; g.a1 = h; g.lda = D;
-    g.a0_bstride = ring_len * D; g.a1_bstride = q * D;
-    g.a_seq = (int)klen; g.a_split = (int)mlen; g.ring_len = (int)(ring_len > 0 ? ring_len : 1);
-    g.ring_head = (int)ring_head;
-    g.seq = (int)klen; g.ldv = (int)L.ldv;
-    g.b = w->w_k; g.epi = xl::EPI_K; g.out0 = W + L.k; g.out1 = nullptr;
-    if ((e = xl::launch_gemm(g, bf, s)) != hipSuccess) return hip_fail(e, "k projection launch");
-    g.b = w->w_v; g.epi = xl::EPI_VT; g.out0 = W + L.vt;
-    if ((e = xl::launch_gemm(g, bf, s)) != hipSuccess) return hip_fail(e, "v projection launch");
+    // 2-4. the input projections as one grid: r = R W_r^T, q with the folded
+    // biases, and k, v over [memory ; segment]
+    xl::GemmArgs g[4];
+    memset(g, 0, sizeof g);
+    int ng = 0;
+    auto base_args = [&](xl::GemmArgs& a) {
+        a.H = (int)H;
+        a.dh = (int)dh;
+        a.scale = scale;
+        a.b_split = 1 << 30;
+    };
+    {   // r = R W_r^T -> [H, n_rel, dh]
+        xl::GemmArgs& a = g[ng++];
+        base_args(a);
+        a.M = (int)L.n_rel; a.N = (int)HD; a.K = (int)D;
+        a.a0 = W + L.rel; a.lda = D;
+        a.b0 = w->w_r; a.epi = xl::EPI_R; a.out0 = W + L.r; a.seq = (int)L.n_rel;
+    }
+    {   // q projection -> qu, qv
+        xl::GemmArgs& a = g[ng++];
+        base_args(a);
+        a.M = (int)(B * q); a.N = (int)HD; a.K = (int)D;
+        a.a0 = h; a.lda = D;
+        a.b0 = w->w_q; a.epi = xl::EPI_Q; a.out0 = W + L.qu; a.out1 = W + L.qv; a.bias0 = w->u; a.bias1 = w->v;
+        a.seq = (int)q;
+    }
+    auto kv_rows = [&](xl::GemmArgs& a) {
+        a.M = (int)(B * klen); a.K = (int)D;
+        a.a0 = mlen ? mem : h; a.a1 = h; a.lda = D;
+        a.a0_bstride = ring_len * D; a.a1_bstride = q * D;
+        a.a_seq = (int)klen; a.a_split = (int)mlen; a.ring_len = (int)(ring_len > 0 ? ring_len : 1);
+        a.ring_head = (int)ring_head;
+        a.seq = (int)klen; a.ldv = (int)L.ldv;
+    };
+    if (HD % 128 == 0) {   // k and v share the A rows: one problem, weight rows [W_k ; W_v]
+        xl::GemmArgs& a = g[ng++];
+        base_args(a);
+        kv_rows(a);
+        a.N = (int)(2 * HD);
+        a.b0 = w->w_k; a.b1 = w->w_v; a.b_split = (int)HD;
+        a.epi = xl::EPI_KV; a.out0 = W + L.k; a.out1 = W + L.vt;
+    } else {
+        xl::GemmArgs& a = g[ng++];
+        base_args(a);
+        kv_rows(a);
+        a.N = (int)HD;
+        a.b0 = w->w_k; a.epi = xl::EPI_K; a.out0 = W + L.k;
+        xl::GemmArgs& c = g[ng++];
+        c = a;
+        c.b0 = w->w_v; c.epi = xl::EPI_VT; c.out0 = W + L.vt;
+    }
+    if ((e = xl::launch_gemms(g, ng, bf, s)) != hipSuccess) return hip_fail(e, "projection launch");
     // 5. fused relative attention
     xl::AttnArgs a;
     a.qu = W + L.qu; a.qv = W + L.qv; a.k = W + L.k; a.vt = W + L.vt; a.r = W + L.r;
@@ -172,12 +200,14 @@ int layer_forward(const xl_attn_desc* d, const xl_attn_weights* w, const void* h
     int st = run_core(a, bf, (int)dh, s);
     if (st != XL_OK) return st;
     // 6. output projection
-    memset(&g, 0, sizeof g);
-    g.M = (int)(B * q); g.N = (int)D; g.K = (int)HD;
-    g.a0 = W + L.attn; g.lda = HD; g.a_seq = 0;
-    g.b = w->w_o; g.epi = xl::EPI_OUT; g.out0 = out; g.out_bf16 = d->out_dtype == XL_BF16;
-    g.H = (int)H; g.dh = (int)dh;
-    if ((e = xl::launch_gemm(g, bf, s)) != hipSuccess) return hip_fail(e, "output projection launch");
+    xl::GemmArgs go;
+    memset(&go, 0, sizeof go);
+    go.M = (int)(B * q); go.N = (int)D; go.K = (int)HD;
+    go.a0 = W + L.attn; go.lda = HD; go.a_seq = 0;
+    go.b0 = w->w_o; go.b_split = 1 << 30; go.epi = xl::EPI_OUT; go.out0 = out;
+    go.out_bf16 = d->out_dtype == XL_BF16;
+    go.H = (int)H; go.dh = (int)dh;
+    if ((e = xl::launch_gemm(go, bf, s)) != hipSuccess) return hip_fail(e, "output projection launch");
     return XL_OK;
 }
 

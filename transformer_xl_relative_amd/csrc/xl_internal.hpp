@@ -16,8 +16,10 @@ enum EpiKind : int {
     EPI_VT = 2,   // vt [B,H,dh,ldv]
     EPI_R = 3,    // r [H, seq, dh] (seq = n_rel rows)
     EPI_OUT = 4,  // out [M, N] row-major, f32 or bf16
+    EPI_KV = 5,   // columns n < b_split: k (out0), the others: vt (out1)
 };
 
+// One projection C = A B^T with its epilogue.
 struct GemmArgs {
     int M, N, K;
     // A-operand rows. Row m of a "concat" problem (a_seq > 0) is token j = m % a_seq
@@ -30,7 +32,10 @@ struct GemmArgs {
     int64_t a0_bstride;      // elements between batches of a0
     int64_t a1_bstride;      // elements between batches of a1
     int a_seq, a_split, ring_len, ring_head;
-    const void* b;           // [N, K]
+    // B-operand rows ([out, in] weights): row n < b_split is b0[n], else b1[n - b_split]
+    const void* b0;
+    const void* b1;
+    int b_split;
     // epilogue
     int epi;
     void* out0;
@@ -42,7 +47,12 @@ struct GemmArgs {
     int out_bf16;            // EPI_OUT: 1 bf16, 0 f32
 };
 
-hipError_t launch_gemm(const GemmArgs& g, bool bf16, hipStream_t s);
+constexpr int kMaxGemms = 4;
+
+// Launch up to kMaxGemms independent projections as one grid (their tiles
+// share the machine). K of every problem must be a multiple of 64 bytes.
+hipError_t launch_gemms(const GemmArgs* g, int count, bool bf16, hipStream_t s);
+inline hipError_t launch_gemm(const GemmArgs& g, bool bf16, hipStream_t s) { return launch_gemms(&g, 1, bf16, s); }
 
 struct AttnArgs {
     const void* qu;
