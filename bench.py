@@ -13,10 +13,21 @@ events recorded around its launch in every timed step), and the CPU oracle
 timed on a bounded sample of the same workload.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+                  [--copy-calib-mib M]        # also run a plain device copy of M MiB (counter calibration)
+  python bench.py --summarize DIR [--copy-calib-mib M]   # markdown summary of rocprofv3 output under DIR
+
+HBM traffic of the attention kernel comes from two rocprofv3 --pmc passes
+(FETCH_SIZE, then WRITE_SIZE) over this script with --copy-calib-mib, each
+counter scaled by known bytes / counted KiB of the plain copy in the same
+run. The scaled figures are recorded in TRAFFIC below together with the
+SHA-256 of the kernel sources they were taken on; when the sources differ,
+the reported traffic is null.
 """
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -27,6 +38,23 @@ sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 HBM_PEAK_GBS = 8000.0
+
+# Sources that make up the fused attention kernel; the traffic record below is
+# valid only for this exact text.
+ATTN_SOURCES = ("transformer_xl_relative_amd/csrc/attn.hip", "transformer_xl_relative_amd/csrc/xl_common.hpp",
+                "transformer_xl_relative_amd/csrc/xl_internal.hpp", "transformer_xl_relative_amd/build.py")
+
+# HBM bytes per launch of the fused attention kernel (calibrated FETCH_SIZE and
+# WRITE_SIZE, see profiles/attn_kernel_<workload>_pmc_traffic.md).
+TRAFFIC = {}
+
+
+def attn_sources_sha():
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 
 def layer_flops(w, mlen):
@@ -79,7 +107,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="large_bf16")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="before warm-up, run a plain device-to-device copy of this many MiB three times")
+    ap.add_argument("--summarize", metavar="DIR", help="print a summary of the rocprofv3 databases under DIR")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args.summarize, args.copy_calib_mib)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the relative attention forward is "
               "built and measured on a single MI355X; see the sharding notes in DESIGN.md", file=sys.stderr)
@@ -112,6 +146,15 @@ def main():
     def step():
         xl.xl_segment_step(desc, L.weights, h, fifo, L.out, L.ws, stream)
 
+    if args.copy_calib_mib > 0:
+        n = args.copy_calib_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -137,7 +180,8 @@ def main():
     flops, attn_flops = layer_flops(w, w.mlen)
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = attn_flops / (core_avg_ms * 1e-3) / 1e12
-    traffic = None
+    rec = TRAFFIC.get(w.name)
+    traffic = rec["bytes"] if rec is not None and rec["sha256"] == attn_sources_sha() else None
     res = {
         "metric": "rel-attn fwd TFLOP/s (4-term+rel_shift) and % bf16 MFMA peak, 1 GPU",
         "value": round(value, 3),
@@ -168,6 +212,53 @@ def main():
         res["cpu_baseline"] = cpu_baseline(w, t)
         res["gpu_over_cpu"] = round(value / res["cpu_baseline"]["value"], 1)
     print(json.dumps(res), flush=True)
+
+
+def summarize(d, copy_mib):
+    """Markdown tables from the rocprofv3 SQLite output under d: per-kernel
+    launch count and average duration, and for counter runs the average
+    counter value per dispatch (with the copy-kernel scale factor when the
+    run held a plain copy of copy_mib MiB)."""
+    import collections
+    import sqlite3
+    dbs = sorted(glob.glob(os.path.join(d, "**", "*.db"), recursive=True))
+    if not dbs:
+        raise SystemExit(f"no rocprofv3 database under {d}")
+
+    def short(name):
+        return name.replace("void ", "").replace("xl::(anonymous namespace)::", "").split("(")[0]
+
+    for db in dbs:
+        c = sqlite3.connect(db)
+        tabs = {r[0] for r in c.execute("select name from sqlite_master")}
+        print(f"### {os.path.relpath(db, d)}\n")
+        if "kernels" in tabs:
+            dur = collections.defaultdict(list)
+            for name, gx, wx, st, en in c.execute("select name, grid_x, workgroup_x, start, end from kernels"):
+                dur[(short(name), gx // max(wx, 1))].append((en - st) / 1e3)
+            if dur:
+                print("| kernel | workgroups | launches | avg us | min us | max us |")
+                print("|---|---|---|---|---|---|")
+                for (k, wg), v in sorted(dur.items(), key=lambda kv: -sum(kv[1])):
+                    print(f"| {k} | {wg} | {len(v)} | {sum(v) / len(v):.3f} | {min(v):.3f} | {max(v):.3f} |")
+                print()
+        if "counters_collection" in tabs:
+            agg = collections.defaultdict(list)
+            for kname, cname, val in c.execute("select kernel_name, counter_name, value from counters_collection"):
+                agg[(short(kname), cname)].append(val)
+            if agg:
+                print("| kernel | counter | dispatches | avg per dispatch |")
+                print("|---|---|---|---|")
+                for (k, cn), v in sorted(agg.items()):
+                    print(f"| {k} | {cn} | {len(v)} | {sum(v) / len(v):.1f} |")
+                print()
+                if copy_mib:
+                    kib = copy_mib * 1024
+                    for (k, cn), v in sorted(agg.items()):
+                        if "copyBuffer" in k and cn in ("FETCH_SIZE", "WRITE_SIZE"):
+                            avg = sum(v) / len(v)
+                            print(f"copy calibration {cn}: {kib} KiB moved, {avg:.1f} KiB counted, "
+                                  f"scale {kib / avg:.4f}\n")
 
 
 def dataclass_replace(w, **kw):

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libxlrel.so")
-SOURCES = ["api.hip", "relpos.hip", "gemm.hip", "attn.hip"]
+SOURCES = ["api.hip", "relpos.hip", "gemm.hip", "attn.hip", "attn_bf16.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -24,6 +24,7 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
 # read them with vector instructions, which AGPRs would force through copies.
 # IEEE mode off (no NaNs occur): maxima compile to v_max3 without quieting.
 PER_SOURCE = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mno-amdgpu-ieee", "-fno-honor-nans"],
+              "attn_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mno-amdgpu-ieee", "-fno-honor-nans"],
               "gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 

@@ -422,7 +422,7 @@ hipError_t launch_dt(const AttnArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_attn(const AttnArgs& a, bool bf16, int dh, hipStream_t s) {
-    if (bf16 && dh == 64) return launch_dt<bf16_t, 64>(a, s);
+    if (bf16 && dh == 64) return launch_attn_bf16(a, s);
     if (!bf16 && dh == 8) return launch_dt<float, 8>(a, s);
     return hipErrorInvalidValue;
 }

@@ -8,8 +8,9 @@
 // issued three stages ahead through a ring of four LDS stages, so the loads of
 // later stages are in flight while a stage is multiplied. Tile rows are 64
 // bytes; the four 16-byte chunks of row r are stored XOR-swizzled by
-// (r >> 1) & 3, which spreads the MFMA operand reads of 8 consecutive rows
-// over all banks. Rows past the end of A or B are clamped to the last row
+// (r >> 2) & 3. A 16-byte LDS read is served 16 lanes at a time, and those
+// lanes must hit 16 distinct 16-byte bank groups: the MFMA operand reads of
+// 16 consecutive rows (4 per 256 bytes) then fall on 16 distinct groups. Rows past the end of A or B are clamped to the last row
 // (their products land in outputs that are never stored).
 //
 // Both operands are K-contiguous, so the MFMA A/B roles are chosen per tile:
@@ -36,7 +37,7 @@ struct GemmBatch {
     int count;
 };
 
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & 3; }
+__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
 
 template <typename T>
 __device__ __forceinline__ const T* a_row_ptr(const GemmArgs& g, int m) {

@@ -68,6 +68,8 @@ struct AttnArgs {
     int bias_clamp;
 };
 
+// fused attention for bf16 operands and d_head 64 (attn_bf16.hip)
+hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, bool bf16, int dh, hipStream_t s);
 
 // FIFO write: copies rows h[b, src0 + t, :] (t < n) to ring row
