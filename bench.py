@@ -46,7 +46,10 @@ ATTN_SOURCES = ("transformer_xl_relative_amd/csrc/attn.hip", "transformer_xl_rel
 
 # HBM bytes per launch of the fused attention kernel (calibrated FETCH_SIZE and
 # WRITE_SIZE, see profiles/attn_kernel_<workload>_pmc_traffic.md).
-TRAFFIC = {}
+TRAFFIC = {
+    "large_bf16": {"sha256": "b49c3b12f5f7be2f2a713e379ec5a3d215a7094e0885238b86e8d0c1749d6a7d",
+                   "bytes": 45952116, "fetch_bytes": 39660660, "write_bytes": 6291456},
+}
 
 
 def attn_sources_sha():
@@ -147,9 +150,12 @@ def main():
         xl.xl_segment_step(desc, L.weights, h, fifo, L.out, L.ws, stream)
 
     if args.copy_calib_mib > 0:
-        n = args.copy_calib_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
-        dst = torch.empty_like(src)
+        # a plain elementwise copy kernel (int32 -> float32 conversion: reads and
+        # writes 4 bytes per element); the runtime's blit copy is not used because
+        # its non-temporal accesses are undercounted by FETCH_SIZE / WRITE_SIZE
+        n = (args.copy_calib_mib << 20) // 4
+        src = torch.ones(n, dtype=torch.int32, device="cuda")
+        dst = torch.empty(n, dtype=torch.float32, device="cuda")
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
@@ -255,7 +261,7 @@ def summarize(d, copy_mib):
                 if copy_mib:
                     kib = copy_mib * 1024
                     for (k, cn), v in sorted(agg.items()):
-                        if "copyBuffer" in k and cn in ("FETCH_SIZE", "WRITE_SIZE"):
+                        if "copy_kernel" in k and cn in ("FETCH_SIZE", "WRITE_SIZE"):
                             avg = sum(v) / len(v)
                             print(f"copy calibration {cn}: {kib} KiB moved, {avg:.1f} KiB counted, "
                                   f"scale {kib / avg:.4f}\n")

@@ -188,10 +188,11 @@ int xl_segment_step(const xl_attn_desc* desc, const xl_attn_weights* w, const vo
                     xl_mem_fifo* fifo, void* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * Timing hook: when both are non-NULL, hipEvent_t handles ev_begin/ev_end are
- * recorded on the launch stream immediately before and after the fused
- * attention kernel of the next calls of xl_rel_attn_fwd, xl_segment_step and
- * xl_rel_attn_core on this thread. NULL, NULL switches it off.
+ * Timing hook: when both are non-NULL, the hipEvent_t handles ev_begin/ev_end
+ * take the start and end timestamps of the fused attention kernel itself
+ * (passed to the runtime with the kernel launch) in the next calls of
+ * xl_rel_attn_fwd, xl_segment_step and xl_rel_attn_core on this thread, on the
+ * launch stream. NULL, NULL switches it off. Returns XL_OK.
  */
 int xl_set_core_events(void* ev_begin, void* ev_end);
 

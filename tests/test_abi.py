@@ -74,6 +74,7 @@ def _fwd(desc, w=None, h=FAKE[8], mem=FAKE[9], out=FAKE[10], ws=FAKE[11], ws_byt
     (dict(base=-1.0), xl.XL_BAD_SHAPE),
     (dict(scale=float("inf")), xl.XL_BAD_SHAPE),
     (dict(qlen=1 << 30), xl.XL_UNSUPPORTED),
+    (dict(bias_clamp=128, mlen=20000, qlen=200), xl.XL_UNSUPPORTED),   # LDS bias table limit
 ])
 def test_fwd_rejects_bad_descriptors(over, status):
     assert _fwd(_desc(**over)) == status

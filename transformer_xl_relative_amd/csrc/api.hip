@@ -39,6 +39,10 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 size_t esize(int dt) { return dt == XL_BF16 ? 2 : 4; }
 
+// longest context the bf16 attention's LDS bias table covers (80 KB of tiles
+// and rings plus 4 bytes per table entry, mlen + qlen + 384 entries, <= 160 KB)
+constexpr int64_t kMaxBiasKlen = (80 * 1024) / 4 - 384;
+
 // Validate the shape part of a descriptor (mlen given separately).
 int check_desc(const xl_attn_desc* d, int64_t mlen, bool need_dmodel) {
     if (!d) return fail(XL_NULL_ARG, "desc is NULL");
@@ -69,6 +73,9 @@ int check_desc(const xl_attn_desc* d, int64_t mlen, bool need_dmodel) {
         (double)d->batch * d->n_head * klen * d->d_head > 9.0e15)
         return fail(XL_UNSUPPORTED, "problem too large for this build");
     if (d->batch * d->n_head * ((d->qlen + 127) / 128) > kI32) return fail(XL_UNSUPPORTED, "grid too large");
+    // the bf16 attention keeps the bias table of a workgroup's distances in LDS
+    if (d->bias_clamp >= 0 && d->dtype == XL_BF16 && klen > kMaxBiasKlen)
+        return fail(XL_UNSUPPORTED, "with a bias table, mlen + qlen must be <= %lld", (long long)kMaxBiasKlen);
     return XL_OK;
 }
 
@@ -104,16 +111,11 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 int run_core(const xl::AttnArgs& a, bool bf16, int dh, hipStream_t s) {
-    if (g_ev_begin && g_ev_end) {
-        hipError_t e = hipEventRecord((hipEvent_t)g_ev_begin, s);
-        if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-    }
-    hipError_t e = xl::launch_attn(a, bf16, dh, s);
+    // with timing events set, the runtime timestamps the kernel itself
+    const bool timed = g_ev_begin && g_ev_end;
+    hipError_t e = xl::launch_attn(a, bf16, dh, s, timed ? (hipEvent_t)g_ev_begin : nullptr,
+                                   timed ? (hipEvent_t)g_ev_end : nullptr);
     if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
-    if (g_ev_begin && g_ev_end) {
-        e = hipEventRecord((hipEvent_t)g_ev_end, s);
-        if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-    }
     return XL_OK;
 }
 

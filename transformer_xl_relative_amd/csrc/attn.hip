@@ -35,6 +35,7 @@
 // rows of r go from L2 straight into the MFMA operand registers one block
 // ahead; qu/qv stay in registers.
 #include "xl_common.hpp"
+#include <hip/hip_ext.h>
 #include "xl_internal.hpp"
 
 #include <type_traits>
@@ -395,7 +396,7 @@ __global__ void __launch_bounds__(NW * 64) attn_kernel(AttnArgs a) {
 }
 
 template <typename T, int DH, int NW, bool HAS_BIAS>
-hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
+hipError_t launch_t(const AttnArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     using L = AttnLds<T, DH, NW>;
     static bool attr_set = false;
     if (!attr_set) {
@@ -409,21 +410,22 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
     const int64_t grid = (int64_t)a.B * a.H * nqt;
     if (grid <= 0) return hipSuccess;
     (void)hipGetLastError();   // drop a stale error of an earlier runtime call
-    hipLaunchKernelGGL((attn_kernel<T, DH, NW, HAS_BIAS>), dim3((unsigned)grid), dim3(NW * 64), L::TOTAL, s, a);
+    hipExtLaunchKernelGGL((attn_kernel<T, DH, NW, HAS_BIAS>), dim3((unsigned)grid), dim3(NW * 64), L::TOTAL, s, ev0,
+                          ev1, 0u, a);
     return hipGetLastError();
 }
 
 template <typename T, int DH>
-hipError_t launch_dt(const AttnArgs& a, hipStream_t s) {
+hipError_t launch_dt(const AttnArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     constexpr int NW = XL_ATTN_WAVES;
-    return a.bias ? launch_t<T, DH, NW, true>(a, s) : launch_t<T, DH, NW, false>(a, s);
+    return a.bias ? launch_t<T, DH, NW, true>(a, s, ev0, ev1) : launch_t<T, DH, NW, false>(a, s, ev0, ev1);
 }
 
 }  // namespace
 
-hipError_t launch_attn(const AttnArgs& a, bool bf16, int dh, hipStream_t s) {
-    if (bf16 && dh == 64) return launch_attn_bf16(a, s);
-    if (!bf16 && dh == 8) return launch_dt<float, 8>(a, s);
+hipError_t launch_attn(const AttnArgs& a, bool bf16, int dh, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+    if (bf16 && dh == 64) return launch_attn_bf16(a, s, ev0, ev1);
+    if (!bf16 && dh == 8) return launch_dt<float, 8>(a, s, ev0, ev1);
     return hipErrorInvalidValue;
 }
 

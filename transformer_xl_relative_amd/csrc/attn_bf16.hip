@@ -42,6 +42,7 @@
 // buffer return zeros (buffer range checking), which keeps the load count per
 // step fixed and the waits exact.
 #include "xl_common.hpp"
+#include <hip/hip_ext.h>
 #include "xl_internal.hpp"
 
 #include <type_traits>
@@ -502,7 +503,7 @@ __global__ void __launch_bounds__(NT, 2) attn_bf16_kernel(AttnArgs a) {
 }
 
 template <bool HAS_BIAS>
-hipError_t launch_bf16(const AttnArgs& a, hipStream_t s) {
+hipError_t launch_bf16(const AttnArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     const int nqt = (a.qlen + BQ - 1) / BQ;
     const int64_t grid = (int64_t)a.B * a.H * nqt;
     if (grid <= 0) return hipSuccess;
@@ -520,14 +521,14 @@ hipError_t launch_bf16(const AttnArgs& a, hipStream_t s) {
         attr = 160 * 1024;
     }
     (void)hipGetLastError();   // drop a stale error of an earlier runtime call
-    hipLaunchKernelGGL(attn_bf16_kernel<HAS_BIAS>, dim3((unsigned)grid), dim3(NT), lds, s, a);
+    hipExtLaunchKernelGGL(attn_bf16_kernel<HAS_BIAS>, dim3((unsigned)grid), dim3(NT), (uint32_t)lds, s, ev0, ev1, 0u, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s) {
-    return a.bias ? launch_bf16<true>(a, s) : launch_bf16<false>(a, s);
+hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+    return a.bias ? launch_bf16<true>(a, s, ev0, ev1) : launch_bf16<false>(a, s, ev0, ev1);
 }
 
 }  // namespace xl

@@ -69,8 +69,11 @@ struct AttnArgs {
 };
 
 // fused attention for bf16 operands and d_head 64 (attn_bf16.hip)
-hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s);
-hipError_t launch_attn(const AttnArgs& a, bool bf16, int dh, hipStream_t s);
+// ev0/ev1 (may be null): events the runtime timestamps at the start and end of
+// the attention kernel itself
+hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
+hipError_t launch_attn(const AttnArgs& a, bool bf16, int dh, hipStream_t s, hipEvent_t ev0 = nullptr,
+                       hipEvent_t ev1 = nullptr);
 
 // FIFO write: copies rows h[b, src0 + t, :] (t < n) to ring row
 // (dst0 + t) % ring_len of batch b.
