@@ -17,8 +17,7 @@
 // for row-major outputs the weight rows feed the MFMA A operand and a lane
 // owns one output row and 4 consecutive output columns; for the transposed
 // value layout a lane owns one output column and 4 consecutive rows.
-#include "xl_common.hpp"
-#include "xl_internal.hpp"
+#include "gemm_common.hpp"
 
 namespace xl {
 namespace {
@@ -30,131 +29,9 @@ constexpr int OPB = 128 * ROWB;                // one operand tile per stage
 constexpr int STAGEB = 2 * OPB;                // A and B
 constexpr int GEMM_LDS = STAGES * STAGEB;      // 64 KiB
 
-struct GemmBatch {
-    GemmArgs p[kMaxGemms];
-    int tile_start[kMaxGemms + 1];
-    int tiles_n[kMaxGemms];
-    int count;
-};
+using namespace gemm;
 
 __device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
-
-template <typename T>
-__device__ __forceinline__ const T* a_row_ptr(const GemmArgs& g, int m) {
-    const T* a0 = (const T*)g.a0;
-    if (g.a_seq == 0) return a0 + (int64_t)m * g.lda;
-    const int b = m / g.a_seq, j = m - b * g.a_seq;
-    if (j < g.a_split) {
-        int pr = g.ring_head + j;
-        if (pr >= g.ring_len) pr -= g.ring_len;
-        return a0 + (int64_t)b * g.a0_bstride + (int64_t)pr * g.lda;
-    }
-    return (const T*)g.a1 + (int64_t)b * g.a1_bstride + (int64_t)(j - g.a_split) * g.lda;
-}
-
-template <typename T>
-__device__ __forceinline__ const T* b_row_ptr(const GemmArgs& g, int n) {
-    return n < g.b_split ? (const T*)g.b0 + (int64_t)n * g.K : (const T*)g.b1 + (int64_t)(n - g.b_split) * g.K;
-}
-
-// Store 4 consecutive outputs: row_out -> (m, n..n+3), else (m..m+3, n).
-template <typename T>
-__device__ __forceinline__ void store4(const GemmArgs& g, int m, int n, const f32x4 v) {
-    constexpr bool BF = Elem<T>::kBf16;
-    int epi = g.epi;
-    void* out = g.out0;
-    if (epi == EPI_KV) {
-        if (n < g.b_split) {
-            epi = EPI_K;
-        } else {
-            epi = EPI_VT;
-            n -= g.b_split;
-            out = g.out1;
-        }
-    }
-    if (epi == EPI_OUT) {
-        if (m >= g.M) return;
-        if (g.out_bf16) {
-            bf16_t* o = (bf16_t*)out + (int64_t)m * g.N + n;
-            if (n + 3 < g.N) {
-                *(u32x2*)o = (u32x2){pack2bf(v[0], v[1]), pack2bf(v[2], v[3])};
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) if (n + e < g.N) o[e] = f2bf(v[e]);
-            }
-        } else {
-            float* o = (float*)out + (int64_t)m * g.N + n;
-            if (n + 3 < g.N) *(f32x4*)o = (f32x4){v[0], v[1], v[2], v[3]};
-            else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) if (n + e < g.N) o[e] = v[e];
-            }
-        }
-        return;
-    }
-    const int ncols = g.epi == EPI_KV ? g.b_split : g.N;
-    if (epi == EPI_VT) {
-        // column n = (h, d); rows m..m+3 = tokens of (possibly) different batches
-        if (n >= ncols) return;
-        const int hh = n / g.dh, d = n - hh * g.dh;
-        const int b = m / g.seq, j = m - b * g.seq;
-        T* o = (T*)out + ((int64_t)(b * g.H + hh) * g.dh + d) * g.ldv + j;
-        if (m + 3 < g.M && j + 3 < g.seq && (j & 3) == 0) {
-            if constexpr (BF) *(u32x2*)o = (u32x2){pack2bf(v[0], v[1]), pack2bf(v[2], v[3])};
-            else *(f32x4*)o = (f32x4){v[0], v[1], v[2], v[3]};
-            return;
-        }
-        #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int mm = m + e;
-            if (mm >= g.M) break;
-            const int bb = mm / g.seq, jj = mm - bb * g.seq;
-            T* oe = (T*)out + ((int64_t)(bb * g.H + hh) * g.dh + d) * g.ldv + jj;
-            if constexpr (BF) *oe = f2bf(v[e]); else *oe = v[e];
-        }
-        return;
-    }
-    // row-major-per-head outputs: (m, n..n+3) with n..n+3 inside one head
-    if (m >= g.M || n >= ncols) return;
-    const int hh = n / g.dh, d = n - hh * g.dh;
-    int64_t off;
-    if (epi == EPI_R) {
-        off = ((int64_t)hh * g.seq + m) * g.dh + d;
-    } else {
-        const int b = m / g.seq, j = m - b * g.seq;
-        off = ((int64_t)(b * g.H + hh) * g.seq + j) * g.dh + d;
-    }
-    if (epi == EPI_Q) {
-        const T* u = (const T*)g.bias0 + hh * g.dh + d;
-        const T* vb = (const T*)g.bias1 + hh * g.dh + d;
-        float a[4], c[4];
-        #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            a[e] = g.scale * (v[e] + Elem<T>::to_f(u[e]));
-            c[e] = g.scale * (v[e] + Elem<T>::to_f(vb[e]));
-        }
-        T* o0 = (T*)out + off;
-        T* o1 = (T*)g.out1 + off;
-        if constexpr (BF) {
-            *(u32x2*)o0 = (u32x2){pack2bf(a[0], a[1]), pack2bf(a[2], a[3])};
-            *(u32x2*)o1 = (u32x2){pack2bf(c[0], c[1]), pack2bf(c[2], c[3])};
-        } else {
-            *(f32x4*)o0 = (f32x4){a[0], a[1], a[2], a[3]};
-            *(f32x4*)o1 = (f32x4){c[0], c[1], c[2], c[3]};
-        }
-        return;
-    }
-    T* o = (T*)out + off;
-    if constexpr (BF) *(u32x2*)o = (u32x2){pack2bf(v[0], v[1]), pack2bf(v[2], v[3])};
-    else *(f32x4*)o = (f32x4){v[0], v[1], v[2], v[3]};
-}
-
-// s_waitcnt with vmcnt = N and the other counters left alone
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 template <typename T, bool kRowOut>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int m0, int n0, char* smem) {
@@ -310,6 +187,7 @@ hipError_t set_lds_attr() {
 }  // namespace
 
 hipError_t launch_gemms(const GemmArgs* g, int count, bool bf16, hipStream_t s) {
+    if (bf16) return launch_gemms_bf16(g, count, s);
     if (count < 1 || count > kMaxGemms) return hipErrorInvalidValue;
     GemmBatch gb;
     gb.count = 0;

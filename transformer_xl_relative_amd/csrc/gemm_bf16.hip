@@ -1,0 +1,413 @@
+// gemm_bf16.hip -- projection GEMMs C = A B^T for bf16 operands on MFMA (the
+// Q, K|V, R and output projections of the relative attention layer;
+// nn.Linear weights [out, in]).
+//
+// Up to four independent projections run as one grid; each workgroup owns a
+// square output tile of one of them: 256 x 256 (eight waves, 4 x 2, each
+// holding 64 x 128 in 2 x 4 accumulator blocks of 32 x 32; two waves per SIMD)
+// or 128 x 128 (four waves, 2 x 2, each 64 x 64) for grids that the large
+// tile would leave too small.
+//
+// K advances 32 elements (64 bytes per operand row) per stage. Operand tiles
+// move from global memory straight into LDS (global_load_lds, 16 bytes per
+// lane), issued three stages ahead through four LDS stages; the four 16-byte
+// chunks of row r are stored XOR-swizzled by (r >> 2) & 3 so that the MFMA
+// operand reads of 16 consecutive rows fall on 16 distinct bank groups. A
+// wave reads the fragments of the next half stage while the MFMAs of the
+// current one run (two register sets), so LDS latency hides behind the
+// matrix work. Rows past
+// the end of A or B are clamped to the last row (their products land in
+// outputs that are never stored).
+//
+// Both operands are K-contiguous, so the MFMA roles are chosen per tile: for
+// row-major outputs the weight rows feed the MFMA A operand and a lane owns
+// one output row and 4 consecutive columns; for the transposed value layout a
+// lane owns one output column and 4 consecutive rows.
+#include "gemm_common.hpp"
+
+#include <type_traits>
+
+namespace xl {
+namespace {
+
+using namespace gemm;
+
+constexpr int ROWB = 64;      // bytes per operand row per stage
+constexpr int NST = 4;        // LDS stages
+constexpr int KST = ROWB / 2; // K elements per stage
+
+// WM x WN waves, each holding WTM x WTN accumulator blocks of 32 x 32
+template <int WM_, int WN_, int WTM_, int WTN_>
+struct Tile {
+    static constexpr int WM = WM_, WN = WN_, WTM = WTM_, WTN = WTN_;
+    static constexpr int NT = 64 * WM * WN;       // threads
+    static constexpr int BT = 32 * WM * WTM;      // workgroup tile edge
+    static_assert(BT == 32 * WN * WTN, "square tiles");
+    static constexpr int OPB = BT * ROWB;         // one operand tile per stage
+    static constexpr int STAGEB = 2 * OPB;
+    static constexpr int LDS = NST * STAGEB;
+    static constexpr int NI = BT * 4 / NT;        // loads per thread per operand per stage
+};
+using Big = Tile<4, 2, 2, 4>;     // 256 x 256, 8 waves
+using Small = Tile<2, 2, 2, 2>;   // 128 x 128, 4 waves
+
+template <typename T, bool kRowOut>
+__device__ __forceinline__ void tile_bf16(const GemmArgs& g, int m0, int n0, char* smem) {
+    constexpr int WTM = T::WTM, WTN = T::WTN, NW = T::NT / 64;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31, hf = lane >> 5;
+    const int wm = wave / T::WN, wn = wave % T::WN;
+
+    // loader: instruction i of this wave fills the 64 chunks (i*NW+wave)*64 + lane
+    // of an operand tile: row r = chunk / 4, stored chunk chunk % 4, which holds
+    // logical chunk (chunk % 4) ^ ((r >> 2) & 3)
+    const bf16_t* asrc[T::NI];
+    const bf16_t* bsrc[T::NI];
+#pragma unroll
+    for (int i = 0; i < T::NI; ++i) {
+        const int chunk = (i * NW + wave) * 64 + lane;
+        const int r = chunk >> 2, lc = (chunk & 3) ^ ((r >> 2) & 3);
+        asrc[i] = a_row_ptr<bf16_t>(g, min(m0 + r, g.M - 1)) + lc * 8;
+        bsrc[i] = b_row_ptr<bf16_t>(g, min(n0 + r, g.N - 1)) + lc * 8;
+    }
+    auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
+        char* base = smem + stage * T::STAGEB;
+#pragma unroll
+        for (int i = 0; i < T::NI; ++i) {
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(asrc[i] + kt * KST),
+                                             (__attribute__((address_space(3))) void*)(base + (i * NW + wave) * 1024),
+                                             16, 0, 0);
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void*)(bsrc[i] + kt * KST),
+                (__attribute__((address_space(3))) void*)(base + T::OPB + (i * NW + wave) * 1024), 16, 0, 0);
+        }
+    };
+
+    // fragment rows of this lane: A rows 32 (wm*WTM + i) + l32, B rows 32 (wn*WTN + j) + l32;
+    // their swizzle (row >> 2) & 3 is (l32 >> 2) & 3
+    const int sw = (l32 >> 2) & 3;
+    const uint32_t lds0 = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)smem;
+    uint32_t aoff[2], boff[2];
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+        aoff[kc] = lds0 + (uint32_t)((32 * wm * WTM + l32) * ROWB + (((2 * kc + hf) ^ sw) << 4));
+        boff[kc] = lds0 + (uint32_t)(T::OPB + (32 * wn * WTN + l32) * ROWB + (((2 * kc + hf) ^ sw) << 4));
+    }
+    // fragments of one half stage (16 K elements): two register sets, one
+    // being multiplied while the other is filled
+    u32x4 fa[2][WTM], fb[2][WTN];
+    auto load_frags = [&](int stage, int kc, u32x4 (&a)[WTM], u32x4 (&b)[WTN]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < WTM; ++i)
+            a[i] = *(const __attribute__((address_space(3))) u32x4*)(size_t)(aoff[kc] + stage * T::STAGEB + i * 32 * ROWB);
+#pragma unroll
+        for (int j = 0; j < WTN; ++j)
+            b[j] = *(const __attribute__((address_space(3))) u32x4*)(size_t)(boff[kc] + stage * T::STAGEB + j * 32 * ROWB);
+    };
+
+    f32x16 acc[WTM][WTN];
+#pragma unroll
+    for (int i = 0; i < WTM; ++i)
+#pragma unroll
+        for (int j = 0; j < WTN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    auto compute = [&](const u32x4 (&a)[WTM], const u32x4 (&b)[WTN]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < WTM; ++i)
+#pragma unroll
+            for (int j = 0; j < WTN; ++j)
+                acc[i][j] = kRowOut ? mfma32(as_bf16x8(b[j]), as_bf16x8(a[i]), acc[i][j])
+                                    : mfma32(as_bf16x8(a[i]), as_bf16x8(b[j]), acc[i][j]);
+    };
+
+    constexpr int PER = 2 * T::NI;      // loads per wave per stage
+    const int nk = g.K / KST;
+#pragma unroll
+    for (int st = 0; st < NST - 1; ++st)
+        if (st < nk) issue(st, st);
+    // stage 0 complete (this wave's loads, then every wave's after the barrier)
+    if (nk > 2) wait_vmcnt<2 * PER>();
+    else if (nk > 1) wait_vmcnt<PER>();
+    else wait_vmcnt<0>();
+    __asm__ __volatile__("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ __volatile__("" ::: "memory");
+    load_frags(0, 0, fa[0], fb[0]);
+
+    // one stage; U = kt % 4 (constant), so LDS stages are constants
+    auto stage_step = [&](auto u_c, int kt) __attribute__((always_inline)) {
+        constexpr int U = decltype(u_c)::value;
+        // stage kt+1 complete: at most the loads of stage kt+2 may be in flight
+        if (kt + 2 < nk) wait_vmcnt<PER>();
+        else wait_vmcnt<0>();
+        // after the barrier every wave's loads of stage kt+1 have landed, and no
+        // wave reads stage kt-1 any more (its fragments were consumed by the
+        // MFMAs of the previous stage), so it can be refilled
+        __asm__ __volatile__("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        __asm__ __volatile__("" ::: "memory");
+        if (kt + 3 < nk) issue(kt + 3, (U + 3) % NST);
+        load_frags(U, 1, fa[1], fb[1]);                   // second half of stage kt
+        compute(fa[0], fb[0]);                           // first half of stage kt
+        if (kt + 1 < nk) load_frags((U + 1) % NST, 0, fa[0], fb[0]);   // first half of stage kt+1
+        compute(fa[1], fb[1]);
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+    for (int kt = 0;;) {
+        stage_step(I0{}, kt);
+        if (++kt >= nk) break;
+        stage_step(I1{}, kt);
+        if (++kt >= nk) break;
+        stage_step(I2{}, kt);
+        if (++kt >= nk) break;
+        stage_step(I3{}, kt);
+        if (++kt >= nk) break;
+    }
+
+    // ---- epilogue (d_head 64: the head and offset of a column n are n >> 6 and
+    // n & 63). Each wave stages 32 rows of its tile at a time in its own LDS
+    // region as bf16 (rows padded by 16 bytes against bank conflicts), then
+    // writes them with 16-byte stores that cover whole row segments.
+    constexpr int TC = 32 * WTN;                  // wave tile columns (N)
+    __builtin_amdgcn_s_waitcnt(0xC07F);           // this wave's fragment reads are done
+    __asm__ __volatile__("" ::: "memory");
+    __builtin_amdgcn_s_barrier();                 // ... and every wave's: the stages can be reused
+    __asm__ __volatile__("" ::: "memory");
+    const int mw = m0 + 32 * wm * WTM, nw = n0 + 32 * wn * WTN;   // first row / column of the wave tile
+    auto lds_st64 = [&](uint32_t adr, float v0, float v1, float v2, float v3) __attribute__((always_inline)) {
+        *(__attribute__((address_space(3))) u32x2*)(size_t)adr = (u32x2){pack2bf(v0, v1), pack2bf(v2, v3)};
+    };
+    auto lds_ld128 = [&](uint32_t adr) __attribute__((always_inline)) {
+        return *(const __attribute__((address_space(3))) u32x4*)(size_t)adr;
+    };
+    if constexpr (kRowOut) {
+        constexpr int PITCH = TC * 2 + 16;         // bytes per staged row
+        constexpr int CPR = TC / 8;                // 16-byte chunks per row
+        constexpr int RPI = 64 / CPR;              // rows per wave instruction in the copy
+        static_assert(NW * 32 * PITCH <= T::LDS, "epilogue staging fits in LDS");
+        const uint32_t wbuf = lds0 + (uint32_t)(wave * 32 * PITCH);
+        int epi = g.epi;
+        int ncols = g.N;
+        if (epi == EPI_KV) { epi = EPI_K; ncols = g.b_split; }   // row-output tiles of K|V are K tiles
+        const int64_t headstride = (int64_t)g.seq * 64;
+        if (epi == EPI_Q) {
+            // q+u and q+v from one fp32 staging of 32 rows x 64 columns at a time;
+            // the fold happens on the fp32 products, rounded once
+            constexpr int QP = 64 * 4 + 16;        // bytes per staged fp32 row
+            static_assert(NW * 32 * QP <= T::LDS, "epilogue staging fits in LDS");
+            const uint32_t qbuf = lds0 + (uint32_t)(wave * 32 * QP);
+            const int qch = lane & 7, qrl = lane >> 3;           // chunk of 8 columns, first row
+            const float sc = g.scale;
+#pragma unroll
+            for (int jh = 0; jh < WTN / 2; ++jh) {
+                const int n = nw + 64 * jh + 8 * qch;
+                const bool nok = n < ncols;
+                u32x4 uu = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
+                if (nok) {
+                    uu = *(const u32x4*)((const bf16_t*)g.bias0 + n);
+                    vv = *(const u32x4*)((const bf16_t*)g.bias1 + n);
+                }
+                float uf[8], vf[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    uf[e] = bf2f((e & 1) ? (uu[e >> 1] >> 16) : (uu[e >> 1] & 0xFFFF));
+                    vf[e] = bf2f((e & 1) ? (vv[e >> 1] >> 16) : (vv[e >> 1] & 0xFFFF));
+                }
+#pragma unroll
+                for (int i = 0; i < WTM; ++i) {
+#pragma unroll
+                    for (int jj2 = 0; jj2 < 2; ++jj2)
+#pragma unroll
+                        for (int gq = 0; gq < 4; ++gq) {
+                            const int j = 2 * jh + jj2;
+                            const int c = 32 * jj2 + 8 * gq + 4 * hf;
+                            *(__attribute__((address_space(3))) f32x4*)(size_t)(qbuf + l32 * QP + c * 4) =
+                                (f32x4){acc[i][j][4 * gq], acc[i][j][4 * gq + 1], acc[i][j][4 * gq + 2],
+                                        acc[i][j][4 * gq + 3]};
+                        }
+                    int m = mw + 32 * i + qrl;
+                    int bb = m / g.seq, jj = m - bb * g.seq;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const uint32_t adr = qbuf + (qrl + 8 * k) * QP + qch * 32;
+                        const f32x4 x0 = *(const __attribute__((address_space(3))) f32x4*)(size_t)adr;
+                        const f32x4 x1 = *(const __attribute__((address_space(3))) f32x4*)(size_t)(adr + 16);
+                        if (m < g.M && nok) {
+                            const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+                            u32x4 qa, qb;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                qa[e] = pack2bf(sc * (x[2 * e] + uf[2 * e]), sc * (x[2 * e + 1] + uf[2 * e + 1]));
+                                qb[e] = pack2bf(sc * (x[2 * e] + vf[2 * e]), sc * (x[2 * e + 1] + vf[2 * e + 1]));
+                            }
+                            const int64_t off = ((int64_t)bb * g.H * g.seq + jj) * 64 + (int64_t)(n >> 6) * headstride + (n & 63);
+                            *(u32x4*)((bf16_t*)g.out0 + off) = qa;
+                            *(u32x4*)((bf16_t*)g.out1 + off) = qb;
+                        }
+                        m += 8;
+                        jj += 8;
+                        while (jj >= g.seq) { jj -= g.seq; ++bb; }
+                    }
+                }
+            }
+            return;
+        }
+        const int ch = lane % CPR, rl = lane / CPR;
+        const int n = nw + 8 * ch;
+        bf16_t* out = (bf16_t*)g.out0;
+#pragma unroll
+        for (int i = 0; i < WTM; ++i) {
+#pragma unroll
+            for (int j = 0; j < WTN; ++j)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    const int c = 32 * j + 8 * gq + 4 * hf;
+                    lds_st64(wbuf + l32 * PITCH + c * 2, acc[i][j][4 * gq], acc[i][j][4 * gq + 1],
+                             acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3]);
+                }
+            // copy out rows 32 i .. 32 i + 31: lane -> chunk ch of rows rl + RPI k
+            int m = mw + 32 * i + rl;
+            int bb = 0, jj = 0;
+            if (epi == EPI_K) { bb = m / g.seq; jj = m - bb * g.seq; }
+#pragma unroll
+            for (int k = 0; k < 32 / RPI; ++k) {
+                const u32x4 w = lds_ld128(wbuf + (rl + RPI * k) * PITCH + ch * 16);
+                if (m < g.M && n < ncols) {
+                    if (epi == EPI_OUT) {
+                        if (g.out_bf16) {
+                            *(u32x4*)((bf16_t*)g.out0 + (int64_t)m * g.N + n) = w;
+                        } else {
+                            float* o = (float*)g.out0 + (int64_t)m * g.N + n;
+                            *(f32x4*)o = (f32x4){bf2f(w[0] & 0xFFFF), bf2f(w[0] >> 16), bf2f(w[1] & 0xFFFF),
+                                                 bf2f(w[1] >> 16)};
+                            *(f32x4*)(o + 4) = (f32x4){bf2f(w[2] & 0xFFFF), bf2f(w[2] >> 16), bf2f(w[3] & 0xFFFF),
+                                                       bf2f(w[3] >> 16)};
+                        }
+                    } else {
+                        const int64_t rowoff = epi == EPI_R ? (int64_t)m * 64 : ((int64_t)bb * g.H * g.seq + jj) * 64;
+                        *(u32x4*)(out + rowoff + (int64_t)(n >> 6) * headstride + (n & 63)) = w;
+                    }
+                }
+                m += RPI;
+                if (epi == EPI_K) {
+                    jj += RPI;
+                    while (jj >= g.seq) { jj -= g.seq; ++bb; }
+                }
+            }
+        }
+    } else {
+        // transposed values (V^T [B, H, 64, ldv]); column c is head c >> 6,
+        // offset c & 63. Staging: column c of the tile holds 32 tokens.
+        constexpr int PITCH = 32 * 2 + 16;         // bytes per staged column
+        constexpr int CPI = 16;                    // columns per wave instruction in the copy (4 chunks each)
+        static_assert(NW * TC * PITCH <= T::LDS, "epilogue staging fits in LDS");
+        const uint32_t wbuf = lds0 + (uint32_t)(wave * TC * PITCH);
+        bf16_t* out = (bf16_t*)g.out0;
+        int c0 = nw, ncols = g.N;
+        if (g.epi == EPI_KV) { out = (bf16_t*)g.out1; c0 = nw - g.b_split; ncols = g.N - g.b_split; }
+        const int t = lane & 3, cl = lane >> 2;
+#pragma unroll
+        for (int i = 0; i < WTM; ++i) {
+#pragma unroll
+            for (int j = 0; j < WTN; ++j)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq)
+                    lds_st64(wbuf + (32 * j + l32) * PITCH + (8 * gq + 4 * hf) * 2, acc[i][j][4 * gq],
+                             acc[i][j][4 * gq + 1], acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3]);
+            // copy out: lane -> token chunk t (8 tokens) of columns cl + CPI k
+            const int m = mw + 32 * i + 8 * t;     // first of the chunk's 8 tokens
+            const int bb = m / g.seq, jj = m - bb * g.seq;
+            const bool whole = m + 7 < g.M && jj + 7 < g.seq && (jj & 7) == 0 && (g.ldv & 7) == 0;
+#pragma unroll
+            for (int k = 0; k < TC / CPI; ++k) {
+                const int c = cl + CPI * k;
+                const int cg = c0 + c;
+                const u32x4 w = lds_ld128(wbuf + c * PITCH + t * 16);
+                if (cg >= ncols || m >= g.M) continue;
+                if (whole) {
+                    *(u32x4*)(out + ((int64_t)bb * g.H * 64 + cg) * g.ldv + jj) = w;
+                } else {
+                    int b2 = bb, j2 = jj;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        if (m + e < g.M) {
+                            const uint32_t wd = w[e >> 1];
+                            out[((int64_t)b2 * g.H * 64 + cg) * g.ldv + j2] = (bf16_t)((e & 1) ? (wd >> 16) : (wd & 0xFFFF));
+                        }
+                        if (++j2 == g.seq) { j2 = 0; ++b2; }
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(T::NT, 1) gemm_bf16_kernel(GemmBatch gb) {
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+    const int tile = blockIdx.x;
+    // the problem of this tile: uniform selects on constant indices
+    int k = 0;
+    if (gb.count > 1 && tile >= gb.tile_start[1]) k = 1;
+    if (gb.count > 2 && tile >= gb.tile_start[2]) k = 2;
+    if (gb.count > 3 && tile >= gb.tile_start[3]) k = 3;
+    GemmArgs g = gb.p[0];
+    int start = gb.tile_start[0], tiles_n = gb.tiles_n[0];
+    if (k == 1) { g = gb.p[1]; start = gb.tile_start[1]; tiles_n = gb.tiles_n[1]; }
+    if (k == 2) { g = gb.p[2]; start = gb.tile_start[2]; tiles_n = gb.tiles_n[2]; }
+    if (k == 3) { g = gb.p[3]; start = gb.tile_start[3]; tiles_n = gb.tiles_n[3]; }
+    const int t = tile - start;
+    const int tm = t / tiles_n, tn = t - tm * tiles_n;
+    const int m0 = tm * T::BT, n0 = tn * T::BT;
+    const bool col_out = g.epi == EPI_VT || (g.epi == EPI_KV && n0 >= g.b_split);
+    if (col_out) tile_bf16<T, false>(g, m0, n0, smem);
+    else tile_bf16<T, true>(g, m0, n0, smem);
+}
+
+template <typename T>
+hipError_t launch_tiles(const GemmArgs* g, int count, hipStream_t s) {
+    GemmBatch gb;
+    gb.count = 0;
+    int tiles = 0;
+    for (int i = 0; i < count; ++i) {
+        if (g[i].M <= 0 || g[i].N <= 0) continue;
+        const int k = gb.count++;
+        gb.p[k] = g[i];
+        gb.tiles_n[k] = (g[i].N + T::BT - 1) / T::BT;
+        gb.tile_start[k] = tiles;
+        tiles += gb.tiles_n[k] * ((g[i].M + T::BT - 1) / T::BT);
+    }
+    gb.tile_start[gb.count] = tiles;
+    if (tiles == 0) return hipSuccess;
+    static bool attr = false;
+    if (!attr) {
+        hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<T>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS);
+        if (e != hipSuccess) return e;
+        attr = true;
+    }
+    (void)hipGetLastError();   // drop a stale error of an earlier runtime call
+    hipLaunchKernelGGL(gemm_bf16_kernel<T>, dim3(tiles), dim3(T::NT), T::LDS, s, gb);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// Large tiles when they still give most CUs a tile, else 128 x 128 tiles.
+hipError_t launch_gemms_bf16(const GemmArgs* g, int count, hipStream_t s) {
+    if (count < 1 || count > kMaxGemms) return hipErrorInvalidValue;
+    // the epilogues address heads with d_head 64 (the only bf16 head size)
+    for (int i = 0; i < count; ++i)
+        if (g[i].epi != EPI_OUT && g[i].dh != 64) return hipErrorInvalidValue;
+    int big = 0;
+    for (int i = 0; i < count; ++i)
+        if (g[i].M > 0 && g[i].N > 0) big += ((g[i].M + 255) / 256) * ((g[i].N + 255) / 256);
+    return big >= 192 ? launch_tiles<Big>(g, count, s) : launch_tiles<Small>(g, count, s);
+}
+
+}  // namespace xl

@@ -52,6 +52,8 @@ constexpr int kMaxGemms = 4;
 // Launch up to kMaxGemms independent projections as one grid (their tiles
 // share the machine). K of every problem must be a multiple of 64 bytes.
 hipError_t launch_gemms(const GemmArgs* g, int count, bool bf16, hipStream_t s);
+// the bf16 kernels (gemm_bf16.hip); launch_gemms forwards bf16 problems here
+hipError_t launch_gemms_bf16(const GemmArgs* g, int count, hipStream_t s);
 inline hipError_t launch_gemm(const GemmArgs& g, bool bf16, hipStream_t s) { return launch_gemms(&g, 1, bf16, s); }
 
 struct AttnArgs {
