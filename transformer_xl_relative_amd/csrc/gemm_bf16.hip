@@ -358,11 +358,19 @@ __global__ void __launch_bounds__(T::NT, 1) gemm_bf16_kernel(GemmBatch gb) {
     if (gb.count > 3 && tile >= gb.tile_start[3]) k = 3;
     GemmArgs g = gb.p[0];
     int start = gb.tile_start[0], tiles_n = gb.tiles_n[0];
-    if (k == 1) { g = gb.p[1]; start = gb.tile_start[1]; tiles_n = gb.tiles_n[1]; }
-    if (k == 2) { g = gb.p[2]; start = gb.tile_start[2]; tiles_n = gb.tiles_n[2]; }
-    if (k == 3) { g = gb.p[3]; start = gb.tile_start[3]; tiles_n = gb.tiles_n[3]; }
+    int end = gb.tile_start[1], real = gb.tiles_real[0];
+    if (k == 1) { g = gb.p[1]; start = gb.tile_start[1]; tiles_n = gb.tiles_n[1]; end = gb.tile_start[2]; real = gb.tiles_real[1]; }
+    if (k == 2) { g = gb.p[2]; start = gb.tile_start[2]; tiles_n = gb.tiles_n[2]; end = gb.tile_start[3]; real = gb.tiles_real[2]; }
+    if (k == 3) { g = gb.p[3]; start = gb.tile_start[3]; tiles_n = gb.tiles_n[3]; end = gb.tile_start[4]; real = gb.tiles_real[3]; }
+    // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs
+    // (workgroup w runs on XCD w % 8) and every problem starts at a multiple
+    // of 8, so XCD x takes the x-th eighth of the problem's tiles in row-major
+    // order: tiles that share A row panels (and neighbouring B panels) share
+    // that XCD's L2. Padding workgroups exit at once.
     const int t = tile - start;
-    const int tm = t / tiles_n, tn = t - tm * tiles_n;
+    const int tr = (t & 7) * ((end - start) >> 3) + (t >> 3);
+    if (tr >= real) return;
+    const int tm = tr / tiles_n, tn = tr - tm * tiles_n;
     const int m0 = tm * T::BT, n0 = tn * T::BT;
     const bool col_out = g.epi == EPI_VT || (g.epi == EPI_KV && n0 >= g.b_split);
     if (col_out) tile_bf16<T, false>(g, m0, n0, smem);
@@ -379,8 +387,9 @@ hipError_t launch_tiles(const GemmArgs* g, int count, hipStream_t s) {
         const int k = gb.count++;
         gb.p[k] = g[i];
         gb.tiles_n[k] = (g[i].N + T::BT - 1) / T::BT;
+        gb.tiles_real[k] = gb.tiles_n[k] * ((g[i].M + T::BT - 1) / T::BT);
         gb.tile_start[k] = tiles;
-        tiles += gb.tiles_n[k] * ((g[i].M + T::BT - 1) / T::BT);
+        tiles += (gb.tiles_real[k] + 7) / 8 * 8;     // each problem's range is a multiple of 8
     }
     gb.tile_start[gb.count] = tiles;
     if (tiles == 0) return hipSuccess;

@@ -12,6 +12,7 @@ struct GemmBatch {
     GemmArgs p[kMaxGemms];
     int tile_start[kMaxGemms + 1];
     int tiles_n[kMaxGemms];
+    int tiles_real[kMaxGemms];   // tiles of a problem (its range in the grid may be padded)
     int count;
 };
 
