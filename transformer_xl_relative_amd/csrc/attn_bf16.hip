@@ -486,11 +486,15 @@ __global__ void __launch_bounds__(NT, 2) attn_bf16_kernel(AttnArgs a) {
         if (++s >= nsteps) break;
     }
 
-    // ---- epilogue: o / l, heads concatenated
+    // ---- epilogue: o / l, heads concatenated. The wave stages its 32 x 64
+    // outputs in its own ring (padded rows of 64 bf16), then writes each query's
+    // 128-byte row segment with 16-byte stores.
     const float l_tot = halves_sum(l_run);
-    if (!qok || wsteps == 0) return;
+    if (wsteps == 0) return;
     const float inv = 1.f / l_tot;
-    bf16_t* orow = (bf16_t*)a.out + ((int64_t)b * a.qlen + iq) * ((int64_t)a.H * DH) + (int64_t)h * DH;
+    constexpr int OP = DH * 2 + 16;                // staged row: 64 bf16 + padding
+    static_assert(WQ * OP <= WQ * RROW, "staging fits in the ring");
+    const uint32_t obuf = lds0 + OFF_RING + (uint32_t)(wave * WQ * RROW);
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -498,8 +502,18 @@ __global__ void __launch_bounds__(NT, 2) attn_bf16_kernel(AttnArgs a) {
             const int d = 32 * t + 8 * gq + 4 * hf;
             const float v0 = o[t][4 * gq] * inv, v1 = o[t][4 * gq + 1] * inv;
             const float v2 = o[t][4 * gq + 2] * inv, v3 = o[t][4 * gq + 3] * inv;
-            *(u32x2*)(orow + d) = (u32x2){pack2bf(v0, v1), pack2bf(v2, v3)};
+            *(__attribute__((address_space(3))) u32x2*)(size_t)(obuf + l32 * OP + d * 2) =
+                (u32x2){pack2bf(v0, v1), pack2bf(v2, v3)};
         }
+    // lane -> 16-byte chunk (lane % 8) of queries lane / 8 + 8 k
+    const int ch = lane & 7;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int qi = (lane >> 3) + 8 * k;
+        const u32x4 w = *(const __attribute__((address_space(3))) u32x4*)(size_t)(obuf + qi * OP + ch * 16);
+        if (iw + qi < a.qlen)
+            *(u32x4*)((bf16_t*)a.out + ((int64_t)b * a.qlen + iw + qi) * ((int64_t)a.H * DH) + (int64_t)h * DH + ch * 8) = w;
+    }
 }
 
 template <bool HAS_BIAS>
