@@ -164,6 +164,19 @@ def test_edge_cases(T, label, base, qlen, mlen, clamp, bias):
     gu.compare(label, gu.host64(L.out), ref, dtype=w.dtype)
 
 
+@pytest.mark.parametrize("d_model,n_head", [(32, 1), (96, 2), (160, 3), (544, 8)])
+def test_layer_model_width(T, d_model, n_head):
+    # d_model a multiple of 32 but not of 64: the projections end on a K stage
+    # of half width; also output widths that leave ragged column tiles
+    import dataclasses
+    w = dataclasses.replace(W["base_bf16"], d_model=d_model, n_head=n_head, seed=d_model + n_head)
+    t = xl_inputs.layer_inputs(w, batch=2, qlen=70, mlen=45)
+    L = _run_layer(T, w, t, batch=2, qlen=70, mlen=45)
+    ref = gu.oracle_layer(t, w, t["h"].f64, t["mem"].f64)
+    gu.compare(f"d_model {d_model}", gu.host64(L.out), ref, dtype=w.dtype)
+    _check_intermediates(T, L, w, t, 2, 70, 45)
+
+
 def test_split_invariance_gpu(T):
     # the output of a position does not depend on where the memory/segment split falls
     import dataclasses

@@ -8,12 +8,12 @@
 // or 128 x 128 (four waves, 2 x 2, each 64 x 64) for grids that the large
 // tile would leave too small.
 //
-// K advances 32 elements (64 bytes per operand row) per stage. Operand tiles
-// move from global memory straight into LDS (global_load_lds, 16 bytes per
-// lane), issued three stages ahead through four LDS stages; the four 16-byte
-// chunks of row r are stored XOR-swizzled by (r >> 2) & 3 so that the MFMA
-// operand reads of 16 consecutive rows fall on 16 distinct bank groups. A
-// wave reads the fragments of the next half stage while the MFMAs of the
+// K advances 64 elements (128 bytes, whole cache lines, per operand row) per
+// stage. Operand tiles move from global memory straight into LDS
+// (global_load_lds, 16 bytes per lane) one or two stages ahead; the eight
+// 16-byte chunks of row r are stored XOR-swizzled by (r >> 1) & 7 so that the
+// MFMA operand reads of 16 consecutive rows fall on 16 distinct bank groups.
+// A wave reads the fragments of the next k-step while the MFMAs of the
 // current one run (two register sets), so LDS latency hides behind the
 // matrix work. Rows past
 // the end of A or B are clamped to the last row (their products land in
@@ -32,24 +32,24 @@ namespace {
 
 using namespace gemm;
 
-constexpr int ROWB = 64;      // bytes per operand row per stage
-constexpr int NST = 4;        // LDS stages
+constexpr int ROWB = 128;     // bytes per operand row per stage (64 K elements): whole cache lines
 constexpr int KST = ROWB / 2; // K elements per stage
+constexpr int KC = KST / 16;  // MFMA k-steps per stage
 
-// WM x WN waves, each holding WTM x WTN accumulator blocks of 32 x 32
-template <int WM_, int WN_, int WTM_, int WTN_>
+// WM x WN waves, each holding WTM x WTN accumulator blocks of 32 x 32; NST LDS stages
+template <int WM_, int WN_, int WTM_, int WTN_, int NST_>
 struct Tile {
-    static constexpr int WM = WM_, WN = WN_, WTM = WTM_, WTN = WTN_;
+    static constexpr int WM = WM_, WN = WN_, WTM = WTM_, WTN = WTN_, NST = NST_;
     static constexpr int NT = 64 * WM * WN;       // threads
     static constexpr int BT = 32 * WM * WTM;      // workgroup tile edge
     static_assert(BT == 32 * WN * WTN, "square tiles");
     static constexpr int OPB = BT * ROWB;         // one operand tile per stage
     static constexpr int STAGEB = 2 * OPB;
     static constexpr int LDS = NST * STAGEB;
-    static constexpr int NI = BT * 4 / NT;        // loads per thread per operand per stage
+    static constexpr int NI = BT * (ROWB / 16) / NT;   // loads per thread per operand per stage
 };
-using Big = Tile<4, 2, 2, 4>;     // 256 x 256, 8 waves
-using Small = Tile<2, 2, 2, 2>;   // 128 x 128, 4 waves
+using Big = Tile<4, 2, 2, 4, 2>;     // 256 x 256, 8 waves, 2 stages (128 KiB)
+using Small = Tile<2, 2, 2, 2, 3>;   // 128 x 128, 4 waves, 3 stages (96 KiB)
 
 template <typename T, bool kRowOut>
 __device__ __forceinline__ void tile_bf16(const GemmArgs& g, int m0, int n0, char* smem) {
@@ -60,42 +60,52 @@ __device__ __forceinline__ void tile_bf16(const GemmArgs& g, int m0, int n0, cha
     const int wm = wave / T::WN, wn = wave % T::WN;
 
     // loader: instruction i of this wave fills the 64 chunks (i*NW+wave)*64 + lane
-    // of an operand tile: row r = chunk / 4, stored chunk chunk % 4, which holds
-    // logical chunk (chunk % 4) ^ ((r >> 2) & 3)
+    // of an operand tile: row r = chunk / 8, stored chunk chunk % 8, which holds
+    // logical chunk (chunk % 8) ^ ((r >> 1) & 7)
+    // A K of 32 (mod 64) leaves a last stage of half width: there the lanes of
+    // logical chunks 4..7 load chunk lc - 4 again (in bounds), and the B
+    // fragments of those columns are zeroed before they are multiplied, so every
+    // stage issues the same load instructions
+    const int nk = (g.K + KST - 1) / KST;
+    const bool khalf = (g.K % KST) != 0;
     const bf16_t* asrc[T::NI];
     const bf16_t* bsrc[T::NI];
+    int back[T::NI];
 #pragma unroll
     for (int i = 0; i < T::NI; ++i) {
         const int chunk = (i * NW + wave) * 64 + lane;
-        const int r = chunk >> 2, lc = (chunk & 3) ^ ((r >> 2) & 3);
+        const int r = chunk >> 3, lc = (chunk & 7) ^ ((r >> 1) & 7);
         asrc[i] = a_row_ptr<bf16_t>(g, min(m0 + r, g.M - 1)) + lc * 8;
         bsrc[i] = b_row_ptr<bf16_t>(g, min(n0 + r, g.N - 1)) + lc * 8;
+        back[i] = lc >= 4 ? KST / 2 : 0;
     }
     auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
         char* base = smem + stage * T::STAGEB;
+        const bool half = khalf && kt == nk - 1;
 #pragma unroll
         for (int i = 0; i < T::NI; ++i) {
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(asrc[i] + kt * KST),
+            const int ko = kt * KST - (half ? back[i] : 0);
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(asrc[i] + ko),
                                              (__attribute__((address_space(3))) void*)(base + (i * NW + wave) * 1024),
                                              16, 0, 0);
             __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void*)(bsrc[i] + kt * KST),
+                (const __attribute__((address_space(1))) void*)(bsrc[i] + ko),
                 (__attribute__((address_space(3))) void*)(base + T::OPB + (i * NW + wave) * 1024), 16, 0, 0);
         }
     };
 
     // fragment rows of this lane: A rows 32 (wm*WTM + i) + l32, B rows 32 (wn*WTN + j) + l32;
-    // their swizzle (row >> 2) & 3 is (l32 >> 2) & 3
-    const int sw = (l32 >> 2) & 3;
+    // their swizzle (row >> 1) & 7 is (l32 >> 1) & 7
+    const int sw = (l32 >> 1) & 7;
     const uint32_t lds0 = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)smem;
-    uint32_t aoff[2], boff[2];
+    uint32_t aoff[KC], boff[KC];
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
+    for (int kc = 0; kc < KC; ++kc) {
         aoff[kc] = lds0 + (uint32_t)((32 * wm * WTM + l32) * ROWB + (((2 * kc + hf) ^ sw) << 4));
         boff[kc] = lds0 + (uint32_t)(T::OPB + (32 * wn * WTN + l32) * ROWB + (((2 * kc + hf) ^ sw) << 4));
     }
-    // fragments of one half stage (16 K elements): two register sets, one
-    // being multiplied while the other is filled
+    // fragments of one k-step (16 K elements): two register sets, one being
+    // multiplied while the other is filled
     u32x4 fa[2][WTM], fb[2][WTN];
     auto load_frags = [&](int stage, int kc, u32x4 (&a)[WTM], u32x4 (&b)[WTN]) __attribute__((always_inline)) {
 #pragma unroll
@@ -122,51 +132,57 @@ __device__ __forceinline__ void tile_bf16(const GemmArgs& g, int m0, int n0, cha
                                     : mfma32(as_bf16x8(a[i]), as_bf16x8(b[j]), acc[i][j]);
     };
 
-    constexpr int PER = 2 * T::NI;      // loads per wave per stage
-    const int nk = g.K / KST;
+    constexpr int NST = T::NST;
+    constexpr int PER = 2 * T::NI;      // loads per thread per stage
 #pragma unroll
     for (int st = 0; st < NST - 1; ++st)
         if (st < nk) issue(st, st);
-    // stage 0 complete (this wave's loads, then every wave's after the barrier)
-    if (nk > 2) wait_vmcnt<2 * PER>();
-    else if (nk > 1) wait_vmcnt<PER>();
-    else wait_vmcnt<0>();
-    __asm__ __volatile__("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    __asm__ __volatile__("" ::: "memory");
-    load_frags(0, 0, fa[0], fb[0]);
 
-    // one stage; U = kt % 4 (constant), so LDS stages are constants
+    // one stage; U = kt % NST (constant), so LDS stages are constants
     auto stage_step = [&](auto u_c, int kt) __attribute__((always_inline)) {
         constexpr int U = decltype(u_c)::value;
-        // stage kt+1 complete: at most the loads of stage kt+2 may be in flight
-        if (kt + 2 < nk) wait_vmcnt<PER>();
-        else wait_vmcnt<0>();
-        // after the barrier every wave's loads of stage kt+1 have landed, and no
-        // wave reads stage kt-1 any more (its fragments were consumed by the
-        // MFMAs of the previous stage), so it can be refilled
+        // stage kt complete (this wave's loads): later stages already issued may
+        // still be in flight
+        if constexpr (NST == 3) {
+            if (kt + 1 < nk) wait_vmcnt<PER>();
+            else wait_vmcnt<0>();
+        } else {
+            static_assert(NST == 2, "stage count");
+            wait_vmcnt<0>();
+        }
+        // after the barrier every wave's loads of stage kt have landed, and no
+        // wave reads stage kt-1 any more, so its slot can be refilled
         __asm__ __volatile__("" ::: "memory");
         __builtin_amdgcn_s_barrier();
         __asm__ __volatile__("" ::: "memory");
-        if (kt + 3 < nk) issue(kt + 3, (U + 3) % NST);
-        load_frags(U, 1, fa[1], fb[1]);                   // second half of stage kt
-        compute(fa[0], fb[0]);                           // first half of stage kt
-        if (kt + 1 < nk) load_frags((U + 1) % NST, 0, fa[0], fb[0]);   // first half of stage kt+1
-        compute(fa[1], fb[1]);
+        if (kt + NST - 1 < nk) issue(kt + NST - 1, (U + NST - 1) % NST);
+        // in a half-width last stage the B fragments of k-steps KC/2.. are zeroed
+        const bool half = khalf && kt == nk - 1;
+        load_frags(U, 0, fa[0], fb[0]);
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+            if (kc + 1 < KC) {
+                load_frags(U, kc + 1, fa[(kc + 1) & 1], fb[(kc + 1) & 1]);
+                if (kc + 1 >= KC / 2 && half) {
+#pragma unroll
+                    for (int j = 0; j < WTN; ++j) fb[(kc + 1) & 1][j] = u32x4{0u, 0u, 0u, 0u};
+                }
+            }
+            compute(fa[kc & 1], fb[kc & 1]);
+        }
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
-    using I3 = std::integral_constant<int, 3>;
     for (int kt = 0;;) {
         stage_step(I0{}, kt);
         if (++kt >= nk) break;
         stage_step(I1{}, kt);
         if (++kt >= nk) break;
-        stage_step(I2{}, kt);
-        if (++kt >= nk) break;
-        stage_step(I3{}, kt);
-        if (++kt >= nk) break;
+        if constexpr (NST == 3) {
+            stage_step(I2{}, kt);
+            if (++kt >= nk) break;
+        }
     }
 
     // ---- epilogue (d_head 64: the head and offset of a column n are n >> 6 and
