@@ -8,12 +8,19 @@ are resident in HBM before the timed region starts. The memory FIFO is full,
 so every step attends over 384 memory rows + 384 segment rows.
 
 Prints one JSON line: the layer's algorithmic TFLOP/s (value), the fused
-attention kernel's roofline against the bf16 MFMA peak (kernel time from HIP
-events recorded around its launch in every timed step), and the CPU oracle
-timed on a bounded sample of the same workload.
+attention kernel's roofline (kernel time from HIP events that the runtime
+timestamps at the kernel's own start and end, in every timed step), and the
+CPU oracle timed on a bounded sample of the same workload. The roofline bound
+is the one the kernel's arithmetic intensity (algorithmic FLOPs over minimum
+HBM bytes) selects: HBM below the ridge point 2500 TFLOP/s / 8 TB/s, MFMA
+above it; the fraction of the bf16 MFMA peak is reported beside it.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
                   [--copy-calib-mib M]        # also run a plain device copy of M MiB (counter calibration)
+  python bench.py --core base_bf16,large_bf16,...  [--launches N]
+                  # the fused attention alone (xl_rel_attn_core) per workload, warm and
+                  # cold (1 GiB written between launches to evict the caches): one JSON
+                  # line per workload with the median, p10 and p90 kernel times
   python bench.py --summarize DIR [--copy-calib-mib M]   # markdown summary of rocprofv3 output under DIR
 
 HBM traffic of the attention kernel comes from two rocprofv3 --pmc passes
@@ -41,8 +48,9 @@ HBM_PEAK_GBS = 8000.0
 
 # Sources that make up the fused attention kernel; the traffic record below is
 # valid only for this exact text.
-ATTN_SOURCES = ("transformer_xl_relative_amd/csrc/attn.hip", "transformer_xl_relative_amd/csrc/xl_common.hpp",
-                "transformer_xl_relative_amd/csrc/xl_internal.hpp", "transformer_xl_relative_amd/build.py")
+ATTN_SOURCES = ("transformer_xl_relative_amd/csrc/attn_bf16.hip", "transformer_xl_relative_amd/csrc/attn.hip",
+                "transformer_xl_relative_amd/csrc/xl_common.hpp", "transformer_xl_relative_amd/csrc/xl_internal.hpp",
+                "transformer_xl_relative_amd/build.py")
 
 # HBM bytes per launch of the fused attention kernel (calibrated FETCH_SIZE and
 # WRITE_SIZE, see profiles/attn_kernel_<workload>_pmc_traffic.md).
@@ -72,12 +80,29 @@ def layer_flops(w, mlen):
 
 
 def attn_min_bytes(w, mlen):
-    """Algorithmic HBM bytes of the fused attention: qu, qv, k, v, r read once, output written."""
+    """Algorithmic (minimum) HBM bytes of the fused attention: the queries, keys,
+    values and projected table r read once, the output written once. This
+    implementation reads the queries twice (s(q+u) and s(q+v) are stored
+    separately), which the measured traffic shows."""
     B, H, dh, q = w.batch, w.n_head, w.d_head, w.qlen
     klen = q + mlen
     n_rel = klen if w.clamp_len < 0 else min(klen, w.clamp_len + 1)
     es = 2
-    return es * (2 * B * H * q * dh + 2 * B * H * klen * dh + H * n_rel * dh + B * q * H * dh)
+    return es * (B * H * q * dh + 2 * B * H * klen * dh + H * n_rel * dh + B * q * H * dh)
+
+
+def roofline(flops, nbytes, seconds):
+    """Bound, achieved rate and fraction for one kernel time."""
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    tf = flops / seconds / 1e12
+    gbs = nbytes / seconds / 1e9
+    if flops / nbytes < ridge:
+        return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "mfma_tflops": round(tf, 3),
+                "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+    return {"bound": "mfma", "achieved": round(tf, 3), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "hbm_gbs": round(gbs, 1),
+            "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
 
 
 def cpu_baseline(w, t, min_seconds=10.0):
@@ -113,6 +138,8 @@ def main():
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="before warm-up, run a plain device-to-device copy of this many MiB three times")
     ap.add_argument("--summarize", metavar="DIR", help="print a summary of the rocprofv3 databases under DIR")
+    ap.add_argument("--core", metavar="WORKLOADS", help="comma-separated workloads: time the fused attention alone")
+    ap.add_argument("--launches", type=int, default=100, help="timed launches per --core measurement")
     args = ap.parse_args()
     if args.summarize:
         summarize(args.summarize, args.copy_calib_mib)
@@ -130,6 +157,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.core:
+        core_bench(args.core.split(","), args.launches, args.warmup)
+        return
     w = xl_inputs.WORKLOADS[args.workload]
     if w.dtype != "bf16":
         raise SystemExit("bench.py measures the bf16 workloads")
@@ -185,7 +215,6 @@ def main():
 
     flops, attn_flops = layer_flops(w, w.mlen)
     value = flops / (ms_per_step * 1e-3) / 1e12
-    achieved = attn_flops / (core_avg_ms * 1e-3) / 1e12
     rec = TRAFFIC.get(w.name)
     traffic = rec["bytes"] if rec is not None and rec["sha256"] == attn_sources_sha() else None
     res = {
@@ -206,11 +235,10 @@ def main():
                                f"{w.n_head} heads x {w.d_head}, qlen {w.qlen}, mlen {w.mlen}, causal",
                    "batch": w.batch, "qlen": w.qlen, "mlen": w.mlen, "d_model": D, "n_head": w.n_head,
                    "d_head": w.d_head, "clamp_len": w.clamp_len, "bias_clamp": w.bias_clamp},
-        "roofline": {"kernel": "attn_kernel (fused relative attention)", "bound": "mfma",
-                     "achieved": round(achieved, 3), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
-                     "algorithmic_flops": attn_flops, "avg_kernel_us": round(core_avg_ms * 1e3, 3),
-                     "algorithmic_bytes": attn_min_bytes(w, w.mlen)},
+        "roofline": {"kernel": "attn_bf16_kernel (fused relative attention)",
+                     **roofline(attn_flops, attn_min_bytes(w, w.mlen), core_avg_ms * 1e-3), "traffic": traffic,
+                     "algorithmic_flops": attn_flops, "algorithmic_bytes": attn_min_bytes(w, w.mlen),
+                     "avg_kernel_us": round(core_avg_ms * 1e3, 3)},
         "layer_flops_per_step": flops,
         "wall_s_timed_region": round(wall, 4),
     }
@@ -218,6 +246,66 @@ def main():
         res["cpu_baseline"] = cpu_baseline(w, t)
         res["gpu_over_cpu"] = round(value / res["cpu_baseline"]["value"], 1)
     print(json.dumps(res), flush=True)
+
+
+def core_bench(names, launches, warmup):
+    """The fused attention alone on each workload's projected operands (taken
+    from the workspace of one layer forward): per-launch kernel times from
+    runtime-timestamped HIP events, warm (operands as the projections left
+    them) and cold (1 GiB written between launches, more than the 256 MB
+    last-level cache holds)."""
+    import numpy as np
+    import torch
+    import transformer_xl_relative_amd as xl
+    import xl_inputs
+    from tests import gpu_util as gu
+
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    for name in names:
+        w = xl_inputs.WORKLOADS[name]
+        if w.dtype != "bf16":
+            raise SystemExit("--core measures the bf16 workloads")
+        if w.segments > 1:
+            w = dataclass_replace(w, segments=1)   # one steady-state segment (full memory)
+        t = xl_inputs.layer_inputs(w)
+        L = gu.Layer(w, t, batch=w.batch, qlen=w.qlen, mlen=w.mlen, out_f32=False)
+        xl.xl_rel_attn_fwd(L.desc, L.weights, gu.dev(t["h"]), gu.dev(t["mem"]), L.out, L.ws)
+        lay = L.layout
+        B, H, dh, q = w.batch, w.n_head, w.d_head, w.qlen
+        qu, qv = L.ws_view(lay.qu, (B, H, q, dh)), L.ws_view(lay.qv, (B, H, q, dh))
+        k, vt = L.ws_view(lay.k, (B, H, lay.klen, dh)), L.ws_view(lay.vt, (B, H, dh, lay.ldv))
+        r = L.ws_view(lay.r, (H, lay.n_rel, dh))
+        attn = torch.empty((B, q, H * dh), dtype=torch.bfloat16, device="cuda")
+        nws = xl.xl_rel_attn_core_workspace_size(L.desc)
+        cws = torch.empty(nws, dtype=torch.uint8, device="cuda") if nws else None
+        beta = L.weights.bias_table
+
+        def run():
+            xl.xl_rel_attn_core(L.desc, qu, qv, k, vt, lay.ldv, r, lay.n_rel, beta, attn, cws)
+
+        out = {"workload": name, "splits": int(nws // (B * H * q * (dh + 2) * 4)) if nws else 1}
+        flops = 6.0 * dh * B * H * w.n_valid_pairs()
+        nbytes = attn_min_bytes(w, w.mlen)
+        for mode in ("warm", "cold"):
+            for _ in range(warmup):
+                run()
+            evs = [(xl.HipEvent(), xl.HipEvent()) for _ in range(launches)]
+            torch.cuda.synchronize()
+            for i in range(launches):
+                if mode == "cold":
+                    scratch.fill_(i & 255)
+                xl.xl_set_core_events(*evs[i])
+                run()
+            torch.cuda.synchronize()
+            xl.xl_set_core_events(None, None)
+            us = np.array([a.elapsed_ms(b) for a, b in evs]) * 1e3
+            med = float(np.median(us))
+            out[mode] = {"median_us": round(med, 3), "p10_us": round(float(np.percentile(us, 10)), 3),
+                         "p90_us": round(float(np.percentile(us, 90)), 3),
+                         **roofline(flops, nbytes, med * 1e-6)}
+        out["algorithmic_flops"] = flops
+        out["algorithmic_bytes"] = nbytes
+        print(json.dumps(out), flush=True)
 
 
 def summarize(d, copy_mib):

@@ -96,6 +96,11 @@ typedef struct {
     int32_t dtype;       /* XL_BF16 (d_head 64) or XL_F32 (d_head 8): h, mem,
                             weights, u, v, bias table and every intermediate */
     int32_t out_dtype;   /* XL_F32 or XL_BF16 for the layer output */
+    int32_t attn_splits; /* bf16 fused attention: 0 lets the library choose how
+                            many workgroups share one query tile's keys (it
+                            splits only when the query tiles are too few to
+                            fill the GPU); 1..64 forces that count. Results
+                            agree to rounding for every value. f32: ignored. */
 } xl_attn_desc;
 
 /* Weights of one layer; all device pointers in desc->dtype. */
@@ -120,11 +125,13 @@ typedef struct {
  *   rel     [n_rel, D]            sinusoid rows R_n, n = 0..n_rel-1
  *   r       [H, n_rel, d_head]    projected table r_n = R_n W_r^T
  *   attn    [B, qlen, H*d_head]   attention output before W_o
+ *   part    scratch of the key-split attention (see xl_rel_attn_core)
  * with klen = mlen + qlen and n_rel = min(klen, clamp_len + 1) (klen when
  * there is no clamp).
  */
 typedef struct {
     size_t qu, qv, k, vt, rel, r, attn;
+    size_t part;             /* split partial results (fp32), 0 bytes unless split */
     size_t total;            /* == xl_rel_attn_workspace_size() */
     int64_t klen, ldv, n_rel;
 } xl_ws_layout;
@@ -159,10 +166,17 @@ int xl_rel_attn_fwd(const xl_attn_desc* desc, const xl_attn_weights* w,
  *   attn [B, qlen, H*d_head] output (desc->dtype).
  * The scale is already folded into qu and qv (desc->scale is not used).
  * desc->d_model, base, out_dtype are ignored.
+ * ws: xl_rel_attn_core_workspace_size(desc) bytes, 256-byte aligned, for the
+ * partial results of a key split (may be NULL when that size is 0). With S
+ * splits it holds S*B*H*qlen*(d_head+2) floats: per split, the
+ * unnormalised output, then (running maximum, sum) per query; a second
+ * kernel merges them into attn.
  */
+size_t xl_rel_attn_core_workspace_size(const xl_attn_desc* desc);
 int xl_rel_attn_core(const xl_attn_desc* desc, const void* qu, const void* qv,
                      const void* k, const void* vt, int64_t ldv, const void* r,
-                     int64_t n_rel, const void* bias_table, void* attn, void* stream);
+                     int64_t n_rel, const void* bias_table, void* attn,
+                     void* ws, size_t ws_bytes, void* stream);
 
 /* Caller-owned FIFO memory of one layer: a ring of mlen_max rows per
  * batch element. Logical row t (0 = oldest, t < len) of batch b is at

@@ -75,6 +75,8 @@ def _fwd(desc, w=None, h=FAKE[8], mem=FAKE[9], out=FAKE[10], ws=FAKE[11], ws_byt
     (dict(scale=float("inf")), xl.XL_BAD_SHAPE),
     (dict(qlen=1 << 30), xl.XL_UNSUPPORTED),
     (dict(bias_clamp=128, mlen=20000, qlen=200), xl.XL_UNSUPPORTED),   # LDS bias table limit
+    (dict(attn_splits=-1), xl.XL_BAD_SHAPE),
+    (dict(attn_splits=65), xl.XL_BAD_SHAPE),
 ])
 def test_fwd_rejects_bad_descriptors(over, status):
     assert _fwd(_desc(**over)) == status
@@ -109,7 +111,8 @@ def test_workspace_size_formula():
         a = lambda x: (x + 255) // 256 * 256
         sizes = [B * H * q * dh, B * H * q * dh, B * H * klen * dh, B * H * dh * ldv, n_rel * D, H * n_rel * dh,
                  B * q * H * dh]
-        assert lay.total == sum(a(s * es) for s in sizes)
+        assert lay.total == sum(a(s * es) for s in sizes)   # these shapes fill the GPU without key splits
+        assert lay.part == lay.total and xl.xl_rel_attn_core_workspace_size(d) == 0
         assert (lay.klen, lay.ldv, lay.n_rel) == (klen, ldv, n_rel)
         assert xl.xl_rel_attn_workspace_size(d) == lay.total
         offs = [lay.qu, lay.qv, lay.k, lay.vt, lay.rel, lay.r, lay.attn]
@@ -117,18 +120,43 @@ def test_workspace_size_formula():
     assert xl.xl_rel_attn_workspace_size(_desc(d_head=16)) == 0
 
 
+def test_split_workspace():
+    # long memory, one query tile per head: the library splits the keys and
+    # needs S * B*H*qlen * (d_head + 2) floats of partials, S in [2, 64]
+    d = _desc(batch=1, n_head=2, qlen=64, mlen=1600)
+    per = d.batch * d.n_head * d.qlen * (d.d_head + 2) * 4
+    need = xl.xl_rel_attn_core_workspace_size(d)
+    assert need % per == 0 and 2 <= need // per <= 64
+    lay = xl.xl_rel_attn_workspace_layout(d)
+    assert lay.part % 256 == 0 and lay.total == lay.part + (need + 255) // 256 * 256
+    # a forced count, and no split at all
+    assert xl.xl_rel_attn_core_workspace_size(_desc(batch=1, n_head=2, qlen=64, mlen=1600, attn_splits=5)) == 5 * per
+    assert xl.xl_rel_attn_core_workspace_size(_desc(attn_splits=1)) == 0
+    # f32 never splits
+    assert xl.xl_rel_attn_core_workspace_size(_desc(dtype=xl.XL_F32, d_head=8, d_model=16, attn_splits=7)) == 0
+    assert xl.xl_rel_attn_core_workspace_size(_desc(attn_splits=99)) == 0      # invalid descriptor
+
+
 def test_core_rejects_bad_arguments():
     lib = xl.lib()
     d = _desc()
     klen = d.qlen + d.mlen
-    call = lambda ldv, n_rel, bias=None, desc=d: lib.xl_rel_attn_core(ctypes.byref(desc), *FAKE[:4], ldv, FAKE[5],
-                                                                      n_rel, bias, FAKE[6], None)
+    call = lambda ldv, n_rel, bias=None, desc=d, ws=None, nb=0: lib.xl_rel_attn_core(
+        ctypes.byref(desc), *FAKE[:4], ldv, FAKE[5], n_rel, bias, FAKE[6], ws, nb, None)
     assert call(klen - 8, klen) == xl.XL_BAD_SHAPE            # ldv < klen
     assert call(klen + 4, klen) == xl.XL_BAD_SHAPE            # ldv not a multiple of 8
     assert call(klen, klen - 1) == xl.XL_BAD_SHAPE            # r too short
     assert call(klen, klen, desc=_desc(bias_clamp=4)) == xl.XL_NULL_ARG
     assert lib.xl_rel_attn_core(ctypes.byref(d), None, *FAKE[1:4], klen, FAKE[5], klen, None, FAKE[6],
-                                None) == xl.XL_NULL_ARG
+                                None, 0, None) == xl.XL_NULL_ARG
+    # a split needs its workspace: missing, too small, misaligned, aliasing the output
+    ds = _desc(attn_splits=3)
+    need = xl.xl_rel_attn_core_workspace_size(ds)
+    assert need > 0
+    assert call(klen, klen, desc=ds) == xl.XL_NULL_ARG
+    assert call(klen, klen, desc=ds, ws=FAKE[12], nb=need - 1) == xl.XL_WORKSPACE_TOO_SMALL
+    assert call(klen, klen, desc=ds, ws=FAKE[12] + 16, nb=need) == xl.XL_UNSUPPORTED
+    assert call(klen, klen, desc=ds, ws=FAKE[6], nb=need) == xl.XL_BAD_SHAPE
 
 
 def test_segment_step_rejects_bad_fifo():

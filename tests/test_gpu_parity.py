@@ -195,13 +195,25 @@ def test_split_invariance_gpu(T):
 
 # --- the fused attention kernel alone ----------------------------------------------------------
 
-@pytest.mark.parametrize("dtype,B,H,qlen,mlen,clamp,bias", [
-    ("bf16", 2, 3, 200, 75, -1, -1),
-    ("bf16", 1, 2, 64, 1600, 1000, -1),
-    ("bf16", 2, 2, 129, 128, -1, 128),
-    ("f32", 2, 2, 20, 11, 7, -1),
-])
-def test_core_alone(T, dtype, B, H, qlen, mlen, clamp, bias):
+CORE = [
+    # dtype, B, H, qlen, mlen, clamp, bias, attn_splits (0: the library's choice)
+    ("bf16", 2, 3, 200, 75, -1, -1, 0),
+    ("bf16", 1, 2, 64, 1600, 1000, -1, 0),     # long memory: split by the library
+    ("bf16", 2, 2, 129, 128, -1, 128, 0),
+    ("f32", 2, 2, 20, 11, 7, -1, 0),
+    # forced key splits: uneven boundaries, empty splits (the first query tile
+    # has only three fully visible steps), the diagonal tile, decode-like q = 1
+    ("bf16", 2, 3, 200, 75, -1, -1, 3),
+    ("bf16", 2, 2, 129, 128, -1, 128, 16),
+    ("bf16", 1, 2, 1, 1600, 1000, -1, 7),
+    ("bf16", 1, 1, 300, 0, -1, -1, 2),
+    ("bf16", 2, 2, 64, 700, 300, 40, 64),
+]
+
+
+@pytest.mark.parametrize("dtype,B,H,qlen,mlen,clamp,bias,splits", CORE,
+                         ids=[f"{c[0]}-B{c[1]}H{c[2]}-q{c[3]}m{c[4]}-c{c[5]}b{c[6]}-s{c[7]}" for c in CORE])
+def test_core_alone(T, dtype, B, H, qlen, mlen, clamp, bias, splits):
     import transformer_xl_relative_amd as xl
     dh = 64 if dtype == "bf16" else 8
     klen = qlen + mlen
@@ -217,11 +229,15 @@ def test_core_alone(T, dtype, B, H, qlen, mlen, clamp, bias):
     vt[..., :klen] = ci["v"].f32.transpose(0, 1, 3, 2)
     vt = xl_inputs.Tensor(vt, dtype)
     desc = xl.make_desc(batch=B, d_model=2, n_head=H, d_head=dh, qlen=qlen, mlen=mlen, clamp_len=clamp,
-                        bias_clamp=bias, dtype=xl.XL_BF16 if dtype == "bf16" else xl.XL_F32)
+                        bias_clamp=bias, dtype=xl.XL_BF16 if dtype == "bf16" else xl.XL_F32, attn_splits=splits)
     attn = T.empty((B, qlen, H * dh), dtype=T.bfloat16 if dtype == "bf16" else T.float32, device="cuda")
     beta = gu.dev(ci["beta"]) if bias >= 0 else None
+    nws = xl.xl_rel_attn_core_workspace_size(desc)
+    if splits > 1 or (dtype == "bf16" and mlen >= 1600):
+        assert nws > 0
+    ws = T.empty(nws, dtype=T.uint8, device="cuda") if nws else None
     xl.xl_rel_attn_core(desc, gu.dev(qu), gu.dev(qv), gu.dev(ci["k"]), gu.dev(vt), ldv, gu.dev(ci["r"]), n_rel,
-                        beta, attn)
+                        beta, attn, ws)
     T.cuda.synchronize()
     ref = oracle.rel_attn_core(ci["q"].f64, ci["k"].f64, ci["v"].f64, ci["r"].f64, ci["u"].f64, ci["vb"].f64,
                                scale=s, clamp_len=clamp, beta=ci["beta"].f64 if bias >= 0 else None,

@@ -25,7 +25,7 @@ class xl_attn_desc(ctypes.Structure):
     _fields_ = [("batch", _i64), ("d_model", _i64), ("n_head", _i64), ("d_head", _i64),
                 ("qlen", _i64), ("mlen", _i64), ("clamp_len", _i64), ("bias_clamp", _i64),
                 ("base", ctypes.c_double), ("scale", ctypes.c_float),
-                ("dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32), ("attn_splits", ctypes.c_int32)]
 
 
 class xl_attn_weights(ctypes.Structure):
@@ -33,7 +33,7 @@ class xl_attn_weights(ctypes.Structure):
 
 
 class xl_ws_layout(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_size_t) for n in ("qu", "qv", "k", "vt", "rel", "r", "attn", "total")] + \
+    _fields_ = [(n, ctypes.c_size_t) for n in ("qu", "qv", "k", "vt", "rel", "r", "attn", "part", "total")] + \
                [("klen", _i64), ("ldv", _i64), ("n_rel", _i64)]
 
 
@@ -53,7 +53,8 @@ _STATUS = {0: "XL_OK", 1: "XL_NULL_ARG", 2: "XL_BAD_SHAPE", 3: "XL_UNSUPPORTED",
 _lib = None
 
 EXPORTS = ("xl_status_string", "xl_last_error", "xl_relpos_embed", "xl_rel_attn_workspace_size",
-           "xl_rel_attn_workspace_layout", "xl_rel_attn_fwd", "xl_rel_attn_core", "xl_segment_step",
+           "xl_rel_attn_workspace_layout", "xl_rel_attn_fwd", "xl_rel_attn_core_workspace_size", "xl_rel_attn_core",
+           "xl_segment_step",
            "xl_set_core_events")
 
 
@@ -84,7 +85,10 @@ def lib():
         L.xl_rel_attn_workspace_layout.argtypes = [ctypes.POINTER(xl_attn_desc), ctypes.POINTER(xl_ws_layout)]
         L.xl_rel_attn_fwd.argtypes = [ctypes.POINTER(xl_attn_desc), ctypes.POINTER(xl_attn_weights), _p, _p, _p,
                                       _p, ctypes.c_size_t, _p]
-        L.xl_rel_attn_core.argtypes = [ctypes.POINTER(xl_attn_desc), _p, _p, _p, _p, _i64, _p, _i64, _p, _p, _p]
+        L.xl_rel_attn_core_workspace_size.argtypes = [ctypes.POINTER(xl_attn_desc)]
+        L.xl_rel_attn_core_workspace_size.restype = ctypes.c_size_t
+        L.xl_rel_attn_core.argtypes = [ctypes.POINTER(xl_attn_desc), _p, _p, _p, _p, _i64, _p, _i64, _p, _p, _p,
+                                       ctypes.c_size_t, _p]
         L.xl_segment_step.argtypes = [ctypes.POINTER(xl_attn_desc), ctypes.POINTER(xl_attn_weights), _p,
                                       ctypes.POINTER(xl_mem_fifo), _p, _p, ctypes.c_size_t, _p]
         L.xl_set_core_events.argtypes = [_p, _p]
@@ -121,9 +125,9 @@ def _stream(stream) -> Optional[int]:
 
 
 def make_desc(*, batch, d_model, n_head, d_head, qlen, mlen=0, clamp_len=-1, bias_clamp=-1, base=10000.0,
-              scale=0.0, dtype=XL_BF16, out_dtype=None) -> xl_attn_desc:
+              scale=0.0, dtype=XL_BF16, out_dtype=None, attn_splits=0) -> xl_attn_desc:
     return xl_attn_desc(batch, d_model, n_head, d_head, qlen, mlen, clamp_len, bias_clamp, base, scale,
-                        dtype, dtype if out_dtype is None else out_dtype)
+                        dtype, dtype if out_dtype is None else out_dtype, attn_splits)
 
 
 @dataclasses.dataclass
@@ -166,9 +170,15 @@ def xl_rel_attn_fwd(desc: xl_attn_desc, weights: Weights, h, mem, out, ws, strea
     return out
 
 
-def xl_rel_attn_core(desc: xl_attn_desc, qu, qv, k, vt, ldv: int, r, n_rel: int, bias_table, attn, stream=None):
+def xl_rel_attn_core_workspace_size(desc: xl_attn_desc) -> int:
+    return lib().xl_rel_attn_core_workspace_size(ctypes.byref(desc))
+
+
+def xl_rel_attn_core(desc: xl_attn_desc, qu, qv, k, vt, ldv: int, r, n_rel: int, bias_table, attn, ws=None,
+                     stream=None):
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().xl_rel_attn_core(ctypes.byref(desc), _ptr(qu), _ptr(qv), _ptr(k), _ptr(vt), ldv, _ptr(r), n_rel,
-                                  _ptr(bias_table), _ptr(attn), _stream(stream)))
+                                  _ptr(bias_table), _ptr(attn), _ptr(ws), nbytes, _stream(stream)))
     return attn
 
 

@@ -66,10 +66,12 @@ int check_desc(const xl_attn_desc* d, int64_t mlen, bool need_dmodel) {
         if (!isfinite(d->scale)) return fail(XL_BAD_SHAPE, "scale must be finite");
     }
     if (d->bias_clamp > 65535) return fail(XL_UNSUPPORTED, "bias_clamp above 65535");
+    if (d->attn_splits < 0 || d->attn_splits > xl::kMaxAttnSplits)
+        return fail(XL_BAD_SHAPE, "attn_splits must be in [0, %d]", xl::kMaxAttnSplits);
     const int64_t klen = mlen + d->qlen;
     const int64_t hd = d->n_head * d->d_head;
     // every element count a kernel indexes with 32-bit arithmetic must fit
-    if (klen > kI32 / 64 || d->batch * klen > kI32 / 2 || hd > 65536 || d->batch * d->n_head > kI32 / 64 ||
+    if (klen > kI32 / 128 || d->batch * klen > kI32 / 2 || hd > 65536 || d->batch * d->n_head > kI32 / 64 ||
         (double)d->batch * d->n_head * klen * d->d_head > 9.0e15)
         return fail(XL_UNSUPPORTED, "problem too large for this build");
     if (d->batch * d->n_head * ((d->qlen + 127) / 128) > kI32) return fail(XL_UNSUPPORTED, "grid too large");
@@ -77,6 +79,16 @@ int check_desc(const xl_attn_desc* d, int64_t mlen, bool need_dmodel) {
     if (d->bias_clamp >= 0 && d->dtype == XL_BF16 && klen > kMaxBiasKlen)
         return fail(XL_UNSUPPORTED, "with a bias table, mlen + qlen must be <= %lld", (long long)kMaxBiasKlen);
     return XL_OK;
+}
+
+// key splits of the fused attention (bf16 only)
+int splits_of(const xl_attn_desc* d, int64_t mlen) {
+    if (d->dtype != XL_BF16) return 1;
+    if (d->attn_splits > 0) return d->attn_splits;
+    return xl::attn_bf16_splits(d->batch, d->n_head, d->qlen, mlen);
+}
+size_t part_bytes_of(const xl_attn_desc* d, int64_t mlen) {
+    return d->dtype == XL_BF16 ? xl::attn_bf16_part_bytes(d->batch, d->n_head, d->qlen, splits_of(d, mlen)) : 0;
 }
 
 int64_t n_rel_of(const xl_attn_desc* d, int64_t klen) {
@@ -98,6 +110,7 @@ void fill_layout(const xl_attn_desc* d, int64_t mlen, xl_ws_layout* L) {
     L->rel = take((size_t)(n_rel * D) * es);
     L->r = take((size_t)(H * n_rel * dh) * es);
     L->attn = take((size_t)(B * q * H * dh) * es);
+    L->part = take(part_bytes_of(d, mlen));
     L->total = off;
     L->klen = klen;
     L->ldv = ldv;
@@ -199,6 +212,8 @@ int layer_forward(const xl_attn_desc* d, const xl_attn_weights* w, const void* h
     a.out = W + L.attn;
     a.B = (int)B; a.H = (int)H; a.qlen = (int)q; a.mlen = (int)mlen; a.klen = (int)klen;
     a.ldv = (int)L.ldv; a.n_rel = (int)L.n_rel; a.r_rows = (int)L.n_rel; a.bias_clamp = (int)(d->bias_clamp >= 0 ? d->bias_clamp : 0);
+    a.nsplit = splits_of(d, mlen);
+    a.part = W + L.part;
     int st = run_core(a, bf, (int)dh, s);
     if (st != XL_OK) return st;
     // 6. output projection
@@ -296,8 +311,14 @@ int xl_rel_attn_fwd(const xl_attn_desc* desc, const xl_attn_weights* w, const vo
     return layer_forward(desc, w, h, mem, desc->mlen, desc->mlen, 0, out, ws, ws_bytes, (hipStream_t)stream);
 }
 
+size_t xl_rel_attn_core_workspace_size(const xl_attn_desc* desc) {
+    if (check_desc(desc, desc ? desc->mlen : 0, false) != XL_OK) return 0;
+    return part_bytes_of(desc, desc->mlen);
+}
+
 int xl_rel_attn_core(const xl_attn_desc* desc, const void* qu, const void* qv, const void* k, const void* vt,
-                     int64_t ldv, const void* r, int64_t n_rel, const void* bias_table, void* attn, void* stream) {
+                     int64_t ldv, const void* r, int64_t n_rel, const void* bias_table, void* attn, void* ws,
+                     size_t ws_bytes, void* stream) {
     g_last_error.clear();
     int st = check_desc(desc, desc ? desc->mlen : 0, false);
     if (st != XL_OK) return st;
@@ -316,6 +337,17 @@ int xl_rel_attn_core(const xl_attn_desc* desc, const void* qu, const void* qv, c
     a.B = (int)desc->batch; a.H = (int)desc->n_head; a.qlen = (int)desc->qlen; a.mlen = (int)desc->mlen;
     a.klen = (int)klen; a.ldv = (int)ldv; a.n_rel = (int)need; a.r_rows = (int)n_rel;
     a.bias_clamp = (int)(desc->bias_clamp >= 0 ? desc->bias_clamp : 0);
+    a.nsplit = splits_of(desc, desc->mlen);
+    const size_t need_ws = part_bytes_of(desc, desc->mlen);
+    if (need_ws > 0) {
+        if (!ws) return fail(XL_NULL_ARG, "ws is NULL but the split attention needs %zu bytes", need_ws);
+        if (ws_bytes < need_ws)
+            return fail(XL_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", ws_bytes, need_ws);
+        if (((uintptr_t)ws) % kAlign) return fail(XL_UNSUPPORTED, "workspace must be 256-byte aligned");
+        const size_t ab = (size_t)(desc->batch * desc->qlen * desc->n_head * desc->d_head) * esize(desc->dtype);
+        if (overlaps(ws, need_ws, attn, ab)) return fail(XL_BAD_SHAPE, "ws aliases attn");
+        a.part = ws;
+    }
     return run_core(a, desc->dtype == XL_BF16, (int)desc->d_head, (hipStream_t)stream);
 }
 

@@ -10,7 +10,14 @@
 //
 // Work decomposition: one workgroup = (batch, head, 128 queries), four waves
 // of 32 queries; keys advance 32 per step. Workgroups are issued longest
-// first (query tiles near the end of the segment see more keys).
+// first (query tiles near the end of the segment see more keys). When there
+// are too few query tiles to fill the machine (long memory, short segment),
+// each tile's key steps are split over several workgroups, each writing its
+// unnormalised output with its running maximum and sum; a second kernel
+// merges the splits (the softmax of a union of key sets is the
+// max-rescaled combination of the parts). Split boundaries lie among the
+// steps whose first key every query of the tile sees, so that no query has
+// an empty key set in any non-empty split.
 //
 // Products are computed transposed (keys or distances on the MFMA rows,
 // queries on the columns): a lane owns one query, and the softmax
@@ -142,16 +149,32 @@ __global__ void __launch_bounds__(NT, 2) attn_bf16_kernel(AttnArgs a) {
     // ---- work item (wave-uniform values kept in scalar registers)
     const int nbh = a.B * a.H;
     const int nqt = (a.qlen + BQ - 1) / BQ;
-    const int qt = __builtin_amdgcn_readfirstlane(nqt - 1 - (int)(blockIdx.x / nbh));
-    const int bh = __builtin_amdgcn_readfirstlane((int)(blockIdx.x % nbh));
+    const int nsplit = a.nsplit;
+    const int per_qt = nbh * nsplit;
+    const int qt = __builtin_amdgcn_readfirstlane(nqt - 1 - (int)(blockIdx.x / per_qt));
+    const int rem = (int)(blockIdx.x % per_qt);
+    const int sp = __builtin_amdgcn_readfirstlane(rem / nbh);
+    const int bh = __builtin_amdgcn_readfirstlane(rem % nbh);
     const int h = __builtin_amdgcn_readfirstlane(bh % a.H);
     const int b = __builtin_amdgcn_readfirstlane(bh / a.H);
     const int i0 = qt * BQ;
     const int iw = i0 + wave * WQ;
     const int qend = min(i0 + BQ, a.qlen);
-    const int nsteps = __builtin_amdgcn_readfirstlane((a.mlen + qend + BKY - 1) / BKY);
+    // key steps of the tile; this workgroup's split covers steps [S0, S1). The
+    // loop counts steps from S0 (LDS slots and ring halves follow that local
+    // count); addresses, distances and the mask use the absolute step S0 + s.
+    const int tsteps = (a.mlen + qend + BKY - 1) / BKY;
+    int S0 = 0, S1 = tsteps;
+    if (nsplit > 1) {
+        const int full = min((a.mlen + i0) / BKY + 1, tsteps);   // steps whose first key all queries see
+        auto bnd = [&](int k) { return k >= nsplit ? tsteps : min((int)((int64_t)k * tsteps / nsplit), full - 1); };
+        S0 = bnd(sp);
+        S1 = bnd(sp + 1);
+    }
+    S0 = __builtin_amdgcn_readfirstlane(S0);
+    const int nsteps = __builtin_amdgcn_readfirstlane(S1 - S0);
     const int wlast = iw < a.qlen ? a.mlen + min(iw + WQ, a.qlen) - 1 : -1;
-    const int wsteps = __builtin_amdgcn_readfirstlane(wlast >= 0 ? wlast / BKY + 1 : 0);
+    const int wsteps = __builtin_amdgcn_readfirstlane(wlast >= 0 ? max(min(wlast / BKY + 1, S1) - S0, 0) : 0);
 
     const char* kb = (const char*)a.k + (int64_t)bh * a.klen * (DH * 2);
     const char* vb = (const char*)a.vt + (int64_t)bh * DH * a.ldv * 2;
@@ -165,12 +188,13 @@ __global__ void __launch_bounds__(NT, 2) attn_bf16_kernel(AttnArgs a) {
     // V^T tiles: row rho = 16*wave + lane/4 of 64 bytes, stored chunk lane%4
     // holds chunk (lane%4)^((rho>>2)&3).
     const int krho = 8 * wave + (lane >> 3);
-    const int kvoff = krho * 128 + (((lane & 7) ^ ((krho >> 1) & 7)) << 4);
+    const int kvoff = krho * 128 + (((lane & 7) ^ ((krho >> 1) & 7)) << 4) + S0 * (BKY * DH * 2);
     const int vrho = 16 * wave + (lane >> 2);
-    const int vvoff = vrho * a.ldv * 2 + (((lane & 3) ^ ((vrho >> 2) & 3)) << 4);
-    // shared band block g holds distances gtop - 32 g - row, gtop = mlen + i0 + 127;
+    const int vvoff = vrho * a.ldv * 2 + (((lane & 3) ^ ((vrho >> 2) & 3)) << 4) + S0 * (BKY * 2);
+    // shared band block g (local) holds distances gs - 32 g - row, gs = mlen + i0 + 127 - 32 S0;
     // wave w's position block beta is band block beta + 3 - w
     const int gtop = a.mlen + i0 + BQ - 1;
+    const int gs = gtop - BKY * S0;
     const int rmax = a.n_rel - 1;
 
     // one 16-byte piece per lane; M0 (the LDS destination) is this wave's kilobyte of the slot
@@ -183,17 +207,18 @@ __global__ void __launch_bounds__(NT, 2) attn_bf16_kernel(AttnArgs a) {
                             0, 0);
     };
     auto dma_band = [&](int g, int slot) __attribute__((always_inline)) {
-        const int d = min(max(gtop - BKY * g - krho, 0), rmax);
+        const int d = min(max(gs - BKY * g - krho, 0), rmax);
         raw_buffer_load_lds(rrs, lds_ptr(lds0 + OFF_B + slot * TILE + wave * 1024), 16, d * 128 + (kvoff & 127), 0,
                             0, 0);
     };
     // keys past klen of the last tile: their weight is 0, but the values there
     // (padding columns of V^T) must be finite; each wave zeroes the piece its
     // own load wrote, after that load has landed
-    const int vtail = BKY * nsteps > a.klen ? nsteps - 1 : -1;
+    const int vtail_abs = BKY * tsteps > a.klen ? tsteps - 1 : -1;
+    const int vtail = vtail_abs >= S0 && vtail_abs < S1 ? vtail_abs - S0 : -1;
     auto fix_v_tail = [&](int slot) __attribute__((always_inline)) {
         const int lc = (lane & 3) ^ ((vrho >> 2) & 3);          // chunk of 8 keys this lane loaded
-        const int nval = a.klen - (BKY * vtail + 8 * lc);       // keys of the chunk below klen
+        const int nval = a.klen - (BKY * vtail_abs + 8 * lc);   // keys of the chunk below klen
         if (nval < 8) {
             const uint32_t adr = lds0 + OFF_V + slot * TILE + wave * 1024 + lane * 16;
             u32x4 w = lds_ld<u32x4>(adr);
@@ -223,7 +248,7 @@ __global__ void __launch_bounds__(NT, 2) attn_bf16_kernel(AttnArgs a) {
     bf16x8 pband[3][4];
 #pragma unroll
     for (int be = 0; be < 3; ++be) {
-        const int d = min(max(dtop - BKY * be - l32, 0), rmax);
+        const int d = min(max(dtop - BKY * (S0 + be) - l32, 0), rmax);
         const bf16_t* row = (const bf16_t*)(rb + (int64_t)d * (DH * 2));
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) pband[be][kc] = as_bf16x8(*(const u32x4*)(row + 16 * kc + 8 * hf));
@@ -231,14 +256,17 @@ __global__ void __launch_bounds__(NT, 2) attn_bf16_kernel(AttnArgs a) {
 
     // ---- prologue DMAs, ordered by when they are needed: K(0), K(1), V(0) and
     // band blocks 3..6 before step 0; K(2), V(1), band block 7 may still be in flight then
-    dma_k(0, 0);
-    dma_k(1, 1);
-    dma_v(0, 0);
+    // (an empty split issues none and writes the neutral partial result)
+    if (nsteps > 0) {
+        dma_k(0, 0);
+        dma_k(1, 1);
+        dma_v(0, 0);
 #pragma unroll
-    for (int g = 3; g <= 6; ++g) dma_band(g, g % 6);
-    dma_k(2, 2);
-    dma_v(1, 1);
-    dma_band(7, 1);
+        for (int g = 3; g <= 6; ++g) dma_band(g, g % 6);
+        dma_k(2, 2);
+        dma_v(1, 1);
+        dma_band(7, 1);
+    }
     constexpr int PRO_DMA = 10;
 
     // ---- bias table: entry x holds beta_h[clamp(X0 - x, +-bc)], X0 = gtop,
@@ -255,7 +283,7 @@ __global__ void __launch_bounds__(NT, 2) attn_bf16_kernel(AttnArgs a) {
         block_sync<63>();
     }
     // bias of position block beta: registers 4q..4q+3 hold distances dtop - 32 beta - 8q - 4hf - t
-    const uint32_t tbl_lane = lds0 + OFF_TBL + 4 * (gtop - dtop + 4 * hf);
+    const uint32_t tbl_lane = lds0 + OFF_TBL + 4 * (gtop - dtop + 4 * hf) + 128 * S0;
 
     // ---- LDS read addresses
     const int pr = pi_row(l32);
@@ -331,9 +359,10 @@ __global__ void __launch_bounds__(NT, 2) attn_bf16_kernel(AttnArgs a) {
         for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
-    // visible-key limit of this lane relative to a step: key 32 s + c_r + 8 hf is
-    // visible when c_r <= lim - 32 s
-    const int lim0 = a.mlen + iq - 8 * hf;
+    // visible-key limit of this lane relative to a local step: key
+    // 32 (S0 + s) + c_r + 8 hf is visible when c_r <= lim - 32 s
+    const int lim0 = a.mlen + iq - 8 * hf - BKY * S0;
+    const int mask_from = a.mlen + iw - BKY * S0;
 
     // mask, row maximum and lazy rescale of the scores of step s (before their
     // exponentials are taken): the exponentials use the running maximum, which
@@ -341,7 +370,7 @@ __global__ void __launch_bounds__(NT, 2) attn_bf16_kernel(AttnArgs a) {
     // more than 2^8
     auto prepare = [&](f32x16& sc, int s) __attribute__((always_inline)) {
         // causal mask: only the last steps of a wave reach past its first query
-        if (BKY * s + BKY - 1 > a.mlen + iw) {
+        if (BKY * s + BKY - 1 > mask_from) {
             const int lim = lim0 - BKY * s;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -452,44 +481,65 @@ __global__ void __launch_bounds__(NT, 2) attn_bf16_kernel(AttnArgs a) {
         block_sync<63>();
     };
 
-    // ---- prologue compute: blocks 0 and 1, then the scores of step 0, then block 2
-    wait_vmcnt<PRO_DMA>();                 // query operands and the first band blocks
-    ring_write(pos_reg(0, pband[0]), 0u);
-    ring_write(pos_reg(1, pband[1]), 128u);
-    block_sync<PRO_DMA - 1>();             // K(0)
-    f32x16 s0 = content(ring_read(0u), 0), s1;
-    ring_write(pos_reg(2, pband[2]), 0u);   // block 2 replaces block 0, read above
-    if (wsteps > 0) prepare(s0, 0);
-    wait_vmcnt<INFLIGHT>();
-    if (vtail == 0) fix_v_tail(0);
-    block_sync<63>();
+    if (nsteps > 0) {
+        // ---- prologue compute: blocks 0 and 1, then the scores of step 0, then block 2
+        wait_vmcnt<PRO_DMA>();                 // query operands and the first band blocks
+        ring_write(pos_reg(0, pband[0]), 0u);
+        ring_write(pos_reg(1, pband[1]), 128u);
+        block_sync<PRO_DMA - 1>();             // K(0)
+        f32x16 s0 = content(ring_read(0u), 0), s1;
+        ring_write(pos_reg(2, pband[2]), 0u);   // block 2 replaces block 0, read above
+        if (wsteps > 0) prepare(s0, 0);
+        wait_vmcnt<INFLIGHT>();
+        if (vtail == 0) fix_v_tail(0);
+        block_sync<63>();
 
-    // steps in groups of six (slot indices are compile-time constants)
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
-    using I3 = std::integral_constant<int, 3>;
-    using I4 = std::integral_constant<int, 4>;
-    using I5 = std::integral_constant<int, 5>;
-    for (int s = 0;;) {
-        step(I0{}, s, s0, s1);
-        if (++s >= nsteps) break;
-        step(I1{}, s, s1, s0);
-        if (++s >= nsteps) break;
-        step(I2{}, s, s0, s1);
-        if (++s >= nsteps) break;
-        step(I3{}, s, s1, s0);
-        if (++s >= nsteps) break;
-        step(I4{}, s, s0, s1);
-        if (++s >= nsteps) break;
-        step(I5{}, s, s1, s0);
-        if (++s >= nsteps) break;
+        // steps in groups of six (slot indices are compile-time constants)
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        using I2 = std::integral_constant<int, 2>;
+        using I3 = std::integral_constant<int, 3>;
+        using I4 = std::integral_constant<int, 4>;
+        using I5 = std::integral_constant<int, 5>;
+        for (int s = 0;;) {
+            step(I0{}, s, s0, s1);
+            if (++s >= nsteps) break;
+            step(I1{}, s, s1, s0);
+            if (++s >= nsteps) break;
+            step(I2{}, s, s0, s1);
+            if (++s >= nsteps) break;
+            step(I3{}, s, s1, s0);
+            if (++s >= nsteps) break;
+            step(I4{}, s, s0, s1);
+            if (++s >= nsteps) break;
+            step(I5{}, s, s1, s0);
+            if (++s >= nsteps) break;
+        }
     }
+    wait_vmcnt<0>();   // no load into LDS outlives the workgroup
 
     // ---- epilogue: o / l, heads concatenated. The wave stages its 32 x 64
     // outputs in its own ring (padded rows of 64 bf16), then writes each query's
     // 128-byte row segment with 16-byte stores.
     const float l_tot = halves_sum(l_run);
+    if (nsplit > 1) {
+        // partial result of this split: O (unnormalised, [query][d_head] fp32),
+        // then (running maximum, sum) per query
+        if (iw >= a.qlen) return;
+        const int64_t prow = ((int64_t)sp * nbh + bh) * a.qlen + iq;
+        if (qok) {
+            float* po = (float*)a.part + prow * DH;
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq)
+                    *(f32x4*)(po + 32 * t + 8 * gq + 4 * hf) =
+                        (f32x4){o[t][4 * gq], o[t][4 * gq + 1], o[t][4 * gq + 2], o[t][4 * gq + 3]};
+            if (hf == 0)
+                *(float2*)((float*)a.part + (int64_t)nsplit * nbh * a.qlen * DH + 2 * prow) = make_float2(m_run, l_tot);
+        }
+        return;
+    }
     if (wsteps == 0) return;
     const float inv = 1.f / l_tot;
     constexpr int OP = DH * 2 + 16;                // staged row: 64 bf16 + padding
@@ -516,10 +566,64 @@ __global__ void __launch_bounds__(NT, 2) attn_bf16_kernel(AttnArgs a) {
     }
 }
 
+// Merge of the key splits: for query i of head h, with split partials
+// (O_s, m_s, l_s), out = sum_s e^(m_s - M) O_s / sum_s e^(m_s - M) l_s,
+// M = max_s m_s (an empty split has m_s = -inf, l_s = 0, O_s = 0). A thread
+// produces 4 consecutive outputs of one query; the splits are read in groups
+// of MG with all loads of a group in flight together, and the running
+// maximum moves between groups (rescaling the sums).
+constexpr int MG = 16;
+
+__global__ void __launch_bounds__(256) attn_merge_kernel(AttnArgs a) {
+    const int64_t nrow = (int64_t)a.B * a.H * a.qlen;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= nrow * 16) return;
+    const int c = (int)(idx & 15);
+    const int64_t row = idx >> 4;                  // (b*H + h)*qlen + i
+    const f32x4* po = (const f32x4*)a.part + row * (DH / 4) + c;
+    const float2* pml = (const float2*)((const float*)a.part + (int64_t)a.nsplit * nrow * DH) + row;
+    float M = -INFINITY, L = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < a.nsplit; s0 += MG) {
+        float2 ml[MG];
+        f32x4 v[MG];
+#pragma unroll
+        for (int k = 0; k < MG; ++k) {
+            const int sp = min(s0 + k, a.nsplit - 1);
+            ml[k] = pml[sp * nrow];
+            v[k] = po[sp * nrow * (DH / 4)];
+        }
+        float mg = M;
+#pragma unroll
+        for (int k = 0; k < MG; ++k)
+            if (s0 + k < a.nsplit) mg = fmaxf(mg, ml[k].x);
+        // mg is finite: every query sees a key in some split
+        const float mb = mg * LOG2E;
+        const float alpha = __builtin_amdgcn_exp2f(fmaf(M, LOG2E, -mb));   // 0 while M = -inf
+        L *= alpha;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] *= alpha;
+#pragma unroll
+        for (int k = 0; k < MG; ++k) {
+            const float wgt = s0 + k < a.nsplit ? __builtin_amdgcn_exp2f(fmaf(ml[k].x, LOG2E, -mb)) : 0.f;
+            L = fmaf(wgt, ml[k].y, L);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = fmaf(wgt, v[k][e], acc[e]);
+        }
+        M = mg;
+    }
+    const float inv = 1.f / L;
+    const int64_t bh = row / a.qlen, i = row - bh * a.qlen;
+    const int64_t b = bh / a.H, h = bh - b * a.H;
+    *(u32x2*)((bf16_t*)a.out + (b * a.qlen + i) * ((int64_t)a.H * DH) + h * DH + 4 * c) =
+        (u32x2){pack2bf(acc[0] * inv, acc[1] * inv), pack2bf(acc[2] * inv, acc[3] * inv)};
+}
+
 template <bool HAS_BIAS>
 hipError_t launch_bf16(const AttnArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     const int nqt = (a.qlen + BQ - 1) / BQ;
-    const int64_t grid = (int64_t)a.B * a.H * nqt;
+    if (a.nsplit < 1 || a.nsplit > kMaxAttnSplits || (a.nsplit > 1 && !a.part)) return hipErrorInvalidValue;
+    const int64_t grid = (int64_t)a.B * a.H * nqt * a.nsplit;
     if (grid <= 0) return hipSuccess;
     int lds = OFF_TBL;
     if (HAS_BIAS) {
@@ -535,7 +639,18 @@ hipError_t launch_bf16(const AttnArgs& a, hipStream_t s, hipEvent_t ev0, hipEven
         attr = 160 * 1024;
     }
     (void)hipGetLastError();   // drop a stale error of an earlier runtime call
-    hipExtLaunchKernelGGL(attn_bf16_kernel<HAS_BIAS>, dim3((unsigned)grid), dim3(NT), (uint32_t)lds, s, ev0, ev1, 0u, a);
+    if (a.nsplit == 1) {
+        hipExtLaunchKernelGGL(attn_bf16_kernel<HAS_BIAS>, dim3((unsigned)grid), dim3(NT), (uint32_t)lds, s, ev0, ev1, 0u, a);
+        return hipGetLastError();
+    }
+    // the events bracket both kernels
+    hipExtLaunchKernelGGL(attn_bf16_kernel<HAS_BIAS>, dim3((unsigned)grid), dim3(NT), (uint32_t)lds, s, ev0,
+                          (hipEvent_t) nullptr, 0u, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t threads = (int64_t)a.B * a.H * a.qlen * 16;
+    hipExtLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0u, s,
+                          (hipEvent_t) nullptr, ev1, 0u, a);
     return hipGetLastError();
 }
 
@@ -543,6 +658,24 @@ hipError_t launch_bf16(const AttnArgs& a, hipStream_t s, hipEvent_t ev0, hipEven
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     return a.bias ? launch_bf16<true>(a, s, ev0, ev1) : launch_bf16<false>(a, s, ev0, ev1);
+}
+
+int attn_bf16_splits(int64_t B, int64_t H, int64_t qlen, int64_t mlen) {
+    // split only when the query tiles leave most compute units idle: aim at two
+    // workgroups per compute unit, keeping at least four fully visible key
+    // steps per split
+    const int64_t tiles = B * H * ((qlen + BQ - 1) / BQ);
+    constexpr int64_t kCUs = 256;
+    if (tiles >= kCUs) return 1;
+    const int64_t full = mlen / BKY + 1;          // fully visible steps of the first query tile
+    int64_t n = (2 * kCUs + tiles - 1) / tiles;
+    n = n < full / 4 ? n : full / 4;
+    n = n < kMaxAttnSplits ? n : kMaxAttnSplits;
+    return n < 1 ? 1 : (int)n;
+}
+
+size_t attn_bf16_part_bytes(int64_t B, int64_t H, int64_t qlen, int nsplit) {
+    return nsplit > 1 ? (size_t)nsplit * (size_t)(B * H * qlen) * (DH + 2) * sizeof(float) : 0;
 }
 
 }  // namespace xl

@@ -49,7 +49,8 @@ struct Tile {
     static constexpr int NI = BT * (ROWB / 16) / NT;   // loads per thread per operand per stage
 };
 using Big = Tile<4, 2, 2, 4, 2>;     // 256 x 256, 8 waves, 2 stages (128 KiB)
-using Small = Tile<2, 2, 2, 2, 3>;   // 128 x 128, 4 waves, 3 stages (96 KiB)
+using Small = Tile<2, 2, 2, 2, 3>;   // 128 x 128, 4 waves, 3 stages (96 KiB): one per CU
+using Small2 = Tile<2, 2, 2, 2, 2>;  // 128 x 128, 4 waves, 2 stages (64 KiB): two per CU
 
 template <typename T, bool kRowOut>
 __device__ __forceinline__ void tile_bf16(const GemmArgs& g, int m0, int n0, char* smem) {
@@ -429,10 +430,17 @@ hipError_t launch_gemms_bf16(const GemmArgs* g, int count, hipStream_t s) {
     // the epilogues address heads with d_head 64 (the only bf16 head size)
     for (int i = 0; i < count; ++i)
         if (g[i].epi != EPI_OUT && g[i].dh != 64) return hipErrorInvalidValue;
-    int big = 0;
+    // 256 x 256 tiles when they nearly fill the machine; else 128 x 128 tiles,
+    // with three LDS stages while one workgroup per compute unit suffices and
+    // two stages (two workgroups per compute unit) beyond that
+    int big = 0, small = 0;
     for (int i = 0; i < count; ++i)
-        if (g[i].M > 0 && g[i].N > 0) big += ((g[i].M + 255) / 256) * ((g[i].N + 255) / 256);
-    return big >= 192 ? launch_tiles<Big>(g, count, s) : launch_tiles<Small>(g, count, s);
+        if (g[i].M > 0 && g[i].N > 0) {
+            big += ((g[i].M + 255) / 256) * ((g[i].N + 255) / 256);
+            small += ((g[i].M + 127) / 128) * ((g[i].N + 127) / 128);
+        }
+    if (big >= 192) return launch_tiles<Big>(g, count, s);
+    return small > 256 ? launch_tiles<Small2>(g, count, s) : launch_tiles<Small>(g, count, s);
 }
 
 }  // namespace xl

@@ -12,74 +12,105 @@
 namespace xl {
 namespace {
 
-// A thread owns frequency pair t of RPT consecutive rows: the inverse
-// frequency is evaluated once, the angles and their sin/cos per row.
-constexpr int RPT = 4;
+// A thread owns frequency pair t (blockIdx.x * 256 + threadIdx.x) of RPT
+// consecutive rows: the inverse frequency is evaluated once, then the RPT
+// angles and their sin/cos, which are independent, so their latencies overlap.
+constexpr int RPT = 2;
 
 template <bool kBf16>
 __global__ void __launch_bounds__(256) relpos_kernel(int64_t delta0, int64_t n_rows, int64_t d_model,
                                                      int64_t clamp_len, double base, void* out) {
     const int half = (int)(d_model >> 1);
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t ngroups = (n_rows + RPT - 1) / RPT;
-    if (idx >= ngroups * half) return;
-    const int64_t grp = idx / half;
-    const int t = (int)(idx - grp * half);
+    const int t = (int)blockIdx.x * 256 + (int)threadIdx.x;
+    if (t >= half) return;
     const double inv_freq = pow(base, -(2.0 * (double)t) / (double)d_model);
+    const int64_t ngroups = (n_rows + RPT - 1) / RPT;
+    for (int64_t grp = blockIdx.y; grp < ngroups; grp += gridDim.y) {
+        double sv[RPT], cv[RPT];
 #pragma unroll
-    for (int k = 0; k < RPT; ++k) {
-        const int64_t n = grp * RPT + k;
-        if (n >= n_rows) break;
-        int64_t delta = delta0 + n;
-        if (clamp_len >= 0) delta = delta < -clamp_len ? -clamp_len : (delta > clamp_len ? clamp_len : delta);
-        double sv, cv;
-        sincos((double)delta * inv_freq, &sv, &cv);
-        if constexpr (kBf16) {
-            ((uint32_t*)out)[n * half + t] = (uint32_t)d2bf(sv) | ((uint32_t)d2bf(cv) << 16);
-        } else {
-            ((float2*)out)[n * half + t] = make_float2((float)sv, (float)cv);
+        for (int k = 0; k < RPT; ++k) {
+            const int64_t n = min(grp * RPT + k, n_rows - 1);
+            int64_t delta = delta0 + n;
+            if (clamp_len >= 0) delta = delta < -clamp_len ? -clamp_len : (delta > clamp_len ? clamp_len : delta);
+            sincos((double)delta * inv_freq, &sv[k], &cv[k]);
+        }
+#pragma unroll
+        for (int k = 0; k < RPT; ++k) {
+            const int64_t n = grp * RPT + k;
+            if (n < n_rows) {
+                if constexpr (kBf16) {
+                    ((uint32_t*)out)[n * half + t] = (uint32_t)d2bf(sv[k]) | ((uint32_t)d2bf(cv[k]) << 16);
+                } else {
+                    ((float2*)out)[n * half + t] = make_float2((float)sv[k], (float)cv[k]);
+                }
+            }
         }
     }
 }
 
 // Ring write of the segment-recurrent memory: rows are independent copies of
-// row_bytes each (16-byte multiples); batch b row t of h goes to ring row
-// (dst0 + t) % ring_len. A workgroup copies whole rows (its threads stride
-// over the row's 16-byte chunks), so the row arithmetic is per row.
+// `chunks` 16-byte chunks each; batch b row t of h goes to ring row
+// (dst0 + t) % ring_len. The n * chunks chunks of a batch are numbered
+// row-major; a workgroup moves CPT * 256 consecutive chunks (lane-consecutive,
+// so every wave touches whole cache lines), all loads before the stores.
+constexpr int CPT = 4;
+
 __global__ void __launch_bounds__(256) fifo_kernel(const char* h, int qlen, char* ring, int ring_len, int dst0,
-                                                   int src0, int n, int row_bytes) {
-    const int b = blockIdx.y;
-    const int chunks = row_bytes >> 4;
-    for (int t = blockIdx.x; t < n; t += gridDim.x) {
-        int pr = dst0 + t;
-        pr = pr >= ring_len ? pr % ring_len : pr;
-        const u32x4* src = (const u32x4*)(h + ((int64_t)b * qlen + src0 + t) * row_bytes);
-        u32x4* dst = (u32x4*)(ring + ((int64_t)b * ring_len + pr) * row_bytes);
-        for (int w = threadIdx.x; w < chunks; w += blockDim.x) dst[w] = src[w];
+                                                   int src0, uint32_t total, uint32_t chunks, int B) {
+    const uint32_t c0 = blockIdx.x * (256u * CPT) + threadIdx.x;
+    for (int b = blockIdx.y; b < B; b += gridDim.y) {
+        const u32x4* src = (const u32x4*)h + ((int64_t)b * qlen + src0) * chunks;
+        u32x4* dst = (u32x4*)ring + (int64_t)b * ring_len * chunks;
+        u32x4 v[CPT];
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+            const uint32_t c = c0 + 256u * k;
+            if (c < total) v[k] = src[c];
+        }
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+            const uint32_t c = c0 + 256u * k;
+            if (c < total) {
+                const uint32_t t = c / chunks, w = c - t * chunks;
+                uint32_t pr = (uint32_t)dst0 + t;
+                pr = pr >= (uint32_t)ring_len ? pr % (uint32_t)ring_len : pr;
+                dst[(int64_t)pr * chunks + w] = v[k];
+            }
+        }
     }
 }
 }  // namespace
 
 hipError_t launch_relpos(int64_t delta0, int64_t n_rows, int64_t d_model, int64_t clamp_len, double base,
                          int out_bf16, void* out, hipStream_t s) {
-    const int64_t work = (n_rows + RPT - 1) / RPT * (d_model / 2);
-    if (work <= 0) return hipSuccess;
-    const int64_t blocks = (work + 255) / 256;
+    if (n_rows <= 0 || d_model < 2) return hipSuccess;
+    const int64_t half = d_model / 2, groups = (n_rows + RPT - 1) / RPT;
+    const dim3 grid((unsigned)((half + 255) / 256), (unsigned)(groups < 65535 ? groups : 65535));
     (void)hipGetLastError();   // drop a stale error of an earlier runtime call
-    if (out_bf16) hipLaunchKernelGGL(relpos_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, delta0, n_rows, d_model, clamp_len, base, out);
-    else hipLaunchKernelGGL(relpos_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, delta0, n_rows, d_model, clamp_len, base, out);
+    if (out_bf16) hipLaunchKernelGGL(relpos_kernel<true>, grid, dim3(256), 0, s, delta0, n_rows, d_model, clamp_len, base, out);
+    else hipLaunchKernelGGL(relpos_kernel<false>, grid, dim3(256), 0, s, delta0, n_rows, d_model, clamp_len, base, out);
     return hipGetLastError();
 }
 
 hipError_t launch_fifo_write(const void* h, int64_t qlen, void* ring, int64_t ring_len, int64_t dst0, int64_t src0,
                              int64_t n, int64_t B, int64_t row_bytes, hipStream_t s) {
     if (n <= 0 || B <= 0) return hipSuccess;
-    // the callers keep every count below 2^31 (validated on the host)
-    const int blocks = (int)(n < 4096 ? n : 4096);
+    // the callers keep row and batch counts below 2^31 and row_bytes a multiple
+    // of 16 (validated on the host); rows go in pieces of fewer than 2^31 chunks
+    const int64_t chunks = row_bytes / 16;
+    const int64_t rows_per = ((int64_t)1 << 30) / chunks;
     (void)hipGetLastError();
-    hipLaunchKernelGGL(fifo_kernel, dim3((unsigned)blocks, (unsigned)B), dim3(256), 0, s, (const char*)h, (int)qlen,
-                       (char*)ring, (int)ring_len, (int)dst0, (int)src0, (int)n, (int)row_bytes);
-    return hipGetLastError();
+    for (int64_t t0 = 0; t0 < n; t0 += rows_per) {
+        const int64_t nn = n - t0 < rows_per ? n - t0 : rows_per;
+        const int64_t total = nn * chunks;
+        const int64_t blocks = (total + 256 * CPT - 1) / (256 * CPT);
+        hipLaunchKernelGGL(fifo_kernel, dim3((unsigned)blocks, (unsigned)(B < 65535 ? B : 65535)), dim3(256), 0, s,
+                           (const char*)h, (int)qlen, (char*)ring, (int)ring_len, (int)((dst0 + t0) % ring_len),
+                           (int)(src0 + t0), (uint32_t)total, (uint32_t)chunks, (int)B);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace xl

@@ -68,7 +68,16 @@ struct AttnArgs {
     int n_rel;            // distance delta uses row min(delta, n_rel - 1)
     int r_rows;           // rows per head in r (>= n_rel)
     int bias_clamp;
+    // key splits of the bf16 kernel (1: none); with nsplit > 1, part holds
+    // nsplit * B*H*qlen * (d_head + 2) floats of partial results
+    int nsplit = 1;
+    void* part = nullptr;
 };
+
+constexpr int kMaxAttnSplits = 64;
+// the split count the library chooses for a bf16 problem, and its partial bytes
+int attn_bf16_splits(int64_t B, int64_t H, int64_t qlen, int64_t mlen);
+size_t attn_bf16_part_bytes(int64_t B, int64_t H, int64_t qlen, int nsplit);
 
 // fused attention for bf16 operands and d_head 64 (attn_bf16.hip)
 // ev0/ev1 (may be null): events the runtime timestamps at the start and end of
