@@ -96,11 +96,13 @@ typedef struct {
     int32_t dtype;       /* XL_BF16 (d_head 64) or XL_F32 (d_head 8): h, mem,
                             weights, u, v, bias table and every intermediate */
     int32_t out_dtype;   /* XL_F32 or XL_BF16 for the layer output */
-    int32_t attn_splits; /* bf16 fused attention: 0 lets the library choose how
-                            many workgroups share one query tile's keys (it
-                            splits only when the query tiles are too few to
-                            fill the GPU); 1..64 forces that count. Results
-                            agree to rounding for every value. f32: ignored. */
+    int32_t attn_splits; /* bf16 fused attention: how many workgroups may share
+                            one 128-query tile's keys. 0 lets the library
+                            choose (it splits only when the tiles leave compute
+                            units without a second workgroup); 1..64 caps every
+                            tile at that count (and at its number of 32-key
+                            steps). Results agree to rounding for every value.
+                            f32: ignored. */
 } xl_attn_desc;
 
 /* Weights of one layer; all device pointers in desc->dtype. */
@@ -168,9 +170,9 @@ int xl_rel_attn_fwd(const xl_attn_desc* desc, const xl_attn_weights* w,
  * desc->d_model, base, out_dtype are ignored.
  * ws: xl_rel_attn_core_workspace_size(desc) bytes, 256-byte aligned, for the
  * partial results of a key split (may be NULL when that size is 0). With S
- * splits it holds S*B*H*qlen*(d_head+2) floats: per split, the
- * unnormalised output, then (running maximum, sum) per query; a second
- * kernel merges them into attn.
+ * the largest split count of a tile it holds S*B*H*qlen*(d_head+2) floats:
+ * per split, the unnormalised output, then (running maximum, sum) per query;
+ * a second kernel merges them into attn.
  */
 size_t xl_rel_attn_core_workspace_size(const xl_attn_desc* desc);
 int xl_rel_attn_core(const xl_attn_desc* desc, const void* qu, const void* qv,

@@ -82,10 +82,9 @@ int check_desc(const xl_attn_desc* d, int64_t mlen, bool need_dmodel) {
 }
 
 // key splits of the fused attention (bf16 only)
-int splits_of(const xl_attn_desc* d, int64_t mlen) {
-    if (d->dtype != XL_BF16) return 1;
-    if (d->attn_splits > 0) return d->attn_splits;
-    return xl::attn_bf16_splits(d->batch, d->n_head, d->qlen, mlen);
+xl::SplitPlan splits_of(const xl_attn_desc* d, int64_t mlen) {
+    if (d->dtype != XL_BF16) return {0, 1};
+    return xl::attn_bf16_split_plan(d->batch, d->n_head, d->qlen, mlen, d->attn_splits);
 }
 size_t part_bytes_of(const xl_attn_desc* d, int64_t mlen) {
     return d->dtype == XL_BF16 ? xl::attn_bf16_part_bytes(d->batch, d->n_head, d->qlen, splits_of(d, mlen)) : 0;
@@ -133,9 +132,12 @@ int run_core(const xl::AttnArgs& a, bool bf16, int dh, hipStream_t s) {
 }
 
 // The layer forward on a memory that is either a plain [B, mlen, D] tensor
-// (ring_len == mlen, ring_head == 0) or a FIFO ring.
+// (ring_len == mlen, ring_head == 0) or a FIFO ring; fifo_write (may be null)
+// is the ring update, carried out by the output projection's launch (after
+// every read of the ring).
 int layer_forward(const xl_attn_desc* d, const xl_attn_weights* w, const void* h, const void* mem, int64_t mlen,
-                  int64_t ring_len, int64_t ring_head, void* out, void* ws, size_t ws_bytes, hipStream_t s) {
+                  int64_t ring_len, int64_t ring_head, void* out, void* ws, size_t ws_bytes, hipStream_t s,
+                  const xl::RowCopy* fifo_write) {
     xl_ws_layout L;
     fill_layout(d, mlen, &L);
     if (ws_bytes < L.total)
@@ -212,7 +214,9 @@ int layer_forward(const xl_attn_desc* d, const xl_attn_weights* w, const void* h
     a.out = W + L.attn;
     a.B = (int)B; a.H = (int)H; a.qlen = (int)q; a.mlen = (int)mlen; a.klen = (int)klen;
     a.ldv = (int)L.ldv; a.n_rel = (int)L.n_rel; a.r_rows = (int)L.n_rel; a.bias_clamp = (int)(d->bias_clamp >= 0 ? d->bias_clamp : 0);
-    a.nsplit = splits_of(d, mlen);
+    const xl::SplitPlan sp = splits_of(d, mlen);
+    a.split_steps = sp.steps;
+    a.split_max = sp.max;
     a.part = W + L.part;
     int st = run_core(a, bf, (int)dh, s);
     if (st != XL_OK) return st;
@@ -224,7 +228,7 @@ int layer_forward(const xl_attn_desc* d, const xl_attn_weights* w, const void* h
     go.b0 = w->w_o; go.b_split = 1 << 30; go.epi = xl::EPI_OUT; go.out0 = out;
     go.out_bf16 = d->out_dtype == XL_BF16;
     go.H = (int)H; go.dh = (int)dh;
-    if ((e = xl::launch_gemm(go, bf, s)) != hipSuccess) return hip_fail(e, "output projection launch");
+    if ((e = xl::launch_gemm(go, bf, s, fifo_write)) != hipSuccess) return hip_fail(e, "output projection launch");
     return XL_OK;
 }
 
@@ -308,7 +312,7 @@ int xl_rel_attn_fwd(const xl_attn_desc* desc, const xl_attn_weights* w, const vo
         (desc->mlen > 0 && overlaps(out, out_bytes, mem, (size_t)(desc->batch * desc->mlen * desc->d_model) * es)) ||
         overlaps(out, out_bytes, ws, ws_bytes))
         return fail(XL_BAD_SHAPE, "out aliases an input or the workspace");
-    return layer_forward(desc, w, h, mem, desc->mlen, desc->mlen, 0, out, ws, ws_bytes, (hipStream_t)stream);
+    return layer_forward(desc, w, h, mem, desc->mlen, desc->mlen, 0, out, ws, ws_bytes, (hipStream_t)stream, nullptr);
 }
 
 size_t xl_rel_attn_core_workspace_size(const xl_attn_desc* desc) {
@@ -337,7 +341,9 @@ int xl_rel_attn_core(const xl_attn_desc* desc, const void* qu, const void* qv, c
     a.B = (int)desc->batch; a.H = (int)desc->n_head; a.qlen = (int)desc->qlen; a.mlen = (int)desc->mlen;
     a.klen = (int)klen; a.ldv = (int)ldv; a.n_rel = (int)need; a.r_rows = (int)n_rel;
     a.bias_clamp = (int)(desc->bias_clamp >= 0 ? desc->bias_clamp : 0);
-    a.nsplit = splits_of(desc, desc->mlen);
+    const xl::SplitPlan sp = splits_of(desc, desc->mlen);
+    a.split_steps = sp.steps;
+    a.split_max = sp.max;
     const size_t need_ws = part_bytes_of(desc, desc->mlen);
     if (need_ws > 0) {
         if (!ws) return fail(XL_NULL_ARG, "ws is NULL but the split attention needs %zu bytes", need_ws);
@@ -376,17 +382,15 @@ int xl_segment_step(const xl_attn_desc* desc, const xl_attn_weights* w, const vo
     xl_attn_desc d = *desc;
     d.mlen = fifo->len;
     hipStream_t s = (hipStream_t)stream;
-    st = layer_forward(&d, w, h, fifo->buf, fifo->len, fifo->mlen_max, fifo->head, out, ws, ws_bytes, s);
-    if (st != XL_OK) return st;
     // FIFO update: row t of h lands at ring row (head + len + t) % mlen_max;
     // only the last min(qlen, mlen_max) rows survive, so only those are written.
     const int64_t M = fifo->mlen_max, q = desc->qlen;
     const int64_t n_w = q < M ? q : M;
     const int64_t src0 = q - n_w;
     const int64_t dst0 = (fifo->head + fifo->len + src0) % M;
-    hipError_t e = xl::launch_fifo_write(h, q, fifo->buf, M, dst0, src0, n_w, desc->batch,
-                                         desc->d_model * (int64_t)es, s);
-    if (e != hipSuccess) return hip_fail(e, "fifo write launch");
+    const xl::RowCopy cp{h, fifo->buf, q, M, dst0, src0, n_w, desc->batch, desc->d_model * (int64_t)es};
+    st = layer_forward(&d, w, h, fifo->buf, fifo->len, fifo->mlen_max, fifo->head, out, ws, ws_bytes, s, &cp);
+    if (st != XL_OK) return st;
     const int64_t new_len = fifo->len + q < M ? fifo->len + q : M;
     fifo->head = (fifo->head + fifo->len + q - new_len) % M;
     fifo->len = new_len;

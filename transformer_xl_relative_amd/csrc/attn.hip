@@ -88,7 +88,7 @@ __global__ void __launch_bounds__(NW * 64) attn_kernel(AttnArgs a) {
     using OpT = typename std::conditional<BF, bf16x8, float>::type;
     extern __shared__ __attribute__((aligned(256))) char smem[];
 
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = (int)__builtin_amdgcn_workitem_id_x(), lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: per-wave values live in SGPRs
     const int l32 = lane & 31, hf = lane >> 5;
 
@@ -98,8 +98,9 @@ __global__ void __launch_bounds__(NW * 64) attn_kernel(AttnArgs a) {
     // scalar branches)
     const int nbh = a.B * a.H;
     const int nqt = (a.qlen + BQ - 1) / BQ;
-    const int qt = __builtin_amdgcn_readfirstlane(nqt - 1 - (int)(blockIdx.x / nbh));
-    const int bh = __builtin_amdgcn_readfirstlane((int)(blockIdx.x % nbh));
+    const int wg = (int)__builtin_amdgcn_workgroup_id_x();
+    const int qt = __builtin_amdgcn_readfirstlane(nqt - 1 - wg / nbh);
+    const int bh = __builtin_amdgcn_readfirstlane(wg % nbh);
     const int h = __builtin_amdgcn_readfirstlane(bh % a.H);
     const int b = __builtin_amdgcn_readfirstlane(bh / a.H);
     const int i0 = qt * BQ;

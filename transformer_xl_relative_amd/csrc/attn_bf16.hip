@@ -114,6 +114,18 @@ constexpr int OFF_RING = OFF_B + 6 * TILE;
 constexpr int OFF_TBL = OFF_RING + NW * WQ * RROW;
 static_assert(OFF_TBL == 80 * 1024, "two workgroups per CU without the bias table");
 constexpr int INFLIGHT = 3;     // loads of a step that the next step does not read
+constexpr int kCUs = 256;       // compute units of the GPU
+
+// key steps of query tile qt, and the number of workgroups that share them
+__host__ __device__ inline int tile_steps(int qt, int qlen, int mlen) {
+    const int qend = (qt + 1) * BQ < qlen ? (qt + 1) * BQ : qlen;
+    return (mlen + qend + BKY - 1) / BKY;
+}
+__host__ __device__ inline int tile_splits(int ts, int split_steps, int split_max) {
+    if (split_steps <= 0) return 1;
+    const int n = (ts + split_steps - 1) / split_steps;
+    return n < split_max ? n : split_max;
+}
 
 __device__ __forceinline__ int pi_row(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
@@ -142,28 +154,38 @@ __global__ void __launch_bounds__(NT, 2) attn_bf16_kernel(AttnArgs a) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     const uint32_t lds0 = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)smem;
 
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = (int)__builtin_amdgcn_workitem_id_x(), lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hf = lane >> 5;
 
     // ---- work item (wave-uniform values kept in scalar registers)
     const int nbh = a.B * a.H;
     const int nqt = (a.qlen + BQ - 1) / BQ;
-    const int nsplit = a.nsplit;
-    const int per_qt = nbh * nsplit;
-    const int qt = __builtin_amdgcn_readfirstlane(nqt - 1 - (int)(blockIdx.x / per_qt));
-    const int rem = (int)(blockIdx.x % per_qt);
-    const int sp = __builtin_amdgcn_readfirstlane(rem / nbh);
-    const int bh = __builtin_amdgcn_readfirstlane(rem % nbh);
+    // workgroups in order of decreasing query tile, each tile's splits
+    // (split index slower than batch-head) together
+    int qt = nqt - 1, nsplit = 1, widx = (int)__builtin_amdgcn_workgroup_id_x();
+    if (a.split_steps == 0) {
+        qt = nqt - 1 - widx / nbh;
+        widx %= nbh;
+    } else {
+        for (;; --qt) {
+            nsplit = tile_splits(tile_steps(qt, a.qlen, a.mlen), a.split_steps, a.split_max);
+            if (widx < nbh * nsplit || qt == 0) break;
+            widx -= nbh * nsplit;
+        }
+    }
+    qt = __builtin_amdgcn_readfirstlane(qt);
+    nsplit = __builtin_amdgcn_readfirstlane(nsplit);
+    const int sp = __builtin_amdgcn_readfirstlane(widx / nbh);
+    const int bh = __builtin_amdgcn_readfirstlane(widx % nbh);
     const int h = __builtin_amdgcn_readfirstlane(bh % a.H);
     const int b = __builtin_amdgcn_readfirstlane(bh / a.H);
     const int i0 = qt * BQ;
     const int iw = i0 + wave * WQ;
-    const int qend = min(i0 + BQ, a.qlen);
     // key steps of the tile; this workgroup's split covers steps [S0, S1). The
     // loop counts steps from S0 (LDS slots and ring halves follow that local
     // count); addresses, distances and the mask use the absolute step S0 + s.
-    const int tsteps = (a.mlen + qend + BKY - 1) / BKY;
+    const int tsteps = tile_steps(qt, a.qlen, a.mlen);
     int S0 = 0, S1 = tsteps;
     if (nsplit > 1) {
         const int full = min((a.mlen + i0) / BKY + 1, tsteps);   // steps whose first key all queries see
@@ -536,7 +558,8 @@ __global__ void __launch_bounds__(NT, 2) attn_bf16_kernel(AttnArgs a) {
                     *(f32x4*)(po + 32 * t + 8 * gq + 4 * hf) =
                         (f32x4){o[t][4 * gq], o[t][4 * gq + 1], o[t][4 * gq + 2], o[t][4 * gq + 3]};
             if (hf == 0)
-                *(float2*)((float*)a.part + (int64_t)nsplit * nbh * a.qlen * DH + 2 * prow) = make_float2(m_run, l_tot);
+                *(float2*)((float*)a.part + (int64_t)a.split_max * nbh * a.qlen * DH + 2 * prow) =
+                    make_float2(m_run, l_tot);
         }
         return;
     }
@@ -568,35 +591,41 @@ __global__ void __launch_bounds__(NT, 2) attn_bf16_kernel(AttnArgs a) {
 
 // Merge of the key splits: for query i of head h, with split partials
 // (O_s, m_s, l_s), out = sum_s e^(m_s - M) O_s / sum_s e^(m_s - M) l_s,
-// M = max_s m_s (an empty split has m_s = -inf, l_s = 0, O_s = 0). A thread
-// produces 4 consecutive outputs of one query; the splits are read in groups
-// of MG with all loads of a group in flight together, and the running
-// maximum moves between groups (rescaling the sums).
+// M = max_s m_s (an empty split has m_s = -inf, l_s = 0, O_s = 0). The grid
+// covers the queries from i_first on (the tiles that were split: the split
+// count grows with the tile index); a thread produces 4 consecutive outputs of
+// one query. The splits are read in groups of MG with all loads of a group in
+// flight together, and the running maximum moves between groups.
 constexpr int MG = 16;
 
-__global__ void __launch_bounds__(256) attn_merge_kernel(AttnArgs a) {
-    const int64_t nrow = (int64_t)a.B * a.H * a.qlen;
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+__global__ void __launch_bounds__(256) attn_merge_kernel(AttnArgs a, int i_first) {
+    const int nq = a.qlen - i_first;
+    const int64_t nrow = (int64_t)a.B * a.H * nq;
+    const int64_t idx = (int64_t)__builtin_amdgcn_workgroup_id_x() * 256 + __builtin_amdgcn_workitem_id_x();
     if (idx >= nrow * 16) return;
     const int c = (int)(idx & 15);
-    const int64_t row = idx >> 4;                  // (b*H + h)*qlen + i
+    const int64_t bh = (idx >> 4) / nq;
+    const int i = i_first + (int)((idx >> 4) - bh * nq);
+    const int ns = tile_splits(tile_steps(i / BQ, a.qlen, a.mlen), a.split_steps, a.split_max);
+    if (ns <= 1) return;                            // written by the attention kernel
+    const int64_t row = bh * a.qlen + i, plane = (int64_t)a.B * a.H * a.qlen;
     const f32x4* po = (const f32x4*)a.part + row * (DH / 4) + c;
-    const float2* pml = (const float2*)((const float*)a.part + (int64_t)a.nsplit * nrow * DH) + row;
+    const float2* pml = (const float2*)((const float*)a.part + (int64_t)a.split_max * plane * DH) + row;
     float M = -INFINITY, L = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < a.nsplit; s0 += MG) {
+    for (int s0 = 0; s0 < ns; s0 += MG) {
         float2 ml[MG];
         f32x4 v[MG];
 #pragma unroll
         for (int k = 0; k < MG; ++k) {
-            const int sp = min(s0 + k, a.nsplit - 1);
-            ml[k] = pml[sp * nrow];
-            v[k] = po[sp * nrow * (DH / 4)];
+            const int sp = min(s0 + k, ns - 1);
+            ml[k] = pml[sp * plane];
+            v[k] = po[sp * plane * (DH / 4)];
         }
         float mg = M;
 #pragma unroll
         for (int k = 0; k < MG; ++k)
-            if (s0 + k < a.nsplit) mg = fmaxf(mg, ml[k].x);
+            if (s0 + k < ns) mg = fmaxf(mg, ml[k].x);
         // mg is finite: every query sees a key in some split
         const float mb = mg * LOG2E;
         const float alpha = __builtin_amdgcn_exp2f(fmaf(M, LOG2E, -mb));   // 0 while M = -inf
@@ -605,7 +634,7 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(AttnArgs a) {
         for (int e = 0; e < 4; ++e) acc[e] *= alpha;
 #pragma unroll
         for (int k = 0; k < MG; ++k) {
-            const float wgt = s0 + k < a.nsplit ? __builtin_amdgcn_exp2f(fmaf(ml[k].x, LOG2E, -mb)) : 0.f;
+            const float wgt = s0 + k < ns ? __builtin_amdgcn_exp2f(fmaf(ml[k].x, LOG2E, -mb)) : 0.f;
             L = fmaf(wgt, ml[k].y, L);
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[e] = fmaf(wgt, v[k][e], acc[e]);
@@ -613,7 +642,6 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(AttnArgs a) {
         M = mg;
     }
     const float inv = 1.f / L;
-    const int64_t bh = row / a.qlen, i = row - bh * a.qlen;
     const int64_t b = bh / a.H, h = bh - b * a.H;
     *(u32x2*)((bf16_t*)a.out + (b * a.qlen + i) * ((int64_t)a.H * DH) + h * DH + 4 * c) =
         (u32x2){pack2bf(acc[0] * inv, acc[1] * inv), pack2bf(acc[2] * inv, acc[3] * inv)};
@@ -622,9 +650,17 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(AttnArgs a) {
 template <bool HAS_BIAS>
 hipError_t launch_bf16(const AttnArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     const int nqt = (a.qlen + BQ - 1) / BQ;
-    if (a.nsplit < 1 || a.nsplit > kMaxAttnSplits || (a.nsplit > 1 && !a.part)) return hipErrorInvalidValue;
-    const int64_t grid = (int64_t)a.B * a.H * nqt * a.nsplit;
+    if (a.split_steps < 0 || a.split_max < 1 || a.split_max > kMaxAttnSplits || (a.split_steps > 0 && !a.part))
+        return hipErrorInvalidValue;
+    int64_t grid = 0;
+    int qt_first = nqt;                            // first split tile
+    for (int qt = nqt - 1; qt >= 0; --qt) {
+        const int n = tile_splits(tile_steps(qt, a.qlen, a.mlen), a.split_steps, a.split_max);
+        grid += (int64_t)a.B * a.H * n;
+        if (n > 1) qt_first = qt;
+    }
     if (grid <= 0) return hipSuccess;
+    if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
     int lds = OFF_TBL;
     if (HAS_BIAS) {
         const int gtop_max = a.mlen + (nqt - 1) * BQ + BQ - 1;
@@ -639,7 +675,7 @@ hipError_t launch_bf16(const AttnArgs& a, hipStream_t s, hipEvent_t ev0, hipEven
         attr = 160 * 1024;
     }
     (void)hipGetLastError();   // drop a stale error of an earlier runtime call
-    if (a.nsplit == 1) {
+    if (qt_first == nqt) {
         hipExtLaunchKernelGGL(attn_bf16_kernel<HAS_BIAS>, dim3((unsigned)grid), dim3(NT), (uint32_t)lds, s, ev0, ev1, 0u, a);
         return hipGetLastError();
     }
@@ -648,9 +684,10 @@ hipError_t launch_bf16(const AttnArgs& a, hipStream_t s, hipEvent_t ev0, hipEven
                           (hipEvent_t) nullptr, 0u, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t threads = (int64_t)a.B * a.H * a.qlen * 16;
+    const int i_first = qt_first * BQ;
+    const int64_t threads = (int64_t)a.B * a.H * (a.qlen - i_first) * 16;
     hipExtLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0u, s,
-                          (hipEvent_t) nullptr, ev1, 0u, a);
+                          (hipEvent_t) nullptr, ev1, 0u, a, i_first);
     return hipGetLastError();
 }
 
@@ -660,22 +697,37 @@ hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s, hipEvent_t ev0, hi
     return a.bias ? launch_bf16<true>(a, s, ev0, ev1) : launch_bf16<false>(a, s, ev0, ev1);
 }
 
-int attn_bf16_splits(int64_t B, int64_t H, int64_t qlen, int64_t mlen) {
-    // split only when the query tiles leave most compute units idle: aim at two
-    // workgroups per compute unit, keeping at least four fully visible key
-    // steps per split
-    const int64_t tiles = B * H * ((qlen + BQ - 1) / BQ);
-    constexpr int64_t kCUs = 256;
-    if (tiles >= kCUs) return 1;
-    const int64_t full = mlen / BKY + 1;          // fully visible steps of the first query tile
-    int64_t n = (2 * kCUs + tiles - 1) / tiles;
-    n = n < full / 4 ? n : full / 4;
-    n = n < kMaxAttnSplits ? n : kMaxAttnSplits;
-    return n < 1 ? 1 : (int)n;
+SplitPlan attn_bf16_split_plan(int64_t B, int64_t H, int64_t qlen, int64_t mlen, int forced) {
+    if (forced == 1) return {0, 1};
+    if (forced > 1) return {1, forced};
+    // Split only when the query tiles leave compute units idle (a split's
+    // partial writes and the merge cost more than a second resident workgroup
+    // per compute unit gains). The chosen step count T is the smallest (at
+    // least four steps, so that a split outweighs its fixed cost) whose
+    // workgroups still fit one per compute unit; tiles with more than T steps
+    // are split.
+    constexpr int64_t kSlots = kCUs;
+    const int64_t nbh = B * H, nqt = (qlen + BQ - 1) / BQ;
+    if (nbh * nqt >= kSlots) return {0, 1};
+    const int tmax = tile_steps((int)nqt - 1, (int)qlen, (int)mlen);
+    if (tmax < 8) return {0, 1};
+    int64_t total = 0;
+    for (int qt = 0; qt < nqt; ++qt) total += nbh * tile_steps(qt, (int)qlen, (int)mlen);
+    for (int T = (int)(total / kSlots > 4 ? total / kSlots : 4); T < tmax; ++T) {
+        int64_t w = 0;
+        int mx = 1;
+        for (int qt = 0; qt < nqt; ++qt) {
+            const int n = tile_splits(tile_steps(qt, (int)qlen, (int)mlen), T, kMaxAttnSplits);
+            w += nbh * n;
+            mx = n > mx ? n : mx;
+        }
+        if (w <= kSlots) return mx > 1 ? SplitPlan{T, mx} : SplitPlan{0, 1};
+    }
+    return {0, 1};
 }
 
-size_t attn_bf16_part_bytes(int64_t B, int64_t H, int64_t qlen, int nsplit) {
-    return nsplit > 1 ? (size_t)nsplit * (size_t)(B * H * qlen) * (DH + 2) * sizeof(float) : 0;
+size_t attn_bf16_part_bytes(int64_t B, int64_t H, int64_t qlen, const SplitPlan& p) {
+    return p.steps > 0 ? (size_t)p.max * (size_t)(B * H * qlen) * (DH + 2) * sizeof(float) : 0;
 }
 
 }  // namespace xl

@@ -186,8 +186,8 @@ hipError_t set_lds_attr() {
 
 }  // namespace
 
-hipError_t launch_gemms(const GemmArgs* g, int count, bool bf16, hipStream_t s) {
-    if (bf16) return launch_gemms_bf16(g, count, s);
+hipError_t launch_gemms(const GemmArgs* g, int count, bool bf16, hipStream_t s, const RowCopy* cp) {
+    if (bf16) return launch_gemms_bf16(g, count, s, cp);
     if (count < 1 || count > kMaxGemms) return hipErrorInvalidValue;
     GemmBatch gb;
     gb.count = 0;
@@ -201,13 +201,17 @@ hipError_t launch_gemms(const GemmArgs* g, int count, bool bf16, hipStream_t s) 
         tiles += gb.tiles_n[k] * ((g[i].M + BM - 1) / BM);
     }
     gb.tile_start[gb.count] = tiles;
-    if (tiles == 0) return hipSuccess;
-    hipError_t e = bf16 ? set_lds_attr<bf16_t>() : set_lds_attr<float>();
-    if (e != hipSuccess) return e;
-    (void)hipGetLastError();   // drop a stale error of an earlier runtime call
-    if (bf16) hipLaunchKernelGGL(gemm_kernel<bf16_t>, dim3(tiles), dim3(256), GEMM_LDS, s, gb);
-    else hipLaunchKernelGGL(gemm_kernel<float>, dim3(tiles), dim3(256), GEMM_LDS, s, gb);
-    return hipGetLastError();
+    if (tiles > 0) {
+        hipError_t e = set_lds_attr<float>();
+        if (e != hipSuccess) return e;
+        (void)hipGetLastError();   // drop a stale error of an earlier runtime call
+        hipLaunchKernelGGL(gemm_kernel<float>, dim3(tiles), dim3(256), GEMM_LDS, s, gb);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    // the f32 path copies the rows with a launch of its own
+    return cp ? launch_fifo_write(cp->src, cp->qlen, cp->ring, cp->ring_len, cp->dst0, cp->src0, cp->n, cp->B,
+                                  cp->row_bytes, s)
+              : hipSuccess;
 }
 
 }  // namespace xl

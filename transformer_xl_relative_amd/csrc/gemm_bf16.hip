@@ -367,7 +367,12 @@ __device__ __forceinline__ void tile_bf16(const GemmArgs& g, int m0, int n0, cha
 template <typename T>
 __global__ void __launch_bounds__(T::NT, 1) gemm_bf16_kernel(GemmBatch gb) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];
-    const int tile = blockIdx.x;
+    const int tile = (int)__builtin_amdgcn_workgroup_id_x();
+    // workgroups past the tiles copy rows
+    if (tile >= gb.cp.first_wg) {
+        copy_rows(gb.cp, tile - gb.cp.first_wg, T::NT);
+        return;
+    }
     // the problem of this tile: uniform selects on constant indices
     int k = 0;
     if (gb.count > 1 && tile >= gb.tile_start[1]) k = 1;
@@ -395,7 +400,7 @@ __global__ void __launch_bounds__(T::NT, 1) gemm_bf16_kernel(GemmBatch gb) {
 }
 
 template <typename T>
-hipError_t launch_tiles(const GemmArgs* g, int count, hipStream_t s) {
+hipError_t launch_tiles(const GemmArgs* g, int count, hipStream_t s, const RowCopy* cp) {
     GemmBatch gb;
     gb.count = 0;
     int tiles = 0;
@@ -409,7 +414,28 @@ hipError_t launch_tiles(const GemmArgs* g, int count, hipStream_t s) {
         tiles += (gb.tiles_real[k] + 7) / 8 * 8;     // each problem's range is a multiple of 8
     }
     gb.tile_start[gb.count] = tiles;
-    if (tiles == 0) return hipSuccess;
+    // the row copy: on the compute units the tiles leave idle (one workgroup
+    // per unit at this tile size), else on 32 extra workgroups
+    int copy_wgs = 0;
+    gb.cp = CopyJob{};
+    gb.cp.first_wg = tiles;
+    if (cp && cp->n > 0 && cp->B > 0) {
+        const int64_t rows = cp->B * cp->n;
+        int64_t want = tiles < 256 ? 256 - tiles : 32;
+        want = want > rows ? rows : want;
+        gb.cp.src = (const char*)cp->src;
+        gb.cp.ring = (char*)cp->ring;
+        gb.cp.qlen = (int)cp->qlen;
+        gb.cp.ring_len = (int)cp->ring_len;
+        gb.cp.dst0 = (int)cp->dst0;
+        gb.cp.src0 = (int)cp->src0;
+        gb.cp.n = (int)cp->n;
+        gb.cp.rows = (int)rows;
+        gb.cp.rows_per = (int)((rows + want - 1) / want);
+        gb.cp.chunks = (int)(cp->row_bytes / 16);
+        copy_wgs = (int)((rows + gb.cp.rows_per - 1) / gb.cp.rows_per);
+    }
+    if (tiles + copy_wgs == 0) return hipSuccess;
     static bool attr = false;
     if (!attr) {
         hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<T>,
@@ -418,14 +444,14 @@ hipError_t launch_tiles(const GemmArgs* g, int count, hipStream_t s) {
         attr = true;
     }
     (void)hipGetLastError();   // drop a stale error of an earlier runtime call
-    hipLaunchKernelGGL(gemm_bf16_kernel<T>, dim3(tiles), dim3(T::NT), T::LDS, s, gb);
+    hipLaunchKernelGGL(gemm_bf16_kernel<T>, dim3(tiles + copy_wgs), dim3(T::NT), T::LDS, s, gb);
     return hipGetLastError();
 }
 
 }  // namespace
 
 // Large tiles when they still give most CUs a tile, else 128 x 128 tiles.
-hipError_t launch_gemms_bf16(const GemmArgs* g, int count, hipStream_t s) {
+hipError_t launch_gemms_bf16(const GemmArgs* g, int count, hipStream_t s, const RowCopy* cp) {
     if (count < 1 || count > kMaxGemms) return hipErrorInvalidValue;
     // the epilogues address heads with d_head 64 (the only bf16 head size)
     for (int i = 0; i < count; ++i)
@@ -439,8 +465,10 @@ hipError_t launch_gemms_bf16(const GemmArgs* g, int count, hipStream_t s) {
             big += ((g[i].M + 255) / 256) * ((g[i].N + 255) / 256);
             small += ((g[i].M + 127) / 128) * ((g[i].N + 127) / 128);
         }
-    if (big >= 192) return launch_tiles<Big>(g, count, s);
-    return small > 256 ? launch_tiles<Small2>(g, count, s) : launch_tiles<Small>(g, count, s);
+    if (cp && (cp->row_bytes % 16 || cp->B * cp->n > 0x7FFFFFFF || cp->row_bytes / 16 * (cp->B * cp->n) > 0x7FFFFFFF))
+        return hipErrorInvalidValue;
+    if (big >= 192) return launch_tiles<Big>(g, count, s, cp);
+    return small > 256 ? launch_tiles<Small2>(g, count, s, cp) : launch_tiles<Small>(g, count, s, cp);
 }
 
 }  // namespace xl

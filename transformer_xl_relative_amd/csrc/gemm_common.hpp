@@ -8,13 +8,56 @@
 namespace xl {
 namespace gemm {
 
+// Row copy done by the workgroups after the last tile: rows (b, t), t < n,
+// of src (row b*qlen + src0 + t) go to ring row b*ring_len + (dst0 + t) % ring_len;
+// workgroup w of wgs copies flattened rows [w*rows_per, (w+1)*rows_per).
+struct CopyJob {
+    const char* src;
+    char* ring;
+    int qlen, ring_len, dst0, src0, n, rows, rows_per, chunks;   // chunks: 16-byte pieces per row
+    int first_wg;                // workgroups from this one on copy (past the tiles)
+};
+
 struct GemmBatch {
     GemmArgs p[kMaxGemms];
     int tile_start[kMaxGemms + 1];
     int tiles_n[kMaxGemms];
     int tiles_real[kMaxGemms];   // tiles of a problem (its range in the grid may be padded)
     int count;
+    CopyJob cp;
 };
+
+// The row copy part of workgroup w (nt threads): its rows' 16-byte pieces,
+// eight per thread in flight at a time (all loads before the stores).
+__device__ __forceinline__ void copy_rows(const CopyJob cp, int w, int nt) {
+    const int tid = (int)__builtin_amdgcn_workitem_id_x();
+    const int r0 = w * cp.rows_per;
+    const int r1 = min(r0 + cp.rows_per, cp.rows);
+    if (r1 <= r0) return;
+    const int units = (r1 - r0) * cp.chunks;
+    constexpr int U = 8;
+    for (int u0 = tid; u0 < units; u0 += U * nt) {
+        u32x4 v[U];
+        int64_t doff[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+            const int u = u0 + k * nt;
+            doff[k] = -1;
+            if (u < units) {
+                const int rl = u / cp.chunks, c = u - rl * cp.chunks;
+                const int row = r0 + rl;
+                const int b = row / cp.n, t = row - b * cp.n;
+                int pr = cp.dst0 + t;
+                pr = pr >= cp.ring_len ? pr % cp.ring_len : pr;
+                v[k] = *(const u32x4*)(cp.src + (((int64_t)b * cp.qlen + cp.src0 + t) * cp.chunks + c) * 16);
+                doff[k] = (((int64_t)b * cp.ring_len + pr) * cp.chunks + c) * 16;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < U; ++k)
+            if (doff[k] >= 0) *(u32x4*)(cp.ring + doff[k]) = v[k];
+    }
+}
 
 
 template <typename T>

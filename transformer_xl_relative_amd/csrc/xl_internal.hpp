@@ -49,12 +49,24 @@ struct GemmArgs {
 
 constexpr int kMaxGemms = 4;
 
+// The FIFO ring write (see launch_fifo_write), carried by a GEMM launch whose
+// tiles leave compute units idle: extra workgroups of the same grid copy the
+// rows meanwhile. Nothing the GEMMs read or write may overlap src or ring.
+struct RowCopy {
+    const void* src;
+    void* ring;
+    int64_t qlen, ring_len, dst0, src0, n, B, row_bytes;
+};
+
 // Launch up to kMaxGemms independent projections as one grid (their tiles
-// share the machine). K of every problem must be a multiple of 64 bytes.
-hipError_t launch_gemms(const GemmArgs* g, int count, bool bf16, hipStream_t s);
+// share the machine), and the row copy cp if not null. K of every problem
+// must be a multiple of 64 bytes.
+hipError_t launch_gemms(const GemmArgs* g, int count, bool bf16, hipStream_t s, const RowCopy* cp = nullptr);
 // the bf16 kernels (gemm_bf16.hip); launch_gemms forwards bf16 problems here
-hipError_t launch_gemms_bf16(const GemmArgs* g, int count, hipStream_t s);
-inline hipError_t launch_gemm(const GemmArgs& g, bool bf16, hipStream_t s) { return launch_gemms(&g, 1, bf16, s); }
+hipError_t launch_gemms_bf16(const GemmArgs* g, int count, hipStream_t s, const RowCopy* cp);
+inline hipError_t launch_gemm(const GemmArgs& g, bool bf16, hipStream_t s, const RowCopy* cp = nullptr) {
+    return launch_gemms(&g, 1, bf16, s, cp);
+}
 
 struct AttnArgs {
     const void* qu;
@@ -68,16 +80,22 @@ struct AttnArgs {
     int n_rel;            // distance delta uses row min(delta, n_rel - 1)
     int r_rows;           // rows per head in r (>= n_rel)
     int bias_clamp;
-    // key splits of the bf16 kernel (1: none); with nsplit > 1, part holds
-    // nsplit * B*H*qlen * (d_head + 2) floats of partial results
-    int nsplit = 1;
+    // key splits of the bf16 kernel: a query tile with ts key steps is shared by
+    // min(ceil(ts / split_steps), split_max) workgroups (split_steps 0: none).
+    // part holds split_max * B*H*qlen * (d_head + 2) floats of partial results.
+    int split_steps = 0;
+    int split_max = 1;
     void* part = nullptr;
 };
 
 constexpr int kMaxAttnSplits = 64;
-// the split count the library chooses for a bf16 problem, and its partial bytes
-int attn_bf16_splits(int64_t B, int64_t H, int64_t qlen, int64_t mlen);
-size_t attn_bf16_part_bytes(int64_t B, int64_t H, int64_t qlen, int nsplit);
+// The split plan of a bf16 problem (forced > 0: up to `forced` workgroups per
+// tile), and the bytes of its partial results.
+struct SplitPlan {
+    int steps, max;
+};
+SplitPlan attn_bf16_split_plan(int64_t B, int64_t H, int64_t qlen, int64_t mlen, int forced);
+size_t attn_bf16_part_bytes(int64_t B, int64_t H, int64_t qlen, const SplitPlan& p);
 
 // fused attention for bf16 operands and d_head 64 (attn_bf16.hip)
 // ev0/ev1 (may be null): events the runtime timestamps at the start and end of
