@@ -144,13 +144,12 @@ __device__ __forceinline__ void tile_bf16(const GemmArgs& g, int m0, int n0, cha
         constexpr int U = decltype(u_c)::value;
         // stage kt complete (this wave's loads): later stages already issued may
         // still be in flight
-        if constexpr (NST == 3) {
-            if (kt + 1 < nk) wait_vmcnt<PER>();
-            else wait_vmcnt<0>();
-        } else {
-            static_assert(NST == 2, "stage count");
-            wait_vmcnt<0>();
-        }
+        static_assert(NST >= 2 && NST <= 5, "stage count");
+        const int ahead = min(NST - 2, nk - 1 - kt);    // later stages already issued
+        if (NST >= 5 && ahead == 3) wait_vmcnt<(NST >= 5 ? 3 * PER : 0)>();
+        else if (NST >= 4 && ahead == 2) wait_vmcnt<(NST >= 4 ? 2 * PER : 0)>();
+        else if (NST >= 3 && ahead == 1) wait_vmcnt<(NST >= 3 ? PER : 0)>();
+        else wait_vmcnt<0>();
         // after the barrier every wave's loads of stage kt have landed, and no
         // wave reads stage kt-1 any more, so its slot can be refilled
         __asm__ __volatile__("" ::: "memory");
@@ -180,8 +179,16 @@ __device__ __forceinline__ void tile_bf16(const GemmArgs& g, int m0, int n0, cha
         if (++kt >= nk) break;
         stage_step(I1{}, kt);
         if (++kt >= nk) break;
-        if constexpr (NST == 3) {
+        if constexpr (NST >= 3) {
             stage_step(I2{}, kt);
+            if (++kt >= nk) break;
+        }
+        if constexpr (NST >= 4) {
+            stage_step(std::integral_constant<int, 3>{}, kt);
+            if (++kt >= nk) break;
+        }
+        if constexpr (NST >= 5) {
+            stage_step(std::integral_constant<int, 4>{}, kt);
             if (++kt >= nk) break;
         }
     }
