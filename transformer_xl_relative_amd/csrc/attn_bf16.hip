@@ -161,10 +161,16 @@ __global__ void __launch_bounds__(NT, 2) attn_bf16_kernel(AttnArgs a) {
     // ---- work item (wave-uniform values kept in scalar registers)
     const int nbh = a.B * a.H;
     const int nqt = (a.qlen + BQ - 1) / BQ;
-    // workgroups in order of decreasing query tile, each tile's splits
-    // (split index slower than batch-head) together
+    // workgroups by decreasing query tile (decreasing work), each tile's
+    // splits (split index slower than batch-head) together. Without splits and
+    // with n2 = tiles - 256 in (0, 256], workgroup 256 + i becomes the second
+    // resident of the compute unit that runs workgroup i, so the first n2
+    // workgroups are made the lightest of the heaviest 256: the heaviest tiles
+    // then run alone and the lighter ones in pairs.
     int qt = nqt - 1, nsplit = 1, widx = (int)__builtin_amdgcn_workgroup_id_x();
     if (a.split_steps == 0) {
+        const int n2 = nbh * nqt - kCUs;
+        if (n2 > 0 && n2 <= kCUs) widx = widx < n2 ? widx + kCUs - n2 : (widx < kCUs ? widx - n2 : widx);
         qt = nqt - 1 - widx / nbh;
         widx %= nbh;
     } else {

@@ -52,7 +52,7 @@ using Big = Tile<4, 2, 2, 4, 2>;     // 256 x 256, 8 waves, 2 stages (128 KiB)
 using Small = Tile<2, 2, 2, 2, 3>;   // 128 x 128, 4 waves, 3 stages (96 KiB): one per CU
 using Small2 = Tile<2, 2, 2, 2, 2>;  // 128 x 128, 4 waves, 2 stages (64 KiB): two per CU
 
-template <typename T, bool kRowOut>
+template <typename T, bool kRowOut, bool kHalf>
 __device__ __forceinline__ void tile_bf16(const GemmArgs& g, int m0, int n0, char* smem) {
     constexpr int WTM = T::WTM, WTN = T::WTN, NW = T::NT / 64;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -68,7 +68,7 @@ __device__ __forceinline__ void tile_bf16(const GemmArgs& g, int m0, int n0, cha
     // fragments of those columns are zeroed before they are multiplied, so every
     // stage issues the same load instructions
     const int nk = (g.K + KST - 1) / KST;
-    const bool khalf = (g.K % KST) != 0;
+    const bool khalf = kHalf && (g.K % KST) != 0;   // kHalf: some problem of the launch has such a K
     const bf16_t* asrc[T::NI];
     const bf16_t* bsrc[T::NI];
     int back[T::NI];
@@ -163,11 +163,16 @@ __device__ __forceinline__ void tile_bf16(const GemmArgs& g, int m0, int n0, cha
         for (int kc = 0; kc < KC; ++kc) {
             if (kc + 1 < KC) {
                 load_frags(U, kc + 1, fa[(kc + 1) & 1], fb[(kc + 1) & 1]);
-                if (kc + 1 >= KC / 2 && half) {
+                if constexpr (kHalf) {
+                    if (kc + 1 >= KC / 2 && half) {
 #pragma unroll
-                    for (int j = 0; j < WTN; ++j) fb[(kc + 1) & 1][j] = u32x4{0u, 0u, 0u, 0u};
+                        for (int j = 0; j < WTN; ++j) fb[(kc + 1) & 1][j] = u32x4{0u, 0u, 0u, 0u};
+                    }
                 }
             }
+            // the reads of the next k-step stay ahead of these products (two
+            // register sets), so that their latency hides behind them
+            __builtin_amdgcn_sched_barrier(0);
             compute(fa[kc & 1], fb[kc & 1]);
         }
     };
@@ -371,7 +376,7 @@ __device__ __forceinline__ void tile_bf16(const GemmArgs& g, int m0, int n0, cha
     }
 }
 
-template <typename T>
+template <typename T, bool kHalf>
 __global__ void __launch_bounds__(T::NT, 1) gemm_bf16_kernel(GemmBatch gb) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     const int tile = (int)__builtin_amdgcn_workgroup_id_x();
@@ -402,8 +407,8 @@ __global__ void __launch_bounds__(T::NT, 1) gemm_bf16_kernel(GemmBatch gb) {
     const int tm = tr / tiles_n, tn = tr - tm * tiles_n;
     const int m0 = tm * T::BT, n0 = tn * T::BT;
     const bool col_out = g.epi == EPI_VT || (g.epi == EPI_KV && n0 >= g.b_split);
-    if (col_out) tile_bf16<T, false>(g, m0, n0, smem);
-    else tile_bf16<T, true>(g, m0, n0, smem);
+    if (col_out) tile_bf16<T, false, kHalf>(g, m0, n0, smem);
+    else tile_bf16<T, true, kHalf>(g, m0, n0, smem);
 }
 
 template <typename T>
@@ -443,15 +448,17 @@ hipError_t launch_tiles(const GemmArgs* g, int count, hipStream_t s, const RowCo
         copy_wgs = (int)((rows + gb.cp.rows_per - 1) / gb.cp.rows_per);
     }
     if (tiles + copy_wgs == 0) return hipSuccess;
-    static bool attr = false;
-    if (!attr) {
-        hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<T>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS);
+    bool half = false;
+    for (int i = 0; i < gb.count; ++i) half = half || gb.p[i].K % KST != 0;
+    static bool attr[2] = {false, false};
+    const auto kern = half ? gemm_bf16_kernel<T, true> : gemm_bf16_kernel<T, false>;
+    if (!attr[half]) {
+        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS);
         if (e != hipSuccess) return e;
-        attr = true;
+        attr[half] = true;
     }
     (void)hipGetLastError();   // drop a stale error of an earlier runtime call
-    hipLaunchKernelGGL(gemm_bf16_kernel<T>, dim3(tiles + copy_wgs), dim3(T::NT), T::LDS, s, gb);
+    hipLaunchKernelGGL(kern, dim3(tiles + copy_wgs), dim3(T::NT), T::LDS, s, gb);
     return hipGetLastError();
 }
 
