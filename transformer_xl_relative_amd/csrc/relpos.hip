@@ -12,6 +12,49 @@
 namespace xl {
 namespace {
 
+// sin and cos of x in fp64, for |x| < 2^30 (the library routine beyond).
+// Reduction by pi/2 after Cody and Waite: k = rint(2x/pi), r = x - k pi/2
+// with pi/2 split into three doubles and fused multiply-adds (each product
+// k * part is exact inside the fma), so |r| <= pi/4 up to a rounding of k.
+// Then the Taylor series of sin r and cos r through r^17 and r^18 (the next
+// terms are below 1e-19 on that interval), evaluated by Horner's rule, and the
+// quadrant k mod 4. The constants: pi/2 = 0x1.921fb54442d18p+0
+// + 0x1.1a62633145c07p-54 - 0x1.f1976b7ed8fbcp-110 (to 160 bits), and
+// 2/pi = 0x1.45f306dc9c883p-1; the coefficients are 1/n! with n! exact.
+__device__ __forceinline__ void sincos_f64(double x, double* sp, double* cp) {
+    if (!(fabs(x) < 0x1p30)) {
+        sincos(x, sp, cp);
+        return;
+    }
+    const double k = rint(x * 0x1.45f306dc9c883p-1);
+    double r = fma(-k, 0x1.921fb54442d18p+0, x);
+    r = fma(-k, 0x1.1a62633145c07p-54, r);
+    r = fma(-k, -0x1.f1976b7ed8fbcp-110, r);
+    const double z = r * r;
+    double ps = 1.0 / 355687428096000.0;             // 1/17!
+    ps = fma(ps, z, -1.0 / 1307674368000.0);         // 1/15!
+    ps = fma(ps, z, 1.0 / 6227020800.0);             // 1/13!
+    ps = fma(ps, z, -1.0 / 39916800.0);              // 1/11!
+    ps = fma(ps, z, 1.0 / 362880.0);                 // 1/9!
+    ps = fma(ps, z, -1.0 / 5040.0);                  // 1/7!
+    ps = fma(ps, z, 1.0 / 120.0);                    // 1/5!
+    ps = fma(ps, z, -1.0 / 6.0);                     // 1/3!
+    const double sr = fma(r * z, ps, r);
+    double pc = -1.0 / 6402373705728000.0;           // 1/18!
+    pc = fma(pc, z, 1.0 / 20922789888000.0);         // 1/16!
+    pc = fma(pc, z, -1.0 / 87178291200.0);           // 1/14!
+    pc = fma(pc, z, 1.0 / 479001600.0);              // 1/12!
+    pc = fma(pc, z, -1.0 / 3628800.0);               // 1/10!
+    pc = fma(pc, z, 1.0 / 40320.0);                  // 1/8!
+    pc = fma(pc, z, -1.0 / 720.0);                   // 1/6!
+    pc = fma(pc, z, 1.0 / 24.0);                     // 1/4!
+    pc = fma(pc, z, -0.5);                           // 1/2!
+    const double cr = fma(z, pc, 1.0);
+    const int q = (int)(int64_t)k & 3;
+    *sp = q == 0 ? sr : q == 1 ? cr : q == 2 ? -sr : -cr;
+    *cp = q == 0 ? cr : q == 1 ? -sr : q == 2 ? -cr : sr;
+}
+
 // A thread owns frequency pair t (blockIdx.x * 256 + threadIdx.x) of RPT
 // consecutive rows: the inverse frequency is evaluated once, then the RPT
 // angles and their sin/cos, which are independent, so their latencies overlap.
@@ -32,7 +75,7 @@ __global__ void __launch_bounds__(256) relpos_kernel(int64_t delta0, int64_t n_r
             const int64_t n = min(grp * RPT + k, n_rows - 1);
             int64_t delta = delta0 + n;
             if (clamp_len >= 0) delta = delta < -clamp_len ? -clamp_len : (delta > clamp_len ? clamp_len : delta);
-            sincos((double)delta * inv_freq, &sv[k], &cv[k]);
+            sincos_f64((double)delta * inv_freq, &sv[k], &cv[k]);
         }
 #pragma unroll
         for (int k = 0; k < RPT; ++k) {
