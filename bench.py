@@ -82,9 +82,8 @@ def layer_flops(w, mlen):
 
 def attn_min_bytes(w, mlen):
     """Algorithmic (minimum) HBM bytes of the fused attention: the queries, keys,
-    values and projected table r read once, the output written once. This
-    implementation reads the queries twice (s(q+u) and s(q+v) are stored
-    separately), which the measured traffic shows."""
+    values and projected table r read once, the output written once (the
+    biases u and v, H*d_head each, are not counted)."""
     B, H, dh, q = w.batch, w.n_head, w.d_head, w.qlen
     klen = q + mlen
     n_rel = klen if w.clamp_len < 0 else min(klen, w.clamp_len + 1)
@@ -278,7 +277,7 @@ def core_bench(names, launches, warmup):
         xl.xl_rel_attn_fwd(L.desc, L.weights, gu.dev(t["h"]), gu.dev(t["mem"]), L.out, L.ws)
         lay = L.layout
         B, H, dh, q = w.batch, w.n_head, w.d_head, w.qlen
-        qu, qv = L.ws_view(lay.qu, (B, H, q, dh)), L.ws_view(lay.qv, (B, H, q, dh))
+        qd = L.ws_view(lay.q, (B, H, q, dh))
         k, vt = L.ws_view(lay.k, (B, H, lay.klen, dh)), L.ws_view(lay.vt, (B, H, dh, lay.ldv))
         r = L.ws_view(lay.r, (H, lay.n_rel, dh))
         attn = torch.empty((B, q, H * dh), dtype=torch.bfloat16, device="cuda")
@@ -287,7 +286,7 @@ def core_bench(names, launches, warmup):
         beta = L.weights.bias_table
 
         def run():
-            xl.xl_rel_attn_core(L.desc, qu, qv, k, vt, lay.ldv, r, lay.n_rel, beta, attn, cws)
+            xl.xl_rel_attn_core(L.desc, qd, k, vt, lay.ldv, r, lay.n_rel, L.weights.u, L.weights.v, beta, attn, cws)
 
         out = {"workload": name, "splits": int(nws // (B * H * q * (dh + 2) * 4)) if nws else 1}
         flops = 6.0 * dh * B * H * w.n_valid_pairs()

@@ -121,7 +121,8 @@ typedef struct {
  * Workspace layout of xl_rel_attn_fwd / xl_segment_step: byte offsets
  * (from the workspace base, each 256-byte aligned) of the intermediates the
  * call leaves behind, in desc->dtype:
- *   qu, qv  [B, H, qlen, d_head]  s*(q+u), s*(q+v)   (s = scale)
+ *   q       [B, H, qlen, d_head]  projected queries (u and v are added by the
+ *                                 attention as it loads them)
  *   k       [B, H, klen, d_head]  keys over [memory ; segment]
  *   vt      [B, H, d_head, ldv]   values, transposed; columns >= klen unused
  *   rel     [n_rel, D]            sinusoid rows R_n, n = 0..n_rel-1
@@ -132,7 +133,7 @@ typedef struct {
  * there is no clamp).
  */
 typedef struct {
-    size_t qu, qv, k, vt, rel, r, attn;
+    size_t q, k, vt, rel, r, attn;
     size_t part;             /* split partial results (fp32), 0 bytes unless split */
     size_t total;            /* == xl_rel_attn_workspace_size() */
     int64_t klen, ldv, n_rel;
@@ -148,8 +149,9 @@ int xl_rel_attn_workspace_layout(const xl_attn_desc* desc, xl_ws_layout* layout)
  *   h   [B, qlen, D]  current segment (desc->dtype)
  *   mem [B, mlen, D]  cached memory, oldest first; NULL iff mlen == 0
  *   out [B, qlen, D]  (desc->out_dtype)
- * Steps: sinusoid rows -> r = R W_r^T -> q-projection with s*(q+u), s*(q+v)
- * -> k/v projection of [mem ; h] -> fused relative attention -> W_o.
+ * Steps: sinusoid rows -> r = R W_r^T -> q-projection -> k/v projection of
+ * [mem ; h] -> fused relative attention (scores from s*(q+u) and s*(q+v))
+ * -> W_o.
  * ws must hold xl_rel_attn_workspace_size(desc) bytes, 256-byte aligned.
  */
 int xl_rel_attn_fwd(const xl_attn_desc* desc, const xl_attn_weights* w,
@@ -159,15 +161,18 @@ int xl_rel_attn_fwd(const xl_attn_desc* desc, const xl_attn_weights* w,
 /*
  * The fused attention kernel alone (score, rel-shift, mask, softmax, P.V),
  * on projected operands in desc->dtype, laid out as in xl_ws_layout:
- *   qu, qv [B, H, qlen, d_head]; k [B, H, klen, d_head];
+ *   q [B, H, qlen, d_head] projected queries; k [B, H, klen, d_head];
  *   vt [B, H, d_head, ldv] (ldv >= klen, multiple of 8);
  *   r [H, n_rel, d_head] with row n the projection of distance n, n_rel at
  *     least min(klen, clamp_len + 1) (klen without a clamp); a distance
  *     delta uses row min(delta, C) (C = clamp_len, or klen - 1 unclamped);
+ *   u, v [H, d_head] content and position biases;
  *   bias_table [2*bias_clamp+1, H] or NULL;
  *   attn [B, qlen, H*d_head] output (desc->dtype).
- * The scale is already folded into qu and qv (desc->scale is not used).
- * desc->d_model, base, out_dtype are ignored.
+ * The scores are s*(q_i+u).k_j + s*(q_i+v).r + bias with s = desc->scale
+ * (0 selects 1/sqrt(d_head)); the sums q+u and q+v are rounded to desc->dtype
+ * once, as the kernel loads the queries. desc->d_model, base, out_dtype are
+ * ignored.
  * ws: xl_rel_attn_core_workspace_size(desc) bytes, 256-byte aligned, for the
  * partial results of a key split (may be NULL when that size is 0). With S
  * the largest split count of a tile it holds S*B*H*qlen*(d_head+2) floats:
@@ -175,9 +180,9 @@ int xl_rel_attn_fwd(const xl_attn_desc* desc, const xl_attn_weights* w,
  * a second kernel merges them into attn.
  */
 size_t xl_rel_attn_core_workspace_size(const xl_attn_desc* desc);
-int xl_rel_attn_core(const xl_attn_desc* desc, const void* qu, const void* qv,
-                     const void* k, const void* vt, int64_t ldv, const void* r,
-                     int64_t n_rel, const void* bias_table, void* attn,
+int xl_rel_attn_core(const xl_attn_desc* desc, const void* q, const void* k,
+                     const void* vt, int64_t ldv, const void* r, int64_t n_rel,
+                     const void* u, const void* v, const void* bias_table, void* attn,
                      void* ws, size_t ws_bytes, void* stream);
 
 /* Caller-owned FIFO memory of one layer: a ring of mlen_max rows per

@@ -109,8 +109,7 @@ def test_workspace_size_formula():
         ldv = (klen + 63) // 64 * 64
         n_rel = klen if d.clamp_len < 0 else min(klen, d.clamp_len + 1)
         a = lambda x: (x + 255) // 256 * 256
-        sizes = [B * H * q * dh, B * H * q * dh, B * H * klen * dh, B * H * dh * ldv, n_rel * D, H * n_rel * dh,
-                 B * q * H * dh]
+        sizes = [B * H * q * dh, B * H * klen * dh, B * H * dh * ldv, n_rel * D, H * n_rel * dh, B * q * H * dh]
         # the split attention's partials come last (none for f32 and for the shapes that are not split)
         part = xl.xl_rel_attn_core_workspace_size(d)
         assert lay.part == sum(a(s * es) for s in sizes)
@@ -119,7 +118,7 @@ def test_workspace_size_formula():
             assert part == 0
         assert (lay.klen, lay.ldv, lay.n_rel) == (klen, ldv, n_rel)
         assert xl.xl_rel_attn_workspace_size(d) == lay.total
-        offs = [lay.qu, lay.qv, lay.k, lay.vt, lay.rel, lay.r, lay.attn]
+        offs = [lay.q, lay.k, lay.vt, lay.rel, lay.r, lay.attn]
         assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     assert xl.xl_rel_attn_workspace_size(_desc(d_head=16)) == 0
 
@@ -146,13 +145,15 @@ def test_core_rejects_bad_arguments():
     d = _desc()
     klen = d.qlen + d.mlen
     call = lambda ldv, n_rel, bias=None, desc=d, ws=None, nb=0: lib.xl_rel_attn_core(
-        ctypes.byref(desc), *FAKE[:4], ldv, FAKE[5], n_rel, bias, FAKE[6], ws, nb, None)
+        ctypes.byref(desc), *FAKE[:3], ldv, FAKE[5], n_rel, FAKE[13], FAKE[14], bias, FAKE[6], ws, nb, None)
     assert call(klen - 8, klen) == xl.XL_BAD_SHAPE            # ldv < klen
     assert call(klen + 4, klen) == xl.XL_BAD_SHAPE            # ldv not a multiple of 8
     assert call(klen, klen - 1) == xl.XL_BAD_SHAPE            # r too short
     assert call(klen, klen, desc=_desc(bias_clamp=4)) == xl.XL_NULL_ARG
-    assert lib.xl_rel_attn_core(ctypes.byref(d), None, *FAKE[1:4], klen, FAKE[5], klen, None, FAKE[6],
-                                None, 0, None) == xl.XL_NULL_ARG
+    assert lib.xl_rel_attn_core(ctypes.byref(d), None, *FAKE[1:3], klen, FAKE[5], klen, FAKE[13], FAKE[14], None,
+                                FAKE[6], None, 0, None) == xl.XL_NULL_ARG
+    assert lib.xl_rel_attn_core(ctypes.byref(d), *FAKE[:3], klen, FAKE[5], klen, None, FAKE[14], None,
+                                FAKE[6], None, 0, None) == xl.XL_NULL_ARG      # u missing
     # a split needs its workspace: missing, too small, misaligned, aliasing the output
     ds = _desc(attn_splits=3)
     need = xl.xl_rel_attn_core_workspace_size(ds)

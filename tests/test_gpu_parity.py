@@ -78,7 +78,6 @@ def test_relpos_vs_oracle(T, delta0, n, D, clamp):
 def _check_intermediates(T, L, w, t, batch, qlen, mlen):
     lay = L.layout
     H, dh, D = w.n_head, w.d_head, w.d_model
-    s = 1.0 / np.sqrt(dh)
     h = t["h"].f64[:batch, :qlen]
     mem = t["mem"].f64[:batch, :mlen]
     x = np.concatenate([mem, h], axis=1)
@@ -88,9 +87,7 @@ def _check_intermediates(T, L, w, t, batch, qlen, mlen):
     v = oracle.linear(x, t["w_v"].f64).reshape(batch, klen, H, dh).transpose(0, 2, 1, 3)
     R = oracle.relpos_embed(0, lay.n_rel, D)
     r = oracle.linear(R, t["w_r"].f64).reshape(lay.n_rel, H, dh).transpose(1, 0, 2)
-    u, vb = t["u"].f64, t["v"].f64
-    gu.compare("qu", gu.host64(L.ws_view(lay.qu, (batch, H, qlen, dh))), s * (q + u[None, :, None, :]), dtype=w.dtype)
-    gu.compare("qv", gu.host64(L.ws_view(lay.qv, (batch, H, qlen, dh))), s * (q + vb[None, :, None, :]), dtype=w.dtype)
+    gu.compare("q", gu.host64(L.ws_view(lay.q, (batch, H, qlen, dh))), q, dtype=w.dtype)
     gu.compare("k", gu.host64(L.ws_view(lay.k, (batch, H, klen, dh))), k, dtype=w.dtype)
     vt = gu.host64(L.ws_view(lay.vt, (batch, H, dh, lay.ldv)))[..., :klen]
     gu.compare("vt", vt, v.transpose(0, 1, 3, 2), dtype=w.dtype)
@@ -221,9 +218,7 @@ def test_core_alone(T, dtype, B, H, qlen, mlen, clamp, bias, splits):
     ci = xl_inputs.core_inputs(batch=B, n_head=H, d_head=dh, qlen=qlen, mlen=mlen, n_rows=n_rel, dtype=dtype,
                                seed=B * 100 + qlen, bias_clamp=bias)
     s = 1.0 / np.sqrt(dh)
-    # operands in the kernel's layout: folded query biases, transposed values
-    qu = xl_inputs.Tensor((s * (ci["q"].f64 + ci["u"].f64[None, :, None, :])).astype(np.float32), dtype)
-    qv = xl_inputs.Tensor((s * (ci["q"].f64 + ci["vb"].f64[None, :, None, :])).astype(np.float32), dtype)
+    # operands in the kernel's layout: transposed values
     ldv = (klen + 7) // 8 * 8 + 8
     vt = np.zeros((B, H, dh, ldv), np.float32)
     vt[..., :klen] = ci["v"].f32.transpose(0, 1, 3, 2)
@@ -236,8 +231,8 @@ def test_core_alone(T, dtype, B, H, qlen, mlen, clamp, bias, splits):
     if splits > 1 or (dtype == "bf16" and mlen >= 1600):
         assert nws > 0
     ws = T.empty(nws, dtype=T.uint8, device="cuda") if nws else None
-    xl.xl_rel_attn_core(desc, gu.dev(qu), gu.dev(qv), gu.dev(ci["k"]), gu.dev(vt), ldv, gu.dev(ci["r"]), n_rel,
-                        beta, attn, ws)
+    xl.xl_rel_attn_core(desc, gu.dev(ci["q"]), gu.dev(ci["k"]), gu.dev(vt), ldv, gu.dev(ci["r"]), n_rel,
+                        gu.dev(ci["u"]), gu.dev(ci["vb"]), beta, attn, ws)
     T.cuda.synchronize()
     ref = oracle.rel_attn_core(ci["q"].f64, ci["k"].f64, ci["v"].f64, ci["r"].f64, ci["u"].f64, ci["vb"].f64,
                                scale=s, clamp_len=clamp, beta=ci["beta"].f64 if bias >= 0 else None,

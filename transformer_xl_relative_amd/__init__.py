@@ -33,7 +33,7 @@ class xl_attn_weights(ctypes.Structure):
 
 
 class xl_ws_layout(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_size_t) for n in ("qu", "qv", "k", "vt", "rel", "r", "attn", "part", "total")] + \
+    _fields_ = [(n, ctypes.c_size_t) for n in ("q", "k", "vt", "rel", "r", "attn", "part", "total")] + \
                [("klen", _i64), ("ldv", _i64), ("n_rel", _i64)]
 
 
@@ -87,7 +87,7 @@ def lib():
                                       _p, ctypes.c_size_t, _p]
         L.xl_rel_attn_core_workspace_size.argtypes = [ctypes.POINTER(xl_attn_desc)]
         L.xl_rel_attn_core_workspace_size.restype = ctypes.c_size_t
-        L.xl_rel_attn_core.argtypes = [ctypes.POINTER(xl_attn_desc), _p, _p, _p, _p, _i64, _p, _i64, _p, _p, _p,
+        L.xl_rel_attn_core.argtypes = [ctypes.POINTER(xl_attn_desc), _p, _p, _p, _i64, _p, _i64, _p, _p, _p, _p, _p,
                                        ctypes.c_size_t, _p]
         L.xl_segment_step.argtypes = [ctypes.POINTER(xl_attn_desc), ctypes.POINTER(xl_attn_weights), _p,
                                       ctypes.POINTER(xl_mem_fifo), _p, _p, ctypes.c_size_t, _p]
@@ -174,11 +174,11 @@ def xl_rel_attn_core_workspace_size(desc: xl_attn_desc) -> int:
     return lib().xl_rel_attn_core_workspace_size(ctypes.byref(desc))
 
 
-def xl_rel_attn_core(desc: xl_attn_desc, qu, qv, k, vt, ldv: int, r, n_rel: int, bias_table, attn, ws=None,
+def xl_rel_attn_core(desc: xl_attn_desc, q, k, vt, ldv: int, r, n_rel: int, u, v, bias_table, attn, ws=None,
                      stream=None):
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(lib().xl_rel_attn_core(ctypes.byref(desc), _ptr(qu), _ptr(qv), _ptr(k), _ptr(vt), ldv, _ptr(r), n_rel,
-                                  _ptr(bias_table), _ptr(attn), _ptr(ws), nbytes, _stream(stream)))
+    _check(lib().xl_rel_attn_core(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(vt), ldv, _ptr(r), n_rel, _ptr(u),
+                                  _ptr(v), _ptr(bias_table), _ptr(attn), _ptr(ws), nbytes, _stream(stream)))
     return attn
 
 

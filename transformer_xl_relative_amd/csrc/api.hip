@@ -102,8 +102,7 @@ void fill_layout(const xl_attn_desc* d, int64_t mlen, xl_ws_layout* L) {
     const int64_t n_rel = n_rel_of(d, klen);
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
-    L->qu = take((size_t)(B * H * q * dh) * es);
-    L->qv = take((size_t)(B * H * q * dh) * es);
+    L->q = take((size_t)(B * H * q * dh) * es);
     L->k = take((size_t)(B * H * klen * dh) * es);
     L->vt = take((size_t)(B * H * dh * ldv) * es);
     L->rel = take((size_t)(n_rel * D) * es);
@@ -155,15 +154,14 @@ int layer_forward(const xl_attn_desc* d, const xl_attn_weights* w, const void* h
     e = xl::launch_relpos(0, L.n_rel, D, -1, base, bf ? 1 : 0, W + L.rel, s);
     if (e != hipSuccess) return hip_fail(e, "relpos launch");
 
-    // 2-4. the input projections as one grid: r = R W_r^T, q with the folded
-    // biases, and k, v over [memory ; segment]
+    // 2-4. the input projections as one grid: r = R W_r^T, q, and k, v over
+    // [memory ; segment] (the attention folds u and v into q as it loads it)
     xl::GemmArgs g[4];
     memset(g, 0, sizeof g);
     int ng = 0;
     auto base_args = [&](xl::GemmArgs& a) {
         a.H = (int)H;
         a.dh = (int)dh;
-        a.scale = scale;
         a.b_split = 1 << 30;
     };
     {   // r = R W_r^T -> [H, n_rel, dh]
@@ -173,12 +171,12 @@ int layer_forward(const xl_attn_desc* d, const xl_attn_weights* w, const void* h
         a.a0 = W + L.rel; a.lda = D;
         a.b0 = w->w_r; a.epi = xl::EPI_R; a.out0 = W + L.r; a.seq = (int)L.n_rel;
     }
-    {   // q projection -> qu, qv
+    {   // q projection -> q [B, H, qlen, dh]
         xl::GemmArgs& a = g[ng++];
         base_args(a);
         a.M = (int)(B * q); a.N = (int)HD; a.K = (int)D;
         a.a0 = h; a.lda = D;
-        a.b0 = w->w_q; a.epi = xl::EPI_Q; a.out0 = W + L.qu; a.out1 = W + L.qv; a.bias0 = w->u; a.bias1 = w->v;
+        a.b0 = w->w_q; a.epi = xl::EPI_K; a.out0 = W + L.q;
         a.seq = (int)q;
     }
     auto kv_rows = [&](xl::GemmArgs& a) {
@@ -209,7 +207,8 @@ int layer_forward(const xl_attn_desc* d, const xl_attn_weights* w, const void* h
     if ((e = xl::launch_gemms(g, ng, bf, s)) != hipSuccess) return hip_fail(e, "projection launch");
     // 5. fused relative attention
     xl::AttnArgs a;
-    a.qu = W + L.qu; a.qv = W + L.qv; a.k = W + L.k; a.vt = W + L.vt; a.r = W + L.r;
+    a.q = W + L.q; a.u = w->u; a.v = w->v; a.scale = scale;
+    a.k = W + L.k; a.vt = W + L.vt; a.r = W + L.r;
     a.bias = d->bias_clamp >= 0 ? w->bias_table : nullptr;
     a.out = W + L.attn;
     a.B = (int)B; a.H = (int)H; a.qlen = (int)q; a.mlen = (int)mlen; a.klen = (int)klen;
@@ -320,13 +319,14 @@ size_t xl_rel_attn_core_workspace_size(const xl_attn_desc* desc) {
     return part_bytes_of(desc, desc->mlen);
 }
 
-int xl_rel_attn_core(const xl_attn_desc* desc, const void* qu, const void* qv, const void* k, const void* vt,
-                     int64_t ldv, const void* r, int64_t n_rel, const void* bias_table, void* attn, void* ws,
-                     size_t ws_bytes, void* stream) {
+int xl_rel_attn_core(const xl_attn_desc* desc, const void* q, const void* k, const void* vt, int64_t ldv,
+                     const void* r, int64_t n_rel, const void* u, const void* v, const void* bias_table, void* attn,
+                     void* ws, size_t ws_bytes, void* stream) {
     g_last_error.clear();
     int st = check_desc(desc, desc ? desc->mlen : 0, false);
     if (st != XL_OK) return st;
-    if (!qu || !qv || !k || !vt || !r || !attn) return fail(XL_NULL_ARG, "a core operand is NULL");
+    if (!q || !k || !vt || !r || !u || !v || !attn) return fail(XL_NULL_ARG, "a core operand is NULL");
+    if (!isfinite(desc->scale)) return fail(XL_BAD_SHAPE, "scale must be finite");
     const int64_t klen = desc->mlen + desc->qlen;
     if (ldv < klen || ldv % 8) return fail(XL_BAD_SHAPE, "ldv must be >= klen and a multiple of 8");
     if (ldv > kI32 / 64) return fail(XL_UNSUPPORTED, "ldv too large");
@@ -335,7 +335,9 @@ int xl_rel_attn_core(const xl_attn_desc* desc, const void* qu, const void* qv, c
     if (n_rel > kI32 / 64) return fail(XL_UNSUPPORTED, "r has too many rows");
     if (desc->bias_clamp >= 0 && !bias_table) return fail(XL_NULL_ARG, "bias_clamp >= 0 but bias_table is NULL");
     xl::AttnArgs a;
-    a.qu = qu; a.qv = qv; a.k = k; a.vt = vt; a.r = r;
+    a.q = q; a.u = u; a.v = v;
+    a.scale = desc->scale == 0.f ? (float)(1.0 / sqrt((double)desc->d_head)) : desc->scale;
+    a.k = k; a.vt = vt; a.r = r;
     a.bias = desc->bias_clamp >= 0 ? bias_table : nullptr;
     a.out = attn;
     a.B = (int)desc->batch; a.H = (int)desc->n_head; a.qlen = (int)desc->qlen; a.mlen = (int)desc->mlen;

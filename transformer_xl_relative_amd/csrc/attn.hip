@@ -121,15 +121,29 @@ __global__ void __launch_bounds__(NW * 64) attn_kernel(AttnArgs a) {
     OpT quB[NKC], qvB[NKC];
     {
         const int64_t row = ((int64_t)bh * a.qlen + (qok ? iq : a.qlen - 1)) * DH;
-        const T* qu = (const T*)a.qu + row;
-        const T* qv = (const T*)a.qv + row;
+        const T* qrow = (const T*)a.q + row;
+        const T* ub = (const T*)a.u + h * DH;
+        const T* vbias = (const T*)a.v + h * DH;
+        // the biases fold into the query operands: scale*(q+u), scale*(q+v)
         for (int kc = 0; kc < NKC; ++kc) {
             if constexpr (BF) {
-                quB[kc] = as_bf16x8(*(const u32x4*)(qu + 16 * kc + 8 * hf));
-                qvB[kc] = as_bf16x8(*(const u32x4*)(qv + 16 * kc + 8 * hf));
+                const u32x4 qw = *(const u32x4*)(qrow + 16 * kc + 8 * hf);
+                const u32x4 uw = *(const u32x4*)(ub + 16 * kc + 8 * hf);
+                const u32x4 vw = *(const u32x4*)(vbias + 16 * kc + 8 * hf);
+                u32x4 a_u, a_v;
+                for (int e = 0; e < 4; ++e) {
+                    const float q0 = __uint_as_float(qw[e] << 16), q1 = __uint_as_float(qw[e] & 0xFFFF0000u);
+                    const float u0 = __uint_as_float(uw[e] << 16), u1 = __uint_as_float(uw[e] & 0xFFFF0000u);
+                    const float v0 = __uint_as_float(vw[e] << 16), v1 = __uint_as_float(vw[e] & 0xFFFF0000u);
+                    a_u[e] = pack2bf(a.scale * (q0 + u0), a.scale * (q1 + u1));
+                    a_v[e] = pack2bf(a.scale * (q0 + v0), a.scale * (q1 + v1));
+                }
+                quB[kc] = as_bf16x8(a_u);
+                qvB[kc] = as_bf16x8(a_v);
             } else {
-                quB[kc] = Elem<T>::to_f(qu[2 * kc + hf]);
-                qvB[kc] = Elem<T>::to_f(qv[2 * kc + hf]);
+                const float qe = Elem<T>::to_f(qrow[2 * kc + hf]);
+                quB[kc] = a.scale * (qe + Elem<T>::to_f(ub[2 * kc + hf]));
+                qvB[kc] = a.scale * (qe + Elem<T>::to_f(vbias[2 * kc + hf]));
             }
         }
     }

@@ -263,12 +263,26 @@ __global__ void __launch_bounds__(NT, 2) attn_bf16_kernel(AttnArgs a) {
     bf16x8 quB[4], qvB[4];
     {
         const int64_t row = ((int64_t)bh * a.qlen + (qok ? iq : a.qlen - 1)) * DH;
-        const bf16_t* qu = (const bf16_t*)a.qu + row;
-        const bf16_t* qv = (const bf16_t*)a.qv + row;
+        const bf16_t* qrow = (const bf16_t*)a.q + row;
+        const bf16_t* ub = (const bf16_t*)a.u + h * DH;
+        const bf16_t* vbias = (const bf16_t*)a.v + h * DH;
+        // the biases fold into the query operands: scale*(q+u), scale*(q+v)
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
-            quB[kc] = as_bf16x8(*(const u32x4*)(qu + 16 * kc + 8 * hf));
-            qvB[kc] = as_bf16x8(*(const u32x4*)(qv + 16 * kc + 8 * hf));
+            const u32x4 qw = *(const u32x4*)(qrow + 16 * kc + 8 * hf);
+            const u32x4 uw = *(const u32x4*)(ub + 16 * kc + 8 * hf);
+            const u32x4 vw = *(const u32x4*)(vbias + 16 * kc + 8 * hf);
+            u32x4 a_u, a_v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float q0 = __uint_as_float(qw[e] << 16), q1 = __uint_as_float(qw[e] & 0xFFFF0000u);
+                const float u0 = __uint_as_float(uw[e] << 16), u1 = __uint_as_float(uw[e] & 0xFFFF0000u);
+                const float v0 = __uint_as_float(vw[e] << 16), v1 = __uint_as_float(vw[e] & 0xFFFF0000u);
+                a_u[e] = pack2bf(a.scale * (q0 + u0), a.scale * (q1 + u1));
+                a_v[e] = pack2bf(a.scale * (q0 + v0), a.scale * (q1 + v1));
+            }
+            quB[kc] = as_bf16x8(a_u);
+            qvB[kc] = as_bf16x8(a_v);
         }
     }
     // position blocks 0..2 of this wave come straight from global memory

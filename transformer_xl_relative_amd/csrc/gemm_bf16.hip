@@ -224,68 +224,6 @@ __device__ __forceinline__ void tile_bf16(const GemmArgs& g, int m0, int n0, cha
         int ncols = g.N;
         if (epi == EPI_KV) { epi = EPI_K; ncols = g.b_split; }   // row-output tiles of K|V are K tiles
         const int64_t headstride = (int64_t)g.seq * 64;
-        if (epi == EPI_Q) {
-            // q+u and q+v from one fp32 staging of 32 rows x 64 columns at a time;
-            // the fold happens on the fp32 products, rounded once
-            constexpr int QP = 64 * 4 + 16;        // bytes per staged fp32 row
-            static_assert(NW * 32 * QP <= T::LDS, "epilogue staging fits in LDS");
-            const uint32_t qbuf = lds0 + (uint32_t)(wave * 32 * QP);
-            const int qch = lane & 7, qrl = lane >> 3;           // chunk of 8 columns, first row
-            const float sc = g.scale;
-#pragma unroll
-            for (int jh = 0; jh < WTN / 2; ++jh) {
-                const int n = nw + 64 * jh + 8 * qch;
-                const bool nok = n < ncols;
-                u32x4 uu = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-                if (nok) {
-                    uu = *(const u32x4*)((const bf16_t*)g.bias0 + n);
-                    vv = *(const u32x4*)((const bf16_t*)g.bias1 + n);
-                }
-                float uf[8], vf[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    uf[e] = bf2f((e & 1) ? (uu[e >> 1] >> 16) : (uu[e >> 1] & 0xFFFF));
-                    vf[e] = bf2f((e & 1) ? (vv[e >> 1] >> 16) : (vv[e >> 1] & 0xFFFF));
-                }
-#pragma unroll
-                for (int i = 0; i < WTM; ++i) {
-#pragma unroll
-                    for (int jj2 = 0; jj2 < 2; ++jj2)
-#pragma unroll
-                        for (int gq = 0; gq < 4; ++gq) {
-                            const int j = 2 * jh + jj2;
-                            const int c = 32 * jj2 + 8 * gq + 4 * hf;
-                            *(__attribute__((address_space(3))) f32x4*)(size_t)(qbuf + l32 * QP + c * 4) =
-                                (f32x4){acc[i][j][4 * gq], acc[i][j][4 * gq + 1], acc[i][j][4 * gq + 2],
-                                        acc[i][j][4 * gq + 3]};
-                        }
-                    int m = mw + 32 * i + qrl;
-                    int bb = m / g.seq, jj = m - bb * g.seq;
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        const uint32_t adr = qbuf + (qrl + 8 * k) * QP + qch * 32;
-                        const f32x4 x0 = *(const __attribute__((address_space(3))) f32x4*)(size_t)adr;
-                        const f32x4 x1 = *(const __attribute__((address_space(3))) f32x4*)(size_t)(adr + 16);
-                        if (m < g.M && nok) {
-                            const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-                            u32x4 qa, qb;
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                qa[e] = pack2bf(sc * (x[2 * e] + uf[2 * e]), sc * (x[2 * e + 1] + uf[2 * e + 1]));
-                                qb[e] = pack2bf(sc * (x[2 * e] + vf[2 * e]), sc * (x[2 * e + 1] + vf[2 * e + 1]));
-                            }
-                            const int64_t off = ((int64_t)bb * g.H * g.seq + jj) * 64 + (int64_t)(n >> 6) * headstride + (n & 63);
-                            *(u32x4*)((bf16_t*)g.out0 + off) = qa;
-                            *(u32x4*)((bf16_t*)g.out1 + off) = qb;
-                        }
-                        m += 8;
-                        jj += 8;
-                        while (jj >= g.seq) { jj -= g.seq; ++bb; }
-                    }
-                }
-            }
-            return;
-        }
         const int ch = lane % CPR, rl = lane / CPR;
         const int n = nw + 8 * ch;
         bf16_t* out = (bf16_t*)g.out0;

@@ -145,26 +145,6 @@ __device__ __forceinline__ void store4(const GemmArgs& g, int m, int n, const f3
         const int b = m / g.seq, j = m - b * g.seq;
         off = ((int64_t)(b * g.H + hh) * g.seq + j) * g.dh + d;
     }
-    if (epi == EPI_Q) {
-        const T* u = (const T*)g.bias0 + hh * g.dh + d;
-        const T* vb = (const T*)g.bias1 + hh * g.dh + d;
-        float a[4], c[4];
-        #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            a[e] = g.scale * (v[e] + Elem<T>::to_f(u[e]));
-            c[e] = g.scale * (v[e] + Elem<T>::to_f(vb[e]));
-        }
-        T* o0 = (T*)out + off;
-        T* o1 = (T*)g.out1 + off;
-        if constexpr (BF) {
-            *(u32x2*)o0 = (u32x2){pack2bf(a[0], a[1]), pack2bf(a[2], a[3])};
-            *(u32x2*)o1 = (u32x2){pack2bf(c[0], c[1]), pack2bf(c[2], c[3])};
-        } else {
-            *(f32x4*)o0 = (f32x4){a[0], a[1], a[2], a[3]};
-            *(f32x4*)o1 = (f32x4){c[0], c[1], c[2], c[3]};
-        }
-        return;
-    }
     T* o = (T*)out + off;
     if constexpr (BF) *(u32x2*)o = (u32x2){pack2bf(v[0], v[1]), pack2bf(v[2], v[3])};
     else *(f32x4*)o = (f32x4){v[0], v[1], v[2], v[3]};

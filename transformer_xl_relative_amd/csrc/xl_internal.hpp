@@ -11,8 +11,7 @@ hipError_t launch_relpos(int64_t delta0, int64_t n_rows, int64_t d_model, int64_
 
 // Epilogues of the projection GEMM C = A B^T (A rows: activations, B rows: weights).
 enum EpiKind : int {
-    EPI_Q = 0,    // qu/qv [B,H,seq,dh] = scale*(C + u), scale*(C + v)
-    EPI_K = 1,    // k [B,H,seq,dh]
+    EPI_K = 1,    // q or k [B,H,seq,dh]
     EPI_VT = 2,   // vt [B,H,dh,ldv]
     EPI_R = 3,    // r [H, seq, dh] (seq = n_rel rows)
     EPI_OUT = 4,  // out [M, N] row-major, f32 or bf16
@@ -40,9 +39,6 @@ struct GemmArgs {
     int epi;
     void* out0;
     void* out1;
-    const void* bias0;       // u for EPI_Q
-    const void* bias1;       // v for EPI_Q
-    float scale;
     int H, dh, seq, ldv;
     int out_bf16;            // EPI_OUT: 1 bf16, 0 f32
 };
@@ -69,8 +65,10 @@ inline hipError_t launch_gemm(const GemmArgs& g, bool bf16, hipStream_t s, const
 }
 
 struct AttnArgs {
-    const void* qu;
-    const void* qv;
+    const void* q;        // [B, H, qlen, dh] projected queries
+    const void* u;        // [H, dh] content bias
+    const void* v;        // [H, dh] position bias
+    float scale;          // score scale, applied as scale*(q+u), scale*(q+v)
     const void* k;
     const void* vt;
     const void* r;
