@@ -54,10 +54,10 @@ ATTN_SOURCES = ("transformer_xl_relative_amd/csrc/attn_bf16.hip", "transformer_x
                 "transformer_xl_relative_amd/build.py")
 
 # HBM bytes per launch of the fused attention kernel (calibrated FETCH_SIZE and
-# WRITE_SIZE, see profiles/attn_kernel_<workload>_pmc_traffic.md).
+# WRITE_SIZE, see profiles/attn_bf16_kernel_<workload>_pmc_traffic.md).
 TRAFFIC = {
-    "large_bf16": {"sha256": "b49c3b12f5f7be2f2a713e379ec5a3d215a7094e0885238b86e8d0c1749d6a7d",
-                   "bytes": 45952116, "fetch_bytes": 39660660, "write_bytes": 6291456},
+    "large_bf16": {"sha256": "ca1a7cc03c98891dcc2f7fc94d0a0151cf2a230946880977240c883fb2d9cf12",
+                   "bytes": 39650327, "fetch_bytes": 33358871, "write_bytes": 6291456},
 }
 
 
@@ -333,8 +333,11 @@ def summarize(d, copy_mib):
         print(f"### {os.path.relpath(db, d)}\n")
         if "kernels" in tabs:
             dur = collections.defaultdict(list)
-            for name, gx, wx, st, en in c.execute("select name, grid_x, workgroup_x, start, end from kernels"):
-                dur[(short(name), gx // max(wx, 1))].append((en - st) / 1e3)
+            for name, gx, gy, gz, wx, wy, wz, st, en in c.execute(
+                    "select name, grid_x, grid_y, grid_z, workgroup_x, workgroup_y, workgroup_z, start, end "
+                    "from kernels"):
+                wgs = (gx // max(wx, 1)) * (gy // max(wy, 1)) * (gz // max(wz, 1))
+                dur[(short(name), wgs)].append((en - st) / 1e3)
             if dur:
                 print("| kernel | workgroups | launches | avg us | min us | max us |")
                 print("|---|---|---|---|---|---|")
