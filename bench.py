@@ -21,7 +21,8 @@ above it; the fraction of the bf16 MFMA peak is reported beside it.
   python bench.py --core base_bf16,large_bf16,...  [--launches N]
                   # the fused attention alone (xl_rel_attn_core) per workload, warm and
                   # cold (1 GiB written between launches to evict the caches): one JSON
-                  # line per workload with the median, p10 and p90 kernel times
+                  # line per workload with the median, p10 and p90 kernel times; NAME/tpN
+                  # is one GPU's share (n_head / N heads) under head sharding
   python bench.py --summarize DIR [--copy-calib-mib M]   # markdown summary of rocprofv3 output under DIR
 
 HBM traffic of the attention kernel comes from two rocprofv3 --pmc passes
@@ -126,6 +127,38 @@ def cpu_baseline(w, t, min_seconds=10.0):
             "kind": "oracle",
             "sample": f"{n} full-layer forwards of one batch element (of {w.batch}) of {w.name}, "
                       f"fp64, {el:.1f} s wall"}
+
+
+def cpu_baseline_core(w, t, min_seconds=10.0):
+    """The oracle's attention core alone (the four dots per pair, softmax, P.V)
+    on one batch element's projected operands, repeated until min_seconds; the
+    projections are computed once, outside the timing."""
+    import numpy as np
+    import oracle
+    H, dh, q, m = w.n_head, w.d_head, w.qlen, w.mlen
+    h, mem = t["h"].f64[:1], t["mem"].f64[:1]
+    x = np.concatenate([mem, h], axis=1)
+    heads = lambda a, n: a.reshape(1, n, H, dh).transpose(0, 2, 1, 3).copy()
+    qh = heads(oracle.linear(h, t["w_q"].f64), q)
+    kh = heads(oracle.linear(x, t["w_k"].f64), m + q)
+    vh = heads(oracle.linear(x, t["w_v"].f64), m + q)
+    n_rel = (m + q) if w.clamp_len < 0 else min(m + q, w.clamp_len + 1)
+    rt = oracle.linear(oracle.relpos_embed(0, n_rel, w.d_model), t["w_r"].f64).reshape(n_rel, H, dh)
+    rt = rt.transpose(1, 0, 2).copy()
+    beta = t["beta"].f64 if "beta" in t else None
+    n, t0 = 0, time.perf_counter()
+    while True:
+        oracle.rel_attn_core(qh, kh, vh, rt, t["u"].f64, t["v"].f64, scale=1.0 / np.sqrt(dh),
+                             clamp_len=w.clamp_len, beta=beta, bias_clamp=w.bias_clamp)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    flops = 6.0 * dh * H * w.n_valid_pairs()
+    return {"value": round(flops * n / el / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{n} attention cores (four explicit dots per pair, softmax, P.V) of one batch element "
+                      f"(of {w.batch}) of {w.name}, fp64, {el:.1f} s wall"}
 
 
 def main():
@@ -250,6 +283,10 @@ def main():
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(w, t)
         res["gpu_over_cpu"] = round(value / res["cpu_baseline"]["value"], 1)
+        # the fused attention alone against the oracle's core alone
+        res["cpu_baseline_core"] = cpu_baseline_core(w, t)
+        core_tflops = attn_flops / (core_avg_ms * 1e-3) / 1e12
+        res["gpu_over_cpu_core"] = round(core_tflops / res["cpu_baseline_core"]["value"], 1)
     print(json.dumps(res), flush=True)
 
 
@@ -267,7 +304,13 @@ def core_bench(names, launches, warmup):
 
     scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     for name in names:
-        w = xl_inputs.WORKLOADS[name]
+        # "NAME/tpN": one GPU's share when the heads are sharded over N GPUs
+        base, _, tp = name.partition("/tp")
+        w = xl_inputs.WORKLOADS[base]
+        if tp:
+            if w.n_head % int(tp):
+                raise SystemExit(f"{name}: {w.n_head} heads do not split over {tp} GPUs")
+            w = dataclass_replace(w, n_head=w.n_head // int(tp))
         if w.dtype != "bf16":
             raise SystemExit("--core measures the bf16 workloads")
         if w.segments > 1:
