@@ -208,6 +208,37 @@ typedef struct {
 int xl_segment_step(const xl_attn_desc* desc, const xl_attn_weights* w, const void* h,
                     xl_mem_fifo* fifo, void* out, void* ws, size_t ws_bytes, void* stream);
 
+/* Caller-owned key ring of one layer, for evaluation with fixed weights: the
+ * projected keys and values of the memory are kept instead of its input
+ * states, so a segment step projects only its own rows (the cache reuse of
+ * intelliparadigm.com §3.2 and felixzhao.cn §2.3.1). Key t of the memory
+ * (0 = oldest, t < len) of batch b, head h is row (head + t) % cap of
+ * k[b, h] and column (head + t) % cap of vt[b, h]. */
+typedef struct {
+    void* k;            /* [B, H, cap, d_head] bf16 */
+    void* vt;           /* [B, H, d_head, cap] bf16 (values, transposed) */
+    int64_t cap;        /* ring rows per head, >= mlen_max + qlen */
+    int64_t mlen_max;   /* memory keys kept, >= 1 */
+    int64_t len;        /* memory keys in use, 0 <= len <= mlen_max */
+    int64_t head;       /* ring row of the oldest memory key */
+} xl_kv_fifo;
+
+/*
+ * One segment step on a key ring: the same layer forward as
+ * xl_segment_step with the memory given by its projected keys and values
+ * (mlen = kv->len; desc->mlen is ignored). The segment's keys and values are
+ * projected into the ring right after the memory keys, the attention runs
+ * over all of them, and on return len and head describe the last
+ * min(len + qlen, mlen_max) keys. For the same inputs the keys and values are
+ * those xl_segment_step computes from the stored states, so the outputs
+ * agree. bf16 only; cap, mlen_max, len, head and qlen must be multiples of
+ * 8 (else XL_UNSUPPORTED). ws: xl_segment_step_kv_workspace_size() of desc
+ * with mlen = kv->len (no k or vt regions: they live in the ring).
+ */
+size_t xl_segment_step_kv_workspace_size(const xl_attn_desc* desc);
+int xl_segment_step_kv(const xl_attn_desc* desc, const xl_attn_weights* w, const void* h,
+                       xl_kv_fifo* kv, void* out, void* ws, size_t ws_bytes, void* stream);
+
 /*
  * Timing hook: when both are non-NULL, the hipEvent_t handles ev_begin/ev_end
  * take the start and end timestamps of the fused attention kernel itself

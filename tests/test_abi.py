@@ -183,6 +183,37 @@ def test_segment_step_rejects_bad_fifo():
     assert (f.len, f.head) == (10, 3)                                           # untouched on error
 
 
+def test_segment_step_kv_rejects_bad_ring():
+    lib = xl.lib()
+    d = _desc(mlen=0)                       # qlen 128
+    w = _weights()
+    K, VT = FAKE[12], FAKE[13]
+
+    def step(kv, desc=d, h=FAKE[8], out=FAKE[10], nb=1 << 40):
+        return lib.xl_segment_step_kv(ctypes.byref(desc), ctypes.byref(w), h,
+                                      ctypes.byref(kv) if kv is not None else None, out, FAKE[11], nb, None)
+    ok = lambda **kw: xl.xl_kv_fifo(**{**dict(k=K, vt=VT, cap=256, mlen_max=128, len=64, head=8), **kw})
+    assert step(None) == xl.XL_NULL_ARG
+    assert step(ok(k=None)) == xl.XL_NULL_ARG
+    assert step(ok(cap=200)) == xl.XL_BAD_SHAPE                 # cap < mlen_max + qlen
+    assert step(ok(len=136)) == xl.XL_BAD_SHAPE                 # len > mlen_max
+    assert step(ok(head=256)) == xl.XL_BAD_SHAPE                # head out of range
+    assert step(ok(head=4)) == xl.XL_UNSUPPORTED                # not a multiple of 8
+    assert step(ok(cap=260)) == xl.XL_UNSUPPORTED
+    assert step(ok(), desc=_desc(mlen=0, qlen=100)) == xl.XL_UNSUPPORTED     # qlen not a multiple of 8
+    assert step(ok(), desc=_desc(mlen=0, dtype=xl.XL_F32, d_head=8, d_model=16)) == xl.XL_UNSUPPORTED
+    assert step(ok(), h=K + 64) == xl.XL_BAD_SHAPE              # h inside the key ring
+    assert step(ok(vt=K + 4096)) == xl.XL_BAD_SHAPE             # the two rings overlap
+    kv = ok()
+    assert step(kv, nb=16) == xl.XL_WORKSPACE_TOO_SMALL
+    assert (kv.len, kv.head) == (64, 8)                          # untouched on error
+    # the ring workspace drops the k and v^T regions of the layer workspace
+    dl = _desc(mlen=64)
+    full, lay = xl.xl_rel_attn_workspace_size(dl), xl.xl_rel_attn_workspace_layout(dl)
+    assert xl.xl_segment_step_kv_workspace_size(dl) == full - (lay.rel - lay.k)
+    assert xl.xl_segment_step_kv_workspace_size(_desc(dtype=xl.XL_F32, d_head=8, d_model=16)) == 0
+
+
 def test_relpos_rejects_bad_arguments():
     lib = xl.lib()
     assert lib.xl_relpos_embed(0, 4, 7, -1, 10000.0, xl.XL_F32, FAKE[0], None) == xl.XL_BAD_SHAPE

@@ -296,3 +296,61 @@ def test_segment_run_full_size_sampled(T):
         gu.compare(f"segment {s} (batch 0)", outs[s][:1], routs[s], dtype="bf16")
         want = xl_inputs.bf16_bits(rmems[s].astype(np.float32))
         assert np.array_equal(gu.bits_u16(mems[s][:1]), want)
+
+
+# --- the same run on a key ring of projected keys and values ----------------------------------
+
+def _segment_run_kv(T, w, t, *, batch, qlen, n_seg, mlen_max, cap, head0=0):
+    import transformer_xl_relative_amd as xl
+    L = gu.Layer(w, t, batch=batch, qlen=qlen, mlen=mlen_max)
+    H, dh, D = w.n_head, w.d_head, w.d_model
+    kr = T.empty((batch, H, cap, dh), dtype=T.bfloat16, device="cuda")
+    vr = T.empty((batch, H, dh, cap), dtype=T.bfloat16, device="cuda")
+    kr.fill_(float("nan"))     # never read before written
+    vr.fill_(float("nan"))
+    kv = xl.xl_kv_fifo(kr.data_ptr(), vr.data_ptr(), cap, mlen_max, 0, head0)
+    ws = T.empty(max(xl.xl_segment_step_kv_workspace_size(L.desc), 1), dtype=T.uint8, device="cuda")
+    hs = gu.dev(t["h"])
+    outs = []
+    for s in range(n_seg):
+        h = hs[:, s * qlen:(s + 1) * qlen].contiguous()
+        out = T.empty((batch, qlen, D), dtype=T.float32, device="cuda")
+        desc = xl.make_desc(batch=batch, d_model=D, n_head=H, d_head=dh, qlen=qlen, mlen=0,
+                            clamp_len=w.clamp_len, bias_clamp=w.bias_clamp, dtype=xl.XL_BF16, out_dtype=xl.XL_F32)
+        xl.xl_segment_step_kv(desc, L.weights, h, kv, out, ws)
+        T.cuda.synchronize()
+        outs.append(out.clone())
+        assert kv.len == min((s + 1) * qlen, mlen_max)
+    return outs
+
+
+@pytest.mark.parametrize("qlen,n_seg,mlen_max,cap,head0", [(128, 4, 128, 256, 0), (64, 5, 200, 272, 16),
+                                                           (40, 6, 96, 144, 136), (64, 6, 256, 320, 0)])
+def test_segment_run_kv_ring(T, qlen, n_seg, mlen_max, cap, head0):
+    # the key ring holds the keys and values the state FIFO path computes from
+    # the stored states, so both runs give the same bits; and both match the oracle
+    import dataclasses
+    w = dataclasses.replace(W["segments_bf16"], qlen=qlen, mlen=mlen_max, segments=n_seg)
+    t = xl_inputs.layer_inputs(w, batch=1, qlen=qlen)
+    ring_outs = _segment_run_kv(T, w, t, batch=1, qlen=qlen, n_seg=n_seg, mlen_max=mlen_max, cap=cap,
+                                head0=head0)
+    outs, _ = _segment_run_gpu(T, w, t, batch=1, qlen=qlen, n_seg=n_seg, mlen_max=mlen_max)
+    wts = {k: t[k].f64 for k in ("w_q", "w_k", "w_v", "w_r", "w_o", "u", "v", "beta")}
+    routs, _ = oracle.segment_run(t["h"].f64, n_seg, qlen, mlen_max, wts, n_head=w.n_head, d_head=w.d_head,
+                                  clamp_len=w.clamp_len, bias_clamp=w.bias_clamp)
+    for s in range(n_seg):
+        got = gu.host64(ring_outs[s])
+        assert np.array_equal(got, outs[s]), f"segment {s}: key ring and state FIFO differ"
+        gu.compare(f"key ring segment {s}", got, routs[s], dtype="bf16")
+
+
+def test_segment_run_kv_ring_full_size(T):
+    # the segmented workload at full size (batch 4, 16 heads, qlen = mlen = 512),
+    # key ring against the state FIFO path, bit for bit
+    w = W["segments_bf16"]
+    t = xl_inputs.layer_inputs(w)
+    ring_outs = _segment_run_kv(T, w, t, batch=w.batch, qlen=w.qlen, n_seg=w.segments, mlen_max=w.mlen,
+                                cap=w.mlen + w.qlen + 64, head0=24)
+    outs, _ = _segment_run_gpu(T, w, t, batch=w.batch, qlen=w.qlen, n_seg=w.segments, mlen_max=w.mlen)
+    for s in range(w.segments):
+        assert np.array_equal(gu.host64(ring_outs[s]), outs[s]), f"segment {s} differs"

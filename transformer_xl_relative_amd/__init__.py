@@ -41,6 +41,10 @@ class xl_mem_fifo(ctypes.Structure):
     _fields_ = [("buf", _p), ("mlen_max", _i64), ("len", _i64), ("head", _i64)]
 
 
+class xl_kv_fifo(ctypes.Structure):
+    _fields_ = [("k", _p), ("vt", _p), ("cap", _i64), ("mlen_max", _i64), ("len", _i64), ("head", _i64)]
+
+
 class XLError(RuntimeError):
     def __init__(self, status: int, detail: str):
         super().__init__(f"{_STATUS.get(status, status)}: {detail}")
@@ -54,8 +58,7 @@ _lib = None
 
 EXPORTS = ("xl_status_string", "xl_last_error", "xl_relpos_embed", "xl_rel_attn_workspace_size",
            "xl_rel_attn_workspace_layout", "xl_rel_attn_fwd", "xl_rel_attn_core_workspace_size", "xl_rel_attn_core",
-           "xl_segment_step",
-           "xl_set_core_events")
+           "xl_segment_step", "xl_segment_step_kv_workspace_size", "xl_segment_step_kv", "xl_set_core_events")
 
 
 def lib():
@@ -92,8 +95,12 @@ def lib():
         L.xl_segment_step.argtypes = [ctypes.POINTER(xl_attn_desc), ctypes.POINTER(xl_attn_weights), _p,
                                       ctypes.POINTER(xl_mem_fifo), _p, _p, ctypes.c_size_t, _p]
         L.xl_set_core_events.argtypes = [_p, _p]
+        L.xl_segment_step_kv_workspace_size.argtypes = [ctypes.POINTER(xl_attn_desc)]
+        L.xl_segment_step_kv_workspace_size.restype = ctypes.c_size_t
+        L.xl_segment_step_kv.argtypes = [ctypes.POINTER(xl_attn_desc), ctypes.POINTER(xl_attn_weights), _p,
+                                         ctypes.POINTER(xl_kv_fifo), _p, _p, ctypes.c_size_t, _p]
         for f in ("xl_relpos_embed", "xl_rel_attn_workspace_layout", "xl_rel_attn_fwd", "xl_rel_attn_core",
-                  "xl_segment_step", "xl_set_core_events"):
+                  "xl_segment_step", "xl_set_core_events", "xl_segment_step_kv"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -186,6 +193,17 @@ def xl_segment_step(desc: xl_attn_desc, weights: Weights, h, fifo: xl_mem_fifo, 
     cw = weights.c() if isinstance(weights, Weights) else weights
     _check(lib().xl_segment_step(ctypes.byref(desc), ctypes.byref(cw), _ptr(h), ctypes.byref(fifo), _ptr(out),
                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return out
+
+
+def xl_segment_step_kv_workspace_size(desc: xl_attn_desc) -> int:
+    return lib().xl_segment_step_kv_workspace_size(ctypes.byref(desc))
+
+
+def xl_segment_step_kv(desc: xl_attn_desc, weights: Weights, h, kv: xl_kv_fifo, out, ws, stream=None):
+    cw = weights.c() if isinstance(weights, Weights) else weights
+    _check(lib().xl_segment_step_kv(ctypes.byref(desc), ctypes.byref(cw), _ptr(h), ctypes.byref(kv), _ptr(out),
+                                    _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
     return out
 
 

@@ -94,7 +94,8 @@ int64_t n_rel_of(const xl_attn_desc* d, int64_t klen) {
     return d->clamp_len < 0 ? klen : (klen < d->clamp_len + 1 ? klen : d->clamp_len + 1);
 }
 
-void fill_layout(const xl_attn_desc* d, int64_t mlen, xl_ws_layout* L) {
+// kv_ring: the keys and values live in the caller's key ring (no k, vt regions)
+void fill_layout(const xl_attn_desc* d, int64_t mlen, xl_ws_layout* L, bool kv_ring = false) {
     const size_t es = esize(d->dtype);
     const int64_t B = d->batch, H = d->n_head, dh = d->d_head, q = d->qlen, D = d->d_model;
     const int64_t klen = mlen + q;
@@ -103,8 +104,8 @@ void fill_layout(const xl_attn_desc* d, int64_t mlen, xl_ws_layout* L) {
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
     L->q = take((size_t)(B * H * q * dh) * es);
-    L->k = take((size_t)(B * H * klen * dh) * es);
-    L->vt = take((size_t)(B * H * dh * ldv) * es);
+    L->k = take(kv_ring ? 0 : (size_t)(B * H * klen * dh) * es);
+    L->vt = take(kv_ring ? 0 : (size_t)(B * H * dh * ldv) * es);
     L->rel = take((size_t)(n_rel * D) * es);
     L->r = take((size_t)(H * n_rel * dh) * es);
     L->attn = take((size_t)(B * q * H * dh) * es);
@@ -133,12 +134,15 @@ int run_core(const xl::AttnArgs& a, bool bf16, int dh, hipStream_t s) {
 // The layer forward on a memory that is either a plain [B, mlen, D] tensor
 // (ring_len == mlen, ring_head == 0) or a FIFO ring; fifo_write (may be null)
 // is the ring update, carried out by the output projection's launch (after
-// every read of the ring).
+// every read of the ring). With kv (not null) the memory is a key ring of
+// projected keys and values instead: only the segment's rows are projected,
+// straight into the ring after the memory keys, and the attention reads all
+// keys from it (mem, ring_len, ring_head unused).
 int layer_forward(const xl_attn_desc* d, const xl_attn_weights* w, const void* h, const void* mem, int64_t mlen,
                   int64_t ring_len, int64_t ring_head, void* out, void* ws, size_t ws_bytes, hipStream_t s,
-                  const xl::RowCopy* fifo_write) {
+                  const xl::RowCopy* fifo_write, const xl_kv_fifo* kv = nullptr) {
     xl_ws_layout L;
-    fill_layout(d, mlen, &L);
+    fill_layout(d, mlen, &L, kv != nullptr);
     if (ws_bytes < L.total)
         return fail(XL_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", ws_bytes, L.total);
     if (((uintptr_t)ws) % kAlign) return fail(XL_UNSUPPORTED, "workspace must be 256-byte aligned");
@@ -179,7 +183,18 @@ int layer_forward(const xl_attn_desc* d, const xl_attn_weights* w, const void* h
         a.b0 = w->w_q; a.epi = xl::EPI_K; a.out0 = W + L.q;
         a.seq = (int)q;
     }
+    void* k_out = kv ? kv->k : (void*)(W + L.k);
+    void* vt_out = kv ? kv->vt : (void*)(W + L.vt);
     auto kv_rows = [&](xl::GemmArgs& a) {
+        if (kv) {
+            // the segment's rows only, into ring rows (head + len + t) mod cap
+            a.M = (int)(B * q); a.K = (int)D;
+            a.a0 = h; a.lda = D; a.a_seq = 0;
+            a.seq = (int)q; a.ldv = (int)kv->cap;
+            a.out_rows = (int)kv->cap;
+            a.out_pos0 = (int)((kv->head + kv->len) % kv->cap);
+            return;
+        }
         a.M = (int)(B * klen); a.K = (int)D;
         a.a0 = mlen ? mem : h; a.a1 = h; a.lda = D;
         a.a0_bstride = ring_len * D; a.a1_bstride = q * D;
@@ -193,26 +208,31 @@ int layer_forward(const xl_attn_desc* d, const xl_attn_weights* w, const void* h
         kv_rows(a);
         a.N = (int)(2 * HD);
         a.b0 = w->w_k; a.b1 = w->w_v; a.b_split = (int)HD;
-        a.epi = xl::EPI_KV; a.out0 = W + L.k; a.out1 = W + L.vt;
+        a.epi = xl::EPI_KV; a.out0 = k_out; a.out1 = vt_out;
     } else {
         xl::GemmArgs& a = g[ng++];
         base_args(a);
         kv_rows(a);
         a.N = (int)HD;
-        a.b0 = w->w_k; a.epi = xl::EPI_K; a.out0 = W + L.k;
+        a.b0 = w->w_k; a.epi = xl::EPI_K; a.out0 = k_out;
         xl::GemmArgs& c = g[ng++];
         c = a;
-        c.b0 = w->w_v; c.epi = xl::EPI_VT; c.out0 = W + L.vt;
+        c.b0 = w->w_v; c.epi = xl::EPI_VT; c.out0 = vt_out;
     }
     if ((e = xl::launch_gemms(g, ng, bf, s)) != hipSuccess) return hip_fail(e, "projection launch");
     // 5. fused relative attention
     xl::AttnArgs a;
     a.q = W + L.q; a.u = w->u; a.v = w->v; a.scale = scale;
-    a.k = W + L.k; a.vt = W + L.vt; a.r = W + L.r;
+    a.k = k_out; a.vt = vt_out; a.r = W + L.r;
     a.bias = d->bias_clamp >= 0 ? w->bias_table : nullptr;
     a.out = W + L.attn;
     a.B = (int)B; a.H = (int)H; a.qlen = (int)q; a.mlen = (int)mlen; a.klen = (int)klen;
     a.ldv = (int)L.ldv; a.n_rel = (int)L.n_rel; a.r_rows = (int)L.n_rel; a.bias_clamp = (int)(d->bias_clamp >= 0 ? d->bias_clamp : 0);
+    if (kv) {
+        a.ldv = (int)kv->cap;
+        a.kv_rows = (int)kv->cap;
+        a.kv_head = (int)kv->head;
+    }
     const xl::SplitPlan sp = splits_of(d, mlen);
     a.split_steps = sp.steps;
     a.split_max = sp.max;
@@ -396,6 +416,53 @@ int xl_segment_step(const xl_attn_desc* desc, const xl_attn_weights* w, const vo
     const int64_t new_len = fifo->len + q < M ? fifo->len + q : M;
     fifo->head = (fifo->head + fifo->len + q - new_len) % M;
     fifo->len = new_len;
+    return XL_OK;
+}
+
+size_t xl_segment_step_kv_workspace_size(const xl_attn_desc* desc) {
+    if (check_desc(desc, desc ? desc->mlen : 0, true) != XL_OK || desc->dtype != XL_BF16) return 0;
+    xl_ws_layout L;
+    fill_layout(desc, desc->mlen, &L, true);
+    return L.total;
+}
+
+int xl_segment_step_kv(const xl_attn_desc* desc, const xl_attn_weights* w, const void* h, xl_kv_fifo* kv,
+                       void* out, void* ws, size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    if (!kv) return fail(XL_NULL_ARG, "kv is NULL");
+    if (!kv->k || !kv->vt) return fail(XL_NULL_ARG, "kv->k and kv->vt must be non-NULL");
+    int st = check_desc(desc, kv->len >= 0 ? kv->len : 0, true);
+    if (st != XL_OK) return st;
+    if (desc->dtype != XL_BF16) return fail(XL_UNSUPPORTED, "the key ring path is bf16 only");
+    const int64_t q = desc->qlen, M = kv->mlen_max, C = kv->cap;
+    if (M < 1 || kv->len < 0 || kv->len > M || kv->head < 0 || kv->head >= C || C < M + q)
+        return fail(XL_BAD_SHAPE, "kv state invalid (cap %lld, mlen_max %lld, len %lld, head %lld, qlen %lld)",
+                    (long long)C, (long long)M, (long long)kv->len, (long long)kv->head, (long long)q);
+    if (C % 8 || M % 8 || q % 8 || kv->len % 8 || kv->head % 8)
+        return fail(XL_UNSUPPORTED, "the key ring needs cap, mlen_max, len, head and qlen multiples of 8");
+    if (C > kI32 / 128) return fail(XL_UNSUPPORTED, "cap too large");
+    if ((st = check_weights(desc, w)) != XL_OK) return st;
+    if (!h || !out || !ws) return fail(XL_NULL_ARG, "h, out and ws must be non-NULL");
+    const size_t es = esize(desc->dtype);
+    const size_t h_bytes = (size_t)(desc->batch * q * desc->d_model) * es;
+    const size_t ring_bytes = (size_t)(desc->batch * desc->n_head * C * desc->d_head) * es;
+    const size_t out_bytes = (size_t)(desc->batch * q * desc->d_model) * esize(desc->out_dtype);
+    if (overlaps(kv->k, ring_bytes, kv->vt, ring_bytes)) return fail(XL_BAD_SHAPE, "kv->k aliases kv->vt");
+    for (const void* p : {kv->k, kv->vt})
+        if (overlaps(p, ring_bytes, h, h_bytes) || overlaps(p, ring_bytes, out, out_bytes) ||
+            overlaps(p, ring_bytes, ws, ws_bytes))
+            return fail(XL_BAD_SHAPE, "the key ring aliases h, out or the workspace");
+    if (overlaps(out, out_bytes, h, h_bytes) || overlaps(out, out_bytes, ws, ws_bytes))
+        return fail(XL_BAD_SHAPE, "out aliases h or the workspace");
+    xl_attn_desc d = *desc;
+    d.mlen = kv->len;
+    st = layer_forward(&d, w, h, nullptr, kv->len, 0, 0, out, ws, ws_bytes, (hipStream_t)stream, nullptr, kv);
+    if (st != XL_OK) return st;
+    // the segment's keys now follow the memory keys; keep the last mlen_max
+    const int64_t total = kv->len + q;
+    const int64_t new_len = total < M ? total : M;
+    kv->head = (kv->head + total - new_len) % C;
+    kv->len = new_len;
     return XL_OK;
 }
 

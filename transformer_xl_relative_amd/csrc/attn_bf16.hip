@@ -149,7 +149,7 @@ __device__ __forceinline__ __attribute__((address_space(3))) void* lds_ptr(uint3
     return (__attribute__((address_space(3))) void*)(size_t)addr;
 }
 
-template <bool HAS_BIAS>
+template <bool HAS_BIAS, bool RING>
 __global__ void __launch_bounds__(NT, 2) attn_bf16_kernel(AttnArgs a) {
     extern __shared__ __attribute__((aligned(1024))) char smem[];
     const uint32_t lds0 = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)smem;
@@ -204,10 +204,15 @@ __global__ void __launch_bounds__(NT, 2) attn_bf16_kernel(AttnArgs a) {
     const int wlast = iw < a.qlen ? a.mlen + min(iw + WQ, a.qlen) - 1 : -1;
     const int wsteps = __builtin_amdgcn_readfirstlane(wlast >= 0 ? max(min(wlast / BKY + 1, S1) - S0, 0) : 0);
 
-    const char* kb = (const char*)a.k + (int64_t)bh * a.klen * (DH * 2);
+    // keys in a ring: key j at ring row (kv_head + j) mod kv_rows (one
+    // conditional subtraction covers every key below klen <= kv_rows)
+    const int krows = RING ? a.kv_rows : a.klen;
+    const int kcap = RING ? a.kv_rows : 0x7FFFFFFF;
+    const int kv_head = RING ? a.kv_head : 0;
+    const char* kb = (const char*)a.k + (int64_t)bh * krows * (DH * 2);
     const char* vb = (const char*)a.vt + (int64_t)bh * DH * a.ldv * 2;
     const char* rb = (const char*)a.r + (int64_t)h * a.r_rows * (DH * 2);
-    const i32x4 krs = make_rsrc(kb, (int64_t)a.klen * (DH * 2));
+    const i32x4 krs = make_rsrc(kb, (int64_t)krows * (DH * 2));
     const i32x4 vrs = make_rsrc(vb, (int64_t)DH * a.ldv * 2);
     const i32x4 rrs = make_rsrc(rb, (int64_t)a.r_rows * (DH * 2));
 
@@ -216,9 +221,11 @@ __global__ void __launch_bounds__(NT, 2) attn_bf16_kernel(AttnArgs a) {
     // V^T tiles: row rho = 16*wave + lane/4 of 64 bytes, stored chunk lane%4
     // holds chunk (lane%4)^((rho>>2)&3).
     const int krho = 8 * wave + (lane >> 3);
-    const int kvoff = krho * 128 + (((lane & 7) ^ ((krho >> 1) & 7)) << 4) + S0 * (BKY * DH * 2);
+    const int kvoff = krho * 128 + (((lane & 7) ^ ((krho >> 1) & 7)) << 4);
+    const int kj0 = BKY * S0 + krho + kv_head;                      // ring row of this lane's key in step 0
     const int vrho = 16 * wave + (lane >> 2);
-    const int vvoff = vrho * a.ldv * 2 + (((lane & 3) ^ ((vrho >> 2) & 3)) << 4) + S0 * (BKY * 2);
+    const int vvoff = vrho * a.ldv * 2;
+    const int vj0 = BKY * S0 + 8 * ((lane & 3) ^ ((vrho >> 2) & 3)) + kv_head;     // first of its 8 keys
     // shared band block g (local) holds distances gs - 32 g - row, gs = mlen + i0 + 127 - 32 S0;
     // wave w's position block beta is band block beta + 3 - w
     const int gtop = a.mlen + i0 + BQ - 1;
@@ -227,12 +234,28 @@ __global__ void __launch_bounds__(NT, 2) attn_bf16_kernel(AttnArgs a) {
 
     // one 16-byte piece per lane; M0 (the LDS destination) is this wave's kilobyte of the slot
     auto dma_k = [&](int s, int slot) __attribute__((always_inline)) {
-        raw_buffer_load_lds(krs, lds_ptr(lds0 + OFF_K + slot * TILE + wave * 1024), 16,
-                            kvoff + s * (BKY * DH * 2), 0, 0, 0);
+        int voff;
+        if constexpr (RING) {
+            int p = kj0 + BKY * s;
+            p -= p >= kcap ? kcap : 0;
+            voff = p * 128 + (kvoff & 127);
+        } else {
+            voff = kvoff + BKY * S0 * 128 + s * (BKY * DH * 2);
+        }
+        raw_buffer_load_lds(krs, lds_ptr(lds0 + OFF_K + slot * TILE + wave * 1024), 16, voff, 0, 0, 0);
     };
+    // (the 8 keys of a piece are consecutive ring columns: kv_head and
+    // kv_rows are multiples of 8)
     auto dma_v = [&](int s, int slot) __attribute__((always_inline)) {
-        raw_buffer_load_lds(vrs, lds_ptr(lds0 + OFF_V + slot * TILE + wave * 1024), 16, vvoff + s * (BKY * 2), 0,
-                            0, 0);
+        int voff;
+        if constexpr (RING) {
+            int p = vj0 + BKY * s;
+            p -= p >= kcap ? kcap : 0;
+            voff = vvoff + 2 * p;
+        } else {
+            voff = vvoff + 2 * vj0 + s * (BKY * 2);
+        }
+        raw_buffer_load_lds(vrs, lds_ptr(lds0 + OFF_V + slot * TILE + wave * 1024), 16, voff, 0, 0, 0);
     };
     auto dma_band = [&](int g, int slot) __attribute__((always_inline)) {
         const int d = min(max(gs - BKY * g - krho, 0), rmax);
@@ -667,7 +690,7 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(AttnArgs a, int i_first
         (u32x2){pack2bf(acc[0] * inv, acc[1] * inv), pack2bf(acc[2] * inv, acc[3] * inv)};
 }
 
-template <bool HAS_BIAS>
+template <bool HAS_BIAS, bool RING>
 hipError_t launch_bf16(const AttnArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     const int nqt = (a.qlen + BQ - 1) / BQ;
     if (a.split_steps < 0 || a.split_max < 1 || a.split_max > kMaxAttnSplits || (a.split_steps > 0 && !a.part))
@@ -689,18 +712,18 @@ hipError_t launch_bf16(const AttnArgs& a, hipStream_t s, hipEvent_t ev0, hipEven
     if (lds > 160 * 1024) return hipErrorInvalidValue;
     static int attr = 0;
     if (lds > attr) {
-        hipError_t e = hipFuncSetAttribute((const void*)attn_bf16_kernel<HAS_BIAS>,
+        hipError_t e = hipFuncSetAttribute((const void*)attn_bf16_kernel<HAS_BIAS, RING>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (e != hipSuccess) return e;
         attr = 160 * 1024;
     }
     (void)hipGetLastError();   // drop a stale error of an earlier runtime call
     if (qt_first == nqt) {
-        hipExtLaunchKernelGGL(attn_bf16_kernel<HAS_BIAS>, dim3((unsigned)grid), dim3(NT), (uint32_t)lds, s, ev0, ev1, 0u, a);
+        hipExtLaunchKernelGGL(attn_bf16_kernel<HAS_BIAS, RING>, dim3((unsigned)grid), dim3(NT), (uint32_t)lds, s, ev0, ev1, 0u, a);
         return hipGetLastError();
     }
     // the events bracket both kernels
-    hipExtLaunchKernelGGL(attn_bf16_kernel<HAS_BIAS>, dim3((unsigned)grid), dim3(NT), (uint32_t)lds, s, ev0,
+    hipExtLaunchKernelGGL(attn_bf16_kernel<HAS_BIAS, RING>, dim3((unsigned)grid), dim3(NT), (uint32_t)lds, s, ev0,
                           (hipEvent_t) nullptr, 0u, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -714,7 +737,9 @@ hipError_t launch_bf16(const AttnArgs& a, hipStream_t s, hipEvent_t ev0, hipEven
 }  // namespace
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-    return a.bias ? launch_bf16<true>(a, s, ev0, ev1) : launch_bf16<false>(a, s, ev0, ev1);
+    if (a.kv_rows > 0)
+        return a.bias ? launch_bf16<true, true>(a, s, ev0, ev1) : launch_bf16<false, true>(a, s, ev0, ev1);
+    return a.bias ? launch_bf16<true, false>(a, s, ev0, ev1) : launch_bf16<false, false>(a, s, ev0, ev1);
 }
 
 SplitPlan attn_bf16_split_plan(int64_t B, int64_t H, int64_t qlen, int64_t mlen, int forced) {

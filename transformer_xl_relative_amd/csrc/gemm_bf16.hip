@@ -223,7 +223,9 @@ __device__ __forceinline__ void tile_bf16(const GemmArgs& g, int m0, int n0, cha
         int epi = g.epi;
         int ncols = g.N;
         if (epi == EPI_KV) { epi = EPI_K; ncols = g.b_split; }   // row-output tiles of K|V are K tiles
-        const int64_t headstride = (int64_t)g.seq * 64;
+        // rows per head of a q/k output; a key ring wraps token j to row (pos0 + j) mod rows
+        const int krows = g.out_rows > 0 ? g.out_rows : g.seq;
+        const int64_t headstride = (int64_t)krows * 64;
         const int ch = lane % CPR, rl = lane / CPR;
         const int n = nw + 8 * ch;
         bf16_t* out = (bf16_t*)g.out0;
@@ -241,6 +243,8 @@ __device__ __forceinline__ void tile_bf16(const GemmArgs& g, int m0, int n0, cha
             int m = mw + 32 * i + rl;
             int bb = 0, jj = 0;
             if (epi == EPI_K) { bb = m / g.seq; jj = m - bb * g.seq; }
+            int jp = jj + g.out_pos0;              // ring row of token jj
+            if (jp >= krows) jp -= krows;
 #pragma unroll
             for (int k = 0; k < 32 / RPI; ++k) {
                 const u32x4 w = lds_ld128(wbuf + (rl + RPI * k) * PITCH + ch * 16);
@@ -256,14 +260,16 @@ __device__ __forceinline__ void tile_bf16(const GemmArgs& g, int m0, int n0, cha
                                                        bf2f(w[3] >> 16)};
                         }
                     } else {
-                        const int64_t rowoff = epi == EPI_R ? (int64_t)m * 64 : ((int64_t)bb * g.H * g.seq + jj) * 64;
+                        const int64_t rowoff = epi == EPI_R ? (int64_t)m * 64 : ((int64_t)bb * g.H * krows + jp) * 64;
                         *(u32x4*)(out + rowoff + (int64_t)(n >> 6) * headstride + (n & 63)) = w;
                     }
                 }
                 m += RPI;
                 if (epi == EPI_K) {
                     jj += RPI;
-                    while (jj >= g.seq) { jj -= g.seq; ++bb; }
+                    jp += RPI;
+                    while (jj >= g.seq) { jj -= g.seq; ++bb; jp = jj + g.out_pos0; }
+                    if (jp >= krows) jp -= krows;
                 }
             }
         }
@@ -289,7 +295,10 @@ __device__ __forceinline__ void tile_bf16(const GemmArgs& g, int m0, int n0, cha
             // copy out: lane -> token chunk t (8 tokens) of columns cl + CPI k
             const int m = mw + 32 * i + 8 * t;     // first of the chunk's 8 tokens
             const int bb = m / g.seq, jj = m - bb * g.seq;
-            const bool whole = m + 7 < g.M && jj + 7 < g.seq && (jj & 7) == 0 && (g.ldv & 7) == 0;
+            // column of token jj: (out_pos0 + jj) mod ldv in a key ring
+            int jc = jj + g.out_pos0;
+            if (jc >= g.ldv) jc -= g.ldv;
+            const bool whole = m + 7 < g.M && jj + 7 < g.seq && (jc & 7) == 0 && jc + 7 < g.ldv && (g.ldv & 7) == 0;
 #pragma unroll
             for (int k = 0; k < TC / CPI; ++k) {
                 const int c = cl + CPI * k;
@@ -297,14 +306,16 @@ __device__ __forceinline__ void tile_bf16(const GemmArgs& g, int m0, int n0, cha
                 const u32x4 w = lds_ld128(wbuf + c * PITCH + t * 16);
                 if (cg >= ncols || m >= g.M) continue;
                 if (whole) {
-                    *(u32x4*)(out + ((int64_t)bb * g.H * 64 + cg) * g.ldv + jj) = w;
+                    *(u32x4*)(out + ((int64_t)bb * g.H * 64 + cg) * g.ldv + jc) = w;
                 } else {
                     int b2 = bb, j2 = jj;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         if (m + e < g.M) {
                             const uint32_t wd = w[e >> 1];
-                            out[((int64_t)b2 * g.H * 64 + cg) * g.ldv + j2] = (bf16_t)((e & 1) ? (wd >> 16) : (wd & 0xFFFF));
+                            int c2 = j2 + g.out_pos0;
+                            if (c2 >= g.ldv) c2 -= g.ldv;
+                            out[((int64_t)b2 * g.H * 64 + cg) * g.ldv + c2] = (bf16_t)((e & 1) ? (wd >> 16) : (wd & 0xFFFF));
                         }
                         if (++j2 == g.seq) { j2 = 0; ++b2; }
                     }

@@ -41,6 +41,12 @@ struct GemmArgs {
     void* out1;
     int H, dh, seq, ldv;
     int out_bf16;            // EPI_OUT: 1 bf16, 0 f32
+    // K and V^T outputs into a key ring (EPI_KV, bf16): token j of a batch
+    // lands at ring row (out_pos0 + j) mod out_rows of its head (k: out_rows
+    // rows per head; V^T: ldv == out_rows columns). out_rows 0: no ring (k has
+    // seq rows per head, token j at row j).
+    int out_rows = 0;
+    int out_pos0 = 0;
 };
 
 constexpr int kMaxGemms = 4;
@@ -77,6 +83,11 @@ struct AttnArgs {
     int B, H, qlen, mlen, klen, ldv;
     int n_rel;            // distance delta uses row min(delta, n_rel - 1)
     int r_rows;           // rows per head in r (>= n_rel)
+    // keys in a ring (bf16 kernel): key j of a head is ring row
+    // (kv_head + j) mod kv_rows of k ([B,H,kv_rows,dh]) and column of vt
+    // (ldv == kv_rows); kv_rows 0: k has klen rows per head, key j at row j
+    int kv_rows = 0;
+    int kv_head = 0;
     int bias_clamp;
     // key splits of the bf16 kernel: a query tile with ts key steps is shared by
     // min(ceil(ts / split_steps), split_max) workgroups (split_steps 0: none).
