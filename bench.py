@@ -70,14 +70,17 @@ def attn_sources_sha():
     return h.hexdigest()
 
 
-def layer_flops(w, mlen):
-    """Algorithmic FLOPs of one layer step: projections + fused attention."""
+def layer_flops(w, mlen, kv_ring=False):
+    """Algorithmic FLOPs of one layer step: projections + fused attention
+    (kv_ring: the keys and values of the memory are kept, so only the
+    segment's rows are projected)."""
     B, D, H, dh, q = w.batch, w.d_model, w.n_head, w.d_head, w.qlen
     HD = H * dh
     klen = q + mlen
     n_rel = klen if w.clamp_len < 0 else min(klen, w.clamp_len + 1)
     attn = 6.0 * dh * B * H * w.n_valid_pairs(mlen)          # (q+u).k, (q+v).r, P.V
-    proj = 2.0 * D * HD * (n_rel + B * q + 2 * B * klen + B * q)   # r, q, k+v, o
+    kv_rows = B * q if kv_ring else B * klen
+    proj = 2.0 * D * HD * (n_rel + B * q + 2 * kv_rows + B * q)   # r, q, k+v, o
     return attn + proj, attn
 
 
@@ -173,6 +176,8 @@ def main():
     ap.add_argument("--summarize", metavar="DIR", help="print a summary of the rocprofv3 databases under DIR")
     ap.add_argument("--core", metavar="WORKLOADS", help="comma-separated workloads: time the fused attention alone")
     ap.add_argument("--launches", type=int, default=100, help="timed launches per --core measurement")
+    ap.add_argument("--kv-ring", action="store_true",
+                    help="step with xl_segment_step_kv (projected keys and values of the memory kept in a ring)")
     args = ap.parse_args()
     if args.summarize:
         summarize(args.summarize, args.copy_calib_mib)
@@ -212,6 +217,26 @@ def main():
     def step():
         xl.xl_segment_step(desc, L.weights, h, fifo, L.out, L.ws, stream)
 
+    if args.kv_ring:
+        # the key ring starts empty and fills with the first steps' keys (a
+        # memory of mlen keys after ceil(mlen / qlen) steps, before the warm-up)
+        if w.qlen % 8 or w.mlen % 8:
+            raise SystemExit("--kv-ring needs qlen and mlen multiples of 8")
+        cap = (w.mlen + w.qlen + 7) // 8 * 8
+        kr = torch.zeros((w.batch, w.n_head, cap, w.d_head), dtype=torch.bfloat16, device="cuda")
+        vr = torch.zeros((w.batch, w.n_head, w.d_head, cap), dtype=torch.bfloat16, device="cuda")
+        kv = xl.xl_kv_fifo(kr.data_ptr(), vr.data_ptr(), cap, w.mlen, 0, 0)
+        kdesc = xl.make_desc(batch=w.batch, d_model=D, n_head=w.n_head, d_head=w.d_head, qlen=w.qlen, mlen=w.mlen,
+                             clamp_len=w.clamp_len, bias_clamp=w.bias_clamp, dtype=xl.XL_BF16,
+                             out_dtype=xl.XL_BF16)
+        kws = torch.empty(xl.xl_segment_step_kv_workspace_size(kdesc), dtype=torch.uint8, device="cuda")
+
+        def step():
+            xl.xl_segment_step_kv(desc, L.weights, h, kv, L.out, kws, stream)
+
+        while kv.len < w.mlen:
+            step()
+
     if args.copy_calib_mib > 0:
         # a plain elementwise copy kernel (int32 -> float32 conversion: reads and
         # writes 4 bytes per element); the runtime's blit copy is not used because
@@ -249,9 +274,9 @@ def main():
     xl.xl_set_core_events(None, None)
     core_ms = np.array([a.elapsed_ms(b) for a, b in evs])
     core_avg_ms = float(core_ms.mean())
-    assert fifo.len == w.mlen
+    assert (kv.len if args.kv_ring else fifo.len) == w.mlen
 
-    flops, attn_flops = layer_flops(w, w.mlen)
+    flops, attn_flops = layer_flops(w, w.mlen, args.kv_ring)
     value = flops / (ms_per_step * 1e-3) / 1e12
     rec = TRAFFIC.get(w.name)
     traffic = rec["bytes"] if rec is not None and rec["sha256"] == attn_sources_sha() else None
@@ -268,9 +293,14 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) activations and memory, N(0,0.02) weights; resident in HBM)",
-        "config": {"workload": f"{w.name}: one segment step (sinusoid, R/Q/K/V projections, fused relative "
-                               f"attention, output projection, FIFO update), batch {w.batch}, d_model {D}, "
-                               f"{w.n_head} heads x {w.d_head}, qlen {w.qlen}, mlen {w.mlen}, causal",
+        "config": {"workload": (f"{w.name}: one segment step (sinusoid, R/Q/K/V projections, fused relative "
+                                f"attention, output projection, FIFO update), batch {w.batch}, d_model {D}, "
+                                f"{w.n_head} heads x {w.d_head}, qlen {w.qlen}, mlen {w.mlen}, causal")
+                               if not args.kv_ring else
+                               (f"{w.name}: one segment step on a key ring (sinusoid, R/Q projections, K/V "
+                                f"projection of the segment's rows only, fused relative attention over the ring, "
+                                f"output projection), batch {w.batch}, d_model {D}, {w.n_head} heads x {w.d_head}, "
+                                f"qlen {w.qlen}, mlen {w.mlen}, causal"),
                    "batch": w.batch, "qlen": w.qlen, "mlen": w.mlen, "d_model": D, "n_head": w.n_head,
                    "d_head": w.d_head, "clamp_len": w.clamp_len, "bias_clamp": w.bias_clamp},
         "roofline": {"kernel": "attn_bf16_kernel (fused relative attention)",

@@ -51,6 +51,7 @@ struct Tile {
 using Big = Tile<4, 2, 2, 4, 2>;     // 256 x 256, 8 waves, 2 stages (128 KiB)
 using Small = Tile<2, 2, 2, 2, 3>;   // 128 x 128, 4 waves, 3 stages (96 KiB): one per CU
 using Small2 = Tile<2, 2, 2, 2, 2>;  // 128 x 128, 4 waves, 2 stages (64 KiB): two per CU
+using Tiny = Tile<2, 2, 1, 1, 8>;    // 64 x 64, 4 waves, 8 stages (128 KiB): seven stages in flight
 
 template <typename T, bool kRowOut, bool kHalf>
 __device__ __forceinline__ void tile_bf16(const GemmArgs& g, int m0, int n0, char* smem) {
@@ -144,12 +145,9 @@ __device__ __forceinline__ void tile_bf16(const GemmArgs& g, int m0, int n0, cha
         constexpr int U = decltype(u_c)::value;
         // stage kt complete (this wave's loads): later stages already issued may
         // still be in flight
-        static_assert(NST >= 2 && NST <= 5, "stage count");
+        static_assert(NST >= 2 && NST <= 8 && (NST - 2) * PER < 64, "stage count");
         const int ahead = min(NST - 2, nk - 1 - kt);    // later stages already issued
-        if (NST >= 5 && ahead == 3) wait_vmcnt<(NST >= 5 ? 3 * PER : 0)>();
-        else if (NST >= 4 && ahead == 2) wait_vmcnt<(NST >= 4 ? 2 * PER : 0)>();
-        else if (NST >= 3 && ahead == 1) wait_vmcnt<(NST >= 3 ? PER : 0)>();
-        else wait_vmcnt<0>();
+        wait_stages<NST - 2, PER>(ahead);
         // after the barrier every wave's loads of stage kt have landed, and no
         // wave reads stage kt-1 any more, so its slot can be refilled
         __asm__ __volatile__("" ::: "memory");
@@ -176,26 +174,16 @@ __device__ __forceinline__ void tile_bf16(const GemmArgs& g, int m0, int n0, cha
             compute(fa[kc & 1], fb[kc & 1]);
         }
     };
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
+    // NST stages per pass, so that every stage index is a constant
     for (int kt = 0;;) {
-        stage_step(I0{}, kt);
-        if (++kt >= nk) break;
-        stage_step(I1{}, kt);
-        if (++kt >= nk) break;
-        if constexpr (NST >= 3) {
-            stage_step(I2{}, kt);
-            if (++kt >= nk) break;
-        }
-        if constexpr (NST >= 4) {
-            stage_step(std::integral_constant<int, 3>{}, kt);
-            if (++kt >= nk) break;
-        }
-        if constexpr (NST >= 5) {
-            stage_step(std::integral_constant<int, 4>{}, kt);
-            if (++kt >= nk) break;
-        }
+        bool done = false;
+        static_for<NST>([&](auto u_c) __attribute__((always_inline)) {
+            if (!done) {
+                stage_step(u_c, kt);
+                done = ++kt >= nk;
+            }
+        });
+        if (done) break;
     }
 
     // ---- epilogue (d_head 64: the head and offset of a column n are n >> 6 and
@@ -421,7 +409,8 @@ hipError_t launch_gemms_bf16(const GemmArgs* g, int count, hipStream_t s, const 
         if (g[i].epi != EPI_OUT && g[i].dh != 64) return hipErrorInvalidValue;
     // 256 x 256 tiles when they nearly fill the machine; else 128 x 128 tiles,
     // with three LDS stages while one workgroup per compute unit suffices and
-    // two stages (two workgroups per compute unit) beyond that
+    // two stages (two workgroups per compute unit) beyond that; 64 x 64 tiles
+    // for small problems
     int big = 0, small = 0;
     for (int i = 0; i < count; ++i)
         if (g[i].M > 0 && g[i].N > 0) {
@@ -431,7 +420,11 @@ hipError_t launch_gemms_bf16(const GemmArgs* g, int count, hipStream_t s, const 
     if (cp && (cp->row_bytes % 16 || cp->B * cp->n > 0x7FFFFFFF || cp->row_bytes / 16 * (cp->B * cp->n) > 0x7FFFFFFF))
         return hipErrorInvalidValue;
     if (big >= 192) return launch_tiles<Big>(g, count, s, cp);
-    return small > 256 ? launch_tiles<Small2>(g, count, s, cp) : launch_tiles<Small>(g, count, s, cp);
+    if (small > 256) return launch_tiles<Small2>(g, count, s, cp);
+    // few tiles: their stage latency, not the machine, sets the time; 64 x 64
+    // tiles with seven stages in flight cut it and fill more compute units
+    if (small < 128) return launch_tiles<Tiny>(g, count, s, cp);
+    return launch_tiles<Small>(g, count, s, cp);
 }
 
 }  // namespace xl

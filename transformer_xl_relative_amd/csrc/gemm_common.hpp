@@ -5,6 +5,8 @@
 #include "xl_common.hpp"
 #include "xl_internal.hpp"
 
+#include <type_traits>
+
 namespace xl {
 namespace gemm {
 
@@ -155,6 +157,27 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// wait until at most ahead * PER vector loads are outstanding, for a runtime
+// ahead in [0, MAXA] (each count is an immediate of its own)
+template <int MAXA, int PER>
+__device__ __forceinline__ void wait_stages(int ahead) {
+    if constexpr (MAXA == 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (ahead >= MAXA) wait_vmcnt<MAXA * PER>();
+        else wait_stages<MAXA - 1, PER>(ahead);
+    }
+}
+
+// f(integral_constant<int, i>) for i = 0 .. N-1, unrolled
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<N, I + 1>(f);
+    }
 }
 
 
