@@ -5,12 +5,13 @@
 // Up to four independent projections run as one grid; each workgroup owns a
 // square output tile of one of them: 256 x 256 (eight waves, 4 x 2, each
 // holding 64 x 128 in 2 x 4 accumulator blocks of 32 x 32; two waves per SIMD)
-// or 128 x 128 (four waves, 2 x 2, each 64 x 64) for grids that the large
-// tile would leave too small.
+// or 128 x 128 (eight waves, 2 x 4, each 64 x 32) for grids that the large
+// tile would leave too small, or 64 x 64 (four waves, each 32 x 32, eight LDS
+// stages) for small problems whose time is set by the latency of each stage.
 //
 // K advances 64 elements (128 bytes, whole cache lines, per operand row) per
 // stage. Operand tiles move from global memory straight into LDS
-// (global_load_lds, 16 bytes per lane) one or two stages ahead; the eight
+// (global_load_lds, 16 bytes per lane) one to seven stages ahead; the eight
 // 16-byte chunks of row r are stored XOR-swizzled by (r >> 1) & 7 so that the
 // MFMA operand reads of 16 consecutive rows fall on 16 distinct bank groups.
 // A wave reads the fragments of the next k-step while the MFMAs of the
@@ -49,8 +50,8 @@ struct Tile {
     static constexpr int NI = BT * (ROWB / 16) / NT;   // loads per thread per operand per stage
 };
 using Big = Tile<4, 2, 2, 4, 2>;     // 256 x 256, 8 waves, 2 stages (128 KiB)
-using Small = Tile<2, 2, 2, 2, 3>;   // 128 x 128, 4 waves, 3 stages (96 KiB): one per CU
-using Small2 = Tile<2, 2, 2, 2, 2>;  // 128 x 128, 4 waves, 2 stages (64 KiB): two per CU
+using Small = Tile<2, 4, 2, 1, 3>;   // 128 x 128, 8 waves (each 64 x 32), 3 stages (96 KiB): one per CU
+using Small2 = Tile<2, 4, 2, 1, 2>;  // 128 x 128, 8 waves, 2 stages (64 KiB): two per CU
 using Tiny = Tile<2, 2, 1, 1, 8>;    // 64 x 64, 4 waves, 8 stages (128 KiB): seven stages in flight
 
 template <typename T, bool kRowOut, bool kHalf>
