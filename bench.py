@@ -57,8 +57,8 @@ ATTN_SOURCES = ("transformer_xl_relative_amd/csrc/attn_bf16.hip", "transformer_x
 # HBM bytes per launch of the fused attention kernel (calibrated FETCH_SIZE and
 # WRITE_SIZE, see profiles/attn_bf16_kernel_<workload>_pmc_traffic.md).
 TRAFFIC = {
-    "large_bf16": {"sha256": "ca1a7cc03c98891dcc2f7fc94d0a0151cf2a230946880977240c883fb2d9cf12",
-                   "bytes": 39650327, "fetch_bytes": 33358871, "write_bytes": 6291456},
+    "large_bf16": {"sha256": "4834d304dbfd63aa89f61ec016548c5b26687fb2e2a1e63bf8510847876194e5",
+                   "bytes": 39633754, "fetch_bytes": 33342298, "write_bytes": 6291456},
 }
 
 
