@@ -29,8 +29,11 @@ def _load():
         lib = ctypes.CDLL(_LIB_PATH)
         lib.orc_relpos_embed.argtypes = [_i64, _i64, _i64, _i64, _dbl, _p]
         lib.orc_linear.argtypes = [_p, _i64, _i64, _p, _i64, _p]
-        lib.orc_rel_attn_core.argtypes = [_i64] * 5 + [_p, _p, _i64, _i64, _dbl] + [_p] * 4 + [_i64, _i64] + [_p] * 6
-        lib.orc_rel_attn_fwd.argtypes = [_i64] * 8 + [_dbl, _dbl] + [_p] * 15
+        lib.orc_rel_attn_core.argtypes = [_i64] * 5 + [_p, _p, _i64, _i64, _i64, _dbl] + [_p] * 4 + [_i64, _i64] + \
+            [_p] * 6
+        lib.orc_rel_attn_fwd.argtypes = [_i64] * 9 + [_dbl, _dbl] + [_p] * 15
+        lib.orc_t5_bucket.argtypes = [_i64]
+        lib.orc_t5_bucket.restype = _i64
         lib.orc_fifo_update.argtypes = [_i64, _i64, _i64, _i64, _p, _i64, _p, _p, ctypes.POINTER(_i64)]
         lib.orc_num_threads.argtypes = []
         lib.orc_num_threads.restype = ctypes.c_int
@@ -61,6 +64,11 @@ def _check(status, what):
         raise OracleError(f"{what} returned status {status}")
 
 
+def t5_bucket(delta: int) -> int:
+    """T5 bucket of a relative distance (12 buckets)."""
+    return int(_load().orc_t5_bucket(int(delta)))
+
+
 def num_threads() -> int:
     """OpenMP threads the oracle uses."""
     return int(_load().orc_num_threads())
@@ -85,11 +93,13 @@ def linear(x, W):
 
 
 def rel_attn_core(q, k, v, rtab, u, vb, *, scale: float, clamp_len: int = -1, rtab_delta0: int = 0,
-                  beta=None, bias_clamp: int = -1, qpos=None, kpos=None,
+                  beta=None, bias_clamp: int = -1, bias_kind: int = 0, qpos=None, kpos=None,
                   want_terms: bool = False, want_probs: bool = False):
     """Attention core on head-major q [B,H,q,dh], k/v [B,H,klen,dh] and a projected
     relative table rtab [H, n, dh] (row n <-> clamped distance rtab_delta0+n).
-    Returns o [B, q, H*dh] (and optionally the four terms [4,B,H,q,klen], probs)."""
+    beta is the scalar bias table: [2*bias_clamp+1, H] rows by clamped distance
+    (bias_kind 0) or [12, H] rows by T5 bucket (bias_kind 1). Returns o [B, q, H*dh] (and optionally the four terms
+    [4,B,H,q,klen], probs)."""
     q, k, v, rtab, u, vb, beta = map(_f64, (q, k, v, rtab, u, vb, beta))
     B, H, ql, dh = q.shape
     kl = k.shape[2]
@@ -97,7 +107,8 @@ def rel_attn_core(q, k, v, rtab, u, vb, *, scale: float, clamp_len: int = -1, rt
     terms = np.empty((4, B, H, ql, kl), np.float64) if want_terms else None
     probs = np.empty((B, H, ql, kl), np.float64) if want_probs else None
     qpos, kpos = _i64arr(qpos), _i64arr(kpos)
-    st = _load().orc_rel_attn_core(B, H, dh, ql, kl, _ptr(qpos), _ptr(kpos), clamp_len, bias_clamp, scale,
+    st = _load().orc_rel_attn_core(B, H, dh, ql, kl, _ptr(qpos), _ptr(kpos), clamp_len, bias_clamp, bias_kind,
+                                   scale,
                                    _ptr(q), _ptr(k), _ptr(v), _ptr(rtab), rtab_delta0, rtab.shape[1],
                                    _ptr(u), _ptr(vb), _ptr(beta), _ptr(o), _ptr(terms), _ptr(probs))
     _check(st, "orc_rel_attn_core")
@@ -110,8 +121,8 @@ def rel_attn_core(q, k, v, rtab, u, vb, *, scale: float, clamp_len: int = -1, rt
 
 
 def rel_attn_fwd(h, mem, w_q, w_k, w_v, w_r, w_o, u, vb, *, n_head: int, d_head: int,
-                 clamp_len: int = -1, beta=None, bias_clamp: int = -1, scale: float | None = None,
-                 base: float = 10000.0, qpos=None, kpos=None, want_terms=False, want_probs=False):
+                 clamp_len: int = -1, beta=None, bias_clamp: int = -1, bias_kind: int = 0,
+                 scale: float | None = None, base: float = 10000.0, qpos=None, kpos=None, want_terms=False, want_probs=False):
     """Full layer: out [B, qlen, D] from h [B, qlen, D] and mem [B, mlen, D]."""
     h = _f64(h)
     B, ql, D = h.shape
@@ -125,7 +136,7 @@ def rel_attn_fwd(h, mem, w_q, w_k, w_v, w_r, w_o, u, vb, *, n_head: int, d_head:
     terms = np.empty((4, B, n_head, ql, kl), np.float64) if want_terms else None
     probs = np.empty((B, n_head, ql, kl), np.float64) if want_probs else None
     qpos, kpos = _i64arr(qpos), _i64arr(kpos)
-    st = _load().orc_rel_attn_fwd(B, D, n_head, d_head, ql, ml, clamp_len, bias_clamp, scale, base,
+    st = _load().orc_rel_attn_fwd(B, D, n_head, d_head, ql, ml, clamp_len, bias_clamp, bias_kind, scale, base,
                                   _ptr(qpos), _ptr(kpos), _ptr(h), _ptr(mem),
                                   _ptr(w_q), _ptr(w_k), _ptr(w_v), _ptr(w_r), _ptr(w_o),
                                   _ptr(u), _ptr(vb), _ptr(beta), _ptr(out), _ptr(terms), _ptr(probs))
@@ -155,7 +166,7 @@ def fifo_update(mem, h, mlen_max: int):
 
 
 def segment_run(stream, n_seg: int, qlen: int, mlen_max: int, weights: dict, *, n_head: int, d_head: int,
-                clamp_len: int = -1, bias_clamp: int = -1):
+                clamp_len: int = -1, bias_clamp: int = -1, bias_kind: int = 0):
     """Segment-recurrent run [felixzhao.cn 118 §2.3.1]: segment t attends over
     [mem_t ; h_t]; afterwards mem_{t+1} = FIFO(mem_t, h_t). The run starts with
     an empty memory. Returns the per-segment outputs and memories."""
@@ -167,7 +178,8 @@ def segment_run(stream, n_seg: int, qlen: int, mlen_max: int, weights: dict, *, 
         h = stream[:, t * qlen:(t + 1) * qlen]
         out = rel_attn_fwd(h, mem, weights["w_q"], weights["w_k"], weights["w_v"], weights["w_r"],
                            weights["w_o"], weights["u"], weights["v"], n_head=n_head, d_head=d_head,
-                           clamp_len=clamp_len, beta=weights.get("beta"), bias_clamp=bias_clamp)
+                           clamp_len=clamp_len, beta=weights.get("beta"), bias_clamp=bias_clamp,
+                           bias_kind=bias_kind)
         outs.append(out)
         mem = fifo_update(mem, h, mlen_max)
         mems.append(mem)

@@ -54,6 +54,30 @@
 
 static int64_t clamp64(int64_t x, int64_t lo, int64_t hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
+/*
+ * T5-style bucket of a relative distance [P4 §4.2]: the boundaries
+ * 1, 2, 4, ..., 1024 on a log scale and one more bucket for larger
+ * distances, 12 buckets: bucket i (i < 11) holds the distances up to
+ * boundary i that the previous boundaries do not hold, bucket 11 everything
+ * above 1024. Negative distances (only masked pairs have them here) share
+ * bucket 0.
+ */
+static const int64_t T5_BOUNDS[11] = {1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024};
+enum { T5_BUCKETS = 12 };
+
+int64_t orc_t5_bucket(int64_t delta) {
+    if (delta < 0) return 0;
+    for (int i = 0; i < 11; ++i)
+        if (delta <= T5_BOUNDS[i]) return i;
+    return T5_BUCKETS - 1;
+}
+
+/* row of the scalar bias table for a distance: kind 0 the clamped distance
+ * [P4 §3.1], kind 1 its T5 bucket [P4 §4.2] */
+static int64_t bias_row(int64_t delta, int64_t bias_kind, int64_t bias_clamp) {
+    return bias_kind == 1 ? orc_t5_bucket(delta) : clamp64(delta, -bias_clamp, bias_clamp) + bias_clamp;
+}
+
 /* One sinusoid row R_delta of width d_model [P2 §2; P5 §2.3.2]:
  * R[2t] = sin(delta * base^(-2t/d_model)), R[2t+1] = cos(same angle). */
 static void sinusoid_row(double delta, int64_t d_model, double base, double* out) {
@@ -105,13 +129,16 @@ static double dot(const double* a, const double* b, int64_t n) {
  *   rtab [H, n_rtab, dh]: projected relative embedding, row n is distance
  *       rtab_delta0 + n (after clamping).
  *   u, vb [H, dh]: global content / position biases [P1 §2.3; P5 §2.3.2].
- *   beta [2*bias_clamp+1, H] or NULL: scalar bias table [P4 §3.1].
+ *   beta [2*bias_clamp+1, H] (bias_kind 0) or [12, H] (bias_kind 1, T5
+ *       buckets) or NULL: scalar bias table [P4 §3.1, §4.2]; bias_clamp < 0
+ *       switches the bias off.
  *   qpos [qlen], kpos [klen]: absolute positions, or NULL for the default
  *       qpos[i] = klen - qlen + i, kpos[j] = j (memory first [P3 §2.1]).
  * For every pair with kpos[j] <= qpos[i] (causal), with
  * delta = qpos[i] - kpos[j] and dc = delta clamped to [-C, C]:
  *   a = q_i.k_j, b = q_i.r_dc, c = u.k_j, d = vb.r_dc      [P2 §3; P5 §2.3.2]
- *   l_ij = scale*(a+b+c+d) + beta[clamp(delta,-bc,bc)+bc, h]  [P3 §2.1; P4 §3.4]
+ *   l_ij = scale*(a+b+c+d) + beta[row(delta), h]   [P3 §2.1; P4 §3.4]
+ *   with row(delta) = clamp(delta,-bc,bc)+bc, or the T5 bucket of delta
  * then p_i = softmax_j(l_i) over the visible keys and o_i = sum_j p_ij v_j.
  * Output o [B, qlen, H*dh] (heads concatenated, [P1 §3.1]).
  * Optional: terms [4, B, H, qlen, klen] (a, b, c, d; 0 where masked),
@@ -119,7 +146,7 @@ static double dot(const double* a, const double* b, int64_t n) {
  */
 int orc_rel_attn_core(int64_t B, int64_t H, int64_t dh, int64_t qlen, int64_t klen,
                       const int64_t* qpos, const int64_t* kpos,
-                      int64_t clamp_len, int64_t bias_clamp, double scale,
+                      int64_t clamp_len, int64_t bias_clamp, int64_t bias_kind, double scale,
                       const double* q, const double* k, const double* v,
                       const double* rtab, int64_t rtab_delta0, int64_t n_rtab,
                       const double* u, const double* vb, const double* beta,
@@ -127,6 +154,7 @@ int orc_rel_attn_core(int64_t B, int64_t H, int64_t dh, int64_t qlen, int64_t kl
     if (B < 0 || H <= 0 || dh <= 0 || qlen < 0 || klen < qlen) return ORC_BAD_ARG;
     if (!q || !k || !v || !rtab || !u || !vb || !o) return ORC_BAD_ARG;
     if (bias_clamp >= 0 && !beta) return ORC_BAD_ARG;
+    if (bias_kind != 0 && bias_kind != 1) return ORC_BAD_ARG;
     const int64_t mlen = klen - qlen;
     int status = ORC_OK;
 #pragma omp parallel for collapse(3) schedule(dynamic, 1)
@@ -166,8 +194,7 @@ int orc_rel_attn_core(int64_t B, int64_t H, int64_t dh, int64_t qlen, int64_t kl
                     const double tc = dot(uh, kj, dh);
                     const double td = dot(vh, rj, dh);
                     double l = scale * (ta + tb + tc + td);
-                    if (bias_clamp >= 0)
-                        l += beta[(clamp64(delta, -bias_clamp, bias_clamp) + bias_clamp) * H + hh];
+                    if (bias_clamp >= 0) l += beta[bias_row(delta, bias_kind, bias_clamp) * H + hh];
                     logit[j] = l;
                     if (l > mx) mx = l;
                     if (terms) {
@@ -213,7 +240,7 @@ int orc_rel_attn_core(int64_t B, int64_t H, int64_t dh, int64_t qlen, int64_t kl
  * out [B, qlen, D]. qpos/kpos/terms/probs as for the core.
  */
 int orc_rel_attn_fwd(int64_t B, int64_t D, int64_t H, int64_t dh, int64_t qlen, int64_t mlen,
-                     int64_t clamp_len, int64_t bias_clamp, double scale, double base,
+                     int64_t clamp_len, int64_t bias_clamp, int64_t bias_kind, double scale, double base,
                      const int64_t* qpos, const int64_t* kpos,
                      const double* h, const double* mem,
                      const double* w_q, const double* w_k, const double* w_v,
@@ -277,7 +304,7 @@ int orc_rel_attn_fwd(int64_t B, int64_t D, int64_t H, int64_t dh, int64_t qlen, 
         for (int64_t n = 0; n < n_r; ++n)
             memcpy(rh + (hh * n_r + n) * dh, rp + n * HD + hh * dh, sizeof(double) * (size_t)dh);
 
-    status = orc_rel_attn_core(B, H, dh, qlen, klen, qpos, kpos, clamp_len, bias_clamp, scale,
+    status = orc_rel_attn_core(B, H, dh, qlen, klen, qpos, kpos, clamp_len, bias_clamp, bias_kind, scale,
                                qh, kh, vh, rh, dmin, n_r, u, vb, beta, o, terms, probs);
     if (status == ORC_OK) orc_linear(o, B * qlen, HD, w_o, D, out);
 done:

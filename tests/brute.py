@@ -21,10 +21,11 @@ def sinusoid_table(deltas: np.ndarray, d_model: int, base: float = 10000.0) -> n
 
 
 def layer(h, mem, w_q, w_k, w_v, w_r, w_o, u, vb, *, n_head, d_head, clamp_len=-1, beta=None,
-          bias_clamp=-1, scale=None, p1_scaling=False, return_terms=False):
+          bias_clamp=-1, bias_kind=0, scale=None, p1_scaling=False, return_terms=False):
     """Forward of one layer on [mem ; h]. With p1_scaling the 1/sqrt(d) factor
     multiplies only terms (a) and (b), as in the 2kiu.com module; otherwise it
-    multiplies the whole sum."""
+    multiplies the whole sum. bias_kind 1 indexes beta by the T5 bucket, found
+    here by a sorted search over the log-scale boundaries 1, 2, 4, ..., 1024."""
     h = np.asarray(h, np.float64)
     B, q, D = h.shape
     mem = np.zeros((B, 0, D)) if mem is None else np.asarray(mem, np.float64)
@@ -53,7 +54,11 @@ def layer(h, mem, w_q, w_k, w_v, w_r, w_o, u, vb, *, n_head, d_head, clamp_len=-
     else:
         score = (ta + tb + tc + td) * s
     if beta is not None:
-        idx = np.clip(delta, -bias_clamp, bias_clamp) + bias_clamp
+        if bias_kind == 1:
+            bounds = 2 ** np.arange(11)
+            idx = np.searchsorted(bounds, np.maximum(delta, 0), side="left")
+        else:
+            idx = np.clip(delta, -bias_clamp, bias_clamp) + bias_clamp
         score = score + np.asarray(beta, np.float64)[idx].transpose(2, 0, 1)[None]
     visible = kj <= qi
     score = np.where(visible[None, None], score, -np.inf)

@@ -17,7 +17,7 @@ from tests import brute
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
-def _tiny(seed=0, B=2, D=16, H=2, dh=8, q=6, m=5, bias_clamp=-1, clamp_len=-1):
+def _tiny(seed=0, B=2, D=16, H=2, dh=8, q=6, m=5, bias_clamp=-1, clamp_len=-1, bias_kind=0):
     rng = np.random.default_rng(seed)
     HD = H * dh
     w = {
@@ -32,8 +32,9 @@ def _tiny(seed=0, B=2, D=16, H=2, dh=8, q=6, m=5, bias_clamp=-1, clamp_len=-1):
         "v": rng.standard_normal((H, dh)) * 0.3,
     }
     if bias_clamp >= 0:
-        w["beta"] = rng.standard_normal((2 * bias_clamp + 1, H)) * 0.5
-    w.update(n_head=H, d_head=dh, clamp_len=clamp_len, bias_clamp=bias_clamp)
+        rows = 12 if bias_kind == 1 else 2 * bias_clamp + 1
+        w["beta"] = rng.standard_normal((rows, H)) * 0.5
+    w.update(n_head=H, d_head=dh, clamp_len=clamp_len, bias_clamp=bias_clamp, bias_kind=bias_kind)
     return w
 
 
@@ -42,7 +43,7 @@ def _fwd(w, **over):
     a.update(over)
     return oracle.rel_attn_fwd(a["h"], a["mem"], a["w_q"], a["w_k"], a["w_v"], a["w_r"], a["w_o"], a["u"], a["v"],
                                n_head=a["n_head"], d_head=a["d_head"], clamp_len=a["clamp_len"],
-                               beta=a.get("beta"), bias_clamp=a["bias_clamp"],
+                               beta=a.get("beta"), bias_clamp=a["bias_clamp"], bias_kind=a.get("bias_kind", 0),
                                **{k: a[k] for k in ("qpos", "kpos", "want_terms", "want_probs", "scale") if k in a})
 
 
@@ -51,7 +52,8 @@ def _brute(w, **over):
     a.update(over)
     return brute.layer(a["h"], a["mem"], a["w_q"], a["w_k"], a["w_v"], a["w_r"], a["w_o"], a["u"], a["v"],
                        n_head=a["n_head"], d_head=a["d_head"], clamp_len=a["clamp_len"], beta=a.get("beta"),
-                       bias_clamp=a["bias_clamp"], **{k: a[k] for k in ("p1_scaling", "return_terms", "scale") if k in a})
+                       bias_clamp=a["bias_clamp"], bias_kind=a.get("bias_kind", 0),
+                       **{k: a[k] for k in ("p1_scaling", "return_terms", "scale") if k in a})
 
 
 def _close(a, b, tol=1e-12):
@@ -243,6 +245,69 @@ def test_bias_only_closed_form():
             logits = beta[np.clip(d, -2, 2) + 2, hh]
             p = np.exp(logits) / np.exp(logits).sum()
             _close(probs[0, hh, i, :m + i + 1], p, 1e-13)
+
+
+def _t5_golden():
+    return json.load(open(os.path.join(GOLDEN, "t5_buckets.json")))
+
+
+def _t5_from_ranges(d, ranges):
+    for i, (lo, hi) in enumerate(ranges):
+        if d >= lo and (hi is None or d <= hi):
+            return i
+    raise AssertionError(f"distance {d} in no range")
+
+
+def test_t5_bucket_matches_page_ranges():
+    g = _t5_golden()
+    assert g["num_buckets"] == len(g["boundaries"]) + 1 == len(g["ranges"])
+    # the ranges tile [0, inf) and each upper end is the page's boundary
+    assert g["ranges"][0][0] == 0
+    for (lo, hi), (lo2, _), b in zip(g["ranges"], g["ranges"][1:], g["boundaries"]):
+        assert hi == b and lo2 == hi + 1
+    for d in list(range(0, 3000)) + [4095, 4096, 1 << 20, (1 << 40) + 3]:
+        assert oracle.t5_bucket(d) == _t5_from_ranges(d, g["ranges"]), d
+    for d in (-1, -2, -1025):
+        assert oracle.t5_bucket(d) == 0
+
+
+def test_t5_bias_only_closed_form():
+    # zero projections and biases: the logits are beta[bucket(distance)]; key
+    # positions chosen so that the distances reach every bucket
+    g = _t5_golden()
+    H = 2
+    w = _tiny(17, H=H, q=3, m=13, bias_clamp=0, bias_kind=1)
+    z = {k: np.zeros_like(w[k]) for k in ("w_q", "w_k", "w_r", "u", "v")}
+    kpos = np.array([0, 1, 500, 1000, 1020, 1500, 1700, 1800, 1900, 1950, 1990, 2005, 2010, 2013, 2015, 2016])
+    qpos = np.array([2014, 2016, 2017])
+    _, probs = _fwd(w, want_probs=True, qpos=qpos, kpos=kpos, **z)
+    beta = w["beta"]
+    seen = set()
+    for hh in range(H):
+        for i, pi in enumerate(qpos):
+            vis = kpos <= pi
+            b = [_t5_from_ranges(int(pi - pj), g["ranges"]) for pj in kpos[vis]]
+            seen.update(b)
+            logits = beta[b, hh]
+            p = np.exp(logits) / np.exp(logits).sum()
+            _close(probs[0, hh, i, vis], p, 1e-13)
+            assert np.all(probs[0, hh, i, ~vis] == 0)
+    assert seen == set(range(12))
+
+
+@pytest.mark.parametrize("seed,q,m,clamp", [(18, 6, 5, -1), (19, 9, 40, 8), (20, 1, 0, -1)])
+def test_t5_oracle_matches_independent_formulation(seed, q, m, clamp):
+    w = _tiny(seed, q=q, m=m, clamp_len=clamp, bias_clamp=0, bias_kind=1)
+    _close(_fwd(w), _brute(w), 1e-12)
+
+
+def test_t5_and_clamp_tables_agree_where_buckets_are_distances():
+    # distances 0..2 fall in buckets 0, 0, 1; a clamp table with the same
+    # values per distance gives the same layer
+    w = _tiny(21, q=2, m=1, bias_clamp=0, bias_kind=1)
+    t5 = w["beta"]
+    clamp_tab = np.stack([t5[1], t5[0], t5[0], t5[0], t5[1]])   # rows d = -2..2
+    _close(_fwd(w), _fwd(w, bias_kind=0, bias_clamp=2, beta=clamp_tab), 1e-14)
 
 
 def test_p1_scaling_is_rescaled_biases():
