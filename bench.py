@@ -119,7 +119,8 @@ def cpu_baseline(w, t, min_seconds=10.0):
         oracle.rel_attn_fwd(t["h"].f64[b:b + 1], t["mem"].f64[b:b + 1], t["w_q"].f64, t["w_k"].f64,
                             t["w_v"].f64, t["w_r"].f64, t["w_o"].f64, t["u"].f64, t["v"].f64,
                             n_head=w.n_head, d_head=w.d_head, clamp_len=w.clamp_len,
-                            beta=t["beta"].f64 if "beta" in t else None, bias_clamp=w.bias_clamp)
+                            beta=t["beta"].f64 if "beta" in t else None, bias_clamp=w.bias_clamp,
+                            bias_kind=w.bias_kind)
         n += 1
         el = time.perf_counter() - t0
         if el >= min_seconds:
@@ -152,7 +153,7 @@ def cpu_baseline_core(w, t, min_seconds=10.0):
     n, t0 = 0, time.perf_counter()
     while True:
         oracle.rel_attn_core(qh, kh, vh, rt, t["u"].f64, t["v"].f64, scale=1.0 / np.sqrt(dh),
-                             clamp_len=w.clamp_len, beta=beta, bias_clamp=w.bias_clamp)
+                             clamp_len=w.clamp_len, beta=beta, bias_clamp=w.bias_clamp, bias_kind=w.bias_kind)
         n += 1
         el = time.perf_counter() - t0
         if el >= min_seconds:
@@ -211,7 +212,8 @@ def main():
     ring = gu.dev(t["mem"]).contiguous()
     fifo = xl.xl_mem_fifo(ring.data_ptr(), w.mlen, w.mlen, 0)   # full memory, oldest row first
     desc = xl.make_desc(batch=w.batch, d_model=D, n_head=w.n_head, d_head=w.d_head, qlen=w.qlen, mlen=0,
-                        clamp_len=w.clamp_len, bias_clamp=w.bias_clamp, dtype=xl.XL_BF16, out_dtype=xl.XL_BF16)
+                        clamp_len=w.clamp_len, bias_clamp=w.bias_clamp, bias_kind=w.bias_kind, dtype=xl.XL_BF16,
+                        out_dtype=xl.XL_BF16)
     stream = torch.cuda.current_stream()
 
     def step():
@@ -227,7 +229,7 @@ def main():
         vr = torch.zeros((w.batch, w.n_head, w.d_head, cap), dtype=torch.bfloat16, device="cuda")
         kv = xl.xl_kv_fifo(kr.data_ptr(), vr.data_ptr(), cap, w.mlen, 0, 0)
         kdesc = xl.make_desc(batch=w.batch, d_model=D, n_head=w.n_head, d_head=w.d_head, qlen=w.qlen, mlen=w.mlen,
-                             clamp_len=w.clamp_len, bias_clamp=w.bias_clamp, dtype=xl.XL_BF16,
+                             clamp_len=w.clamp_len, bias_clamp=w.bias_clamp, bias_kind=w.bias_kind, dtype=xl.XL_BF16,
                              out_dtype=xl.XL_BF16)
         kws = torch.empty(xl.xl_segment_step_kv_workspace_size(kdesc), dtype=torch.uint8, device="cuda")
 

@@ -17,7 +17,9 @@
  *    "Transformer-XL架构解析" §2.1); causal mask after the whole sum
  *    (2kiu.com §4.2), softmax, P.V, output projection (2kiu.com §3.1);
  *  - optional per-head scalar bias b_{clamp(i-j, +-k)} added after scaling
- *    (jsqmd.com 1364567 "Transformer偏置型相对位置编码" §2.2, §3.1-§3.4);
+ *    (jsqmd.com 1364567 "Transformer偏置型相对位置编码" §2.2, §3.1-§3.4),
+ *    or, instead of the clamped distance, its T5 log-scale bucket (same
+ *    page, §4.2);
  *  - FIFO memory update: the newest states push out the oldest
  *    (intelliparadigm.com §1.1), memory is a detached copy (felixzhao.cn
  *    §2.3.1).
@@ -60,6 +62,17 @@ enum {
 /* Element types. */
 enum { XL_F32 = 0, XL_BF16 = 1 };
 
+/* Rows of the scalar bias table (xl_attn_desc.bias_kind), by the distance
+ * delta = i - j of a visible pair (delta >= 0):
+ *  XL_BIAS_CLAMP: row clamp(delta, -k, k) + k of 2k+1 rows, k = bias_clamp
+ *                 (jsqmd.com 1364567 §3.1);
+ *  XL_BIAS_T5:    row bucket(delta) of XL_T5_BUCKETS rows, on the log-scale
+ *                 boundaries 1, 2, 4, ..., 1024 (same page, §4.2): bucket 0
+ *                 holds delta <= 1, bucket b in 1..10 holds
+ *                 2^(b-1) < delta <= 2^b, bucket 11 every delta > 1024. */
+enum { XL_BIAS_CLAMP = 0, XL_BIAS_T5 = 1 };
+enum { XL_T5_BUCKETS = 12 };
+
 /* Human-readable name of a status code (static string). */
 const char* xl_status_string(int status);
 /* Detail of the last error on the calling thread ("" if none). */
@@ -90,7 +103,9 @@ typedef struct {
     int64_t qlen;        /* segment length, >= 1 */
     int64_t mlen;        /* memory length, >= 0 (ignored by xl_segment_step) */
     int64_t clamp_len;   /* < 0: no clamp; else distances clamp to [-C, C] */
-    int64_t bias_clamp;  /* < 0: no scalar bias table; else table has 2k+1 rows */
+    int64_t bias_clamp;  /* < 0: no scalar bias table; else the table is on,
+                            with 2k+1 rows (k = bias_clamp) for
+                            XL_BIAS_CLAMP, XL_T5_BUCKETS rows for XL_BIAS_T5 */
     double base;         /* sinusoid base; 0 selects 10000 */
     float scale;         /* score scale; 0 selects 1/sqrt(d_head) */
     int32_t dtype;       /* XL_BF16 (d_head 64) or XL_F32 (d_head 8): h, mem,
@@ -103,6 +118,9 @@ typedef struct {
                             tile at that count (and at its number of 32-key
                             steps). Results agree to rounding for every value.
                             f32: ignored. */
+    int32_t bias_kind;   /* XL_BIAS_CLAMP (0) or XL_BIAS_T5: how a distance
+                            picks its bias table row; ignored when
+                            bias_clamp < 0 */
 } xl_attn_desc;
 
 /* Weights of one layer; all device pointers in desc->dtype. */
@@ -114,7 +132,9 @@ typedef struct {
     const void* w_o;         /* [D, H*d_head] */
     const void* u;           /* [H, d_head]  content bias */
     const void* v;           /* [H, d_head]  position bias */
-    const void* bias_table;  /* [2*bias_clamp+1, H] or NULL when bias_clamp < 0 */
+    const void* bias_table;  /* [2*bias_clamp+1, H] (XL_BIAS_CLAMP) or
+                                [XL_T5_BUCKETS, H] (XL_BIAS_T5); NULL when
+                                bias_clamp < 0 */
 } xl_attn_weights;
 
 /*
@@ -167,7 +187,8 @@ int xl_rel_attn_fwd(const xl_attn_desc* desc, const xl_attn_weights* w,
  *     least min(klen, clamp_len + 1) (klen without a clamp); a distance
  *     delta uses row min(delta, C) (C = clamp_len, or klen - 1 unclamped);
  *   u, v [H, d_head] content and position biases;
- *   bias_table [2*bias_clamp+1, H] or NULL;
+ *   bias_table [2*bias_clamp+1, H], [XL_T5_BUCKETS, H] (desc->bias_kind
+ *       XL_BIAS_T5) or NULL;
  *   attn [B, qlen, H*d_head] output (desc->dtype).
  * The scores are s*(q_i+u).k_j + s*(q_i+v).r + bias with s = desc->scale
  * (0 selects 1/sqrt(d_head)); the sums q+u and q+v are rounded to desc->dtype

@@ -64,7 +64,8 @@ class Layer:
         self.w = w
         self.dt = xl.XL_BF16 if w.dtype == "bf16" else xl.XL_F32
         self.desc = xl.make_desc(batch=batch, d_model=w.d_model, n_head=w.n_head, d_head=w.d_head, qlen=qlen,
-                                 mlen=mlen, clamp_len=w.clamp_len, bias_clamp=w.bias_clamp, dtype=self.dt,
+                                 mlen=mlen, clamp_len=w.clamp_len, bias_clamp=w.bias_clamp,
+                                 bias_kind=w.bias_kind, dtype=self.dt,
                                  out_dtype=xl.XL_F32 if out_f32 else self.dt)
         self.weights = xl.Weights(*(dev(t[k]) for k in ("w_q", "w_k", "w_v", "w_r", "w_o", "u", "v")),
                                   bias_table=dev(t["beta"]) if "beta" in t else None)
@@ -88,4 +89,5 @@ def oracle_layer(t: dict, w: xl_inputs.Workload, h, mem, bsel=None):
         mem = mem[bsel]
     return oracle.rel_attn_fwd(h, mem, t["w_q"].f64, t["w_k"].f64, t["w_v"].f64, t["w_r"].f64, t["w_o"].f64,
                                t["u"].f64, t["v"].f64, n_head=w.n_head, d_head=w.d_head, clamp_len=w.clamp_len,
-                               beta=t["beta"].f64 if "beta" in t else None, bias_clamp=w.bias_clamp)
+                               beta=t["beta"].f64 if "beta" in t else None, bias_clamp=w.bias_clamp,
+                               bias_kind=w.bias_kind)

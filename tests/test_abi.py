@@ -77,6 +77,8 @@ def _fwd(desc, w=None, h=FAKE[8], mem=FAKE[9], out=FAKE[10], ws=FAKE[11], ws_byt
     (dict(bias_clamp=128, mlen=20000, qlen=200), xl.XL_UNSUPPORTED),   # LDS bias table limit
     (dict(attn_splits=-1), xl.XL_BAD_SHAPE),
     (dict(attn_splits=65), xl.XL_BAD_SHAPE),
+    (dict(bias_kind=2), xl.XL_BAD_SHAPE),
+    (dict(bias_kind=-1, bias_clamp=4), xl.XL_BAD_SHAPE),
 ])
 def test_fwd_rejects_bad_descriptors(over, status):
     assert _fwd(_desc(**over)) == status

@@ -174,6 +174,19 @@ def test_layer_model_width(T, d_model, n_head):
     _check_intermediates(T, L, w, t, 2, 70, 45)
 
 
+@pytest.mark.parametrize("base,qlen,mlen,clamp", [("base_bf16", 70, 1000, -1), ("base_bf16", 130, 0, -1),
+                                                  ("longmem_bf16", 64, 1600, 1000), ("tiny_f32", 9, 1030, 5)])
+def test_layer_t5_bias(T, base, qlen, mlen, clamp):
+    # the whole layer with the T5 bucket table
+    import dataclasses
+    w = dataclasses.replace(W[base], clamp_len=clamp, bias_clamp=0, bias_kind=1, seed=qlen + mlen)
+    t = xl_inputs.layer_inputs(w, batch=2, qlen=qlen, mlen=mlen)
+    assert t["beta"].f32.shape == (12, w.n_head)
+    L = _run_layer(T, w, t, batch=2, qlen=qlen, mlen=mlen)
+    ref = gu.oracle_layer(t, w, t["h"].f64, t["mem"].f64)
+    gu.compare(f"t5 {base} q{qlen} m{mlen}", gu.host64(L.out), ref, dtype=w.dtype)
+
+
 def test_split_invariance_gpu(T):
     # the output of a position does not depend on where the memory/segment split falls
     import dataclasses
@@ -211,12 +224,32 @@ CORE = [
 @pytest.mark.parametrize("dtype,B,H,qlen,mlen,clamp,bias,splits", CORE,
                          ids=[f"{c[0]}-B{c[1]}H{c[2]}-q{c[3]}m{c[4]}-c{c[5]}b{c[6]}-s{c[7]}" for c in CORE])
 def test_core_alone(T, dtype, B, H, qlen, mlen, clamp, bias, splits):
+    _core_case(T, dtype, B, H, qlen, mlen, clamp, bias, splits)
+
+
+CORE_T5 = [
+    # T5 bucket rows: distances past 1024 reach the last bucket; with key
+    # splits; a tile whose distances stay in the first buckets; fp32
+    ("bf16", 2, 2, 129, 1000, -1, 0),
+    ("bf16", 1, 3, 64, 1600, 1000, 7),
+    ("bf16", 2, 2, 40, 0, -1, 0),
+    ("f32", 2, 2, 40, 1100, -1, 0),
+]
+
+
+@pytest.mark.parametrize("dtype,B,H,qlen,mlen,clamp,splits", CORE_T5,
+                         ids=[f"{c[0]}-B{c[1]}H{c[2]}-q{c[3]}m{c[4]}-c{c[5]}-s{c[6]}" for c in CORE_T5])
+def test_core_t5_bias(T, dtype, B, H, qlen, mlen, clamp, splits):
+    _core_case(T, dtype, B, H, qlen, mlen, clamp, 0, splits, bias_kind=1)
+
+
+def _core_case(T, dtype, B, H, qlen, mlen, clamp, bias, splits, bias_kind=0):
     import transformer_xl_relative_amd as xl
     dh = 64 if dtype == "bf16" else 8
     klen = qlen + mlen
     n_rel = klen if clamp < 0 else min(klen, clamp + 1)
     ci = xl_inputs.core_inputs(batch=B, n_head=H, d_head=dh, qlen=qlen, mlen=mlen, n_rows=n_rel, dtype=dtype,
-                               seed=B * 100 + qlen, bias_clamp=bias)
+                               seed=B * 100 + qlen + 7 * bias_kind, bias_clamp=bias, bias_kind=bias_kind)
     s = 1.0 / np.sqrt(dh)
     # operands in the kernel's layout: transposed values
     ldv = (klen + 7) // 8 * 8 + 8
@@ -224,7 +257,8 @@ def test_core_alone(T, dtype, B, H, qlen, mlen, clamp, bias, splits):
     vt[..., :klen] = ci["v"].f32.transpose(0, 1, 3, 2)
     vt = xl_inputs.Tensor(vt, dtype)
     desc = xl.make_desc(batch=B, d_model=2, n_head=H, d_head=dh, qlen=qlen, mlen=mlen, clamp_len=clamp,
-                        bias_clamp=bias, dtype=xl.XL_BF16 if dtype == "bf16" else xl.XL_F32, attn_splits=splits)
+                        bias_clamp=bias, dtype=xl.XL_BF16 if dtype == "bf16" else xl.XL_F32, attn_splits=splits,
+                        bias_kind=bias_kind)
     attn = T.empty((B, qlen, H * dh), dtype=T.bfloat16 if dtype == "bf16" else T.float32, device="cuda")
     beta = gu.dev(ci["beta"]) if bias >= 0 else None
     nws = xl.xl_rel_attn_core_workspace_size(desc)
@@ -236,7 +270,7 @@ def test_core_alone(T, dtype, B, H, qlen, mlen, clamp, bias, splits):
     T.cuda.synchronize()
     ref = oracle.rel_attn_core(ci["q"].f64, ci["k"].f64, ci["v"].f64, ci["r"].f64, ci["u"].f64, ci["vb"].f64,
                                scale=s, clamp_len=clamp, beta=ci["beta"].f64 if bias >= 0 else None,
-                               bias_clamp=bias)
+                               bias_clamp=bias, bias_kind=bias_kind)
     gu.compare("core", gu.host64(attn), ref, dtype=dtype)
 
 
@@ -257,7 +291,8 @@ def _segment_run_gpu(T, w, t, *, batch, qlen, n_seg, mlen_max, head0=0):
         h = hs[:, s * qlen:(s + 1) * qlen].contiguous()
         out = T.empty((batch, qlen, D), dtype=T.float32, device="cuda")
         desc = xl.make_desc(batch=batch, d_model=D, n_head=w.n_head, d_head=w.d_head, qlen=qlen, mlen=0,
-                            clamp_len=w.clamp_len, bias_clamp=w.bias_clamp, dtype=dt, out_dtype=xl.XL_F32)
+                            clamp_len=w.clamp_len, bias_clamp=w.bias_clamp, bias_kind=w.bias_kind, dtype=dt,
+                            out_dtype=xl.XL_F32)
         xl.xl_segment_step(desc, L.weights, h, fifo, out, L.ws)
         T.cuda.synchronize()
         outs.append(gu.host64(out))
@@ -277,7 +312,7 @@ def test_segment_run_reduced(T, qlen, n_seg, mlen_max, head0):
     outs, mems = _segment_run_gpu(T, w, t, batch=1, qlen=qlen, n_seg=n_seg, mlen_max=mlen_max, head0=head0)
     wts = {k: t[k].f64 for k in ("w_q", "w_k", "w_v", "w_r", "w_o", "u", "v", "beta")}
     routs, rmems = oracle.segment_run(t["h"].f64, n_seg, qlen, mlen_max, wts, n_head=w.n_head, d_head=w.d_head,
-                                      clamp_len=w.clamp_len, bias_clamp=w.bias_clamp)
+                                      clamp_len=w.clamp_len, bias_clamp=w.bias_clamp, bias_kind=w.bias_kind)
     for s in range(n_seg):
         gu.compare(f"segment {s}", outs[s], routs[s], dtype="bf16")
         # the memory holds copies of the input states: bit-exact
@@ -291,7 +326,8 @@ def test_segment_run_full_size_sampled(T):
     outs, mems = _segment_run_gpu(T, w, t, batch=w.batch, qlen=w.qlen, n_seg=w.segments, mlen_max=w.mlen)
     wts = {k: t[k].f64 for k in ("w_q", "w_k", "w_v", "w_r", "w_o", "u", "v", "beta")}
     routs, rmems = oracle.segment_run(t["h"].f64[:1], w.segments, w.qlen, w.mlen, wts, n_head=w.n_head,
-                                      d_head=w.d_head, clamp_len=w.clamp_len, bias_clamp=w.bias_clamp)
+                                      d_head=w.d_head, clamp_len=w.clamp_len, bias_clamp=w.bias_clamp,
+                                      bias_kind=w.bias_kind)
     for s in range(w.segments):
         gu.compare(f"segment {s} (batch 0)", outs[s][:1], routs[s], dtype="bf16")
         want = xl_inputs.bf16_bits(rmems[s].astype(np.float32))
@@ -316,7 +352,8 @@ def _segment_run_kv(T, w, t, *, batch, qlen, n_seg, mlen_max, cap, head0=0):
         h = hs[:, s * qlen:(s + 1) * qlen].contiguous()
         out = T.empty((batch, qlen, D), dtype=T.float32, device="cuda")
         desc = xl.make_desc(batch=batch, d_model=D, n_head=H, d_head=dh, qlen=qlen, mlen=0,
-                            clamp_len=w.clamp_len, bias_clamp=w.bias_clamp, dtype=xl.XL_BF16, out_dtype=xl.XL_F32)
+                            clamp_len=w.clamp_len, bias_clamp=w.bias_clamp, bias_kind=w.bias_kind,
+                            dtype=xl.XL_BF16, out_dtype=xl.XL_F32)
         xl.xl_segment_step_kv(desc, L.weights, h, kv, out, ws)
         T.cuda.synchronize()
         outs.append(out.clone())
@@ -337,11 +374,27 @@ def test_segment_run_kv_ring(T, qlen, n_seg, mlen_max, cap, head0):
     outs, _ = _segment_run_gpu(T, w, t, batch=1, qlen=qlen, n_seg=n_seg, mlen_max=mlen_max)
     wts = {k: t[k].f64 for k in ("w_q", "w_k", "w_v", "w_r", "w_o", "u", "v", "beta")}
     routs, _ = oracle.segment_run(t["h"].f64, n_seg, qlen, mlen_max, wts, n_head=w.n_head, d_head=w.d_head,
-                                  clamp_len=w.clamp_len, bias_clamp=w.bias_clamp)
+                                  clamp_len=w.clamp_len, bias_clamp=w.bias_clamp, bias_kind=w.bias_kind)
     for s in range(n_seg):
         got = gu.host64(ring_outs[s])
         assert np.array_equal(got, outs[s]), f"segment {s}: key ring and state FIFO differ"
         gu.compare(f"key ring segment {s}", got, routs[s], dtype="bf16")
+
+
+def test_segment_run_kv_ring_t5(T):
+    # the segment step on the key ring with the T5 bucket table: memory grows
+    # past 1024 positions, so every bucket is used
+    import dataclasses
+    qlen, n_seg, mlen_max, cap = 256, 6, 1024, 1280
+    w = dataclasses.replace(W["segments_bf16"], n_head=4, qlen=qlen, mlen=mlen_max, segments=n_seg, bias_clamp=0,
+                            bias_kind=1)
+    t = xl_inputs.layer_inputs(w, batch=1, qlen=qlen)
+    ring_outs = _segment_run_kv(T, w, t, batch=1, qlen=qlen, n_seg=n_seg, mlen_max=mlen_max, cap=cap, head0=8)
+    wts = {k: t[k].f64 for k in ("w_q", "w_k", "w_v", "w_r", "w_o", "u", "v", "beta")}
+    routs, _ = oracle.segment_run(t["h"].f64, n_seg, qlen, mlen_max, wts, n_head=w.n_head, d_head=w.d_head,
+                                  clamp_len=w.clamp_len, bias_clamp=w.bias_clamp, bias_kind=w.bias_kind)
+    for s in range(n_seg):
+        gu.compare(f"t5 key ring segment {s}", gu.host64(ring_outs[s]), routs[s], dtype="bf16")
 
 
 def test_segment_run_kv_ring_full_size(T):

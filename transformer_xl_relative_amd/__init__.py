@@ -16,6 +16,8 @@ LIB_PATH = os.path.join(_HERE, "libxlrel.so")
 
 XL_OK, XL_NULL_ARG, XL_BAD_SHAPE, XL_UNSUPPORTED, XL_WORKSPACE_TOO_SMALL, XL_HIP_ERROR = range(6)
 XL_F32, XL_BF16 = 0, 1
+XL_BIAS_CLAMP, XL_BIAS_T5 = 0, 1
+XL_T5_BUCKETS = 12
 
 _i64 = ctypes.c_int64
 _p = ctypes.c_void_p
@@ -25,7 +27,8 @@ class xl_attn_desc(ctypes.Structure):
     _fields_ = [("batch", _i64), ("d_model", _i64), ("n_head", _i64), ("d_head", _i64),
                 ("qlen", _i64), ("mlen", _i64), ("clamp_len", _i64), ("bias_clamp", _i64),
                 ("base", ctypes.c_double), ("scale", ctypes.c_float),
-                ("dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32), ("attn_splits", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32), ("attn_splits", ctypes.c_int32),
+                ("bias_kind", ctypes.c_int32)]
 
 
 class xl_attn_weights(ctypes.Structure):
@@ -132,9 +135,9 @@ def _stream(stream) -> Optional[int]:
 
 
 def make_desc(*, batch, d_model, n_head, d_head, qlen, mlen=0, clamp_len=-1, bias_clamp=-1, base=10000.0,
-              scale=0.0, dtype=XL_BF16, out_dtype=None, attn_splits=0) -> xl_attn_desc:
+              scale=0.0, dtype=XL_BF16, out_dtype=None, attn_splits=0, bias_kind=0) -> xl_attn_desc:
     return xl_attn_desc(batch, d_model, n_head, d_head, qlen, mlen, clamp_len, bias_clamp, base, scale,
-                        dtype, dtype if out_dtype is None else out_dtype, attn_splits)
+                        dtype, dtype if out_dtype is None else out_dtype, attn_splits, bias_kind)
 
 
 @dataclasses.dataclass

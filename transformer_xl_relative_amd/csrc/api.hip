@@ -66,6 +66,8 @@ int check_desc(const xl_attn_desc* d, int64_t mlen, bool need_dmodel) {
         if (!isfinite(d->scale)) return fail(XL_BAD_SHAPE, "scale must be finite");
     }
     if (d->bias_clamp > 65535) return fail(XL_UNSUPPORTED, "bias_clamp above 65535");
+    if (d->bias_kind != XL_BIAS_CLAMP && d->bias_kind != XL_BIAS_T5)
+        return fail(XL_BAD_SHAPE, "bias_kind must be XL_BIAS_CLAMP or XL_BIAS_T5");
     if (d->attn_splits < 0 || d->attn_splits > xl::kMaxAttnSplits)
         return fail(XL_BAD_SHAPE, "attn_splits must be in [0, %d]", xl::kMaxAttnSplits);
     const int64_t klen = mlen + d->qlen;
@@ -227,7 +229,9 @@ int layer_forward(const xl_attn_desc* d, const xl_attn_weights* w, const void* h
     a.bias = d->bias_clamp >= 0 ? w->bias_table : nullptr;
     a.out = W + L.attn;
     a.B = (int)B; a.H = (int)H; a.qlen = (int)q; a.mlen = (int)mlen; a.klen = (int)klen;
-    a.ldv = (int)L.ldv; a.n_rel = (int)L.n_rel; a.r_rows = (int)L.n_rel; a.bias_clamp = (int)(d->bias_clamp >= 0 ? d->bias_clamp : 0);
+    a.ldv = (int)L.ldv; a.n_rel = (int)L.n_rel; a.r_rows = (int)L.n_rel;
+    a.bias_clamp = (int)(d->bias_clamp >= 0 ? d->bias_clamp : 0);
+    a.bias_kind = d->bias_kind;
     if (kv) {
         a.ldv = (int)kv->cap;
         a.kv_rows = (int)kv->cap;
@@ -363,6 +367,7 @@ int xl_rel_attn_core(const xl_attn_desc* desc, const void* q, const void* k, con
     a.B = (int)desc->batch; a.H = (int)desc->n_head; a.qlen = (int)desc->qlen; a.mlen = (int)desc->mlen;
     a.klen = (int)klen; a.ldv = (int)ldv; a.n_rel = (int)need; a.r_rows = (int)n_rel;
     a.bias_clamp = (int)(desc->bias_clamp >= 0 ? desc->bias_clamp : 0);
+    a.bias_kind = desc->bias_kind;
     const xl::SplitPlan sp = splits_of(desc, desc->mlen);
     a.split_steps = sp.steps;
     a.split_max = sp.max;

@@ -167,8 +167,8 @@ __global__ void __launch_bounds__(NW * 64) attn_kernel(AttnArgs a) {
             const T* bias = (const T*)a.bias;
             const int dblk = dtop - BKY * beta;
             for (int r = 0; r < 16; ++r) {
-                const int d = max(0, min(dblk - acc_row(r, hf), a.bias_clamp));
-                g[r] = Elem<T>::to_f(bias[(d + a.bias_clamp) * a.H + h]);
+                const int d = max(0, dblk - acc_row(r, hf));
+                g[r] = Elem<T>::to_f(bias[bias_row(d, a.bias_kind, a.bias_clamp) * a.H + h]);
             }
         } else {
             for (int r = 0; r < 16; ++r) g[r] = 0.f;

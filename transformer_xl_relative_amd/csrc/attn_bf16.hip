@@ -334,17 +334,14 @@ __global__ void __launch_bounds__(NT, 2) attn_bf16_kernel(AttnArgs a) {
     }
     constexpr int PRO_DMA = 10;
 
-    // ---- bias table: entry x holds beta_h[clamp(X0 - x, +-bc)], X0 = gtop,
-    // so that four consecutive registers (descending distance) are one
-    // aligned 16-byte read
+    // ---- bias table: entry x holds beta_h[row(X0 - x)], X0 = gtop (row: the
+    // clamped distance or its T5 bucket), so that four consecutive registers
+    // (descending distance) are one aligned 16-byte read
     const int ntbl = (gtop + 2 * BQ + 3) & ~3;
     if constexpr (HAS_BIAS) {
         const bf16_t* bias = (const bf16_t*)a.bias;
-        const int bc = a.bias_clamp;
-        for (int x = tid; x < ntbl; x += NT) {
-            const int d = min(max(gtop - x, -bc), bc);
-            *(float*)(smem + OFF_TBL + 4 * x) = bf2f(bias[(d + bc) * a.H + h]);
-        }
+        for (int x = tid; x < ntbl; x += NT)
+            *(float*)(smem + OFF_TBL + 4 * x) = bf2f(bias[bias_row(gtop - x, a.bias_kind, a.bias_clamp) * a.H + h]);
         block_sync<63>();
     }
     // bias of position block beta: registers 4q..4q+3 hold distances dtop - 32 beta - 8q - 4hf - t

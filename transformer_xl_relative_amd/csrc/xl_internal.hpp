@@ -78,7 +78,7 @@ struct AttnArgs {
     const void* k;
     const void* vt;
     const void* r;
-    const void* bias;     // [2*bias_clamp+1, H] or nullptr
+    const void* bias;     // [2*bias_clamp+1, H], [12, H] (bias_kind 1) or nullptr
     void* out;            // [B, qlen, H*dh]
     int B, H, qlen, mlen, klen, ldv;
     int n_rel;            // distance delta uses row min(delta, n_rel - 1)
@@ -89,6 +89,7 @@ struct AttnArgs {
     int kv_rows = 0;
     int kv_head = 0;
     int bias_clamp;
+    int bias_kind = 0;    // 0: row clamp(delta, +-bias_clamp) + bias_clamp; 1: t5_bucket(delta)
     // key splits of the bf16 kernel: a query tile with ts key steps is shared by
     // min(ceil(ts / split_steps), split_max) workgroups (split_steps 0: none).
     // part holds split_max * B*H*qlen * (d_head + 2) floats of partial results.
@@ -96,6 +97,19 @@ struct AttnArgs {
     int split_max = 1;
     void* part = nullptr;
 };
+
+// T5 bucket of a distance on the boundaries 1, 2, 4, ..., 1024: 0 for
+// delta <= 1, b for 2^(b-1) < delta <= 2^b (b <= 10), 11 beyond 1024.
+__host__ __device__ inline int t5_bucket(int delta) {
+    if (delta <= 1) return 0;
+    const int b = 32 - __builtin_clz((unsigned)(delta - 1));
+    return b < 11 ? b : 11;
+}
+// bias table row of a distance
+__host__ __device__ inline int bias_row(int delta, int bias_kind, int bias_clamp) {
+    if (bias_kind) return t5_bucket(delta);
+    return (delta < -bias_clamp ? -bias_clamp : delta > bias_clamp ? bias_clamp : delta) + bias_clamp;
+}
 
 constexpr int kMaxAttnSplits = 64;
 // The split plan of a bf16 problem (forced > 0: up to `forced` workgroups per

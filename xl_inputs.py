@@ -11,8 +11,8 @@ Workloads (value recipe, applied to every one):
     W_o ([d_model, n_head*d_head]) N(0, 0.02) -- the nn.Linear [out, in]
     layout, so a projection is y = x @ W^T;
   * global biases u, v ([n_head, d_head]) N(0, 0.02);
-  * the optional per-head scalar bias table beta ([2*bias_clamp+1, n_head])
-    N(0, 0.02).
+  * the optional per-head scalar bias table beta ([2*bias_clamp+1, n_head],
+    or [12, n_head] for the T5 buckets) N(0, 0.02).
 Draws are float32 from numpy.random.default_rng(seed) in the order
 h, mem, W_q, W_k, W_v, W_r, W_o, u, v, beta; bf16 workloads round every draw
 once to bfloat16 (round to nearest even) and both sides consume those bits.
@@ -34,6 +34,7 @@ class Workload:
     mlen: int
     clamp_len: int = -1     # < 0: no clamp of the relative distance
     bias_clamp: int = -1    # < 0: no scalar bias table
+    bias_kind: int = 0      # 0: rows by clamped distance, 1: twelve T5 bucket rows
     dtype: str = "bf16"     # "f32" or "bf16"
     segments: int = 1       # > 1: segment-recurrent run with FIFO memory
     seed: int = 0
@@ -98,6 +99,11 @@ def _normal(rng, shape, std):
     return (rng.standard_normal(size=shape, dtype=np.float32) * np.float32(std)).astype(np.float32)
 
 
+def bias_rows(bias_clamp: int, bias_kind: int) -> int:
+    """Rows of the scalar bias table: 2k+1 clamped distances, or 12 buckets."""
+    return 12 if bias_kind == 1 else 2 * bias_clamp + 1
+
+
 def layer_inputs(w: Workload, *, batch: int | None = None, qlen: int | None = None,
                  mlen: int | None = None, seed: int | None = None) -> dict:
     """Draw one layer call's inputs. Sizes default to the workload's.
@@ -129,12 +135,12 @@ def layer_inputs(w: Workload, *, batch: int | None = None, qlen: int | None = No
         "v": _normal(rng, (w.n_head, w.d_head), 0.02),
     }
     if w.bias_clamp >= 0:
-        out["beta"] = _normal(rng, (2 * w.bias_clamp + 1, w.n_head), 0.02)
+        out["beta"] = _normal(rng, (bias_rows(w.bias_clamp, w.bias_kind), w.n_head), 0.02)
     return {k: Tensor(a, w.dtype) for k, a in out.items()}
 
 
 def core_inputs(*, batch: int, n_head: int, d_head: int, qlen: int, mlen: int, n_rows: int,
-                dtype: str, seed: int, bias_clamp: int = -1) -> dict:
+                dtype: str, seed: int, bias_clamp: int = -1, bias_kind: int = 0) -> dict:
     """Inputs for the attention core alone: head-major q, k, v, a projected
     relative table r ([n_head, n_rows, d_head], row n <-> distance n) and the
     biases u, v. Magnitudes are those of projected N(0,1) activations."""
@@ -149,5 +155,5 @@ def core_inputs(*, batch: int, n_head: int, d_head: int, qlen: int, mlen: int, n
         "vb": _normal(rng, (n_head, d_head), 0.3),
     }
     if bias_clamp >= 0:
-        out["beta"] = _normal(rng, (2 * bias_clamp + 1, n_head), 0.3)
+        out["beta"] = _normal(rng, (bias_rows(bias_clamp, bias_kind), n_head), 0.3)
     return {k: Tensor(a, dtype) for k, a in out.items()}
