@@ -257,11 +257,12 @@ __global__ void __launch_bounds__(NT, 2) attn_bf16_kernel(AttnArgs a) {
         }
         raw_buffer_load_lds(vrs, lds_ptr(lds0 + OFF_V + slot * TILE + wave * 1024), 16, voff, 0, 0, 0);
     };
-    auto dma_band = [&](int g, int slot) __attribute__((always_inline)) {
+    // band block g into the 4 KB slot at LDS offset `at`
+    auto dma_band_at = [&](int g, int at) __attribute__((always_inline)) {
         const int d = min(max(gs - BKY * g - krho, 0), rmax);
-        raw_buffer_load_lds(rrs, lds_ptr(lds0 + OFF_B + slot * TILE + wave * 1024), 16, d * 128 + (kvoff & 127), 0,
-                            0, 0);
+        raw_buffer_load_lds(rrs, lds_ptr(lds0 + at + wave * 1024), 16, d * 128 + (kvoff & 127), 0, 0, 0);
     };
+    auto dma_band = [&](int g, int slot) __attribute__((always_inline)) { dma_band_at(g, OFF_B + slot * TILE); };
     // keys past klen of the last tile: their weight is 0, but the values there
     // (padding columns of V^T) must be finite; each wave zeroes the piece its
     // own load wrote, after that load has landed
@@ -308,31 +309,25 @@ __global__ void __launch_bounds__(NT, 2) attn_bf16_kernel(AttnArgs a) {
             qvB[kc] = as_bf16x8(a_v);
         }
     }
-    // position blocks 0..2 of this wave come straight from global memory
     const int dtop = a.mlen + iw + WQ - 1;
-    bf16x8 pband[3][4];
-#pragma unroll
-    for (int be = 0; be < 3; ++be) {
-        const int d = min(max(dtop - BKY * (S0 + be) - l32, 0), rmax);
-        const bf16_t* row = (const bf16_t*)(rb + (int64_t)d * (DH * 2));
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) pband[be][kc] = as_bf16x8(*(const u32x4*)(row + 16 * kc + 8 * hf));
-    }
 
-    // ---- prologue DMAs, ordered by when they are needed: K(0), K(1), V(0) and
-    // band blocks 3..6 before step 0; K(2), V(1), band block 7 may still be in flight then
+    // ---- prologue DMAs, ordered by when they are needed. Position blocks 0..2
+    // of wave w are band blocks 3-w .. 5-w, so the prologue needs band blocks
+    // 0..5; blocks 0 and 1 go to the K and V slots that K(2) and V(1) take
+    // after the prologue (their band slots hold blocks 6 and 7 by then).
+    //   band 0..4 | K(0), band 5 | K(1), V(0), band 6 | band 7
     // (an empty split issues none and writes the neutral partial result)
+    auto band0_at = [&](int g) { return g == 0 ? OFF_V + TILE : g == 1 ? OFF_K + 2 * TILE : OFF_B + (g % 6) * TILE; };
     if (nsteps > 0) {
+#pragma unroll
+        for (int g = 0; g <= 4; ++g) dma_band_at(g, band0_at(g));
         dma_k(0, 0);
+        dma_band(5, 5);
         dma_k(1, 1);
         dma_v(0, 0);
-#pragma unroll
-        for (int g = 3; g <= 6; ++g) dma_band(g, g % 6);
-        dma_k(2, 2);
-        dma_v(1, 1);
+        dma_band(6, 0);
         dma_band(7, 1);
     }
-    constexpr int PRO_DMA = 10;
 
     // ---- bias table: entry x holds beta_h[row(X0 - x)], X0 = gtop (row: the
     // clamped distance or its T5 bucket), so that four consecutive registers
@@ -406,7 +401,12 @@ __global__ void __launch_bounds__(NT, 2) attn_bf16_kernel(AttnArgs a) {
         }
         return g;
     };
-    auto pos_reg = [&](int beta, const bf16x8* band) __attribute__((always_inline)) {
+    // position block beta (< 3) of the prologue, from band block beta + 3 - wave
+    auto pos_pro = [&](int beta) __attribute__((always_inline)) {
+        const uint32_t base = lds0 + (uint32_t)band0_at(beta + 3 - wave);
+        bf16x8 band[4];
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) band[kc] = as_bf16x8(lds_ld<u32x4>(base + baddr[kc]));
         f32x16 g = pos_init(beta);
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) g = mfma32(band[kc], qvB[kc], g);
@@ -545,16 +545,18 @@ __global__ void __launch_bounds__(NT, 2) attn_bf16_kernel(AttnArgs a) {
 
     if (nsteps > 0) {
         // ---- prologue compute: blocks 0 and 1, then the scores of step 0, then block 2
-        wait_vmcnt<PRO_DMA>();                 // query operands and the first band blocks
-        ring_write(pos_reg(0, pband[0]), 0u);
-        ring_write(pos_reg(1, pband[1]), 128u);
-        block_sync<PRO_DMA - 1>();             // K(0)
+        block_sync<6>();                       // query operands, band blocks 0..4
+        ring_write(pos_pro(0), 0u);
+        ring_write(pos_pro(1), 128u);
+        block_sync<4>();                       // K(0), band block 5
         f32x16 s0 = content(ring_read(0u), 0), s1;
-        ring_write(pos_reg(2, pband[2]), 0u);   // block 2 replaces block 0, read above
+        ring_write(pos_pro(2), 0u);            // block 2 replaces block 0, read above
         if (wsteps > 0) prepare(s0, 0);
-        wait_vmcnt<INFLIGHT>();
+        wait_vmcnt<1>();                       // all but band block 7
         if (vtail == 0) fix_v_tail(0);
         block_sync<63>();
+        dma_k(2, 2);                           // into the slots band blocks 1 and 0 held
+        dma_v(1, 1);
 
         // steps in groups of six (slot indices are compile-time constants)
         using I0 = std::integral_constant<int, 0>;
