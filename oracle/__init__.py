@@ -35,6 +35,8 @@ def _load():
         lib.orc_t5_bucket.argtypes = [_i64]
         lib.orc_t5_bucket.restype = _i64
         lib.orc_fifo_update.argtypes = [_i64, _i64, _i64, _i64, _p, _i64, _p, _p, ctypes.POINTER(_i64)]
+        lib.orc_layer_norm.argtypes = [_i64, _i64, _p, _p, _p, _dbl, _p]
+        lib.orc_layer_norm.restype = ctypes.c_int
         lib.orc_num_threads.argtypes = []
         lib.orc_num_threads.restype = ctypes.c_int
         for f in ("orc_relpos_embed", "orc_linear", "orc_rel_attn_core", "orc_rel_attn_fwd", "orc_fifo_update"):
@@ -184,3 +186,67 @@ def segment_run(stream, n_seg: int, qlen: int, mlen_max: int, weights: dict, *, 
         mem = fifo_update(mem, h, mlen_max)
         mems.append(mem)
     return outs, mems
+
+
+# --- the decoder layer and stack around the attention -------------------------------------------
+
+def layer_norm(x, gamma=None, beta=None, eps: float = 1e-5):
+    """Row-wise layer normalisation over the last axis (population variance)."""
+    x = _f64(x)
+    D = x.shape[-1]
+    x2 = x.reshape(-1, D)
+    y = np.empty_like(x2)
+    g, bt = _f64(gamma), _f64(beta)
+    _check(_load().orc_layer_norm(x2.shape[0], D, _ptr(x2), _ptr(g), _ptr(bt), eps, _ptr(y)), "orc_layer_norm")
+    return y.reshape(x.shape)
+
+
+def ffn(x, w1, b1, w2, b2):
+    """Position-wise feed-forward network: two linear layers (with biases)
+    around a ReLU [felixzhao.cn 118 §1: two linear layers and a nonlinear
+    activation; ReLU is the reading taken]."""
+    y1 = linear(x, w1) + _f64(b1)
+    y1 = np.maximum(y1, 0.0)
+    return linear(y1, w2) + _f64(b2)
+
+
+def decoder_layer_fwd(h, mem, w: dict, *, n_head: int, d_head: int, clamp_len: int = -1, bias_clamp: int = -1,
+                      bias_kind: int = 0, eps: float = 1e-5):
+    """One pre-LN decoder layer [felixzhao.cn 118 §2.3.1: N modules of masked
+    self-attention and FFN, each feeding the next; 2kiu.com §3.4: the
+    attention input is layer-normalised]:
+        a   = RelAttn(queries LN1(h), keys and values over [LN1(mem) ; LN1(h)])
+        h1  = h + a
+        out = h1 + FFN(LN2(h1)).
+    The memory holds the previous segment's layer *input* (un-normalised)."""
+    h = _f64(h)
+    xh = layer_norm(h, w["ln1_g"], w["ln1_b"], eps)
+    xm = layer_norm(mem, w["ln1_g"], w["ln1_b"], eps) if mem is not None and mem.shape[1] > 0 else None
+    a = rel_attn_fwd(xh, xm, w["w_q"], w["w_k"], w["w_v"], w["w_r"], w["w_o"], w["u"], w["v"], n_head=n_head,
+                     d_head=d_head, clamp_len=clamp_len, beta=w.get("beta"), bias_clamp=bias_clamp,
+                     bias_kind=bias_kind)
+    h1 = h + a
+    return h1 + ffn(layer_norm(h1, w["ln2_g"], w["ln2_b"], eps), w["w1"], w["b1"], w["w2"], w["b2"])
+
+
+def decoder_stack_run(stream, n_seg: int, qlen: int, mlen_max: int, layers: list, *, n_head: int, d_head: int,
+                      clamp_len: int = -1, bias_clamp: int = -1, bias_kind: int = 0, eps: float = 1e-5):
+    """Segment-recurrent run of an N-layer stack [felixzhao.cn 118 §2.3.1]:
+    layer n of segment t attends over [mem_t^n ; h_t^(n-1)] and afterwards
+    mem_(t+1)^n = FIFO(mem_t^n, h_t^(n-1)), its own input; h_t^0 is the
+    segment of the input stream. Returns the per-segment outputs of the last
+    layer and the per-segment lists of per-layer memories."""
+    stream = _f64(stream)
+    B, _, D = stream.shape
+    mems = [np.zeros((B, 0, D)) for _ in layers]
+    outs, mem_hist = [], []
+    for t in range(n_seg):
+        x = stream[:, t * qlen:(t + 1) * qlen]
+        for n, w in enumerate(layers):
+            y = decoder_layer_fwd(x, mems[n], w, n_head=n_head, d_head=d_head, clamp_len=clamp_len,
+                                  bias_clamp=bias_clamp, bias_kind=bias_kind, eps=eps)
+            mems[n] = fifo_update(mems[n], x, mlen_max)
+            x = y
+        outs.append(x)
+        mem_hist.append([m.copy() for m in mems])
+    return outs, mem_hist

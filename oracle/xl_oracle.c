@@ -338,6 +338,33 @@ int orc_fifo_update(int64_t B, int64_t D, int64_t mlen_max, int64_t mem_len, con
     return ORC_OK;
 }
 
+/*
+ * Layer normalisation of each row of x [rows, D]: the row's mean and
+ * (population) variance, then y = (x - mean) / sqrt(var + eps) * gamma + beta
+ * elementwise. The pre-LN decoder layer normalises the attention input this
+ * way [P1 §3.4: the input of the attention module is layer-normalised]; the
+ * epsilon is a parameter (the pages name 1e-5 as the usual value [P3 §4.2]).
+ * gamma and beta [D] may be NULL (1 and 0).
+ */
+int orc_layer_norm(int64_t rows, int64_t D, const double* x, const double* gamma, const double* beta, double eps,
+                   double* y) {
+    if (rows < 0 || D <= 0 || (rows && (!x || !y)) || !(eps >= 0.0)) return ORC_BAD_ARG;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const double* xr = x + r * D;
+        double mean = 0.0;
+        for (int64_t k = 0; k < D; ++k) mean += xr[k];
+        mean /= (double)D;
+        double var = 0.0;
+        for (int64_t k = 0; k < D; ++k) var += (xr[k] - mean) * (xr[k] - mean);
+        var /= (double)D;
+        const double inv = 1.0 / sqrt(var + eps);
+        for (int64_t k = 0; k < D; ++k)
+            y[r * D + k] = (xr[k] - mean) * inv * (gamma ? gamma[k] : 1.0) + (beta ? beta[k] : 0.0);
+    }
+    return ORC_OK;
+}
+
 /* Number of OpenMP threads the oracle's parallel loops use (1 without OpenMP). */
 #ifdef _OPENMP
 #include <omp.h>

@@ -71,3 +71,26 @@ def layer(h, mem, w_q, w_k, w_v, w_r, w_o, u, vb, *, n_head, d_head, clamp_len=-
         mask = visible[None, None]
         return out, [np.where(mask, t, 0.0) for t in (ta, tb, tc, td)], p
     return out
+
+
+def layer_norm(x, gamma, beta, eps):
+    """Row-wise layer normalisation with numpy's mean and variance."""
+    x = np.asarray(x, np.float64)
+    mu = x.mean(axis=-1, keepdims=True)
+    var = x.var(axis=-1, keepdims=True)
+    return (x - mu) / np.sqrt(var + eps) * np.asarray(gamma, np.float64) + np.asarray(beta, np.float64)
+
+
+def decoder_layer(h, mem, w, *, n_head, d_head, clamp_len=-1, eps=1e-5):
+    """Pre-LN decoder layer built from the gather/einsum attention above."""
+    h = np.asarray(h, np.float64)
+    xm = layer_norm(mem, w["ln1_g"], w["ln1_b"], eps) if mem is not None else None
+    xh = layer_norm(h, w["ln1_g"], w["ln1_b"], eps)
+    a = layer(xh, xm, w["w_q"], w["w_k"], w["w_v"], w["w_r"], w["w_o"], w["u"], w["v"], n_head=n_head,
+              d_head=d_head, clamp_len=clamp_len)
+    h1 = h + a
+    x2 = layer_norm(h1, w["ln2_g"], w["ln2_b"], eps)
+    y = np.maximum(np.einsum("mk,nk->mn", x2.reshape(-1, x2.shape[-1]), np.asarray(w["w1"], np.float64))
+                   + np.asarray(w["b1"], np.float64), 0.0)
+    y = y @ np.asarray(w["w2"], np.float64).T + np.asarray(w["b2"], np.float64)
+    return h1 + y.reshape(h1.shape)

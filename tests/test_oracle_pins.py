@@ -332,6 +332,91 @@ def test_causality_and_masked_keys_ignored():
     assert np.all(np.max(np.abs(_fwd(w, mem=mem2) - base), axis=-1) > 1e-6)
 
 
+# --- layer normalisation and the decoder layer ----------------------------------------------
+
+def test_layer_norm_moments_and_invariances():
+    rng = np.random.default_rng(30)
+    x = rng.standard_normal((7, 48)) * 3.0 + 1.5
+    y = oracle.layer_norm(x, eps=0.0)
+    _close(y.mean(axis=1), np.zeros(7), 1e-14)
+    _close((y * y).mean(axis=1), np.ones(7), 1e-13)           # population variance 1
+    _close(oracle.layer_norm(2.5 * x - 4.0, eps=0.0), y, 1e-13)  # affine invariance of the input
+    g, bt = rng.standard_normal(48), rng.standard_normal(48)
+    _close(oracle.layer_norm(x, g, bt, eps=0.0), y * g + bt, 1e-13)
+    # a constant row normalises to beta; eps shrinks the output variance to var/(var+eps)
+    c = np.full((2, 48), 3.25)
+    _close(oracle.layer_norm(c, g, bt, eps=1e-5), np.broadcast_to(bt, (2, 48)), 0.0)
+    v = x.var(axis=1)
+    ye = oracle.layer_norm(x, eps=0.5)
+    _close((ye * ye).mean(axis=1), v / (v + 0.5), 1e-13)
+
+
+def _dec_weights(seed, D=16, H=2, dh=8, d_inner=24):
+    w = _tiny(seed, D=D, H=H, dh=dh)
+    rng = np.random.default_rng(seed + 1000)
+    w.update(ln1_g=1.0 + 0.2 * rng.standard_normal(D), ln1_b=0.1 * rng.standard_normal(D),
+             ln2_g=1.0 + 0.2 * rng.standard_normal(D), ln2_b=0.1 * rng.standard_normal(D),
+             w1=0.3 * rng.standard_normal((d_inner, D)), b1=0.1 * rng.standard_normal(d_inner),
+             w2=0.3 * rng.standard_normal((D, d_inner)), b2=0.1 * rng.standard_normal(D))
+    return w
+
+
+def _dec(w, **over):
+    a = dict(w)
+    a.update(over)
+    return oracle.decoder_layer_fwd(a["h"], a["mem"], a, n_head=a["n_head"], d_head=a["d_head"],
+                                    clamp_len=a["clamp_len"])
+
+
+@pytest.mark.parametrize("seed,q,m,clamp", [(31, 6, 5, -1), (32, 1, 0, -1), (33, 7, 9, 3)])
+def test_decoder_layer_matches_independent_formulation(seed, q, m, clamp):
+    w = _dec_weights(seed)
+    rng = np.random.default_rng(seed)
+    w["h"] = rng.standard_normal((2, q, 16))
+    w["mem"] = rng.standard_normal((2, m, 16))
+    w["clamp_len"] = clamp
+    ref = brute.decoder_layer(w["h"], w["mem"] if m else None, w, n_head=2, d_head=8, clamp_len=clamp)
+    _close(_dec(w), ref, 1e-12)
+
+
+def test_decoder_layer_identity_and_relu_cut():
+    w = _dec_weights(34)
+    # both sublayers contribute nothing: the layer is the identity
+    z = dict(w_o=np.zeros_like(w["w_o"]), w2=np.zeros_like(w["w2"]), b2=np.zeros_like(w["b2"]))
+    _close(_dec(w, **z), w["h"], 0.0)
+    # a first-layer bias far below zero switches every ReLU off: the FFN adds b2
+    h1 = w["h"] + oracle.rel_attn_fwd(oracle.layer_norm(w["h"], w["ln1_g"], w["ln1_b"]),
+                                      oracle.layer_norm(w["mem"], w["ln1_g"], w["ln1_b"]), w["w_q"], w["w_k"],
+                                      w["w_v"], w["w_r"], w["w_o"], w["u"], w["v"], n_head=2, d_head=8)
+    _close(_dec(w, b1=np.full_like(w["b1"], -1e3)), h1 + w["b2"], 1e-13)
+
+
+def test_decoder_stack_run_memories_and_identity():
+    rng = np.random.default_rng(35)
+    layers = [_dec_weights(36 + n) for n in range(3)]
+    stream = rng.standard_normal((2, 4 * 5, 16))
+    outs, mems = oracle.decoder_stack_run(stream, 4, 5, 7, layers, n_head=2, d_head=8)
+    # layer 0's memory is the input stream itself (the last 7 rows seen)
+    for t in range(4):
+        seen = stream[:, :(t + 1) * 5]
+        _close(mems[t][0], seen[:, -7:], 0.0)
+    # a one-layer stack is the single-layer segment run with the decoder layer
+    outs1, _ = oracle.decoder_stack_run(stream, 4, 5, 7, layers[:1], n_head=2, d_head=8)
+    mem = np.zeros((2, 0, 16))
+    for t in range(4):
+        h = stream[:, t * 5:(t + 1) * 5]
+        _close(outs1[t], oracle.decoder_layer_fwd(h, mem, layers[0], n_head=2, d_head=8), 0.0)
+        mem = np.concatenate([mem, h], axis=1)[:, -7:]
+    # identity layers pass the stream through and every layer remembers it
+    ident = [dict(l, w_o=np.zeros_like(l["w_o"]), w2=np.zeros_like(l["w2"]), b2=np.zeros_like(l["b2"]))
+             for l in layers]
+    outs_i, mems_i = oracle.decoder_stack_run(stream, 4, 5, 7, ident, n_head=2, d_head=8)
+    for t in range(4):
+        _close(outs_i[t], stream[:, t * 5:(t + 1) * 5], 0.0)
+        for n in range(3):
+            _close(mems_i[t][n], mems_i[t][0], 0.0)
+
+
 def test_fifo_update_and_segment_run():
     rng = np.random.default_rng(17)
     B, D, q, mmax = 2, 16, 4, 6
