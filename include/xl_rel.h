@@ -261,6 +261,64 @@ int xl_segment_step_kv(const xl_attn_desc* desc, const xl_attn_weights* w, const
                        xl_kv_fifo* kv, void* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * ---- The decoder layer around the attention, and the stacked layers ----
+ * A decoder layer is one module of masked self-attention and a position-wise
+ * feed-forward network; N of them are stacked, each module's output feeding
+ * the next, and layer n keeps as its memory its own input states of the
+ * previous segments (felixzhao.cn article 118 §1, §2.3.1). The attention
+ * input is layer-normalised (2kiu.com §3.4), i.e. the layer is pre-LN:
+ *     a   = RelAttn(queries LN1(h), keys and values over [LN1(mem) ; LN1(h)])
+ *     h1  = h + a
+ *     out = h1 + W2 relu(W1 LN2(h1) + b1) + b2
+ * where LN is the row-wise layer normalisation (population variance,
+ * y = (x - mean) / sqrt(var + eps) * gamma + beta; eps: ln_eps, 0 selects
+ * 1e-5, the value intelliparadigm.com §4.2 names) and RelAttn is the layer of
+ * xl_rel_attn_fwd. The pages name two linear layers around a nonlinearity
+ * for the feed-forward network; the biases and the ReLU are readings taken
+ * where they are silent. h1 is rounded to desc->dtype; out is in
+ * desc->out_dtype. Every weight is in desc->dtype, on the device.
+ */
+typedef struct {
+    xl_attn_weights attn;    /* the attention sublayer (its bias table too) */
+    const void* ln1_g;       /* [D] LN1 gain */
+    const void* ln1_b;       /* [D] LN1 shift */
+    const void* ln2_g;       /* [D] LN2 gain */
+    const void* ln2_b;       /* [D] LN2 shift */
+    const void* w1;          /* [d_inner, D] */
+    const void* b1;          /* [d_inner] */
+    const void* w2;          /* [D, d_inner] */
+    const void* b2;          /* [D] */
+} xl_decoder_weights;
+
+/*
+ * One decoder layer on h [B, qlen, D] with the memory mem [B, mlen, D]
+ * (desc->mlen; may be NULL when 0). d_inner: the feed-forward width, a
+ * multiple of 32 (bf16) or 16 (f32). ws: xl_decoder_layer_workspace_size()
+ * bytes (0 for an invalid desc), 256-byte aligned. out must not alias h, mem
+ * or ws. Errors as xl_rel_attn_fwd, plus XL_BAD_SHAPE for d_inner or ln_eps.
+ */
+size_t xl_decoder_layer_workspace_size(const xl_attn_desc* desc, int64_t d_inner);
+int xl_decoder_layer_fwd(const xl_attn_desc* desc, int64_t d_inner, float ln_eps, const xl_decoder_weights* w,
+                         const void* h, const void* mem, void* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * One segment of an n_layer stack (w[n_layer], fifos[n_layer]): layer n runs
+ * on its input (h for layer 0, else layer n-1's output) over
+ * [memory of fifos[n] ; input], then fifos[n] takes that input as in
+ * xl_segment_step (its ring is written after the layer has read it; len and
+ * head are updated on return). The last layer writes out (desc->out_dtype);
+ * the inner layers' outputs stay in the workspace (desc->dtype). Every
+ * fifo's len must be <= desc->mlen; the rings must not overlap each other,
+ * h, out or ws. ws: xl_decoder_stack_workspace_size() of desc with mlen the
+ * largest fifo len of the call. On an error no fifo has been advanced unless
+ * the status is XL_HIP_ERROR.
+ */
+size_t xl_decoder_stack_workspace_size(const xl_attn_desc* desc, int64_t d_inner);
+int xl_decoder_stack_step(const xl_attn_desc* desc, int64_t d_inner, float ln_eps, int64_t n_layer,
+                          const xl_decoder_weights* w, const void* h, xl_mem_fifo* fifos, void* out, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/*
  * Timing hook: when both are non-NULL, the hipEvent_t handles ev_begin/ev_end
  * take the start and end timestamps of the fused attention kernel itself
  * (passed to the runtime with the kernel launch) in the next calls of

@@ -91,3 +91,17 @@ def oracle_layer(t: dict, w: xl_inputs.Workload, h, mem, bsel=None):
                                t["u"].f64, t["v"].f64, n_head=w.n_head, d_head=w.d_head, clamp_len=w.clamp_len,
                                beta=t["beta"].f64 if "beta" in t else None, bias_clamp=w.bias_clamp,
                                bias_kind=w.bias_kind)
+
+
+DEC_KEYS = ("ln1_g", "ln1_b", "ln2_g", "ln2_b", "w1", "b1", "w2", "b2")
+
+
+def dec_weights(lw: dict):
+    """Device weights of one decoder layer from decoder_inputs' per-layer dict."""
+    attn = xl.Weights(*(dev(lw[k]) for k in ("w_q", "w_k", "w_v", "w_r", "w_o", "u", "v")),
+                      bias_table=dev(lw["beta"]) if "beta" in lw else None)
+    return xl.DecoderWeights(attn, *(dev(lw[k]) for k in DEC_KEYS))
+
+
+def oracle_dec_weights(lw: dict) -> dict:
+    return {k: v.f64 for k, v in lw.items()}

@@ -224,3 +224,67 @@ def test_relpos_rejects_bad_arguments():
     assert lib.xl_relpos_embed(0, 4, 8, -1, 10000.0, 5, FAKE[0], None) == xl.XL_BAD_SHAPE
     assert lib.xl_relpos_embed(0, 4, 8, -1, 10000.0, xl.XL_F32, None, None) == xl.XL_NULL_ARG
     assert lib.xl_relpos_embed(0, 0, 8, -1, 10000.0, xl.XL_F32, None, None) == xl.XL_OK   # nothing to do
+
+
+def _dec_weights(bias=False, **over):
+    f = dict(ln1_g=FAKE[1], ln1_b=FAKE[2], ln2_g=FAKE[3], ln2_b=FAKE[4], w1=FAKE[5], b1=FAKE[6], w2=FAKE[7],
+             b2=FAKE[13])
+    f.update(over)
+    return xl.xl_decoder_weights(_weights(bias), *[f[k] for k in ("ln1_g", "ln1_b", "ln2_g", "ln2_b", "w1", "b1",
+                                                                  "w2", "b2")])
+
+
+def test_decoder_layer_rejects_bad_arguments():
+    lib = xl.lib()
+
+    def call(desc=None, d_inner=2048, eps=0.0, w=None, h=FAKE[8], mem=FAKE[9], out=FAKE[10], ws=FAKE[11],
+             nb=1 << 40):
+        desc = _desc() if desc is None else desc
+        w = _dec_weights() if w is None else w
+        return lib.xl_decoder_layer_fwd(ctypes.byref(desc), d_inner, eps, ctypes.byref(w), h, mem, out, ws, nb,
+                                        None)
+    assert call(w=_dec_weights(w2=None)) == xl.XL_NULL_ARG
+    assert call(w=_dec_weights(ln1_g=None)) == xl.XL_NULL_ARG
+    assert call(d_inner=0) == xl.XL_BAD_SHAPE
+    assert call(d_inner=100) == xl.XL_BAD_SHAPE                  # not a multiple of 32
+    assert call(eps=-1.0) == xl.XL_BAD_SHAPE
+    assert call(eps=float("nan")) == xl.XL_BAD_SHAPE
+    assert call(w=_dec_weights(b1=FAKE[6] + 8)) == xl.XL_UNSUPPORTED   # misaligned bias
+    assert call(h=FAKE[8] + 2) == xl.XL_UNSUPPORTED
+    assert call(out=FAKE[8]) == xl.XL_BAD_SHAPE                  # out aliases h
+    assert call(h=None) == xl.XL_NULL_ARG
+    assert call(nb=16) == xl.XL_WORKSPACE_TOO_SMALL
+    assert call(ws=FAKE[11] + 16) == xl.XL_UNSUPPORTED           # workspace alignment
+    d = _desc()
+    need = xl.xl_decoder_layer_workspace_size(d, 2048)
+    assert need > xl.xl_rel_attn_workspace_size(d)
+    assert call(nb=need - 1) == xl.XL_WORKSPACE_TOO_SMALL
+    assert xl.xl_decoder_layer_workspace_size(_desc(qlen=0), 2048) == 0
+
+
+def test_decoder_stack_rejects_bad_arguments():
+    lib = xl.lib()
+    d = _desc(mlen=128)
+
+    def call(n=2, fifos=None, w=None, h=FAKE[8], out=FAKE[10], nb=1 << 40, d_inner=2048):
+        fifos = fifos if fifos is not None else (xl.xl_mem_fifo * 2)(xl.xl_mem_fifo(FAKE[12], 128, 64, 0),
+                                                                     xl.xl_mem_fifo(FAKE[14], 128, 64, 0))
+        w = w if w is not None else (xl.xl_decoder_weights * 2)(*[_dec_weights() for _ in range(2)])
+        return lib.xl_decoder_stack_step(ctypes.byref(d), d_inner, 0.0, n, w, h, fifos, out, FAKE[11], nb, None)
+    assert call(n=0) == xl.XL_BAD_SHAPE
+    two = lambda a, b: (xl.xl_mem_fifo * 2)(a, b)
+    assert call(fifos=two(xl.xl_mem_fifo(FAKE[12], 128, 129, 0), xl.xl_mem_fifo(FAKE[14], 128, 0, 0))) == \
+        xl.XL_BAD_SHAPE                                              # len > mlen_max
+    assert call(fifos=two(xl.xl_mem_fifo(FAKE[12], 256, 200, 0), xl.xl_mem_fifo(FAKE[14], 256, 0, 0))) == \
+        xl.XL_BAD_SHAPE                                              # len > desc->mlen
+    assert call(fifos=two(xl.xl_mem_fifo(FAKE[12], 128, 64, 0), xl.xl_mem_fifo(FAKE[12] + 4096, 128, 64, 0))) == \
+        xl.XL_BAD_SHAPE                                              # rings overlap
+    assert call(h=FAKE[14] + 64) == xl.XL_BAD_SHAPE                  # h inside a ring
+    assert call(out=FAKE[8]) == xl.XL_BAD_SHAPE                      # out aliases h
+    assert call(d_inner=48) == xl.XL_BAD_SHAPE
+    fifos = two(xl.xl_mem_fifo(FAKE[12], 128, 64, 5), xl.xl_mem_fifo(FAKE[14], 128, 64, 7))
+    assert call(fifos=fifos, nb=16) == xl.XL_WORKSPACE_TOO_SMALL
+    assert [(f.len, f.head) for f in fifos] == [(64, 5), (64, 7)]    # untouched on error
+    need = xl.xl_decoder_stack_workspace_size(d, 2048)
+    assert need > xl.xl_decoder_layer_workspace_size(d, 2048)
+    assert call(fifos=fifos, nb=need - 1) == xl.XL_WORKSPACE_TOO_SMALL

@@ -1,0 +1,114 @@
+"""GPU parity of the pre-LN decoder layer and the segment-recurrent decoder
+stack against the fp64 oracle, through the C ABI."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle
+import transformer_xl_relative_amd as xl
+import xl_inputs
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+W = xl_inputs.WORKLOADS
+
+
+@pytest.fixture(scope="module")
+def T():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    xl.lib()
+    return torch
+
+
+def _desc(w, *, batch, qlen, mlen, out_f32=True):
+    dt = xl.XL_BF16 if w.dtype == "bf16" else xl.XL_F32
+    return xl.make_desc(batch=batch, d_model=w.d_model, n_head=w.n_head, d_head=w.d_head, qlen=qlen, mlen=mlen,
+                        clamp_len=w.clamp_len, bias_clamp=w.bias_clamp, bias_kind=w.bias_kind, dtype=dt,
+                        out_dtype=xl.XL_F32 if out_f32 else dt)
+
+
+def _oracle_layer(t, w, lw, h, mem):
+    return oracle.decoder_layer_fwd(h, mem, gu.oracle_dec_weights(lw), n_head=w.n_head, d_head=w.d_head,
+                                    clamp_len=w.clamp_len, bias_clamp=w.bias_clamp, bias_kind=w.bias_kind)
+
+
+def _run_layer(T, w, t, *, batch, qlen, mlen, d_inner):
+    desc = _desc(w, batch=batch, qlen=qlen, mlen=mlen)
+    ws = T.empty(xl.xl_decoder_layer_workspace_size(desc, d_inner), dtype=T.uint8, device="cuda")
+    out = T.empty((batch, qlen, w.d_model), dtype=T.float32, device="cuda")
+    xl.xl_decoder_layer_fwd(desc, d_inner, 0.0, gu.dec_weights(t["layers"][0]), gu.dev(t["h"]),
+                            gu.dev(t["mem"]) if mlen else None, out, ws)
+    T.cuda.synchronize()
+    return gu.host64(out)
+
+
+@pytest.mark.parametrize("base,qlen,mlen,d_inner,bias", [("base_bf16", 70, 45, 256, -1), ("base_bf16", 128, 0, 512, -1),
+                                                         ("base_bf16", 37, 91, 96, 16), ("tiny_f32", 9, 13, 32, -1),
+                                                         ("tiny_f32", 8, 8, 64, 3)])
+def test_decoder_layer(T, base, qlen, mlen, d_inner, bias):
+    w = dataclasses.replace(W[base], bias_clamp=bias, seed=qlen * 7 + mlen)
+    t = xl_inputs.decoder_inputs(w, d_inner=d_inner, n_layer=1, batch=2, qlen=qlen, mlen=mlen)
+    got = _run_layer(T, w, t, batch=2, qlen=qlen, mlen=mlen, d_inner=d_inner)
+    ref = _oracle_layer(t, w, t["layers"][0], t["h"].f64, t["mem"].f64)
+    gu.compare(f"decoder layer {base} q{qlen} m{mlen}", got, ref, dtype=w.dtype)
+
+
+def test_decoder_layer_large_sampled(T):
+    # the large workload's shape with a 4096-wide feed-forward network; batch 0 checked
+    w = W["large_bf16"]
+    t = xl_inputs.decoder_inputs(w, d_inner=4096, n_layer=1)
+    got = _run_layer(T, w, t, batch=w.batch, qlen=w.qlen, mlen=w.mlen, d_inner=4096)
+    ref = _oracle_layer(t, w, t["layers"][0], t["h"].f64[:1], t["mem"].f64[:1])
+    gu.compare("decoder layer large (batch 0)", got[:1], ref, dtype="bf16")
+
+
+def _stack_run(T, w, t, *, batch, qlen, n_seg, mlen_max, d_inner, n_layer, head0=0):
+    D = w.d_model
+    dt = T.bfloat16 if w.dtype == "bf16" else T.float32
+    rings = [T.zeros((batch, mlen_max, D), dtype=dt, device="cuda") for _ in range(n_layer)]
+    fifos = (xl.xl_mem_fifo * n_layer)(*[xl.xl_mem_fifo(r.data_ptr(), mlen_max, 0, head0) for r in rings])
+    weights = [gu.dec_weights(lw) for lw in t["layers"]]
+    hs = gu.dev(t["h"])
+    outs, mems = [], []
+    for s in range(n_seg):
+        desc = _desc(w, batch=batch, qlen=qlen, mlen=fifos[0].len)
+        ws = T.empty(xl.xl_decoder_stack_workspace_size(desc, d_inner), dtype=T.uint8, device="cuda")
+        h = hs[:, s * qlen:(s + 1) * qlen].contiguous()
+        out = T.empty((batch, qlen, D), dtype=T.float32, device="cuda")
+        xl.xl_decoder_stack_step(desc, d_inner, 0.0, weights, h, fifos, out, ws)
+        T.cuda.synchronize()
+        outs.append(gu.host64(out))
+        # each ring in age order (oldest first)
+        cur = []
+        for n in range(n_layer):
+            f = fifos[n]
+            idx = [(f.head + i) % mlen_max for i in range(f.len)]
+            cur.append(rings[n][:, idx].clone())
+        mems.append(cur)
+    return outs, mems
+
+
+@pytest.mark.parametrize("base,qlen,n_seg,mlen_max,d_inner,n_layer,head0",
+                         [("base_bf16", 64, 4, 96, 256, 3, 0), ("base_bf16", 40, 3, 100, 128, 2, 37),
+                          ("tiny_f32", 8, 4, 12, 32, 3, 5)])
+def test_decoder_stack_run(T, base, qlen, n_seg, mlen_max, d_inner, n_layer, head0):
+    w = dataclasses.replace(W[base], segments=n_seg, qlen=qlen, mlen=mlen_max, seed=n_layer * 10 + qlen)
+    t = xl_inputs.decoder_inputs(w, d_inner=d_inner, n_layer=n_layer, batch=2, qlen=qlen)
+    outs, mems = _stack_run(T, w, t, batch=2, qlen=qlen, n_seg=n_seg, mlen_max=mlen_max, d_inner=d_inner,
+                            n_layer=n_layer, head0=head0)
+    routs, rmems = oracle.decoder_stack_run(t["h"].f64, n_seg, qlen, mlen_max,
+                                            [gu.oracle_dec_weights(lw) for lw in t["layers"]], n_head=w.n_head,
+                                            d_head=w.d_head, clamp_len=w.clamp_len)
+    for s in range(n_seg):
+        gu.compare(f"stack segment {s}", outs[s], routs[s], dtype=w.dtype)
+        # layer 0 keeps the input stream itself: bit for bit
+        if w.dtype == "bf16":
+            want = xl_inputs.bf16_bits(rmems[s][0].astype(np.float32))
+            assert np.array_equal(gu.bits_u16(mems[s][0]), want), f"layer 0 memory after segment {s}"
+        else:
+            assert np.array_equal(gu.host64(mems[s][0]), rmems[s][0]), f"layer 0 memory after segment {s}"
+        for n in range(1, n_layer):
+            gu.compare(f"layer {n} memory after segment {s}", gu.host64(mems[s][n]), rmems[s][n], dtype=w.dtype)

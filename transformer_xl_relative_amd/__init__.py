@@ -61,7 +61,9 @@ _lib = None
 
 EXPORTS = ("xl_status_string", "xl_last_error", "xl_relpos_embed", "xl_rel_attn_workspace_size",
            "xl_rel_attn_workspace_layout", "xl_rel_attn_fwd", "xl_rel_attn_core_workspace_size", "xl_rel_attn_core",
-           "xl_segment_step", "xl_segment_step_kv_workspace_size", "xl_segment_step_kv", "xl_set_core_events")
+           "xl_segment_step", "xl_segment_step_kv_workspace_size", "xl_segment_step_kv", "xl_set_core_events",
+           "xl_decoder_layer_workspace_size", "xl_decoder_layer_fwd", "xl_decoder_stack_workspace_size",
+           "xl_decoder_stack_step")
 
 
 def lib():
@@ -102,8 +104,18 @@ def lib():
         L.xl_segment_step_kv_workspace_size.restype = ctypes.c_size_t
         L.xl_segment_step_kv.argtypes = [ctypes.POINTER(xl_attn_desc), ctypes.POINTER(xl_attn_weights), _p,
                                          ctypes.POINTER(xl_kv_fifo), _p, _p, ctypes.c_size_t, _p]
+        D = ctypes.POINTER(xl_attn_desc)
+        L.xl_decoder_layer_workspace_size.argtypes = [D, _i64]
+        L.xl_decoder_layer_workspace_size.restype = ctypes.c_size_t
+        L.xl_decoder_layer_fwd.argtypes = [D, _i64, ctypes.c_float, ctypes.POINTER(xl_decoder_weights), _p, _p, _p,
+                                           _p, ctypes.c_size_t, _p]
+        L.xl_decoder_stack_workspace_size.argtypes = [D, _i64]
+        L.xl_decoder_stack_workspace_size.restype = ctypes.c_size_t
+        L.xl_decoder_stack_step.argtypes = [D, _i64, ctypes.c_float, _i64, ctypes.POINTER(xl_decoder_weights), _p,
+                                            ctypes.POINTER(xl_mem_fifo), _p, _p, ctypes.c_size_t, _p]
         for f in ("xl_relpos_embed", "xl_rel_attn_workspace_layout", "xl_rel_attn_fwd", "xl_rel_attn_core",
-                  "xl_segment_step", "xl_set_core_events", "xl_segment_step_kv"):
+                  "xl_segment_step", "xl_set_core_events", "xl_segment_step_kv", "xl_decoder_layer_fwd",
+                  "xl_decoder_stack_step"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -155,6 +167,29 @@ class Weights:
     def c(self) -> xl_attn_weights:
         return xl_attn_weights(*[_ptr(getattr(self, f)) for f in
                                  ("w_q", "w_k", "w_v", "w_r", "w_o", "u", "v", "bias_table")])
+
+
+class xl_decoder_weights(ctypes.Structure):
+    _fields_ = [("attn", xl_attn_weights)] + [(n, _p) for n in ("ln1_g", "ln1_b", "ln2_g", "ln2_b", "w1", "b1", "w2",
+                                                                "b2")]
+
+
+@dataclasses.dataclass
+class DecoderWeights:
+    """Weights of one pre-LN decoder layer as device tensors."""
+    attn: Weights
+    ln1_g: object
+    ln1_b: object
+    ln2_g: object
+    ln2_b: object
+    w1: object
+    b1: object
+    w2: object
+    b2: object
+
+    def c(self) -> xl_decoder_weights:
+        return xl_decoder_weights(self.attn.c(), *[_ptr(getattr(self, f)) for f in
+                                                   ("ln1_g", "ln1_b", "ln2_g", "ln2_b", "w1", "b1", "w2", "b2")])
 
 
 def xl_relpos_embed(delta0: int, n_rows: int, d_model: int, clamp_len: int, base: float, out, stream=None):
@@ -260,3 +295,31 @@ class HipEvent:
     def __del__(self):
         if self._rt is not None and self.handle:
             self._rt.hipEventDestroy(self.handle)
+
+
+def xl_decoder_layer_workspace_size(desc: xl_attn_desc, d_inner: int) -> int:
+    return lib().xl_decoder_layer_workspace_size(ctypes.byref(desc), d_inner)
+
+
+def xl_decoder_layer_fwd(desc: xl_attn_desc, d_inner: int, ln_eps: float, weights, h, mem, out, ws, stream=None):
+    cw = weights.c() if isinstance(weights, DecoderWeights) else weights
+    _check(lib().xl_decoder_layer_fwd(ctypes.byref(desc), d_inner, ln_eps, ctypes.byref(cw), _ptr(h), _ptr(mem),
+                                      _ptr(out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return out
+
+
+def xl_decoder_stack_workspace_size(desc: xl_attn_desc, d_inner: int) -> int:
+    return lib().xl_decoder_stack_workspace_size(ctypes.byref(desc), d_inner)
+
+
+def xl_decoder_stack_step(desc: xl_attn_desc, d_inner: int, ln_eps: float, weights: list, h, fifos, out, ws,
+                          stream=None):
+    """weights: one DecoderWeights (or xl_decoder_weights) per layer; fifos: a
+    ctypes array of xl_mem_fifo (updated in place)."""
+    n = len(weights)
+    cw = (xl_decoder_weights * n)(*[w.c() if isinstance(w, DecoderWeights) else w for w in weights])
+    if len(fifos) != n:
+        raise ValueError("one fifo per layer")
+    _check(lib().xl_decoder_stack_step(ctypes.byref(desc), d_inner, ln_eps, n, cw, _ptr(h), fifos, _ptr(out),
+                                       _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return out

@@ -133,7 +133,8 @@ int run_core(const xl::AttnArgs& a, bool bf16, int dh, hipStream_t s) {
     return XL_OK;
 }
 
-// The layer forward on a memory that is either a plain [B, mlen, D] tensor
+// The layer forward (residual, when not null: [B, qlen, D] in desc->dtype,
+// added to the output projection) on a memory that is either a plain [B, mlen, D] tensor
 // (ring_len == mlen, ring_head == 0) or a FIFO ring; fifo_write (may be null)
 // is the ring update, carried out by the output projection's launch (after
 // every read of the ring). With kv (not null) the memory is a key ring of
@@ -142,7 +143,7 @@ int run_core(const xl::AttnArgs& a, bool bf16, int dh, hipStream_t s) {
 // keys from it (mem, ring_len, ring_head unused).
 int layer_forward(const xl_attn_desc* d, const xl_attn_weights* w, const void* h, const void* mem, int64_t mlen,
                   int64_t ring_len, int64_t ring_head, void* out, void* ws, size_t ws_bytes, hipStream_t s,
-                  const xl::RowCopy* fifo_write, const xl_kv_fifo* kv = nullptr) {
+                  const xl::RowCopy* fifo_write, const xl_kv_fifo* kv = nullptr, const void* residual = nullptr) {
     xl_ws_layout L;
     fill_layout(d, mlen, &L, kv != nullptr);
     if (ws_bytes < L.total)
@@ -250,6 +251,7 @@ int layer_forward(const xl_attn_desc* d, const xl_attn_weights* w, const void* h
     go.a0 = W + L.attn; go.lda = HD; go.a_seq = 0;
     go.b0 = w->w_o; go.b_split = 1 << 30; go.epi = xl::EPI_OUT; go.out0 = out;
     go.out_bf16 = d->out_dtype == XL_BF16;
+    go.res = residual;
     go.H = (int)H; go.dh = (int)dh;
     if ((e = xl::launch_gemm(go, bf, s, fifo_write)) != hipSuccess) return hip_fail(e, "output projection launch");
     return XL_OK;
@@ -261,6 +263,134 @@ int check_weights(const xl_attn_desc* d, const xl_attn_weights* w) {
         return fail(XL_NULL_ARG, "a weight pointer is NULL");
     if (d->bias_clamp >= 0 && !w->bias_table) return fail(XL_NULL_ARG, "bias_clamp >= 0 but bias_table is NULL");
     return XL_OK;
+}
+
+// ---- the pre-LN decoder layer around the attention ----------------------------------------------
+
+struct DecLayout {
+    size_t attn_total;                    // the attention layer's workspace, at offset 0
+    size_t xm, xs, h1, x2, y1, buf0, buf1, total;
+};
+
+// stack: two more [B, qlen, D] buffers for the outputs of the inner layers
+void dec_layout(const xl_attn_desc* d, int64_t mlen, int64_t d_inner, bool stack, DecLayout* L) {
+    xl_ws_layout A;
+    fill_layout(d, mlen, &A);
+    const size_t es = esize(d->dtype);
+    const int64_t B = d->batch, q = d->qlen, D = d->d_model;
+    size_t off = align_up(A.total);
+    auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
+    L->attn_total = A.total;
+    L->xm = take((size_t)(B * mlen * D) * es);
+    L->xs = take((size_t)(B * q * D) * es);
+    L->h1 = take((size_t)(B * q * D) * es);
+    L->x2 = take((size_t)(B * q * D) * es);
+    L->y1 = take((size_t)(B * q * d_inner) * es);
+    L->buf0 = take(stack ? (size_t)(B * q * D) * es : 0);
+    L->buf1 = take(stack ? (size_t)(B * q * D) * es : 0);
+    L->total = off;
+}
+
+int check_decoder(const xl_attn_desc* d, int64_t d_inner, float eps, const xl_decoder_weights* w) {
+    if (!w) return fail(XL_NULL_ARG, "weights is NULL");
+    int st = check_weights(d, &w->attn);
+    if (st != XL_OK) return st;
+    if (!w->ln1_g || !w->ln1_b || !w->ln2_g || !w->ln2_b || !w->w1 || !w->b1 || !w->w2 || !w->b2)
+        return fail(XL_NULL_ARG, "a layer norm or feed-forward weight pointer is NULL");
+    const int64_t mult = d->dtype == XL_BF16 ? 32 : 16;
+    if (d_inner < 1 || d_inner % mult) return fail(XL_BAD_SHAPE, "d_inner must be a positive multiple of %lld", (long long)mult);
+    if (d_inner > 262144) return fail(XL_UNSUPPORTED, "d_inner above 262144");
+    if (d->batch * d->qlen * d_inner > kI32) return fail(XL_UNSUPPORTED, "batch * qlen * d_inner too large");
+    if (!(eps >= 0.f) || !isfinite(eps)) return fail(XL_BAD_SHAPE, "ln_eps must be finite and >= 0");
+    // the bf16 epilogue reads the biases 16 bytes at a time
+    if (((uintptr_t)w->b1 | (uintptr_t)w->b2) % 16) return fail(XL_UNSUPPORTED, "b1 and b2 must be 16-byte aligned");
+    return XL_OK;
+}
+
+// One decoder layer on a memory that is a plain tensor or a FIFO ring (as in
+// layer_forward); fifo_write (may be null) copies h into the ring after every
+// read of it.
+//   xm, xs = LN1(mem), LN1(h); h1 = h + RelAttn(xs over [xm ; xs]);
+//   out = h1 + W2 relu(W1 LN2(h1) + b1) + b2
+int decoder_forward(const xl_attn_desc* d, int64_t d_inner, float eps, const xl_decoder_weights* w, const void* h,
+                    const void* mem, int64_t mlen, int64_t ring_len, int64_t ring_head, void* out, void* ws,
+                    size_t ws_bytes, hipStream_t s, const xl::RowCopy* fifo_write) {
+    DecLayout L;
+    dec_layout(d, mlen, d_inner, false, &L);
+    if (ws_bytes < L.total)
+        return fail(XL_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", ws_bytes, L.total);
+    if (((uintptr_t)ws) % kAlign) return fail(XL_UNSUPPORTED, "workspace must be 256-byte aligned");
+    const bool bf = d->dtype == XL_BF16;
+    const int64_t B = d->batch, q = d->qlen, D = d->d_model, klen = mlen + q;
+    char* W = (char*)ws;
+    hipError_t e;
+    // 1. LN1 of every row of [memory ; segment]
+    xl::LnArgs ln;
+    memset(&ln, 0, sizeof ln);
+    ln.a0 = mlen ? mem : h; ln.a1 = h;
+    ln.a0_bstride = ring_len * D; ln.a1_bstride = q * D;
+    ln.a_seq = (int)klen; ln.a_split = (int)mlen; ln.ring_len = (int)(ring_len > 0 ? ring_len : 1);
+    ln.ring_head = (int)ring_head;
+    ln.y0 = W + L.xm; ln.y1 = W + L.xs;
+    ln.gamma = w->ln1_g; ln.beta = w->ln1_b;
+    ln.rows = (int)(B * klen); ln.D = (int)D; ln.eps = eps;
+    if ((e = xl::launch_layer_norm(ln, bf, s)) != hipSuccess) return hip_fail(e, "layer norm launch");
+    // 2. attention sublayer with the residual: h1 = h + RelAttn(...)
+    xl_attn_desc da = *d;
+    da.mlen = mlen;
+    da.out_dtype = d->dtype;
+    int st = layer_forward(&da, &w->attn, W + L.xs, W + L.xm, mlen, mlen, 0, W + L.h1, W, L.attn_total, s, fifo_write,
+                           nullptr, h);
+    if (st != XL_OK) return st;
+    // 3. LN2(h1)
+    ln.a0 = W + L.h1; ln.a1 = W + L.h1;
+    ln.a0_bstride = q * D; ln.a1_bstride = q * D;
+    ln.a_seq = (int)q; ln.a_split = 0; ln.ring_len = 1; ln.ring_head = 0;
+    ln.y0 = W + L.x2; ln.y1 = W + L.x2;
+    ln.gamma = w->ln2_g; ln.beta = w->ln2_b;
+    ln.rows = (int)(B * q);
+    if ((e = xl::launch_layer_norm(ln, bf, s)) != hipSuccess) return hip_fail(e, "layer norm launch");
+    // 4-5. the feed-forward network with its residual
+    xl::GemmArgs g;
+    memset(&g, 0, sizeof g);
+    g.M = (int)(B * q); g.N = (int)d_inner; g.K = (int)D;
+    g.a0 = W + L.x2; g.lda = D; g.a_seq = 0;
+    g.b0 = w->w1; g.b_split = 1 << 30; g.epi = xl::EPI_OUT; g.out0 = W + L.y1; g.out_bf16 = bf ? 1 : 0;
+    g.H = (int)d->n_head; g.dh = (int)d->d_head;
+    g.bias_n = w->b1; g.relu = 1;
+    if ((e = xl::launch_gemm(g, bf, s)) != hipSuccess) return hip_fail(e, "feed-forward launch");
+    g.N = (int)D; g.K = (int)d_inner;
+    g.a0 = W + L.y1; g.lda = d_inner;
+    g.b0 = w->w2; g.out0 = out; g.out_bf16 = d->out_dtype == XL_BF16;
+    g.bias_n = w->b2; g.relu = 0; g.res = W + L.h1;
+    if ((e = xl::launch_gemm(g, bf, s)) != hipSuccess) return hip_fail(e, "feed-forward launch");
+    return XL_OK;
+}
+
+int check_fifo(const xl_mem_fifo* f) {
+    if (!f) return fail(XL_NULL_ARG, "fifo is NULL");
+    if (!f->buf) return fail(XL_NULL_ARG, "fifo->buf is NULL");
+    if (f->mlen_max < 1 || f->len < 0 || f->len > f->mlen_max || f->head < 0 || f->head >= f->mlen_max)
+        return fail(XL_BAD_SHAPE, "fifo state invalid (mlen_max %lld, len %lld, head %lld)", (long long)f->mlen_max,
+                    (long long)f->len, (long long)f->head);
+    if (f->mlen_max > kI32 / 64) return fail(XL_UNSUPPORTED, "mlen_max too large");
+    return XL_OK;
+}
+
+// the FIFO update of a segment step: row t of h lands at ring row
+// (head + len + t) % mlen_max; only the last min(qlen, mlen_max) rows survive
+xl::RowCopy fifo_copy(const xl_attn_desc* d, const xl_mem_fifo* f, const void* h) {
+    const int64_t M = f->mlen_max, q = d->qlen;
+    const int64_t n_w = q < M ? q : M;
+    const int64_t src0 = q - n_w;
+    const int64_t dst0 = (f->head + f->len + src0) % M;
+    return xl::RowCopy{h, f->buf, q, M, dst0, src0, n_w, d->batch, d->d_model * (int64_t)esize(d->dtype)};
+}
+void fifo_advance(const xl_attn_desc* d, xl_mem_fifo* f) {
+    const int64_t M = f->mlen_max, q = d->qlen;
+    const int64_t new_len = f->len + q < M ? f->len + q : M;
+    f->head = (f->head + f->len + q - new_len) % M;
+    f->len = new_len;
 }
 
 }  // namespace
@@ -387,15 +517,9 @@ int xl_rel_attn_core(const xl_attn_desc* desc, const void* q, const void* k, con
 int xl_segment_step(const xl_attn_desc* desc, const xl_attn_weights* w, const void* h, xl_mem_fifo* fifo, void* out,
                     void* ws, size_t ws_bytes, void* stream) {
     g_last_error.clear();
-    if (!fifo) return fail(XL_NULL_ARG, "fifo is NULL");
-    if (!fifo->buf) return fail(XL_NULL_ARG, "fifo->buf is NULL");
-    if (fifo->mlen_max < 1 || fifo->len < 0 || fifo->len > fifo->mlen_max || fifo->head < 0 ||
-        fifo->head >= fifo->mlen_max)
-        return fail(XL_BAD_SHAPE, "fifo state invalid (mlen_max %lld, len %lld, head %lld)", (long long)fifo->mlen_max,
-                    (long long)fifo->len, (long long)fifo->head);
-    int st = check_desc(desc, fifo->len, true);
+    int st = check_fifo(fifo);
     if (st != XL_OK) return st;
-    if (fifo->mlen_max > kI32 / 64) return fail(XL_UNSUPPORTED, "mlen_max too large");
+    if ((st = check_desc(desc, fifo->len, true)) != XL_OK) return st;
     if ((st = check_weights(desc, w)) != XL_OK) return st;
     if (!h || !out || !ws) return fail(XL_NULL_ARG, "h, out and ws must be non-NULL");
     const size_t es = esize(desc->dtype);
@@ -409,18 +533,10 @@ int xl_segment_step(const xl_attn_desc* desc, const xl_attn_weights* w, const vo
     xl_attn_desc d = *desc;
     d.mlen = fifo->len;
     hipStream_t s = (hipStream_t)stream;
-    // FIFO update: row t of h lands at ring row (head + len + t) % mlen_max;
-    // only the last min(qlen, mlen_max) rows survive, so only those are written.
-    const int64_t M = fifo->mlen_max, q = desc->qlen;
-    const int64_t n_w = q < M ? q : M;
-    const int64_t src0 = q - n_w;
-    const int64_t dst0 = (fifo->head + fifo->len + src0) % M;
-    const xl::RowCopy cp{h, fifo->buf, q, M, dst0, src0, n_w, desc->batch, desc->d_model * (int64_t)es};
+    const xl::RowCopy cp = fifo_copy(desc, fifo, h);
     st = layer_forward(&d, w, h, fifo->buf, fifo->len, fifo->mlen_max, fifo->head, out, ws, ws_bytes, s, &cp);
     if (st != XL_OK) return st;
-    const int64_t new_len = fifo->len + q < M ? fifo->len + q : M;
-    fifo->head = (fifo->head + fifo->len + q - new_len) % M;
-    fifo->len = new_len;
+    fifo_advance(desc, fifo);
     return XL_OK;
 }
 
@@ -468,6 +584,97 @@ int xl_segment_step_kv(const xl_attn_desc* desc, const xl_attn_weights* w, const
     const int64_t new_len = total < M ? total : M;
     kv->head = (kv->head + total - new_len) % C;
     kv->len = new_len;
+    return XL_OK;
+}
+
+size_t xl_decoder_layer_workspace_size(const xl_attn_desc* desc, int64_t d_inner) {
+    if (!desc || check_desc(desc, desc->mlen, true) != XL_OK || d_inner < 1) return 0;
+    DecLayout L;
+    dec_layout(desc, desc->mlen, d_inner, false, &L);
+    return L.total;
+}
+
+int xl_decoder_layer_fwd(const xl_attn_desc* desc, int64_t d_inner, float ln_eps, const xl_decoder_weights* w,
+                         const void* h, const void* mem, void* out, void* ws, size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    int st = check_desc(desc, desc ? desc->mlen : 0, true);
+    if (st != XL_OK) return st;
+    const float eps = ln_eps == 0.f ? 1e-5f : ln_eps;
+    if ((st = check_decoder(desc, d_inner, eps, w)) != XL_OK) return st;
+    if (!h || !out || !ws) return fail(XL_NULL_ARG, "h, out and ws must be non-NULL");
+    if (desc->mlen > 0 && !mem) return fail(XL_NULL_ARG, "mem is NULL with mlen > 0");
+    if ((uintptr_t)h % 16) return fail(XL_UNSUPPORTED, "h must be 16-byte aligned");
+    const size_t es = esize(desc->dtype);
+    const size_t out_bytes = (size_t)(desc->batch * desc->qlen * desc->d_model) * esize(desc->out_dtype);
+    const size_t h_bytes = (size_t)(desc->batch * desc->qlen * desc->d_model) * es;
+    if (overlaps(out, out_bytes, h, h_bytes) ||
+        (desc->mlen > 0 && overlaps(out, out_bytes, mem, (size_t)(desc->batch * desc->mlen * desc->d_model) * es)) ||
+        overlaps(out, out_bytes, ws, ws_bytes))
+        return fail(XL_BAD_SHAPE, "out aliases an input or the workspace");
+    return decoder_forward(desc, d_inner, eps, w, h, mem, desc->mlen, desc->mlen, 0, out, ws, ws_bytes,
+                           (hipStream_t)stream, nullptr);
+}
+
+size_t xl_decoder_stack_workspace_size(const xl_attn_desc* desc, int64_t d_inner) {
+    if (!desc || check_desc(desc, desc->mlen, true) != XL_OK || d_inner < 1) return 0;
+    DecLayout L;
+    dec_layout(desc, desc->mlen, d_inner, true, &L);
+    return L.total;
+}
+
+int xl_decoder_stack_step(const xl_attn_desc* desc, int64_t d_inner, float ln_eps, int64_t n_layer,
+                          const xl_decoder_weights* w, const void* h, xl_mem_fifo* fifos, void* out, void* ws,
+                          size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    if (!desc) return fail(XL_NULL_ARG, "desc is NULL");
+    if (n_layer < 1 || n_layer > 4096) return fail(XL_BAD_SHAPE, "n_layer must be in [1, 4096]");
+    if (!w || !fifos) return fail(XL_NULL_ARG, "weights and fifos must be non-NULL");
+    if (!h || !out || !ws) return fail(XL_NULL_ARG, "h, out and ws must be non-NULL");
+    if ((uintptr_t)h % 16) return fail(XL_UNSUPPORTED, "h must be 16-byte aligned");
+    const float eps = ln_eps == 0.f ? 1e-5f : ln_eps;
+    const size_t es = esize(desc->dtype);
+    const size_t h_bytes = (size_t)(desc->batch * desc->qlen * desc->d_model) * es;
+    const size_t out_bytes = (size_t)(desc->batch * desc->qlen * desc->d_model) * esize(desc->out_dtype);
+    int st;
+    for (int64_t n = 0; n < n_layer; ++n) {
+        if ((st = check_fifo(&fifos[n])) != XL_OK) return st;
+        if (fifos[n].len > desc->mlen)
+            return fail(XL_BAD_SHAPE, "fifo %lld holds %lld rows, more than desc->mlen = %lld", (long long)n,
+                        (long long)fifos[n].len, (long long)desc->mlen);
+        if ((st = check_desc(desc, fifos[n].len, true)) != XL_OK) return st;
+        if ((st = check_decoder(desc, d_inner, eps, &w[n])) != XL_OK) return st;
+        const size_t ring_bytes = (size_t)(desc->batch * fifos[n].mlen_max * desc->d_model) * es;
+        if (overlaps(h, h_bytes, fifos[n].buf, ring_bytes) || overlaps(out, out_bytes, fifos[n].buf, ring_bytes) ||
+            overlaps(ws, ws_bytes, fifos[n].buf, ring_bytes))
+            return fail(XL_BAD_SHAPE, "fifo %lld's ring aliases h, out or the workspace", (long long)n);
+        for (int64_t k = 0; k < n; ++k)
+            if (overlaps(fifos[k].buf, (size_t)(desc->batch * fifos[k].mlen_max * desc->d_model) * es, fifos[n].buf,
+                         ring_bytes))
+                return fail(XL_BAD_SHAPE, "the rings of fifos %lld and %lld overlap", (long long)k, (long long)n);
+    }
+    if (overlaps(out, out_bytes, h, h_bytes) || overlaps(out, out_bytes, ws, ws_bytes))
+        return fail(XL_BAD_SHAPE, "out aliases h or the workspace");
+    DecLayout L;
+    dec_layout(desc, desc->mlen, d_inner, true, &L);
+    if (ws_bytes < L.total)
+        return fail(XL_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", ws_bytes, L.total);
+    hipStream_t s = (hipStream_t)stream;
+    char* W = (char*)ws;
+    // layer n reads the output of layer n-1 and keeps that input in its own ring
+    const void* x = h;
+    for (int64_t n = 0; n < n_layer; ++n) {
+        const bool last = n == n_layer - 1;
+        void* y = last ? out : (void*)(W + ((n & 1) ? L.buf1 : L.buf0));
+        xl_attn_desc d = *desc;
+        d.mlen = fifos[n].len;
+        if (!last) d.out_dtype = desc->dtype;
+        const xl::RowCopy cp = fifo_copy(desc, &fifos[n], x);
+        st = decoder_forward(&d, d_inner, eps, &w[n], x, fifos[n].buf, fifos[n].len, fifos[n].mlen_max, fifos[n].head,
+                             y, W, L.buf0, s, &cp);
+        if (st != XL_OK) return st;
+        fifo_advance(desc, &fifos[n]);
+        x = y;
+    }
     return XL_OK;
 }
 

@@ -239,14 +239,23 @@ __device__ __forceinline__ void tile_bf16(const GemmArgs& g, int m0, int n0, cha
                 const u32x4 w = lds_ld128(wbuf + (rl + RPI * k) * PITCH + ch * 16);
                 if (m < g.M && n < ncols) {
                     if (epi == EPI_OUT) {
-                        if (g.out_bf16) {
+                        // the extras apply to the staged (rounded) values, 8 columns at a time
+                        const bool extras = g.bias_n || g.res || g.relu;
+                        if (g.out_bf16 && !extras) {
                             *(u32x4*)((bf16_t*)g.out0 + (int64_t)m * g.N + n) = w;
                         } else {
-                            float* o = (float*)g.out0 + (int64_t)m * g.N + n;
-                            *(f32x4*)o = (f32x4){bf2f(w[0] & 0xFFFF), bf2f(w[0] >> 16), bf2f(w[1] & 0xFFFF),
-                                                 bf2f(w[1] >> 16)};
-                            *(f32x4*)(o + 4) = (f32x4){bf2f(w[2] & 0xFFFF), bf2f(w[2] >> 16), bf2f(w[3] & 0xFFFF),
-                                                       bf2f(w[3] >> 16)};
+                            float f[8];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) { f[2 * e] = bf2f(w[e] & 0xFFFF); f[2 * e + 1] = bf2f(w[e] >> 16); }
+                            if (extras) out_extras8(g, m, n, f);
+                            if (g.out_bf16) {
+                                *(u32x4*)((bf16_t*)g.out0 + (int64_t)m * g.N + n) =
+                                    (u32x4){pack2bf(f[0], f[1]), pack2bf(f[2], f[3]), pack2bf(f[4], f[5]), pack2bf(f[6], f[7])};
+                            } else {
+                                float* o = (float*)g.out0 + (int64_t)m * g.N + n;
+                                *(f32x4*)o = (f32x4){f[0], f[1], f[2], f[3]};
+                                *(f32x4*)(o + 4) = (f32x4){f[4], f[5], f[6], f[7]};
+                            }
                         }
                     } else {
                         const int64_t rowoff = epi == EPI_R ? (int64_t)m * 64 : ((int64_t)bb * g.H * krows + jp) * 64;

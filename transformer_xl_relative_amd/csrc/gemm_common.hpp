@@ -80,6 +80,40 @@ __device__ __forceinline__ const T* b_row_ptr(const GemmArgs& g, int n) {
     return n < g.b_split ? (const T*)g.b0 + (int64_t)n * g.K : (const T*)g.b1 + (int64_t)(n - g.b_split) * g.K;
 }
 
+// EPI_OUT extras on the outputs (m, n..n+3), for m < M: bias, ReLU, residual
+template <typename T>
+__device__ __forceinline__ void out_extras(const GemmArgs& g, int m, int n, f32x4& w) {
+    if (!g.bias_n && !g.res && !g.relu) return;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        if (n + e >= g.N) break;
+        float t = w[e];
+        if (g.bias_n) t += Elem<T>::to_f(((const T*)g.bias_n)[n + e]);
+        if (g.relu) t = fmaxf(t, 0.f);
+        if (g.res) t += Elem<T>::to_f(((const T*)g.res)[(int64_t)m * g.N + n + e]);
+        w[e] = t;
+    }
+}
+
+// the same for 8 outputs (m, n..n+7) of the bf16 kernel, n a multiple of 8
+// and N of 32: bias_n and res are read 16 bytes at a time
+__device__ __forceinline__ void out_extras8(const GemmArgs& g, int m, int n, float* f) {
+    if (g.bias_n) {
+        const u32x4 b = *(const u32x4*)((const bf16_t*)g.bias_n + n);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { f[2 * e] += bf2f(b[e] & 0xFFFF); f[2 * e + 1] += bf2f(b[e] >> 16); }
+    }
+    if (g.relu) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = fmaxf(f[e], 0.f);
+    }
+    if (g.res) {
+        const u32x4 r = *(const u32x4*)((const bf16_t*)g.res + (int64_t)m * g.N + n);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { f[2 * e] += bf2f(r[e] & 0xFFFF); f[2 * e + 1] += bf2f(r[e] >> 16); }
+    }
+}
+
 // Store 4 consecutive outputs: row_out -> (m, n..n+3), else (m..m+3, n).
 template <typename T>
 __device__ __forceinline__ void store4(const GemmArgs& g, int m, int n, const f32x4 v) {
@@ -97,20 +131,22 @@ __device__ __forceinline__ void store4(const GemmArgs& g, int m, int n, const f3
     }
     if (epi == EPI_OUT) {
         if (m >= g.M) return;
+        f32x4 w = v;
+        out_extras<T>(g, m, n, w);
         if (g.out_bf16) {
             bf16_t* o = (bf16_t*)out + (int64_t)m * g.N + n;
             if (n + 3 < g.N) {
-                *(u32x2*)o = (u32x2){pack2bf(v[0], v[1]), pack2bf(v[2], v[3])};
+                *(u32x2*)o = (u32x2){pack2bf(w[0], w[1]), pack2bf(w[2], w[3])};
             } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) if (n + e < g.N) o[e] = f2bf(v[e]);
+                for (int e = 0; e < 4; ++e) if (n + e < g.N) o[e] = f2bf(w[e]);
             }
         } else {
             float* o = (float*)out + (int64_t)m * g.N + n;
-            if (n + 3 < g.N) *(f32x4*)o = (f32x4){v[0], v[1], v[2], v[3]};
+            if (n + 3 < g.N) *(f32x4*)o = (f32x4){w[0], w[1], w[2], w[3]};
             else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) if (n + e < g.N) o[e] = v[e];
+                for (int e = 0; e < 4; ++e) if (n + e < g.N) o[e] = w[e];
             }
         }
         return;

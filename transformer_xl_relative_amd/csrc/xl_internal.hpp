@@ -47,6 +47,11 @@ struct GemmArgs {
     // seq rows per head, token j at row j).
     int out_rows = 0;
     int out_pos0 = 0;
+    // EPI_OUT extras: out = act(acc + bias_n[n]) + res[m, n], act the ReLU when
+    // relu; bias_n [N] and res [M, N] (row-major) in the operand type, or null
+    const void* bias_n = nullptr;
+    const void* res = nullptr;
+    int relu = 0;
 };
 
 constexpr int kMaxGemms = 4;
@@ -126,6 +131,26 @@ size_t attn_bf16_part_bytes(int64_t B, int64_t H, int64_t qlen, const SplitPlan&
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
 hipError_t launch_attn(const AttnArgs& a, bool bf16, int dh, hipStream_t s, hipEvent_t ev0 = nullptr,
                        hipEvent_t ev1 = nullptr);
+
+// Layer normalisation of rows (b, j), j < a_seq, b < rows / a_seq: row j <
+// a_split of batch b is ring row (ring_head + j) % ring_len of a0 (batch
+// stride a0_bstride elements) and goes to y0 [B, a_split, D]; the others are
+// row j - a_split of a1 (batch stride a1_bstride) and go to y1
+// [B, a_seq - a_split, D]. gamma, beta [D]; every tensor in one element type;
+// D a multiple of 8 (bf16) or 4 (f32).
+struct LnArgs {
+    const void* a0;
+    const void* a1;
+    int64_t a0_bstride, a1_bstride;
+    int a_seq, a_split, ring_len, ring_head;
+    void* y0;
+    void* y1;
+    const void* gamma;
+    const void* beta;
+    int rows, D;
+    float eps;
+};
+hipError_t launch_layer_norm(const LnArgs& a, bool bf16, hipStream_t s);
 
 // FIFO write: copies rows h[b, src0 + t, :] (t < n) to ring row
 // (dst0 + t) % ring_len of batch b.

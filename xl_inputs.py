@@ -139,6 +139,47 @@ def layer_inputs(w: Workload, *, batch: int | None = None, qlen: int | None = No
     return {k: Tensor(a, w.dtype) for k, a in out.items()}
 
 
+def decoder_inputs(w: Workload, *, d_inner: int, n_layer: int, batch: int | None = None, qlen: int | None = None,
+                   mlen: int | None = None, seed: int | None = None) -> dict:
+    """Inputs of a decoder stack: 'h' (or the whole stream of a
+    segment-recurrent workload) and 'mem' as layer_inputs draws them, then per
+    layer, in order, the attention weights (the same recipe as layer_inputs),
+    LN1 gain 1 + N(0, 0.02) and shift N(0, 0.02), the same for LN2, W1
+    [d_inner, D], b1 [d_inner], W2 [D, d_inner], b2 [D], all N(0, 0.02).
+    Returns {'h', 'mem', 'layers': [dict per layer]}."""
+    B = w.batch if batch is None else batch
+    q = w.qlen if qlen is None else qlen
+    m = w.mlen if mlen is None else mlen
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    HD, D = w.n_head * w.d_head, w.d_model
+    if w.segments > 1:
+        h = _normal(rng, (B, w.segments * q, D), 1.0)
+        mem = np.zeros((B, 0, D), np.float32)
+    else:
+        h = _normal(rng, (B, q, D), 1.0)
+        mem = _normal(rng, (B, m, D), 1.0)
+    layers = []
+    for _ in range(n_layer):
+        lw = {
+            "w_q": _normal(rng, (HD, D), 0.02), "w_k": _normal(rng, (HD, D), 0.02),
+            "w_v": _normal(rng, (HD, D), 0.02), "w_r": _normal(rng, (HD, D), 0.02),
+            "w_o": _normal(rng, (D, HD), 0.02),
+            "u": _normal(rng, (w.n_head, w.d_head), 0.02), "v": _normal(rng, (w.n_head, w.d_head), 0.02),
+        }
+        if w.bias_clamp >= 0:
+            lw["beta"] = _normal(rng, (bias_rows(w.bias_clamp, w.bias_kind), w.n_head), 0.02)
+        lw["ln1_g"] = (1.0 + _normal(rng, (D,), 0.02)).astype(np.float32)
+        lw["ln1_b"] = _normal(rng, (D,), 0.02)
+        lw["ln2_g"] = (1.0 + _normal(rng, (D,), 0.02)).astype(np.float32)
+        lw["ln2_b"] = _normal(rng, (D,), 0.02)
+        lw["w1"] = _normal(rng, (d_inner, D), 0.02)
+        lw["b1"] = _normal(rng, (d_inner,), 0.02)
+        lw["w2"] = _normal(rng, (D, d_inner), 0.02)
+        lw["b2"] = _normal(rng, (D,), 0.02)
+        layers.append({k: Tensor(a, w.dtype) for k, a in lw.items()})
+    return {"h": Tensor(h, w.dtype), "mem": Tensor(mem, w.dtype), "layers": layers}
+
+
 def core_inputs(*, batch: int, n_head: int, d_head: int, qlen: int, mlen: int, n_rows: int,
                 dtype: str, seed: int, bias_clamp: int = -1, bias_kind: int = 0) -> dict:
     """Inputs for the attention core alone: head-major q, k, v, a projected
