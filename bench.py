@@ -24,6 +24,10 @@ above it; the fraction of the bf16 MFMA peak is reported beside it.
                   # line per workload with the median, p10 and p90 kernel times; NAME/tpN
                   # is one GPU's share (n_head / N heads) under head sharding
   python bench.py --summarize DIR [--copy-calib-mib M]   # markdown summary of rocprofv3 output under DIR
+  python bench.py --decoder N [--d-inner F] [--workload NAME] [--steps K] [--warmup W] [--no-cpu]
+                  # one segment step of an N-layer pre-LN decoder stack (xl_decoder_stack_step),
+                  # every layer's memory full: one JSON line (a separate measurement, not the
+                  # headline); F defaults to 4 * d_model
 
 HBM traffic of the attention kernel comes from two rocprofv3 --pmc passes
 (FETCH_SIZE, then WRITE_SIZE) over this script with --copy-calib-mib, each
@@ -57,8 +61,8 @@ ATTN_SOURCES = ("transformer_xl_relative_amd/csrc/attn_bf16.hip", "transformer_x
 # HBM bytes per launch of the fused attention kernel (calibrated FETCH_SIZE and
 # WRITE_SIZE, see profiles/attn_bf16_kernel_<workload>_pmc_traffic.md).
 TRAFFIC = {
-    "large_bf16": {"sha256": "4834d304dbfd63aa89f61ec016548c5b26687fb2e2a1e63bf8510847876194e5",
-                   "bytes": 39633754, "fetch_bytes": 33342298, "write_bytes": 6291456},
+    "large_bf16": {"sha256": "944c2f6933ce39b39231e094a3dc0ae633023bf00257e3e1baab3b099c13c0b0",
+                   "bytes": 39648690, "fetch_bytes": 33357234, "write_bytes": 6291456},
 }
 
 
@@ -177,6 +181,9 @@ def main():
     ap.add_argument("--summarize", metavar="DIR", help="print a summary of the rocprofv3 databases under DIR")
     ap.add_argument("--core", metavar="WORKLOADS", help="comma-separated workloads: time the fused attention alone")
     ap.add_argument("--launches", type=int, default=100, help="timed launches per --core measurement")
+    ap.add_argument("--decoder", type=int, default=0, metavar="N",
+                    help="time one segment step of an N-layer decoder stack instead of the attention layer")
+    ap.add_argument("--d-inner", type=int, default=0, help="feed-forward width of --decoder (0: 4 * d_model)")
     ap.add_argument("--kv-ring", action="store_true",
                     help="step with xl_segment_step_kv (projected keys and values of the memory kept in a ring)")
     args = ap.parse_args()
@@ -202,6 +209,9 @@ def main():
     w = xl_inputs.WORKLOADS[args.workload]
     if w.dtype != "bf16":
         raise SystemExit("bench.py measures the bf16 workloads")
+    if args.decoder > 0:
+        decoder_bench(w, args.decoder, args.d_inner or 4 * w.d_model, args.steps, args.warmup, args.no_cpu)
+        return
     t = xl_inputs.layer_inputs(w) if w.segments == 1 else None
     if t is None:
         # segment workload: bench one steady-state segment (full memory)
@@ -319,6 +329,86 @@ def main():
         res["cpu_baseline_core"] = cpu_baseline_core(w, t)
         core_tflops = attn_flops / (core_avg_ms * 1e-3) / 1e12
         res["gpu_over_cpu_core"] = round(core_tflops / res["cpu_baseline_core"]["value"], 1)
+    print(json.dumps(res), flush=True)
+
+
+def decoder_flops(w, d_inner):
+    """Algorithmic FLOPs of one decoder layer step: the attention layer and the
+    two feed-forward GEMMs (layer norms, biases, ReLU and residuals are
+    elementwise and not counted)."""
+    flops, _ = layer_flops(w, w.mlen)
+    return flops + 2.0 * 2.0 * w.batch * w.qlen * w.d_model * d_inner
+
+
+def decoder_bench(w, n_layer, d_inner, K, warmup, no_cpu):
+    import numpy as np
+    import torch
+    import transformer_xl_relative_amd as xl
+    import xl_inputs
+    from tests import gpu_util as gu
+    if w.segments > 1:
+        w = dataclass_replace(w, segments=1)
+    t = xl_inputs.decoder_inputs(w, d_inner=d_inner, n_layer=n_layer)
+    D = w.d_model
+    weights = [gu.dec_weights(lw) for lw in t["layers"]]
+    # every layer's memory full (the drawn memory rows, oldest first)
+    rings = [gu.dev(t["mem"]).contiguous() for _ in range(n_layer)]
+    fifos = (xl.xl_mem_fifo * n_layer)(*[xl.xl_mem_fifo(r.data_ptr(), w.mlen, w.mlen, 0) for r in rings])
+    desc = xl.make_desc(batch=w.batch, d_model=D, n_head=w.n_head, d_head=w.d_head, qlen=w.qlen, mlen=w.mlen,
+                        clamp_len=w.clamp_len, bias_clamp=w.bias_clamp, bias_kind=w.bias_kind, dtype=xl.XL_BF16,
+                        out_dtype=xl.XL_BF16)
+    ws = torch.empty(xl.xl_decoder_stack_workspace_size(desc, d_inner), dtype=torch.uint8, device="cuda")
+    h = gu.dev(t["h"])
+    out = torch.empty((w.batch, w.qlen, D), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        xl.xl_decoder_stack_step(desc, d_inner, 0.0, weights, h, fifos, out, ws, stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(K):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    flops = n_layer * decoder_flops(w, d_inner)
+    value = flops / (ms * 1e-3) / 1e12
+    res = {
+        "metric": "decoder stack fwd TFLOP/s (pre-LN layers: relative attention + FFN), 1 GPU",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations and memories, N(0,0.02) weights, LN gains 1+N(0,0.02))",
+        "config": {"workload": (f"{w.name} decoder stack: one segment step of {n_layer} pre-LN layers (LN1 over "
+                                f"[memory ; segment], relative attention + residual, LN2, FFN {D}->{d_inner}->{D} "
+                                f"+ residual, per-layer FIFO update), batch {w.batch}, qlen {w.qlen}, mlen {w.mlen}"),
+                   "n_layer": n_layer, "d_inner": d_inner, "batch": w.batch, "qlen": w.qlen, "mlen": w.mlen,
+                   "d_model": D, "n_head": w.n_head, "d_head": w.d_head},
+        "flops_per_step": flops,
+    }
+    if not no_cpu:
+        import oracle
+        lw = gu.oracle_dec_weights(t["layers"][0])
+        n, t0 = 0, time.perf_counter()
+        while True:
+            b = n % w.batch
+            oracle.decoder_layer_fwd(t["h"].f64[b:b + 1], t["mem"].f64[b:b + 1], lw, n_head=w.n_head,
+                                     d_head=w.d_head, clamp_len=w.clamp_len, bias_clamp=w.bias_clamp,
+                                     bias_kind=w.bias_kind)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= 10.0:
+                break
+        cpu = decoder_flops(w, d_inner) / w.batch * n / el / 1e12
+        res["cpu_baseline"] = {"value": round(cpu, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+                               "kind": "oracle",
+                               "sample": f"{n} decoder-layer forwards of one batch element (of {w.batch}) of "
+                                         f"{w.name}, fp64, {el:.1f} s wall"}
+        res["gpu_over_cpu"] = round(value / cpu, 1)
     print(json.dumps(res), flush=True)
 
 

@@ -6,10 +6,12 @@
 // normalised attention input). Statistics accumulate in fp32; the output is
 // rounded once to the element type.
 //
-// One wave owns one row: 16-byte pieces, 64 lanes across the row, three
-// passes (sum, sum of squared deviations, output); the second and third
-// passes re-read the row from the L1/L2 caches. HBM-bound: every element is
-// read from memory once and written once.
+// One wave owns one row: 16-byte pieces, 64 lanes across the row. Rows of up
+// to MAXP pieces per lane stay in registers (the loads of the row, gamma and
+// beta issued before the first sum, then the squared deviations and the
+// output from the registers); longer
+// rows take three passes whose second and third re-read the row from the
+// caches. HBM-bound: every element is read from memory once and written once.
 #include "xl_common.hpp"
 #include "xl_internal.hpp"
 
@@ -50,6 +52,8 @@ struct Piece<float> {
     __device__ static void store(float* p, const float* v) { *(f32x4*)p = (f32x4){v[0], v[1], v[2], v[3]}; }
 };
 
+constexpr int MAXP = 4;   // pieces per lane kept in registers (D <= 2048 bf16, 1024 f32)
+
 template <typename T>
 __global__ void __launch_bounds__(256) ln_kernel(LnArgs a) {
     const int lane = (int)__builtin_amdgcn_workitem_id_x() & 63;
@@ -71,6 +75,48 @@ __global__ void __launch_bounds__(256) ln_kernel(LnArgs a) {
     }
     constexpr int N = Piece<T>::N;
     const int stride = 64 * N;
+    const T* g = (const T*)a.gamma;
+    const T* bt = (const T*)a.beta;
+    if (a.D <= MAXP * stride) {
+        // the row, gamma and beta all requested before the first use
+        float r[MAXP][N], gv[MAXP][N], bv[MAXP][N];
+#pragma unroll
+        for (int p = 0; p < MAXP; ++p) {
+            const int k = p * stride + lane * N;
+            if (k < a.D) {
+                Piece<T>::load(x + k, r[p]);
+                Piece<T>::load(g + k, gv[p]);
+                Piece<T>::load(bt + k, bv[p]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < N; ++e) r[p][e] = gv[p][e] = bv[p][e] = 0.f;
+            }
+        }
+        float s = 0.f;
+#pragma unroll
+        for (int p = 0; p < MAXP; ++p)
+#pragma unroll
+            for (int e = 0; e < N; ++e) s += r[p][e];
+        const float mean = wave_sum(s) / (float)a.D;
+        float q = 0.f;
+#pragma unroll
+        for (int p = 0; p < MAXP; ++p)
+            if (p * stride + lane * N < a.D) {
+#pragma unroll
+                for (int e = 0; e < N; ++e) q += (r[p][e] - mean) * (r[p][e] - mean);
+            }
+        const float inv = 1.f / sqrtf(wave_sum(q) / (float)a.D + a.eps);
+#pragma unroll
+        for (int p = 0; p < MAXP; ++p) {
+            const int k = p * stride + lane * N;
+            if (k < a.D) {
+#pragma unroll
+                for (int e = 0; e < N; ++e) r[p][e] = (r[p][e] - mean) * inv * gv[p][e] + bv[p][e];
+                Piece<T>::store(y + k, r[p]);
+            }
+        }
+        return;
+    }
     float v[N];
     float s = 0.f;
     for (int k = lane * N; k < a.D; k += stride) {
@@ -86,8 +132,6 @@ __global__ void __launch_bounds__(256) ln_kernel(LnArgs a) {
         for (int e = 0; e < N; ++e) q += (v[e] - mean) * (v[e] - mean);
     }
     const float inv = 1.f / sqrtf(wave_sum(q) / (float)a.D + a.eps);
-    const T* g = (const T*)a.gamma;
-    const T* bt = (const T*)a.beta;
     for (int k = lane * N; k < a.D; k += stride) {
         float gv[N], bv[N];
         Piece<T>::load(x + k, v);
