@@ -35,6 +35,8 @@ def _load():
         lib.orc_t5_bucket.argtypes = [_i64]
         lib.orc_t5_bucket.restype = _i64
         lib.orc_fifo_update.argtypes = [_i64, _i64, _i64, _i64, _p, _i64, _p, _p, ctypes.POINTER(_i64)]
+        lib.orc_rel_attn_core_bwd.argtypes = [_i64] * 8 + [_dbl] + [_p] * 4 + [_i64] + [_p] * 11
+        lib.orc_rel_attn_core_bwd.restype = ctypes.c_int
         lib.orc_layer_norm.argtypes = [_i64, _i64, _p, _p, _p, _dbl, _p]
         lib.orc_layer_norm.restype = ctypes.c_int
         lib.orc_num_threads.argtypes = []
@@ -120,6 +122,26 @@ def rel_attn_core(q, k, v, rtab, u, vb, *, scale: float, clamp_len: int = -1, rt
     if want_probs:
         res.append(probs)
     return res[0] if len(res) == 1 else tuple(res)
+
+
+def rel_attn_core_bwd(q, k, v, rtab, u, vb, dout, *, scale: float, clamp_len: int = -1, beta=None,
+                      bias_clamp: int = -1, bias_kind: int = 0):
+    """Gradients of the attention core for the upstream gradient dout
+    [B, qlen, H*dh] of its output: a dict with dq [B,H,q,dh], dk, dv
+    [B,H,klen,dh], dr [H,n,dh] (per table row), du, dv_bias [H,dh] and dbeta
+    (or None). Default positions (query i at mlen+i, key j at j)."""
+    q, k, v, rtab, u, vb, beta, dout = map(_f64, (q, k, v, rtab, u, vb, beta, dout))
+    B, H, ql, dh = q.shape
+    kl = k.shape[2]
+    out = {"dq": np.empty_like(q), "dk": np.empty_like(k), "dv": np.empty_like(v), "dr": np.empty_like(rtab),
+           "du": np.empty_like(u), "dv_bias": np.empty_like(vb),
+           "dbeta": np.empty_like(beta) if beta is not None else None}
+    st = _load().orc_rel_attn_core_bwd(B, H, dh, ql, kl, clamp_len, bias_clamp, bias_kind, scale, _ptr(q), _ptr(k),
+                                       _ptr(v), _ptr(rtab), rtab.shape[1], _ptr(u), _ptr(vb), _ptr(beta),
+                                       _ptr(dout), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                                       _ptr(out["dr"]), _ptr(out["du"]), _ptr(out["dv_bias"]), _ptr(out["dbeta"]))
+    _check(st, "orc_rel_attn_core_bwd")
+    return out
 
 
 def rel_attn_fwd(h, mem, w_q, w_k, w_v, w_r, w_o, u, vb, *, n_head: int, d_head: int,

@@ -231,6 +231,111 @@ int orc_rel_attn_core(int64_t B, int64_t H, int64_t dh, int64_t qlen, int64_t kl
 }
 
 /*
+ * Gradients of the attention core (default positions: query i at mlen+i,
+ * key j at j) for an upstream gradient dout [B, qlen, H*dh] of o. With the
+ * logits l_ij = scale*(q_i.k_j + q_i.r + u.k_j + v.r) + beta (as the forward)
+ * and P = softmax_j(l), per (b, h, i):
+ *   dP_ij = dout_i . v_j,  D_i = sum_j P_ij dP_ij,  dS_ij = P_ij (dP_ij - D_i)
+ *   dq_i  = scale sum_j dS_ij (k_j + r_ij)     dk_j += scale dS_ij (q_i + u)
+ *   dv_j += P_ij dout_i                        dr_row += scale dS_ij (q_i + v)
+ *   du   += scale sum_j dS_ij k_j              dvb  += scale sum_j dS_ij r_ij
+ *   dbeta[brow, h] += dS_ij
+ * where r_ij is the table row of the clamped distance (memory gets no other
+ * gradient path here: the memory rows of k and v receive theirs like any key).
+ * The chain rule of the softmax and of the four dot products, written out per
+ * pair. Outputs are overwritten: dq [B,H,qlen,dh], dk, dv [B,H,klen,dh],
+ * drtab [H, n_rtab, dh], du, dvb [H, dh], dbeta as beta (or NULL).
+ */
+int orc_rel_attn_core_bwd(int64_t B, int64_t H, int64_t dh, int64_t qlen, int64_t klen, int64_t clamp_len,
+                          int64_t bias_clamp, int64_t bias_kind, double scale, const double* q, const double* k,
+                          const double* v, const double* rtab, int64_t n_rtab, const double* u, const double* vb,
+                          const double* beta, const double* dout, double* dq, double* dk, double* dv, double* drtab,
+                          double* du, double* dvb, double* dbeta) {
+    if (B < 0 || H <= 0 || dh <= 0 || qlen < 0 || klen < qlen || n_rtab <= 0) return ORC_BAD_ARG;
+    if (!q || !k || !v || !rtab || !u || !vb || !dout || !dq || !dk || !dv || !drtab || !du || !dvb)
+        return ORC_BAD_ARG;
+    if (bias_clamp >= 0 && (!beta || !dbeta)) return ORC_BAD_ARG;
+    if (bias_kind != 0 && bias_kind != 1) return ORC_BAD_ARG;
+    const int64_t mlen = klen - qlen;
+    const int64_t n_beta = bias_kind == 1 ? 12 : 2 * bias_clamp + 1;
+    memset(dq, 0, sizeof(double) * (size_t)(B * H * qlen * dh));
+    memset(dk, 0, sizeof(double) * (size_t)(B * H * klen * dh));
+    memset(dv, 0, sizeof(double) * (size_t)(B * H * klen * dh));
+    memset(drtab, 0, sizeof(double) * (size_t)(H * n_rtab * dh));
+    memset(du, 0, sizeof(double) * (size_t)(H * dh));
+    memset(dvb, 0, sizeof(double) * (size_t)(H * dh));
+    if (bias_clamp >= 0) memset(dbeta, 0, sizeof(double) * (size_t)(n_beta * H));
+    int status = ORC_OK;
+    /* heads are independent; everything a head accumulates belongs to it */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t hh = 0; hh < H; ++hh) {
+        double* P = (double*)malloc(sizeof(double) * (size_t)(klen ? klen : 1));
+        double* dS = (double*)malloc(sizeof(double) * (size_t)(klen ? klen : 1));
+        int64_t* rrow = (int64_t*)malloc(sizeof(int64_t) * (size_t)(klen ? klen : 1));
+        if (!P || !dS || !rrow) {
+            free(P); free(dS); free(rrow);
+#pragma omp atomic write
+            status = ORC_NO_MEM;
+            continue;
+        }
+        const double* uh = u + hh * dh;
+        const double* vh = vb + hh * dh;
+        for (int64_t b = 0; b < B; ++b)
+            for (int64_t i = 0; i < qlen; ++i) {
+                const double* qi = q + ((b * H + hh) * qlen + i) * dh;
+                const double* gi = dout + (b * qlen + i) * (H * dh) + hh * dh;
+                const int64_t nv = mlen + i + 1;   /* visible keys j <= mlen + i */
+                double mx = -INFINITY;
+                for (int64_t j = 0; j < nv; ++j) {
+                    const int64_t delta = mlen + i - j;
+                    const int64_t dc = clamp_len >= 0 ? clamp64(delta, -clamp_len, clamp_len) : delta;
+                    if (dc >= n_rtab) {
+#pragma omp atomic write
+                        status = ORC_RANGE;
+                        rrow[j] = n_rtab - 1;
+                    } else {
+                        rrow[j] = dc;
+                    }
+                    const double* kj = k + ((b * H + hh) * klen + j) * dh;
+                    const double* rj = rtab + (hh * n_rtab + rrow[j]) * dh;
+                    double l = scale * (dot(qi, kj, dh) + dot(qi, rj, dh) + dot(uh, kj, dh) + dot(vh, rj, dh));
+                    if (bias_clamp >= 0) l += beta[bias_row(delta, bias_kind, bias_clamp) * H + hh];
+                    P[j] = l;
+                    if (l > mx) mx = l;
+                }
+                double den = 0.0;
+                for (int64_t j = 0; j < nv; ++j) { P[j] = exp(P[j] - mx); den += P[j]; }
+                double Di = 0.0;
+                for (int64_t j = 0; j < nv; ++j) {
+                    P[j] /= den;
+                    dS[j] = dot(gi, v + ((b * H + hh) * klen + j) * dh, dh);   /* dP_ij for now */
+                    Di += P[j] * dS[j];
+                }
+                double* dqi = dq + ((b * H + hh) * qlen + i) * dh;
+                for (int64_t j = 0; j < nv; ++j) {
+                    dS[j] = P[j] * (dS[j] - Di);
+                    const double* kj = k + ((b * H + hh) * klen + j) * dh;
+                    const double* rj = rtab + (hh * n_rtab + rrow[j]) * dh;
+                    double* dkj = dk + ((b * H + hh) * klen + j) * dh;
+                    double* dvj = dv + ((b * H + hh) * klen + j) * dh;
+                    double* drj = drtab + (hh * n_rtab + rrow[j]) * dh;
+                    for (int64_t d = 0; d < dh; ++d) {
+                        dqi[d] += scale * dS[j] * (kj[d] + rj[d]);
+                        dkj[d] += scale * dS[j] * (qi[d] + uh[d]);
+                        dvj[d] += P[j] * gi[d];
+                        drj[d] += scale * dS[j] * (qi[d] + vh[d]);
+                        du[hh * dh + d] += scale * dS[j] * kj[d];
+                        dvb[hh * dh + d] += scale * dS[j] * rj[d];
+                    }
+                    if (bias_clamp >= 0) dbeta[bias_row(mlen + i - j, bias_kind, bias_clamp) * H + hh] += dS[j];
+                }
+            }
+        free(P); free(dS); free(rrow);
+    }
+    return status;
+}
+
+/*
  * Full layer forward [P5 §2.3.1-§2.3.2; P1 §3.1]:
  *   x~ = [mem ; h] per batch (memory rows first)
  *   q = h W_q^T, k = x~ W_k^T, v = x~ W_v^T   (weights [H*dh, D])

@@ -436,3 +436,68 @@ def test_fifo_update_and_segment_run():
     # a long memory equals attending over the whole prefix
     outs_long, _ = oracle.segment_run(stream, 3, q, 100, wts, n_head=2, d_head=8)
     _close(outs_long[2], _fwd(w, h=stream[:, 2 * q:3 * q], mem=stream[:, :2 * q]), 0.0)
+
+
+# --- the backward of the attention core --------------------------------------------------------
+
+def _core_case(seed, B=2, H=2, dh=4, q=3, m=2, clamp=-1, bias=-1, kind=0):
+    rng = np.random.default_rng(seed)
+    kl = q + m
+    n_rel = kl if clamp < 0 else min(kl, clamp + 1)
+    c = dict(q=rng.standard_normal((B, H, q, dh)), k=rng.standard_normal((B, H, kl, dh)),
+             v=rng.standard_normal((B, H, kl, dh)), r=rng.standard_normal((H, n_rel, dh)),
+             u=0.5 * rng.standard_normal((H, dh)), vb=0.5 * rng.standard_normal((H, dh)),
+             dout=rng.standard_normal((B, q, H * dh)), clamp=clamp, bias=bias, kind=kind, scale=0.7)
+    c["beta"] = rng.standard_normal(((12 if kind else 2 * bias + 1), H)) * 0.5 if bias >= 0 else None
+    return c
+
+
+def _core_loss(c, **over):
+    a = dict(c)
+    a.update(over)
+    o = oracle.rel_attn_core(a["q"], a["k"], a["v"], a["r"], a["u"], a["vb"], scale=a["scale"], clamp_len=a["clamp"],
+                             beta=a["beta"], bias_clamp=a["bias"], bias_kind=a["kind"])
+    return float(np.sum(o * a["dout"]))
+
+
+def _core_grads(c):
+    return oracle.rel_attn_core_bwd(c["q"], c["k"], c["v"], c["r"], c["u"], c["vb"], c["dout"], scale=c["scale"],
+                                    clamp_len=c["clamp"], beta=c["beta"], bias_clamp=c["bias"], bias_kind=c["kind"])
+
+
+@pytest.mark.parametrize("seed,q,m,clamp,bias,kind", [(40, 3, 2, -1, -1, 0), (41, 4, 3, 2, 1, 0), (42, 2, 0, -1, -1, 0),
+                                                       (43, 3, 4, 1, 0, 1)])
+def test_core_backward_matches_finite_differences(seed, q, m, clamp, bias, kind):
+    c = _core_case(seed, q=q, m=m, clamp=clamp, bias=bias, kind=kind)
+    g = _core_grads(c)
+    eps = 1e-6
+    for name, key in [("q", "dq"), ("k", "dk"), ("v", "dv"), ("r", "dr"), ("u", "du"), ("vb", "dv_bias"),
+                      ("beta", "dbeta")]:
+        if c[name] is None:
+            assert g[key] is None
+            continue
+        x = c[name]
+        fd = np.empty_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            fd[idx] = (_core_loss(c, **{name: xp}) - _core_loss(c, **{name: xm})) / (2 * eps)
+        _close(g[key], fd, 1e-7)
+
+
+def test_core_backward_invariants():
+    c = _core_case(44, B=2, H=3, dh=5, q=6, m=4, bias=2)
+    g = _core_grads(c)
+    # shifting every key of a head moves each query's logits by a constant
+    _close(g["dk"].sum(axis=2), np.zeros((2, 3, 5)), 1e-12)
+    # shifting every value shifts every output: sum_j dv_j = sum_i dout_i
+    dsum = c["dout"].reshape(2, 6, 3, 5).sum(axis=1)
+    _close(g["dv"].sum(axis=2), dsum, 1e-12)
+    # a constant added to a head's whole bias table changes nothing
+    _close(g["dbeta"].sum(axis=0), np.zeros(3), 1e-12)
+    # q_i enters as q_i + u and q_i + v: du + dv_bias = sum over (b, i) of dq
+    _close(g["du"] + g["dv_bias"], g["dq"].sum(axis=(0, 2)), 1e-12)
+    z = _core_grads(dict(c, dout=np.zeros_like(c["dout"])))
+    for key in ("dq", "dk", "dv", "dr", "du", "dv_bias", "dbeta"):
+        assert np.all(z[key] == 0.0)
