@@ -261,6 +261,35 @@ int xl_segment_step_kv(const xl_attn_desc* desc, const xl_attn_weights* w, const
                        xl_kv_fifo* kv, void* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Gradients of xl_rel_attn_core for an upstream gradient dout [B, qlen,
+ * H*d_head] (desc->dtype) of its output. The inputs are those of the forward
+ * call (same layouts, desc->mlen keys of memory). With the logits l of the
+ * forward and P = softmax(l): dP = dout . v, D_i = sum_j P_ij dP_ij,
+ * dS = P (dP - D), then (s = desc->scale)
+ *   dq_i = s sum_j dS_ij (k_j + r_ij),   dk_j = s sum_i dS_ij (q_i + u),
+ *   dv_j = sum_i P_ij dout_i,            dr_c = s sum_{pairs of row c} dS_ij (q_i + v),
+ *   du = s sum_ij dS_ij k_j,             dv_bias = s sum_ij dS_ij r_ij,
+ *   dbias[row, h] = sum_{pairs of row} dS_ij
+ * (the chain rule through the softmax and the four dot products of
+ * qidao123.com thread-401555 §3; dr gathers the band back per distance, the
+ * transpose of the relative shift). Rows of r at or beyond the rows in use
+ * get zero. All gradients are fp32 and overwritten: dq [B, H, qlen, d_head],
+ * dk, dv [B, H, klen, d_head], dr [H, n_rel, d_head], du, dv_bias
+ * [H, d_head], dbias like bias_table (needed when desc->bias_clamp >= 0).
+ * The memory keys receive gradients like any key; a caller that detaches the
+ * memory drops those rows. A plain form: fp32 vector arithmetic, P and dS
+ * materialised in the workspace (xl_rel_attn_core_bwd_workspace_size():
+ * 8 bytes per (query, key) pair plus 8 per query element), no atomics.
+ * Errors as xl_rel_attn_core; gradients must not overlap inputs, each other
+ * or the workspace (XL_BAD_SHAPE).
+ */
+size_t xl_rel_attn_core_bwd_workspace_size(const xl_attn_desc* desc);
+int xl_rel_attn_core_bwd(const xl_attn_desc* desc, const void* q, const void* k, const void* vt, int64_t ldv,
+                         const void* r, int64_t n_rel, const void* u, const void* v, const void* bias_table,
+                         const void* dout, float* dq, float* dk, float* dv, float* dr, float* du, float* dv_bias,
+                         float* dbias, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * ---- The decoder layer around the attention, and the stacked layers ----
  * A decoder layer is one module of masked self-attention and a position-wise
  * feed-forward network; N of them are stacked, each module's output feeding

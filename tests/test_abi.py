@@ -288,3 +288,26 @@ def test_decoder_stack_rejects_bad_arguments():
     need = xl.xl_decoder_stack_workspace_size(d, 2048)
     assert need > xl.xl_decoder_layer_workspace_size(d, 2048)
     assert call(fifos=fifos, nb=need - 1) == xl.XL_WORKSPACE_TOO_SMALL
+
+
+def test_core_backward_rejects_bad_arguments():
+    lib = xl.lib()
+    d = _desc(mlen=64, qlen=64)
+    klen = 128
+    need = xl.xl_rel_attn_core_bwd_workspace_size(d)
+    assert need == 2 * (2 * 8 * 64 * klen * 4) + 2 * (2 * 8 * 64 * 64 * 4)
+
+    def call(ldv=klen, n_rel=klen, bias=None, dbias=None, desc=d, ws=FAKE[15], nb=need, dq=FAKE[9], dk=FAKE[10]):
+        return lib.xl_rel_attn_core_bwd(ctypes.byref(desc), FAKE[0], FAKE[1], FAKE[2], ldv, FAKE[3], n_rel, FAKE[4],
+                                        FAKE[5], bias, FAKE[6], dq, dk, FAKE[11], FAKE[12], FAKE[13], FAKE[14], dbias,
+                                        ws, nb, None)
+    assert call(ldv=klen - 8) == xl.XL_BAD_SHAPE
+    assert call(n_rel=klen - 1) == xl.XL_BAD_SHAPE
+    assert call(dq=None) == xl.XL_NULL_ARG
+    assert call(desc=_desc(mlen=64, qlen=64, bias_clamp=4), bias=FAKE[7]) == xl.XL_NULL_ARG   # no dbias
+    assert call(nb=need - 1) == xl.XL_WORKSPACE_TOO_SMALL
+    assert call(ws=None) == xl.XL_WORKSPACE_TOO_SMALL
+    assert call(ws=FAKE[15] + 16) == xl.XL_UNSUPPORTED
+    assert call(dq=FAKE[0]) == xl.XL_BAD_SHAPE            # dq aliases q
+    assert call(dk=FAKE[9] + 64) == xl.XL_BAD_SHAPE       # dk overlaps dq
+    assert xl.xl_rel_attn_core_bwd_workspace_size(_desc(qlen=0)) == 0

@@ -62,7 +62,7 @@ _lib = None
 EXPORTS = ("xl_status_string", "xl_last_error", "xl_relpos_embed", "xl_rel_attn_workspace_size",
            "xl_rel_attn_workspace_layout", "xl_rel_attn_fwd", "xl_rel_attn_core_workspace_size", "xl_rel_attn_core",
            "xl_segment_step", "xl_segment_step_kv_workspace_size", "xl_segment_step_kv", "xl_set_core_events",
-           "xl_decoder_layer_workspace_size", "xl_decoder_layer_fwd", "xl_decoder_stack_workspace_size",
+           "xl_rel_attn_core_bwd_workspace_size", "xl_rel_attn_core_bwd", "xl_decoder_layer_workspace_size", "xl_decoder_layer_fwd", "xl_decoder_stack_workspace_size",
            "xl_decoder_stack_step")
 
 
@@ -105,6 +105,10 @@ def lib():
         L.xl_segment_step_kv.argtypes = [ctypes.POINTER(xl_attn_desc), ctypes.POINTER(xl_attn_weights), _p,
                                          ctypes.POINTER(xl_kv_fifo), _p, _p, ctypes.c_size_t, _p]
         D = ctypes.POINTER(xl_attn_desc)
+        L.xl_rel_attn_core_bwd_workspace_size.argtypes = [D]
+        L.xl_rel_attn_core_bwd_workspace_size.restype = ctypes.c_size_t
+        L.xl_rel_attn_core_bwd.argtypes = [D, _p, _p, _p, _i64, _p, _i64, _p, _p, _p, _p] + [_p] * 8 + \
+            [ctypes.c_size_t, _p]
         L.xl_decoder_layer_workspace_size.argtypes = [D, _i64]
         L.xl_decoder_layer_workspace_size.restype = ctypes.c_size_t
         L.xl_decoder_layer_fwd.argtypes = [D, _i64, ctypes.c_float, ctypes.POINTER(xl_decoder_weights), _p, _p, _p,
@@ -115,6 +119,7 @@ def lib():
                                             ctypes.POINTER(xl_mem_fifo), _p, _p, ctypes.c_size_t, _p]
         for f in ("xl_relpos_embed", "xl_rel_attn_workspace_layout", "xl_rel_attn_fwd", "xl_rel_attn_core",
                   "xl_segment_step", "xl_set_core_events", "xl_segment_step_kv", "xl_decoder_layer_fwd",
+                  "xl_rel_attn_core_bwd",
                   "xl_decoder_stack_step"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -323,3 +328,19 @@ def xl_decoder_stack_step(desc: xl_attn_desc, d_inner: int, ln_eps: float, weigh
     _check(lib().xl_decoder_stack_step(ctypes.byref(desc), d_inner, ln_eps, n, cw, _ptr(h), fifos, _ptr(out),
                                        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
     return out
+
+
+def xl_rel_attn_core_bwd_workspace_size(desc: xl_attn_desc) -> int:
+    return lib().xl_rel_attn_core_bwd_workspace_size(ctypes.byref(desc))
+
+
+def xl_rel_attn_core_bwd(desc: xl_attn_desc, q, k, vt, ldv: int, r, n_rel: int, u, v, bias_table, dout, grads: dict,
+                         ws, stream=None):
+    """grads: fp32 device tensors dq, dk, dv, dr, du, dv_bias (and dbias with a
+    bias table), overwritten."""
+    _check(lib().xl_rel_attn_core_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(vt), ldv, _ptr(r), n_rel, _ptr(u),
+                                      _ptr(v), _ptr(bias_table), _ptr(dout), _ptr(grads["dq"]), _ptr(grads["dk"]),
+                                      _ptr(grads["dv"]), _ptr(grads["dr"]), _ptr(grads["du"]),
+                                      _ptr(grads["dv_bias"]), _ptr(grads.get("dbias")), _ptr(ws),
+                                      ws.numel() * ws.element_size(), _stream(stream)))
+    return grads

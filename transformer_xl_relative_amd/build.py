@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libxlrel.so")
-SOURCES = ["api.hip", "relpos.hip", "gemm.hip", "gemm_bf16.hip", "attn.hip", "attn_bf16.hip", "ln.hip"]
+SOURCES = ["api.hip", "relpos.hip", "gemm.hip", "gemm_bf16.hip", "attn.hip", "attn_bf16.hip", "ln.hip", "attn_bwd.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

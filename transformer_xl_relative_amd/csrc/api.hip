@@ -587,6 +587,75 @@ int xl_segment_step_kv(const xl_attn_desc* desc, const xl_attn_weights* w, const
     return XL_OK;
 }
 
+size_t xl_rel_attn_core_bwd_workspace_size(const xl_attn_desc* desc) {
+    if (!desc || check_desc(desc, desc->mlen, false) != XL_OK) return 0;
+    const int64_t rows = desc->batch * desc->n_head * desc->qlen;
+    const int64_t klen = desc->mlen + desc->qlen;
+    return 2 * align_up((size_t)(rows * klen) * 4) + 2 * align_up((size_t)(rows * desc->d_head) * 4);
+}
+
+int xl_rel_attn_core_bwd(const xl_attn_desc* desc, const void* q, const void* k, const void* vt, int64_t ldv,
+                         const void* r, int64_t n_rel, const void* u, const void* v, const void* bias_table,
+                         const void* dout, float* dq, float* dk, float* dv, float* dr, float* du, float* dv_bias,
+                         float* dbias, void* ws, size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    int st = check_desc(desc, desc ? desc->mlen : 0, false);
+    if (st != XL_OK) return st;
+    if (!q || !k || !vt || !r || !u || !v || !dout) return fail(XL_NULL_ARG, "an input pointer is NULL");
+    if (!dq || !dk || !dv || !dr || !du || !dv_bias) return fail(XL_NULL_ARG, "an output pointer is NULL");
+    if (desc->bias_clamp >= 0 && (!bias_table || !dbias))
+        return fail(XL_NULL_ARG, "bias_clamp >= 0 but bias_table or dbias is NULL");
+    const int64_t klen = desc->mlen + desc->qlen;
+    if (ldv < klen) return fail(XL_BAD_SHAPE, "ldv must be >= klen");
+    if (ldv > kI32 / 64) return fail(XL_UNSUPPORTED, "ldv too large");
+    const int64_t need = n_rel_of(desc, klen);
+    if (n_rel < need) return fail(XL_BAD_SHAPE, "r has %lld rows, needs %lld", (long long)n_rel, (long long)need);
+    if (n_rel > kI32 / 64) return fail(XL_UNSUPPORTED, "r has too many rows");
+    const int64_t rows = desc->batch * desc->n_head * desc->qlen;
+    if (rows * klen > ((int64_t)1 << 40)) return fail(XL_UNSUPPORTED, "problem too large for the plain backward");
+    const size_t need_ws = xl_rel_attn_core_bwd_workspace_size(desc);
+    if (!ws || ws_bytes < need_ws)
+        return fail(XL_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", ws ? ws_bytes : 0, need_ws);
+    if (((uintptr_t)ws) % kAlign) return fail(XL_UNSUPPORTED, "workspace must be 256-byte aligned");
+    const size_t es = esize(desc->dtype);
+    const int64_t dh = desc->d_head, H = desc->n_head;
+    const size_t qb = (size_t)(rows * dh), kb = (size_t)(desc->batch * H * klen * dh);
+    // no output may overlap an input, another output or the workspace
+    const void* outs[] = {dq, dk, dv, dr, du, dv_bias};
+    const size_t osz[] = {qb * 4, kb * 4, kb * 4, (size_t)(H * n_rel * dh) * 4, (size_t)(H * dh) * 4,
+                          (size_t)(H * dh) * 4};
+    const void* ins[] = {q, k, vt, r, dout, ws};
+    const size_t isz[] = {qb * es, kb * es, (size_t)(desc->batch * H * dh * ldv) * es, (size_t)(H * n_rel * dh) * es,
+                          qb * es, ws_bytes};
+    for (int x = 0; x < 6; ++x) {
+        for (int y = 0; y < 6; ++y)
+            if (overlaps(outs[x], osz[x], ins[y], isz[y])) return fail(XL_BAD_SHAPE, "a gradient aliases an input");
+        for (int y = 0; y < x; ++y)
+            if (overlaps(outs[x], osz[x], outs[y], osz[y])) return fail(XL_BAD_SHAPE, "two gradients overlap");
+    }
+    xl::AttnBwdArgs a;
+    memset(&a, 0, sizeof a);
+    a.q = q; a.k = k; a.vt = vt; a.r = r; a.u = u; a.v = v;
+    a.bias = desc->bias_clamp >= 0 ? bias_table : nullptr;
+    a.dout = dout;
+    a.scale = desc->scale == 0.f ? (float)(1.0 / sqrt((double)dh)) : desc->scale;
+    a.B = (int)desc->batch; a.H = (int)H; a.qlen = (int)desc->qlen; a.mlen = (int)desc->mlen; a.klen = (int)klen;
+    a.ldv = (int)ldv; a.n_rel = (int)need; a.r_rows = (int)n_rel;
+    a.bias_clamp = (int)(desc->bias_clamp >= 0 ? desc->bias_clamp : 0);
+    a.bias_kind = desc->bias_kind;
+    a.bias_rows = desc->bias_kind == XL_BIAS_T5 ? XL_T5_BUCKETS : 2 * a.bias_clamp + 1;
+    char* W = (char*)ws;
+    size_t off = 0;
+    a.P = (float*)(W + off); off += align_up((size_t)(rows * klen) * 4);
+    a.dS = (float*)(W + off); off += align_up((size_t)(rows * klen) * 4);
+    a.dqu = (float*)(W + off); off += align_up(qb * 4);
+    a.dqv = (float*)(W + off);
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dr = dr; a.du = du; a.dvb = dv_bias; a.dbias = dbias;
+    const hipError_t e = xl::launch_attn_bwd(a, desc->dtype == XL_BF16, (int)dh, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "backward launch");
+    return XL_OK;
+}
+
 size_t xl_decoder_layer_workspace_size(const xl_attn_desc* desc, int64_t d_inner) {
     if (!desc || check_desc(desc, desc->mlen, true) != XL_OK || d_inner < 1) return 0;
     DecLayout L;

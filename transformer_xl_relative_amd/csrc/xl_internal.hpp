@@ -132,6 +132,38 @@ hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t s, hipEvent_t ev0, hi
 hipError_t launch_attn(const AttnArgs& a, bool bf16, int dh, hipStream_t s, hipEvent_t ev0 = nullptr,
                        hipEvent_t ev1 = nullptr);
 
+// Gradients of the attention core (attn_bwd.hip). Inputs as AttnArgs (q, k,
+// vt, r with r_rows rows per head, u, v, bias) in the element type, dout
+// [B, qlen, H*dh] likewise; P and dS are workspace [B, H, qlen, klen] fp32,
+// dqu and dqv workspace [B, H, qlen, dh] fp32. Outputs fp32: dq [B,H,qlen,dh],
+// dk, dv [B,H,klen,dh], dr [H, r_rows, dh], du, dvb [H, dh], dbias
+// [bias_rows, H] (when bias).
+struct AttnBwdArgs {
+    const void* q;
+    const void* k;
+    const void* vt;
+    const void* r;
+    const void* u;
+    const void* v;
+    const void* bias;
+    const void* dout;
+    float scale;
+    int B, H, qlen, mlen, klen, ldv, n_rel, r_rows;
+    int bias_clamp, bias_kind, bias_rows;
+    float* P;
+    float* dS;
+    float* dqu;
+    float* dqv;
+    float* dq;
+    float* dk;
+    float* dv;
+    float* dr;
+    float* du;
+    float* dvb;
+    float* dbias;
+};
+hipError_t launch_attn_bwd(const AttnBwdArgs& a, bool bf16, int dh, hipStream_t s);
+
 // Layer normalisation of rows (b, j), j < a_seq, b < rows / a_seq: row j <
 // a_split of batch b is ring row (ring_head + j) % ring_len of a0 (batch
 // stride a0_bstride elements) and goes to y0 [B, a_split, D]; the others are
