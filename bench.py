@@ -28,6 +28,9 @@ above it; the fraction of the bf16 MFMA peak is reported beside it.
                   # one segment step of an N-layer pre-LN decoder stack (xl_decoder_stack_step),
                   # every layer's memory full: one JSON line (a separate measurement, not the
                   # headline); F defaults to 4 * d_model
+  python bench.py --backward [--workload NAME] [--steps K] [--warmup W] [--no-cpu]
+                  # the attention-core gradients (xl_rel_attn_core_bwd) on the workload's
+                  # shape: one JSON line with the kernel sequence's time and its rate
 
 HBM traffic of the attention kernel comes from two rocprofv3 --pmc passes
 (FETCH_SIZE, then WRITE_SIZE) over this script with --copy-calib-mib, each
@@ -184,6 +187,7 @@ def main():
     ap.add_argument("--decoder", type=int, default=0, metavar="N",
                     help="time one segment step of an N-layer decoder stack instead of the attention layer")
     ap.add_argument("--d-inner", type=int, default=0, help="feed-forward width of --decoder (0: 4 * d_model)")
+    ap.add_argument("--backward", action="store_true", help="time the attention-core gradients instead")
     ap.add_argument("--kv-ring", action="store_true",
                     help="step with xl_segment_step_kv (projected keys and values of the memory kept in a ring)")
     args = ap.parse_args()
@@ -209,6 +213,9 @@ def main():
     w = xl_inputs.WORKLOADS[args.workload]
     if w.dtype != "bf16":
         raise SystemExit("bench.py measures the bf16 workloads")
+    if args.backward:
+        backward_bench(w, args.steps, args.warmup, args.no_cpu)
+        return
     if args.decoder > 0:
         decoder_bench(w, args.decoder, args.d_inner or 4 * w.d_model, args.steps, args.warmup, args.no_cpu)
         return
@@ -329,6 +336,91 @@ def main():
         res["cpu_baseline_core"] = cpu_baseline_core(w, t)
         core_tflops = attn_flops / (core_avg_ms * 1e-3) / 1e12
         res["gpu_over_cpu_core"] = round(core_tflops / res["cpu_baseline_core"]["value"], 1)
+    print(json.dumps(res), flush=True)
+
+
+FP32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector (packed) peak
+
+
+def backward_flops(w):
+    """Algorithmic FLOPs of the core gradients: per valid pair the two logit
+    dots recomputed (4 dh), dP (2 dh), dq from k and r (4 dh), dk, dv and dr
+    (2 dh each): 16 dh per pair."""
+    return 16.0 * w.d_head * w.batch * w.n_head * w.n_valid_pairs()
+
+
+def backward_bench(w, K, warmup, no_cpu):
+    import numpy as np
+    import torch
+    import transformer_xl_relative_amd as xl
+    import xl_inputs
+    from tests import gpu_util as gu
+    B, H, dh, q, m = w.batch, w.n_head, w.d_head, w.qlen, w.mlen
+    klen = q + m
+    n_rel = klen if w.clamp_len < 0 else min(klen, w.clamp_len + 1)
+    ci = xl_inputs.core_inputs(batch=B, n_head=H, d_head=dh, qlen=q, mlen=m, n_rows=n_rel, dtype="bf16", seed=w.seed,
+                               bias_clamp=w.bias_clamp, bias_kind=w.bias_kind)
+    rng = np.random.default_rng(w.seed + 1)
+    dout = xl_inputs.Tensor(rng.standard_normal((B, q, H * dh)).astype(np.float32), "bf16")
+    ldv = (klen + 63) // 64 * 64
+    vt = np.zeros((B, H, dh, ldv), np.float32)
+    vt[..., :klen] = ci["v"].f32.transpose(0, 1, 3, 2)
+    vt = gu.dev(xl_inputs.Tensor(vt, "bf16"))
+    desc = xl.make_desc(batch=B, d_model=H * dh, n_head=H, d_head=dh, qlen=q, mlen=m, clamp_len=w.clamp_len,
+                        bias_clamp=w.bias_clamp, bias_kind=w.bias_kind)
+    f32 = lambda *sh: torch.empty(sh, dtype=torch.float32, device="cuda")
+    g = {"dq": f32(B, H, q, dh), "dk": f32(B, H, klen, dh), "dv": f32(B, H, klen, dh), "dr": f32(H, n_rel, dh),
+         "du": f32(H, dh), "dv_bias": f32(H, dh)}
+    if w.bias_clamp >= 0:
+        g["dbias"] = f32(*ci["beta"].shape)
+    ws = torch.empty(xl.xl_rel_attn_core_bwd_workspace_size(desc), dtype=torch.uint8, device="cuda")
+    args = [gu.dev(ci[k]) for k in ("q", "k")] + [vt, ldv, gu.dev(ci["r"]), n_rel, gu.dev(ci["u"]), gu.dev(ci["vb"]),
+                                                  gu.dev(ci["beta"]) if w.bias_clamp >= 0 else None, gu.dev(dout)]
+    stream = torch.cuda.current_stream()
+
+    def run():
+        xl.xl_rel_attn_core_bwd(desc, *args, g, ws, stream)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(K):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    flops = backward_flops(w)
+    tf = flops / (ms * 1e-3) / 1e12
+    res = {"metric": "rel-attn core backward TFLOP/s (dq, dk, dv, dr, du, dv), 1 GPU", "value": round(tf, 3),
+           "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": warmup, "ms_per_step": round(ms, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32 (bf16 operands)",
+           "data": "synthetic (seeded projected operands of the workload's shape)",
+           "config": {"workload": f"{w.name}: gradients of the fused attention core, batch {B}, {H} heads x {dh}, "
+                                  f"qlen {q}, mlen {m}", "batch": B, "qlen": q, "mlen": m, "n_head": H, "d_head": dh},
+           "roofline": {"kernel": "the backward kernel sequence (fp32 vector arithmetic)", "bound": "alu",
+                        "achieved": round(tf, 3), "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tf / FP32_VALU_PEAK_TFLOPS, 4), "traffic": None,
+                        "algorithmic_flops": flops}}
+    if not no_cpu:
+        import oracle
+        n, t0 = 0, time.perf_counter()
+        while True:
+            b = n % B
+            oracle.rel_attn_core_bwd(ci["q"].f64[b:b + 1], ci["k"].f64[b:b + 1], ci["v"].f64[b:b + 1], ci["r"].f64,
+                                     ci["u"].f64, ci["vb"].f64, dout.f64[b:b + 1], scale=1.0 / np.sqrt(dh),
+                                     clamp_len=w.clamp_len, beta=ci["beta"].f64 if w.bias_clamp >= 0 else None,
+                                     bias_clamp=w.bias_clamp, bias_kind=w.bias_kind)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= 10.0:
+                break
+        cpu = flops / B * n / el / 1e12
+        res["cpu_baseline"] = {"value": round(cpu, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+                               "kind": "oracle", "sample": f"{n} core backwards of one batch element (of {B}) of "
+                                                           f"{w.name}, fp64, {el:.1f} s wall"}
+        res["gpu_over_cpu"] = round(tf / cpu, 1)
     print(json.dumps(res), flush=True)
 
 

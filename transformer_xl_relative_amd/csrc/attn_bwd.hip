@@ -24,6 +24,9 @@
 //   dr:    one wave per table row, d_head across the lanes, over the pairs of
 //          that distance (the last row takes every clamped distance)
 //   small: du, dv and the bias table gradient
+// The row, dq, dk/dv and dr kernels re-read key, table and query rows from
+// the caches for every pair (no tile reuse): a correct baseline, bound by
+// cache bandwidth and latency rather than arithmetic.
 #include "xl_common.hpp"
 #include "xl_internal.hpp"
 
@@ -185,23 +188,41 @@ __global__ void __launch_bounds__(256) bwd_dr_kernel(AttnBwdArgs a) {
     a.dr[w * DH + lane] = acc;
 }
 
-// du, dv (one wave per head, d_head across the lanes) and the bias table
-// gradient (one wave per (head, table row): the lanes split the (b, i) pairs
-// of each distance of the row)
+// du, dv: one workgroup of UVW waves per head, d_head across the lanes; wave
+// w sums the query rows w, w + UVW, ... of the head, then the waves' sums add
+// up in LDS. The bias table gradient: one wave per (head, table row), the
+// lanes split the (b, i) pairs of each distance of the row.
+constexpr int UVW = 16;
+
 template <int DH>
-__global__ void __launch_bounds__(64) bwd_uv_kernel(AttnBwdArgs a) {
-    const int lane = (int)__builtin_amdgcn_workitem_id_x();
+__global__ void __launch_bounds__(64 * UVW) bwd_uv_kernel(AttnBwdArgs a) {
+    __shared__ float part[2][UVW][DH];
+    const int lane = (int)__builtin_amdgcn_workitem_id_x() & 63;
+    const int wave = (int)__builtin_amdgcn_workitem_id_x() >> 6;
     const int h = (int)__builtin_amdgcn_workgroup_id_x();
-    if (lane >= DH) return;
     float su = 0.f, sv = 0.f;
-    for (int b = 0; b < a.B; ++b)
-        for (int i = 0; i < a.qlen; ++i) {
+    if (lane < DH) {
+        const int n = a.B * a.qlen;
+#pragma unroll 4
+        for (int t = wave; t < n; t += UVW) {
+            const int b = t / a.qlen, i = t - b * a.qlen;
             const int64_t row = ((int64_t)b * a.H + h) * a.qlen + i;
             su += a.dqu[row * DH + lane];
             sv += a.dqv[row * DH + lane];
         }
-    a.du[h * DH + lane] = a.scale * su;
-    a.dvb[h * DH + lane] = a.scale * sv;
+        part[0][wave][lane] = su;
+        part[1][wave][lane] = sv;
+    }
+    __syncthreads();
+    if (wave == 0 && lane < DH) {
+        float tu = 0.f, tv = 0.f;
+        for (int x = 0; x < UVW; ++x) {
+            tu += part[0][x][lane];
+            tv += part[1][x][lane];
+        }
+        a.du[h * DH + lane] = a.scale * tu;
+        a.dvb[h * DH + lane] = a.scale * tv;
+    }
 }
 
 __global__ void __launch_bounds__(64) bwd_bias_kernel(AttnBwdArgs a) {
@@ -243,7 +264,7 @@ hipError_t launch_t(const AttnBwdArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<T, DH>), dim3((unsigned)((keys + 3) / 4)), dim3(256), 0, s, a);
     hipLaunchKernelGGL((bwd_dr_kernel<T, DH>), dim3((unsigned)(((int64_t)a.H * a.r_rows + 3) / 4)), dim3(256), 0, s,
                        a);
-    hipLaunchKernelGGL((bwd_uv_kernel<DH>), dim3((unsigned)a.H), dim3(64), 0, s, a);
+    hipLaunchKernelGGL((bwd_uv_kernel<DH>), dim3((unsigned)a.H), dim3(64 * UVW), 0, s, a);
     if (a.bias) hipLaunchKernelGGL(bwd_bias_kernel, dim3((unsigned)(a.bias_rows * a.H)), dim3(64), 0, s, a);
     return hipGetLastError();
 }
