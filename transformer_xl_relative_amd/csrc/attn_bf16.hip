@@ -284,18 +284,26 @@ __global__ void __launch_bounds__(NT, 2) attn_bf16_kernel(AttnArgs a) {
     // ---- query operands (MFMA B operand): lane owns query iw + l32, d_head chunk 16 kc + 8 hf
     const int iq = iw + l32;
     const bool qok = iq < a.qlen;
-    bf16x8 quB[4], qvB[4];
+    // the queries now; u and v of the head reach LDS with the first DMAs (one
+    // instruction each per wave instead of four loads each per lane), and the
+    // biases fold into the query operands once they have landed
+    u32x4 qraw[4];
     {
         const int64_t row = ((int64_t)bh * a.qlen + (qok ? iq : a.qlen - 1)) * DH;
         const bf16_t* qrow = (const bf16_t*)a.q + row;
-        const bf16_t* ub = (const bf16_t*)a.u + h * DH;
-        const bf16_t* vbias = (const bf16_t*)a.v + h * DH;
-        // the biases fold into the query operands: scale*(q+u), scale*(q+v)
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) qraw[kc] = *(const u32x4*)(qrow + 16 * kc + 8 * hf);
+    }
+    bf16x8 quB[4], qvB[4];
+    // u at byte 0 and v at byte 1024 of this wave's ring, before the ring is first written
+    const uint32_t uv_lds = lds0 + OFF_RING + (uint32_t)(wave * WQ * RROW);
+    auto fold_uv = [&]() __attribute__((always_inline)) {
+        // scale*(q+u) and scale*(q+v), rounded once to bf16
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
-            const u32x4 qw = *(const u32x4*)(qrow + 16 * kc + 8 * hf);
-            const u32x4 uw = *(const u32x4*)(ub + 16 * kc + 8 * hf);
-            const u32x4 vw = *(const u32x4*)(vbias + 16 * kc + 8 * hf);
+            const u32x4 uw = lds_ld<u32x4>(uv_lds + 32 * kc + 16 * hf);
+            const u32x4 vw = lds_ld<u32x4>(uv_lds + 1024 + 32 * kc + 16 * hf);
+            const u32x4 qw = qraw[kc];
             u32x4 a_u, a_v;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -308,17 +316,21 @@ __global__ void __launch_bounds__(NT, 2) attn_bf16_kernel(AttnArgs a) {
             quB[kc] = as_bf16x8(a_u);
             qvB[kc] = as_bf16x8(a_v);
         }
-    }
+    };
     const int dtop = a.mlen + iw + WQ - 1;
 
     // ---- prologue DMAs, ordered by when they are needed. Position blocks 0..2
     // of wave w are band blocks 3-w .. 5-w, so the prologue needs band blocks
     // 0..5; blocks 0 and 1 go to the K and V slots that K(2) and V(1) take
     // after the prologue (their band slots hold blocks 6 and 7 by then).
-    //   band 0..4 | K(0), band 5 | K(1), V(0), band 6 | band 7
+    //   u, v, band 0..4 | K(0), band 5 | K(1), V(0), band 6 | band 7
     // (an empty split issues none and writes the neutral partial result)
     auto band0_at = [&](int g) { return g == 0 ? OFF_V + TILE : g == 1 ? OFF_K + 2 * TILE : OFF_B + (g % 6) * TILE; };
     if (nsteps > 0) {
+        // (lanes past the 128 bytes of a head read zeros: the range check)
+        raw_buffer_load_lds(make_rsrc((const char*)a.u + h * (DH * 2), DH * 2), lds_ptr(uv_lds), 16, lane * 16, 0, 0, 0);
+        raw_buffer_load_lds(make_rsrc((const char*)a.v + h * (DH * 2), DH * 2), lds_ptr(uv_lds + 1024), 16, lane * 16,
+                            0, 0, 0);
 #pragma unroll
         for (int g = 0; g <= 4; ++g) dma_band_at(g, band0_at(g));
         dma_k(0, 0);
@@ -545,7 +557,8 @@ __global__ void __launch_bounds__(NT, 2) attn_bf16_kernel(AttnArgs a) {
 
     if (nsteps > 0) {
         // ---- prologue compute: blocks 0 and 1, then the scores of step 0, then block 2
-        block_sync<6>();                       // query operands, band blocks 0..4
+        block_sync<6>();                       // queries, u, v, band blocks 0..4
+        fold_uv();
         ring_write(pos_pro(0), 0u);
         ring_write(pos_pro(1), 128u);
         block_sync<4>();                       // K(0), band block 5
