@@ -196,7 +196,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the relative attention forward is "
-              "built and measured on a single MI355X; see the sharding notes in DESIGN.md", file=sys.stderr)
+              "built and measured on a single MI355X", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

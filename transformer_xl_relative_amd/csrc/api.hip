@@ -75,7 +75,7 @@ int check_desc(const xl_attn_desc* d, int64_t mlen, bool need_dmodel) {
     // every element count a kernel indexes with 32-bit arithmetic must fit
     if (klen > kI32 / 128 || d->batch * klen > kI32 / 2 || hd > 65536 || d->batch * d->n_head > kI32 / 64 ||
         (double)d->batch * d->n_head * klen * d->d_head > 9.0e15)
-        return fail(XL_UNSUPPORTED, "problem too large for this build");
+        return fail(XL_UNSUPPORTED, "problem too large for the 32-bit element offsets of the kernels");
     if (d->batch * d->n_head * ((d->qlen + 127) / 128) > kI32) return fail(XL_UNSUPPORTED, "grid too large");
     // the bf16 attention keeps the bias table of a workgroup's distances in LDS
     if (d->bias_clamp >= 0 && d->dtype == XL_BF16 && klen > kMaxBiasKlen)
