@@ -302,6 +302,7 @@ def test_core_backward_rejects_bad_arguments():
                                         FAKE[5], bias, FAKE[6], dq, dk, FAKE[11], FAKE[12], FAKE[13], FAKE[14], dbias,
                                         ws, nb, None)
     assert call(ldv=klen - 8) == xl.XL_BAD_SHAPE
+    assert call(ldv=klen + 4) == xl.XL_BAD_SHAPE          # not a multiple of 8
     assert call(n_rel=klen - 1) == xl.XL_BAD_SHAPE
     assert call(dq=None) == xl.XL_NULL_ARG
     assert call(desc=_desc(mlen=64, qlen=64, bias_clamp=4), bias=FAKE[7]) == xl.XL_NULL_ARG   # no dbias

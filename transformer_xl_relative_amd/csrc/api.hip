@@ -606,7 +606,7 @@ int xl_rel_attn_core_bwd(const xl_attn_desc* desc, const void* q, const void* k,
     if (desc->bias_clamp >= 0 && (!bias_table || !dbias))
         return fail(XL_NULL_ARG, "bias_clamp >= 0 but bias_table or dbias is NULL");
     const int64_t klen = desc->mlen + desc->qlen;
-    if (ldv < klen) return fail(XL_BAD_SHAPE, "ldv must be >= klen");
+    if (ldv < klen || ldv % 8) return fail(XL_BAD_SHAPE, "ldv must be >= klen and a multiple of 8");
     if (ldv > kI32 / 64) return fail(XL_UNSUPPORTED, "ldv too large");
     const int64_t need = n_rel_of(desc, klen);
     if (n_rel < need) return fail(XL_BAD_SHAPE, "r has %lld rows, needs %lld", (long long)n_rel, (long long)need);

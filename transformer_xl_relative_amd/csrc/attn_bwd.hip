@@ -113,6 +113,128 @@ __global__ void __launch_bounds__(256) bwd_rows_kernel(AttnBwdArgs a) {
     for (int j = lane; j < nv; j += 64) S[j] = P[j] * (S[j] - D);
 }
 
+// The same for bf16 operands and d_head 64, with the key, table and value
+// rows shared through LDS: a workgroup takes RQ consecutive queries of one
+// (b, h) (one wave each) and walks the keys in chunks of RK; each chunk's K
+// rows, the table rows of its RK + RQ - 1 distances, and later its V rows
+// (transposed from V^T as they are stored) are read from memory once for
+// the RQ queries. Rows are padded to 144 bytes so that the lanes' 16-byte
+// reads of their own rows fall on distinct banks.
+constexpr int RQ = 8, RK = 64, KP = 64 * 2 + 16;
+
+__device__ __forceinline__ float dot8(const float* a, const u32x4 w) {
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        s += a[2 * e] * __uint_as_float(w[e] << 16) + a[2 * e + 1] * __uint_as_float(w[e] & 0xFFFF0000u);
+    return s;
+}
+
+__global__ void __launch_bounds__(RQ * 64) bwd_rows_tiled_kernel(AttnBwdArgs a) {
+    constexpr int DH = 64;
+    __shared__ __attribute__((aligned(16))) char kt[RK * KP];
+    __shared__ __attribute__((aligned(16))) char rt[(RK + RQ - 1) * KP];
+    __shared__ __attribute__((aligned(16))) float sh[RQ][3][DH];   // per wave: qu, qv, dO
+    const int tid = (int)__builtin_amdgcn_workitem_id_x();
+    const int lane = tid & 63, wave = tid >> 6;
+    const int nqb = (a.qlen + RQ - 1) / RQ;
+    const int wg = (int)__builtin_amdgcn_workgroup_id_x();
+    const int bh = wg / nqb, i0 = (wg - bh * nqb) * RQ;
+    const int h = bh % a.H, b = bh / a.H;
+    const int i = i0 + wave;
+    const bool live = i < a.qlen;
+    const int64_t row = (int64_t)bh * a.qlen + (live ? i : a.qlen - 1);
+    {
+        const float qd = bf2f(((const bf16_t*)a.q)[row * DH + lane]);
+        sh[wave][0][lane] = a.scale * (qd + bf2f(((const bf16_t*)a.u)[h * DH + lane]));
+        sh[wave][1][lane] = a.scale * (qd + bf2f(((const bf16_t*)a.v)[h * DH + lane]));
+        sh[wave][2][lane] = bf2f(((const bf16_t*)a.dout)[((int64_t)b * a.qlen + (row - (int64_t)bh * a.qlen)) * a.H * DH +
+                                                         h * DH + lane]);
+    }
+    const int nv = live ? a.mlen + i + 1 : 0;                      // visible keys of this wave's query
+    const int jend = a.mlen + (i0 + RQ < a.qlen ? i0 + RQ : a.qlen); // keys any query of the block sees
+    float* P = a.P + row * a.klen;
+    float* S = a.dS + row * a.klen;
+    const bf16_t* kb = (const bf16_t*)a.k + (int64_t)bh * a.klen * DH;
+    const bf16_t* rb = (const bf16_t*)a.r + (int64_t)h * a.r_rows * DH;
+    const bf16_t* vb = (const bf16_t*)a.vt + (int64_t)bh * DH * a.ldv;
+    const float* qu = sh[wave][0];
+    const float* qv = sh[wave][1];
+    const float* go = sh[wave][2];
+    float m = -INFINITY;
+    for (int j0 = 0; j0 < jend; j0 += RK) {
+        // K rows j0 .. j0+RK-1: RK*8 pieces of 16 bytes, one per thread
+        {
+            const int key = tid >> 3, c = tid & 7, jj = j0 + key;
+            const u32x4 w = jj < a.klen ? *(const u32x4*)(kb + (int64_t)jj * DH + 8 * c) : (u32x4){0u, 0u, 0u, 0u};
+            *(u32x4*)(kt + key * KP + 16 * c) = w;
+        }
+        // table rows of distances dlo + n, n < RK + RQ - 1 (clamped into the table)
+        const int dlo = a.mlen + i0 - (j0 + RK - 1);
+        for (int t = tid; t < (RK + RQ - 1) * 8; t += RQ * 64) {
+            const int n = t >> 3, c = t & 7;
+            int dist = dlo + n;
+            dist = dist < 0 ? 0 : (dist > a.n_rel - 1 ? a.n_rel - 1 : dist);
+            const u32x4 w = *(const u32x4*)(rb + (int64_t)dist * DH + 8 * c);
+            *(u32x4*)(rt + n * KP + 16 * c) = w;
+        }
+        __syncthreads();
+        const int j = j0 + lane;
+        if (j < nv) {
+            const int delta = a.mlen + i - j;
+            const int n = delta - dlo;
+            float l = 0.f;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const u32x4 kw = *(const u32x4*)(kt + lane * KP + 16 * c);
+                const u32x4 rw = *(const u32x4*)(rt + n * KP + 16 * c);
+                l += dot8(qu + 8 * c, kw) + dot8(qv + 8 * c, rw);
+            }
+            if (a.bias) l += bf2f(((const bf16_t*)a.bias)[(int64_t)brow(a, delta) * a.H + h]);
+            P[j] = l;
+            m = fmaxf(m, l);
+        }
+        __syncthreads();
+    }
+    m = wmax(m);
+    float s = 0.f;
+    for (int j = lane; j < nv; j += 64) {
+        const float e = __expf(P[j] - m);
+        P[j] = e;
+        s += e;
+    }
+    const float inv = 1.f / wsum(s);
+    float dsum = 0.f;
+    for (int j0 = 0; j0 < jend; j0 += RK) {
+        // V rows of keys j0 .. j0+RK-1, transposed from V^T: a thread reads 8
+        // keys of one d_head row and writes them to 8 key rows
+        {
+            const int d = tid >> 3, c = tid & 7, jj = j0 + 8 * c;
+            const u32x4 w = jj < a.ldv ? *(const u32x4*)(vb + (int64_t)d * a.ldv + jj) : (u32x4){0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t half = (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                *(bf16_t*)(kt + (8 * c + e) * KP + 2 * d) = (bf16_t)half;
+            }
+        }
+        __syncthreads();
+        const int j = j0 + lane;
+        if (j < nv) {
+            float dp = 0.f;
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                dp += dot8(go + 8 * c, *(const u32x4*)(kt + lane * KP + 16 * c));
+            const float p = P[j] * inv;
+            P[j] = p;
+            S[j] = dp;
+            dsum += p * dp;
+        }
+        __syncthreads();
+    }
+    const float D = wsum(dsum);
+    for (int j = lane; j < nv; j += 64) S[j] = P[j] * (S[j] - D);
+}
+
 template <typename T, int DH>
 __global__ void __launch_bounds__(256) bwd_dq_kernel(AttnBwdArgs a) {
     const int lane = (int)__builtin_amdgcn_workitem_id_x() & 63;
@@ -259,7 +381,12 @@ template <typename T, int DH>
 hipError_t launch_t(const AttnBwdArgs& a, hipStream_t s) {
     const int64_t rows = (int64_t)a.B * a.H * a.qlen, keys = (int64_t)a.B * a.H * a.klen;
     (void)hipGetLastError();
-    hipLaunchKernelGGL((bwd_rows_kernel<T, DH>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
+    if constexpr (DH == 64) {
+        const int64_t nqb = (a.qlen + RQ - 1) / RQ;
+        hipLaunchKernelGGL(bwd_rows_tiled_kernel, dim3((unsigned)((int64_t)a.B * a.H * nqb)), dim3(RQ * 64), 0, s, a);
+    } else {
+        hipLaunchKernelGGL((bwd_rows_kernel<T, DH>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
+    }
     hipLaunchKernelGGL((bwd_dq_kernel<T, DH>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
     hipLaunchKernelGGL((bwd_dkdv_kernel<T, DH>), dim3((unsigned)((keys + 3) / 4)), dim3(256), 0, s, a);
     hipLaunchKernelGGL((bwd_dr_kernel<T, DH>), dim3((unsigned)(((int64_t)a.H * a.r_rows + 3) / 4)), dim3(256), 0, s,
