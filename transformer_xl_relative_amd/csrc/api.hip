@@ -591,7 +591,11 @@ size_t xl_rel_attn_core_bwd_workspace_size(const xl_attn_desc* desc) {
     if (!desc || check_desc(desc, desc->mlen, false) != XL_OK) return 0;
     const int64_t rows = desc->batch * desc->n_head * desc->qlen;
     const int64_t klen = desc->mlen + desc->qlen;
-    return 2 * align_up((size_t)(rows * klen) * 4) + 2 * align_up((size_t)(rows * desc->d_head) * 4);
+    const int64_t dr_rows = n_rel_of(desc, klen) - 1;   // per-batch-element partial sums of dr
+    const int64_t kblocks = (klen + 63) / 64;   // softmax partials per query row and block of 64 keys
+    return 2 * align_up((size_t)(rows * klen) * 4) + 2 * align_up((size_t)(rows * desc->d_head) * 4) +
+           align_up((size_t)(desc->batch * desc->n_head * dr_rows * desc->d_head) * 4) +
+           align_up((size_t)(rows * kblocks * 3) * 4) + align_up((size_t)(rows * 3) * 4);
 }
 
 int xl_rel_attn_core_bwd(const xl_attn_desc* desc, const void* q, const void* k, const void* vt, int64_t ldv,
@@ -649,7 +653,14 @@ int xl_rel_attn_core_bwd(const xl_attn_desc* desc, const void* q, const void* k,
     a.P = (float*)(W + off); off += align_up((size_t)(rows * klen) * 4);
     a.dS = (float*)(W + off); off += align_up((size_t)(rows * klen) * 4);
     a.dqu = (float*)(W + off); off += align_up(qb * 4);
-    a.dqv = (float*)(W + off);
+    a.dqv = (float*)(W + off); off += align_up(qb * 4);
+    a.drp = (float*)(W + off); off += align_up((size_t)(desc->batch * H * (need - 1) * dh) * 4);
+    if (dh == 64) {   // the tiled path keeps l and dP with the rows' softmax statistics
+        a.rpart = (float*)(W + off); off += align_up((size_t)(rows * ((klen + 63) / 64) * 3) * 4);
+        a.rstat = (float*)(W + off);
+    }
+    a.uvp = a.dqu;   // the tiled path's du/dv partials (2 x 64 floats per 64 queries) reuse the dq_u, dq_v regions
+    a.dr_first = dh == 64 ? a.n_rel - 1 : 0;   // the tiled dr path (d_head 64) takes the rows below the last
     a.dq = dq; a.dk = dk; a.dv = dv; a.dr = dr; a.du = du; a.dvb = dv_bias; a.dbias = dbias;
     const hipError_t e = xl::launch_attn_bwd(a, desc->dtype == XL_BF16, (int)dh, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "backward launch");

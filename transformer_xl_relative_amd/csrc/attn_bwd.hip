@@ -14,19 +14,23 @@
 // qidao123.com thread-401555 §3; the shift's transpose gathers the band
 // back per distance, felixzhao.cn article 118 §2.3.2).
 //
-// A first, plain form: fp32 vector arithmetic, P and dS materialised in the
-// workspace ([B, H, qlen, klen] fp32 each), every output written by exactly
-// one wave (no atomics):
-//   rows:  one wave per query row, keys across the lanes: logits, softmax,
-//          dP, D, dS
-//   dq:    one wave per query row, d_head across the lanes
-//   dk/dv: one wave per key, d_head across the lanes
-//   dr:    one wave per table row, d_head across the lanes, over the pairs of
-//          that distance (the last row takes every clamped distance)
-//   small: du, dv and the bias table gradient
-// The row, dq, dk/dv and dr kernels re-read key, table and query rows from
-// the caches for every pair (no tile reuse): a correct baseline, bound by
-// cache bandwidth and latency rather than arithmetic.
+// P and dS are materialised in the workspace ([B, H, qlen, klen] fp32 each),
+// the arithmetic is fp32 vector, every output is written by one thread (no
+// atomics). For bf16 operands with d_head 64 the work runs in 64 x 64 blocks
+// staged through LDS:
+//   logits: l and dP per block of (queries, keys), with per-block softmax
+//           partials; row stats combines them into (m, 1/s, D) per row
+//   dk/dv:  rows keys, summed over queries; its loader turns l, dP into
+//           P, dS and writes them back in place for the kernels after it
+//   dq:     rows queries, summed over keys and over distances; it also
+//           leaves per-block column sums for du, dv
+//   dr:     rows table rows below the last in use, summed over the queries
+//           of one batch element; a reduce adds the elements
+//   small:  the last table row in use (every clamped distance), du, dv and
+//           the bias table gradient
+// For fp32 operands (d_head 8) a plain form: one wave per query row (logits,
+// softmax, dP, dS; then dq), per key (dk, dv) and per table row (dr), d_head
+// or keys across the lanes, rows re-read from the caches for every pair.
 #include "xl_common.hpp"
 #include "xl_internal.hpp"
 
@@ -52,6 +56,17 @@ __device__ __forceinline__ float ld(const void* p, int64_t i) {
 // the bias table row of a visible distance (delta >= 0)
 __device__ __forceinline__ int brow(const AttnBwdArgs& a, int delta) {
     return bias_row(delta, a.bias_kind, a.bias_clamp);
+}
+
+// P_ij and dS_ij of a visible pair. With row statistics (the tiled path)
+// the P buffer holds the logits l and the dS buffer dP, and
+// P = exp(l - m_i) / s_i, dS = P (dP - D_i) from the row's (m, 1/s, D).
+__device__ __forceinline__ float2 pds_at(const AttnBwdArgs& a, int64_t row, int j) {
+    const int64_t o = row * a.klen + j;
+    if (!a.rstat) return make_float2(a.P[o], a.dS[o]);
+    const float* st = a.rstat + row * 3;
+    const float p = __expf(a.P[o] - st[0]) * st[1];
+    return make_float2(p, p * (a.dS[o] - st[2]));
 }
 
 template <typename T, int DH>
@@ -113,132 +128,15 @@ __global__ void __launch_bounds__(256) bwd_rows_kernel(AttnBwdArgs a) {
     for (int j = lane; j < nv; j += 64) S[j] = P[j] * (S[j] - D);
 }
 
-// The same for bf16 operands and d_head 64, with the key, table and value
-// rows shared through LDS: a workgroup takes RQ consecutive queries of one
-// (b, h) (one wave each) and walks the keys in chunks of RK; each chunk's K
-// rows, the table rows of its RK + RQ - 1 distances, and later its V rows
-// (transposed from V^T as they are stored) are read from memory once for
-// the RQ queries. Rows are padded to 144 bytes so that the lanes' 16-byte
-// reads of their own rows fall on distinct banks.
-constexpr int RQ = 8, RK = 64, KP = 64 * 2 + 16;
-
-__device__ __forceinline__ float dot8(const float* a, const u32x4 w) {
-    float s = 0.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-        s += a[2 * e] * __uint_as_float(w[e] << 16) + a[2 * e + 1] * __uint_as_float(w[e] & 0xFFFF0000u);
-    return s;
-}
-
-__global__ void __launch_bounds__(RQ * 64) bwd_rows_tiled_kernel(AttnBwdArgs a) {
-    constexpr int DH = 64;
-    __shared__ __attribute__((aligned(16))) char kt[RK * KP];
-    __shared__ __attribute__((aligned(16))) char rt[(RK + RQ - 1) * KP];
-    __shared__ __attribute__((aligned(16))) float sh[RQ][3][DH];   // per wave: qu, qv, dO
-    const int tid = (int)__builtin_amdgcn_workitem_id_x();
-    const int lane = tid & 63, wave = tid >> 6;
-    const int nqb = (a.qlen + RQ - 1) / RQ;
-    const int wg = (int)__builtin_amdgcn_workgroup_id_x();
-    const int bh = wg / nqb, i0 = (wg - bh * nqb) * RQ;
-    const int h = bh % a.H, b = bh / a.H;
-    const int i = i0 + wave;
-    const bool live = i < a.qlen;
-    const int64_t row = (int64_t)bh * a.qlen + (live ? i : a.qlen - 1);
-    {
-        const float qd = bf2f(((const bf16_t*)a.q)[row * DH + lane]);
-        sh[wave][0][lane] = a.scale * (qd + bf2f(((const bf16_t*)a.u)[h * DH + lane]));
-        sh[wave][1][lane] = a.scale * (qd + bf2f(((const bf16_t*)a.v)[h * DH + lane]));
-        sh[wave][2][lane] = bf2f(((const bf16_t*)a.dout)[((int64_t)b * a.qlen + (row - (int64_t)bh * a.qlen)) * a.H * DH +
-                                                         h * DH + lane]);
-    }
-    const int nv = live ? a.mlen + i + 1 : 0;                      // visible keys of this wave's query
-    const int jend = a.mlen + (i0 + RQ < a.qlen ? i0 + RQ : a.qlen); // keys any query of the block sees
-    float* P = a.P + row * a.klen;
-    float* S = a.dS + row * a.klen;
-    const bf16_t* kb = (const bf16_t*)a.k + (int64_t)bh * a.klen * DH;
-    const bf16_t* rb = (const bf16_t*)a.r + (int64_t)h * a.r_rows * DH;
-    const bf16_t* vb = (const bf16_t*)a.vt + (int64_t)bh * DH * a.ldv;
-    const float* qu = sh[wave][0];
-    const float* qv = sh[wave][1];
-    const float* go = sh[wave][2];
-    float m = -INFINITY;
-    for (int j0 = 0; j0 < jend; j0 += RK) {
-        // K rows j0 .. j0+RK-1: RK*8 pieces of 16 bytes, one per thread
-        {
-            const int key = tid >> 3, c = tid & 7, jj = j0 + key;
-            const u32x4 w = jj < a.klen ? *(const u32x4*)(kb + (int64_t)jj * DH + 8 * c) : (u32x4){0u, 0u, 0u, 0u};
-            *(u32x4*)(kt + key * KP + 16 * c) = w;
-        }
-        // table rows of distances dlo + n, n < RK + RQ - 1 (clamped into the table)
-        const int dlo = a.mlen + i0 - (j0 + RK - 1);
-        for (int t = tid; t < (RK + RQ - 1) * 8; t += RQ * 64) {
-            const int n = t >> 3, c = t & 7;
-            int dist = dlo + n;
-            dist = dist < 0 ? 0 : (dist > a.n_rel - 1 ? a.n_rel - 1 : dist);
-            const u32x4 w = *(const u32x4*)(rb + (int64_t)dist * DH + 8 * c);
-            *(u32x4*)(rt + n * KP + 16 * c) = w;
-        }
-        __syncthreads();
-        const int j = j0 + lane;
-        if (j < nv) {
-            const int delta = a.mlen + i - j;
-            const int n = delta - dlo;
-            float l = 0.f;
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const u32x4 kw = *(const u32x4*)(kt + lane * KP + 16 * c);
-                const u32x4 rw = *(const u32x4*)(rt + n * KP + 16 * c);
-                l += dot8(qu + 8 * c, kw) + dot8(qv + 8 * c, rw);
-            }
-            if (a.bias) l += bf2f(((const bf16_t*)a.bias)[(int64_t)brow(a, delta) * a.H + h]);
-            P[j] = l;
-            m = fmaxf(m, l);
-        }
-        __syncthreads();
-    }
-    m = wmax(m);
-    float s = 0.f;
-    for (int j = lane; j < nv; j += 64) {
-        const float e = __expf(P[j] - m);
-        P[j] = e;
-        s += e;
-    }
-    const float inv = 1.f / wsum(s);
-    float dsum = 0.f;
-    for (int j0 = 0; j0 < jend; j0 += RK) {
-        // V rows of keys j0 .. j0+RK-1, transposed from V^T: a thread reads 8
-        // keys of one d_head row and writes them to 8 key rows
-        {
-            const int d = tid >> 3, c = tid & 7, jj = j0 + 8 * c;
-            const u32x4 w = jj < a.ldv ? *(const u32x4*)(vb + (int64_t)d * a.ldv + jj) : (u32x4){0u, 0u, 0u, 0u};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t half = (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-                *(bf16_t*)(kt + (8 * c + e) * KP + 2 * d) = (bf16_t)half;
-            }
-        }
-        __syncthreads();
-        const int j = j0 + lane;
-        if (j < nv) {
-            float dp = 0.f;
-#pragma unroll
-            for (int c = 0; c < 8; ++c)
-                dp += dot8(go + 8 * c, *(const u32x4*)(kt + lane * KP + 16 * c));
-            const float p = P[j] * inv;
-            P[j] = p;
-            S[j] = dp;
-            dsum += p * dp;
-        }
-        __syncthreads();
-    }
-    const float D = wsum(dsum);
-    for (int j = lane; j < nv; j += 64) S[j] = P[j] * (S[j] - D);
-}
+// waves per workgroup of the dq, dk/dv and dr kernels: neighbouring rows of
+// one head in one workgroup share their key, query and table rows in L1
+constexpr int BW = 4;
+constexpr int ILP = 4;   // independent partial sums per lane in their loops
 
 template <typename T, int DH>
-__global__ void __launch_bounds__(256) bwd_dq_kernel(AttnBwdArgs a) {
+__global__ void __launch_bounds__(64 * BW) bwd_dq_kernel(AttnBwdArgs a) {
     const int lane = (int)__builtin_amdgcn_workitem_id_x() & 63;
-    const int64_t row = (int64_t)__builtin_amdgcn_workgroup_id_x() * 4 + ((int)__builtin_amdgcn_workitem_id_x() >> 6);
+    const int64_t row = (int64_t)__builtin_amdgcn_workgroup_id_x() * BW + ((int)__builtin_amdgcn_workitem_id_x() >> 6);
     if (row >= (int64_t)a.B * a.H * a.qlen || lane >= DH) return;
     const int i = (int)(row % a.qlen);
     const int bh = (int)(row / a.qlen);
@@ -246,14 +144,31 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(AttnBwdArgs a) {
     const int nv = a.mlen + i + 1;
     const float* S = a.dS + row * a.klen;
     const int64_t kbase = (int64_t)bh * a.klen;
-    float cu = 0.f, cv = 0.f;
-#pragma unroll 4
-    for (int j = 0; j < nv; ++j) {
+    // ILP partial sums: four keys in flight per iteration
+    float pu[ILP] = {}, pv[ILP] = {};
+    int j = 0;
+    for (; j + ILP <= nv; j += ILP) {
+#pragma unroll
+        for (int x = 0; x < ILP; ++x) {
+            const int delta = a.mlen + i - (j + x);
+            const int c = delta < a.n_rel - 1 ? delta : a.n_rel - 1;
+            const float ds = S[j + x];
+            pu[x] += ds * ld<T>(a.k, (kbase + j + x) * DH + lane);
+            pv[x] += ds * ld<T>(a.r, ((int64_t)h * a.r_rows + c) * DH + lane);
+        }
+    }
+    for (; j < nv; ++j) {
         const int delta = a.mlen + i - j;
         const int c = delta < a.n_rel - 1 ? delta : a.n_rel - 1;
         const float ds = S[j];
-        cu += ds * ld<T>(a.k, (kbase + j) * DH + lane);
-        cv += ds * ld<T>(a.r, ((int64_t)h * a.r_rows + c) * DH + lane);
+        pu[0] += ds * ld<T>(a.k, (kbase + j) * DH + lane);
+        pv[0] += ds * ld<T>(a.r, ((int64_t)h * a.r_rows + c) * DH + lane);
+    }
+    float cu = 0.f, cv = 0.f;
+#pragma unroll
+    for (int x = 0; x < ILP; ++x) {
+        cu += pu[x];
+        cv += pv[x];
     }
     a.dq[row * DH + lane] = a.scale * (cu + cv);
     a.dqu[row * DH + lane] = cu;
@@ -261,9 +176,9 @@ __global__ void __launch_bounds__(256) bwd_dq_kernel(AttnBwdArgs a) {
 }
 
 template <typename T, int DH>
-__global__ void __launch_bounds__(256) bwd_dkdv_kernel(AttnBwdArgs a) {
+__global__ void __launch_bounds__(64 * BW) bwd_dkdv_kernel(AttnBwdArgs a) {
     const int lane = (int)__builtin_amdgcn_workitem_id_x() & 63;
-    const int64_t key = (int64_t)__builtin_amdgcn_workgroup_id_x() * 4 + ((int)__builtin_amdgcn_workitem_id_x() >> 6);
+    const int64_t key = (int64_t)__builtin_amdgcn_workgroup_id_x() * BW + ((int)__builtin_amdgcn_workitem_id_x() >> 6);
     if (key >= (int64_t)a.B * a.H * a.klen || lane >= DH) return;
     const int j = (int)(key % a.klen);
     const int bh = (int)(key / a.klen);
@@ -285,11 +200,12 @@ __global__ void __launch_bounds__(256) bwd_dkdv_kernel(AttnBwdArgs a) {
 
 // one wave per (head, table row c); rows >= n_rel (unused by any pair) get 0
 template <typename T, int DH>
-__global__ void __launch_bounds__(256) bwd_dr_kernel(AttnBwdArgs a) {
+__global__ void __launch_bounds__(64 * BW) bwd_dr_kernel(AttnBwdArgs a) {
     const int lane = (int)__builtin_amdgcn_workitem_id_x() & 63;
-    const int64_t w = (int64_t)__builtin_amdgcn_workgroup_id_x() * 4 + ((int)__builtin_amdgcn_workitem_id_x() >> 6);
-    if (w >= (int64_t)a.H * a.r_rows || lane >= DH) return;
-    const int c = (int)(w % a.r_rows), h = (int)(w / a.r_rows);
+    const int64_t w = (int64_t)__builtin_amdgcn_workgroup_id_x() * BW + ((int)__builtin_amdgcn_workitem_id_x() >> 6);
+    const int nr = a.r_rows - a.dr_first;
+    if (w >= (int64_t)a.H * nr || lane >= DH) return;
+    const int c = a.dr_first + (int)(w % nr), h = (int)(w / nr);
     float acc = 0.f;
     if (c < a.n_rel) {
         const int d_hi = c < a.n_rel - 1 ? c : a.klen - 1;   // distances of row c: [c, d_hi]
@@ -298,16 +214,457 @@ __global__ void __launch_bounds__(256) bwd_dr_kernel(AttnBwdArgs a) {
             const int64_t rbase = ((int64_t)b * a.H + h) * a.qlen;
             for (int delta = c; delta <= d_hi; ++delta) {
                 const int i0 = delta > a.mlen ? delta - a.mlen : 0;
-#pragma unroll 4
-                for (int i = i0; i < a.qlen; ++i) {
-                    const int64_t row = rbase + i;
-                    const float ds = a.dS[row * a.klen + (a.mlen + i - delta)];
-                    acc += ds * a.scale * (ld<T>(a.q, row * DH + lane) + vd);
+                float pa[ILP] = {};
+                int i = i0;
+                for (; i + ILP <= a.qlen; i += ILP) {
+#pragma unroll
+                    for (int x = 0; x < ILP; ++x) {
+                        const int64_t row = rbase + i + x;
+                        pa[x] += pds_at(a, row, a.mlen + i + x - delta).y * (ld<T>(a.q, row * DH + lane) + vd);
+                    }
                 }
+                for (; i < a.qlen; ++i) {
+                    const int64_t row = rbase + i;
+                    pa[0] += pds_at(a, row, a.mlen + i - delta).y * (ld<T>(a.q, row * DH + lane) + vd);
+                }
+#pragma unroll
+                for (int x = 0; x < ILP; ++x) acc += a.scale * pa[x];
             }
         }
     }
-    a.dr[w * DH + lane] = acc;
+    a.dr[((int64_t)h * a.r_rows + c) * DH + lane] = acc;
+}
+
+
+
+// ---- Logits and dP in 64 x 64 blocks (d_head 64) ----
+// A workgroup takes queries i0..i0+63 and keys j0..j0+63 of one head
+// (blocks with no visible pair exit at once) and computes, 4 x 4 pairs per
+// thread, over d_head in chunks of 16 staged through LDS as fp32:
+//   l_ij  = qu_i . k_j + qv_i . r_c(i,j) (+ the bias table entry)
+//   dP_ij = dO_i . v_j
+// The pairs of one block span 127 distances, so the table rows of
+// dlo .. dlo + 127 (dlo = mlen + i0 - j0 - 63, clamped into the table) are
+// staged once and each thread reads the 7 its pairs use. l and dP of the
+// visible pairs go to the P and dS buffers; per row the block's softmax
+// statistics (its max m_t, sum of exp(l - m_t), and sum of exp(l - m_t) dP)
+// go to the partials that bwd_row_stats_kernel combines.
+constexpr int DC = 16, IP = 64 + 4, RP = 128 + 4;
+
+__device__ __forceinline__ void unpack8(const u32x4 w, float* f) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        f[2 * e] = __uint_as_float(w[e] << 16);
+        f[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+    }
+}
+
+__global__ void __launch_bounds__(256) bwd_logits_tile_kernel(AttnBwdArgs a) {
+    constexpr int DH = 64;
+    __shared__ __attribute__((aligned(16))) float quT[DC][IP];
+    __shared__ __attribute__((aligned(16))) float qvT[DC][IP];
+    __shared__ __attribute__((aligned(16))) float doT[DC][IP];
+    __shared__ __attribute__((aligned(16))) float kT[DC][IP];
+    __shared__ __attribute__((aligned(16))) float vT[DC][IP];
+    __shared__ __attribute__((aligned(16))) float rT[DC][RP];
+    const int tid = (int)__builtin_amdgcn_workitem_id_x();
+    const int nit = (a.qlen + 63) / 64, njt = (a.klen + 63) / 64;
+    int wg = (int)__builtin_amdgcn_workgroup_id_x();
+    const int g = wg / (nit * njt);
+    wg -= g * nit * njt;
+    const int it = wg / njt, jt = wg - it * njt;
+    const int i0 = 64 * it, j0 = 64 * jt;
+    const int ilast = i0 + 63 < a.qlen ? i0 + 63 : a.qlen - 1;
+    if (j0 > a.mlen + ilast) return;   // no visible pair in the block
+    const int h = g % a.H, b = g / a.H;
+    const int64_t rb = (int64_t)g * a.qlen;
+    const int dlo = a.mlen + i0 - j0 - 63;
+    const bf16_t* qp = (const bf16_t*)a.q;
+    const bf16_t* op = (const bf16_t*)a.dout;
+    const bf16_t* kp = (const bf16_t*)a.k;
+    const bf16_t* vp = (const bf16_t*)a.vt;
+    const bf16_t* rp = (const bf16_t*)a.r;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    // per chunk a thread loads 16 bytes of three of: q or dO rows (by query),
+    // k rows or V^T rows (by key), and table rows (by distance)
+    const int t7 = tid & 127, row = t7 >> 1, half = t7 & 1;
+    u32x4 f0, f1, f2, fu, fv;
+    auto fetch = [&](int d0) __attribute__((always_inline)) {
+        const int d = d0 + 8 * half, i = i0 + row, j = j0 + row;
+        if (tid < 128) {
+            f0 = i < a.qlen ? *(const u32x4*)(qp + (rb + i) * DH + d) : z;
+            f1 = j < a.klen ? *(const u32x4*)(kp + ((int64_t)g * a.klen + j) * DH + d) : z;
+            fu = *(const u32x4*)((const bf16_t*)a.u + h * DH + d);
+            fv = *(const u32x4*)((const bf16_t*)a.v + h * DH + d);
+        } else {
+            f0 = i < a.qlen ? *(const u32x4*)(op + (((int64_t)b * a.qlen + i) * a.H + h) * DH + d) : z;
+            const int dd = d0 + (t7 >> 3), jj = j0 + 8 * (t7 & 7);
+            f1 = jj < a.ldv ? *(const u32x4*)(vp + ((int64_t)g * DH + dd) * a.ldv + jj) : z;
+        }
+        int dist = dlo + (tid >> 1);
+        dist = dist < 0 ? 0 : (dist > a.n_rel - 1 ? a.n_rel - 1 : dist);
+        f2 = *(const u32x4*)(rp + ((int64_t)h * a.r_rows + dist) * DH + d0 + 8 * (tid & 1));
+    };
+    auto stash = [&]() __attribute__((always_inline)) {
+        float x[8], y[8];
+        unpack8(f0, x);
+        if (tid < 128) {
+            float uu[8], vv[8];
+            unpack8(fu, uu);
+            unpack8(fv, vv);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                quT[8 * half + e][row] = a.scale * (x[e] + uu[e]);
+                qvT[8 * half + e][row] = a.scale * (x[e] + vv[e]);
+            }
+            unpack8(f1, y);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) kT[8 * half + e][row] = y[e];
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) doT[8 * half + e][row] = x[e];
+            unpack8(f1, y);
+            *(f32x4*)&vT[t7 >> 3][8 * (t7 & 7)] = (f32x4){y[0], y[1], y[2], y[3]};
+            *(f32x4*)&vT[t7 >> 3][8 * (t7 & 7) + 4] = (f32x4){y[4], y[5], y[6], y[7]};
+        }
+        unpack8(f2, y);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) rT[8 * (tid & 1) + e][tid >> 1] = y[e];
+    };
+    const int tm = tid >> 4, td = tid & 15;
+    const int n3 = 60 + 4 * (tm - td);   // first of the 8 staged distances this thread reads
+    float al[4][4], ap[4][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) al[r][c] = ap[r][c] = 0.f;
+    fetch(0);
+    for (int d0 = 0; d0 < DH; d0 += DC) {
+        __syncthreads();
+        stash();
+        __syncthreads();
+        if (d0 + DC < DH) fetch(d0 + DC);
+#pragma unroll 4
+        for (int d = 0; d < DC; ++d) {
+            const f32x4 xq = *(const f32x4*)&quT[d][4 * tm];
+            const f32x4 xv = *(const f32x4*)&qvT[d][4 * tm];
+            const f32x4 xo = *(const f32x4*)&doT[d][4 * tm];
+            const f32x4 yk = *(const f32x4*)&kT[d][4 * td];
+            const f32x4 yv = *(const f32x4*)&vT[d][4 * td];
+            const f32x4 r0 = *(const f32x4*)&rT[d][n3];
+            const f32x4 r1 = *(const f32x4*)&rT[d][n3 + 4];
+            const float rr[8] = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    al[r][c] += xq[r] * yk[c] + xv[r] * rr[3 + r - c];
+                    ap[r][c] += xo[r] * yv[c];
+                }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int i = i0 + 4 * tm + r;
+        const int64_t o = (rb + (i < a.qlen ? i : 0)) * a.klen;
+        float m = -INFINITY;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int j = j0 + 4 * td + c;
+            const bool vis = i < a.qlen && j <= a.mlen + i;
+            if (vis) {
+                float l = al[r][c];
+                if (a.bias) l += bf2f(((const bf16_t*)a.bias)[(int64_t)brow(a, a.mlen + i - j) * a.H + h]);
+                al[r][c] = l;
+                a.P[o + j] = l;
+                a.dS[o + j] = ap[r][c];
+                m = fmaxf(m, l);
+            }
+        }
+#pragma unroll
+        for (int x = 1; x < 16; x <<= 1) m = fmaxf(m, __shfl_xor(m, x, 64));
+        float se = 0.f, sd = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int j = j0 + 4 * td + c;
+            if (i < a.qlen && j <= a.mlen + i) {
+                const float e = __expf(al[r][c] - m);
+                se += e;
+                sd += e * ap[r][c];
+            }
+        }
+#pragma unroll
+        for (int x = 1; x < 16; x <<= 1) {
+            se += __shfl_xor(se, x, 64);
+            sd += __shfl_xor(sd, x, 64);
+        }
+        if (td == 0 && i < a.qlen) {
+            float* pt = a.rpart + ((rb + i) * njt + jt) * 3;
+            pt[0] = m;
+            pt[1] = se;
+            pt[2] = sd;
+        }
+    }
+}
+
+// per query row: m = max of the blocks' maxima, s = sum of their exp sums
+// rescaled to m, D = (rescaled sum of exp(l - m_t) dP) / s; stored (m, 1/s, D)
+__global__ void __launch_bounds__(256) bwd_row_stats_kernel(AttnBwdArgs a) {
+    const int64_t row = (int64_t)__builtin_amdgcn_workgroup_id_x() * 256 + (int)__builtin_amdgcn_workitem_id_x();
+    if (row >= (int64_t)a.B * a.H * a.qlen) return;
+    const int i = (int)(row % a.qlen);
+    const int njt = (a.klen + 63) / 64, nt = (a.mlen + i) / 64 + 1;
+    const float* pt = a.rpart + row * njt * 3;
+    float m = -INFINITY;
+    for (int t = 0; t < nt; ++t) m = fmaxf(m, pt[3 * t]);
+    float s = 0.f, e = 0.f;
+    for (int t = 0; t < nt; ++t) {
+        const float w = __expf(pt[3 * t] - m);
+        s += pt[3 * t + 1] * w;
+        e += pt[3 * t + 2] * w;
+    }
+    a.rstat[row * 3] = m;
+    a.rstat[row * 3 + 1] = 1.f / s;
+    a.rstat[row * 3 + 2] = e / s;
+}
+
+// ---- Tiled products for d_head 64 ----
+// With P and dS stored, the dq, dk/dv and dr sums are products of a
+// [rows x t] slice of dS or P with a [t x 64] slice of query, key, table or
+// dO rows, causal entries masked out:
+//   dk/dv: rows keys j,  t queries i:   dS_ij (q_i + u),  P_ij dO_i
+//   dq:    rows queries i, t keys j:    dS_ij k_j, and with t a distance
+//          delta = mlen + i - j:        dS_i(mlen+i-delta) r_min(delta, n_rel-1)
+//   dr:    rows table rows c < n_rel - 1, t queries i of one batch element:
+//          dS_i(mlen+i-c) (q_i + v)
+// A workgroup of 256 threads computes a 64 x 64 block of one head's output,
+// each thread 4 rows x 4 columns of it (one or two products), and stages 32
+// values of t of each operand through LDS as fp32: per t a thread reads one
+// float4 of the [t x rows] slice (four distinct addresses per wave, broadcast)
+// and one of the [t x 64] slice (sixteen contiguous), for 16 fma per product.
+// The next stage's operands are loaded into registers while this one is
+// computed. dr splits over the batch elements (partial sums per element,
+// added by bwd_dr_reduce_kernel) so that its grid fills the chip.
+enum : int { TP_DKDV = 0, TP_DQ = 1, TP_DR = 2 };
+constexpr int TM = 64, TT = 32, AP = TM + 4;
+
+template <int MODE>
+__global__ void __launch_bounds__(256) bwd_tile_kernel(AttnBwdArgs a) {
+    constexpr int DH = 64;
+    constexpr int NP = MODE == TP_DR ? 1 : 2;   // products per block
+    __shared__ __attribute__((aligned(16))) float As[NP][TT][AP];
+    __shared__ __attribute__((aligned(16))) float Bs[NP][TT][DH];
+    const int tid = (int)__builtin_amdgcn_workitem_id_x();
+    const int nrows = MODE == TP_DKDV ? a.klen : (MODE == TP_DQ ? a.qlen : a.dr_first);
+    const int nmt = (nrows + TM - 1) / TM;
+    int wg = (int)__builtin_amdgcn_workgroup_id_x();
+    int b = 0;
+    if (MODE == TP_DR) {   // grid: (batch element, head, row tile)
+        b = wg / (a.H * nmt);
+        wg -= b * a.H * nmt;
+    }
+    const int g = wg / nmt, m0 = (wg - g * nmt) * TM;   // g: b*H + h, or h for dr
+    const int h = MODE == TP_DR ? g : g % a.H;
+    if (MODE != TP_DR) b = g / a.H;
+    const int64_t rb = ((int64_t)b * a.H + h) * a.qlen;   // first query row of the head
+    // t range
+    int t_lo = 0, t_hi;
+    if (MODE == TP_DQ) {
+        const int last = m0 + TM < a.qlen ? m0 + TM - 1 : a.qlen - 1;
+        t_hi = a.mlen + last + 1;
+    } else {
+        t_lo = m0 > a.mlen ? m0 - a.mlen : 0;
+        t_hi = a.qlen;
+    }
+    // the stage operands of this thread
+    float bias8[8];
+    {
+        const int d8 = tid & 7;
+        const bf16_t* bv = (const bf16_t*)(MODE == TP_DKDV ? a.u : a.v) + h * DH + 8 * d8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bias8[e] = (MODE == TP_DQ) ? 0.f : bf2f(bv[e]);
+    }
+    float ra[NP][8];
+    u32x4 rbv[NP];
+    auto fetch = [&](int t0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            int m, t;
+            if (MODE == TP_DQ) {
+                t = t0 + (tid & 31);
+                m = m0 + (tid >> 5) + 8 * k;
+            } else {
+                m = m0 + (tid & 63);
+                t = t0 + (tid >> 6) + 4 * k;
+            }
+            float x0 = 0.f, x1 = 0.f;
+            if (MODE == TP_DKDV) {
+                if (m < a.klen && t < a.qlen && m <= a.mlen + t) {
+                    const float2 pd = pds_at(a, rb + t, m);
+                    x0 = pd.y;
+                    x1 = pd.x;
+                    if (a.rstat) {   // this block is the only reader of the pair: leave P and dS final
+                        const int64_t o = (rb + t) * a.klen + m;
+                        a.P[o] = pd.x;
+                        a.dS[o] = pd.y;
+                    }
+                }
+            } else if (MODE == TP_DQ) {
+                if (m < a.qlen && t <= a.mlen + m) {
+                    x0 = pds_at(a, rb + m, t).y;
+                    x1 = pds_at(a, rb + m, a.mlen + m - t).y;
+                }
+            } else {
+                if (m < a.dr_first && t < a.qlen && m <= a.mlen + t) x0 = pds_at(a, rb + t, a.mlen + t - m).y;
+            }
+            ra[0][k] = x0;
+            if (NP > 1) ra[NP - 1][k] = x1;
+        }
+        const int t = t0 + (tid >> 3), c = 8 * (tid & 7);
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        if (MODE == TP_DKDV) {
+            rbv[0] = t < a.qlen ? *(const u32x4*)((const bf16_t*)a.q + (rb + t) * DH + c) : z;
+            rbv[NP - 1] = t < a.qlen ? *(const u32x4*)((const bf16_t*)a.dout + (((int64_t)b * a.qlen + t) * a.H + h) * DH + c) : z;
+        } else if (MODE == TP_DQ) {
+            const int rr = t < a.n_rel - 1 ? t : a.n_rel - 1;
+            rbv[0] = t < a.klen ? *(const u32x4*)((const bf16_t*)a.k + ((int64_t)g * a.klen + t) * DH + c) : z;
+            rbv[NP - 1] = t < a.klen ? *(const u32x4*)((const bf16_t*)a.r + ((int64_t)h * a.r_rows + rr) * DH + c) : z;
+        } else {
+            rbv[0] = t < a.qlen ? *(const u32x4*)((const bf16_t*)a.q + (rb + t) * DH + c) : z;
+        }
+    };
+    auto stash = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                if (MODE == TP_DQ) As[p][tid & 31][(tid >> 5) + 8 * k] = ra[p][k];
+                else As[p][(tid >> 6) + 4 * k][tid & 63] = ra[p][k];
+            }
+            // the [t x 64] operand in fp32; the first product of dk/dv and dr adds its bias vector
+            const bool add = (MODE == TP_DKDV && p == 0) || MODE == TP_DR;
+            f32x4 lo, hi;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float a0 = __uint_as_float(rbv[p][e] << 16), a1 = __uint_as_float(rbv[p][e] & 0xFFFF0000u);
+                const float b0 = add ? bias8[2 * e] : 0.f, b1 = add ? bias8[2 * e + 1] : 0.f;
+                if (e < 2) {
+                    lo[2 * e] = a0 + b0;
+                    lo[2 * e + 1] = a1 + b1;
+                } else {
+                    hi[2 * e - 4] = a0 + b0;
+                    hi[2 * e - 3] = a1 + b1;
+                }
+            }
+            // rows past the t range hold zeros (their A entries are zero too)
+            *(f32x4*)&Bs[p][tid >> 3][8 * (tid & 7)] = lo;
+            *(f32x4*)&Bs[p][tid >> 3][8 * (tid & 7) + 4] = hi;
+        }
+    };
+    const int tm = tid >> 4, td = tid & 15;
+    float acc[NP][4][4];
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[p][r][c] = 0.f;
+    if (t_lo < t_hi) fetch(t_lo);
+    for (int t0 = t_lo; t0 < t_hi; t0 += TT) {
+        __syncthreads();
+        stash();
+        __syncthreads();
+        if (t0 + TT < t_hi) fetch(t0 + TT);
+#pragma unroll 4
+        for (int t = 0; t < TT; ++t) {
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                const f32x4 x = *(const f32x4*)&As[p][t][4 * tm];
+                const f32x4 y = *(const f32x4*)&Bs[p][t][4 * td];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) acc[p][r][c] += x[r] * y[c];
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int m = m0 + 4 * tm + r;
+        if (m >= nrows) continue;
+        f32x4 o0, o1;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            if (MODE == TP_DKDV) {
+                o0[c] = a.scale * acc[0][r][c];
+                o1[c] = acc[NP - 1][r][c];
+            } else if (MODE == TP_DQ) {
+                o0[c] = a.scale * (acc[0][r][c] + acc[NP - 1][r][c]);
+            } else {
+                o0[c] = acc[0][r][c];
+            }
+        }
+        const int d = 4 * td;
+        if (MODE == TP_DKDV) {
+            const int64_t o = ((int64_t)g * a.klen + m) * DH + d;
+            *(f32x4*)(a.dk + o) = o0;
+            *(f32x4*)(a.dv + o) = o1;
+        } else if (MODE == TP_DQ) {
+            *(f32x4*)(a.dq + (rb + m) * DH + d) = o0;
+        } else {
+            *(f32x4*)(a.drp + (((int64_t)b * a.H + h) * a.dr_first + m) * DH + d) = o0;
+        }
+    }
+    if (MODE == TP_DQ) {
+        // du, dv: the block's column sums of the two products (rows past
+        // qlen are zero), 16 row groups added in LDS, one partial per block
+        float* red = &As[0][0][0];   // 2 x 16 x 64 floats, within As
+        __syncthreads();
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                red[(p * 16 + tm) * DH + 4 * td + c] = acc[p][0][c] + acc[p][1][c] + acc[p][2][c] + acc[p][3][c];
+        __syncthreads();
+        if (tid < 2 * DH) {
+            const int p = tid >> 6, col = tid & 63;
+            float sum = 0.f;
+#pragma unroll
+            for (int x = 0; x < 16; ++x) sum += red[(p * 16 + x) * DH + col];
+            a.uvp[((int64_t)g * nmt + m0 / TM) * 2 * DH + tid] = sum;
+        }
+    }
+}
+
+// du, dv on the tiled path: one workgroup per head adds the dq blocks'
+// partial column sums over the batch elements and query blocks
+__global__ void __launch_bounds__(128) bwd_uv_tiled_kernel(AttnBwdArgs a) {
+    constexpr int DH = 64;
+    const int tid = (int)__builtin_amdgcn_workitem_id_x();
+    const int h = (int)__builtin_amdgcn_workgroup_id_x();
+    const int nmt = (a.qlen + TM - 1) / TM;
+    const int n = a.B * nmt;
+    float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int x = 0; x < n; ++x) {
+        const int b = x / nmt, mt = x - b * nmt;
+        s4[x & 3] += a.uvp[(((int64_t)b * a.H + h) * nmt + mt) * 2 * DH + tid];
+    }
+    const float sum = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+    float* out = tid < DH ? a.du : a.dvb;
+    out[h * DH + (tid & 63)] = a.scale * sum;
+}
+
+// dr rows c < dr_first: the sum of the batch elements' partial sums, scaled
+__global__ void __launch_bounds__(256) bwd_dr_reduce_kernel(AttnBwdArgs a) {
+    constexpr int DH = 64;
+    const int64_t n = (int64_t)a.H * a.dr_first * DH;
+    const int64_t e = (int64_t)__builtin_amdgcn_workgroup_id_x() * 256 + (int)__builtin_amdgcn_workitem_id_x();
+    if (e >= n) return;
+    float s = 0.f;
+    for (int b = 0; b < a.B; ++b) s += a.drp[b * n + e];
+    const int64_t h = e / ((int64_t)a.dr_first * DH), rest = e - h * a.dr_first * DH;
+    a.dr[(h * a.r_rows) * DH + rest] = a.scale * s;
 }
 
 // du, dv: one workgroup of UVW waves per head, d_head across the lanes; wave
@@ -370,7 +727,7 @@ __global__ void __launch_bounds__(64) bwd_bias_kernel(AttnBwdArgs a) {
             for (int t = lane; t < n; t += 64) {
                 const int b = t / (a.qlen - i0), i = i0 + t % (a.qlen - i0);
                 const int64_t row = ((int64_t)b * a.H + h) * a.qlen + i;
-                s += a.dS[row * a.klen + (a.mlen + i - delta)];
+                s += pds_at(a, row, a.mlen + i - delta).y;
             }
         }
     s = wsum(s);
@@ -380,19 +737,36 @@ __global__ void __launch_bounds__(64) bwd_bias_kernel(AttnBwdArgs a) {
 template <typename T, int DH>
 hipError_t launch_t(const AttnBwdArgs& a, hipStream_t s) {
     const int64_t rows = (int64_t)a.B * a.H * a.qlen, keys = (int64_t)a.B * a.H * a.klen;
+    AttnBwdArgs f = a;   // the arguments once P and dS are final
     (void)hipGetLastError();
     if constexpr (DH == 64) {
-        const int64_t nqb = (a.qlen + RQ - 1) / RQ;
-        hipLaunchKernelGGL(bwd_rows_tiled_kernel, dim3((unsigned)((int64_t)a.B * a.H * nqb)), dim3(RQ * 64), 0, s, a);
+        const int64_t nblk = (int64_t)a.B * a.H * ((a.qlen + 63) / 64) * ((a.klen + 63) / 64);
+        hipLaunchKernelGGL(bwd_logits_tile_kernel, dim3((unsigned)nblk), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(bwd_row_stats_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, a);
     } else {
         hipLaunchKernelGGL((bwd_rows_kernel<T, DH>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
     }
-    hipLaunchKernelGGL((bwd_dq_kernel<T, DH>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, DH>), dim3((unsigned)((keys + 3) / 4)), dim3(256), 0, s, a);
-    hipLaunchKernelGGL((bwd_dr_kernel<T, DH>), dim3((unsigned)(((int64_t)a.H * a.r_rows + 3) / 4)), dim3(256), 0, s,
-                       a);
-    hipLaunchKernelGGL((bwd_uv_kernel<DH>), dim3((unsigned)a.H), dim3(64 * UVW), 0, s, a);
-    if (a.bias) hipLaunchKernelGGL(bwd_bias_kernel, dim3((unsigned)(a.bias_rows * a.H)), dim3(64), 0, s, a);
+    if constexpr (DH == 64) {
+        const int64_t BH = (int64_t)a.B * a.H;
+        // dk/dv first: it turns l, dP into P, dS in place, which the later kernels read
+        hipLaunchKernelGGL(bwd_tile_kernel<TP_DKDV>, dim3((unsigned)(BH * ((a.klen + TM - 1) / TM))), dim3(256), 0, s, a);
+        f.rstat = nullptr;
+        hipLaunchKernelGGL(bwd_tile_kernel<TP_DQ>, dim3((unsigned)(BH * ((a.qlen + TM - 1) / TM))), dim3(256), 0, s, f);
+        if (a.dr_first > 0) {
+            hipLaunchKernelGGL(bwd_tile_kernel<TP_DR>, dim3((unsigned)(BH * ((a.dr_first + TM - 1) / TM))), dim3(256), 0, s,
+                               f);
+            hipLaunchKernelGGL(bwd_dr_reduce_kernel,
+                               dim3((unsigned)(((int64_t)a.H * a.dr_first * DH + 255) / 256)), dim3(256), 0, s, f);
+        }
+    } else {
+        hipLaunchKernelGGL((bwd_dq_kernel<T, DH>), dim3((unsigned)((rows + BW - 1) / BW)), dim3(64 * BW), 0, s, a);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<T, DH>), dim3((unsigned)((keys + BW - 1) / BW)), dim3(64 * BW), 0, s, a);
+    }
+    const int64_t nr = a.r_rows - a.dr_first;   // the last table row in use and the unused rows
+    hipLaunchKernelGGL((bwd_dr_kernel<T, DH>), dim3((unsigned)((a.H * nr + BW - 1) / BW)), dim3(64 * BW), 0, s, f);
+    if constexpr (DH == 64) hipLaunchKernelGGL(bwd_uv_tiled_kernel, dim3((unsigned)a.H), dim3(128), 0, s, f);
+    else hipLaunchKernelGGL((bwd_uv_kernel<DH>), dim3((unsigned)a.H), dim3(64 * UVW), 0, s, f);
+    if (a.bias) hipLaunchKernelGGL(bwd_bias_kernel, dim3((unsigned)(a.bias_rows * a.H)), dim3(64), 0, s, f);
     return hipGetLastError();
 }
 
