@@ -339,7 +339,7 @@ def main():
     print(json.dumps(res), flush=True)
 
 
-FP32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector (packed) peak
+FP32_PEAK_TFLOPS = 157.3   # MI355X fp32 peak: dense matrix cores and packed vector alike
 
 
 def backward_flops(w):
@@ -399,9 +399,9 @@ def backward_bench(w, K, warmup, no_cpu):
            "data": "synthetic (seeded projected operands of the workload's shape)",
            "config": {"workload": f"{w.name}: gradients of the fused attention core, batch {B}, {H} heads x {dh}, "
                                   f"qlen {q}, mlen {m}", "batch": B, "qlen": q, "mlen": m, "n_head": H, "d_head": dh},
-           "roofline": {"kernel": "the backward kernel sequence (fp32 vector arithmetic)", "bound": "alu",
-                        "achieved": round(tf, 3), "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
-                        "frac": round(tf / FP32_VALU_PEAK_TFLOPS, 4), "traffic": None,
+           "roofline": {"kernel": "the backward kernel sequence (fp32 matrix-core products)", "bound": "mfma",
+                        "achieved": round(tf, 3), "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tf / FP32_PEAK_TFLOPS, 4), "traffic": None,
                         "algorithmic_flops": flops}}
     if not no_cpu:
         import oracle

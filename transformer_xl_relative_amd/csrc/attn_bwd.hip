@@ -58,6 +58,17 @@ __device__ __forceinline__ int brow(const AttnBwdArgs& a, int delta) {
     return bias_row(delta, a.bias_kind, a.bias_clamp);
 }
 
+// XCD-aware block order for the blocked kernels: workgroups are dealt
+// round-robin to the 8 XCDs (workgroup w runs on XCD w % 8), so numbering
+// them such that XCD x takes the x-th eighth of the n blocks keeps the rows
+// of one head within one L2. Grids are padded to a multiple of 8; a result
+// >= n is padding.
+__device__ __forceinline__ int xcd_block(int n) {
+    const int w = (int)__builtin_amdgcn_workgroup_id_x(), per = (n + 7) / 8;
+    return (w & 7) * per + (w >> 3);
+}
+__host__ __forceinline__ unsigned xcd_grid(int64_t n) { return (unsigned)((n + 7) / 8 * 8); }
+
 // P_ij and dS_ij of a visible pair. With row statistics (the tiled path)
 // the P buffer holds the logits l and the dS buffer dP, and
 // P = exp(l - m_i) / s_i, dS = P (dP - D_i) from the row's (m, 1/s, D).
@@ -239,17 +250,22 @@ __global__ void __launch_bounds__(64 * BW) bwd_dr_kernel(AttnBwdArgs a) {
 
 // ---- Logits and dP in 64 x 64 blocks (d_head 64) ----
 // A workgroup takes queries i0..i0+63 and keys j0..j0+63 of one head
-// (blocks with no visible pair exit at once) and computes, 4 x 4 pairs per
-// thread, over d_head in chunks of 16 staged through LDS as fp32:
-//   l_ij  = qu_i . k_j + qv_i . r_c(i,j) (+ the bias table entry)
-//   dP_ij = dO_i . v_j
-// The pairs of one block span 127 distances, so the table rows of
-// dlo .. dlo + 127 (dlo = mlen + i0 - j0 - 63, clamped into the table) are
-// staged once and each thread reads the 7 its pairs use. l and dP of the
-// visible pairs go to the P and dS buffers; per row the block's softmax
-// statistics (its max m_t, sum of exp(l - m_t), and sum of exp(l - m_t) dP)
-// go to the partials that bwd_row_stats_kernel combines.
-constexpr int DC = 16, IP = 64 + 4, RP = 128 + 4;
+// (blocks with no visible pair exit at once); each of its 4 waves computes a
+// 32 x 32 quarter (queries wm.., keys wn..) on the fp32 matrix cores:
+//   content  qu . k      one 32 x 32 product
+//   dP       dO . v      one 32 x 32 product
+//   position qv . r      a 32 x 64 product over the 64 distances the quarter
+//                        spans, n = 32 + wm - wn + (0..63) counted from
+//                        dlo = mlen + i0 - j0 - 63, then gathered through
+//                        LDS: pair (i, j) takes distance column 31 + i - j
+// Operands are staged as fp32, 16 of d_head at a time, d-contiguous per row
+// (80-byte rows: the lanes' 16-byte reads of 16 rows fall on distinct banks):
+// lane (li, half) feeds row li with d = 8*half .. 8*half + 7. The logits of
+// visible pairs (plus the bias table entry) go to the P buffer, dP to the dS
+// buffer, and per row and half block of 32 keys the softmax partials (max
+// m_t, sum of exp(l - m_t), sum of exp(l - m_t) dP) to those that
+// bwd_row_stats_kernel combines.
+constexpr int DC = 16, DP = DC + 4, BDP = 64 + 4;
 
 __device__ __forceinline__ void unpack8(const u32x4 w, float* f) {
 #pragma unroll
@@ -261,15 +277,18 @@ __device__ __forceinline__ void unpack8(const u32x4 w, float* f) {
 
 __global__ void __launch_bounds__(256) bwd_logits_tile_kernel(AttnBwdArgs a) {
     constexpr int DH = 64;
-    __shared__ __attribute__((aligned(16))) float quT[DC][IP];
-    __shared__ __attribute__((aligned(16))) float qvT[DC][IP];
-    __shared__ __attribute__((aligned(16))) float doT[DC][IP];
-    __shared__ __attribute__((aligned(16))) float kT[DC][IP];
-    __shared__ __attribute__((aligned(16))) float vT[DC][IP];
-    __shared__ __attribute__((aligned(16))) float rT[DC][RP];
+    // operands: qu, qv, dO, k, v rows (64 each) and the table rows of 128 distances
+    __shared__ __attribute__((aligned(16))) float ops[5 * 64 * DP + 128 * DP];
+    float (*quS)[DP] = (float (*)[DP])(ops);
+    float (*qvS)[DP] = (float (*)[DP])(ops + 64 * DP);
+    float (*doS)[DP] = (float (*)[DP])(ops + 2 * 64 * DP);
+    float (*kS)[DP] = (float (*)[DP])(ops + 3 * 64 * DP);
+    float (*vS)[DP] = (float (*)[DP])(ops + 4 * 64 * DP);
+    float (*rS)[DP] = (float (*)[DP])(ops + 5 * 64 * DP);
     const int tid = (int)__builtin_amdgcn_workitem_id_x();
-    const int nit = (a.qlen + 63) / 64, njt = (a.klen + 63) / 64;
-    int wg = (int)__builtin_amdgcn_workgroup_id_x();
+    const int nit = (a.qlen + 63) / 64, njt = (a.klen + 63) / 64, nh = (a.klen + 31) / 32;
+    int wg = xcd_block(a.B * a.H * nit * njt);
+    if (wg >= a.B * a.H * nit * njt) return;
     const int g = wg / (nit * njt);
     wg -= g * nit * njt;
     const int it = wg / njt, jt = wg - it * njt;
@@ -287,10 +306,10 @@ __global__ void __launch_bounds__(256) bwd_logits_tile_kernel(AttnBwdArgs a) {
     const u32x4 z = {0u, 0u, 0u, 0u};
     // per chunk a thread loads 16 bytes of three of: q or dO rows (by query),
     // k rows or V^T rows (by key), and table rows (by distance)
-    const int t7 = tid & 127, row = t7 >> 1, half = t7 & 1;
+    const int t7 = tid & 127, row = t7 >> 1, hf = t7 & 1;
     u32x4 f0, f1, f2, fu, fv;
     auto fetch = [&](int d0) __attribute__((always_inline)) {
-        const int d = d0 + 8 * half, i = i0 + row, j = j0 + row;
+        const int d = d0 + 8 * hf, i = i0 + row, j = j0 + row;
         if (tid < 128) {
             f0 = i < a.qlen ? *(const u32x4*)(qp + (rb + i) * DH + d) : z;
             f1 = j < a.klen ? *(const u32x4*)(kp + ((int64_t)g * a.klen + j) * DH + d) : z;
@@ -308,98 +327,135 @@ __global__ void __launch_bounds__(256) bwd_logits_tile_kernel(AttnBwdArgs a) {
     auto stash = [&]() __attribute__((always_inline)) {
         float x[8], y[8];
         unpack8(f0, x);
+        unpack8(f1, y);
         if (tid < 128) {
             float uu[8], vv[8];
             unpack8(fu, uu);
             unpack8(fv, vv);
+            f32x4 a0, a1, c0, c1;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                quT[8 * half + e][row] = a.scale * (x[e] + uu[e]);
-                qvT[8 * half + e][row] = a.scale * (x[e] + vv[e]);
+            for (int e = 0; e < 4; ++e) {
+                a0[e] = a.scale * (x[e] + uu[e]);
+                a1[e] = a.scale * (x[e + 4] + uu[e + 4]);
+                c0[e] = a.scale * (x[e] + vv[e]);
+                c1[e] = a.scale * (x[e + 4] + vv[e + 4]);
             }
-            unpack8(f1, y);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) kT[8 * half + e][row] = y[e];
+            *(f32x4*)&quS[row][8 * hf] = a0;
+            *(f32x4*)&quS[row][8 * hf + 4] = a1;
+            *(f32x4*)&qvS[row][8 * hf] = c0;
+            *(f32x4*)&qvS[row][8 * hf + 4] = c1;
+            *(f32x4*)&kS[row][8 * hf] = (f32x4){y[0], y[1], y[2], y[3]};
+            *(f32x4*)&kS[row][8 * hf + 4] = (f32x4){y[4], y[5], y[6], y[7]};
         } else {
+            *(f32x4*)&doS[row][8 * hf] = (f32x4){x[0], x[1], x[2], x[3]};
+            *(f32x4*)&doS[row][8 * hf + 4] = (f32x4){x[4], x[5], x[6], x[7]};
 #pragma unroll
-            for (int e = 0; e < 8; ++e) doT[8 * half + e][row] = x[e];
-            unpack8(f1, y);
-            *(f32x4*)&vT[t7 >> 3][8 * (t7 & 7)] = (f32x4){y[0], y[1], y[2], y[3]};
-            *(f32x4*)&vT[t7 >> 3][8 * (t7 & 7) + 4] = (f32x4){y[4], y[5], y[6], y[7]};
+            for (int e = 0; e < 8; ++e) vS[8 * (t7 & 7) + e][t7 >> 3] = y[e];   // V^T -> key rows
         }
         unpack8(f2, y);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) rT[8 * (tid & 1) + e][tid >> 1] = y[e];
+        *(f32x4*)&rS[tid >> 1][8 * (tid & 1)] = (f32x4){y[0], y[1], y[2], y[3]};
+        *(f32x4*)&rS[tid >> 1][8 * (tid & 1) + 4] = (f32x4){y[4], y[5], y[6], y[7]};
     };
-    const int tm = tid >> 4, td = tid & 15;
-    const int n3 = 60 + 4 * (tm - td);   // first of the 8 staged distances this thread reads
-    float al[4][4], ap[4][4];
+    const int lane = tid & 63, wave = tid >> 6, half = lane >> 5, li = lane & 31;
+    const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
+    const int nb = 32 + wm - wn;   // first staged distance row of this quarter
+    f32x16 ac, ap, ab0, ab1;
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) al[r][c] = ap[r][c] = 0.f;
+    for (int v = 0; v < 16; ++v) ac[v] = ap[v] = ab0[v] = ab1[v] = 0.f;
     fetch(0);
     for (int d0 = 0; d0 < DH; d0 += DC) {
         __syncthreads();
         stash();
         __syncthreads();
         if (d0 + DC < DH) fetch(d0 + DC);
-#pragma unroll 4
-        for (int d = 0; d < DC; ++d) {
-            const f32x4 xq = *(const f32x4*)&quT[d][4 * tm];
-            const f32x4 xv = *(const f32x4*)&qvT[d][4 * tm];
-            const f32x4 xo = *(const f32x4*)&doT[d][4 * tm];
-            const f32x4 yk = *(const f32x4*)&kT[d][4 * td];
-            const f32x4 yv = *(const f32x4*)&vT[d][4 * td];
-            const f32x4 r0 = *(const f32x4*)&rT[d][n3];
-            const f32x4 r1 = *(const f32x4*)&rT[d][n3 + 4];
-            const float rr[8] = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
+        for (int s2 = 0; s2 < 2; ++s2) {
+            const int c = 8 * half + 4 * s2;
+            const f32x4 xq = *(const f32x4*)&quS[wm + li][c];
+            const f32x4 xv = *(const f32x4*)&qvS[wm + li][c];
+            const f32x4 xo = *(const f32x4*)&doS[wm + li][c];
+            const f32x4 yk = *(const f32x4*)&kS[wn + li][c];
+            const f32x4 yv = *(const f32x4*)&vS[wn + li][c];
+            const f32x4 r0 = *(const f32x4*)&rS[nb + li][c];
+            const f32x4 r1 = *(const f32x4*)&rS[nb + 32 + li][c];
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    al[r][c] += xq[r] * yk[c] + xv[r] * rr[3 + r - c];
-                    ap[r][c] += xo[r] * yv[c];
-                }
+            for (int e = 0; e < 4; ++e) {
+                ac = __builtin_amdgcn_mfma_f32_32x32x2f32(xq[e], yk[e], ac, 0, 0, 0);
+                ab0 = __builtin_amdgcn_mfma_f32_32x32x2f32(xv[e], r0[e], ab0, 0, 0, 0);
+                ab1 = __builtin_amdgcn_mfma_f32_32x32x2f32(xv[e], r1[e], ab1, 0, 0, 0);
+                ap = __builtin_amdgcn_mfma_f32_32x32x2f32(xo[e], yv[e], ap, 0, 0, 0);
+            }
         }
     }
+    // the positional quarter through LDS (reusing the operand area, 4 x 32 x BDP floats)
+    float (*bd)[BDP] = (float (*)[BDP])(ops + wave * 32 * BDP);
+    __syncthreads();
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int i = i0 + 4 * tm + r;
-        const int64_t o = (rb + (i < a.qlen ? i : 0)) * a.klen;
-        float m = -INFINITY;
+    for (int v = 0; v < 16; ++v) {
+        const int r = 8 * (v >> 2) + 4 * half + (v & 3);
+        bd[r][li] = ab0[v];
+        bd[r][32 + li] = ab1[v];
+    }
+    __syncthreads();
+    // accumulator v of lane (li, half): query row wm + r, r = 8 (v / 4) + 4 half + v % 4; key wn + li
+    const int j = j0 + wn + li;
+    float lv[16];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int j = j0 + 4 * td + c;
-            const bool vis = i < a.qlen && j <= a.mlen + i;
-            if (vis) {
-                float l = al[r][c];
-                if (a.bias) l += bf2f(((const bf16_t*)a.bias)[(int64_t)brow(a, a.mlen + i - j) * a.H + h]);
-                al[r][c] = l;
-                a.P[o + j] = l;
-                a.dS[o + j] = ap[r][c];
-                m = fmaxf(m, l);
+    for (int v = 0; v < 16; ++v) {
+        const int r = 8 * (v >> 2) + 4 * half + (v & 3);
+        const int i = i0 + wm + r;
+        const bool vis = i < a.qlen && j <= a.mlen + i;
+        float l = ac[v] + bd[r][31 + r - li];
+        if (vis && a.bias) l += bf2f(((const bf16_t*)a.bias)[(int64_t)brow(a, a.mlen + i - j) * a.H + h]);
+        if (vis) {
+            const int64_t o = (rb + i) * a.klen + j;
+            a.P[o] = l;
+            a.dS[o] = ap[v];
+        }
+        lv[v] = vis ? l : -INFINITY;
+    }
+    // the softmax partials from l and dP laid out by row in LDS: thread
+    // (row, q) reduces keys 16 q .. 16 q + 15, two threads per half block
+    float (*ls)[BDP] = (float (*)[BDP])(ops);
+    float (*dps)[BDP] = (float (*)[BDP])(ops + 64 * BDP);
+    __syncthreads();
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        const int r = 8 * (v >> 2) + 4 * half + (v & 3);
+        ls[wm + r][wn + li] = lv[v];
+        dps[wm + r][wn + li] = ap[v];
+    }
+    __syncthreads();
+    {
+        const int rr = tid >> 2, q = tid & 3;
+        float lx[16], px[16];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const f32x4 x = *(const f32x4*)&ls[rr][16 * q + 4 * k];
+            const f32x4 y = *(const f32x4*)&dps[rr][16 * q + 4 * k];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                lx[4 * k + e] = x[e];
+                px[4 * k + e] = y[e];
             }
         }
+        float m = lx[0];
 #pragma unroll
-        for (int x = 1; x < 16; x <<= 1) m = fmaxf(m, __shfl_xor(m, x, 64));
+        for (int k = 1; k < 16; ++k) m = fmaxf(m, lx[k]);
+        m = fmaxf(m, __shfl_xor(m, 1, 64));
         float se = 0.f, sd = 0.f;
+        if (m != -INFINITY)   // a half block with no visible pair in this row contributes nothing
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int j = j0 + 4 * td + c;
-            if (i < a.qlen && j <= a.mlen + i) {
-                const float e = __expf(al[r][c] - m);
+            for (int k = 0; k < 16; ++k) {
+                const float e = __expf(lx[k] - m);
                 se += e;
-                sd += e * ap[r][c];
+                sd += e * px[k];
             }
-        }
-#pragma unroll
-        for (int x = 1; x < 16; x <<= 1) {
-            se += __shfl_xor(se, x, 64);
-            sd += __shfl_xor(sd, x, 64);
-        }
-        if (td == 0 && i < a.qlen) {
-            float* pt = a.rpart + ((rb + i) * njt + jt) * 3;
+        se += __shfl_xor(se, 1, 64);
+        sd += __shfl_xor(sd, 1, 64);
+        const int i = i0 + rr, hb = q >> 1;
+        if ((q & 1) == 0 && i < a.qlen && j0 + 32 * hb < a.klen) {   // half blocks past klen have no partials
+            float* pt = a.rpart + ((rb + i) * nh + 2 * jt + hb) * 3;
             pt[0] = m;
             pt[1] = se;
             pt[2] = sd;
@@ -407,14 +463,15 @@ __global__ void __launch_bounds__(256) bwd_logits_tile_kernel(AttnBwdArgs a) {
     }
 }
 
-// per query row: m = max of the blocks' maxima, s = sum of their exp sums
-// rescaled to m, D = (rescaled sum of exp(l - m_t) dP) / s; stored (m, 1/s, D)
+// per query row: m = max of the half blocks' maxima, s = sum of their exp
+// sums rescaled to m, D = (rescaled sum of exp(l - m_t) dP) / s; stored
+// (m, 1/s, D)
 __global__ void __launch_bounds__(256) bwd_row_stats_kernel(AttnBwdArgs a) {
     const int64_t row = (int64_t)__builtin_amdgcn_workgroup_id_x() * 256 + (int)__builtin_amdgcn_workitem_id_x();
     if (row >= (int64_t)a.B * a.H * a.qlen) return;
     const int i = (int)(row % a.qlen);
-    const int njt = (a.klen + 63) / 64, nt = (a.mlen + i) / 64 + 1;
-    const float* pt = a.rpart + row * njt * 3;
+    const int nh = (a.klen + 31) / 32, nt = (a.mlen + i) / 32 + 1;
+    const float* pt = a.rpart + row * nh * 3;
     float m = -INFINITY;
     for (int t = 0; t < nt; ++t) m = fmaxf(m, pt[3 * t]);
     float s = 0.f, e = 0.f;
@@ -437,27 +494,30 @@ __global__ void __launch_bounds__(256) bwd_row_stats_kernel(AttnBwdArgs a) {
 //          delta = mlen + i - j:        dS_i(mlen+i-delta) r_min(delta, n_rel-1)
 //   dr:    rows table rows c < n_rel - 1, t queries i of one batch element:
 //          dS_i(mlen+i-c) (q_i + v)
-// A workgroup of 256 threads computes a 64 x 64 block of one head's output,
-// each thread 4 rows x 4 columns of it (one or two products), and stages 32
-// values of t of each operand through LDS as fp32: per t a thread reads one
-// float4 of the [t x rows] slice (four distinct addresses per wave, broadcast)
-// and one of the [t x 64] slice (sixteen contiguous), for 16 fma per product.
-// The next stage's operands are loaded into registers while this one is
-// computed. dr splits over the batch elements (partial sums per element,
+// A workgroup of 4 waves computes a 64 x 64 block of one head's output, a
+// 32 x 32 quarter per wave on the fp32 matrix cores (v_mfma_f32_32x32x2_f32,
+// one or two products), and stages 32 values of t of each operand through
+// LDS as fp32, both operands t-contiguous per row (rows padded to 144 bytes):
+// lane (li, half) feeds row li with the t values 16*half .. 16*half + 15, so
+// four 16-byte LDS reads per operand serve the stage's 16 matrix
+// instructions (k of an instruction is the lane half; the two halves take
+// different t, which only reorders the sum). The next stage's operands are
+// loaded into registers while this one is computed. dr splits over the batch elements (partial sums per element,
 // added by bwd_dr_reduce_kernel) so that its grid fills the chip.
 enum : int { TP_DKDV = 0, TP_DQ = 1, TP_DR = 2 };
-constexpr int TM = 64, TT = 32, AP = TM + 4;
+constexpr int TM = 64, TT = 32, TP = TT + 4;
 
 template <int MODE>
 __global__ void __launch_bounds__(256) bwd_tile_kernel(AttnBwdArgs a) {
     constexpr int DH = 64;
     constexpr int NP = MODE == TP_DR ? 1 : 2;   // products per block
-    __shared__ __attribute__((aligned(16))) float As[NP][TT][AP];
-    __shared__ __attribute__((aligned(16))) float Bs[NP][TT][DH];
+    __shared__ __attribute__((aligned(16))) float As[NP][TM][TP];
+    __shared__ __attribute__((aligned(16))) float Bs[NP][DH][TP];
     const int tid = (int)__builtin_amdgcn_workitem_id_x();
     const int nrows = MODE == TP_DKDV ? a.klen : (MODE == TP_DQ ? a.qlen : a.dr_first);
     const int nmt = (nrows + TM - 1) / TM;
-    int wg = (int)__builtin_amdgcn_workgroup_id_x();
+    int wg = xcd_block(a.B * a.H * nmt);
+    if (wg >= a.B * a.H * nmt) return;
     int b = 0;
     if (MODE == TP_DR) {   // grid: (batch element, head, row tile)
         b = wg / (a.H * nmt);
@@ -499,23 +559,24 @@ __global__ void __launch_bounds__(256) bwd_tile_kernel(AttnBwdArgs a) {
             }
             float x0 = 0.f, x1 = 0.f;
             if (MODE == TP_DKDV) {
+                // P, dS from l, dP and the row's statistics; this block is the
+                // only reader of the pair, so it leaves P and dS final in place
                 if (m < a.klen && t < a.qlen && m <= a.mlen + t) {
-                    const float2 pd = pds_at(a, rb + t, m);
-                    x0 = pd.y;
-                    x1 = pd.x;
-                    if (a.rstat) {   // this block is the only reader of the pair: leave P and dS final
-                        const int64_t o = (rb + t) * a.klen + m;
-                        a.P[o] = pd.x;
-                        a.dS[o] = pd.y;
-                    }
+                    const int64_t o = (rb + t) * a.klen + m;
+                    const float* st = a.rstat + (rb + t) * 3;
+                    x1 = __expf(a.P[o] - st[0]) * st[1];
+                    x0 = x1 * (a.dS[o] - st[2]);
+                    a.P[o] = x1;
+                    a.dS[o] = x0;
                 }
-            } else if (MODE == TP_DQ) {
+            } else if (MODE == TP_DQ) {   // dS is final by now
                 if (m < a.qlen && t <= a.mlen + m) {
-                    x0 = pds_at(a, rb + m, t).y;
-                    x1 = pds_at(a, rb + m, a.mlen + m - t).y;
+                    const int64_t o = (rb + m) * a.klen;
+                    x0 = a.dS[o + t];
+                    x1 = a.dS[o + (a.mlen + m - t)];
                 }
             } else {
-                if (m < a.dr_first && t < a.qlen && m <= a.mlen + t) x0 = pds_at(a, rb + t, a.mlen + t - m).y;
+                if (m < a.dr_first && t < a.qlen && m <= a.mlen + t) x0 = a.dS[(rb + t) * a.klen + (a.mlen + t - m)];
             }
             ra[0][k] = x0;
             if (NP > 1) ra[NP - 1][k] = x1;
@@ -538,100 +599,82 @@ __global__ void __launch_bounds__(256) bwd_tile_kernel(AttnBwdArgs a) {
         for (int p = 0; p < NP; ++p) {
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                if (MODE == TP_DQ) As[p][tid & 31][(tid >> 5) + 8 * k] = ra[p][k];
-                else As[p][(tid >> 6) + 4 * k][tid & 63] = ra[p][k];
+                if (MODE == TP_DQ) As[p][(tid >> 5) + 8 * k][tid & 31] = ra[p][k];
+                else As[p][tid & 63][(tid >> 6) + 4 * k] = ra[p][k];
             }
             // the [t x 64] operand in fp32; the first product of dk/dv and dr adds its bias vector
             const bool add = (MODE == TP_DKDV && p == 0) || MODE == TP_DR;
-            f32x4 lo, hi;
+            // t past the range hold zeros (their A entries are zero too)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float a0 = __uint_as_float(rbv[p][e] << 16), a1 = __uint_as_float(rbv[p][e] & 0xFFFF0000u);
                 const float b0 = add ? bias8[2 * e] : 0.f, b1 = add ? bias8[2 * e + 1] : 0.f;
-                if (e < 2) {
-                    lo[2 * e] = a0 + b0;
-                    lo[2 * e + 1] = a1 + b1;
-                } else {
-                    hi[2 * e - 4] = a0 + b0;
-                    hi[2 * e - 3] = a1 + b1;
-                }
+                Bs[p][8 * (tid & 7) + 2 * e][tid >> 3] = a0 + b0;
+                Bs[p][8 * (tid & 7) + 2 * e + 1][tid >> 3] = a1 + b1;
             }
-            // rows past the t range hold zeros (their A entries are zero too)
-            *(f32x4*)&Bs[p][tid >> 3][8 * (tid & 7)] = lo;
-            *(f32x4*)&Bs[p][tid >> 3][8 * (tid & 7) + 4] = hi;
         }
     };
-    const int tm = tid >> 4, td = tid & 15;
-    float acc[NP][4][4];
+    const int lane = tid & 63, wave = tid >> 6, half = lane >> 5, li = lane & 31;
+    const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;   // this wave's quarter of the block
+    f32x16 acc[NP];
 #pragma unroll
     for (int p = 0; p < NP; ++p)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) acc[p][r][c] = 0.f;
+        for (int v = 0; v < 16; ++v) acc[p][v] = 0.f;
     if (t_lo < t_hi) fetch(t_lo);
     for (int t0 = t_lo; t0 < t_hi; t0 += TT) {
         __syncthreads();
         stash();
         __syncthreads();
         if (t0 + TT < t_hi) fetch(t0 + TT);
-#pragma unroll 4
-        for (int t = 0; t < TT; ++t) {
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
 #pragma unroll
             for (int p = 0; p < NP; ++p) {
-                const f32x4 x = *(const f32x4*)&As[p][t][4 * tm];
-                const f32x4 y = *(const f32x4*)&Bs[p][t][4 * td];
+                const f32x4 x = *(const f32x4*)&As[p][wm + li][16 * half + 4 * s4];
+                const f32x4 y = *(const f32x4*)&Bs[p][wn + li][16 * half + 4 * s4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) acc[p][r][c] += x[r] * y[c];
+                for (int e = 0; e < 4; ++e) acc[p] = __builtin_amdgcn_mfma_f32_32x32x2f32(x[e], y[e], acc[p], 0, 0, 0);
             }
         }
     }
+    // accumulator v of lane (li, half): row wm + 8 (v / 4) + 4 half + v % 4, column wn + li
+    const int d = wn + li;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int m = m0 + 4 * tm + r;
+    for (int v = 0; v < 16; ++v) {
+        const int m = m0 + wm + 8 * (v >> 2) + 4 * half + (v & 3);
         if (m >= nrows) continue;
-        f32x4 o0, o1;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            if (MODE == TP_DKDV) {
-                o0[c] = a.scale * acc[0][r][c];
-                o1[c] = acc[NP - 1][r][c];
-            } else if (MODE == TP_DQ) {
-                o0[c] = a.scale * (acc[0][r][c] + acc[NP - 1][r][c]);
-            } else {
-                o0[c] = acc[0][r][c];
-            }
-        }
-        const int d = 4 * td;
         if (MODE == TP_DKDV) {
             const int64_t o = ((int64_t)g * a.klen + m) * DH + d;
-            *(f32x4*)(a.dk + o) = o0;
-            *(f32x4*)(a.dv + o) = o1;
+            a.dk[o] = a.scale * acc[0][v];
+            a.dv[o] = acc[NP - 1][v];
         } else if (MODE == TP_DQ) {
-            *(f32x4*)(a.dq + (rb + m) * DH + d) = o0;
+            a.dq[(rb + m) * DH + d] = a.scale * (acc[0][v] + acc[NP - 1][v]);
         } else {
-            *(f32x4*)(a.drp + (((int64_t)b * a.H + h) * a.dr_first + m) * DH + d) = o0;
+            a.drp[(((int64_t)b * a.H + h) * a.dr_first + m) * DH + d] = acc[0][v];
         }
     }
     if (MODE == TP_DQ) {
         // du, dv: the block's column sums of the two products (rows past
-        // qlen are zero), 16 row groups added in LDS, one partial per block
-        float* red = &As[0][0][0];   // 2 x 16 x 64 floats, within As
+        // qlen are zero): a lane's 16 rows, the other half's, then the two
+        // waves of each column half added in LDS; one partial per block
+        float* red = &As[0][0][0];   // 2 products x 2 row halves x 64 floats, within As
+        float cs[NP];
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            float x = 0.f;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) x += acc[p][v];
+            cs[p] = x + __shfl_xor(x, 32, 64);
+        }
         __syncthreads();
+        if (half == 0)
 #pragma unroll
-        for (int p = 0; p < NP; ++p)
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-                red[(p * 16 + tm) * DH + 4 * td + c] = acc[p][0][c] + acc[p][1][c] + acc[p][2][c] + acc[p][3][c];
+            for (int p = 0; p < NP; ++p) red[(p * 2 + (wave >> 1)) * DH + d] = cs[p];
         __syncthreads();
         if (tid < 2 * DH) {
             const int p = tid >> 6, col = tid & 63;
-            float sum = 0.f;
-#pragma unroll
-            for (int x = 0; x < 16; ++x) sum += red[(p * 16 + x) * DH + col];
-            a.uvp[((int64_t)g * nmt + m0 / TM) * 2 * DH + tid] = sum;
+            a.uvp[((int64_t)g * nmt + m0 / TM) * 2 * DH + tid] = red[(p * 2) * DH + col] + red[(p * 2 + 1) * DH + col];
         }
     }
 }
@@ -741,7 +784,7 @@ hipError_t launch_t(const AttnBwdArgs& a, hipStream_t s) {
     (void)hipGetLastError();
     if constexpr (DH == 64) {
         const int64_t nblk = (int64_t)a.B * a.H * ((a.qlen + 63) / 64) * ((a.klen + 63) / 64);
-        hipLaunchKernelGGL(bwd_logits_tile_kernel, dim3((unsigned)nblk), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(bwd_logits_tile_kernel, dim3(xcd_grid(nblk)), dim3(256), 0, s, a);
         hipLaunchKernelGGL(bwd_row_stats_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, a);
     } else {
         hipLaunchKernelGGL((bwd_rows_kernel<T, DH>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
@@ -749,11 +792,11 @@ hipError_t launch_t(const AttnBwdArgs& a, hipStream_t s) {
     if constexpr (DH == 64) {
         const int64_t BH = (int64_t)a.B * a.H;
         // dk/dv first: it turns l, dP into P, dS in place, which the later kernels read
-        hipLaunchKernelGGL(bwd_tile_kernel<TP_DKDV>, dim3((unsigned)(BH * ((a.klen + TM - 1) / TM))), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(bwd_tile_kernel<TP_DKDV>, dim3(xcd_grid(BH * ((a.klen + TM - 1) / TM))), dim3(256), 0, s, a);
         f.rstat = nullptr;
-        hipLaunchKernelGGL(bwd_tile_kernel<TP_DQ>, dim3((unsigned)(BH * ((a.qlen + TM - 1) / TM))), dim3(256), 0, s, f);
+        hipLaunchKernelGGL(bwd_tile_kernel<TP_DQ>, dim3(xcd_grid(BH * ((a.qlen + TM - 1) / TM))), dim3(256), 0, s, f);
         if (a.dr_first > 0) {
-            hipLaunchKernelGGL(bwd_tile_kernel<TP_DR>, dim3((unsigned)(BH * ((a.dr_first + TM - 1) / TM))), dim3(256), 0, s,
+            hipLaunchKernelGGL(bwd_tile_kernel<TP_DR>, dim3(xcd_grid(BH * ((a.dr_first + TM - 1) / TM))), dim3(256), 0, s,
                                f);
             hipLaunchKernelGGL(bwd_dr_reduce_kernel,
                                dim3((unsigned)(((int64_t)a.H * a.dr_first * DH + 255) / 256)), dim3(256), 0, s, f);
