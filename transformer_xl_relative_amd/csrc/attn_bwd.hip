@@ -21,7 +21,7 @@
 //   logits: l and dP per block of (queries, keys), with per-block softmax
 //           partials; row stats combines them into (m, 1/s, D) per row
 //   dk/dv:  rows keys, summed over queries; its loader turns l, dP into
-//           P, dS and writes them back in place for the kernels after it
+//           P, dS and writes dS back in place for the kernels after it
 //   dq:     rows queries, summed over keys and over distances; it also
 //           leaves per-block column sums for du, dv
 //   dr:     rows table rows below the last in use, summed over the queries
@@ -560,13 +560,13 @@ __global__ void __launch_bounds__(256) bwd_tile_kernel(AttnBwdArgs a) {
             float x0 = 0.f, x1 = 0.f;
             if (MODE == TP_DKDV) {
                 // P, dS from l, dP and the row's statistics; this block is the
-                // only reader of the pair, so it leaves P and dS final in place
+                // only reader of the pair, so it leaves dS final in place (the
+                // kernels after it read dS only)
                 if (m < a.klen && t < a.qlen && m <= a.mlen + t) {
                     const int64_t o = (rb + t) * a.klen + m;
                     const float* st = a.rstat + (rb + t) * 3;
                     x1 = __expf(a.P[o] - st[0]) * st[1];
                     x0 = x1 * (a.dS[o] - st[2]);
-                    a.P[o] = x1;
                     a.dS[o] = x0;
                 }
             } else if (MODE == TP_DQ) {   // dS is final by now

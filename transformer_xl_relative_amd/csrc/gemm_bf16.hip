@@ -3,10 +3,12 @@
 // nn.Linear weights [out, in]).
 //
 // Up to four independent projections run as one grid; each workgroup owns a
-// square output tile of one of them: 256 x 256 (eight waves, 4 x 2, each
-// holding 64 x 128 in 2 x 4 accumulator blocks of 32 x 32; two waves per SIMD)
-// or 128 x 128 (eight waves, 2 x 4, each 64 x 32) for grids that the large
-// tile would leave too small, or 64 x 64 (four waves, each 32 x 32, eight LDS
+// square output tile of one of them: 256 x 256 (sixteen waves, 4 x 4, each
+// holding 64 x 64 in 2 x 2 accumulator blocks of 32 x 32; four waves per SIMD,
+// which hide the operand loads better than eight waves of 64 x 128)
+// or 128 x 128 (sixteen waves, each 32 x 32, three stages; eight waves of
+// 64 x 32 with two stages where two workgroups share a CU) for grids that the
+// large tile would leave too small, or 64 x 64 (four waves, each 32 x 32, eight LDS
 // stages) for small problems whose time is set by the latency of each stage.
 //
 // K advances 64 elements (128 bytes, whole cache lines, per operand row) per
@@ -33,40 +35,46 @@ namespace {
 
 using namespace gemm;
 
-constexpr int ROWB = 128;     // bytes per operand row per stage (64 K elements): whole cache lines
-constexpr int KST = ROWB / 2; // K elements per stage
-constexpr int KC = KST / 16;  // MFMA k-steps per stage
-
-// WM x WN waves, each holding WTM x WTN accumulator blocks of 32 x 32; NST LDS stages
-template <int WM_, int WN_, int WTM_, int WTN_, int NST_>
+// WM x WN waves, each holding WTM x WTN accumulator blocks of 32 x 32; NST LDS
+// stages of RB bytes per operand row (128: 64 K elements, whole cache lines;
+// 64: 32 K elements, for deeper pipelines in the same LDS)
+template <int WM_, int WN_, int WTM_, int WTN_, int NST_, int RB_ = 128>
 struct Tile {
     static constexpr int WM = WM_, WN = WN_, WTM = WTM_, WTN = WTN_, NST = NST_;
+    static constexpr int ROWB = RB_;              // bytes per operand row per stage
+    static constexpr int KST = ROWB / 2;          // K elements per stage
+    static constexpr int KC = KST / 16;           // MFMA k-steps per stage
+    static constexpr int CPR = ROWB / 16;         // 16-byte chunks per row
+    static constexpr int SWS = CPR == 8 ? 1 : 2;  // swizzle of row r: (r >> SWS) & (CPR - 1)
+    static_assert(RB_ == 128 || RB_ == 64, "row bytes per stage");
     static constexpr int NT = 64 * WM * WN;       // threads
     static constexpr int BT = 32 * WM * WTM;      // workgroup tile edge
     static_assert(BT == 32 * WN * WTN, "square tiles");
     static constexpr int OPB = BT * ROWB;         // one operand tile per stage
     static constexpr int STAGEB = 2 * OPB;
     static constexpr int LDS = NST * STAGEB;
-    static constexpr int NI = BT * (ROWB / 16) / NT;   // loads per thread per operand per stage
+    static constexpr int NI = BT * CPR / NT;      // loads per thread per operand per stage
 };
-using Big = Tile<4, 2, 2, 4, 2>;     // 256 x 256, 8 waves, 2 stages (128 KiB)
-using Small = Tile<2, 4, 2, 1, 3>;   // 128 x 128, 8 waves (each 64 x 32), 3 stages (96 KiB): one per CU
+using Big = Tile<4, 4, 2, 2, 2>;     // 256 x 256, 16 waves (each 64 x 64), 2 stages (128 KiB)
+using Small = Tile<4, 4, 1, 1, 3>;   // 128 x 128, 16 waves (each 32 x 32), 3 stages (96 KiB): one per CU
 using Small2 = Tile<2, 4, 2, 1, 2>;  // 128 x 128, 8 waves, 2 stages (64 KiB): two per CU
 using Tiny = Tile<2, 2, 1, 1, 8>;    // 64 x 64, 4 waves, 8 stages (128 KiB): seven stages in flight
 
 template <typename T, bool kRowOut, bool kHalf>
 __device__ __forceinline__ void tile_bf16(const GemmArgs& g, int m0, int n0, char* smem) {
     constexpr int WTM = T::WTM, WTN = T::WTN, NW = T::NT / 64;
+    constexpr int ROWB = T::ROWB, KST = T::KST, KC = T::KC, CPR = T::CPR;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hf = lane >> 5;
     const int wm = wave / T::WN, wn = wave % T::WN;
 
     // loader: instruction i of this wave fills the 64 chunks (i*NW+wave)*64 + lane
-    // of an operand tile: row r = chunk / 8, stored chunk chunk % 8, which holds
-    // logical chunk (chunk % 8) ^ ((r >> 1) & 7)
-    // A K of 32 (mod 64) leaves a last stage of half width: there the lanes of
-    // logical chunks 4..7 load chunk lc - 4 again (in bounds), and the B
+    // of an operand tile: row r = chunk / CPR, stored chunk chunk % CPR, which
+    // holds logical chunk (chunk % CPR) ^ ((r >> SWS) & (CPR - 1)), so that the
+    // operand reads of 16 consecutive rows fall on 16 distinct bank groups
+    // A K of KST/2 (mod KST) leaves a last stage of half width: there the lanes of
+    // the upper half of the logical chunks load chunk lc - CPR/2 again (in bounds), and the B
     // fragments of those columns are zeroed before they are multiplied, so every
     // stage issues the same load instructions
     const int nk = (g.K + KST - 1) / KST;
@@ -77,10 +85,10 @@ __device__ __forceinline__ void tile_bf16(const GemmArgs& g, int m0, int n0, cha
 #pragma unroll
     for (int i = 0; i < T::NI; ++i) {
         const int chunk = (i * NW + wave) * 64 + lane;
-        const int r = chunk >> 3, lc = (chunk & 7) ^ ((r >> 1) & 7);
+        const int r = chunk / CPR, lc = (chunk % CPR) ^ ((r >> T::SWS) & (CPR - 1));
         asrc[i] = a_row_ptr<bf16_t>(g, min(m0 + r, g.M - 1)) + lc * 8;
         bsrc[i] = b_row_ptr<bf16_t>(g, min(n0 + r, g.N - 1)) + lc * 8;
-        back[i] = lc >= 4 ? KST / 2 : 0;
+        back[i] = lc >= CPR / 2 ? KST / 2 : 0;
     }
     auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
         char* base = smem + stage * T::STAGEB;
@@ -98,8 +106,8 @@ __device__ __forceinline__ void tile_bf16(const GemmArgs& g, int m0, int n0, cha
     };
 
     // fragment rows of this lane: A rows 32 (wm*WTM + i) + l32, B rows 32 (wn*WTN + j) + l32;
-    // their swizzle (row >> 1) & 7 is (l32 >> 1) & 7
-    const int sw = (l32 >> 1) & 7;
+    // their swizzle depends on the row mod 16 only, so it is that of l32
+    const int sw = (l32 >> T::SWS) & (CPR - 1);
     const uint32_t lds0 = (uint32_t)(size_t)(__attribute__((address_space(3))) char*)smem;
     uint32_t aoff[KC], boff[KC];
 #pragma unroll
@@ -396,7 +404,7 @@ hipError_t launch_tiles(const GemmArgs* g, int count, hipStream_t s, const RowCo
     }
     if (tiles + copy_wgs == 0) return hipSuccess;
     bool half = false;
-    for (int i = 0; i < gb.count; ++i) half = half || gb.p[i].K % KST != 0;
+    for (int i = 0; i < gb.count; ++i) half = half || gb.p[i].K % T::KST != 0;
     static bool attr[2] = {false, false};
     const auto kern = half ? gemm_bf16_kernel<T, true> : gemm_bf16_kernel<T, false>;
     if (!attr[half]) {
