@@ -96,3 +96,15 @@ def test_core_backward_extra_table_rows(T):
 def test_core_backward_large(T):
     # the large workload's shape (batch 8, 16 heads, qlen = mlen = 384), all gradients
     _run(T, "bf16", 8, 16, 384, 384, -1, -1, seed=11)
+
+
+def test_core_backward_longmem(T):
+    # the long-memory workload's shape: batch 4, 8 heads, qlen 64, 1600 memory keys, clamp 1000 (the
+    # last table row takes the 600 clamped distances)
+    _run(T, "bf16", 4, 8, 64, 1600, 1000, -1, seed=13)
+
+
+def test_core_backward_segment_bias(T):
+    # a steady-state segment of the segment workload (qlen = mlen = 512) with the +-128 bias table, one
+    # batch element of 4
+    _run(T, "bf16", 1, 16, 512, 512, -1, 128, seed=17)
