@@ -1,10 +1,12 @@
 """GPU parity of the attention-core gradients (xl_rel_attn_core_bwd) against
 the fp64 oracle's, on the same seeded operands, through the C ABI.
 
-Tolerance: the GPU computes every gradient in fp32 from the exact stored
-input values (bf16 or fp32), so the differences come from fp32 rounding of
-sums over at most klen (or B*qlen) terms: each gradient tensor must agree
-elementwise within 1e-3 * |ref| + 1e-3 * max|ref|."""
+Tolerance: the GPU accumulates every gradient in fp32 from the stored input
+values (bf16 or fp32); on the bf16 path its products take fp32 operands
+(softmax terms, q + u, q + v) as a high and a low bf16 part, about 16 bits of
+mantissa, so each product carries a relative error near 2^-16 and the sums
+over at most klen (or B*qlen) terms add fp32 rounding: each gradient tensor
+must agree elementwise within 1e-3 * |ref| + 1e-3 * max|ref|."""
 import numpy as np
 import pytest
 

@@ -15,9 +15,10 @@
 // back per distance, felixzhao.cn article 118 §2.3.2).
 //
 // P and dS are materialised in the workspace ([B, H, qlen, klen] fp32 each),
-// the arithmetic is fp32 vector, every output is written by one thread (no
-// atomics). For bf16 operands with d_head 64 the work runs in 64 x 64 blocks
-// staged through LDS:
+// every output is written by one thread (no atomics). For bf16 operands with
+// d_head 64 the work runs in 64 x 64 blocks staged through LDS, the products
+// on the bf16 matrix cores with fp32 operands split into a high and a low
+// bf16 part (fp32 accumulation, about 16 bits of mantissa per operand):
 //   logits: l and dP per block of (queries, keys), with per-block softmax
 //           partials; row stats combines them into (m, 1/s, D) per row
 //   dk/dv:  rows keys, summed over queries; its loader turns l, dP into
@@ -69,16 +70,9 @@ __device__ __forceinline__ int xcd_block(int n) {
 }
 __host__ __forceinline__ unsigned xcd_grid(int64_t n) { return (unsigned)((n + 7) / 8 * 8); }
 
-// P_ij and dS_ij of a visible pair. With row statistics (the tiled path)
-// the P buffer holds the logits l and the dS buffer dP, and
-// P = exp(l - m_i) / s_i, dS = P (dP - D_i) from the row's (m, 1/s, D).
-__device__ __forceinline__ float2 pds_at(const AttnBwdArgs& a, int64_t row, int j) {
-    const int64_t o = row * a.klen + j;
-    if (!a.rstat) return make_float2(a.P[o], a.dS[o]);
-    const float* st = a.rstat + row * 3;
-    const float p = __expf(a.P[o] - st[0]) * st[1];
-    return make_float2(p, p * (a.dS[o] - st[2]));
-}
+// dS_ij of a visible pair, once final (after the row kernel of the plain
+// path, after the dk/dv kernel of the tiled path)
+__device__ __forceinline__ float ds_at(const AttnBwdArgs& a, int64_t row, int j) { return a.dS[row * a.klen + j]; }
 
 template <typename T, int DH>
 __global__ void __launch_bounds__(256) bwd_rows_kernel(AttnBwdArgs a) {
@@ -231,12 +225,12 @@ __global__ void __launch_bounds__(64 * BW) bwd_dr_kernel(AttnBwdArgs a) {
 #pragma unroll
                     for (int x = 0; x < ILP; ++x) {
                         const int64_t row = rbase + i + x;
-                        pa[x] += pds_at(a, row, a.mlen + i + x - delta).y * (ld<T>(a.q, row * DH + lane) + vd);
+                        pa[x] += ds_at(a, row, a.mlen + i + x - delta) * (ld<T>(a.q, row * DH + lane) + vd);
                     }
                 }
                 for (; i < a.qlen; ++i) {
                     const int64_t row = rbase + i;
-                    pa[0] += pds_at(a, row, a.mlen + i - delta).y * (ld<T>(a.q, row * DH + lane) + vd);
+                    pa[0] += ds_at(a, row, a.mlen + i - delta) * (ld<T>(a.q, row * DH + lane) + vd);
                 }
 #pragma unroll
                 for (int x = 0; x < ILP; ++x) acc += a.scale * pa[x];
@@ -251,21 +245,28 @@ __global__ void __launch_bounds__(64 * BW) bwd_dr_kernel(AttnBwdArgs a) {
 // ---- Logits and dP in 64 x 64 blocks (d_head 64) ----
 // A workgroup takes queries i0..i0+63 and keys j0..j0+63 of one head
 // (blocks with no visible pair exit at once); each of its 4 waves computes a
-// 32 x 32 quarter (queries wm.., keys wn..) on the fp32 matrix cores:
-//   content  qu . k      one 32 x 32 product
-//   dP       dO . v      one 32 x 32 product
-//   position qv . r      a 32 x 64 product over the 64 distances the quarter
+// 32 x 32 quarter (queries wm.., keys wn..) on the bf16 matrix cores
+// (v_mfma_f32_32x32x16_bf16, fp32 accumulation):
+//   content  qu . k      qu = s (q + u) enters as a high and a low bf16 part
+//                        (hi = bf16(qu), lo = bf16(qu - hi): 16 bits of
+//                        mantissa), k is exact: two products
+//   dP       dO . v      both exact bf16: one product
+//   position qv . r      qv split like qu, over the 64 distances the quarter
 //                        spans, n = 32 + wm - wn + (0..63) counted from
-//                        dlo = mlen + i0 - j0 - 63, then gathered through
-//                        LDS: pair (i, j) takes distance column 31 + i - j
-// Operands are staged as fp32, 16 of d_head at a time, d-contiguous per row
-// (80-byte rows: the lanes' 16-byte reads of 16 rows fall on distinct banks):
-// lane (li, half) feeds row li with d = 8*half .. 8*half + 7. The logits of
+//                        dlo = mlen + i0 - j0 - 63: four products, then
+//                        gathered through LDS: pair (i, j) takes distance
+//                        column 31 + i - j
+// Operands are staged as bf16, 32 of d_head at a time, d-contiguous per row
+// (80-byte rows: the lanes' 16-byte reads of 16 rows fall on distinct bank
+// groups); lane (li, half) feeds row li with d = 16 kk + 8 half .. + 7. V is
+// stored transposed (V^T rows by d_head) and staged by key. The logits of
 // visible pairs (plus the bias table entry) go to the P buffer, dP to the dS
 // buffer, and per row and half block of 32 keys the softmax partials (max
 // m_t, sum of exp(l - m_t), sum of exp(l - m_t) dP) to those that
 // bwd_row_stats_kernel combines.
-constexpr int DC = 16, DP = DC + 4, BDP = 64 + 4;
+constexpr int LDC = 32;              // d_head per stage
+constexpr int LRB = LDC * 2 + 16;    // bytes per staged bf16 row
+constexpr int BDP = 64 + 4;
 
 __device__ __forceinline__ void unpack8(const u32x4 w, float* f) {
 #pragma unroll
@@ -277,14 +278,11 @@ __device__ __forceinline__ void unpack8(const u32x4 w, float* f) {
 
 __global__ void __launch_bounds__(256) bwd_logits_tile_kernel(AttnBwdArgs a) {
     constexpr int DH = 64;
-    // operands: qu, qv, dO, k, v rows (64 each) and the table rows of 128 distances
-    __shared__ __attribute__((aligned(16))) float ops[5 * 64 * DP + 128 * DP];
-    float (*quS)[DP] = (float (*)[DP])(ops);
-    float (*qvS)[DP] = (float (*)[DP])(ops + 64 * DP);
-    float (*doS)[DP] = (float (*)[DP])(ops + 2 * 64 * DP);
-    float (*kS)[DP] = (float (*)[DP])(ops + 3 * 64 * DP);
-    float (*vS)[DP] = (float (*)[DP])(ops + 4 * 64 * DP);
-    float (*rS)[DP] = (float (*)[DP])(ops + 5 * 64 * DP);
+    // staged rows: qu high, qu low, qv high, qv low, dO (64 queries each), k, v
+    // (64 keys each), the table rows of 128 distances
+    constexpr int QH = 0, QL = 64, VH = 128, VL = 192, OR = 256, KR = 320, VR = 384, RR = 448, NROW = 576;
+    __shared__ __attribute__((aligned(16))) char stg[NROW * LRB];
+    float* ops = (float*)stg;   // reused by the epilogue
     const int tid = (int)__builtin_amdgcn_workitem_id_x();
     const int nit = (a.qlen + 63) / 64, njt = (a.klen + 63) / 64, nh = (a.klen + 31) / 32;
     int wg = xcd_block(a.B * a.H * nit * njt);
@@ -304,57 +302,64 @@ __global__ void __launch_bounds__(256) bwd_logits_tile_kernel(AttnBwdArgs a) {
     const bf16_t* vp = (const bf16_t*)a.vt;
     const bf16_t* rp = (const bf16_t*)a.r;
     const u32x4 z = {0u, 0u, 0u, 0u};
-    // per chunk a thread loads 16 bytes of three of: q or dO rows (by query),
-    // k rows or V^T rows (by key), and table rows (by distance)
-    const int t7 = tid & 127, row = t7 >> 1, hf = t7 & 1;
-    u32x4 f0, f1, f2, fu, fv;
+    // per stage a thread loads 16 bytes (8 of d_head) of a q, dO and k row,
+    // of u and v, 8 keys of a V^T row, and 16 bytes of two table rows
+    const int row = tid >> 2, pc = tid & 3;
+    const int vd = tid >> 3, vj = tid & 7;
+    int dist0 = dlo + row, dist1 = dlo + 64 + row;
+    dist0 = dist0 < 0 ? 0 : (dist0 > a.n_rel - 1 ? a.n_rel - 1 : dist0);
+    dist1 = dist1 < 0 ? 0 : (dist1 > a.n_rel - 1 ? a.n_rel - 1 : dist1);
+    u32x4 fq, fo, fk, fvt, fr0, fr1, fu, fv;
     auto fetch = [&](int d0) __attribute__((always_inline)) {
-        const int d = d0 + 8 * hf, i = i0 + row, j = j0 + row;
-        if (tid < 128) {
-            f0 = i < a.qlen ? *(const u32x4*)(qp + (rb + i) * DH + d) : z;
-            f1 = j < a.klen ? *(const u32x4*)(kp + ((int64_t)g * a.klen + j) * DH + d) : z;
-            fu = *(const u32x4*)((const bf16_t*)a.u + h * DH + d);
-            fv = *(const u32x4*)((const bf16_t*)a.v + h * DH + d);
-        } else {
-            f0 = i < a.qlen ? *(const u32x4*)(op + (((int64_t)b * a.qlen + i) * a.H + h) * DH + d) : z;
-            const int dd = d0 + (t7 >> 3), jj = j0 + 8 * (t7 & 7);
-            f1 = jj < a.ldv ? *(const u32x4*)(vp + ((int64_t)g * DH + dd) * a.ldv + jj) : z;
-        }
-        int dist = dlo + (tid >> 1);
-        dist = dist < 0 ? 0 : (dist > a.n_rel - 1 ? a.n_rel - 1 : dist);
-        f2 = *(const u32x4*)(rp + ((int64_t)h * a.r_rows + dist) * DH + d0 + 8 * (tid & 1));
+        const int d = d0 + 8 * pc, i = i0 + row, j = j0 + row;
+        fq = i < a.qlen ? *(const u32x4*)(qp + (rb + i) * DH + d) : z;
+        fo = i < a.qlen ? *(const u32x4*)(op + (((int64_t)b * a.qlen + i) * a.H + h) * DH + d) : z;
+        fk = j < a.klen ? *(const u32x4*)(kp + ((int64_t)g * a.klen + j) * DH + d) : z;
+        fu = *(const u32x4*)((const bf16_t*)a.u + h * DH + d);
+        fv = *(const u32x4*)((const bf16_t*)a.v + h * DH + d);
+        const int jj = j0 + 8 * vj;
+        fvt = jj < a.ldv ? *(const u32x4*)(vp + ((int64_t)g * DH + d0 + vd) * a.ldv + jj) : z;
+        fr0 = *(const u32x4*)(rp + ((int64_t)h * a.r_rows + dist0) * DH + d);
+        fr1 = *(const u32x4*)(rp + ((int64_t)h * a.r_rows + dist1) * DH + d);
+    };
+    auto put = [&](int r, const u32x4 w) __attribute__((always_inline)) {
+        *(u32x4*)(stg + r * LRB + 16 * pc) = w;
     };
     auto stash = [&]() __attribute__((always_inline)) {
-        float x[8], y[8];
-        unpack8(f0, x);
-        unpack8(f1, y);
-        if (tid < 128) {
-            float uu[8], vv[8];
-            unpack8(fu, uu);
-            unpack8(fv, vv);
-            f32x4 a0, a1, c0, c1;
+        float x[8], uu[8], vv[8];
+        unpack8(fq, x);
+        unpack8(fu, uu);
+        unpack8(fv, vv);
+        u32x4 uh, ul, wh, wl;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                a0[e] = a.scale * (x[e] + uu[e]);
-                a1[e] = a.scale * (x[e + 4] + uu[e + 4]);
-                c0[e] = a.scale * (x[e] + vv[e]);
-                c1[e] = a.scale * (x[e + 4] + vv[e + 4]);
+        for (int e = 0; e < 4; ++e) {
+            float hv[2], lv[2], hw[2], lw[2];
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const float qu = a.scale * (x[2 * e + k] + uu[2 * e + k]);
+                const float qv = a.scale * (x[2 * e + k] + vv[2 * e + k]);
+                hv[k] = bf2f(f2bf(qu));
+                lv[k] = qu - hv[k];
+                hw[k] = bf2f(f2bf(qv));
+                lw[k] = qv - hw[k];
             }
-            *(f32x4*)&quS[row][8 * hf] = a0;
-            *(f32x4*)&quS[row][8 * hf + 4] = a1;
-            *(f32x4*)&qvS[row][8 * hf] = c0;
-            *(f32x4*)&qvS[row][8 * hf + 4] = c1;
-            *(f32x4*)&kS[row][8 * hf] = (f32x4){y[0], y[1], y[2], y[3]};
-            *(f32x4*)&kS[row][8 * hf + 4] = (f32x4){y[4], y[5], y[6], y[7]};
-        } else {
-            *(f32x4*)&doS[row][8 * hf] = (f32x4){x[0], x[1], x[2], x[3]};
-            *(f32x4*)&doS[row][8 * hf + 4] = (f32x4){x[4], x[5], x[6], x[7]};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) vS[8 * (t7 & 7) + e][t7 >> 3] = y[e];   // V^T -> key rows
+            uh[e] = pack2bf(hv[0], hv[1]);
+            ul[e] = pack2bf(lv[0], lv[1]);
+            wh[e] = pack2bf(hw[0], hw[1]);
+            wl[e] = pack2bf(lw[0], lw[1]);
         }
-        unpack8(f2, y);
-        *(f32x4*)&rS[tid >> 1][8 * (tid & 1)] = (f32x4){y[0], y[1], y[2], y[3]};
-        *(f32x4*)&rS[tid >> 1][8 * (tid & 1) + 4] = (f32x4){y[4], y[5], y[6], y[7]};
+        put(QH + row, uh);
+        put(QL + row, ul);
+        put(VH + row, wh);
+        put(VL + row, wl);
+        put(OR + row, fo);
+        put(KR + row, fk);
+        put(RR + row, fr0);
+        put(RR + 64 + row, fr1);
+        // V^T -> key rows: key 8 vj + e, d_head offset vd
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            *(bf16_t*)(stg + (VR + 8 * vj + e) * LRB + 2 * vd) = (bf16_t)((fvt[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
     };
     const int lane = tid & 63, wave = tid >> 6, half = lane >> 5, li = lane & 31;
     const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
@@ -362,29 +367,30 @@ __global__ void __launch_bounds__(256) bwd_logits_tile_kernel(AttnBwdArgs a) {
     f32x16 ac, ap, ab0, ab1;
 #pragma unroll
     for (int v = 0; v < 16; ++v) ac[v] = ap[v] = ab0[v] = ab1[v] = 0.f;
+    auto rd = [&](int r, int off) __attribute__((always_inline)) {
+        return as_bf16x8(*(const u32x4*)(stg + r * LRB + off));
+    };
     fetch(0);
-    for (int d0 = 0; d0 < DH; d0 += DC) {
+    for (int d0 = 0; d0 < DH; d0 += LDC) {
         __syncthreads();
         stash();
         __syncthreads();
-        if (d0 + DC < DH) fetch(d0 + DC);
+        if (d0 + LDC < DH) fetch(d0 + LDC);
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-            const int c = 8 * half + 4 * s2;
-            const f32x4 xq = *(const f32x4*)&quS[wm + li][c];
-            const f32x4 xv = *(const f32x4*)&qvS[wm + li][c];
-            const f32x4 xo = *(const f32x4*)&doS[wm + li][c];
-            const f32x4 yk = *(const f32x4*)&kS[wn + li][c];
-            const f32x4 yv = *(const f32x4*)&vS[wn + li][c];
-            const f32x4 r0 = *(const f32x4*)&rS[nb + li][c];
-            const f32x4 r1 = *(const f32x4*)&rS[nb + 32 + li][c];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                ac = __builtin_amdgcn_mfma_f32_32x32x2f32(xq[e], yk[e], ac, 0, 0, 0);
-                ab0 = __builtin_amdgcn_mfma_f32_32x32x2f32(xv[e], r0[e], ab0, 0, 0, 0);
-                ab1 = __builtin_amdgcn_mfma_f32_32x32x2f32(xv[e], r1[e], ab1, 0, 0, 0);
-                ap = __builtin_amdgcn_mfma_f32_32x32x2f32(xo[e], yv[e], ap, 0, 0, 0);
-            }
+        for (int kk = 0; kk < LDC / 16; ++kk) {
+            const int off = 32 * kk + 16 * half;
+            const bf16x8 qh = rd(QH + wm + li, off), ql = rd(QL + wm + li, off);
+            const bf16x8 vh = rd(VH + wm + li, off), vl = rd(VL + wm + li, off);
+            const bf16x8 ov = rd(OR + wm + li, off);
+            const bf16x8 kv = rd(KR + wn + li, off), vv = rd(VR + wn + li, off);
+            const bf16x8 r0 = rd(RR + nb + li, off), r1 = rd(RR + nb + 32 + li, off);
+            ac = mfma32(qh, kv, ac);
+            ab0 = mfma32(vh, r0, ab0);
+            ab1 = mfma32(vh, r1, ab1);
+            ap = mfma32(ov, vv, ap);
+            ac = mfma32(ql, kv, ac);
+            ab0 = mfma32(vl, r0, ab0);
+            ab1 = mfma32(vl, r1, ab1);
         }
     }
     // the positional quarter through LDS (reusing the operand area, 4 x 32 x BDP floats)
@@ -495,24 +501,27 @@ __global__ void __launch_bounds__(256) bwd_row_stats_kernel(AttnBwdArgs a) {
 //   dr:    rows table rows c < n_rel - 1, t queries i of one batch element:
 //          dS_i(mlen+i-c) (q_i + v)
 // A workgroup of 4 waves computes a 64 x 64 block of one head's output, a
-// 32 x 32 quarter per wave on the fp32 matrix cores (v_mfma_f32_32x32x2_f32,
-// one or two products), and stages 32 values of t of each operand through
-// LDS as fp32, both operands t-contiguous per row (rows padded to 144 bytes):
-// lane (li, half) feeds row li with the t values 16*half .. 16*half + 15, so
-// four 16-byte LDS reads per operand serve the stage's 16 matrix
-// instructions (k of an instruction is the lane half; the two halves take
-// different t, which only reorders the sum). The next stage's operands are
-// loaded into registers while this one is computed. dr splits over the batch elements (partial sums per element,
+// 32 x 32 quarter per wave on the bf16 matrix cores (v_mfma_f32_32x32x16_bf16,
+// fp32 accumulation), and stages 32 values of t of each operand through LDS
+// as bf16, both operands t-contiguous per row (80-byte rows): lane (li, half)
+// feeds row li with t = 16 kk + 8 half .. + 7. The fp32 operands (dS, P, and
+// q + u, q + v) enter as a high and a low bf16 part (hi = bf16(x),
+// lo = bf16(x - hi): 16 bits of mantissa); key, table and dO rows are exact
+// bf16. A product of two split operands takes hi.hi + hi.lo + lo.hi (the
+// dropped lo.lo is below 2^-16 of it), one split and one exact operand two
+// instructions. The next stage's operands are loaded into registers while
+// this one is computed. dr splits over the batch elements (partial sums per element,
 // added by bwd_dr_reduce_kernel) so that its grid fills the chip.
 enum : int { TP_DKDV = 0, TP_DQ = 1, TP_DR = 2 };
-constexpr int TM = 64, TT = 32, TP = TT + 4;
+constexpr int TM = 64, TT = 32, TPB = TT * 2 + 16;   // TPB: bytes per staged bf16 row
 
 template <int MODE>
 __global__ void __launch_bounds__(256) bwd_tile_kernel(AttnBwdArgs a) {
     constexpr int DH = 64;
     constexpr int NP = MODE == TP_DR ? 1 : 2;   // products per block
-    __shared__ __attribute__((aligned(16))) float As[NP][TM][TP];
-    __shared__ __attribute__((aligned(16))) float Bs[NP][DH][TP];
+    // per product: A high and low parts (rows m), B high and low parts (rows d)
+    __shared__ __attribute__((aligned(16))) char sA[NP][2][TM * TPB];
+    __shared__ __attribute__((aligned(16))) char sB[NP][2][DH * TPB];
     const int tid = (int)__builtin_amdgcn_workitem_id_x();
     const int nrows = MODE == TP_DKDV ? a.klen : (MODE == TP_DQ ? a.qlen : a.dr_first);
     const int nmt = (nrows + TM - 1) / TM;
@@ -599,18 +608,29 @@ __global__ void __launch_bounds__(256) bwd_tile_kernel(AttnBwdArgs a) {
         for (int p = 0; p < NP; ++p) {
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                if (MODE == TP_DQ) As[p][(tid >> 5) + 8 * k][tid & 31] = ra[p][k];
-                else As[p][tid & 63][(tid >> 6) + 4 * k] = ra[p][k];
+                const int m = MODE == TP_DQ ? (tid >> 5) + 8 * k : tid & 63;
+                const int t = MODE == TP_DQ ? tid & 31 : (tid >> 6) + 4 * k;
+                const bf16_t hi = f2bf(ra[p][k]);
+                *(bf16_t*)(sA[p][0] + m * TPB + 2 * t) = hi;
+                *(bf16_t*)(sA[p][1] + m * TPB + 2 * t) = f2bf(ra[p][k] - bf2f(hi));
             }
-            // the [t x 64] operand in fp32; the first product of dk/dv and dr adds its bias vector
+            // the [t x 64] operand: the first product of dk/dv and dr adds its
+            // bias vector (then it is split); t past the range hold zeros
+            // (their A entries are zero too)
             const bool add = (MODE == TP_DKDV && p == 0) || MODE == TP_DR;
-            // t past the range hold zeros (their A entries are zero too)
+            const int t = tid >> 3;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float a0 = __uint_as_float(rbv[p][e] << 16), a1 = __uint_as_float(rbv[p][e] & 0xFFFF0000u);
-                const float b0 = add ? bias8[2 * e] : 0.f, b1 = add ? bias8[2 * e + 1] : 0.f;
-                Bs[p][8 * (tid & 7) + 2 * e][tid >> 3] = a0 + b0;
-                Bs[p][8 * (tid & 7) + 2 * e + 1][tid >> 3] = a1 + b1;
+            for (int e = 0; e < 8; ++e) {
+                const int d = 8 * (tid & 7) + e;
+                const uint32_t raw = (rbv[p][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+                if (add) {
+                    const float x = bf2f((bf16_t)raw) + bias8[e];
+                    const bf16_t hi = f2bf(x);
+                    *(bf16_t*)(sB[p][0] + d * TPB + 2 * t) = hi;
+                    *(bf16_t*)(sB[p][1] + d * TPB + 2 * t) = f2bf(x - bf2f(hi));
+                } else {
+                    *(bf16_t*)(sB[p][0] + d * TPB + 2 * t) = (bf16_t)raw;
+                }
             }
         }
     };
@@ -628,13 +648,20 @@ __global__ void __launch_bounds__(256) bwd_tile_kernel(AttnBwdArgs a) {
         __syncthreads();
         if (t0 + TT < t_hi) fetch(t0 + TT);
 #pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
+        for (int kk = 0; kk < TT / 16; ++kk) {
+            const int off = 32 * kk + 16 * half;
 #pragma unroll
             for (int p = 0; p < NP; ++p) {
-                const f32x4 x = *(const f32x4*)&As[p][wm + li][16 * half + 4 * s4];
-                const f32x4 y = *(const f32x4*)&Bs[p][wn + li][16 * half + 4 * s4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[p] = __builtin_amdgcn_mfma_f32_32x32x2f32(x[e], y[e], acc[p], 0, 0, 0);
+                const bool split_b = (MODE == TP_DKDV && p == 0) || MODE == TP_DR;
+                const bf16x8 ah = as_bf16x8(*(const u32x4*)(sA[p][0] + (wm + li) * TPB + off));
+                const bf16x8 al = as_bf16x8(*(const u32x4*)(sA[p][1] + (wm + li) * TPB + off));
+                const bf16x8 bh = as_bf16x8(*(const u32x4*)(sB[p][0] + (wn + li) * TPB + off));
+                acc[p] = mfma32(ah, bh, acc[p]);
+                acc[p] = mfma32(al, bh, acc[p]);
+                if (split_b) {
+                    const bf16x8 bl = as_bf16x8(*(const u32x4*)(sB[p][1] + (wn + li) * TPB + off));
+                    acc[p] = mfma32(ah, bl, acc[p]);
+                }
             }
         }
     }
@@ -658,7 +685,7 @@ __global__ void __launch_bounds__(256) bwd_tile_kernel(AttnBwdArgs a) {
         // du, dv: the block's column sums of the two products (rows past
         // qlen are zero): a lane's 16 rows, the other half's, then the two
         // waves of each column half added in LDS; one partial per block
-        float* red = &As[0][0][0];   // 2 products x 2 row halves x 64 floats, within As
+        float* red = (float*)&sA[0][0][0];   // 2 products x 2 row halves x 64 floats, within sA
         float cs[NP];
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
@@ -770,7 +797,7 @@ __global__ void __launch_bounds__(64) bwd_bias_kernel(AttnBwdArgs a) {
             for (int t = lane; t < n; t += 64) {
                 const int b = t / (a.qlen - i0), i = i0 + t % (a.qlen - i0);
                 const int64_t row = ((int64_t)b * a.H + h) * a.qlen + i;
-                s += pds_at(a, row, a.mlen + i - delta).y;
+                s += ds_at(a, row, a.mlen + i - delta);
             }
         }
     s = wsum(s);
