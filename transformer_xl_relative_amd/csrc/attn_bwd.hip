@@ -554,8 +554,11 @@ __global__ void __launch_bounds__(256) bwd_tile_kernel(AttnBwdArgs a) {
         for (int e = 0; e < 8; ++e) bias8[e] = (MODE == TP_DQ) ? 0.f : bf2f(bv[e]);
     }
     float ra[NP][8];
+    float rs[MODE == TP_DKDV ? 8 : 1][3];   // dk/dv: the row statistics of the fetched pairs
     u32x4 rbv[NP];
+    int ft0 = 0;                            // first t of the fetched stage
     auto fetch = [&](int t0) __attribute__((always_inline)) {
+        ft0 = t0;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             int m, t;
@@ -568,16 +571,21 @@ __global__ void __launch_bounds__(256) bwd_tile_kernel(AttnBwdArgs a) {
             }
             float x0 = 0.f, x1 = 0.f;
             if (MODE == TP_DKDV) {
-                // P, dS from l, dP and the row's statistics; this block is the
-                // only reader of the pair, so it leaves dS final in place (the
-                // kernels after it read dS only)
+                // l, dP and the row's statistics, raw: stash() turns them into
+                // P and dS once this stage's products have been issued
+                float s0 = 0.f, s1 = 0.f, s2 = 0.f;
                 if (m < a.klen && t < a.qlen && m <= a.mlen + t) {
                     const int64_t o = (rb + t) * a.klen + m;
                     const float* st = a.rstat + (rb + t) * 3;
-                    x1 = __expf(a.P[o] - st[0]) * st[1];
-                    x0 = x1 * (a.dS[o] - st[2]);
-                    a.dS[o] = x0;
+                    x0 = a.P[o];
+                    x1 = a.dS[o];
+                    s0 = st[0];
+                    s1 = st[1];
+                    s2 = st[2];
                 }
+                rs[k][0] = s0;
+                rs[k][1] = s1;
+                rs[k][2] = s2;
             } else if (MODE == TP_DQ) {   // dS is final by now
                 if (m < a.qlen && t <= a.mlen + m) {
                     const int64_t o = (rb + m) * a.klen;
@@ -604,6 +612,23 @@ __global__ void __launch_bounds__(256) bwd_tile_kernel(AttnBwdArgs a) {
         }
     };
     auto stash = [&]() __attribute__((always_inline)) {
+        if (MODE == TP_DKDV) {
+            // P = exp(l - m) / s, dS = P (dP - D); this block is the only
+            // reader of the pair, so it leaves dS final in place (the kernels
+            // after it read dS only)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int m = m0 + (tid & 63), t = ft0 + (tid >> 6) + 4 * k;
+                float pv = 0.f, dv = 0.f;
+                if (m < a.klen && t < a.qlen && m <= a.mlen + t) {
+                    pv = __expf(ra[0][k] - rs[k][0]) * rs[k][1];
+                    dv = pv * (ra[NP - 1][k] - rs[k][2]);
+                    a.dS[(rb + t) * a.klen + m] = dv;
+                }
+                ra[0][k] = dv;
+                ra[NP - 1][k] = pv;
+            }
+        }
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
 #pragma unroll
