@@ -277,7 +277,9 @@ int xl_segment_step_kv(const xl_attn_desc* desc, const xl_attn_weights* w, const
  * dk, dv [B, H, klen, d_head], dr [H, n_rel, d_head], du, dv_bias
  * [H, d_head], dbias like bias_table (needed when desc->bias_clamp >= 0).
  * The memory keys receive gradients like any key; a caller that detaches the
- * memory drops those rows. A plain form: fp32 vector arithmetic, P and dS
+ * memory drops those rows. Gradients accumulate in fp32 (for bf16 operands
+ * the products run on the bf16 matrix cores with fp32 operands split into a
+ * high and a low bf16 part, about 16 bits of mantissa), P and dS are
  * materialised in the workspace (xl_rel_attn_core_bwd_workspace_size():
  * 8 bytes per (query, key) pair, 8 per query element, 4 per element of
  * batch x n_head x (table rows in use - 1) x d_head for per-batch-element

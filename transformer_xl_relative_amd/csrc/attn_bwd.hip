@@ -471,24 +471,38 @@ __global__ void __launch_bounds__(256) bwd_logits_tile_kernel(AttnBwdArgs a) {
 
 // per query row: m = max of the half blocks' maxima, s = sum of their exp
 // sums rescaled to m, D = (rescaled sum of exp(l - m_t) dP) / s; stored
-// (m, 1/s, D)
+// (m, 1/s, D). RSL lanes share a row: lane x takes half blocks x, x + RSL,
+// ..., and the lanes' (m, s, e) merge by rescaling to the larger maximum.
+constexpr int RSL = 8;
+
+__device__ __forceinline__ void merge_stats(float& m, float& s, float& e, float m2, float s2, float e2) {
+    const float mx = fmaxf(m, m2);
+    if (mx == -INFINITY) return;   // both empty
+    const float w1 = __expf(m - mx), w2 = __expf(m2 - mx);
+    s = s * w1 + s2 * w2;
+    e = e * w1 + e2 * w2;
+    m = mx;
+}
+
 __global__ void __launch_bounds__(256) bwd_row_stats_kernel(AttnBwdArgs a) {
-    const int64_t row = (int64_t)__builtin_amdgcn_workgroup_id_x() * 256 + (int)__builtin_amdgcn_workitem_id_x();
-    if (row >= (int64_t)a.B * a.H * a.qlen) return;
-    const int i = (int)(row % a.qlen);
-    const int nh = (a.klen + 31) / 32, nt = (a.mlen + i) / 32 + 1;
-    const float* pt = a.rpart + row * nh * 3;
-    float m = -INFINITY;
-    for (int t = 0; t < nt; ++t) m = fmaxf(m, pt[3 * t]);
-    float s = 0.f, e = 0.f;
-    for (int t = 0; t < nt; ++t) {
-        const float w = __expf(pt[3 * t] - m);
-        s += pt[3 * t + 1] * w;
-        e += pt[3 * t + 2] * w;
+    const int64_t idx = (int64_t)__builtin_amdgcn_workgroup_id_x() * 256 + (int)__builtin_amdgcn_workitem_id_x();
+    const int64_t row = idx / RSL;
+    const int x = (int)(idx % RSL);
+    const int64_t rows = (int64_t)a.B * a.H * a.qlen;
+    const bool live = row < rows;   // every lane takes part in the shuffles
+    const int i = live ? (int)(row % a.qlen) : 0;
+    const int nh = (a.klen + 31) / 32, nt = live ? (a.mlen + i) / 32 + 1 : 0;
+    const float* pt = a.rpart + (live ? row : 0) * nh * 3;
+    float m = -INFINITY, s = 0.f, e = 0.f;
+    for (int t = x; t < nt; t += RSL) merge_stats(m, s, e, pt[3 * t], pt[3 * t + 1], pt[3 * t + 2]);
+#pragma unroll
+    for (int o = 1; o < RSL; o <<= 1)
+        merge_stats(m, s, e, __shfl_xor(m, o, 64), __shfl_xor(s, o, 64), __shfl_xor(e, o, 64));
+    if (live && x == 0) {
+        a.rstat[row * 3] = m;
+        a.rstat[row * 3 + 1] = 1.f / s;
+        a.rstat[row * 3 + 2] = e / s;
     }
-    a.rstat[row * 3] = m;
-    a.rstat[row * 3 + 1] = 1.f / s;
-    a.rstat[row * 3 + 2] = e / s;
 }
 
 // ---- Tiled products for d_head 64 ----
@@ -837,7 +851,7 @@ hipError_t launch_t(const AttnBwdArgs& a, hipStream_t s) {
     if constexpr (DH == 64) {
         const int64_t nblk = (int64_t)a.B * a.H * ((a.qlen + 63) / 64) * ((a.klen + 63) / 64);
         hipLaunchKernelGGL(bwd_logits_tile_kernel, dim3(xcd_grid(nblk)), dim3(256), 0, s, a);
-        hipLaunchKernelGGL(bwd_row_stats_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(bwd_row_stats_kernel, dim3((unsigned)((rows * RSL + 255) / 256)), dim3(256), 0, s, a);
     } else {
         hipLaunchKernelGGL((bwd_rows_kernel<T, DH>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
     }
