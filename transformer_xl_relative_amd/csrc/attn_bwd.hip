@@ -276,7 +276,9 @@ __device__ __forceinline__ void unpack8(const u32x4 w, float* f) {
     }
 }
 
-__global__ void __launch_bounds__(256) bwd_logits_tile_kernel(AttnBwdArgs a) {
+// (three workgroups per compute unit: the registers fit 3 waves per SIMD
+// without spilling, and the LDS 3 x 45 KB)
+__global__ void __launch_bounds__(256, 3) bwd_logits_tile_kernel(AttnBwdArgs a) {
     constexpr int DH = 64;
     // staged rows: qu high, qu low, qv high, qv low, dO (64 queries each), k, v
     // (64 keys each), the table rows of 128 distances
@@ -529,8 +531,9 @@ __global__ void __launch_bounds__(256) bwd_row_stats_kernel(AttnBwdArgs a) {
 enum : int { TP_DKDV = 0, TP_DQ = 1, TP_DR = 2 };
 constexpr int TM = 64, TT = 32, TPB = TT * 2 + 16;   // TPB: bytes per staged bf16 row
 
+// (dq fits 4 waves per SIMD without spilling; dk/dv would spill)
 template <int MODE>
-__global__ void __launch_bounds__(256) bwd_tile_kernel(AttnBwdArgs a) {
+__global__ void __launch_bounds__(256, MODE == TP_DQ ? 4 : 1) bwd_tile_kernel(AttnBwdArgs a) {
     constexpr int DH = 64;
     constexpr int NP = MODE == TP_DR ? 1 : 2;   // products per block
     // per product: A high and low parts (rows m), B high and low parts (rows d)
