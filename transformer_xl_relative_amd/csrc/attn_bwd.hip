@@ -307,7 +307,9 @@ __global__ void __launch_bounds__(256, 3) bwd_logits_tile_kernel(AttnBwdArgs a) 
     // per stage a thread loads 16 bytes (8 of d_head) of a q, dO and k row,
     // of u and v, 8 keys of a V^T row, and 16 bytes of two table rows
     const int row = tid >> 2, pc = tid & 3;
-    const int vd = tid >> 3, vj = tid & 7;
+    // V^T: lane d of 32 rows, 8 keys each; consecutive lanes then write
+    // consecutive bytes of a key row when V is staged by key
+    const int vd = tid & 31, vj = tid >> 5;
     int dist0 = dlo + row, dist1 = dlo + 64 + row;
     dist0 = dist0 < 0 ? 0 : (dist0 > a.n_rel - 1 ? a.n_rel - 1 : dist0);
     dist1 = dist1 < 0 ? 0 : (dist1 > a.n_rel - 1 ? a.n_rel - 1 : dist1);
@@ -565,7 +567,7 @@ __global__ void __launch_bounds__(256, MODE == TP_DQ ? 4 : 1) bwd_tile_kernel(At
     // the stage operands of this thread
     float bias8[8];
     {
-        const int d8 = tid & 7;
+        const int d8 = tid >> 5;
         const bf16_t* bv = (const bf16_t*)(MODE == TP_DKDV ? a.u : a.v) + h * DH + 8 * d8;
 #pragma unroll
         for (int e = 0; e < 8; ++e) bias8[e] = (MODE == TP_DQ) ? 0.f : bf2f(bv[e]);
@@ -583,8 +585,8 @@ __global__ void __launch_bounds__(256, MODE == TP_DQ ? 4 : 1) bwd_tile_kernel(At
                 t = t0 + (tid & 31);
                 m = m0 + (tid >> 5) + 8 * k;
             } else {
-                m = m0 + (tid & 63);
-                t = t0 + (tid >> 6) + 4 * k;
+                m = m0 + (tid & 63);   // lanes along m: coalesced rows of dS and P
+                t = t0 + 8 * (tid >> 6) + k;   // 8 consecutive t per lane: one 16-byte LDS write
             }
             float x0 = 0.f, x1 = 0.f;
             if (MODE == TP_DKDV) {
@@ -615,7 +617,10 @@ __global__ void __launch_bounds__(256, MODE == TP_DQ ? 4 : 1) bwd_tile_kernel(At
             ra[0][k] = x0;
             if (NP > 1) ra[NP - 1][k] = x1;
         }
-        const int t = t0 + (tid >> 3), c = 8 * (tid & 7);
+        // the [t x 64] rows: lane t of 32 consecutive rows, 8 columns per lane;
+        // each wave covers 32 rows x 16 columns, so that its transposed 2-byte
+        // LDS writes (rows by column, t-contiguous) fall on 32 distinct banks
+        const int t = t0 + (tid & 31), c = 8 * (tid >> 5);
         const u32x4 z = {0u, 0u, 0u, 0u};
         if (MODE == TP_DKDV) {
             rbv[0] = t < a.qlen ? *(const u32x4*)((const bf16_t*)a.q + (rb + t) * DH + c) : z;
@@ -635,7 +640,7 @@ __global__ void __launch_bounds__(256, MODE == TP_DQ ? 4 : 1) bwd_tile_kernel(At
             // after it read dS only)
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                const int m = m0 + (tid & 63), t = ft0 + (tid >> 6) + 4 * k;
+                const int m = m0 + (tid & 63), t = ft0 + 8 * (tid >> 6) + k;
                 float pv = 0.f, dv = 0.f;
                 if (m < a.klen && t < a.qlen && m <= a.mlen + t) {
                     pv = __expf(ra[0][k] - rs[k][0]) * rs[k][1];
@@ -648,22 +653,36 @@ __global__ void __launch_bounds__(256, MODE == TP_DQ ? 4 : 1) bwd_tile_kernel(At
         }
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
+            if (MODE == TP_DQ) {
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int m = MODE == TP_DQ ? (tid >> 5) + 8 * k : tid & 63;
-                const int t = MODE == TP_DQ ? tid & 31 : (tid >> 6) + 4 * k;
-                const bf16_t hi = f2bf(ra[p][k]);
-                *(bf16_t*)(sA[p][0] + m * TPB + 2 * t) = hi;
-                *(bf16_t*)(sA[p][1] + m * TPB + 2 * t) = f2bf(ra[p][k] - bf2f(hi));
+                for (int k = 0; k < 8; ++k) {
+                    const int m = (tid >> 5) + 8 * k, t = tid & 31;
+                    const bf16_t hi = f2bf(ra[p][k]);
+                    *(bf16_t*)(sA[p][0] + m * TPB + 2 * t) = hi;
+                    *(bf16_t*)(sA[p][1] + m * TPB + 2 * t) = f2bf(ra[p][k] - bf2f(hi));
+                }
+            } else {
+                // row m, t = 8 (tid / 64) .. + 7: high and low parts, 16 bytes each
+                u32x4 wh, wl;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float x0 = ra[p][2 * e], x1 = ra[p][2 * e + 1];
+                    const bf16_t h0 = f2bf(x0), h1 = f2bf(x1);
+                    wh[e] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+                    wl[e] = pack2bf(x0 - bf2f(h0), x1 - bf2f(h1));
+                }
+                const int off = (tid & 63) * TPB + 16 * (tid >> 6);
+                *(u32x4*)(sA[p][0] + off) = wh;
+                *(u32x4*)(sA[p][1] + off) = wl;
             }
             // the [t x 64] operand: the first product of dk/dv and dr adds its
             // bias vector (then it is split); t past the range hold zeros
             // (their A entries are zero too)
             const bool add = (MODE == TP_DKDV && p == 0) || MODE == TP_DR;
-            const int t = tid >> 3;
+            const int t = tid & 31;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int d = 8 * (tid & 7) + e;
+                const int d = 8 * (tid >> 5) + e;
                 const uint32_t raw = (rbv[p][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
                 if (add) {
                     const float x = bf2f((bf16_t)raw) + bias8[e];
