@@ -572,6 +572,7 @@ __global__ void __launch_bounds__(256, MODE == TP_DQ ? 4 : 1) bwd_tile_kernel(At
 #pragma unroll
         for (int e = 0; e < 8; ++e) bias8[e] = (MODE == TP_DQ) ? 0.f : bf2f(bv[e]);
     }
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
     float ra[NP][8];
     float rs[MODE == TP_DKDV ? 8 : 1][3];   // dk/dv: the row statistics of the fetched pairs
     u32x4 rbv[NP];
@@ -586,21 +587,25 @@ __global__ void __launch_bounds__(256, MODE == TP_DQ ? 4 : 1) bwd_tile_kernel(At
                 m = m0 + (tid >> 5) + 8 * k;
             } else {
                 m = m0 + (tid & 63);   // lanes along m: coalesced rows of dS and P
-                t = t0 + 8 * (tid >> 6) + k;   // 8 consecutive t per lane: one 16-byte LDS write
+                t = t0 + 8 * wv + k;   // 8 consecutive t per lane: one 16-byte LDS write
             }
             float x0 = 0.f, x1 = 0.f;
             if (MODE == TP_DKDV) {
                 // l, dP and the row's statistics, raw: stash() turns them into
                 // P and dS once this stage's products have been issued
+                // (t is uniform across the wave, so the statistics come
+                // through scalar loads)
                 float s0 = 0.f, s1 = 0.f, s2 = 0.f;
-                if (m < a.klen && t < a.qlen && m <= a.mlen + t) {
-                    const int64_t o = (rb + t) * a.klen + m;
+                if (t < a.qlen) {
                     const float* st = a.rstat + (rb + t) * 3;
-                    x0 = a.P[o];
-                    x1 = a.dS[o];
                     s0 = st[0];
                     s1 = st[1];
                     s2 = st[2];
+                }
+                if (m < a.klen && t < a.qlen && m <= a.mlen + t) {
+                    const int64_t o = (rb + t) * a.klen + m;
+                    x0 = a.P[o];
+                    x1 = a.dS[o];
                 }
                 rs[k][0] = s0;
                 rs[k][1] = s1;
@@ -640,7 +645,7 @@ __global__ void __launch_bounds__(256, MODE == TP_DQ ? 4 : 1) bwd_tile_kernel(At
             // after it read dS only)
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                const int m = m0 + (tid & 63), t = ft0 + 8 * (tid >> 6) + k;
+                const int m = m0 + (tid & 63), t = ft0 + 8 * wv + k;
                 float pv = 0.f, dv = 0.f;
                 if (m < a.klen && t < a.qlen && m <= a.mlen + t) {
                     pv = __expf(ra[0][k] - rs[k][0]) * rs[k][1];
