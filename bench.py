@@ -64,8 +64,8 @@ ATTN_SOURCES = ("transformer_xl_relative_amd/csrc/attn_bf16.hip", "transformer_x
 # HBM bytes per launch of the fused attention kernel (calibrated FETCH_SIZE and
 # WRITE_SIZE, see profiles/attn_bf16_kernel_<workload>_pmc_traffic.md).
 TRAFFIC = {
-    "large_bf16": {"sha256": "97b5d1ad7228aa9eb7c61e0b58a8d6bc21a764cfb6612c5182e092db73d1a83f",
-                   "bytes": 39646676, "fetch_bytes": 33355220, "write_bytes": 6291456},
+    "large_bf16": {"sha256": "9a742cf0b3e2f9398edb801d6e7840e0877b230d721547c699a472f7ebf0cd86",
+                   "bytes": 39651587, "fetch_bytes": 33360131, "write_bytes": 6291456},
 }
 
 
