@@ -45,13 +45,13 @@ def _run_layer(T, w, t, *, batch, qlen, mlen, d_inner):
     return gu.host64(out)
 
 
-# (the last two: rows longer than the layer norm keeps in registers)
-@pytest.mark.parametrize("base,qlen,mlen,d_inner,bias,wide", [
-    ("base_bf16", 70, 45, 256, -1, 0), ("base_bf16", 128, 0, 512, -1, 0), ("base_bf16", 37, 91, 96, 16, 0),
-    ("tiny_f32", 9, 13, 32, -1, 0), ("tiny_f32", 8, 8, 64, 3, 0), ("base_bf16", 20, 12, 64, -1, 2560),
-    ("tiny_f32", 6, 5, 32, -1, 1040)])
-def test_decoder_layer(T, base, qlen, mlen, d_inner, bias, wide):
-    w = dataclasses.replace(W[base], bias_clamp=bias, seed=qlen * 7 + mlen)
+# (the last two: rows longer than the layer norm keeps in registers; kind 1: the T5 log-bucket table)
+@pytest.mark.parametrize("base,qlen,mlen,d_inner,bias,wide,kind", [
+    ("base_bf16", 70, 45, 256, -1, 0, 0), ("base_bf16", 128, 0, 512, -1, 0, 0), ("base_bf16", 37, 91, 96, 16, 0, 0),
+    ("tiny_f32", 9, 13, 32, -1, 0, 0), ("tiny_f32", 8, 8, 64, 3, 0, 0), ("base_bf16", 20, 12, 64, -1, 2560, 0),
+    ("tiny_f32", 6, 5, 32, -1, 1040, 0), ("base_bf16", 48, 1100, 128, 0, 0, 1), ("tiny_f32", 7, 40, 32, 0, 0, 1)])
+def test_decoder_layer(T, base, qlen, mlen, d_inner, bias, wide, kind):
+    w = dataclasses.replace(W[base], bias_clamp=bias, bias_kind=kind, seed=qlen * 7 + mlen)
     if wide:
         w = dataclasses.replace(w, d_model=wide, n_head=2)
     t = xl_inputs.decoder_inputs(w, d_inner=d_inner, n_layer=1, batch=2, qlen=qlen, mlen=mlen)
