@@ -79,6 +79,7 @@ BWD = [
     ("bf16", 1, 1, 1, 0, -1, -1, 0),           # a single key
     ("f32", 2, 2, 20, 11, 7, -1, 0),
     ("f32", 1, 2, 9, 4, -1, 3, 0),
+    ("f32", 2, 2, 11, 40, -1, 0, 1),           # fp32 path with the T5 buckets
     ("bf16", 3, 2, 13, 60, 20, 5, 0),          # query blocks of 8 with a ragged last block
     ("bf16", 1, 1, 70, 1, -1, -1, 0),          # key chunks of 64 with a ragged last chunk
 ]
