@@ -95,17 +95,21 @@ def _stack_run(T, w, t, *, batch, qlen, n_seg, mlen_max, d_inner, n_layer, head0
     return outs, mems
 
 
-@pytest.mark.parametrize("base,qlen,n_seg,mlen_max,d_inner,n_layer,head0",
-                         [("base_bf16", 64, 4, 96, 256, 3, 0), ("base_bf16", 40, 3, 100, 128, 2, 37),
-                          ("tiny_f32", 8, 4, 12, 32, 3, 5)])
-def test_decoder_stack_run(T, base, qlen, n_seg, mlen_max, d_inner, n_layer, head0):
-    w = dataclasses.replace(W[base], segments=n_seg, qlen=qlen, mlen=mlen_max, seed=n_layer * 10 + qlen)
+# (bias, kind: the scalar bias table, clamped (0) or T5 buckets (1); -1: none)
+@pytest.mark.parametrize("base,qlen,n_seg,mlen_max,d_inner,n_layer,head0,bias,kind",
+                         [("base_bf16", 64, 4, 96, 256, 3, 0, -1, 0), ("base_bf16", 40, 3, 100, 128, 2, 37, -1, 0),
+                          ("tiny_f32", 8, 4, 12, 32, 3, 5, -1, 0), ("base_bf16", 32, 3, 80, 128, 2, 11, 8, 0),
+                          ("tiny_f32", 8, 4, 12, 32, 2, 3, 0, 1)])
+def test_decoder_stack_run(T, base, qlen, n_seg, mlen_max, d_inner, n_layer, head0, bias, kind):
+    w = dataclasses.replace(W[base], segments=n_seg, qlen=qlen, mlen=mlen_max, seed=n_layer * 10 + qlen,
+                            bias_clamp=bias, bias_kind=kind)
     t = xl_inputs.decoder_inputs(w, d_inner=d_inner, n_layer=n_layer, batch=2, qlen=qlen)
     outs, mems = _stack_run(T, w, t, batch=2, qlen=qlen, n_seg=n_seg, mlen_max=mlen_max, d_inner=d_inner,
                             n_layer=n_layer, head0=head0)
     routs, rmems = oracle.decoder_stack_run(t["h"].f64, n_seg, qlen, mlen_max,
                                             [gu.oracle_dec_weights(lw) for lw in t["layers"]], n_head=w.n_head,
-                                            d_head=w.d_head, clamp_len=w.clamp_len)
+                                            d_head=w.d_head, clamp_len=w.clamp_len, bias_clamp=w.bias_clamp,
+                                            bias_kind=w.bias_kind)
     for s in range(n_seg):
         gu.compare(f"stack segment {s}", outs[s], routs[s], dtype=w.dtype)
         # layer 0 keeps the input stream itself: bit for bit
