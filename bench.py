@@ -7,14 +7,17 @@ output projection and the FIFO memory update, on synthetic seeded inputs that
 are resident in HBM before the timed region starts. The memory FIFO is full,
 so every step attends over 384 memory rows + 384 segment rows.
 
-Prints one JSON line: the layer's algorithmic TFLOP/s (value, from K timed
-steps), the fused attention kernel's roofline (kernel time from HIP events
-that the runtime timestamps at the kernel's own start and end, over K further
-steps, so that the events do not perturb the timed ones), and the
-CPU oracle timed on a bounded sample of the same workload. The roofline bound
-is the one the kernel's arithmetic intensity (algorithmic FLOPs over minimum
-HBM bytes) selects: HBM below the ridge point 2500 TFLOP/s / 8 TB/s, MFMA
-above it; the fraction of the bf16 MFMA peak is reported beside it.
+Prints one JSON line. value is the metric: the fused relative attention's
+algorithmic TFLOP/s (6 d_head flops per visible query-key pair) over that
+kernel's own time, from HIP events that the runtime timestamps at the
+kernel's start and end, over K further steps so that the events do not
+perturb the timed ones (the merge of key splits is inside the bracket when
+the keys are split). ms_per_step is the whole step's time over the K timed
+steps, and layer_tflops the layer's algorithmic rate over it. The roofline
+object is the fused attention's against the bf16 MFMA peak (the metric's
+denominator), with its HBM rate and fraction beside it; cpu_baseline is the
+oracle's attention core on a bounded sample of the same workload (the same
+flop count), cpu_baseline_layer the oracle's whole layer.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
                   [--copy-calib-mib M]        # also run a plain device copy of M MiB (counter calibration)
@@ -102,18 +105,34 @@ def attn_min_bytes(w, mlen):
     return es * (B * H * q * dh + 2 * B * H * klen * dh + H * n_rel * dh + B * q * H * dh)
 
 
-def roofline(flops, nbytes, seconds):
-    """Bound, achieved rate and fraction for one kernel time."""
+def host_cpu_model():
+    """The host CPU's model name (lscpu's 'Model name', from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def roofline(flops, nbytes, seconds, bound=None):
+    """Bound, achieved rate and fraction for one kernel time. The bound is
+    chosen by arithmetic intensity against the ridge point unless given."""
     ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
     tf = flops / seconds / 1e12
     gbs = nbytes / seconds / 1e9
-    if flops / nbytes < ridge:
+    if bound is None:
+        bound = "hbm" if flops / nbytes < ridge else "mfma"
+    if bound == "hbm":
         return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(gbs / HBM_PEAK_GBS, 4), "mfma_tflops": round(tf, 3),
                 "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
     return {"bound": "mfma", "achieved": round(tf, 3), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "hbm_gbs": round(gbs, 1),
-            "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+            "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "mfma_tflops": round(tf, 3),
+            "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "hbm_gbs": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def cpu_baseline(w, t, min_seconds=10.0):
@@ -135,7 +154,7 @@ def cpu_baseline(w, t, min_seconds=10.0):
     flops, _ = layer_flops(w, w.mlen)
     per_elem = flops / w.batch
     return {"value": round(per_elem * n / el / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": host_cpu_model(),
             "sample": f"{n} full-layer forwards of one batch element (of {w.batch}) of {w.name}, "
                       f"fp64, {el:.1f} s wall"}
 
@@ -167,7 +186,7 @@ def cpu_baseline_core(w, t, min_seconds=10.0):
             break
     flops = 6.0 * dh * H * w.n_valid_pairs()
     return {"value": round(flops * n / el / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": host_cpu_model(),
             "sample": f"{n} attention cores (four explicit dots per pair, softmax, P.V) of one batch element "
                       f"(of {w.batch}) of {w.name}, fp64, {el:.1f} s wall"}
 
@@ -296,7 +315,11 @@ def main():
     assert (kv.len if args.kv_ring else fifo.len) == w.mlen
 
     flops, attn_flops = layer_flops(w, w.mlen, args.kv_ring)
-    value = flops / (ms_per_step * 1e-3) / 1e12
+    # the metric: the fused relative attention's algorithmic TFLOP/s over its
+    # own kernel time (the merge of key splits included); the whole step's
+    # rate is reported beside it as layer_tflops
+    value = attn_flops / (core_avg_ms * 1e-3) / 1e12
+    layer_tflops = flops / (ms_per_step * 1e-3) / 1e12
     rec = TRAFFIC.get(w.name)
     traffic = rec["bytes"] if rec is not None and rec["sha256"] == attn_sources_sha() else None
     res = {
@@ -323,19 +346,21 @@ def main():
                    "batch": w.batch, "qlen": w.qlen, "mlen": w.mlen, "d_model": D, "n_head": w.n_head,
                    "d_head": w.d_head, "clamp_len": w.clamp_len, "bias_clamp": w.bias_clamp},
         "roofline": {"kernel": "attn_bf16_kernel (fused relative attention)",
-                     **roofline(attn_flops, attn_min_bytes(w, w.mlen), core_avg_ms * 1e-3), "traffic": traffic,
+                     **roofline(attn_flops, attn_min_bytes(w, w.mlen), core_avg_ms * 1e-3, bound="mfma"),
+                     "traffic": traffic,
                      "algorithmic_flops": attn_flops, "algorithmic_bytes": attn_min_bytes(w, w.mlen),
                      "avg_kernel_us": round(core_avg_ms * 1e3, 3)},
+        "layer_tflops": round(layer_tflops, 3),
         "layer_flops_per_step": flops,
         "wall_s_timed_region": round(wall, 4),
     }
     if not args.no_cpu:
-        res["cpu_baseline"] = cpu_baseline(w, t)
+        # the metric's own scope: the oracle's attention core against the fused attention
+        res["cpu_baseline"] = cpu_baseline_core(w, t)
         res["gpu_over_cpu"] = round(value / res["cpu_baseline"]["value"], 1)
-        # the fused attention alone against the oracle's core alone
-        res["cpu_baseline_core"] = cpu_baseline_core(w, t)
-        core_tflops = attn_flops / (core_avg_ms * 1e-3) / 1e12
-        res["gpu_over_cpu_core"] = round(core_tflops / res["cpu_baseline_core"]["value"], 1)
+        # and the whole layer against the step
+        res["cpu_baseline_layer"] = cpu_baseline(w, t)
+        res["gpu_over_cpu_layer"] = round(layer_tflops / res["cpu_baseline_layer"]["value"], 1)
     print(json.dumps(res), flush=True)
 
 

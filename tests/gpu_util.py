@@ -6,9 +6,7 @@ import numpy as np
 
 import transformer_xl_relative_amd as xl
 import xl_inputs
-
-BF16_RTOL, BF16_ATOL = 2e-2, 1e-2   # bf16 inputs, fp32 accumulation
-F32_RTOL = 1e-5                     # fp32 workload; atol = 1e-5 * max|ref|
+from tests.guards import BF16_ATOL, BF16_RTOL, F32_RTOL, tolerance  # noqa: F401  (one tolerance for all tests)
 
 
 def torch():
@@ -40,10 +38,7 @@ def compare(name, got, ref, *, dtype: str, report=None):
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
     assert np.all(np.isfinite(got)), f"{name}: non-finite values in the GPU result"
-    if dtype == "bf16":
-        rtol, atol = BF16_RTOL, BF16_ATOL
-    else:
-        rtol, atol = F32_RTOL, F32_RTOL * max(float(np.max(np.abs(ref))), 1e-30)
+    rtol, atol = tolerance(ref, dtype)
     err = np.abs(got - ref)
     bad = err > atol + rtol * np.abs(ref)
     rel = err / np.maximum(np.abs(ref), atol)

@@ -16,6 +16,9 @@ Workloads (value recipe, applied to every one):
 Draws are float32 from numpy.random.default_rng(seed) in the order
 h, mem, W_q, W_k, W_v, W_r, W_o, u, v, beta; bf16 workloads round every draw
 once to bfloat16 (round to nearest even) and both sides consume those bits.
+A second recipe ("sensitive", see RECIPES) draws the same shapes in the same
+order with larger parameter scales, for parity tests that must see every
+term of the score in the layer output.
 """
 from __future__ import annotations
 
@@ -104,13 +107,33 @@ def bias_rows(bias_clamp: int, bias_kind: int) -> int:
     return 12 if bias_kind == 1 else 2 * bias_clamp + 1
 
 
+# Standard deviations of the drawn parameters. "config" is the workloads' own
+# recipe. "sensitive" is a second recipe for parity tests of the composed
+# layer: projections N(0, 1/fan_in) (so that projected queries, keys, values
+# and table rows are of unit size), u and v N(0, 0.5), the bias table N(0, 1).
+# Under it every term of the score moves the layer output by much more than
+# the bf16 tolerance, which the config recipe's tiny weights do not.
+RECIPES = ("config", "sensitive")
+
+
+def _std(recipe: str, name: str, fan_in: int) -> float:
+    if recipe == "config":
+        return 0.02
+    if recipe == "sensitive":
+        if name in ("w_q", "w_k", "w_v", "w_r", "w_o"):
+            return float(1.0 / np.sqrt(fan_in))
+        return {"u": 0.5, "v": 0.5, "beta": 1.0}[name]
+    raise ValueError(recipe)
+
+
 def layer_inputs(w: Workload, *, batch: int | None = None, qlen: int | None = None,
-                 mlen: int | None = None, seed: int | None = None) -> dict:
+                 mlen: int | None = None, seed: int | None = None, recipe: str = "config") -> dict:
     """Draw one layer call's inputs. Sizes default to the workload's.
 
     For a segment-recurrent workload, 'h' is the whole input stream
     [batch, segments*qlen, d_model] and 'mem' is empty (the run starts with
-    no memory).
+    no memory). recipe selects the parameter scales (RECIPES); the draw order
+    is the same for both.
     """
     B = w.batch if batch is None else batch
     q = w.qlen if qlen is None else qlen
@@ -124,28 +147,30 @@ def layer_inputs(w: Workload, *, batch: int | None = None, qlen: int | None = No
     else:
         h = _normal(rng, (B, q, D), 1.0)
         mem = _normal(rng, (B, m, D), 1.0)
+    sd = lambda name, fan_in=0: _std(recipe, name, fan_in)
     out = {
         "h": h, "mem": mem,
-        "w_q": _normal(rng, (HD, D), 0.02),
-        "w_k": _normal(rng, (HD, D), 0.02),
-        "w_v": _normal(rng, (HD, D), 0.02),
-        "w_r": _normal(rng, (HD, D), 0.02),
-        "w_o": _normal(rng, (D, HD), 0.02),
-        "u": _normal(rng, (w.n_head, w.d_head), 0.02),
-        "v": _normal(rng, (w.n_head, w.d_head), 0.02),
+        "w_q": _normal(rng, (HD, D), sd("w_q", D)),
+        "w_k": _normal(rng, (HD, D), sd("w_k", D)),
+        "w_v": _normal(rng, (HD, D), sd("w_v", D)),
+        "w_r": _normal(rng, (HD, D), sd("w_r", D)),
+        "w_o": _normal(rng, (D, HD), sd("w_o", HD)),
+        "u": _normal(rng, (w.n_head, w.d_head), sd("u")),
+        "v": _normal(rng, (w.n_head, w.d_head), sd("v")),
     }
     if w.bias_clamp >= 0:
-        out["beta"] = _normal(rng, (bias_rows(w.bias_clamp, w.bias_kind), w.n_head), 0.02)
+        out["beta"] = _normal(rng, (bias_rows(w.bias_clamp, w.bias_kind), w.n_head), sd("beta"))
     return {k: Tensor(a, w.dtype) for k, a in out.items()}
 
 
 def decoder_inputs(w: Workload, *, d_inner: int, n_layer: int, batch: int | None = None, qlen: int | None = None,
-                   mlen: int | None = None, seed: int | None = None) -> dict:
+                   mlen: int | None = None, seed: int | None = None, recipe: str = "config") -> dict:
     """Inputs of a decoder stack: 'h' (or the whole stream of a
     segment-recurrent workload) and 'mem' as layer_inputs draws them, then per
     layer, in order, the attention weights (the same recipe as layer_inputs),
     LN1 gain 1 + N(0, 0.02) and shift N(0, 0.02), the same for LN2, W1
     [d_inner, D], b1 [d_inner], W2 [D, d_inner], b2 [D], all N(0, 0.02).
+    recipe scales the attention weights as layer_inputs does (RECIPES).
     Returns {'h', 'mem', 'layers': [dict per layer]}."""
     B = w.batch if batch is None else batch
     q = w.qlen if qlen is None else qlen
@@ -160,14 +185,15 @@ def decoder_inputs(w: Workload, *, d_inner: int, n_layer: int, batch: int | None
         mem = _normal(rng, (B, m, D), 1.0)
     layers = []
     for _ in range(n_layer):
+        sd = lambda name, fan_in=0: _std(recipe, name, fan_in)
         lw = {
-            "w_q": _normal(rng, (HD, D), 0.02), "w_k": _normal(rng, (HD, D), 0.02),
-            "w_v": _normal(rng, (HD, D), 0.02), "w_r": _normal(rng, (HD, D), 0.02),
-            "w_o": _normal(rng, (D, HD), 0.02),
-            "u": _normal(rng, (w.n_head, w.d_head), 0.02), "v": _normal(rng, (w.n_head, w.d_head), 0.02),
+            "w_q": _normal(rng, (HD, D), sd("w_q", D)), "w_k": _normal(rng, (HD, D), sd("w_k", D)),
+            "w_v": _normal(rng, (HD, D), sd("w_v", D)), "w_r": _normal(rng, (HD, D), sd("w_r", D)),
+            "w_o": _normal(rng, (D, HD), sd("w_o", HD)),
+            "u": _normal(rng, (w.n_head, w.d_head), sd("u")), "v": _normal(rng, (w.n_head, w.d_head), sd("v")),
         }
         if w.bias_clamp >= 0:
-            lw["beta"] = _normal(rng, (bias_rows(w.bias_clamp, w.bias_kind), w.n_head), 0.02)
+            lw["beta"] = _normal(rng, (bias_rows(w.bias_clamp, w.bias_kind), w.n_head), sd("beta"))
         lw["ln1_g"] = (1.0 + _normal(rng, (D,), 0.02)).astype(np.float32)
         lw["ln1_b"] = _normal(rng, (D,), 0.02)
         lw["ln2_g"] = (1.0 + _normal(rng, (D,), 0.02)).astype(np.float32)
