@@ -27,7 +27,8 @@
  * Conventions for every entry point
  *  - All tensors are dense, row-major, on the device of the current HIP
  *    device, owned by the caller. The library allocates no device memory:
- *    scratch space comes from the caller's workspace.
+ *    scratch space comes from the caller's workspace (xl_segment_step_noalloc
+ *    alone uses a static device array the library holds instead).
  *  - 'stream' is a hipStream_t (NULL: the null stream). Work is enqueued
  *    asynchronously; device-side results are valid once the stream reaches
  *    that point. Host-side outputs (status, FIFO bookkeeping) are final on
@@ -228,6 +229,26 @@ typedef struct {
  */
 int xl_segment_step(const xl_attn_desc* desc, const xl_attn_weights* w, const void* h,
                     xl_mem_fifo* fifo, void* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * xl_segment_step for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * The same step, with the workspace taken from a static device array of
+ * XL_NOALLOC_SCRATCH_BYTES held by the library on each GPU it runs on (from
+ * the library's load until the process ends) instead of a caller's buffer.
+ * The call allocates nothing; the first call on a device looks up that
+ * device's array address once. Limit: a step whose
+ * xl_rel_attn_workspace_size() (desc with mlen = fifo->len) exceeds
+ * XL_NOALLOC_SCRATCH_BYTES returns XL_WORKSPACE_TOO_SMALL and leaves the fifo
+ * untouched. Every call on one GPU shares that GPU's array, which keeps the
+ * last call's contents (nothing in it needs to start at zero): calls that
+ * overlap on one GPU (other streams, other threads) race and must be
+ * serialised by the caller. Arguments, outputs and errors otherwise as
+ * xl_segment_step.
+ */
+#define XL_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int xl_segment_step_noalloc(const xl_attn_desc* desc, const xl_attn_weights* w, const void* h,
+                            xl_mem_fifo* fifo, void* out, void* stream);
 
 /* Caller-owned key ring of one layer, for evaluation with fixed weights: the
  * projected keys and values of the memory are kept instead of its input

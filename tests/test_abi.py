@@ -185,6 +185,27 @@ def test_segment_step_rejects_bad_fifo():
     assert (f.len, f.head) == (10, 3)                                           # untouched on error
 
 
+def test_segment_step_noalloc_rejects_before_any_launch():
+    # host checks of the allocation-free step: bad fifo, bad shapes, and a step
+    # whose workspace would exceed the static scratch; the fifo stays untouched
+    lib = xl.lib()
+    w = _weights()
+    step = lambda d, fifo: lib.xl_segment_step_noalloc(ctypes.byref(d), ctypes.byref(w), FAKE[8],
+                                                       ctypes.byref(fifo) if fifo is not None else None,
+                                                       FAKE[10], None)
+    d = _desc(mlen=0)
+    assert step(d, None) == xl.XL_NULL_ARG
+    assert step(d, xl.xl_mem_fifo(FAKE[12], 128, 129, 0)) == xl.XL_BAD_SHAPE
+    big = _desc(mlen=0, batch=64, d_model=1024, n_head=16, qlen=1024)
+    f = xl.xl_mem_fifo(FAKE[12], 1024, 1024, 5)
+    ws_need = lib.xl_rel_attn_workspace_size(ctypes.byref(_desc(mlen=1024, batch=64, d_model=1024, n_head=16,
+                                                                qlen=1024)))
+    assert ws_need > xl.XL_NOALLOC_SCRATCH_BYTES
+    assert step(big, f) == xl.XL_WORKSPACE_TOO_SMALL
+    assert b"allocation-free" in lib.xl_last_error()
+    assert (f.len, f.head) == (1024, 5)
+
+
 def test_segment_step_kv_rejects_bad_ring():
     lib = xl.lib()
     d = _desc(mlen=0)                       # qlen 128

@@ -63,7 +63,10 @@ EXPORTS = ("xl_status_string", "xl_last_error", "xl_relpos_embed", "xl_rel_attn_
            "xl_rel_attn_workspace_layout", "xl_rel_attn_fwd", "xl_rel_attn_core_workspace_size", "xl_rel_attn_core",
            "xl_segment_step", "xl_segment_step_kv_workspace_size", "xl_segment_step_kv", "xl_set_core_events",
            "xl_rel_attn_core_bwd_workspace_size", "xl_rel_attn_core_bwd", "xl_decoder_layer_workspace_size", "xl_decoder_layer_fwd", "xl_decoder_stack_workspace_size",
-           "xl_decoder_stack_step")
+           "xl_decoder_stack_step", "xl_segment_step_noalloc")
+
+# bytes of the static scratch of xl_segment_step_noalloc (XL_NOALLOC_SCRATCH_BYTES)
+XL_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def lib():
@@ -99,6 +102,8 @@ def lib():
                                        ctypes.c_size_t, _p]
         L.xl_segment_step.argtypes = [ctypes.POINTER(xl_attn_desc), ctypes.POINTER(xl_attn_weights), _p,
                                       ctypes.POINTER(xl_mem_fifo), _p, _p, ctypes.c_size_t, _p]
+        L.xl_segment_step_noalloc.argtypes = [ctypes.POINTER(xl_attn_desc), ctypes.POINTER(xl_attn_weights), _p,
+                                              ctypes.POINTER(xl_mem_fifo), _p, _p]
         L.xl_set_core_events.argtypes = [_p, _p]
         L.xl_segment_step_kv_workspace_size.argtypes = [ctypes.POINTER(xl_attn_desc)]
         L.xl_segment_step_kv_workspace_size.restype = ctypes.c_size_t
@@ -119,7 +124,7 @@ def lib():
                                             ctypes.POINTER(xl_mem_fifo), _p, _p, ctypes.c_size_t, _p]
         for f in ("xl_relpos_embed", "xl_rel_attn_workspace_layout", "xl_rel_attn_fwd", "xl_rel_attn_core",
                   "xl_segment_step", "xl_set_core_events", "xl_segment_step_kv", "xl_decoder_layer_fwd",
-                  "xl_rel_attn_core_bwd",
+                  "xl_rel_attn_core_bwd", "xl_segment_step_noalloc",
                   "xl_decoder_stack_step"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -236,6 +241,13 @@ def xl_segment_step(desc: xl_attn_desc, weights: Weights, h, fifo: xl_mem_fifo, 
     cw = weights.c() if isinstance(weights, Weights) else weights
     _check(lib().xl_segment_step(ctypes.byref(desc), ctypes.byref(cw), _ptr(h), ctypes.byref(fifo), _ptr(out),
                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return out
+
+
+def xl_segment_step_noalloc(desc: xl_attn_desc, weights: Weights, h, fifo: xl_mem_fifo, out, stream=None):
+    cw = weights.c() if isinstance(weights, Weights) else weights
+    _check(lib().xl_segment_step_noalloc(ctypes.byref(desc), ctypes.byref(cw), _ptr(h), ctypes.byref(fifo),
+                                         _ptr(out), _stream(stream)))
     return out
 
 

@@ -6,10 +6,17 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "../../include/xl_rel.h"
 #include "xl_internal.hpp"
+
+// Workspace of xl_segment_step_noalloc: one copy per GPU, resident from the
+// library's load until the process ends. Host code never passes this name to a
+// kernel or a copy: it is a host-side stand-in, and the device address comes
+// from hipGetSymbolAddress (scratch_ptr below).
+static __device__ __attribute__((aligned(256))) unsigned char scratch[XL_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -393,6 +400,29 @@ void fifo_advance(const xl_attn_desc* d, xl_mem_fifo* f) {
     f->len = new_len;
 }
 
+// Device address of this GPU's copy of `scratch`, looked up once per device
+// (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // guarded by g_scratch_mu
+
+int scratch_ptr(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(XL_UNSUPPORTED, "device index %d beyond %d", dev, kMaxDevices - 1);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p || (uintptr_t)p % kAlign) return fail(XL_HIP_ERROR, "scratch is not 256-byte aligned");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return XL_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -538,6 +568,22 @@ int xl_segment_step(const xl_attn_desc* desc, const xl_attn_weights* w, const vo
     if (st != XL_OK) return st;
     fifo_advance(desc, fifo);
     return XL_OK;
+}
+
+int xl_segment_step_noalloc(const xl_attn_desc* desc, const xl_attn_weights* w, const void* h, xl_mem_fifo* fifo,
+                            void* out, void* stream) {
+    g_last_error.clear();
+    int st = check_fifo(fifo);
+    if (st != XL_OK) return st;
+    if ((st = check_desc(desc, fifo->len, true)) != XL_OK) return st;
+    xl_ws_layout L;
+    fill_layout(desc, fifo->len, &L);
+    if (L.total > XL_NOALLOC_SCRATCH_BYTES)
+        return fail(XL_WORKSPACE_TOO_SMALL, "this step needs %zu bytes of scratch; the allocation-free step holds %zu",
+                    L.total, (size_t)XL_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    if ((st = scratch_ptr(&ws)) != XL_OK) return st;
+    return xl_segment_step(desc, w, h, fifo, out, ws, XL_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 size_t xl_segment_step_kv_workspace_size(const xl_attn_desc* desc) {
