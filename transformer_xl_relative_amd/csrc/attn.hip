@@ -1,4 +1,5 @@
-// attn.hip -- fused Transformer-XL relative attention forward on MFMA.
+// attn.hip -- fused Transformer-XL relative attention forward on MFMA, fp32
+// operands (the tiny configuration, d_head 8; v_mfma_f32_32x32x2_f32).
 //
 // For one head, query i (segment position, absolute position mlen+i) and key
 // j over [memory ; segment] (qidao123.com thread-401555 §3; felixzhao.cn
@@ -38,26 +39,21 @@
 #include <hip/hip_ext.h>
 #include "xl_internal.hpp"
 
-#include <type_traits>
-
-#ifndef XL_ATTN_WAVES
-#define XL_ATTN_WAVES 4
-#endif
-
 namespace xl {
 namespace {
 
+constexpr int NW = 4;            // waves per workgroup
 constexpr int WQ = 32;           // queries per wave
 constexpr int BKY = 32;          // keys per step
 constexpr int RING = 64;         // key slots per query in the ring (floats, 256 B per row)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float RESCALE_TH = 5.5451774444795623f;   // 8 ln 2: rescale only when the max grows by 2^8
 
-template <typename T, int DH, int NW>
+template <int DH>
 struct AttnLds {
-    static constexpr int KROW = DH * (int)sizeof(T) + 16;     // padded key row
+    static constexpr int KROW = DH * 4 + 16;      // padded key row
     static constexpr int KTILE = BKY * KROW;
-    static constexpr int VROW = BKY * (int)sizeof(T) + 8;     // padded row of V^T
+    static constexpr int VROW = BKY * 4 + 8;      // padded row of V^T
     static constexpr int VTILE = DH * VROW;
     static constexpr int OFF_K = 0;
     static constexpr int OFF_V = 2 * KTILE;
@@ -76,16 +72,15 @@ __device__ __forceinline__ float halves_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <typename T, int DH, int NW, bool HAS_BIAS>
+template <int DH, bool HAS_BIAS>
 __global__ void __launch_bounds__(NW * 64) attn_kernel(AttnArgs a) {
-    using L = AttnLds<T, DH, NW>;
-    constexpr bool BF = Elem<T>::kBf16;
+    using L = AttnLds<DH>;
+    using T = float;
     constexpr int NT = NW * 64;
     constexpr int BQ = NW * WQ;
-    constexpr int EPC = 16 / (int)sizeof(T);          // elements per 16-byte chunk
-    constexpr int NKC = BF ? DH / 16 : DH / 2;        // MFMA k-steps over d_head
-    static_assert(NKC >= 1, "d_head too small");
-    using OpT = typename std::conditional<BF, bf16x8, float>::type;
+    constexpr int EPC = 4;                            // elements per 16-byte chunk
+    constexpr int NKC = DH / 2;                       // MFMA k-steps over d_head
+    static_assert(NKC >= 1 && DH <= 32, "d_head");
     extern __shared__ __attribute__((aligned(256))) char smem[];
 
     const int tid = (int)__builtin_amdgcn_workitem_id_x(), lane = tid & 63;
@@ -118,7 +113,7 @@ __global__ void __launch_bounds__(NW * 64) attn_kernel(AttnArgs a) {
     // ---- query operands (MFMA B operand): lane owns query iw + l32
     const int iq = iw + l32;
     const bool qok = iq < a.qlen;
-    OpT quB[NKC], qvB[NKC];
+    float quB[NKC], qvB[NKC];
     {
         const int64_t row = ((int64_t)bh * a.qlen + (qok ? iq : a.qlen - 1)) * DH;
         const T* qrow = (const T*)a.q + row;
@@ -126,40 +121,21 @@ __global__ void __launch_bounds__(NW * 64) attn_kernel(AttnArgs a) {
         const T* vbias = (const T*)a.v + h * DH;
         // the biases fold into the query operands: scale*(q+u), scale*(q+v)
         for (int kc = 0; kc < NKC; ++kc) {
-            if constexpr (BF) {
-                const u32x4 qw = *(const u32x4*)(qrow + 16 * kc + 8 * hf);
-                const u32x4 uw = *(const u32x4*)(ub + 16 * kc + 8 * hf);
-                const u32x4 vw = *(const u32x4*)(vbias + 16 * kc + 8 * hf);
-                u32x4 a_u, a_v;
-                for (int e = 0; e < 4; ++e) {
-                    const float q0 = __uint_as_float(qw[e] << 16), q1 = __uint_as_float(qw[e] & 0xFFFF0000u);
-                    const float u0 = __uint_as_float(uw[e] << 16), u1 = __uint_as_float(uw[e] & 0xFFFF0000u);
-                    const float v0 = __uint_as_float(vw[e] << 16), v1 = __uint_as_float(vw[e] & 0xFFFF0000u);
-                    a_u[e] = pack2bf(a.scale * (q0 + u0), a.scale * (q1 + u1));
-                    a_v[e] = pack2bf(a.scale * (q0 + v0), a.scale * (q1 + v1));
-                }
-                quB[kc] = as_bf16x8(a_u);
-                qvB[kc] = as_bf16x8(a_v);
-            } else {
-                const float qe = Elem<T>::to_f(qrow[2 * kc + hf]);
-                quB[kc] = a.scale * (qe + Elem<T>::to_f(ub[2 * kc + hf]));
-                qvB[kc] = a.scale * (qe + Elem<T>::to_f(vbias[2 * kc + hf]));
-            }
+            const float qe = qrow[2 * kc + hf];
+            quB[kc] = a.scale * (qe + ub[2 * kc + hf]);
+            qvB[kc] = a.scale * (qe + vbias[2 * kc + hf]);
         }
     }
 
     // ---- band operand (MFMA A operand of the position product)
     // block beta covers distances dtop - 32*beta - c, c = 0..31 (descending)
     const int dtop = a.mlen + iw + WQ - 1;
-    OpT band[NKC];
+    float band[NKC];
     auto load_band = [&](int beta) {
         int d = dtop - BKY * beta - l32;
         d = max(0, min(d, a.n_rel - 1));
         const T* row = rbase + (int64_t)d * DH;
-        for (int kc = 0; kc < NKC; ++kc) {
-            if constexpr (BF) band[kc] = as_bf16x8(*(const u32x4*)(row + 16 * kc + 8 * hf));
-            else band[kc] = Elem<T>::to_f(row[2 * kc + hf]);
-        }
+        for (int kc = 0; kc < NKC; ++kc) band[kc] = row[2 * kc + hf];
     };
     auto pos_product = [&](int beta) {
         f32x16 g;
@@ -168,7 +144,7 @@ __global__ void __launch_bounds__(NW * 64) attn_kernel(AttnArgs a) {
             const int dblk = dtop - BKY * beta;
             for (int r = 0; r < 16; ++r) {
                 const int d = max(0, dblk - acc_row(r, hf));
-                g[r] = Elem<T>::to_f(bias[bias_row(d, a.bias_kind, a.bias_clamp) * a.H + h]);
+                g[r] = bias[bias_row(d, a.bias_kind, a.bias_clamp) * a.H + h];
             }
         } else {
             for (int r = 0; r < 16; ++r) g[r] = 0.f;
@@ -208,12 +184,7 @@ __global__ void __launch_bounds__(NW * 64) attn_kernel(AttnArgs a) {
     // content product of a step (its K tile in LDS buffer kbuf) on top of its position terms
     auto content = [&](f32x16 acc, int kbuf) {
         const char* kt = smem + L::OFF_K + kbuf * L::KTILE + l32 * L::KROW;
-        for (int kc = 0; kc < NKC; ++kc) {
-            OpT ka;
-            if constexpr (BF) ka = as_bf16x8(*(const u32x4*)(kt + (2 * kc + hf) * 16));
-            else ka = *(const float*)(kt + (2 * kc + hf) * 4);
-            acc = mfma32(ka, quB[kc], acc);
-        }
+        for (int kc = 0; kc < NKC; ++kc) acc = mfma32(*(const float*)(kt + (2 * kc + hf) * 4), quB[kc], acc);
         return acc;
     };
 
@@ -353,30 +324,7 @@ __global__ void __launch_bounds__(NW * 64) attn_kernel(AttnArgs a) {
             if (want_block) ring_write(gnext, par ^ 1);      // block s+3 replaces block s+1, already read
             // O^T += V^T P^T
             const char* vt = smem + L::OFF_V + par * L::VTILE;
-            if constexpr (BF) {
-                bf16x8 pb[2];
-                for (int kc = 0; kc < 2; ++kc)
-                    for (int e = 0; e < 8; ++e) pb[kc][e] = (__bf16)p[8 * kc + e];
-                // the row sum uses the same rounded weights as P.V
-                typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-                const bf16x2v one = {(__bf16)1.0f, (__bf16)1.0f};
-                float psum = 0.f;
-                for (int kc = 0; kc < 2; ++kc)
-                    for (int e = 0; e < 8; e += 2) {
-                        const bf16x2v pr = {pb[kc][e], pb[kc][e + 1]};
-                        psum = __builtin_amdgcn_fdot2_f32_bf16(pr, one, psum, false);
-                    }
-                l_run += psum;
-                for (int t = 0; t < NDT; ++t) {
-                    const char* vrow = vt + (32 * t + l32) * L::VROW;
-                    for (int kc = 0; kc < 2; ++kc) {
-                        const u32x2 lo = *(const u32x2*)(vrow + (16 * kc + 4 * hf) * 2);
-                        const u32x2 hi = *(const u32x2*)(vrow + (16 * kc + 8 + 4 * hf) * 2);
-                        const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
-                        o[t] = mfma32(as_bf16x8(w), pb[kc], o[t]);
-                    }
-                }
-            } else {
+            {
                 float psum = 0.f;
                 for (int r = 0; r < 16; ++r) psum += p[r];
                 l_run += psum;
@@ -405,42 +353,37 @@ __global__ void __launch_bounds__(NW * 64) attn_kernel(AttnArgs a) {
             if (d >= DH) continue;
             const float v0 = o[t][4 * gq] * inv, v1 = o[t][4 * gq + 1] * inv;
             const float v2 = o[t][4 * gq + 2] * inv, v3 = o[t][4 * gq + 3] * inv;
-            if constexpr (BF) *(u32x2*)(orow + d) = (u32x2){pack2bf(v0, v1), pack2bf(v2, v3)};
-            else *(f32x4*)(orow + d) = (f32x4){v0, v1, v2, v3};
+            *(f32x4*)(orow + d) = (f32x4){v0, v1, v2, v3};
         }
 }
 
-template <typename T, int DH, int NW, bool HAS_BIAS>
+template <int DH, bool HAS_BIAS>
 hipError_t launch_t(const AttnArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-    using L = AttnLds<T, DH, NW>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)attn_kernel<T, DH, NW, HAS_BIAS>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, L::TOTAL);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    using L = AttnLds<DH>;
+    // the LDS limit is raised once per process (thread-safe: a function-local static)
+    static const hipError_t attr = hipFuncSetAttribute((const void*)attn_kernel<DH, HAS_BIAS>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, L::TOTAL);
+    if (attr != hipSuccess) return attr;
     constexpr int BQ = NW * WQ;
     const int nqt = (a.qlen + BQ - 1) / BQ;
     const int64_t grid = (int64_t)a.B * a.H * nqt;
     if (grid <= 0) return hipSuccess;
     (void)hipGetLastError();   // drop a stale error of an earlier runtime call
-    hipExtLaunchKernelGGL((attn_kernel<T, DH, NW, HAS_BIAS>), dim3((unsigned)grid), dim3(NW * 64), L::TOTAL, s, ev0,
-                          ev1, 0u, a);
+    hipExtLaunchKernelGGL((attn_kernel<DH, HAS_BIAS>), dim3((unsigned)grid), dim3(NW * 64), L::TOTAL, s, ev0, ev1, 0u,
+                          a);
     return hipGetLastError();
 }
 
-template <typename T, int DH>
+template <int DH>
 hipError_t launch_dt(const AttnArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-    constexpr int NW = XL_ATTN_WAVES;
-    return a.bias ? launch_t<T, DH, NW, true>(a, s, ev0, ev1) : launch_t<T, DH, NW, false>(a, s, ev0, ev1);
+    return a.bias ? launch_t<DH, true>(a, s, ev0, ev1) : launch_t<DH, false>(a, s, ev0, ev1);
 }
 
 }  // namespace
 
 hipError_t launch_attn(const AttnArgs& a, bool bf16, int dh, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     if (bf16 && dh == 64) return launch_attn_bf16(a, s, ev0, ev1);
-    if (!bf16 && dh == 8) return launch_dt<float, 8>(a, s, ev0, ev1);
+    if (!bf16 && dh == 8) return launch_dt<8>(a, s, ev0, ev1);
     return hipErrorInvalidValue;
 }
 

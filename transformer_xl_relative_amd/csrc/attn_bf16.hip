@@ -722,13 +722,12 @@ hipError_t launch_bf16(const AttnArgs& a, hipStream_t s, hipEvent_t ev0, hipEven
         lds += 4 * ((gtop_max + 2 * BQ + 3) & ~3);
     }
     if (lds > 160 * 1024) return hipErrorInvalidValue;
-    static int attr = 0;
-    if (lds > attr) {
-        hipError_t e = hipFuncSetAttribute((const void*)attn_bf16_kernel<HAS_BIAS, RING>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        if (e != hipSuccess) return e;
-        attr = 160 * 1024;
-    }
+    // the LDS limit is raised to the whole 160 KB once per process (a
+    // function-local static is initialised exactly once, also under
+    // concurrent launches)
+    static const hipError_t attr = hipFuncSetAttribute((const void*)attn_bf16_kernel<HAS_BIAS, RING>,
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (attr != hipSuccess) return attr;
     (void)hipGetLastError();   // drop a stale error of an earlier runtime call
     if (qt_first == nqt) {
         hipExtLaunchKernelGGL(attn_bf16_kernel<HAS_BIAS, RING>, dim3((unsigned)grid), dim3(NT), (uint32_t)lds, s, ev0, ev1, 0u, a);

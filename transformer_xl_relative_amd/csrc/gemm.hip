@@ -172,16 +172,13 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(GemmBatch gb) {
     else gemm_tile<T, true>(g, m0, n0, smem);
 }
 
+// The LDS limit is raised once per process; a function-local static is
+// initialised exactly once even when several threads launch at the same time.
 template <typename T>
 hipError_t set_lds_attr() {
-    static bool done = false;
-    if (!done) {
-        hipError_t e = hipFuncSetAttribute((const void*)gemm_kernel<T>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           GEMM_LDS);
-        if (e != hipSuccess) return e;
-        done = true;
-    }
-    return hipSuccess;
+    static const hipError_t e =
+        hipFuncSetAttribute((const void*)gemm_kernel<T>, hipFuncAttributeMaxDynamicSharedMemorySize, GEMM_LDS);
+    return e;
 }
 
 }  // namespace

@@ -405,13 +405,14 @@ hipError_t launch_tiles(const GemmArgs* g, int count, hipStream_t s, const RowCo
     if (tiles + copy_wgs == 0) return hipSuccess;
     bool half = false;
     for (int i = 0; i < gb.count; ++i) half = half || gb.p[i].K % T::KST != 0;
-    static bool attr[2] = {false, false};
     const auto kern = half ? gemm_bf16_kernel<T, true> : gemm_bf16_kernel<T, false>;
-    if (!attr[half]) {
-        hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS);
-        if (e != hipSuccess) return e;
-        attr[half] = true;
-    }
+    // the LDS limit of each variant is raised once per process (function-local
+    // statics are initialised exactly once, also under concurrent launches)
+    static const hipError_t attr_full =
+        hipFuncSetAttribute((const void*)gemm_bf16_kernel<T, false>, hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS);
+    static const hipError_t attr_half =
+        hipFuncSetAttribute((const void*)gemm_bf16_kernel<T, true>, hipFuncAttributeMaxDynamicSharedMemorySize, T::LDS);
+    if ((half ? attr_half : attr_full) != hipSuccess) return half ? attr_half : attr_full;
     (void)hipGetLastError();   // drop a stale error of an earlier runtime call
     hipLaunchKernelGGL(kern, dim3(tiles + copy_wgs), dim3(T::NT), T::LDS, s, gb);
     return hipGetLastError();
