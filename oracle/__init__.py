@@ -12,7 +12,8 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# XL_ORACLE_LIB names another build of the same source (the sanitizer build)
+_LIB_PATH = os.environ.get("XL_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 _i64 = ctypes.c_int64

@@ -12,15 +12,21 @@ SRC = os.path.join(HERE, "xl_oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
-           "-fno-fast-math", "-ffp-contract=off", SRC, "-o", tmp, "-lm"]
+# AddressSanitizer and UndefinedBehaviorSanitizer build (for a process that
+# preloads gcc's libasan and libubsan): every out-of-bounds access or
+# undefined operation in the oracle then aborts the run with a report.
+SANITIZE = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
+
+
+def build(verbose: bool = False, out: str = LIB, sanitize: bool = False) -> str:
+    tmp = out + ".tmp"
+    cmd = ["gcc", "-O1" if sanitize else "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+           "-fno-fast-math", "-ffp-contract=off", *(SANITIZE if sanitize else []), SRC, "-o", tmp, "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -12,7 +12,8 @@ import os
 from typing import Optional
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libxlrel.so")
+# XL_LIB names another build of the same sources (the host-sanitizer build)
+LIB_PATH = os.environ.get("XL_LIB") or os.path.join(_HERE, "libxlrel.so")
 
 XL_OK, XL_NULL_ARG, XL_BAD_SHAPE, XL_UNSUPPORTED, XL_WORKSPACE_TOO_SMALL, XL_HIP_ERROR = range(6)
 XL_F32, XL_BF16 = 0, 1

@@ -28,10 +28,17 @@ PER_SOURCE = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mno-amdgpu-ieee
               "gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
-def _compile(src: str, verbose: bool, build_dir: str, defines) -> str:
+# AddressSanitizer and UndefinedBehaviorSanitizer on the host code only (the
+# validation, layout and launch code; the kernels are built as usual), for a
+# process that preloads clang's ASan runtime: each flag goes to the host pass.
+HOST_SANITIZE = [f for opt in ("-fsanitize=address", "-fsanitize=undefined", "-fno-sanitize-recover=all",
+                               "-fno-omit-frame-pointer") for f in ("-Xarch_host", opt)]
+
+
+def _compile(src: str, verbose: bool, build_dir: str, defines, host_sanitize: bool = False) -> str:
     obj = os.path.join(build_dir, src.replace(".hip", ".o"))
-    cmd = [HIPCC, *FLAGS, *PER_SOURCE.get(src, []), *[f"-D{d}" for d in defines], "-c",
-           os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *PER_SOURCE.get(src, []), *(HOST_SANITIZE if host_sanitize else []),
+           *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -45,11 +52,11 @@ def _compile(src: str, verbose: bool, build_dir: str, defines) -> str:
     return obj
 
 
-def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+def build(verbose: bool = False, out: str = LIB, defines=(), host_sanitize: bool = False) -> str:
     build_dir = BUILD if out == LIB else os.path.join(os.path.dirname(os.path.abspath(out)), "_build")
     os.makedirs(build_dir, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=4) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose, build_dir, defines), SOURCES))
+        objs = list(ex.map(lambda s: _compile(s, verbose, build_dir, defines, host_sanitize), SOURCES))
     tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
