@@ -209,6 +209,10 @@ def main():
     ap.add_argument("--backward", action="store_true", help="time the attention-core gradients instead")
     ap.add_argument("--kv-ring", action="store_true",
                     help="step with xl_segment_step_kv (projected keys and values of the memory kept in a ring)")
+    ap.add_argument("--reuse-table", action="store_true",
+                    help="steps after the first skip the sinusoid and the R projection (XL_REUSE_TABLE; the "
+                         "memory is full, so the table is that of the first step): a separate measurement, "
+                         "the default step computes every row of the path")
     args = ap.parse_args()
     if args.summarize:
         summarize(args.summarize, args.copy_calib_mib)
@@ -274,6 +278,10 @@ def main():
 
         while kv.len < w.mlen:
             step()
+
+    if args.reuse_table:
+        step()                       # a full-memory step computes the table; the next ones reuse it
+        desc.flags = xl.XL_REUSE_TABLE
 
     if args.copy_calib_mib > 0:
         # a plain elementwise copy kernel (int32 -> float32 conversion: reads and
@@ -344,7 +352,8 @@ def main():
                                 f"output projection), batch {w.batch}, d_model {D}, {w.n_head} heads x {w.d_head}, "
                                 f"qlen {w.qlen}, mlen {w.mlen}, causal"),
                    "batch": w.batch, "qlen": w.qlen, "mlen": w.mlen, "d_model": D, "n_head": w.n_head,
-                   "d_head": w.d_head, "clamp_len": w.clamp_len, "bias_clamp": w.bias_clamp},
+                   "d_head": w.d_head, "clamp_len": w.clamp_len, "bias_clamp": w.bias_clamp,
+                   "reuse_table": bool(args.reuse_table)},
         "roofline": {"kernel": "attn_bf16_kernel (fused relative attention)",
                      **roofline(attn_flops, attn_min_bytes(w, w.mlen), core_avg_ms * 1e-3, bound="mfma"),
                      "traffic": traffic,

@@ -122,7 +122,22 @@ typedef struct {
     int32_t bias_kind;   /* XL_BIAS_CLAMP (0) or XL_BIAS_T5: how a distance
                             picks its bias table row; ignored when
                             bias_clamp < 0 */
+    int32_t flags;       /* 0 or XL_REUSE_TABLE (below) */
 } xl_attn_desc;
+
+/* xl_attn_desc.flags. XL_REUSE_TABLE: the rel and r regions of the workspace
+ * already hold this call's table rows -- an earlier xl_rel_attn_fwd /
+ * xl_segment_step / xl_segment_step_kv / xl_segment_step_noalloc call wrote
+ * them into the same workspace (for xl_segment_step_noalloc: the same GPU's
+ * scratch) with the same d_model, n_head, clamp_len, base, w_r contents and
+ * the same number of table rows n_rel = min(mlen + qlen, clamp_len + 1)
+ * (for a segment run: once the memory is full). The sinusoid and the R
+ * projection are then skipped: the table depends on the distance alone
+ * (felixzhao.cn article 118 §2.3.2), so a recurrent run with fixed weights
+ * computes it once. The library cannot check this promise; a stale table
+ * gives wrong outputs. Not accepted by the decoder entry points (every layer
+ * writes its own table into the shared workspace). */
+enum { XL_REUSE_TABLE = 1 };
 
 /* Weights of one layer; all device pointers in desc->dtype. */
 typedef struct {

@@ -79,6 +79,7 @@ def _fwd(desc, w=None, h=FAKE[8], mem=FAKE[9], out=FAKE[10], ws=FAKE[11], ws_byt
     (dict(attn_splits=65), xl.XL_BAD_SHAPE),
     (dict(bias_kind=2), xl.XL_BAD_SHAPE),
     (dict(bias_kind=-1, bias_clamp=4), xl.XL_BAD_SHAPE),
+    (dict(flags=2), xl.XL_BAD_SHAPE),                    # unknown flag bit
 ])
 def test_fwd_rejects_bad_descriptors(over, status):
     assert _fwd(_desc(**over)) == status
@@ -140,6 +141,19 @@ def test_split_workspace():
     # f32 never splits
     assert xl.xl_rel_attn_core_workspace_size(_desc(dtype=xl.XL_F32, d_head=8, d_model=16, attn_splits=7)) == 0
     assert xl.xl_rel_attn_core_workspace_size(_desc(attn_splits=99)) == 0      # invalid descriptor
+
+
+def test_workspace_grows_with_memory():
+    # a workspace sized for the longest memory serves every shorter one: the
+    # split partials are sized for any memory length
+    for kw in (dict(batch=4, n_head=8, qlen=64, d_model=512), dict(batch=1, n_head=2, qlen=64, d_model=128)):
+        sizes = [xl.xl_rel_attn_workspace_size(_desc(mlen=m, **kw)) for m in range(0, 2100, 8)]
+        assert all(a <= b for a, b in zip(sizes, sizes[1:])), kw
+        core = [xl.xl_rel_attn_core_workspace_size(_desc(mlen=m, **kw)) for m in range(0, 2100, 8)]
+        assert all(a <= b for a, b in zip(core, core[1:])), kw
+    dec = [xl.xl_decoder_stack_workspace_size(_desc(batch=2, n_head=8, qlen=64, d_model=256, mlen=m), 1024)
+           for m in range(1800, 2100, 8)]
+    assert all(a <= b for a, b in zip(dec, dec[1:]))
 
 
 def test_core_rejects_bad_arguments():
@@ -266,6 +280,7 @@ def test_decoder_layer_rejects_bad_arguments():
                                         None)
     assert call(w=_dec_weights(w2=None)) == xl.XL_NULL_ARG
     assert call(w=_dec_weights(ln1_g=None)) == xl.XL_NULL_ARG
+    assert call(desc=_desc(flags=xl.XL_REUSE_TABLE)) == xl.XL_UNSUPPORTED   # layers share the workspace
     assert call(d_inner=0) == xl.XL_BAD_SHAPE
     assert call(d_inner=100) == xl.XL_BAD_SHAPE                  # not a multiple of 32
     assert call(eps=-1.0) == xl.XL_BAD_SHAPE

@@ -407,3 +407,47 @@ def test_segment_run_kv_ring_full_size(T):
     outs, _ = _segment_run_gpu(T, w, t, batch=w.batch, qlen=w.qlen, n_seg=w.segments, mlen_max=w.mlen)
     for s in range(w.segments):
         assert np.array_equal(gu.host64(ring_outs[s]), outs[s]), f"segment {s} differs"
+
+
+# --- the table of a full-memory segment run, computed once -----------------------------------
+
+@pytest.mark.parametrize("kv_ring", [False, True])
+def test_reuse_table_bit_identical(T, kv_ring):
+    # once the memory is full the table rows no longer change (they depend on
+    # the distance alone); steps that skip the sinusoid and the R projection
+    # (XL_REUSE_TABLE) give the same bits as steps that recompute them
+    import dataclasses
+    import transformer_xl_relative_amd as xl
+    qlen, n_seg, mlen_max = 64, 6, 128
+    w = dataclasses.replace(W["segments_bf16"], n_head=4, qlen=qlen, mlen=mlen_max, segments=n_seg, bias_clamp=16,
+                            clamp_len=150, seed=61)
+    t = xl_inputs.layer_inputs(w, batch=2, qlen=qlen, recipe="sensitive")
+    L = gu.Layer(w, t, batch=2, qlen=qlen, mlen=mlen_max)
+    H, dh, D = w.n_head, w.d_head, w.d_model
+    hs = gu.dev(t["h"])
+    runs = []
+    for reuse in (False, True):
+        ring = T.zeros((2, mlen_max, D), dtype=T.bfloat16, device="cuda")
+        fifo = xl.xl_mem_fifo(ring.data_ptr(), mlen_max, 0, 0)
+        cap = mlen_max + qlen + 8
+        kr = T.zeros((2, H, cap, dh), dtype=T.bfloat16, device="cuda")
+        vr = T.zeros((2, H, dh, cap), dtype=T.bfloat16, device="cuda")
+        kv = xl.xl_kv_fifo(kr.data_ptr(), vr.data_ptr(), cap, mlen_max, 0, 0)
+        ws = T.empty(L.ws.numel(), dtype=T.uint8, device="cuda")
+        outs = []
+        for s in range(n_seg):
+            full = (fifo.len if not kv_ring else kv.len) == mlen_max
+            flags = xl.XL_REUSE_TABLE if reuse and full and s >= 3 else 0
+            desc = xl.make_desc(batch=2, d_model=D, n_head=H, d_head=dh, qlen=qlen, mlen=0, clamp_len=w.clamp_len,
+                                bias_clamp=w.bias_clamp, dtype=xl.XL_BF16, out_dtype=xl.XL_F32, flags=flags)
+            out = T.empty((2, qlen, D), dtype=T.float32, device="cuda")
+            h = hs[:, s * qlen:(s + 1) * qlen].contiguous()
+            if kv_ring:
+                xl.xl_segment_step_kv(desc, L.weights, h, kv, out, ws)
+            else:
+                xl.xl_segment_step(desc, L.weights, h, fifo, out, ws)
+            T.cuda.synchronize()
+            outs.append(gu.host64(out))
+        runs.append(outs)
+    for s in range(n_seg):
+        assert np.array_equal(runs[0][s], runs[1][s]), f"segment {s}"

@@ -19,6 +19,7 @@ XL_OK, XL_NULL_ARG, XL_BAD_SHAPE, XL_UNSUPPORTED, XL_WORKSPACE_TOO_SMALL, XL_HIP
 XL_F32, XL_BF16 = 0, 1
 XL_BIAS_CLAMP, XL_BIAS_T5 = 0, 1
 XL_T5_BUCKETS = 12
+XL_REUSE_TABLE = 1
 
 _i64 = ctypes.c_int64
 _p = ctypes.c_void_p
@@ -29,7 +30,7 @@ class xl_attn_desc(ctypes.Structure):
                 ("qlen", _i64), ("mlen", _i64), ("clamp_len", _i64), ("bias_clamp", _i64),
                 ("base", ctypes.c_double), ("scale", ctypes.c_float),
                 ("dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32), ("attn_splits", ctypes.c_int32),
-                ("bias_kind", ctypes.c_int32)]
+                ("bias_kind", ctypes.c_int32), ("flags", ctypes.c_int32)]
 
 
 class xl_attn_weights(ctypes.Structure):
@@ -158,9 +159,9 @@ def _stream(stream) -> Optional[int]:
 
 
 def make_desc(*, batch, d_model, n_head, d_head, qlen, mlen=0, clamp_len=-1, bias_clamp=-1, base=10000.0,
-              scale=0.0, dtype=XL_BF16, out_dtype=None, attn_splits=0, bias_kind=0) -> xl_attn_desc:
+              scale=0.0, dtype=XL_BF16, out_dtype=None, attn_splits=0, bias_kind=0, flags=0) -> xl_attn_desc:
     return xl_attn_desc(batch, d_model, n_head, d_head, qlen, mlen, clamp_len, bias_clamp, base, scale,
-                        dtype, dtype if out_dtype is None else out_dtype, attn_splits, bias_kind)
+                        dtype, dtype if out_dtype is None else out_dtype, attn_splits, bias_kind, flags)
 
 
 @dataclasses.dataclass

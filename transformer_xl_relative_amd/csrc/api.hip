@@ -75,6 +75,7 @@ int check_desc(const xl_attn_desc* d, int64_t mlen, bool need_dmodel) {
     if (d->bias_clamp > 65535) return fail(XL_UNSUPPORTED, "bias_clamp above 65535");
     if (d->bias_kind != XL_BIAS_CLAMP && d->bias_kind != XL_BIAS_T5)
         return fail(XL_BAD_SHAPE, "bias_kind must be XL_BIAS_CLAMP or XL_BIAS_T5");
+    if (d->flags & ~XL_REUSE_TABLE) return fail(XL_BAD_SHAPE, "unknown flags 0x%x", (unsigned)d->flags);
     if (d->attn_splits < 0 || d->attn_splits > xl::kMaxAttnSplits)
         return fail(XL_BAD_SHAPE, "attn_splits must be in [0, %d]", xl::kMaxAttnSplits);
     const int64_t klen = mlen + d->qlen;
@@ -95,8 +96,11 @@ xl::SplitPlan splits_of(const xl_attn_desc* d, int64_t mlen) {
     if (d->dtype != XL_BF16) return {0, 1};
     return xl::attn_bf16_split_plan(d->batch, d->n_head, d->qlen, mlen, d->attn_splits);
 }
+// (sized for every memory length up to mlen: a caller may size one workspace
+// for its longest memory and run shorter ones in it)
 size_t part_bytes_of(const xl_attn_desc* d, int64_t mlen) {
-    return d->dtype == XL_BF16 ? xl::attn_bf16_part_bytes(d->batch, d->n_head, d->qlen, splits_of(d, mlen)) : 0;
+    (void)mlen;
+    return d->dtype == XL_BF16 ? xl::attn_bf16_part_bytes_bound(d->batch, d->n_head, d->qlen, d->attn_splits) : 0;
 }
 
 int64_t n_rel_of(const xl_attn_desc* d, int64_t klen) {
@@ -164,9 +168,13 @@ int layer_forward(const xl_attn_desc* d, const xl_attn_weights* w, const void* h
     char* W = (char*)ws;
     hipError_t e;
 
-    // 1. sinusoid rows R_n, n < n_rel (a distance uses row min(delta, n_rel-1))
-    e = xl::launch_relpos(0, L.n_rel, D, -1, base, bf ? 1 : 0, W + L.rel, s);
-    if (e != hipSuccess) return hip_fail(e, "relpos launch");
+    // 1. sinusoid rows R_n, n < n_rel (a distance uses row min(delta, n_rel-1)),
+    // unless the caller vouches that the workspace holds this table already
+    const bool reuse = (d->flags & XL_REUSE_TABLE) != 0;
+    if (!reuse) {
+        e = xl::launch_relpos(0, L.n_rel, D, -1, base, bf ? 1 : 0, W + L.rel, s);
+        if (e != hipSuccess) return hip_fail(e, "relpos launch");
+    }
 
     // 2-4. the input projections as one grid: r = R W_r^T, q, and k, v over
     // [memory ; segment] (the attention folds u and v into q as it loads it)
@@ -178,7 +186,7 @@ int layer_forward(const xl_attn_desc* d, const xl_attn_weights* w, const void* h
         a.dh = (int)dh;
         a.b_split = 1 << 30;
     };
-    {   // r = R W_r^T -> [H, n_rel, dh]
+    if (!reuse) {   // r = R W_r^T -> [H, n_rel, dh]
         xl::GemmArgs& a = g[ng++];
         base_args(a);
         a.M = (int)L.n_rel; a.N = (int)HD; a.K = (int)D;
@@ -300,6 +308,8 @@ void dec_layout(const xl_attn_desc* d, int64_t mlen, int64_t d_inner, bool stack
 
 int check_decoder(const xl_attn_desc* d, int64_t d_inner, float eps, const xl_decoder_weights* w) {
     if (!w) return fail(XL_NULL_ARG, "weights is NULL");
+    if (d->flags & XL_REUSE_TABLE)
+        return fail(XL_UNSUPPORTED, "XL_REUSE_TABLE: every decoder layer writes its own table into the workspace");
     int st = check_weights(d, &w->attn);
     if (st != XL_OK) return st;
     if (!w->ln1_g || !w->ln1_b || !w->ln2_g || !w->ln2_b || !w->w1 || !w->b1 || !w->w2 || !w->b2)

@@ -782,6 +782,18 @@ SplitPlan attn_bf16_split_plan(int64_t B, int64_t H, int64_t qlen, int64_t mlen,
     return {0, 1};
 }
 
+size_t attn_bf16_part_bytes_bound(int64_t B, int64_t H, int64_t qlen, int forced) {
+    // the library's plan splits only when the query tiles leave compute units
+    // idle, and its workgroups (B*H per split of a tile) then fit the 256
+    // units: no tile takes more than 256 / (B*H) splits, whatever the memory
+    // length; a forced count caps every tile at that count
+    const int64_t nbh = B * H, nqt = (qlen + BQ - 1) / BQ;
+    int64_t smax = 0;
+    if (forced > 1) smax = forced;
+    else if (forced == 0 && nbh * nqt < kCUs) smax = kCUs / nbh < kMaxAttnSplits ? kCUs / nbh : kMaxAttnSplits;
+    return smax > 1 ? (size_t)smax * (size_t)(nbh * qlen) * (DH + 2) * sizeof(float) : 0;
+}
+
 size_t attn_bf16_part_bytes(int64_t B, int64_t H, int64_t qlen, const SplitPlan& p) {
     return p.steps > 0 ? (size_t)p.max * (size_t)(B * H * qlen) * (DH + 2) * sizeof(float) : 0;
 }

@@ -124,6 +124,9 @@ struct SplitPlan {
 };
 SplitPlan attn_bf16_split_plan(int64_t B, int64_t H, int64_t qlen, int64_t mlen, int forced);
 size_t attn_bf16_part_bytes(int64_t B, int64_t H, int64_t qlen, const SplitPlan& p);
+// bytes of the split partials for every memory length at once (a bound on the
+// split count that does not depend on mlen, so workspace sizes grow with mlen)
+size_t attn_bf16_part_bytes_bound(int64_t B, int64_t H, int64_t qlen, int forced);
 
 // fused attention for bf16 operands and d_head 64 (attn_bf16.hip)
 // ev0/ev1 (may be null): events the runtime timestamps at the start and end of
