@@ -34,6 +34,9 @@ flop count), cpu_baseline_layer the oracle's whole layer.
   python bench.py --backward [--workload NAME] [--steps K] [--warmup W] [--no-cpu]
                   # the attention-core gradients (xl_rel_attn_core_bwd) on the workload's
                   # shape: one JSON line with the kernel sequence's time and its rate
+  python bench.py --vendor-gemm [--workload NAME] [--launches N]
+                  # the layer's projection shapes as plain torch.matmul GEMMs (the ROCm
+                  # BLAS library): the platform's own rate on them, for context
 
 HBM traffic of the attention kernel comes from two rocprofv3 --pmc passes
 (FETCH_SIZE, then WRITE_SIZE) over this script with --copy-calib-mib, each
@@ -213,6 +216,9 @@ def main():
                     help="steps after the first skip the sinusoid and the R projection (XL_REUSE_TABLE; the "
                          "memory is full, so the table is that of the first step): a separate measurement, "
                          "the default step computes every row of the path")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="time the layer's projection shapes as plain torch.matmul (the ROCm BLAS library): "
+                         "context for the projection kernels' rates, not a path of the library")
     args = ap.parse_args()
     if args.summarize:
         summarize(args.summarize, args.copy_calib_mib)
@@ -232,6 +238,9 @@ def main():
     torch.cuda.set_device(0)
     if args.core:
         core_bench(args.core.split(","), args.launches, args.warmup)
+        return
+    if args.vendor_gemm:
+        vendor_gemm_bench(xl_inputs.WORKLOADS[args.workload], args.launches, args.warmup)
         return
     w = xl_inputs.WORKLOADS[args.workload]
     if w.dtype != "bf16":
@@ -536,6 +545,55 @@ def decoder_bench(w, n_layer, d_inner, K, warmup, no_cpu):
                                          f"{w.name}, fp64, {el:.1f} s wall"}
         res["gpu_over_cpu"] = round(value / cpu, 1)
     print(json.dumps(res), flush=True)
+
+
+def vendor_gemm_bench(w, launches, warmup):
+    """The layer's four projection products as plain row-major GEMMs through
+    torch.matmul (hipBLASLt on ROCm), `launches` calls each replayed from a
+    captured graph and timed with events: the rate the platform's own GEMM
+    reaches on these shapes, printed as one JSON line. No epilogue (head layout, V^T, ring) and no grouping: a
+    reference point for the projection kernels, whose times come from the
+    kernel traces of the layer step."""
+    import torch
+    D, HD = w.d_model, w.n_head * w.d_head
+    klen = w.qlen + w.mlen
+    n_rel = klen if w.clamp_len < 0 else min(klen, w.clamp_len + 1)
+    shapes = {"r": (n_rel, HD, D), "q": (w.batch * w.qlen, HD, D), "kv": (w.batch * klen, 2 * HD, D),
+              "o": (w.batch * w.qlen, D, HD)}
+    out = {"workload": w.name, "library": "torch.matmul (bf16 in, bf16 out), graph replay", "launches": launches}
+    g = torch.Generator(device="cuda").manual_seed(0)
+    for name, (M, N, K) in shapes.items():
+        a = torch.randn(M, K, device="cuda", generator=g).to(torch.bfloat16)
+        b = torch.randn(N, K, device="cuda", generator=g).to(torch.bfloat16)
+        bt = b.t()
+        c = torch.empty(M, N, device="cuda", dtype=torch.bfloat16)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(max(warmup, 3)):
+                torch.matmul(a, bt, out=c)
+        torch.cuda.current_stream().wait_stream(side)
+        # the calls replayed from a captured graph, so that the host's
+        # per-call cost does not pace the GPU
+        per_graph = 20
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(per_graph):
+                torch.matmul(a, bt, out=c)
+        replays = max(launches // per_graph, 1)
+        graph.replay()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(replays):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (replays * per_graph)
+        tf = 2.0 * M * N * K / (us * 1e-6) / 1e12
+        out[name] = {"M": M, "N": N, "K": K, "us": round(us, 3), "tflops": round(tf, 1),
+                     "frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)}
+    print(json.dumps(out), flush=True)
 
 
 def core_bench(names, launches, warmup):
