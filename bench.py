@@ -25,7 +25,8 @@ flop count), cpu_baseline_layer the oracle's whole layer.
                   # the fused attention alone (xl_rel_attn_core) per workload, warm and
                   # cold (1 GiB written between launches to evict the caches): one JSON
                   # line per workload with the median, p10 and p90 kernel times; NAME/tpN
-                  # is one GPU's share (n_head / N heads) under head sharding
+                  # is one GPU's share (n_head / N heads) under head sharding, NAME@mM the
+                  # workload with M memory rows
   python bench.py --summarize DIR [--copy-calib-mib M]   # markdown summary of rocprofv3 output under DIR
   python bench.py --decoder N [--d-inner F] [--workload NAME] [--steps K] [--warmup W] [--no-cpu]
                   # one segment step of an N-layer pre-LN decoder stack (xl_decoder_stack_step),
@@ -610,9 +611,13 @@ def core_bench(names, launches, warmup):
 
     scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     for name in names:
-        # "NAME/tpN": one GPU's share when the heads are sharded over N GPUs
+        # "NAME/tpN": one GPU's share when the heads are sharded over N GPUs;
+        # "NAME@mM": the workload with M memory rows (a sweep of the key count)
         base, _, tp = name.partition("/tp")
+        base, _, mem_rows = base.partition("@m")
         w = xl_inputs.WORKLOADS[base]
+        if mem_rows:
+            w = dataclass_replace(w, mlen=int(mem_rows))
         if tp:
             if w.n_head % int(tp):
                 raise SystemExit(f"{name}: {w.n_head} heads do not split over {tp} GPUs")
