@@ -110,15 +110,24 @@ def attn_min_bytes(w, mlen):
 
 
 def host_cpu_model():
-    """The host CPU's model name (lscpu's 'Model name', from /proc/cpuinfo)."""
+    """The host CPU's model name (lscpu's 'Model name', from /proc/cpuinfo),
+    with its family, model and stepping numbers (a virtualised host may give
+    only a short name)."""
+    fields = {}
     try:
         with open("/proc/cpuinfo") as fh:
             for line in fh:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                k, _, v = line.partition(":")
+                k = k.strip()
+                if k in ("model name", "cpu family", "model", "stepping") and k not in fields:
+                    fields[k] = v.strip()
+                if not line.strip() and fields:
+                    break
     except OSError:
         pass
-    return "unknown"
+    name = fields.get("model name", "unknown")
+    nums = [f"{k} {fields[k]}" for k in ("cpu family", "model", "stepping") if k in fields]
+    return f"{name} ({', '.join(nums)})" if nums else name
 
 
 def roofline(flops, nbytes, seconds, bound=None):
