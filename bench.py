@@ -71,8 +71,8 @@ ATTN_SOURCES = ("transformer_xl_relative_amd/csrc/attn_bf16.hip", "transformer_x
 # HBM bytes per launch of the fused attention kernel (calibrated FETCH_SIZE and
 # WRITE_SIZE, see profiles/attn_bf16_kernel_<workload>_pmc_traffic.md).
 TRAFFIC = {
-    "large_bf16": {"sha256": "b8b4fd930c0beebf61b652712c2cafebff24299842d13b3b344e82f6bdfb4d30",
-                   "bytes": 39647667, "fetch_bytes": 33356211, "write_bytes": 6291456},
+    "large_bf16": {"sha256": "c71c37b2ee79801441896dce9ced2799767ac1986f9972f09170d7a379d7a57b",
+                   "bytes": 39651350, "fetch_bytes": 33359894, "write_bytes": 6291456},
 }
 
 

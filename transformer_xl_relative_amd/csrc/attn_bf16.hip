@@ -649,14 +649,17 @@ __global__ void __launch_bounds__(NT, 2) attn_bf16_kernel(AttnArgs a) {
 // M = max_s m_s (an empty split has m_s = -inf, l_s = 0, O_s = 0). The grid
 // covers the queries from i_first on (the tiles that were split: the split
 // count grows with the tile index); a thread produces 4 consecutive outputs of
-// one query. The splits are read in groups of MG with all loads of a group in
-// flight together, and the running maximum moves between groups.
-constexpr int MG = 16;
+// one query. The splits are read in groups of MG (the launch's largest split
+// count rounded up to 4, 8 or 16) with all loads of a group in flight
+// together, and the running maximum moves between groups. Workgroups of one
+// wave spread the few thousand threads over every compute unit.
+constexpr int MWG = 64;
 
-__global__ void __launch_bounds__(256) attn_merge_kernel(AttnArgs a, int i_first) {
+template <int MG>
+__global__ void __launch_bounds__(MWG) attn_merge_kernel(AttnArgs a, int i_first) {
     const int nq = a.qlen - i_first;
     const int64_t nrow = (int64_t)a.B * a.H * nq;
-    const int64_t idx = (int64_t)__builtin_amdgcn_workgroup_id_x() * 256 + __builtin_amdgcn_workitem_id_x();
+    const int64_t idx = (int64_t)__builtin_amdgcn_workgroup_id_x() * MWG + __builtin_amdgcn_workitem_id_x();
     if (idx >= nrow * 16) return;
     const int c = (int)(idx & 15);
     const int64_t bh = (idx >> 4) / nq;
@@ -740,8 +743,11 @@ hipError_t launch_bf16(const AttnArgs& a, hipStream_t s, hipEvent_t ev0, hipEven
     if (e != hipSuccess) return e;
     const int i_first = qt_first * BQ;
     const int64_t threads = (int64_t)a.B * a.H * (a.qlen - i_first) * 16;
-    hipExtLaunchKernelGGL(attn_merge_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0u, s,
-                          (hipEvent_t) nullptr, ev1, 0u, a, i_first);
+    const auto merge = a.split_max <= 4   ? attn_merge_kernel<4>
+                       : a.split_max <= 8 ? attn_merge_kernel<8>
+                                          : attn_merge_kernel<16>;
+    hipExtLaunchKernelGGL(merge, dim3((unsigned)((threads + MWG - 1) / MWG)), dim3(MWG), 0u, s, (hipEvent_t) nullptr,
+                          ev1, 0u, a, i_first);
     return hipGetLastError();
 }
 
