@@ -350,3 +350,55 @@ def test_core_backward_rejects_bad_arguments():
     assert call(dq=FAKE[0]) == xl.XL_BAD_SHAPE            # dq aliases q
     assert call(dk=FAKE[9] + 64) == xl.XL_BAD_SHAPE       # dk overlaps dq
     assert xl.xl_rel_attn_core_bwd_workspace_size(_desc(qlen=0)) == 0
+
+
+BIG = 1 << 62   # a product of two such sizes overflows int64
+
+
+@pytest.mark.parametrize("field", ["batch", "n_head", "qlen", "mlen", "d_model"])
+def test_huge_sizes_rejected_without_overflow(field):
+    # every caller size is bounded on its own before any product of sizes is
+    # formed; the sanitizer run of this file catches a product that overflows
+    lib = xl.lib()
+    d = _desc(**{field: BIG})
+    assert _fwd(d) == xl.XL_UNSUPPORTED
+    assert xl.xl_rel_attn_workspace_size(d) == 0
+    assert xl.xl_rel_attn_core_workspace_size(d) == (0 if field != "d_model" else
+                                                    xl.xl_rel_attn_core_workspace_size(_desc()))
+    assert xl.xl_rel_attn_core_bwd_workspace_size(d) == (0 if field != "d_model" else
+                                                        xl.xl_rel_attn_core_bwd_workspace_size(_desc()))
+    assert xl.xl_decoder_layer_workspace_size(d, 2048) == 0
+    assert xl.xl_decoder_stack_workspace_size(d, 2048) == 0
+    if field != "mlen":   # the segment step takes its memory length from the FIFO
+        ds = _desc(mlen=0, **{field: BIG})
+        f = xl.xl_mem_fifo(FAKE[12], 128, 0, 0)
+        assert lib.xl_segment_step(ctypes.byref(ds), ctypes.byref(_weights()), FAKE[8], ctypes.byref(f), FAKE[10],
+                                   FAKE[11], 1 << 40, None) == xl.XL_UNSUPPORTED
+
+
+def test_huge_fifo_and_ring_rejected_without_overflow():
+    lib = xl.lib()
+    w = _weights()
+    d = _desc(mlen=0, batch=1 << 20)
+    # batch x mlen_max rows beyond the 32-bit row range
+    f = xl.xl_mem_fifo(FAKE[12], 1 << 20, 0, 0)
+    assert lib.xl_segment_step(ctypes.byref(d), ctypes.byref(w), FAKE[8], ctypes.byref(f), FAKE[10], FAKE[11],
+                               1 << 40, None) == xl.XL_UNSUPPORTED
+    assert b"mlen_max" in lib.xl_last_error()
+    f = xl.xl_mem_fifo(FAKE[12], BIG, 0, 0)
+    assert lib.xl_segment_step(ctypes.byref(d), ctypes.byref(w), FAKE[8], ctypes.byref(f), FAKE[10], FAKE[11],
+                               1 << 40, None) == xl.XL_UNSUPPORTED
+    # key ring: mlen_max + qlen would overflow; batch x cap beyond the row range
+    for kw in (dict(mlen_max=(1 << 63) - 8, cap=256), dict(mlen_max=128, cap=BIG)):
+        kv = xl.xl_kv_fifo(**{**dict(k=FAKE[12], vt=FAKE[13], len=0, head=0), **kw})
+        assert lib.xl_segment_step_kv(ctypes.byref(_desc(mlen=0)), ctypes.byref(w), FAKE[8], ctypes.byref(kv),
+                                      FAKE[10], FAKE[11], 1 << 40, None) == xl.XL_UNSUPPORTED
+    kv = xl.xl_kv_fifo(k=FAKE[12], vt=FAKE[13], cap=1 << 16, mlen_max=128, len=0, head=0)
+    assert lib.xl_segment_step_kv(ctypes.byref(d), ctypes.byref(w), FAKE[8], ctypes.byref(kv), FAKE[10], FAKE[11],
+                                  1 << 40, None) == xl.XL_UNSUPPORTED
+    # decoder: d_inner far beyond the feed-forward's limit
+    assert xl.xl_decoder_layer_workspace_size(_desc(), BIG) == 0
+    assert xl.xl_decoder_stack_workspace_size(_desc(), BIG) == 0
+    # the plain backward's score matrix beyond 2^40 elements
+    db = _desc(batch=4096, n_head=16, qlen=8192, mlen=0)   # 2^42 scores
+    assert xl.xl_rel_attn_core_bwd_workspace_size(db) == 0

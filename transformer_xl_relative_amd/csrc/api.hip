@@ -56,6 +56,9 @@ int check_desc(const xl_attn_desc* d, int64_t mlen, bool need_dmodel) {
     if (d->batch < 1 || d->n_head < 1 || d->qlen < 1 || mlen < 0)
         return fail(XL_BAD_SHAPE, "batch, n_head, qlen must be >= 1 and mlen >= 0 (got %lld, %lld, %lld, %lld)",
                     (long long)d->batch, (long long)d->n_head, (long long)d->qlen, (long long)mlen);
+    // every size on its own first, so that the products below cannot overflow
+    if (d->batch > kI32 || d->n_head > kI32 || d->qlen > kI32 || mlen > kI32)
+        return fail(XL_UNSUPPORTED, "batch, n_head, qlen and mlen must each be below 2^31");
     if (d->dtype != XL_BF16 && d->dtype != XL_F32) return fail(XL_BAD_SHAPE, "dtype must be XL_F32 or XL_BF16");
     if (!((d->dtype == XL_BF16 && d->d_head == 64) || (d->dtype == XL_F32 && d->d_head == 8)))
         return fail(XL_UNSUPPORTED, "supported (dtype, d_head): (bf16, 64), (f32, 8); got (%d, %lld)", (int)d->dtype,
@@ -81,7 +84,7 @@ int check_desc(const xl_attn_desc* d, int64_t mlen, bool need_dmodel) {
     const int64_t klen = mlen + d->qlen;
     const int64_t hd = d->n_head * d->d_head;
     // every element count a kernel indexes with 32-bit arithmetic must fit
-    if (klen > kI32 / 128 || d->batch * klen > kI32 / 2 || hd > 65536 || d->batch * d->n_head > kI32 / 64 ||
+    if (klen > kI32 / 128 || d->batch > kI32 / 2 / klen || hd > 65536 || d->batch > kI32 / 64 / d->n_head ||
         (double)d->batch * d->n_head * klen * d->d_head > 9.0e15)
         return fail(XL_UNSUPPORTED, "problem too large for the 32-bit element offsets of the kernels");
     if (d->batch * d->n_head * ((d->qlen + 127) / 128) > kI32) return fail(XL_UNSUPPORTED, "grid too large");
@@ -394,6 +397,12 @@ int check_fifo(const xl_mem_fifo* f) {
     return XL_OK;
 }
 
+// a FIFO's rows across the batch, bounded like the key rows (after check_desc)
+int check_fifo_rows(const xl_attn_desc* d, const xl_mem_fifo* f) {
+    if (f->mlen_max > kI32 / 2 / d->batch) return fail(XL_UNSUPPORTED, "batch * fifo->mlen_max too large");
+    return XL_OK;
+}
+
 // the FIFO update of a segment step: row t of h lands at ring row
 // (head + len + t) % mlen_max; only the last min(qlen, mlen_max) rows survive
 xl::RowCopy fifo_copy(const xl_attn_desc* d, const xl_mem_fifo* f, const void* h) {
@@ -560,6 +569,7 @@ int xl_segment_step(const xl_attn_desc* desc, const xl_attn_weights* w, const vo
     int st = check_fifo(fifo);
     if (st != XL_OK) return st;
     if ((st = check_desc(desc, fifo->len, true)) != XL_OK) return st;
+    if ((st = check_fifo_rows(desc, fifo)) != XL_OK) return st;
     if ((st = check_weights(desc, w)) != XL_OK) return st;
     if (!h || !out || !ws) return fail(XL_NULL_ARG, "h, out and ws must be non-NULL");
     const size_t es = esize(desc->dtype);
@@ -612,12 +622,13 @@ int xl_segment_step_kv(const xl_attn_desc* desc, const xl_attn_weights* w, const
     if (st != XL_OK) return st;
     if (desc->dtype != XL_BF16) return fail(XL_UNSUPPORTED, "the key ring path is bf16 only");
     const int64_t q = desc->qlen, M = kv->mlen_max, C = kv->cap;
+    if (M > kI32 / 128 || C > kI32 / 128) return fail(XL_UNSUPPORTED, "cap or mlen_max too large");
     if (M < 1 || kv->len < 0 || kv->len > M || kv->head < 0 || kv->head >= C || C < M + q)
         return fail(XL_BAD_SHAPE, "kv state invalid (cap %lld, mlen_max %lld, len %lld, head %lld, qlen %lld)",
                     (long long)C, (long long)M, (long long)kv->len, (long long)kv->head, (long long)q);
     if (C % 8 || M % 8 || q % 8 || kv->len % 8 || kv->head % 8)
         return fail(XL_UNSUPPORTED, "the key ring needs cap, mlen_max, len, head and qlen multiples of 8");
-    if (C > kI32 / 128) return fail(XL_UNSUPPORTED, "cap too large");
+    if (C > kI32 / 2 / desc->batch) return fail(XL_UNSUPPORTED, "batch * cap too large");
     if ((st = check_weights(desc, w)) != XL_OK) return st;
     if (!h || !out || !ws) return fail(XL_NULL_ARG, "h, out and ws must be non-NULL");
     const size_t es = esize(desc->dtype);
@@ -647,6 +658,7 @@ size_t xl_rel_attn_core_bwd_workspace_size(const xl_attn_desc* desc) {
     if (!desc || check_desc(desc, desc->mlen, false) != XL_OK) return 0;
     const int64_t rows = desc->batch * desc->n_head * desc->qlen;
     const int64_t klen = desc->mlen + desc->qlen;
+    if (rows > (((int64_t)1 << 40) / klen)) return 0;   // the call rejects it too
     const int64_t dr_rows = n_rel_of(desc, klen) - 1;   // per-batch-element partial sums of dr
     const int64_t kblocks = (klen + 31) / 32;   // softmax partials per query row and block of 32 keys
     return 2 * align_up((size_t)(rows * klen) * 4) + 2 * align_up((size_t)(rows * desc->d_head) * 4) +
@@ -672,7 +684,7 @@ int xl_rel_attn_core_bwd(const xl_attn_desc* desc, const void* q, const void* k,
     if (n_rel < need) return fail(XL_BAD_SHAPE, "r has %lld rows, needs %lld", (long long)n_rel, (long long)need);
     if (n_rel > kI32 / 64) return fail(XL_UNSUPPORTED, "r has too many rows");
     const int64_t rows = desc->batch * desc->n_head * desc->qlen;
-    if (rows * klen > ((int64_t)1 << 40)) return fail(XL_UNSUPPORTED, "problem too large for the plain backward");
+    if (rows > (((int64_t)1 << 40) / klen)) return fail(XL_UNSUPPORTED, "problem too large for the plain backward");
     const size_t need_ws = xl_rel_attn_core_bwd_workspace_size(desc);
     if (!ws || ws_bytes < need_ws)
         return fail(XL_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", ws ? ws_bytes : 0, need_ws);
@@ -723,8 +735,13 @@ int xl_rel_attn_core_bwd(const xl_attn_desc* desc, const void* q, const void* k,
     return XL_OK;
 }
 
+// d_inner as check_decoder bounds it (the size functions have no weights to check)
+bool d_inner_ok(const xl_attn_desc* d, int64_t d_inner) {
+    return d_inner >= 1 && d_inner <= 262144 && d->batch * d->qlen * d_inner <= kI32;
+}
+
 size_t xl_decoder_layer_workspace_size(const xl_attn_desc* desc, int64_t d_inner) {
-    if (!desc || check_desc(desc, desc->mlen, true) != XL_OK || d_inner < 1) return 0;
+    if (!desc || check_desc(desc, desc->mlen, true) != XL_OK || !d_inner_ok(desc, d_inner)) return 0;
     DecLayout L;
     dec_layout(desc, desc->mlen, d_inner, false, &L);
     return L.total;
@@ -752,7 +769,7 @@ int xl_decoder_layer_fwd(const xl_attn_desc* desc, int64_t d_inner, float ln_eps
 }
 
 size_t xl_decoder_stack_workspace_size(const xl_attn_desc* desc, int64_t d_inner) {
-    if (!desc || check_desc(desc, desc->mlen, true) != XL_OK || d_inner < 1) return 0;
+    if (!desc || check_desc(desc, desc->mlen, true) != XL_OK || !d_inner_ok(desc, d_inner)) return 0;
     DecLayout L;
     dec_layout(desc, desc->mlen, d_inner, true, &L);
     return L.total;
@@ -767,13 +784,15 @@ int xl_decoder_stack_step(const xl_attn_desc* desc, int64_t d_inner, float ln_ep
     if (!w || !fifos) return fail(XL_NULL_ARG, "weights and fifos must be non-NULL");
     if (!h || !out || !ws) return fail(XL_NULL_ARG, "h, out and ws must be non-NULL");
     if ((uintptr_t)h % 16) return fail(XL_UNSUPPORTED, "h must be 16-byte aligned");
+    int st = check_desc(desc, desc->mlen, true);   // the sizes, before any product of them
+    if (st != XL_OK) return st;
     const float eps = ln_eps == 0.f ? 1e-5f : ln_eps;
     const size_t es = esize(desc->dtype);
     const size_t h_bytes = (size_t)(desc->batch * desc->qlen * desc->d_model) * es;
     const size_t out_bytes = (size_t)(desc->batch * desc->qlen * desc->d_model) * esize(desc->out_dtype);
-    int st;
     for (int64_t n = 0; n < n_layer; ++n) {
         if ((st = check_fifo(&fifos[n])) != XL_OK) return st;
+        if ((st = check_fifo_rows(desc, &fifos[n])) != XL_OK) return st;
         if (fifos[n].len > desc->mlen)
             return fail(XL_BAD_SHAPE, "fifo %lld holds %lld rows, more than desc->mlen = %lld", (long long)n,
                         (long long)fifos[n].len, (long long)desc->mlen);
