@@ -71,7 +71,7 @@ ATTN_SOURCES = ("transformer_xl_relative_amd/csrc/attn_bf16.hip", "transformer_x
 # HBM bytes per launch of the fused attention kernel (calibrated FETCH_SIZE and
 # WRITE_SIZE, see profiles/attn_bf16_kernel_<workload>_pmc_traffic.md).
 TRAFFIC = {
-    "large_bf16": {"sha256": "c71c37b2ee79801441896dce9ced2799767ac1986f9972f09170d7a379d7a57b",
+    "large_bf16": {"sha256": "8397f57ff7963cc378b5e89db565d9fe7192daae74de05f4821209ed7030aadf",
                    "bytes": 39651350, "fetch_bytes": 33359894, "write_bytes": 6291456},
 }
 

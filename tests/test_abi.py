@@ -402,3 +402,12 @@ def test_huge_fifo_and_ring_rejected_without_overflow():
     # the plain backward's score matrix beyond 2^40 elements
     db = _desc(batch=4096, n_head=16, qlen=8192, mlen=0)   # 2^42 scores
     assert xl.xl_rel_attn_core_bwd_workspace_size(db) == 0
+
+
+def test_key_count_limit_boundary():
+    # the largest key count per head the kernels' 32-bit K offsets allow is
+    # accepted, one more key is refused
+    klen_max = (2 ** 31 - 1) // 128
+    ok = _desc(batch=1, n_head=1, qlen=64, mlen=klen_max - 64)
+    assert xl.xl_rel_attn_core_workspace_size(ok) > 0
+    assert xl.xl_rel_attn_core_workspace_size(_desc(batch=1, n_head=1, qlen=64, mlen=klen_max - 63)) == 0

@@ -224,7 +224,9 @@ __global__ void __launch_bounds__(NT, 2) attn_bf16_kernel(AttnArgs a) {
     const int kvoff = krho * 128 + (((lane & 7) ^ ((krho >> 1) & 7)) << 4);
     const int kj0 = BKY * S0 + krho + kv_head;                      // ring row of this lane's key in step 0
     const int vrho = 16 * wave + (lane >> 2);
-    const int vvoff = vrho * a.ldv * 2;
+    // (byte offsets within a head's V^T reach 128 ldv, past 2^31 for the
+    // largest accepted ldv: unsigned, as the instruction's offset is)
+    const uint32_t vvoff = (uint32_t)vrho * (uint32_t)a.ldv * 2u;
     const int vj0 = BKY * S0 + 8 * ((lane & 3) ^ ((vrho >> 2) & 3)) + kv_head;     // first of its 8 keys
     // shared band block g (local) holds distances gs - 32 g - row, gs = mlen + i0 + 127 - 32 S0;
     // wave w's position block beta is band block beta + 3 - w
@@ -247,15 +249,15 @@ __global__ void __launch_bounds__(NT, 2) attn_bf16_kernel(AttnArgs a) {
     // (the 8 keys of a piece are consecutive ring columns: kv_head and
     // kv_rows are multiples of 8)
     auto dma_v = [&](int s, int slot) __attribute__((always_inline)) {
-        int voff;
+        uint32_t voff;
         if constexpr (RING) {
             int p = vj0 + BKY * s;
             p -= p >= kcap ? kcap : 0;
-            voff = vvoff + 2 * p;
+            voff = vvoff + 2u * (uint32_t)p;
         } else {
-            voff = vvoff + 2 * vj0 + s * (BKY * 2);
+            voff = vvoff + 2u * (uint32_t)(vj0 + BKY * s);
         }
-        raw_buffer_load_lds(vrs, lds_ptr(lds0 + OFF_V + slot * TILE + wave * 1024), 16, voff, 0, 0, 0);
+        raw_buffer_load_lds(vrs, lds_ptr(lds0 + OFF_V + slot * TILE + wave * 1024), 16, (int)voff, 0, 0, 0);
     };
     // band block g into the 4 KB slot at LDS offset `at`
     auto dma_band_at = [&](int g, int at) __attribute__((always_inline)) {

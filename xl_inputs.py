@@ -224,3 +224,57 @@ def core_inputs(*, batch: int, n_head: int, d_head: int, qlen: int, mlen: int, n
     if bias_clamp >= 0:
         out["beta"] = _normal(rng, (bias_rows(bias_clamp, bias_kind), n_head), 0.3)
     return {k: Tensor(a, dtype) for k, a in out.items()}
+
+
+def long_key_core_inputs(*, qlen: int, mlen: int, n_rows: int, seed: int, probes: dict, pool: int = 4096) -> dict:
+    """Inputs for the attention core over a very long key range (one batch
+    element, one head, d_head 64, bf16), drawn in seconds even for tens of
+    millions of keys, and built so that a sampled output shows a key or value
+    read from the wrong place:
+
+    * a shared direction c and one direction w_i per probed query row i:
+      seeded, orthonormal;
+    * query row i: 3 c + 3 w_i (probed rows only) + N(0, 0.3);
+    * keys and values: rows of two seeded pools of `pool` N(0, 0.6) rows, one
+      seeded index per key; every key then has 55 c subtracted, so its scaled
+      content score is near -20 for every query and all of them together weigh
+      little against one probe;
+    * probes {query row i: key j}: key j is 20 w_i and its value a seeded N(0, 1)
+      row, so that query row i, when it sees key j, puts almost all of its
+      weight there (scaled score about 7.5, against about 0 for the other
+      probes), and none when the causal mask hides key j from it;
+    * r (n_rows distance rows) N(0, 0.6); u and v N(0, 0.3).
+
+    Draw order: c and the directions, q noise, the two pools, the key index, the
+    value index, the probe values, r, u, v. Returns Tensor objects for q, r, u
+    and vb, and for k and v the bf16 bits [k_len, 64] ("k_bits", "v_bits") and
+    their exact values [1, 1, k_len, 64] as float64 ("k", "v")."""
+    dh = 64
+    k_len = qlen + mlen
+    rows = sorted(probes)
+    assert all(0 <= i < qlen for i in rows) and all(0 <= probes[i] < k_len for i in rows)
+    rng = np.random.default_rng(seed)
+    basis, _ = np.linalg.qr(rng.standard_normal((dh, len(rows) + 1)))
+    c, w = basis[:, 0], {i: basis[:, 1 + n] for n, i in enumerate(rows)}
+    q = 3.0 * c[None, :] + rng.standard_normal((qlen, dh)) * 0.3
+    for i in rows:
+        q[i] += 3.0 * w[i]
+    pools = [bf16_bits(_normal(rng, (pool, dh), 0.6) - (55.0 * c[None, :] if n == 0 else 0.0)) for n in range(2)]
+    out = {}
+    for name, bits in (("k", pools[0]), ("v", pools[1])):
+        idx = rng.integers(0, pool, size=k_len)
+        out[name + "_bits"] = bits[idx]
+        out[name] = bf16_to_f32(bits).astype(np.float64)[idx][None, None]
+    vals = bf16_bits(rng.standard_normal((len(rows), dh)).astype(np.float32))
+    for n, i in enumerate(rows):
+        j = probes[i]
+        kb = bf16_bits((20.0 * w[i]).astype(np.float32))
+        out["k_bits"][j] = kb
+        out["k"][0, 0, j] = bf16_to_f32(kb)
+        out["v_bits"][j] = vals[n]
+        out["v"][0, 0, j] = bf16_to_f32(vals[n])
+    out["q"] = Tensor(q.astype(np.float32)[None, None], "bf16")
+    out["r"] = Tensor(_normal(rng, (1, n_rows, dh), 0.6), "bf16")
+    out["u"] = Tensor(_normal(rng, (1, dh), 0.3), "bf16")
+    out["vb"] = Tensor(_normal(rng, (1, dh), 0.3), "bf16")
+    return out
