@@ -1,9 +1,11 @@
-"""The fused attention at the largest key count per head that the library
-accepts: klen = (2^31 - 1) // 128 = 16,777,215, so that a head's K rows of
-128 bytes stay within 32-bit offsets, and V^T rows of 16,777,224 columns,
-whose byte offsets pass 2^31. One batch element and head, 64 queries, the
-clamped distance table of the long-memory workload, the library's own key
-split (64 workgroups of 8192 steps).
+"""The path at the largest key count per head that the library accepts:
+klen = (2^31 - 1) // 128 = 16,777,215, so that a head's K rows of 128 bytes
+stay within 32-bit offsets.
+
+The fused attention alone, with V^T rows of 16,777,224 columns, whose byte
+offsets pass 2^31: one batch element and head, 64 queries, the clamped
+distance table of the long-memory workload, the library's own key split (64
+workgroups of 8192 steps).
 
 Keys and values come from seeded pools (xl_inputs.long_key_core_inputs)
 with one dominant probe key per sampled query row, placed where an offset
@@ -12,6 +14,12 @@ boundary, both sides of 2^23, near 2^24, the last two keys (the last one in
 the ragged final tile) and one key just past a row's causal limit, which
 must get no weight. The sampled rows are compared with the oracle, which
 sums over every key.
+
+One segment step on a full FIFO of that many memory rows (d_model 32: one
+head, projections with a K of 32), whose ring starts mid-buffer and wraps:
+the projected keys and values at the rows where an offset error would first
+show against the oracle's projection of those rows, the FIFO update bit for
+bit, and a finite output.
 """
 import time
 
@@ -71,3 +79,43 @@ def test_core_max_key_count(T):
                                scale=0.125, clamp_len=CLAMP, qpos=[MLEN + i for i in rows])
     print(f"  oracle done at {time.time() - t0:.1f} s", flush=True)
     gu.compare("max key count, sampled rows", got, ref, dtype="bf16")
+
+
+@pytest.mark.timeout(600)
+def test_segment_step_max_memory(T):
+    import transformer_xl_relative_amd as xl
+    D = 32
+    t0 = time.time()
+    li = xl_inputs.long_memory_layer_inputs(d_model=D, n_head=1, qlen=QLEN, mlen=MLEN, seed=29)
+    head0 = 1_000_003
+    ring_np = np.roll(li["mem_bits"], head0, axis=1)   # logical row j at physical row (head0 + j) % MLEN
+    ring = T.from_numpy(ring_np.view(np.int16)).cuda().view(T.bfloat16)
+    del ring_np
+    print(f"\n  inputs drawn in {time.time() - t0:.1f} s", flush=True)
+    fifo = xl.xl_mem_fifo(ring.data_ptr(), MLEN, MLEN, head0)
+    desc = xl.make_desc(batch=1, d_model=D, n_head=1, d_head=64, qlen=QLEN, mlen=MLEN, clamp_len=CLAMP,
+                        dtype=xl.XL_BF16, out_dtype=xl.XL_F32)
+    ws = T.empty(xl.xl_rel_attn_workspace_size(desc), dtype=T.uint8, device="cuda")
+    lay = xl.xl_rel_attn_workspace_layout(desc)
+    w = xl.Weights(*(gu.dev(li[k]) for k in ("w_q", "w_k", "w_v", "w_r", "w_o", "u", "v")), bias_table=None)
+    out = T.empty((1, QLEN, D), dtype=T.float32, device="cuda")
+    xl.xl_segment_step(desc, w, gu.dev(li["h"]), fifo, out, ws)
+    T.cuda.synchronize()
+    print(f"  GPU done at {time.time() - t0:.1f} s", flush=True)
+    assert (fifo.len, fifo.head) == (MLEN, (head0 + QLEN) % MLEN)
+    assert bool(T.isfinite(out).all())
+    # keys and values as projected, at the rows where an offset error would first show
+    rows = [0, 1, 2 ** 23 - 1, 2 ** 23, MLEN - 1, MLEN, KLEN - 1]
+    x = np.stack([li["mem_pool"].f64[li["mem_idx"][j]] if j < MLEN else li["h"].f64[0, j - MLEN] for j in rows])
+    kview = ws[lay.k:lay.k + KLEN * 64 * 2].view(T.bfloat16).view(KLEN, 64)
+    vview = ws[lay.vt:lay.vt + 64 * lay.ldv * 2].view(T.bfloat16).view(64, lay.ldv)
+    gu.compare("max memory: projected keys", gu.host64(kview[rows]), oracle.linear(x, li["w_k"].f64), dtype="bf16")
+    gu.compare("max memory: projected values", gu.host64(vview[:, rows].T), oracle.linear(x, li["w_v"].f64),
+               dtype="bf16")
+    # the FIFO: the segment's rows replaced the oldest QLEN rows, bit for bit; the others stay
+    h_bits = li["h"].bits[0]
+    new = [(head0 + t) % MLEN for t in range(QLEN)]
+    assert np.array_equal(gu.bits_u16(ring[0, new]), h_bits)
+    kept = [QLEN, QLEN + 2 ** 23, MLEN - 1]
+    got_kept = gu.bits_u16(ring[0, [(head0 + j) % MLEN for j in kept]])
+    assert np.array_equal(got_kept, li["mem_bits"][0, kept])

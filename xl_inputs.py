@@ -278,3 +278,25 @@ def long_key_core_inputs(*, qlen: int, mlen: int, n_rows: int, seed: int, probes
     out["u"] = Tensor(_normal(rng, (1, dh), 0.3), "bf16")
     out["vb"] = Tensor(_normal(rng, (1, dh), 0.3), "bf16")
     return out
+
+
+def long_memory_layer_inputs(*, d_model: int, n_head: int, qlen: int, mlen: int, seed: int, pool: int = 4096) -> dict:
+    """Layer inputs (one batch element, bf16, d_head 64) with a memory of tens
+    of millions of rows, drawn in seconds: each memory row is a row of a seeded
+    pool of `pool` N(0, 1) rows, picked by a seeded index per memory row; h
+    N(0, 1); W_q, W_k, W_v, W_r, W_o and u, v N(0, 0.02), the workloads' recipe.
+    Draw order: h, the pool, the index, W_q, W_k, W_v, W_r, W_o, u, v. Returns
+    Tensor objects for h, the pool ("mem_pool") and the weights, the index
+    ("mem_idx") and the memory's bf16 bits [1, mlen, d_model] ("mem_bits")."""
+    rng = np.random.default_rng(seed)
+    hd = n_head * 64
+    out = {"h": Tensor(_normal(rng, (1, qlen, d_model), 1.0), "bf16")}
+    out["mem_pool"] = Tensor(_normal(rng, (pool, d_model), 1.0), "bf16")
+    out["mem_idx"] = rng.integers(0, pool, size=mlen)
+    out["mem_bits"] = out["mem_pool"].bits[out["mem_idx"]][None]
+    for name, shape in (("w_q", (hd, d_model)), ("w_k", (hd, d_model)), ("w_v", (hd, d_model)),
+                        ("w_r", (hd, d_model)), ("w_o", (d_model, hd))):
+        out[name] = Tensor(_normal(rng, shape, 0.02), "bf16")
+    out["u"] = Tensor(_normal(rng, (n_head, 64), 0.02), "bf16")
+    out["v"] = Tensor(_normal(rng, (n_head, 64), 0.02), "bf16")
+    return out
