@@ -15,6 +15,14 @@ the ragged final tile) and one key just past a row's causal limit, which
 must get no weight. The sampled rows are compared with the oracle, which
 sums over every key.
 
+One key-ring segment step on a full ring of the largest capacity under that
+limit (16,777,208 slots, a multiple of 8), starting mid-buffer and wrapping:
+the memory keys and values are the probe construction above, the layer's
+query and output projections the identity (d_model 64, one head), so the
+sampled outputs are the probed attention rows, checked against the oracle
+over every key; and the segment's projected keys and values land in the
+ring at the wrapped rows.
+
 One segment step on a full FIFO of that many memory rows (d_model 32: one
 head, projections with a K of 32), whose ring starts mid-buffer and wraps:
 the projected keys and values at the rows where an offset error would first
@@ -119,3 +127,53 @@ def test_segment_step_max_memory(T):
     kept = [QLEN, QLEN + 2 ** 23, MLEN - 1]
     got_kept = gu.bits_u16(ring[0, [(head0 + j) % MLEN for j in kept]])
     assert np.array_equal(got_kept, li["mem_bits"][0, kept])
+
+
+@pytest.mark.timeout(600)
+def test_segment_step_kv_max_ring(T):
+    import transformer_xl_relative_amd as xl
+    cap = KLEN // 8 * 8
+    mem = cap - QLEN                 # the memory is full: len = mlen_max
+    head0 = 1_000_008
+    probes = {0: 0, 1: 262143, 2: 262144, 31: 2 ** 23 - 1, 32: 2 ** 23, 33: mem - 1024, 63: mem - 1}
+    t0 = time.time()
+    ci = xl_inputs.long_key_core_inputs(qlen=QLEN, mlen=mem, n_rows=2, seed=31, probes=probes)
+    wt = xl_inputs.identity_head_weights(seed=37)
+    nan = np.full((QLEN, 64), 0x7FC0, np.uint16)          # ring slots the step writes before reading
+    kr = np.roll(np.concatenate([ci["k_bits"][:mem], nan]), head0, axis=0)
+    vr = np.roll(np.concatenate([ci["v_bits"][:mem], nan]).T, head0, axis=1)
+    up = lambda bits: T.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(T.bfloat16)
+    kr_d, vr_d = up(kr), up(vr)
+    del kr, vr
+    print(f"\n  inputs drawn in {time.time() - t0:.1f} s", flush=True)
+    kv = xl.xl_kv_fifo(kr_d.data_ptr(), vr_d.data_ptr(), cap, mem, mem, head0)
+    desc = xl.make_desc(batch=1, d_model=64, n_head=1, d_head=64, qlen=QLEN, mlen=0, clamp_len=CLAMP,
+                        dtype=xl.XL_BF16, out_dtype=xl.XL_F32)
+    dd = xl.make_desc(batch=1, d_model=64, n_head=1, d_head=64, qlen=QLEN, mlen=mem, clamp_len=CLAMP,
+                      dtype=xl.XL_BF16, out_dtype=xl.XL_F32)
+    ws = T.empty(xl.xl_segment_step_kv_workspace_size(dd), dtype=T.uint8, device="cuda")
+    w = xl.Weights(*(gu.dev(x) for x in (wt["w_q"], wt["w_k"], wt["w_v"], wt["w_r"], wt["w_o"], ci["u"], ci["vb"])),
+                   bias_table=None)
+    h = gu.dev(ci["q"]).view(1, QLEN, 64)
+    out = T.empty((1, QLEN, 64), dtype=T.float32, device="cuda")
+    xl.xl_segment_step_kv(desc, w, h, kv, out, ws)
+    T.cuda.synchronize()
+    print(f"  GPU done at {time.time() - t0:.1f} s", flush=True)
+    assert (kv.len, kv.head) == (mem, (head0 + QLEN) % cap)
+    # the segment's keys and values, projected into the ring at the wrapped rows
+    h64 = ci["q"].f64[0, 0]
+    k_seg, v_seg = oracle.linear(h64, wt["w_k"].f64), oracle.linear(h64, wt["w_v"].f64)
+    slots = [(head0 + mem + t) % cap for t in range(QLEN)]
+    gu.compare("max ring: segment keys", gu.host64(kr_d[slots]), k_seg, dtype="bf16")
+    gu.compare("max ring: segment values", gu.host64(vr_d[:, slots].T), v_seg, dtype="bf16")
+    # the probed rows of the output against the oracle over every key
+    k_all, v_all = ci["k"], ci["v"]
+    k_all[0, 0, mem:] = k_seg
+    v_all[0, 0, mem:] = v_seg
+    n_rel = CLAMP + 1
+    r_tab = oracle.linear(oracle.relpos_embed(0, n_rel, 64, CLAMP), wt["w_r"].f64)[None]
+    rows = sorted(probes)
+    ref = oracle.rel_attn_core(h64[None, None, rows], k_all, v_all, r_tab, ci["u"].f64, ci["vb"].f64, scale=0.125,
+                               clamp_len=CLAMP, qpos=[mem + i for i in rows])
+    print(f"  oracle done at {time.time() - t0:.1f} s", flush=True)
+    gu.compare("max ring: probed rows", gu.host64(out)[:, rows], ref, dtype="bf16")

@@ -300,3 +300,16 @@ def long_memory_layer_inputs(*, d_model: int, n_head: int, qlen: int, mlen: int,
     out["u"] = Tensor(_normal(rng, (n_head, 64), 0.02), "bf16")
     out["v"] = Tensor(_normal(rng, (n_head, 64), 0.02), "bf16")
     return out
+
+
+def identity_head_weights(*, seed: int) -> dict:
+    """Layer weights of one head (d_head 64) at d_model 64 whose query and
+    output projections are the identity, so that the layer's queries are its
+    input rows and its output is the attention output; W_k, W_v, W_r
+    N(0, 0.02), drawn in that order."""
+    rng = np.random.default_rng(seed)
+    eye = np.eye(64, dtype=np.float32)
+    out = {"w_q": Tensor(eye, "bf16"), "w_o": Tensor(eye, "bf16")}
+    for name in ("w_k", "w_v", "w_r"):
+        out[name] = Tensor(_normal(rng, (64, 64), 0.02), "bf16")
+    return out
