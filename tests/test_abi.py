@@ -411,3 +411,11 @@ def test_key_count_limit_boundary():
     ok = _desc(batch=1, n_head=1, qlen=64, mlen=klen_max - 64)
     assert xl.xl_rel_attn_core_workspace_size(ok) > 0
     assert xl.xl_rel_attn_core_workspace_size(_desc(batch=1, n_head=1, qlen=64, mlen=klen_max - 63)) == 0
+
+
+def test_bias_table_context_boundary():
+    # with a bias table the kernel keeps one value per distance in LDS: the
+    # longest context it takes is accepted, one more key is refused
+    kmax = 80 * 1024 // 4 - 384
+    assert xl.xl_rel_attn_core_workspace_size(_desc(batch=1, n_head=1, qlen=64, mlen=kmax - 64, bias_clamp=8)) > 0
+    assert xl.xl_rel_attn_core_workspace_size(_desc(batch=1, n_head=1, qlen=64, mlen=kmax - 63, bias_clamp=8)) == 0

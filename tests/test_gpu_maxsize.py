@@ -23,6 +23,10 @@ sampled outputs are the probed attention rows, checked against the oracle
 over every key; and the segment's projected keys and values land in the
 ring at the wrapped rows.
 
+The fused attention with a bias table at the longest context that the
+kernel's LDS copy of the table allows (20,096 keys), for both kinds of
+table, element-wise against the oracle.
+
 One segment step on a full FIFO of that many memory rows (d_model 32: one
 head, projections with a K of 32), whose ring starts mid-buffer and wraps:
 the projected keys and values at the rows where an offset error would first
@@ -37,6 +41,7 @@ import pytest
 import oracle
 import xl_inputs
 from tests import gpu_util as gu
+from tests.test_gpu_parity import _core_case
 
 pytestmark = pytest.mark.gpu
 
@@ -177,3 +182,15 @@ def test_segment_step_kv_max_ring(T):
                                clamp_len=CLAMP, qpos=[mem + i for i in rows])
     print(f"  oracle done at {time.time() - t0:.1f} s", flush=True)
     gu.compare("max ring: probed rows", gu.host64(out)[:, rows], ref, dtype="bf16")
+
+
+# (80 KB of tiles and rings plus 4 bytes per table entry, mlen + qlen + 384
+# entries, within the 160 KB of LDS)
+BIAS_KLEN_MAX = 80 * 1024 // 4 - 384
+
+
+# qlen 1 and 129 leave a last query tile of one query, where the table (which
+# covers the tile's 128 rows) fills the LDS exactly
+@pytest.mark.parametrize("qlen,bias_kind,bias", [(1, 0, 128), (64, 1, 0), (129, 0, 16)])
+def test_core_bias_table_max_context(T, qlen, bias_kind, bias):
+    _core_case(T, "bf16", 1, 2, qlen, BIAS_KLEN_MAX - qlen, -1, bias, 0, bias_kind=bias_kind)
