@@ -419,3 +419,12 @@ def test_bias_table_context_boundary():
     kmax = 80 * 1024 // 4 - 384
     assert xl.xl_rel_attn_core_workspace_size(_desc(batch=1, n_head=1, qlen=64, mlen=kmax - 64, bias_clamp=8)) > 0
     assert xl.xl_rel_attn_core_workspace_size(_desc(batch=1, n_head=1, qlen=64, mlen=kmax - 63, bias_clamp=8)) == 0
+
+
+def test_width_limit_boundaries():
+    # d_model and n_head * d_head up to 65536 are accepted, one step more is refused
+    size = lambda **kw: xl.xl_rel_attn_workspace_size(_desc(batch=1, qlen=64, mlen=64, **kw))
+    assert size(d_model=65536, n_head=1) > 0
+    assert size(d_model=65536 + 32, n_head=1) == 0
+    assert size(d_model=64, n_head=1024) > 0
+    assert size(d_model=64, n_head=1025) == 0

@@ -27,6 +27,11 @@ The fused attention with a bias table at the longest context that the
 kernel's LDS copy of the table allows (20,096 keys), for both kinds of
 table, element-wise against the oracle.
 
+The layer at the widest shapes accepted: d_model 65,536 with one head
+(projections with a K of 65,536, an output projection of 65,536 columns,
+32,768 sinusoid frequencies) and 1,024 heads (n_head * d_head = 65,536) at
+d_model 64, under the sensitive recipe, element-wise against the oracle.
+
 One segment step on a full FIFO of that many memory rows (d_model 32: one
 head, projections with a K of 32), whose ring starts mid-buffer and wraps:
 the projected keys and values at the rows where an offset error would first
@@ -41,7 +46,7 @@ import pytest
 import oracle
 import xl_inputs
 from tests import gpu_util as gu
-from tests.test_gpu_parity import _core_case
+from tests.test_gpu_parity import W, _core_case, _run_layer
 
 pytestmark = pytest.mark.gpu
 
@@ -194,3 +199,14 @@ BIAS_KLEN_MAX = 80 * 1024 // 4 - 384
 @pytest.mark.parametrize("qlen,bias_kind,bias", [(1, 0, 128), (64, 1, 0), (129, 0, 16)])
 def test_core_bias_table_max_context(T, qlen, bias_kind, bias):
     _core_case(T, "bf16", 1, 2, qlen, BIAS_KLEN_MAX - qlen, -1, bias, 0, bias_kind=bias_kind)
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("d_model,n_head", [(65536, 1), (64, 1024)])
+def test_layer_max_width(T, d_model, n_head):
+    import dataclasses
+    w = dataclasses.replace(W["base_bf16"], d_model=d_model, n_head=n_head, seed=41)
+    t = xl_inputs.layer_inputs(w, batch=1, qlen=QLEN, mlen=QLEN, recipe="sensitive")
+    L = _run_layer(T, w, t, batch=1, qlen=QLEN, mlen=QLEN)
+    ref = gu.oracle_layer(t, w, t["h"].f64, t["mem"].f64)
+    gu.compare(f"d_model {d_model}, {n_head} heads", gu.host64(L.out), ref, dtype="bf16")
