@@ -214,7 +214,10 @@ def main():
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="before warm-up, run a plain device-to-device copy of this many MiB three times")
     ap.add_argument("--summarize", metavar="DIR", help="print a summary of the rocprofv3 databases under DIR")
-    ap.add_argument("--core", metavar="WORKLOADS", help="comma-separated workloads: time the fused attention alone")
+    ap.add_argument("--core", metavar="WORKLOADS",
+                    help="comma-separated workloads: time the fused attention alone; a name may carry @mM (M "
+                         "memory rows), @bB (batch B), @sS (at most S workgroups per query tile, as the "
+                         "descriptor's attn_splits) and /tpN (one GPU's heads under N-way head sharding)")
     ap.add_argument("--launches", type=int, default=100, help="timed launches per --core measurement")
     ap.add_argument("--decoder", type=int, default=0, metavar="N",
                     help="time one segment step of an N-layer decoder stack instead of the attention layer")
@@ -621,12 +624,23 @@ def core_bench(names, launches, warmup):
     scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     for name in names:
         # "NAME/tpN": one GPU's share when the heads are sharded over N GPUs;
-        # "NAME@mM": the workload with M memory rows (a sweep of the key count)
+        # "@mM": M memory rows (a sweep of the key count); "@bB": batch B (every
+        # compute unit with two workgroups, for instance); "@sS": the key-split
+        # cap S of the descriptor (a sweep of the split count)
         base, _, tp = name.partition("/tp")
-        base, _, mem_rows = base.partition("@m")
+        base, *mods = base.split("@")
         w = xl_inputs.WORKLOADS[base]
-        if mem_rows:
-            w = dataclass_replace(w, mlen=int(mem_rows))
+        splits = 0
+        for mod in mods:
+            key, val = mod[:1], int(mod[1:])
+            if key == "m":
+                w = dataclass_replace(w, mlen=val)
+            elif key == "b":
+                w = dataclass_replace(w, batch=val)
+            elif key == "s":
+                splits = val
+            else:
+                raise SystemExit(f"{name}: unknown modifier @{mod}")
         if tp:
             if w.n_head % int(tp):
                 raise SystemExit(f"{name}: {w.n_head} heads do not split over {tp} GPUs")
@@ -644,6 +658,7 @@ def core_bench(names, launches, warmup):
         k, vt = L.ws_view(lay.k, (B, H, lay.klen, dh)), L.ws_view(lay.vt, (B, H, dh, lay.ldv))
         r = L.ws_view(lay.r, (H, lay.n_rel, dh))
         attn = torch.empty((B, q, H * dh), dtype=torch.bfloat16, device="cuda")
+        L.desc.attn_splits = splits
         nws = xl.xl_rel_attn_core_workspace_size(L.desc)
         cws = torch.empty(nws, dtype=torch.uint8, device="cuda") if nws else None
         beta = L.weights.bias_table
