@@ -60,6 +60,24 @@ enum {
     XL_HIP_ERROR = 5             /* a HIP launch/runtime call failed */
 };
 
+/*
+ * The supported envelope (outside it a call returns XL_UNSUPPORTED, or
+ * XL_BAD_SHAPE where a size is not meaningful at all), with klen = mlen + qlen:
+ *   (dtype, d_head) = (XL_BF16, 64) or (XL_F32, 8);
+ *   d_model <= 65536, a multiple of 32 (bf16) or 16 (f32); n_head * d_head
+ *     <= 65536 and a multiple of 32 (bf16) or 16 (f32);
+ *   klen <= (2^31 - 1) / 128 (a head's keys within 32-bit byte offsets),
+ *     batch * klen < 2^30, batch * n_head < 2^25, every tensor of the call
+ *     (keys, values, memory rows) at most 2^40 elements;
+ *   with a bias table in bf16: klen <= 20096 (the table of a workgroup's
+ *     distances sits in LDS); bias_clamp <= 65535; attn_splits <= 64;
+ *   FIFO memory: mlen_max < 2^25 and batch * mlen_max < 2^30; key ring:
+ *     cap and mlen_max <= (2^31 - 1) / 128, batch * cap < 2^30, cap,
+ *     mlen_max, len, head and qlen multiples of 8;
+ *   decoder: d_inner <= 262144 and batch * qlen * d_inner < 2^31.
+ * Every limit is checked before any product of caller sizes is formed.
+ */
+
 /* Element types. */
 enum { XL_F32 = 0, XL_BF16 = 1 };
 

@@ -428,3 +428,12 @@ def test_width_limit_boundaries():
     assert size(d_model=65536 + 32, n_head=1) == 0
     assert size(d_model=64, n_head=1024) > 0
     assert size(d_model=64, n_head=1025) == 0
+
+
+def test_tensor_size_bound():
+    # within every per-size limit, but with 2^45 key elements: refused before
+    # any product of sizes could overflow the projection launches' tile counts
+    d = _desc(batch=32, n_head=1024, d_model=64, qlen=64, mlen=(2 ** 31 - 1) // 128 - 64)
+    assert _fwd(d) == xl.XL_UNSUPPORTED
+    assert b"2^40" in xl.lib().xl_last_error()
+    assert xl.xl_rel_attn_core_workspace_size(d) == 0

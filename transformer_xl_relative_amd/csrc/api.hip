@@ -84,9 +84,14 @@ int check_desc(const xl_attn_desc* d, int64_t mlen, bool need_dmodel) {
     const int64_t klen = mlen + d->qlen;
     const int64_t hd = d->n_head * d->d_head;
     // every element count a kernel indexes with 32-bit arithmetic must fit
-    if (klen > kI32 / 128 || d->batch > kI32 / 2 / klen || hd > 65536 || d->batch > kI32 / 64 / d->n_head ||
-        (double)d->batch * d->n_head * klen * d->d_head > 9.0e15)
+    if (klen > kI32 / 128 || d->batch > kI32 / 2 / klen || hd > 65536 || d->batch > kI32 / 64 / d->n_head)
         return fail(XL_UNSUPPORTED, "problem too large for the 32-bit element offsets of the kernels");
+    // the keys (and the memory rows) beyond 2^40 elements would not fit any
+    // device; below it every tile count of the projection launches fits an int
+    constexpr double kMaxElems = 1099511627776.0;   // 2^40
+    if ((double)d->batch * d->n_head * klen * d->d_head > kMaxElems ||
+        (need_dmodel && (double)d->batch * klen * d->d_model > kMaxElems))
+        return fail(XL_UNSUPPORTED, "problem larger than 2^40 elements per tensor");
     if (d->batch * d->n_head * ((d->qlen + 127) / 128) > kI32) return fail(XL_UNSUPPORTED, "grid too large");
     // the bf16 attention keeps the bias table of a workgroup's distances in LDS
     if (d->bias_clamp >= 0 && d->dtype == XL_BF16 && klen > kMaxBiasKlen)
