@@ -71,7 +71,7 @@ ATTN_SOURCES = ("transformer_xl_relative_amd/csrc/attn_bf16.hip", "transformer_x
 # HBM bytes per launch of the fused attention kernel (calibrated FETCH_SIZE and
 # WRITE_SIZE, see profiles/attn_bf16_kernel_<workload>_pmc_traffic.md).
 TRAFFIC = {
-    "large_bf16": {"sha256": "8397f57ff7963cc378b5e89db565d9fe7192daae74de05f4821209ed7030aadf",
+    "large_bf16": {"sha256": "f8a6b49035082c96374062113bfc2ccec7c2c972ed82eb4b2631405365496985",
                    "bytes": 39651350, "fetch_bytes": 33359894, "write_bytes": 6291456},
 }
 

@@ -69,6 +69,18 @@ def test_decoder_layer_large_sampled(T):
     gu.compare("decoder layer large (batch 0)", got[:1], ref, dtype="bf16")
 
 
+def test_decoder_layer_ragged_tall_tiles(T):
+    # the first feed-forward product, 1520 x 8000 x 1056, makes 6 x 32 = 192 tiles of
+    # 256 x 256 and 8 x 32 = 256 of 192 x 256, so it runs on the latter, with ragged
+    # row and column tiles (1520 = 7 x 192 + 176, 8000 = 31 x 256 + 64) and a K of
+    # 32 mod 64 (a half-width last stage); batch 0 checked
+    w = dataclasses.replace(W["base_bf16"], d_model=1056, n_head=2, seed=1056)
+    t = xl_inputs.decoder_inputs(w, d_inner=8000, n_layer=1, batch=2, qlen=760, mlen=24)
+    got = _run_layer(T, w, t, batch=2, qlen=760, mlen=24, d_inner=8000)
+    ref = _oracle_layer(t, w, t["layers"][0], t["h"].f64[:1], t["mem"].f64[:1])
+    gu.compare("decoder layer ragged 192 x 256 tiles (batch 0)", got[:1], ref, dtype="bf16")
+
+
 def _stack_run(T, w, t, *, batch, qlen, n_seg, mlen_max, d_inner, n_layer, head0=0):
     D = w.d_model
     dt = T.bfloat16 if w.dtype == "bf16" else T.float32

@@ -306,7 +306,7 @@ void dec_layout(const xl_attn_desc* d, int64_t mlen, int64_t d_inner, bool stack
     L->attn_total = A.total;
     L->xm = take((size_t)(B * mlen * D) * es);
     L->xs = take((size_t)(B * q * D) * es);
-    L->h1 = take((size_t)(B * q * D) * es);
+    L->h1 = take((size_t)(B * q * D) * 4);   // fp32 for either element type
     L->x2 = take((size_t)(B * q * D) * es);
     L->y1 = take((size_t)(B * q * d_inner) * es);
     L->buf0 = take(stack ? (size_t)(B * q * D) * es : 0);
@@ -337,6 +337,9 @@ int check_decoder(const xl_attn_desc* d, int64_t d_inner, float eps, const xl_de
 // read of it.
 //   xm, xs = LN1(mem), LN1(h); h1 = h + RelAttn(xs over [xm ; xs]);
 //   out = h1 + W2 relu(W1 LN2(h1) + b1) + b2
+// h1 stays fp32 in the workspace: out adds it back after the feed-forward
+// network, and a bf16 copy would put half an ulp of h1 (0.016 at |h1| >= 4)
+// into out however small out is after that sum.
 int decoder_forward(const xl_attn_desc* d, int64_t d_inner, float eps, const xl_decoder_weights* w, const void* h,
                     const void* mem, int64_t mlen, int64_t ring_len, int64_t ring_head, void* out, void* ws,
                     size_t ws_bytes, hipStream_t s, const xl::RowCopy* fifo_write) {
@@ -363,7 +366,7 @@ int decoder_forward(const xl_attn_desc* d, int64_t d_inner, float eps, const xl_
     // 2. attention sublayer with the residual: h1 = h + RelAttn(...)
     xl_attn_desc da = *d;
     da.mlen = mlen;
-    da.out_dtype = d->dtype;
+    da.out_dtype = XL_F32;
     int st = layer_forward(&da, &w->attn, W + L.xs, W + L.xm, mlen, mlen, 0, W + L.h1, W, L.attn_total, s, fifo_write,
                            nullptr, h);
     if (st != XL_OK) return st;
@@ -374,6 +377,7 @@ int decoder_forward(const xl_attn_desc* d, int64_t d_inner, float eps, const xl_
     ln.y0 = W + L.x2; ln.y1 = W + L.x2;
     ln.gamma = w->ln2_g; ln.beta = w->ln2_b;
     ln.rows = (int)(B * q);
+    ln.x_f32 = 1;
     if ((e = xl::launch_layer_norm(ln, bf, s)) != hipSuccess) return hip_fail(e, "layer norm launch");
     // 4-5. the feed-forward network with its residual
     xl::GemmArgs g;
@@ -387,7 +391,7 @@ int decoder_forward(const xl_attn_desc* d, int64_t d_inner, float eps, const xl_
     g.N = (int)D; g.K = (int)d_inner;
     g.a0 = W + L.y1; g.lda = d_inner;
     g.b0 = w->w2; g.out0 = out; g.out_bf16 = d->out_dtype == XL_BF16;
-    g.bias_n = w->b2; g.relu = 0; g.res = W + L.h1;
+    g.bias_n = w->b2; g.relu = 0; g.res = W + L.h1; g.res_f32 = 1;
     if ((e = xl::launch_gemm(g, bf, s)) != hipSuccess) return hip_fail(e, "feed-forward launch");
     return XL_OK;
 }

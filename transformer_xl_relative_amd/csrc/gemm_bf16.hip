@@ -48,17 +48,21 @@ struct Tile {
     static constexpr int SWS = CPR == 8 ? 1 : 2;  // swizzle of row r: (r >> SWS) & (CPR - 1)
     static_assert(RB_ == 128 || RB_ == 64, "row bytes per stage");
     static constexpr int NT = 64 * WM * WN;       // threads
-    static constexpr int BT = 32 * WM * WTM;      // workgroup tile edge
-    static_assert(BT == 32 * WN * WTN, "square tiles");
-    static constexpr int OPB = BT * ROWB;         // one operand tile per stage
-    static constexpr int STAGEB = 2 * OPB;
+    static constexpr int BTM = 32 * WM * WTM;     // workgroup tile rows (M)
+    static constexpr int BTN = 32 * WN * WTN;     // workgroup tile columns (N)
+    static constexpr int OPA = BTM * ROWB;        // the A tile of a stage, then
+    static constexpr int OPB = BTN * ROWB;        // the B tile
+    static constexpr int STAGEB = OPA + OPB;
     static constexpr int LDS = NST * STAGEB;
-    static constexpr int NI = BT * CPR / NT;      // loads per thread per operand per stage
+    static constexpr int NIA = BTM * CPR / NT;    // loads per thread per stage: A, B
+    static constexpr int NIB = BTN * CPR / NT;
+    static_assert(NIA * NT == BTM * CPR && NIB * NT == BTN * CPR, "whole loads per thread");
 };
 using Big = Tile<4, 4, 2, 2, 2>;     // 256 x 256, 16 waves (each 64 x 64), 2 stages (128 KiB)
 using Small = Tile<4, 4, 1, 1, 3>;   // 128 x 128, 16 waves (each 32 x 32), 3 stages (96 KiB): one per CU
 using Small2 = Tile<2, 4, 2, 1, 2>;  // 128 x 128, 8 waves, 2 stages (64 KiB): two per CU
 using Tiny = Tile<2, 2, 1, 1, 8>;    // 64 x 64, 4 waves, 8 stages (128 KiB): seven stages in flight
+using Tall = Tile<2, 4, 3, 2, 2>;    // 192 x 256, 8 waves (each 96 x 64), 2 stages (112 KiB)
 
 template <typename T, bool kRowOut, bool kHalf>
 __device__ __forceinline__ void tile_bf16(const GemmArgs& g, int m0, int n0, char* smem) {
@@ -79,29 +83,42 @@ __device__ __forceinline__ void tile_bf16(const GemmArgs& g, int m0, int n0, cha
     // stage issues the same load instructions
     const int nk = (g.K + KST - 1) / KST;
     const bool khalf = kHalf && (g.K % KST) != 0;   // kHalf: some problem of the launch has such a K
-    const bf16_t* asrc[T::NI];
-    const bf16_t* bsrc[T::NI];
-    int back[T::NI];
-#pragma unroll
-    for (int i = 0; i < T::NI; ++i) {
+    const bf16_t* asrc[T::NIA];
+    const bf16_t* bsrc[T::NIB];
+    int aback[T::NIA], bback[T::NIB];
+    // (the chunk's row and its logical chunk; the back step of a half-width stage)
+    auto chunk_of = [&](int i, int& r, int& lc) __attribute__((always_inline)) {
         const int chunk = (i * NW + wave) * 64 + lane;
-        const int r = chunk / CPR, lc = (chunk % CPR) ^ ((r >> T::SWS) & (CPR - 1));
+        r = chunk / CPR;
+        lc = (chunk % CPR) ^ ((r >> T::SWS) & (CPR - 1));
+    };
+#pragma unroll
+    for (int i = 0; i < T::NIA; ++i) {
+        int r, lc;
+        chunk_of(i, r, lc);
         asrc[i] = a_row_ptr<bf16_t>(g, min(m0 + r, g.M - 1)) + lc * 8;
+        aback[i] = lc >= CPR / 2 ? KST / 2 : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < T::NIB; ++i) {
+        int r, lc;
+        chunk_of(i, r, lc);
         bsrc[i] = b_row_ptr<bf16_t>(g, min(n0 + r, g.N - 1)) + lc * 8;
-        back[i] = lc >= CPR / 2 ? KST / 2 : 0;
+        bback[i] = lc >= CPR / 2 ? KST / 2 : 0;
     }
     auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
         char* base = smem + stage * T::STAGEB;
         const bool half = khalf && kt == nk - 1;
 #pragma unroll
-        for (int i = 0; i < T::NI; ++i) {
-            const int ko = kt * KST - (half ? back[i] : 0);
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(asrc[i] + ko),
-                                             (__attribute__((address_space(3))) void*)(base + (i * NW + wave) * 1024),
-                                             16, 0, 0);
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void*)(bsrc[i] + ko),
-                (__attribute__((address_space(3))) void*)(base + T::OPB + (i * NW + wave) * 1024), 16, 0, 0);
+        for (int i = 0; i < (T::NIA > T::NIB ? T::NIA : T::NIB); ++i) {
+            if (i < T::NIA)
+                __builtin_amdgcn_global_load_lds(
+                    (const __attribute__((address_space(1))) void*)(asrc[i] + kt * KST - (half ? aback[i] : 0)),
+                    (__attribute__((address_space(3))) void*)(base + (i * NW + wave) * 1024), 16, 0, 0);
+            if (i < T::NIB)
+                __builtin_amdgcn_global_load_lds(
+                    (const __attribute__((address_space(1))) void*)(bsrc[i] + kt * KST - (half ? bback[i] : 0)),
+                    (__attribute__((address_space(3))) void*)(base + T::OPA + (i * NW + wave) * 1024), 16, 0, 0);
         }
     };
 
@@ -113,7 +130,7 @@ __device__ __forceinline__ void tile_bf16(const GemmArgs& g, int m0, int n0, cha
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
         aoff[kc] = lds0 + (uint32_t)((32 * wm * WTM + l32) * ROWB + (((2 * kc + hf) ^ sw) << 4));
-        boff[kc] = lds0 + (uint32_t)(T::OPB + (32 * wn * WTN + l32) * ROWB + (((2 * kc + hf) ^ sw) << 4));
+        boff[kc] = lds0 + (uint32_t)(T::OPA + (32 * wn * WTN + l32) * ROWB + (((2 * kc + hf) ^ sw) << 4));
     }
     // fragments of one k-step (16 K elements): two register sets, one being
     // multiplied while the other is filled
@@ -144,7 +161,7 @@ __device__ __forceinline__ void tile_bf16(const GemmArgs& g, int m0, int n0, cha
     };
 
     constexpr int NST = T::NST;
-    constexpr int PER = 2 * T::NI;      // loads per thread per stage
+    constexpr int PER = T::NIA + T::NIB;   // loads per thread per stage
 #pragma unroll
     for (int st = 0; st < NST - 1; ++st)
         if (st < nk) issue(st, st);
@@ -211,7 +228,45 @@ __device__ __forceinline__ void tile_bf16(const GemmArgs& g, int m0, int n0, cha
     auto lds_ld128 = [&](uint32_t adr) __attribute__((always_inline)) {
         return *(const __attribute__((address_space(3))) u32x4*)(size_t)adr;
     };
-    if constexpr (kRowOut) {
+    if (kRowOut && g.epi == EPI_OUT && (!g.out_bf16 || g.bias_n || g.res || g.relu)) {
+        // fp32 outputs, or bias / ReLU / residual: the fp32 accumulators are
+        // staged, one 32 x 32 block at a time, and rounded once after the
+        // extras (a product rounded before its residual is added keeps that
+        // rounding however far the sum cancels)
+        constexpr int PF = 32 * 4 + 16;            // bytes per staged row
+        static_assert(NW * 32 * PF <= T::LDS, "fp32 epilogue staging fits in LDS");
+        const uint32_t fbuf = lds0 + (uint32_t)(wave * 32 * PF);
+        const int fc = lane & 3, fr = lane >> 2;   // lane -> columns 8 fc .. 8 fc + 7 of rows fr and fr + 16
+#pragma unroll
+        for (int i = 0; i < WTM; ++i)
+#pragma unroll
+            for (int j = 0; j < WTN; ++j) {
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq)
+                    *(__attribute__((address_space(3))) f32x4*)(size_t)(fbuf + l32 * PF + (8 * gq + 4 * hf) * 4) =
+                        (f32x4){acc[i][j][4 * gq], acc[i][j][4 * gq + 1], acc[i][j][4 * gq + 2], acc[i][j][4 * gq + 3]};
+                const int n = nw + 32 * j + 8 * fc;
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const int m = mw + 32 * i + fr + 16 * k;
+                    const uint32_t src = fbuf + (fr + 16 * k) * PF + fc * 32;
+                    const f32x4 lo = *(const __attribute__((address_space(3))) f32x4*)(size_t)src;
+                    const f32x4 hi = *(const __attribute__((address_space(3))) f32x4*)(size_t)(src + 16);
+                    if (m < g.M && n < g.N) {
+                        float f[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                        out_extras8(g, m, n, f);
+                        if (g.out_bf16) {
+                            *(u32x4*)((bf16_t*)g.out0 + (int64_t)m * g.N + n) =
+                                (u32x4){pack2bf(f[0], f[1]), pack2bf(f[2], f[3]), pack2bf(f[4], f[5]), pack2bf(f[6], f[7])};
+                        } else {
+                            float* o = (float*)g.out0 + (int64_t)m * g.N + n;
+                            *(f32x4*)o = (f32x4){f[0], f[1], f[2], f[3]};
+                            *(f32x4*)(o + 4) = (f32x4){f[4], f[5], f[6], f[7]};
+                        }
+                    }
+                }
+            }
+    } else if constexpr (kRowOut) {
         constexpr int PITCH = TC * 2 + 16;         // bytes per staged row
         constexpr int CPR = TC / 8;                // 16-byte chunks per row
         constexpr int RPI = 64 / CPR;              // rows per wave instruction in the copy
@@ -246,25 +301,8 @@ __device__ __forceinline__ void tile_bf16(const GemmArgs& g, int m0, int n0, cha
             for (int k = 0; k < 32 / RPI; ++k) {
                 const u32x4 w = lds_ld128(wbuf + (rl + RPI * k) * PITCH + ch * 16);
                 if (m < g.M && n < ncols) {
-                    if (epi == EPI_OUT) {
-                        // the extras apply to the staged (rounded) values, 8 columns at a time
-                        const bool extras = g.bias_n || g.res || g.relu;
-                        if (g.out_bf16 && !extras) {
-                            *(u32x4*)((bf16_t*)g.out0 + (int64_t)m * g.N + n) = w;
-                        } else {
-                            float f[8];
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) { f[2 * e] = bf2f(w[e] & 0xFFFF); f[2 * e + 1] = bf2f(w[e] >> 16); }
-                            if (extras) out_extras8(g, m, n, f);
-                            if (g.out_bf16) {
-                                *(u32x4*)((bf16_t*)g.out0 + (int64_t)m * g.N + n) =
-                                    (u32x4){pack2bf(f[0], f[1]), pack2bf(f[2], f[3]), pack2bf(f[4], f[5]), pack2bf(f[6], f[7])};
-                            } else {
-                                float* o = (float*)g.out0 + (int64_t)m * g.N + n;
-                                *(f32x4*)o = (f32x4){f[0], f[1], f[2], f[3]};
-                                *(f32x4*)(o + 4) = (f32x4){f[4], f[5], f[6], f[7]};
-                            }
-                        }
+                    if (epi == EPI_OUT) {   // bf16 results without extras
+                        *(u32x4*)((bf16_t*)g.out0 + (int64_t)m * g.N + n) = w;
                     } else {
                         const int64_t rowoff = epi == EPI_R ? (int64_t)m * 64 : ((int64_t)bb * g.H * krows + jp) * 64;
                         *(u32x4*)(out + rowoff + (int64_t)(n >> 6) * headstride + (n & 63)) = w;
@@ -360,7 +398,7 @@ __global__ void __launch_bounds__(T::NT, 1) gemm_bf16_kernel(GemmBatch gb) {
     const int tr = (t & 7) * ((end - start) >> 3) + (t >> 3);
     if (tr >= real) return;
     const int tm = tr / tiles_n, tn = tr - tm * tiles_n;
-    const int m0 = tm * T::BT, n0 = tn * T::BT;
+    const int m0 = tm * T::BTM, n0 = tn * T::BTN;
     const bool col_out = g.epi == EPI_VT || (g.epi == EPI_KV && n0 >= g.b_split);
     if (col_out) tile_bf16<T, false, kHalf>(g, m0, n0, smem);
     else tile_bf16<T, true, kHalf>(g, m0, n0, smem);
@@ -375,8 +413,8 @@ hipError_t launch_tiles(const GemmArgs* g, int count, hipStream_t s, const RowCo
         if (g[i].M <= 0 || g[i].N <= 0) continue;
         const int k = gb.count++;
         gb.p[k] = g[i];
-        gb.tiles_n[k] = (g[i].N + T::BT - 1) / T::BT;
-        gb.tiles_real[k] = gb.tiles_n[k] * ((g[i].M + T::BT - 1) / T::BT);
+        gb.tiles_n[k] = (g[i].N + T::BTN - 1) / T::BTN;
+        gb.tiles_real[k] = gb.tiles_n[k] * ((g[i].M + T::BTM - 1) / T::BTM);
         gb.tile_start[k] = tiles;
         tiles += (gb.tiles_real[k] + 7) / 8 * 8;     // each problem's range is a multiple of 8
     }
@@ -430,14 +468,19 @@ hipError_t launch_gemms_bf16(const GemmArgs* g, int count, hipStream_t s, const 
     // with three LDS stages while one workgroup per compute unit suffices and
     // two stages (two workgroups per compute unit) beyond that; 64 x 64 tiles
     // for small problems
-    int big = 0, small = 0;
+    int big = 0, small = 0, tall = 0;
     for (int i = 0; i < count; ++i)
         if (g[i].M > 0 && g[i].N > 0) {
             big += ((g[i].M + 255) / 256) * ((g[i].N + 255) / 256);
             small += ((g[i].M + 127) / 128) * ((g[i].N + 127) / 128);
+            tall += ((g[i].M + 191) / 192) * ((g[i].N + 255) / 256);
         }
     if (cp && (cp->row_bytes % 16 || cp->B * cp->n > 0x7FFFFFFF || cp->row_bytes / 16 * (cp->B * cp->n) > 0x7FFFFFFF))
         return hipErrorInvalidValue;
+    // where 256 x 256 tiles leave compute units idle and 192 x 256 tiles
+    // still fit one round, the latter (the decoder's first feed-forward
+    // product at the measured workload: 192 tiles against 256)
+    if (big >= 192 && big < 240 && tall > big && tall <= 256) return launch_tiles<Tall>(g, count, s, cp);
     if (big >= 192) return launch_tiles<Big>(g, count, s, cp);
     if (small > 256) return launch_tiles<Small2>(g, count, s, cp);
     // few tiles: their stage latency, not the machine, sets the time; 64 x 64

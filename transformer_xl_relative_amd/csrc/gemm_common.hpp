@@ -96,7 +96,8 @@ __device__ __forceinline__ void out_extras(const GemmArgs& g, int m, int n, f32x
 }
 
 // the same for 8 outputs (m, n..n+7) of the bf16 kernel, n a multiple of 8
-// and N of 32: bias_n and res are read 16 bytes at a time
+// and N of 32: bias_n and a bf16 res are read 16 bytes at a time, an fp32 res
+// (res_f32) 32 bytes
 __device__ __forceinline__ void out_extras8(const GemmArgs& g, int m, int n, float* f) {
     if (g.bias_n) {
         const u32x4 b = *(const u32x4*)((const bf16_t*)g.bias_n + n);
@@ -107,7 +108,12 @@ __device__ __forceinline__ void out_extras8(const GemmArgs& g, int m, int n, flo
 #pragma unroll
         for (int e = 0; e < 8; ++e) f[e] = fmaxf(f[e], 0.f);
     }
-    if (g.res) {
+    if (g.res && g.res_f32) {
+        const float* r = (const float*)g.res + (int64_t)m * g.N + n;
+        const f32x4 r0 = *(const f32x4*)r, r1 = *(const f32x4*)(r + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { f[e] += r0[e]; f[4 + e] += r1[e]; }
+    } else if (g.res) {
         const u32x4 r = *(const u32x4*)((const bf16_t*)g.res + (int64_t)m * g.N + n);
 #pragma unroll
         for (int e = 0; e < 4; ++e) { f[2 * e] += bf2f(r[e] & 0xFFFF); f[2 * e + 1] += bf2f(r[e] >> 16); }

@@ -48,10 +48,12 @@ struct GemmArgs {
     int out_rows = 0;
     int out_pos0 = 0;
     // EPI_OUT extras: out = act(acc + bias_n[n]) + res[m, n], act the ReLU when
-    // relu; bias_n [N] and res [M, N] (row-major) in the operand type, or null
+    // relu; bias_n [N] and res [M, N] (row-major) in the operand type, or null;
+    // res_f32: res is fp32 also for bf16 operands
     const void* bias_n = nullptr;
     const void* res = nullptr;
     int relu = 0;
+    int res_f32 = 0;
 };
 
 constexpr int kMaxGemms = 4;
@@ -189,6 +191,7 @@ struct LnArgs {
     const void* beta;
     int rows, D;
     float eps;
+    int x_f32;   // bf16: the rows read (a0, a1) are fp32; gamma, beta and y stay bf16
 };
 hipError_t launch_layer_norm(const LnArgs& a, bool bf16, hipStream_t s);
 
