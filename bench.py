@@ -71,7 +71,7 @@ ATTN_SOURCES = ("transformer_xl_relative_amd/csrc/attn_bf16.hip", "transformer_x
 # HBM bytes per launch of the fused attention kernel (calibrated FETCH_SIZE and
 # WRITE_SIZE, see profiles/attn_bf16_kernel_<workload>_pmc_traffic.md).
 TRAFFIC = {
-    "large_bf16": {"sha256": "f8a6b49035082c96374062113bfc2ccec7c2c972ed82eb4b2631405365496985",
+    "large_bf16": {"sha256": "407d58b72e062c773fd1d98ba5d345757d7fd95be84802a9f606d2629b38de06",
                    "bytes": 39651350, "fetch_bytes": 33359894, "write_bytes": 6291456},
 }
 

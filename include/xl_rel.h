@@ -337,8 +337,8 @@ int xl_segment_step_kv(const xl_attn_desc* desc, const xl_attn_weights* w, const
  * materialised in the workspace (xl_rel_attn_core_bwd_workspace_size():
  * 8 bytes per (query, key) pair, 8 per query element, 4 per element of
  * batch x n_head x (table rows in use - 1) x d_head for per-batch-element
- * partial sums of dr, and 12 bytes per query row and block of 32 keys plus
- * 12 per query row for the softmax statistics), no atomics.
+ * partial sums of dr, and 12 per query row for the softmax statistics), no
+ * atomics.
  * Errors as xl_rel_attn_core; gradients must not overlap inputs, each other
  * or the workspace (XL_BAD_SHAPE).
  */

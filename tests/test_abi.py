@@ -332,8 +332,8 @@ def test_core_backward_rejects_bad_arguments():
     klen = 128
     need = xl.xl_rel_attn_core_bwd_workspace_size(d)
     rows = 2 * 8 * 64   # batch x heads x qlen
-    # P and dS, dq_u and dq_v, the dr partials (batch x heads x (klen - 1) rows), softmax partials and row stats
-    assert need == 2 * (rows * klen * 4) + 2 * (rows * 64 * 4) + 2 * 8 * (klen - 1) * 64 * 4 + rows * 4 * 3 * 4 + rows * 3 * 4
+    # P and dS, dq_u and dq_v, the dr partials (batch x heads x (klen - 1) rows), the row stats
+    assert need == 2 * (rows * klen * 4) + 2 * (rows * 64 * 4) + 2 * 8 * (klen - 1) * 64 * 4 + rows * 3 * 4
 
     def call(ldv=klen, n_rel=klen, bias=None, dbias=None, desc=d, ws=FAKE[15], nb=need, dq=FAKE[9], dk=FAKE[10]):
         return lib.xl_rel_attn_core_bwd(ctypes.byref(desc), FAKE[0], FAKE[1], FAKE[2], ldv, FAKE[3], n_rel, FAKE[4],

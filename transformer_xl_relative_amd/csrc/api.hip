@@ -669,10 +669,9 @@ size_t xl_rel_attn_core_bwd_workspace_size(const xl_attn_desc* desc) {
     const int64_t klen = desc->mlen + desc->qlen;
     if (rows > (((int64_t)1 << 40) / klen)) return 0;   // the call rejects it too
     const int64_t dr_rows = n_rel_of(desc, klen) - 1;   // per-batch-element partial sums of dr
-    const int64_t kblocks = (klen + 31) / 32;   // softmax partials per query row and block of 32 keys
     return 2 * align_up((size_t)(rows * klen) * 4) + 2 * align_up((size_t)(rows * desc->d_head) * 4) +
            align_up((size_t)(desc->batch * desc->n_head * dr_rows * desc->d_head) * 4) +
-           align_up((size_t)(rows * kblocks * 3) * 4) + align_up((size_t)(rows * 3) * 4);
+           align_up((size_t)(rows * 3) * 4);
 }
 
 int xl_rel_attn_core_bwd(const xl_attn_desc* desc, const void* q, const void* k, const void* vt, int64_t ldv,
@@ -732,10 +731,7 @@ int xl_rel_attn_core_bwd(const xl_attn_desc* desc, const void* q, const void* k,
     a.dqu = (float*)(W + off); off += align_up(qb * 4);
     a.dqv = (float*)(W + off); off += align_up(qb * 4);
     a.drp = (float*)(W + off); off += align_up((size_t)(desc->batch * H * (need - 1) * dh) * 4);
-    if (dh == 64) {   // the tiled path keeps l and dP with the rows' softmax statistics
-        a.rpart = (float*)(W + off); off += align_up((size_t)(rows * ((klen + 31) / 32) * 3) * 4);
-        a.rstat = (float*)(W + off);
-    }
+    if (dh == 64) a.rstat = (float*)(W + off);   // the tiled path: the rows' softmax statistics
     a.uvp = a.dqu;   // the tiled path's du/dv partials (2 x 64 floats per 64 queries) reuse the dq_u, dq_v regions
     a.dr_first = dh == 64 ? a.n_rel - 1 : 0;   // the tiled dr path (d_head 64) takes the rows below the last
     a.dq = dq; a.dk = dk; a.dv = dv; a.dr = dr; a.du = du; a.dvb = dv_bias; a.dbias = dbias;

@@ -19,8 +19,8 @@
 // d_head 64 the work runs in 64 x 64 blocks staged through LDS, the products
 // on the bf16 matrix cores with fp32 operands split into a high and a low
 // bf16 part (fp32 accumulation, about 16 bits of mantissa per operand):
-//   logits: l and dP per block of (queries, keys), with per-block softmax
-//           partials; row stats combines them into (m, 1/s, D) per row
+//   logits: one workgroup per 64 queries walks their key blocks: l and dP
+//           per pair, and the row statistics (m, 1/s, D)
 //   dk/dv:  rows keys, summed over queries; its loader turns l, dP into
 //           P, dS and writes dS back in place for the kernels after it
 //   dq:     rows queries, summed over keys and over distances; it also
@@ -240,34 +240,7 @@ __global__ void __launch_bounds__(64 * BW) bwd_dr_kernel(AttnBwdArgs a) {
     a.dr[((int64_t)h * a.r_rows + c) * DH + lane] = acc;
 }
 
-
-
-// ---- Logits and dP in 64 x 64 blocks (d_head 64) ----
-// A workgroup takes queries i0..i0+63 and keys j0..j0+63 of one head
-// (blocks with no visible pair exit at once); each of its 4 waves computes a
-// 32 x 32 quarter (queries wm.., keys wn..) on the bf16 matrix cores
-// (v_mfma_f32_32x32x16_bf16, fp32 accumulation):
-//   content  qu . k      qu = s (q + u) enters as a high and a low bf16 part
-//                        (hi = bf16(qu), lo = bf16(qu - hi): 16 bits of
-//                        mantissa), k is exact: two products
-//   dP       dO . v      both exact bf16: one product
-//   position qv . r      qv split like qu, over the 64 distances the quarter
-//                        spans, n = 32 + wm - wn + (0..63) counted from
-//                        dlo = mlen + i0 - j0 - 63: four products, then
-//                        gathered through LDS: pair (i, j) takes distance
-//                        column 31 + i - j
-// Operands are staged as bf16, 32 of d_head at a time, d-contiguous per row
-// (80-byte rows: the lanes' 16-byte reads of 16 rows fall on distinct bank
-// groups); lane (li, half) feeds row li with d = 16 kk + 8 half .. + 7. V is
-// stored transposed (V^T rows by d_head) and staged by key. The logits of
-// visible pairs (plus the bias table entry) go to the P buffer, dP to the dS
-// buffer, and per row and half block of 32 keys the softmax partials (max
-// m_t, sum of exp(l - m_t), sum of exp(l - m_t) dP) to those that
-// bwd_row_stats_kernel combines.
-constexpr int LDC = 32;              // d_head per stage
-constexpr int LRB = LDC * 2 + 16;    // bytes per staged bf16 row
-constexpr int BDP = 64 + 4;
-
+// the eight bf16 of a 16-byte piece as floats
 __device__ __forceinline__ void unpack8(const u32x4 w, float* f) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -276,209 +249,7 @@ __device__ __forceinline__ void unpack8(const u32x4 w, float* f) {
     }
 }
 
-// (three workgroups per compute unit: the registers fit 3 waves per SIMD
-// without spilling, and the LDS 3 x 45 KB)
-__global__ void __launch_bounds__(256, 3) bwd_logits_tile_kernel(AttnBwdArgs a) {
-    constexpr int DH = 64;
-    // staged rows: qu high, qu low, qv high, qv low, dO (64 queries each), k, v
-    // (64 keys each), the table rows of 128 distances
-    constexpr int QH = 0, QL = 64, VH = 128, VL = 192, OR = 256, KR = 320, VR = 384, RR = 448, NROW = 576;
-    __shared__ __attribute__((aligned(16))) char stg[NROW * LRB];
-    float* ops = (float*)stg;   // reused by the epilogue
-    const int tid = (int)__builtin_amdgcn_workitem_id_x();
-    const int nit = (a.qlen + 63) / 64, njt = (a.klen + 63) / 64, nh = (a.klen + 31) / 32;
-    int wg = xcd_block(a.B * a.H * nit * njt);
-    if (wg >= a.B * a.H * nit * njt) return;
-    const int g = wg / (nit * njt);
-    wg -= g * nit * njt;
-    const int it = wg / njt, jt = wg - it * njt;
-    const int i0 = 64 * it, j0 = 64 * jt;
-    const int ilast = i0 + 63 < a.qlen ? i0 + 63 : a.qlen - 1;
-    if (j0 > a.mlen + ilast) return;   // no visible pair in the block
-    const int h = g % a.H, b = g / a.H;
-    const int64_t rb = (int64_t)g * a.qlen;
-    const int dlo = a.mlen + i0 - j0 - 63;
-    const bf16_t* qp = (const bf16_t*)a.q;
-    const bf16_t* op = (const bf16_t*)a.dout;
-    const bf16_t* kp = (const bf16_t*)a.k;
-    const bf16_t* vp = (const bf16_t*)a.vt;
-    const bf16_t* rp = (const bf16_t*)a.r;
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    // per stage a thread loads 16 bytes (8 of d_head) of a q, dO and k row,
-    // of u and v, 8 keys of a V^T row, and 16 bytes of two table rows
-    const int row = tid >> 2, pc = tid & 3;
-    // V^T: lane d of 32 rows, 8 keys each; consecutive lanes then write
-    // consecutive bytes of a key row when V is staged by key
-    const int vd = tid & 31, vj = tid >> 5;
-    int dist0 = dlo + row, dist1 = dlo + 64 + row;
-    dist0 = dist0 < 0 ? 0 : (dist0 > a.n_rel - 1 ? a.n_rel - 1 : dist0);
-    dist1 = dist1 < 0 ? 0 : (dist1 > a.n_rel - 1 ? a.n_rel - 1 : dist1);
-    u32x4 fq, fo, fk, fvt, fr0, fr1, fu, fv;
-    auto fetch = [&](int d0) __attribute__((always_inline)) {
-        const int d = d0 + 8 * pc, i = i0 + row, j = j0 + row;
-        fq = i < a.qlen ? *(const u32x4*)(qp + (rb + i) * DH + d) : z;
-        fo = i < a.qlen ? *(const u32x4*)(op + (((int64_t)b * a.qlen + i) * a.H + h) * DH + d) : z;
-        fk = j < a.klen ? *(const u32x4*)(kp + ((int64_t)g * a.klen + j) * DH + d) : z;
-        fu = *(const u32x4*)((const bf16_t*)a.u + h * DH + d);
-        fv = *(const u32x4*)((const bf16_t*)a.v + h * DH + d);
-        const int jj = j0 + 8 * vj;
-        fvt = jj < a.ldv ? *(const u32x4*)(vp + ((int64_t)g * DH + d0 + vd) * a.ldv + jj) : z;
-        fr0 = *(const u32x4*)(rp + ((int64_t)h * a.r_rows + dist0) * DH + d);
-        fr1 = *(const u32x4*)(rp + ((int64_t)h * a.r_rows + dist1) * DH + d);
-    };
-    auto put = [&](int r, const u32x4 w) __attribute__((always_inline)) {
-        *(u32x4*)(stg + r * LRB + 16 * pc) = w;
-    };
-    auto stash = [&]() __attribute__((always_inline)) {
-        float x[8], uu[8], vv[8];
-        unpack8(fq, x);
-        unpack8(fu, uu);
-        unpack8(fv, vv);
-        u32x4 uh, ul, wh, wl;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            float hv[2], lv[2], hw[2], lw[2];
-#pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const float qu = a.scale * (x[2 * e + k] + uu[2 * e + k]);
-                const float qv = a.scale * (x[2 * e + k] + vv[2 * e + k]);
-                hv[k] = bf2f(f2bf(qu));
-                lv[k] = qu - hv[k];
-                hw[k] = bf2f(f2bf(qv));
-                lw[k] = qv - hw[k];
-            }
-            uh[e] = pack2bf(hv[0], hv[1]);
-            ul[e] = pack2bf(lv[0], lv[1]);
-            wh[e] = pack2bf(hw[0], hw[1]);
-            wl[e] = pack2bf(lw[0], lw[1]);
-        }
-        put(QH + row, uh);
-        put(QL + row, ul);
-        put(VH + row, wh);
-        put(VL + row, wl);
-        put(OR + row, fo);
-        put(KR + row, fk);
-        put(RR + row, fr0);
-        put(RR + 64 + row, fr1);
-        // V^T -> key rows: key 8 vj + e, d_head offset vd
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            *(bf16_t*)(stg + (VR + 8 * vj + e) * LRB + 2 * vd) = (bf16_t)((fvt[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-    };
-    const int lane = tid & 63, wave = tid >> 6, half = lane >> 5, li = lane & 31;
-    const int wm = (wave >> 1) * 32, wn = (wave & 1) * 32;
-    const int nb = 32 + wm - wn;   // first staged distance row of this quarter
-    f32x16 ac, ap, ab0, ab1;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) ac[v] = ap[v] = ab0[v] = ab1[v] = 0.f;
-    auto rd = [&](int r, int off) __attribute__((always_inline)) {
-        return as_bf16x8(*(const u32x4*)(stg + r * LRB + off));
-    };
-    fetch(0);
-    for (int d0 = 0; d0 < DH; d0 += LDC) {
-        __syncthreads();
-        stash();
-        __syncthreads();
-        if (d0 + LDC < DH) fetch(d0 + LDC);
-#pragma unroll
-        for (int kk = 0; kk < LDC / 16; ++kk) {
-            const int off = 32 * kk + 16 * half;
-            const bf16x8 qh = rd(QH + wm + li, off), ql = rd(QL + wm + li, off);
-            const bf16x8 vh = rd(VH + wm + li, off), vl = rd(VL + wm + li, off);
-            const bf16x8 ov = rd(OR + wm + li, off);
-            const bf16x8 kv = rd(KR + wn + li, off), vv = rd(VR + wn + li, off);
-            const bf16x8 r0 = rd(RR + nb + li, off), r1 = rd(RR + nb + 32 + li, off);
-            ac = mfma32(qh, kv, ac);
-            ab0 = mfma32(vh, r0, ab0);
-            ab1 = mfma32(vh, r1, ab1);
-            ap = mfma32(ov, vv, ap);
-            ac = mfma32(ql, kv, ac);
-            ab0 = mfma32(vl, r0, ab0);
-            ab1 = mfma32(vl, r1, ab1);
-        }
-    }
-    // the positional quarter through LDS (reusing the operand area, 4 x 32 x BDP floats)
-    float (*bd)[BDP] = (float (*)[BDP])(ops + wave * 32 * BDP);
-    __syncthreads();
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-        const int r = 8 * (v >> 2) + 4 * half + (v & 3);
-        bd[r][li] = ab0[v];
-        bd[r][32 + li] = ab1[v];
-    }
-    __syncthreads();
-    // accumulator v of lane (li, half): query row wm + r, r = 8 (v / 4) + 4 half + v % 4; key wn + li
-    const int j = j0 + wn + li;
-    float lv[16];
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-        const int r = 8 * (v >> 2) + 4 * half + (v & 3);
-        const int i = i0 + wm + r;
-        const bool vis = i < a.qlen && j <= a.mlen + i;
-        float l = ac[v] + bd[r][31 + r - li];
-        if (vis && a.bias) l += bf2f(((const bf16_t*)a.bias)[(int64_t)brow(a, a.mlen + i - j) * a.H + h]);
-        if (vis) {
-            const int64_t o = (rb + i) * a.klen + j;
-            a.P[o] = l;
-            a.dS[o] = ap[v];
-        }
-        lv[v] = vis ? l : -INFINITY;
-    }
-    // the softmax partials from l and dP laid out by row in LDS: thread
-    // (row, q) reduces keys 16 q .. 16 q + 15, two threads per half block
-    float (*ls)[BDP] = (float (*)[BDP])(ops);
-    float (*dps)[BDP] = (float (*)[BDP])(ops + 64 * BDP);
-    __syncthreads();
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-        const int r = 8 * (v >> 2) + 4 * half + (v & 3);
-        ls[wm + r][wn + li] = lv[v];
-        dps[wm + r][wn + li] = ap[v];
-    }
-    __syncthreads();
-    {
-        const int rr = tid >> 2, q = tid & 3;
-        float lx[16], px[16];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const f32x4 x = *(const f32x4*)&ls[rr][16 * q + 4 * k];
-            const f32x4 y = *(const f32x4*)&dps[rr][16 * q + 4 * k];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                lx[4 * k + e] = x[e];
-                px[4 * k + e] = y[e];
-            }
-        }
-        float m = lx[0];
-#pragma unroll
-        for (int k = 1; k < 16; ++k) m = fmaxf(m, lx[k]);
-        m = fmaxf(m, __shfl_xor(m, 1, 64));
-        float se = 0.f, sd = 0.f;
-        if (m != -INFINITY)   // a half block with no visible pair in this row contributes nothing
-#pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                const float e = __expf(lx[k] - m);
-                se += e;
-                sd += e * px[k];
-            }
-        se += __shfl_xor(se, 1, 64);
-        sd += __shfl_xor(sd, 1, 64);
-        const int i = i0 + rr, hb = q >> 1;
-        if ((q & 1) == 0 && i < a.qlen && j0 + 32 * hb < a.klen) {   // half blocks past klen have no partials
-            float* pt = a.rpart + ((rb + i) * nh + 2 * jt + hb) * 3;
-            pt[0] = m;
-            pt[1] = se;
-            pt[2] = sd;
-        }
-    }
-}
-
-// per query row: m = max of the half blocks' maxima, s = sum of their exp
-// sums rescaled to m, D = (rescaled sum of exp(l - m_t) dP) / s; stored
-// (m, 1/s, D). RSL lanes share a row: lane x takes half blocks x, x + RSL,
-// ..., and the lanes' (m, s, e) merge by rescaling to the larger maximum.
-constexpr int RSL = 8;
-
+// merge two (max, sum of exp(x - max), sum of exp(x - max) y) triples of one row
 __device__ __forceinline__ void merge_stats(float& m, float& s, float& e, float m2, float s2, float e2) {
     const float mx = fmaxf(m, m2);
     if (mx == -INFINITY) return;   // both empty
@@ -488,24 +259,263 @@ __device__ __forceinline__ void merge_stats(float& m, float& s, float& e, float 
     m = mx;
 }
 
-__global__ void __launch_bounds__(256) bwd_row_stats_kernel(AttnBwdArgs a) {
-    const int64_t idx = (int64_t)__builtin_amdgcn_workgroup_id_x() * 256 + (int)__builtin_amdgcn_workitem_id_x();
-    const int64_t row = idx / RSL;
-    const int x = (int)(idx % RSL);
-    const int64_t rows = (int64_t)a.B * a.H * a.qlen;
-    const bool live = row < rows;   // every lane takes part in the shuffles
-    const int i = live ? (int)(row % a.qlen) : 0;
-    const int nh = (a.klen + 31) / 32, nt = live ? (a.mlen + i) / 32 + 1 : 0;
-    const float* pt = a.rpart + (live ? row : 0) * nh * 3;
-    float m = -INFINITY, s = 0.f, e = 0.f;
-    for (int t = x; t < nt; t += RSL) merge_stats(m, s, e, pt[3 * t], pt[3 * t + 1], pt[3 * t + 2]);
+// ---- Logits, dP and the row statistics, one workgroup per 64 queries ----
+// A workgroup takes queries i0..i0+63 of one head and walks the key blocks of
+// 64 that they see, so the query operands are loaded and split once, the
+// next block's keys, values and table rows load while the current block is
+// computed, and the softmax statistics of each row stay in registers. Wave
+// (wq, wk) computes the 32 x 32 quarter of queries i0 + 32 wq .. and keys
+// j0 + 32 wk .. of every block, transposed (keys or distances on the MFMA
+// rows, queries on the columns: a lane owns one query), on the bf16 matrix
+// cores (v_mfma_f32_32x32x16_bf16, fp32 accumulation):
+//   content  k . qu      qu = s (q + u) enters as a high and a low bf16 part
+//                        (hi = bf16(qu), lo = bf16(qu - hi): 16 bits of
+//                        mantissa), k is exact: two products
+//   dP       v . dO      both exact bf16: one product
+//   position r . qv      qv split like qu, over the 63 distances the quarter
+//                        spans (two blocks of 32 table rows), then gathered
+//                        through LDS: pair (i, j) takes band row 31 + i - j
+// The logits of visible pairs (plus the bias table entry) go to the P buffer
+// and dP to the dS buffer. Each lane keeps (m, sum exp(l - m), sum exp(l - m) dP) of its query over its keys,
+// merged at the end with the other half-wave and the other key wave into
+// (m, 1/s, D) per row.
+constexpr int LRP = 64 * 2 + 16;     // bytes per staged row of 64 bf16 (conflict-free 16-byte reads)
+constexpr int BSP = 40;              // floats per row of a wave's band scratch
+constexpr int LR_STG = 256 * LRP;    // staged K rows (64), V rows (64), table rows (128)
+constexpr int LR_SCR = 64 * BSP * 4; // per wave: the band quarter (64 rows of 32 queries)
+
+__global__ void __launch_bounds__(256, 2) bwd_logits_rows_kernel(AttnBwdArgs a) {
+    constexpr int DH = 64;
+    constexpr int KS = 0, VS = 64, RS = 128;   // staged rows
+    extern __shared__ __attribute__((aligned(16))) char lsm[];
+    char* stg = lsm;
+    const int tid = (int)__builtin_amdgcn_workitem_id_x();
+    const int lane = tid & 63, wave = tid >> 6, hf = lane >> 5, li = lane & 31;
+    const int wq = wave >> 1, wk = wave & 1;
+    float* scr = (float*)(lsm + LR_STG + wave * LR_SCR);
+    const int BH = a.B * a.H, nit = (a.qlen + 63) / 64;
+    // heaviest query blocks first; with BH a multiple of 8 a head stays on XCD g % 8
+    const int w = (int)__builtin_amdgcn_workgroup_id_x();
+    if (w >= BH * nit) return;
+    const int it = nit - 1 - w / BH, g = w % BH;
+    const int h = g % a.H, b = g / a.H;
+    const int i0 = 64 * it;
+    const int ilast = i0 + 63 < a.qlen ? i0 + 63 : a.qlen - 1;
+    const int njt = (a.klen + 63) / 64;
+    int jt_last = (a.mlen + ilast) / 64;
+    if (jt_last > njt - 1) jt_last = njt - 1;
+    const int64_t rb = (int64_t)g * a.qlen;
+    const bf16_t* kp = (const bf16_t*)a.k;
+    const bf16_t* vp = (const bf16_t*)a.vt;
+    const bf16_t* rp = (const bf16_t*)a.r;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+
+    // ---- query operands (MFMA B): lane owns query iq, d_head 16 kk + 8 hf .. + 7
+    const int iq = i0 + 32 * wq + li;
+    const bool qok = iq < a.qlen;
+    bf16x8 quh[4], qul[4], qvh[4], qvl[4], dob[4];
 #pragma unroll
-    for (int o = 1; o < RSL; o <<= 1)
-        merge_stats(m, s, e, __shfl_xor(m, o, 64), __shfl_xor(s, o, 64), __shfl_xor(e, o, 64));
-    if (live && x == 0) {
-        a.rstat[row * 3] = m;
-        a.rstat[row * 3 + 1] = 1.f / s;
-        a.rstat[row * 3 + 2] = e / s;
+    for (int kk = 0; kk < 4; ++kk) {
+        const int d = 16 * kk + 8 * hf;
+        const u32x4 fq = qok ? *(const u32x4*)((const bf16_t*)a.q + (rb + iq) * DH + d) : z;
+        const u32x4 fo = qok ? *(const u32x4*)((const bf16_t*)a.dout + (((int64_t)b * a.qlen + iq) * a.H + h) * DH + d) : z;
+        const u32x4 fu = *(const u32x4*)((const bf16_t*)a.u + h * DH + d);
+        const u32x4 fv = *(const u32x4*)((const bf16_t*)a.v + h * DH + d);
+        float x[8], uu[8], vv[8];
+        unpack8(fq, x);
+        unpack8(fu, uu);
+        unpack8(fv, vv);
+        u32x4 uh, ul, wh, wl;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float hu[2], lu[2], hw[2], lw[2];
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const float qu = qok ? a.scale * (x[2 * e + k] + uu[2 * e + k]) : 0.f;
+                const float qv = qok ? a.scale * (x[2 * e + k] + vv[2 * e + k]) : 0.f;
+                hu[k] = bf2f(f2bf(qu));
+                lu[k] = qu - hu[k];
+                hw[k] = bf2f(f2bf(qv));
+                lw[k] = qv - hw[k];
+            }
+            uh[e] = pack2bf(hu[0], hu[1]);
+            ul[e] = pack2bf(lu[0], lu[1]);
+            wh[e] = pack2bf(hw[0], hw[1]);
+            wl[e] = pack2bf(lw[0], lw[1]);
+        }
+        quh[kk] = as_bf16x8(uh);
+        qul[kk] = as_bf16x8(ul);
+        qvh[kk] = as_bf16x8(wh);
+        qvl[kk] = as_bf16x8(wl);
+        dob[kk] = as_bf16x8(fo);
+    }
+
+    // ---- staging of key block jt: K rows and V rows (by key, from V^T) of keys
+    // j0 .., table rows of distances dlo + rho, rho < 128, dlo = mlen + i0 - j0 - 63
+    // (clamped to the table). Thread: K chunks (row, 16 bytes) tid, tid + 256;
+    // V^T pieces (d_head row, 8 keys) tid, tid + 256; table chunks tid + 256 t.
+    u32x4 fk[2], fvt[2], fr[4];
+    auto fetch = [&](int jt) __attribute__((always_inline)) {
+        const int j0 = 64 * jt, dlo = a.mlen + i0 - j0 - 63;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int c = tid + 256 * t, row = c >> 3, ch = c & 7;
+            fk[t] = j0 + row < a.klen ? *(const u32x4*)(kp + ((int64_t)g * a.klen + j0 + row) * DH + 8 * ch) : z;
+            const int d = c & 63, kc = c >> 6, jj = j0 + 8 * kc;
+            fvt[t] = jj < a.ldv ? *(const u32x4*)(vp + ((int64_t)g * DH + d) * a.ldv + jj) : z;
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int c = tid + 256 * t, row = c >> 3, ch = c & 7;
+            int dist = dlo + row;
+            dist = dist < 0 ? 0 : (dist > a.n_rel - 1 ? a.n_rel - 1 : dist);
+            fr[t] = *(const u32x4*)(rp + ((int64_t)h * a.r_rows + dist) * DH + 8 * ch);
+        }
+    };
+    auto stash = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int c = tid + 256 * t, row = c >> 3, ch = c & 7;
+            *(u32x4*)(stg + (KS + row) * LRP + 16 * ch) = fk[t];
+            const int d = c & 63, kc = c >> 6;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                *(bf16_t*)(stg + (VS + 8 * kc + e) * LRP + 2 * d) = (bf16_t)((fvt[t][e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int c = tid + 256 * t, row = c >> 3, ch = c & 7;
+            *(u32x4*)(stg + (RS + row) * LRP + 16 * ch) = fr[t];
+        }
+    };
+    auto rd = [&](int r, int off) __attribute__((always_inline)) {
+        return as_bf16x8(*(const u32x4*)(stg + r * LRP + off));
+    };
+
+    // running statistics of query iq over this lane's keys
+    float m = -INFINITY, s = 0.f, sd = 0.f;
+    const int rho0 = 32 + 32 * wq - 32 * wk;   // first staged table row of the quarter
+    const bool vec = (a.klen & 3) == 0;        // rows of P and dS are 16-byte aligned
+    fetch(0);
+    stash();
+    __syncthreads();
+    for (int jt = 0; jt <= jt_last; ++jt) {
+        if (jt < jt_last) fetch(jt + 1);
+        const int j0 = 64 * jt, jq = j0 + 32 * wk;   // first key of the quarter
+        // the quarter sees a pair when its first key is visible to its last query
+        const int iql = i0 + 32 * wq + 31 < a.qlen ? i0 + 32 * wq + 31 : a.qlen - 1;
+        if (jq <= a.mlen + iql) {
+            // in phases, so that at most two accumulator blocks are live: the
+            // band (then parked in LDS), the content with the gathered band,
+            // then dP
+            f32x16 ab0, ab1;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) ab0[v] = ab1[v] = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int off = 32 * kk + 16 * hf;
+                const bf16x8 r0 = rd(RS + rho0 + li, off), r1 = rd(RS + rho0 + 32 + li, off);
+                ab0 = mfma32(r0, qvh[kk], ab0);
+                ab1 = mfma32(r1, qvh[kk], ab1);
+                ab0 = mfma32(r0, qvl[kk], ab0);
+                ab1 = mfma32(r1, qvl[kk], ab1);
+            }
+            // band rows t (distance dlo + rho0 + t) of query li, then the pairs:
+            // key jq + kj takes band row 31 + li - kj
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int t = 8 * (v >> 2) + 4 * hf + (v & 3);
+                scr[t * BSP + li] = ab0[v];
+                scr[(32 + t) * BSP + li] = ab1[v];
+            }
+            __builtin_amdgcn_wave_barrier();
+            __asm__ __volatile__("" ::: "memory");
+            f32x16 ac;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) ac[v] = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int off = 32 * kk + 16 * hf;
+                const bf16x8 kv = rd(KS + 32 * wk + li, off);
+                ac = mfma32(kv, quh[kk], ac);
+                ac = mfma32(kv, qul[kk], ac);
+            }
+            float lv[16];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int kj = 8 * (v >> 2) + 4 * hf + (v & 3);
+                const int j = jq + kj;
+                const bool vis = qok && j <= a.mlen + iq;
+                float l = ac[v] + scr[(31 + li - kj) * BSP + li];
+                if (vis && a.bias) l += bf2f(((const bf16_t*)a.bias)[(int64_t)brow(a, a.mlen + iq - j) * a.H + h]);
+                lv[v] = vis ? l : -INFINITY;
+            }
+            __builtin_amdgcn_wave_barrier();
+            __asm__ __volatile__("" ::: "memory");
+            f32x16 ap;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) ap[v] = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) ap = mfma32(rd(VS + 32 * wk + li, 32 * kk + 16 * hf), dob[kk], ap);
+            // stores: four consecutive keys per register group
+            if (qok) {
+                float* pl = a.P + (rb + iq) * a.klen;
+                float* pd = a.dS + (rb + iq) * a.klen;
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    const int j = jq + 8 * gq + 4 * hf;
+                    if (vec && j + 3 <= a.mlen + iq) {
+                        *(f32x4*)(pl + j) = (f32x4){lv[4 * gq], lv[4 * gq + 1], lv[4 * gq + 2], lv[4 * gq + 3]};
+                        *(f32x4*)(pd + j) = (f32x4){ap[4 * gq], ap[4 * gq + 1], ap[4 * gq + 2], ap[4 * gq + 3]};
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (j + e <= a.mlen + iq) {
+                                pl[j + e] = lv[4 * gq + e];
+                                pd[j + e] = ap[4 * gq + e];
+                            }
+                    }
+                }
+            }
+            // statistics: rescale to a grown maximum, then add the block
+            float mb = lv[0];
+#pragma unroll
+            for (int v = 1; v < 16; ++v) mb = fmaxf(mb, lv[v]);
+            if (mb > m) {
+                const float sc = __expf(m - mb);
+                s *= sc;
+                sd *= sc;
+                m = mb;
+            }
+            if (m != -INFINITY)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    // masked pairs add nothing (dP past klen may be anything)
+                    const float e = lv[v] != -INFINITY ? __expf(lv[v] - m) : 0.f;
+                    s += e;
+                    sd += lv[v] != -INFINITY ? e * ap[v] : 0.f;
+                }
+        }
+        __syncthreads();   // every wave is done with block jt's operands
+        if (jt < jt_last) {
+            stash();
+            __syncthreads();
+        }
+    }
+    // merge the half-waves (the same query), then the two key waves
+    merge_stats(m, s, sd, __shfl_xor(m, 32, 64), __shfl_xor(s, 32, 64), __shfl_xor(sd, 32, 64));
+    float* xs = (float*)(lsm + LR_STG);   // the wave scratch is free now
+    if (wk == 1 && hf == 0) {
+        xs[(wq * 32 + li) * 3] = m;
+        xs[(wq * 32 + li) * 3 + 1] = s;
+        xs[(wq * 32 + li) * 3 + 2] = sd;
+    }
+    __syncthreads();
+    if (wk == 0 && hf == 0 && qok) {
+        merge_stats(m, s, sd, xs[(wq * 32 + li) * 3], xs[(wq * 32 + li) * 3 + 1], xs[(wq * 32 + li) * 3 + 2]);
+        a.rstat[(rb + iq) * 3] = m;
+        a.rstat[(rb + iq) * 3 + 1] = 1.f / s;
+        a.rstat[(rb + iq) * 3 + 2] = sd / s;
     }
 }
 
@@ -876,9 +886,15 @@ hipError_t launch_t(const AttnBwdArgs& a, hipStream_t s) {
     AttnBwdArgs f = a;   // the arguments once P and dS are final
     (void)hipGetLastError();
     if constexpr (DH == 64) {
-        const int64_t nblk = (int64_t)a.B * a.H * ((a.qlen + 63) / 64) * ((a.klen + 63) / 64);
-        hipLaunchKernelGGL(bwd_logits_tile_kernel, dim3(xcd_grid(nblk)), dim3(256), 0, s, a);
-        hipLaunchKernelGGL(bwd_row_stats_kernel, dim3((unsigned)((rows * RSL + 255) / 256)), dim3(256), 0, s, a);
+        // the LDS limit is raised once per process (a function-local static is
+        // initialised exactly once, also under concurrent launches)
+        constexpr int lds = LR_STG + 4 * LR_SCR;
+        static const hipError_t attr =
+            hipFuncSetAttribute((const void*)bwd_logits_rows_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (attr != hipSuccess) return attr;
+        (void)hipGetLastError();
+        const int64_t nwg = (int64_t)a.B * a.H * ((a.qlen + 63) / 64);
+        hipLaunchKernelGGL(bwd_logits_rows_kernel, dim3((unsigned)nwg), dim3(256), lds, s, a);
     } else {
         hipLaunchKernelGGL((bwd_rows_kernel<T, DH>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
     }

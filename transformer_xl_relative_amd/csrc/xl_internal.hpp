@@ -168,7 +168,6 @@ struct AttnBwdArgs {
     float* dbias;
     float* drp;     // per-batch-element partial sums of dr for rows c < dr_first
     float* uvp;     // tiled path: per (b, h, query block) column sums for du, dv
-    float* rpart;   // tiled path: per (query row, block of 64 keys) softmax partials (m, sum e, sum e dP)
     float* rstat;   // tiled path: per query row (m, 1/s, D); P and dS then hold l and dP
     int dr_first;   // rows c >= dr_first of dr come from the per-row kernel
 };
