@@ -589,9 +589,11 @@ __global__ void __launch_bounds__(256, MODE == TP_DQ ? 4 : 1) bwd_tile_kernel(At
     int ft0 = 0;                            // first t of the fetched stage
     auto fetch = [&](int t0) __attribute__((always_inline)) {
         ft0 = t0;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            int m, t;
+        // pair k of this thread: (m, t) as below. Whether it is a visible pair
+        // inside the block is monotone in k for each bound, so when the first
+        // and the last are, all eight are: then the loads go without a
+        // condition each (one branch per thread instead of eight)
+        auto pair = [&](int k, int& m, int& t) __attribute__((always_inline)) {
             if (MODE == TP_DQ) {
                 t = t0 + (tid & 31);
                 m = m0 + (tid >> 5) + 8 * k;
@@ -599,12 +601,46 @@ __global__ void __launch_bounds__(256, MODE == TP_DQ ? 4 : 1) bwd_tile_kernel(At
                 m = m0 + (tid & 63);   // lanes along m: coalesced rows of dS and P
                 t = t0 + 8 * wv + k;   // 8 consecutive t per lane: one 16-byte LDS write
             }
-            float x0 = 0.f, x1 = 0.f;
-            if (MODE == TP_DKDV) {
-                // l, dP and the row's statistics, raw: stash() turns them into
-                // P and dS once this stage's products have been issued
-                // (t is uniform across the wave, so the statistics come
-                // through scalar loads)
+        };
+        auto visible = [&](int k) __attribute__((always_inline)) {
+            int m, t;
+            pair(k, m, t);
+            if (MODE == TP_DKDV) return m < a.klen && t < a.qlen && m <= a.mlen + t;
+            if (MODE == TP_DQ) return m < a.qlen && t <= a.mlen + m;
+            return m < a.dr_first && t < a.qlen && m <= a.mlen + t;
+        };
+        auto load = [&](int k) __attribute__((always_inline)) {
+            int m, t;
+            pair(k, m, t);
+            if (MODE == TP_DKDV) {   // l and dP, raw: stash() turns them into P and dS
+                const int64_t o = (rb + t) * a.klen + m;
+                ra[0][k] = a.P[o];
+                ra[NP - 1][k] = a.dS[o];
+            } else if (MODE == TP_DQ) {   // dS is final by now
+                const int64_t o = (rb + m) * a.klen;
+                ra[0][k] = a.dS[o + t];
+                ra[NP - 1][k] = a.dS[o + (a.mlen + m - t)];
+            } else {
+                ra[0][k] = a.dS[(rb + t) * a.klen + (a.mlen + t - m)];
+            }
+        };
+        if (visible(0) && visible(7)) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) load(k);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                ra[0][k] = 0.f;
+                ra[NP - 1][k] = 0.f;
+                if (visible(k)) load(k);
+            }
+        }
+        if (MODE == TP_DKDV) {
+            // the rows' statistics (t is uniform across the wave, so they come
+            // through scalar loads)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int t = t0 + 8 * wv + k;
                 float s0 = 0.f, s1 = 0.f, s2 = 0.f;
                 if (t < a.qlen) {
                     const float* st = a.rstat + (rb + t) * 3;
@@ -612,25 +648,10 @@ __global__ void __launch_bounds__(256, MODE == TP_DQ ? 4 : 1) bwd_tile_kernel(At
                     s1 = st[1];
                     s2 = st[2];
                 }
-                if (m < a.klen && t < a.qlen && m <= a.mlen + t) {
-                    const int64_t o = (rb + t) * a.klen + m;
-                    x0 = a.P[o];
-                    x1 = a.dS[o];
-                }
                 rs[k][0] = s0;
                 rs[k][1] = s1;
                 rs[k][2] = s2;
-            } else if (MODE == TP_DQ) {   // dS is final by now
-                if (m < a.qlen && t <= a.mlen + m) {
-                    const int64_t o = (rb + m) * a.klen;
-                    x0 = a.dS[o + t];
-                    x1 = a.dS[o + (a.mlen + m - t)];
-                }
-            } else {
-                if (m < a.dr_first && t < a.qlen && m <= a.mlen + t) x0 = a.dS[(rb + t) * a.klen + (a.mlen + t - m)];
             }
-            ra[0][k] = x0;
-            if (NP > 1) ra[NP - 1][k] = x1;
         }
         // the [t x 64] rows: lane t of 32 consecutive rows, 8 columns per lane;
         // each wave covers 32 rows x 16 columns, so that its transposed 2-byte
@@ -653,17 +674,28 @@ __global__ void __launch_bounds__(256, MODE == TP_DQ ? 4 : 1) bwd_tile_kernel(At
             // P = exp(l - m) / s, dS = P (dP - D); this block is the only
             // reader of the pair, so it leaves dS final in place (the kernels
             // after it read dS only)
+            const int m = m0 + (tid & 63), tb = ft0 + 8 * wv;
+            // all eight pairs visible (the first and the last are): no
+            // condition per pair
+            const bool all = m < a.klen && tb + 7 < a.qlen && m <= a.mlen + tb;
+            float* dsr = a.dS + (rb + tb) * a.klen + m;
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                const int m = m0 + (tid & 63), t = ft0 + 8 * wv + k;
                 float pv = 0.f, dv = 0.f;
-                if (m < a.klen && t < a.qlen && m <= a.mlen + t) {
+                if (all || (m < a.klen && tb + k < a.qlen && m <= a.mlen + tb + k)) {
                     pv = __expf(ra[0][k] - rs[k][0]) * rs[k][1];
                     dv = pv * (ra[NP - 1][k] - rs[k][2]);
-                    a.dS[(rb + t) * a.klen + m] = dv;
                 }
                 ra[0][k] = dv;
                 ra[NP - 1][k] = pv;
+            }
+            if (all) {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) dsr[(int64_t)k * a.klen] = ra[0][k];
+            } else {
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    if (m < a.klen && tb + k < a.qlen && m <= a.mlen + tb + k) dsr[(int64_t)k * a.klen] = ra[0][k];
             }
         }
 #pragma unroll
