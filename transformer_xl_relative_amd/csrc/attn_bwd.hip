@@ -440,14 +440,17 @@ __global__ void __launch_bounds__(256, 2) bwd_logits_rows_kernel(AttnBwdArgs a) 
                 ac = mfma32(kv, quh[kk], ac);
                 ac = mfma32(kv, qul[kk], ac);
             }
+            // every pair of the quarter visible (its last key to its first
+            // query, all queries in range): no test per pair
+            const bool full = i0 + 32 * wq + 31 < a.qlen && jq + 31 <= a.mlen + i0 + 32 * wq;
             float lv[16];
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int kj = 8 * (v >> 2) + 4 * hf + (v & 3);
                 const int j = jq + kj;
-                const bool vis = qok && j <= a.mlen + iq;
+                const bool vis = full || (qok && j <= a.mlen + iq);
                 float l = ac[v] + scr[(31 + li - kj) * BSP + li];
-                if (vis && a.bias) l += bf2f(((const bf16_t*)a.bias)[(int64_t)brow(a, a.mlen + iq - j) * a.H + h]);
+                if (a.bias && vis) l += bf2f(((const bf16_t*)a.bias)[(int64_t)brow(a, a.mlen + iq - j) * a.H + h]);
                 lv[v] = vis ? l : -INFINITY;
             }
             __builtin_amdgcn_wave_barrier();
@@ -458,9 +461,16 @@ __global__ void __launch_bounds__(256, 2) bwd_logits_rows_kernel(AttnBwdArgs a) 
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) ap = mfma32(rd(VS + 32 * wk + li, 32 * kk + 16 * hf), dob[kk], ap);
             // stores: four consecutive keys per register group
-            if (qok) {
-                float* pl = a.P + (rb + iq) * a.klen;
-                float* pd = a.dS + (rb + iq) * a.klen;
+            float* pl = a.P + (rb + iq) * a.klen;
+            float* pd = a.dS + (rb + iq) * a.klen;
+            if (full && vec) {
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    const int j = jq + 8 * gq + 4 * hf;
+                    *(f32x4*)(pl + j) = (f32x4){lv[4 * gq], lv[4 * gq + 1], lv[4 * gq + 2], lv[4 * gq + 3]};
+                    *(f32x4*)(pd + j) = (f32x4){ap[4 * gq], ap[4 * gq + 1], ap[4 * gq + 2], ap[4 * gq + 3]};
+                }
+            } else if (qok) {
 #pragma unroll
                 for (int gq = 0; gq < 4; ++gq) {
                     const int j = jq + 8 * gq + 4 * hf;
@@ -487,7 +497,14 @@ __global__ void __launch_bounds__(256, 2) bwd_logits_rows_kernel(AttnBwdArgs a) 
                 sd *= sc;
                 m = mb;
             }
-            if (m != -INFINITY)
+            if (full) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const float e = __expf(lv[v] - m);
+                    s += e;
+                    sd += e * ap[v];
+                }
+            } else if (m != -INFINITY) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     // masked pairs add nothing (dP past klen may be anything)
@@ -495,6 +512,7 @@ __global__ void __launch_bounds__(256, 2) bwd_logits_rows_kernel(AttnBwdArgs a) 
                     s += e;
                     sd += lv[v] != -INFINITY ? e * ap[v] : 0.f;
                 }
+            }
         }
         __syncthreads();   // every wave is done with block jt's operands
         if (jt < jt_last) {
