@@ -111,3 +111,24 @@ def test_core_backward_segment_bias(T):
     # a steady-state segment of the segment workload (qlen = mlen = 512) with the +-128 bias table, one
     # batch element of 4
     _run(T, "bf16", 1, 16, 512, 512, -1, 128, seed=17)
+
+
+def _random_shape(idx):
+    # a seeded random bf16 shape: ragged query blocks, any klen mod 4 (the logits kernel's scalar
+    # store path), no memory (whole quarters of the first key block see no key), clamp and bias kinds
+    rng = np.random.default_rng(4200 + idx)
+    B, H = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+    qlen = int(rng.integers(1, 261))
+    mlen = 0 if idx % 3 == 0 else int(rng.integers(1, 401))
+    klen = qlen + mlen
+    clamp = -1 if rng.random() < 0.5 else int(rng.integers(1, klen + 1))
+    bias = -1 if rng.random() < 0.5 else int(rng.integers(0, 65))
+    kind = int(rng.integers(0, 2)) if bias >= 0 else 0
+    return B, H, qlen, mlen, clamp, bias, kind
+
+
+@pytest.mark.parametrize("idx", range(8))
+def test_core_backward_random(T, idx):
+    B, H, qlen, mlen, clamp, bias, kind = _random_shape(idx)
+    print(f"backward random {idx}: B{B} H{H} q{qlen} m{mlen} clamp {clamp} bias {bias} kind {kind}", flush=True)
+    _run(T, "bf16", B, H, qlen, mlen, clamp, bias, kind, seed=900 + idx)
