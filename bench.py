@@ -224,7 +224,8 @@ def main():
     ap.add_argument("--d-inner", type=int, default=0, help="feed-forward width of --decoder (0: 4 * d_model)")
     ap.add_argument("--backward", action="store_true", help="time the attention-core gradients instead")
     ap.add_argument("--kv-ring", action="store_true",
-                    help="step with xl_segment_step_kv (projected keys and values of the memory kept in a ring)")
+                    help="step with xl_segment_step_kv (projected keys and values of the memory kept in a ring); "
+                         "with --decoder, xl_decoder_stack_step_kv")
     ap.add_argument("--reuse-table", action="store_true",
                     help="steps after the first skip the sinusoid and the R projection (XL_REUSE_TABLE; the "
                          "memory is full, so the table is that of the first step): a separate measurement, "
@@ -262,7 +263,8 @@ def main():
         backward_bench(w, args.steps, args.warmup, args.no_cpu)
         return
     if args.decoder > 0:
-        decoder_bench(w, args.decoder, args.d_inner or 4 * w.d_model, args.steps, args.warmup, args.no_cpu)
+        decoder_bench(w, args.decoder, args.d_inner or 4 * w.d_model, args.steps, args.warmup, args.no_cpu,
+                      args.kv_ring)
         return
     t = xl_inputs.layer_inputs(w) if w.segments == 1 else None
     if t is None:
@@ -480,15 +482,16 @@ def backward_bench(w, K, warmup, no_cpu):
     print(json.dumps(res), flush=True)
 
 
-def decoder_flops(w, d_inner):
+def decoder_flops(w, d_inner, kv_ring=False):
     """Algorithmic FLOPs of one decoder layer step: the attention layer and the
     two feed-forward GEMMs (layer norms, biases, ReLU and residuals are
-    elementwise and not counted)."""
-    flops, _ = layer_flops(w, w.mlen)
+    elementwise and not counted); with key rings only the segment's keys and
+    values are projected."""
+    flops, _ = layer_flops(w, w.mlen, kv_ring)
     return flops + 2.0 * 2.0 * w.batch * w.qlen * w.d_model * d_inner
 
 
-def decoder_bench(w, n_layer, d_inner, K, warmup, no_cpu):
+def decoder_bench(w, n_layer, d_inner, K, warmup, no_cpu, kv_ring=False):
     import numpy as np
     import torch
     import transformer_xl_relative_amd as xl
@@ -513,6 +516,28 @@ def decoder_bench(w, n_layer, d_inner, K, warmup, no_cpu):
     def step():
         xl.xl_decoder_stack_step(desc, d_inner, 0.0, weights, h, fifos, out, ws, stream)
 
+    if kv_ring:
+        # each layer's memory as a full key ring: one step over the drawn memory
+        # rows (qlen = mlen) from empty rings projects them in, then every timed
+        # step runs with len = mlen and moves the ring by qlen
+        if w.qlen % 8 or w.mlen % 8:
+            raise SystemExit("--kv-ring needs qlen and mlen multiples of 8")
+        H, dh, cap = w.n_head, w.d_head, w.mlen + w.qlen
+        kr = [torch.empty((w.batch, H, cap, dh), dtype=torch.bfloat16, device="cuda") for _ in range(n_layer)]
+        vr = [torch.empty((w.batch, H, dh, cap), dtype=torch.bfloat16, device="cuda") for _ in range(n_layer)]
+        kvs = (xl.xl_kv_fifo * n_layer)(*[xl.xl_kv_fifo(k.data_ptr(), v.data_ptr(), cap, w.mlen, 0, 0)
+                                          for k, v in zip(kr, vr)])
+        d0 = xl.make_desc(batch=w.batch, d_model=D, n_head=H, d_head=dh, qlen=w.mlen, mlen=0, clamp_len=w.clamp_len,
+                          bias_clamp=w.bias_clamp, bias_kind=w.bias_kind, dtype=xl.XL_BF16, out_dtype=xl.XL_BF16)
+        ws0 = torch.empty(xl.xl_decoder_stack_kv_workspace_size(d0, d_inner), dtype=torch.uint8, device="cuda")
+        out0 = torch.empty((w.batch, w.mlen, D), dtype=torch.bfloat16, device="cuda")
+        xl.xl_decoder_stack_step_kv(d0, d_inner, 0.0, weights, gu.dev(t["mem"]).contiguous(), kvs, out0, ws0, stream)
+        del ws0, out0
+        ws = torch.empty(xl.xl_decoder_stack_kv_workspace_size(desc, d_inner), dtype=torch.uint8, device="cuda")
+
+        def step():
+            xl.xl_decoder_stack_step_kv(desc, d_inner, 0.0, weights, h, kvs, out, ws, stream)
+
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -523,7 +548,9 @@ def decoder_bench(w, n_layer, d_inner, K, warmup, no_cpu):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / K
-    flops = n_layer * decoder_flops(w, d_inner)
+    if kv_ring:
+        assert all(r.len == w.mlen for r in kvs)
+    flops = n_layer * decoder_flops(w, d_inner, kv_ring)
     value = flops / (ms * 1e-3) / 1e12
     res = {
         "metric": "decoder stack fwd TFLOP/s (pre-LN layers: relative attention + FFN), 1 GPU",
@@ -533,7 +560,12 @@ def decoder_bench(w, n_layer, d_inner, K, warmup, no_cpu):
         "data": "synthetic (seeded N(0,1) activations and memories, N(0,0.02) weights, LN gains 1+N(0,0.02))",
         "config": {"workload": (f"{w.name} decoder stack: one segment step of {n_layer} pre-LN layers (LN1 over "
                                 f"[memory ; segment], relative attention + residual, LN2, FFN {D}->{d_inner}->{D} "
-                                f"+ residual, per-layer FIFO update), batch {w.batch}, qlen {w.qlen}, mlen {w.mlen}"),
+                                f"+ residual, per-layer FIFO update), batch {w.batch}, qlen {w.qlen}, mlen {w.mlen}"
+                                if not kv_ring else
+                                f"{w.name} decoder stack on key rings: one segment step of {n_layer} pre-LN layers "
+                                f"(LN1 over the segment, its keys and values projected into the layer's ring of "
+                                f"projected memory keys, relative attention + residual, LN2, FFN {D}->{d_inner}->{D} "
+                                f"+ residual), batch {w.batch}, qlen {w.qlen}, mlen {w.mlen}"),
                    "n_layer": n_layer, "d_inner": d_inner, "batch": w.batch, "qlen": w.qlen, "mlen": w.mlen,
                    "d_model": D, "n_head": w.n_head, "d_head": w.d_head},
         "flops_per_step": flops,
@@ -551,7 +583,8 @@ def decoder_bench(w, n_layer, d_inner, K, warmup, no_cpu):
             el = time.perf_counter() - t0
             if el >= 10.0:
                 break
-        cpu = decoder_flops(w, d_inner) / w.batch * n / el / 1e12
+        # (the same algorithmic count as the GPU figure: one layer step's work)
+        cpu = decoder_flops(w, d_inner, kv_ring) / w.batch * n / el / 1e12
         res["cpu_baseline"] = {"value": round(cpu, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
                                "kind": "oracle",
                                "sample": f"{n} decoder-layer forwards of one batch element (of {w.batch}) of "

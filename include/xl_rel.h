@@ -407,6 +407,29 @@ int xl_decoder_stack_step(const xl_attn_desc* desc, int64_t d_inner, float ln_ep
                           size_t ws_bytes, void* stream);
 
 /*
+ * The same segment of an n_layer stack with each layer's memory kept as a
+ * key ring of projected keys and values (rings[n_layer], xl_kv_fifo): the
+ * cache reuse of intelliparadigm.com §3.2 applied to every layer of the
+ * stack of felixzhao.cn §2.3.1. A layer's memory enters it only through LN1
+ * and the key and value projections, and those rows were normalised and
+ * projected with the same weights when they were that layer's input, so
+ * layer n normalises and projects only its input's rows, straight into
+ * rings[n] after the memory keys, and attends over the ring. For the same
+ * inputs the outputs are those of xl_decoder_stack_step bit for bit. On
+ * return each ring's len and head describe its last min(len + qlen,
+ * mlen_max) keys. bf16 only; every ring as in xl_segment_step_kv (cap,
+ * mlen_max, len, head and qlen multiples of 8), len <= desc->mlen; the rings
+ * must not overlap each other, h, out or ws. ws:
+ * xl_decoder_stack_kv_workspace_size() of desc with mlen the largest ring
+ * len of the call (no normalised memory rows, no k or vt regions). On an
+ * error no ring has been advanced unless the status is XL_HIP_ERROR.
+ */
+size_t xl_decoder_stack_kv_workspace_size(const xl_attn_desc* desc, int64_t d_inner);
+int xl_decoder_stack_step_kv(const xl_attn_desc* desc, int64_t d_inner, float ln_eps, int64_t n_layer,
+                             const xl_decoder_weights* w, const void* h, xl_kv_fifo* rings, void* out, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/*
  * Timing hook: when both are non-NULL, the hipEvent_t handles ev_begin/ev_end
  * take the start and end timestamps of the fused attention kernel itself
  * (passed to the runtime with the kernel launch) in the next calls of

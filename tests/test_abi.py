@@ -326,6 +326,40 @@ def test_decoder_stack_rejects_bad_arguments():
     assert call(fifos=fifos, nb=need - 1) == xl.XL_WORKSPACE_TOO_SMALL
 
 
+def test_decoder_stack_kv_rejects_bad_arguments():
+    lib = xl.lib()
+    d = _desc(mlen=128)
+    MIB = 1 << 20
+    ring = lambda base, **kw: xl.xl_kv_fifo(**{**dict(k=base, vt=base + MIB, cap=256, mlen_max=128, len=64, head=8),
+                                               **kw})
+    two = lambda a, b: (xl.xl_kv_fifo * 2)(a, b)
+
+    def call(n=2, rings=None, h=FAKE[8], out=FAKE[10], nb=1 << 40, d_inner=2048, desc=d):
+        rings = rings if rings is not None else two(ring(FAKE[12]), ring(FAKE[14]))
+        w = (xl.xl_decoder_weights * 2)(*[_dec_weights() for _ in range(2)])
+        return lib.xl_decoder_stack_step_kv(ctypes.byref(desc), d_inner, 0.0, n, w, h, rings, out, FAKE[11], nb, None)
+    assert call(n=0) == xl.XL_BAD_SHAPE
+    assert call(desc=_desc(mlen=128, dtype=xl.XL_F32, d_head=8)) == xl.XL_UNSUPPORTED       # bf16 only
+    assert call(rings=two(ring(FAKE[12], len=136), ring(FAKE[14]))) == xl.XL_BAD_SHAPE      # len > mlen_max
+    assert call(rings=two(ring(FAKE[12], mlen_max=256, cap=512, len=200), ring(FAKE[14]))) == \
+        xl.XL_BAD_SHAPE                                                                     # len > desc->mlen
+    assert call(rings=two(ring(FAKE[12], cap=160), ring(FAKE[14]))) == xl.XL_BAD_SHAPE      # cap < mlen_max + qlen
+    assert call(rings=two(ring(FAKE[12], head=4), ring(FAKE[14]))) == xl.XL_UNSUPPORTED     # head not a multiple of 8
+    assert call(rings=two(ring(FAKE[12]), ring(FAKE[12] + 4096))) == xl.XL_BAD_SHAPE        # rings overlap
+    assert call(rings=two(ring(FAKE[12], vt=FAKE[12] + 4096), ring(FAKE[14]))) == xl.XL_BAD_SHAPE   # k aliases vt
+    assert call(h=FAKE[14] + 64) == xl.XL_BAD_SHAPE                                          # h inside a ring
+    assert call(out=FAKE[8]) == xl.XL_BAD_SHAPE                                              # out aliases h
+    assert call(d_inner=48) == xl.XL_BAD_SHAPE
+    rings = two(ring(FAKE[12], head=16), ring(FAKE[14], head=24))
+    assert call(rings=rings, nb=16) == xl.XL_WORKSPACE_TOO_SMALL
+    assert [(r.len, r.head) for r in rings] == [(64, 16), (64, 24)]                          # untouched on error
+    need = xl.xl_decoder_stack_kv_workspace_size(d, 2048)
+    # no normalised memory rows and no k or vt regions: smaller than the state-FIFO stack's
+    assert 0 < need < xl.xl_decoder_stack_workspace_size(d, 2048)
+    assert call(rings=rings, nb=need - 1) == xl.XL_WORKSPACE_TOO_SMALL
+    assert xl.xl_decoder_stack_kv_workspace_size(_desc(dtype=xl.XL_F32, d_head=8), 2048) == 0
+
+
 def test_core_backward_rejects_bad_arguments():
     lib = xl.lib()
     d = _desc(mlen=64, qlen=64)

@@ -132,3 +132,48 @@ def test_decoder_stack_run(T, base, qlen, n_seg, mlen_max, d_inner, n_layer, hea
             assert np.array_equal(gu.host64(mems[s][0]), rmems[s][0]), f"layer 0 memory after segment {s}"
         for n in range(1, n_layer):
             gu.compare(f"layer {n} memory after segment {s}", gu.host64(mems[s][n]), rmems[s][n], dtype=w.dtype)
+
+
+def _stack_run_kv(T, w, t, *, batch, qlen, n_seg, mlen_max, cap, d_inner, n_layer, head0=0):
+    D, H, dh = w.d_model, w.n_head, w.d_head
+    kr = [T.full((batch, H, cap, dh), float("nan"), dtype=T.bfloat16, device="cuda") for _ in range(n_layer)]
+    vr = [T.full((batch, H, dh, cap), float("nan"), dtype=T.bfloat16, device="cuda") for _ in range(n_layer)]
+    rings = (xl.xl_kv_fifo * n_layer)(*[xl.xl_kv_fifo(k.data_ptr(), v.data_ptr(), cap, mlen_max, 0, head0)
+                                        for k, v in zip(kr, vr)])
+    weights = [gu.dec_weights(lw) for lw in t["layers"]]
+    hs = gu.dev(t["h"])
+    outs = []
+    for s in range(n_seg):
+        desc = _desc(w, batch=batch, qlen=qlen, mlen=rings[0].len)
+        ws = T.empty(xl.xl_decoder_stack_kv_workspace_size(desc, d_inner), dtype=T.uint8, device="cuda")
+        h = hs[:, s * qlen:(s + 1) * qlen].contiguous()
+        out = T.empty((batch, qlen, D), dtype=T.float32, device="cuda")
+        xl.xl_decoder_stack_step_kv(desc, d_inner, 0.0, weights, h, rings, out, ws)
+        T.cuda.synchronize()
+        outs.append(gu.host64(out))
+        for n in range(n_layer):
+            assert rings[n].len == min((s + 1) * qlen, mlen_max)
+    return outs
+
+
+# the stack on key rings of projected keys and values: bit for bit the state-FIFO stack's
+# outputs (the memory's rows were normalised and projected with the same code when they were the
+# segment), and the oracle's; rings start anywhere and wrap
+@pytest.mark.parametrize("qlen,n_seg,mlen_max,cap,n_layer,head0,bias,kind",
+                         [(64, 4, 96, 160, 3, 0, -1, 0), (40, 3, 80, 128, 2, 56, 8, 0), (32, 4, 64, 104, 2, 24, 0, 1)])
+def test_decoder_stack_kv_matches_fifo(T, qlen, n_seg, mlen_max, cap, n_layer, head0, bias, kind):
+    d_inner = 256
+    w = dataclasses.replace(W["base_bf16"], segments=n_seg, qlen=qlen, mlen=mlen_max, seed=n_layer * 7 + qlen,
+                            bias_clamp=bias, bias_kind=kind)
+    t = xl_inputs.decoder_inputs(w, d_inner=d_inner, n_layer=n_layer, batch=2, qlen=qlen)
+    outs, _ = _stack_run(T, w, t, batch=2, qlen=qlen, n_seg=n_seg, mlen_max=mlen_max, d_inner=d_inner,
+                         n_layer=n_layer)
+    kouts = _stack_run_kv(T, w, t, batch=2, qlen=qlen, n_seg=n_seg, mlen_max=mlen_max, cap=cap, d_inner=d_inner,
+                          n_layer=n_layer, head0=head0)
+    routs, _ = oracle.decoder_stack_run(t["h"].f64, n_seg, qlen, mlen_max,
+                                        [gu.oracle_dec_weights(lw) for lw in t["layers"]], n_head=w.n_head,
+                                        d_head=w.d_head, clamp_len=w.clamp_len, bias_clamp=w.bias_clamp,
+                                        bias_kind=w.bias_kind)
+    for s in range(n_seg):
+        assert np.array_equal(kouts[s], outs[s]), f"segment {s}: key-ring stack differs from the state-FIFO stack"
+        gu.compare(f"key-ring stack segment {s}", kouts[s], routs[s], dtype=w.dtype)

@@ -65,7 +65,8 @@ EXPORTS = ("xl_status_string", "xl_last_error", "xl_relpos_embed", "xl_rel_attn_
            "xl_rel_attn_workspace_layout", "xl_rel_attn_fwd", "xl_rel_attn_core_workspace_size", "xl_rel_attn_core",
            "xl_segment_step", "xl_segment_step_kv_workspace_size", "xl_segment_step_kv", "xl_set_core_events",
            "xl_rel_attn_core_bwd_workspace_size", "xl_rel_attn_core_bwd", "xl_decoder_layer_workspace_size", "xl_decoder_layer_fwd", "xl_decoder_stack_workspace_size",
-           "xl_decoder_stack_step", "xl_segment_step_noalloc")
+           "xl_decoder_stack_step", "xl_segment_step_noalloc", "xl_decoder_stack_kv_workspace_size",
+           "xl_decoder_stack_step_kv")
 
 # bytes of the static scratch of xl_segment_step_noalloc (XL_NOALLOC_SCRATCH_BYTES)
 XL_NOALLOC_SCRATCH_BYTES = 64 << 20
@@ -124,10 +125,14 @@ def lib():
         L.xl_decoder_stack_workspace_size.restype = ctypes.c_size_t
         L.xl_decoder_stack_step.argtypes = [D, _i64, ctypes.c_float, _i64, ctypes.POINTER(xl_decoder_weights), _p,
                                             ctypes.POINTER(xl_mem_fifo), _p, _p, ctypes.c_size_t, _p]
+        L.xl_decoder_stack_kv_workspace_size.argtypes = [D, _i64]
+        L.xl_decoder_stack_kv_workspace_size.restype = ctypes.c_size_t
+        L.xl_decoder_stack_step_kv.argtypes = [D, _i64, ctypes.c_float, _i64, ctypes.POINTER(xl_decoder_weights), _p,
+                                               ctypes.POINTER(xl_kv_fifo), _p, _p, ctypes.c_size_t, _p]
         for f in ("xl_relpos_embed", "xl_rel_attn_workspace_layout", "xl_rel_attn_fwd", "xl_rel_attn_core",
                   "xl_segment_step", "xl_set_core_events", "xl_segment_step_kv", "xl_decoder_layer_fwd",
                   "xl_rel_attn_core_bwd", "xl_segment_step_noalloc",
-                  "xl_decoder_stack_step"):
+                  "xl_decoder_stack_step", "xl_decoder_stack_step_kv"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -341,6 +346,23 @@ def xl_decoder_stack_step(desc: xl_attn_desc, d_inner: int, ln_eps: float, weigh
         raise ValueError("one fifo per layer")
     _check(lib().xl_decoder_stack_step(ctypes.byref(desc), d_inner, ln_eps, n, cw, _ptr(h), fifos, _ptr(out),
                                        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return out
+
+
+def xl_decoder_stack_kv_workspace_size(desc: xl_attn_desc, d_inner: int) -> int:
+    return lib().xl_decoder_stack_kv_workspace_size(ctypes.byref(desc), d_inner)
+
+
+def xl_decoder_stack_step_kv(desc: xl_attn_desc, d_inner: int, ln_eps: float, weights: list, h, rings, out, ws,
+                             stream=None):
+    """weights: one DecoderWeights (or xl_decoder_weights) per layer; rings: a
+    ctypes array of xl_kv_fifo (updated in place)."""
+    n = len(weights)
+    cw = (xl_decoder_weights * n)(*[w.c() if isinstance(w, DecoderWeights) else w for w in weights])
+    if len(rings) != n:
+        raise ValueError("one ring per layer")
+    _check(lib().xl_decoder_stack_step_kv(ctypes.byref(desc), d_inner, ln_eps, n, cw, _ptr(h), rings, _ptr(out),
+                                          _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
     return out
 
 

@@ -295,16 +295,17 @@ struct DecLayout {
     size_t xm, xs, h1, x2, y1, buf0, buf1, total;
 };
 
-// stack: two more [B, qlen, D] buffers for the outputs of the inner layers
-void dec_layout(const xl_attn_desc* d, int64_t mlen, int64_t d_inner, bool stack, DecLayout* L) {
+// stack: two more [B, qlen, D] buffers for the outputs of the inner layers;
+// kv: the memory is a key ring (no normalised memory rows, no k or vt regions)
+void dec_layout(const xl_attn_desc* d, int64_t mlen, int64_t d_inner, bool stack, DecLayout* L, bool kv = false) {
     xl_ws_layout A;
-    fill_layout(d, mlen, &A);
+    fill_layout(d, mlen, &A, kv);
     const size_t es = esize(d->dtype);
     const int64_t B = d->batch, q = d->qlen, D = d->d_model;
     size_t off = align_up(A.total);
     auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
     L->attn_total = A.total;
-    L->xm = take((size_t)(B * mlen * D) * es);
+    L->xm = take(kv ? 0 : (size_t)(B * mlen * D) * es);
     L->xs = take((size_t)(B * q * D) * es);
     L->h1 = take((size_t)(B * q * D) * 4);   // fp32 for either element type
     L->x2 = take((size_t)(B * q * D) * es);
@@ -342,33 +343,36 @@ int check_decoder(const xl_attn_desc* d, int64_t d_inner, float eps, const xl_de
 // into out however small out is after that sum.
 int decoder_forward(const xl_attn_desc* d, int64_t d_inner, float eps, const xl_decoder_weights* w, const void* h,
                     const void* mem, int64_t mlen, int64_t ring_len, int64_t ring_head, void* out, void* ws,
-                    size_t ws_bytes, hipStream_t s, const xl::RowCopy* fifo_write) {
+                    size_t ws_bytes, hipStream_t s, const xl::RowCopy* fifo_write, const xl_kv_fifo* kv = nullptr) {
     DecLayout L;
-    dec_layout(d, mlen, d_inner, false, &L);
+    dec_layout(d, mlen, d_inner, false, &L, kv != nullptr);
     if (ws_bytes < L.total)
         return fail(XL_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", ws_bytes, L.total);
     if (((uintptr_t)ws) % kAlign) return fail(XL_UNSUPPORTED, "workspace must be 256-byte aligned");
     const bool bf = d->dtype == XL_BF16;
-    const int64_t B = d->batch, q = d->qlen, D = d->d_model, klen = mlen + q;
+    const int64_t B = d->batch, q = d->qlen, D = d->d_model;
     char* W = (char*)ws;
     hipError_t e;
-    // 1. LN1 of every row of [memory ; segment]
+    // 1. LN1 of every row of [memory ; segment]; with a key ring only the
+    // segment's (the memory's keys and values were projected from their
+    // normalised rows when those were the segment)
     xl::LnArgs ln;
     memset(&ln, 0, sizeof ln);
-    ln.a0 = mlen ? mem : h; ln.a1 = h;
+    const int64_t mrows = kv ? 0 : mlen;
+    ln.a0 = mrows ? mem : h; ln.a1 = h;
     ln.a0_bstride = ring_len * D; ln.a1_bstride = q * D;
-    ln.a_seq = (int)klen; ln.a_split = (int)mlen; ln.ring_len = (int)(ring_len > 0 ? ring_len : 1);
+    ln.a_seq = (int)(mrows + q); ln.a_split = (int)mrows; ln.ring_len = (int)(ring_len > 0 ? ring_len : 1);
     ln.ring_head = (int)ring_head;
     ln.y0 = W + L.xm; ln.y1 = W + L.xs;
     ln.gamma = w->ln1_g; ln.beta = w->ln1_b;
-    ln.rows = (int)(B * klen); ln.D = (int)D; ln.eps = eps;
+    ln.rows = (int)(B * (mrows + q)); ln.D = (int)D; ln.eps = eps;
     if ((e = xl::launch_layer_norm(ln, bf, s)) != hipSuccess) return hip_fail(e, "layer norm launch");
     // 2. attention sublayer with the residual: h1 = h + RelAttn(...)
     xl_attn_desc da = *d;
     da.mlen = mlen;
     da.out_dtype = XL_F32;
-    int st = layer_forward(&da, &w->attn, W + L.xs, W + L.xm, mlen, mlen, 0, W + L.h1, W, L.attn_total, s, fifo_write,
-                           nullptr, h);
+    int st = layer_forward(&da, &w->attn, W + L.xs, kv ? nullptr : W + L.xm, mlen, mlen, 0, W + L.h1, W, L.attn_total,
+                           s, fifo_write, kv, h);
     if (st != XL_OK) return st;
     // 3. LN2(h1)
     ln.a0 = W + L.h1; ln.a1 = W + L.h1;
@@ -615,16 +619,11 @@ int xl_segment_step_noalloc(const xl_attn_desc* desc, const xl_attn_weights* w, 
     return xl_segment_step(desc, w, h, fifo, out, ws, XL_NOALLOC_SCRATCH_BYTES, stream);
 }
 
-size_t xl_segment_step_kv_workspace_size(const xl_attn_desc* desc) {
-    if (check_desc(desc, desc ? desc->mlen : 0, true) != XL_OK || desc->dtype != XL_BF16) return 0;
-    xl_ws_layout L;
-    fill_layout(desc, desc->mlen, &L, true);
-    return L.total;
-}
+}  // extern "C"
 
-int xl_segment_step_kv(const xl_attn_desc* desc, const xl_attn_weights* w, const void* h, xl_kv_fifo* kv,
-                       void* out, void* ws, size_t ws_bytes, void* stream) {
-    g_last_error.clear();
+namespace {
+// a key ring's state against desc (its len as the memory length)
+int check_kv_ring(const xl_attn_desc* desc, const xl_kv_fifo* kv) {
     if (!kv) return fail(XL_NULL_ARG, "kv is NULL");
     if (!kv->k || !kv->vt) return fail(XL_NULL_ARG, "kv->k and kv->vt must be non-NULL");
     int st = check_desc(desc, kv->len >= 0 ? kv->len : 0, true);
@@ -638,6 +637,33 @@ int xl_segment_step_kv(const xl_attn_desc* desc, const xl_attn_weights* w, const
     if (C % 8 || M % 8 || q % 8 || kv->len % 8 || kv->head % 8)
         return fail(XL_UNSUPPORTED, "the key ring needs cap, mlen_max, len, head and qlen multiples of 8");
     if (C > kI32 / 2 / desc->batch) return fail(XL_UNSUPPORTED, "batch * cap too large");
+    return XL_OK;
+}
+
+// the segment's keys now follow the memory keys: keep the last mlen_max
+void kv_advance(const xl_attn_desc* desc, xl_kv_fifo* kv) {
+    const int64_t total = kv->len + desc->qlen;
+    const int64_t new_len = total < kv->mlen_max ? total : kv->mlen_max;
+    kv->head = (kv->head + total - new_len) % kv->cap;
+    kv->len = new_len;
+}
+}  // namespace
+
+extern "C" {
+
+size_t xl_segment_step_kv_workspace_size(const xl_attn_desc* desc) {
+    if (check_desc(desc, desc ? desc->mlen : 0, true) != XL_OK || desc->dtype != XL_BF16) return 0;
+    xl_ws_layout L;
+    fill_layout(desc, desc->mlen, &L, true);
+    return L.total;
+}
+
+int xl_segment_step_kv(const xl_attn_desc* desc, const xl_attn_weights* w, const void* h, xl_kv_fifo* kv,
+                       void* out, void* ws, size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    int st = check_kv_ring(desc, kv);
+    if (st != XL_OK) return st;
+    const int64_t q = desc->qlen, C = kv->cap;
     if ((st = check_weights(desc, w)) != XL_OK) return st;
     if (!h || !out || !ws) return fail(XL_NULL_ARG, "h, out and ws must be non-NULL");
     const size_t es = esize(desc->dtype);
@@ -655,11 +681,7 @@ int xl_segment_step_kv(const xl_attn_desc* desc, const xl_attn_weights* w, const
     d.mlen = kv->len;
     st = layer_forward(&d, w, h, nullptr, kv->len, 0, 0, out, ws, ws_bytes, (hipStream_t)stream, nullptr, kv);
     if (st != XL_OK) return st;
-    // the segment's keys now follow the memory keys; keep the last mlen_max
-    const int64_t total = kv->len + q;
-    const int64_t new_len = total < M ? total : M;
-    kv->head = (kv->head + total - new_len) % C;
-    kv->len = new_len;
+    kv_advance(desc, kv);
     return XL_OK;
 }
 
@@ -833,6 +855,75 @@ int xl_decoder_stack_step(const xl_attn_desc* desc, int64_t d_inner, float ln_ep
                              y, W, L.buf0, s, &cp);
         if (st != XL_OK) return st;
         fifo_advance(desc, &fifos[n]);
+        x = y;
+    }
+    return XL_OK;
+}
+
+size_t xl_decoder_stack_kv_workspace_size(const xl_attn_desc* desc, int64_t d_inner) {
+    if (!desc || check_desc(desc, desc->mlen, true) != XL_OK || !d_inner_ok(desc, d_inner) || desc->dtype != XL_BF16)
+        return 0;
+    DecLayout L;
+    dec_layout(desc, desc->mlen, d_inner, true, &L, true);
+    return L.total;
+}
+
+int xl_decoder_stack_step_kv(const xl_attn_desc* desc, int64_t d_inner, float ln_eps, int64_t n_layer,
+                             const xl_decoder_weights* w, const void* h, xl_kv_fifo* rings, void* out, void* ws,
+                             size_t ws_bytes, void* stream) {
+    g_last_error.clear();
+    if (!desc) return fail(XL_NULL_ARG, "desc is NULL");
+    if (n_layer < 1 || n_layer > 4096) return fail(XL_BAD_SHAPE, "n_layer must be in [1, 4096]");
+    if (!w || !rings) return fail(XL_NULL_ARG, "weights and rings must be non-NULL");
+    if (!h || !out || !ws) return fail(XL_NULL_ARG, "h, out and ws must be non-NULL");
+    if ((uintptr_t)h % 16) return fail(XL_UNSUPPORTED, "h must be 16-byte aligned");
+    int st = check_desc(desc, desc->mlen, true);   // the sizes, before any product of them
+    if (st != XL_OK) return st;
+    if (desc->dtype != XL_BF16) return fail(XL_UNSUPPORTED, "the key ring path is bf16 only");
+    const float eps = ln_eps == 0.f ? 1e-5f : ln_eps;
+    const size_t es = esize(desc->dtype);
+    const size_t h_bytes = (size_t)(desc->batch * desc->qlen * desc->d_model) * es;
+    const size_t out_bytes = (size_t)(desc->batch * desc->qlen * desc->d_model) * esize(desc->out_dtype);
+    // every layer is checked before any runs, so that on an error no ring has moved
+    for (int64_t n = 0; n < n_layer; ++n) {
+        if ((st = check_kv_ring(desc, &rings[n])) != XL_OK) return st;
+        if (rings[n].len > desc->mlen)
+            return fail(XL_BAD_SHAPE, "ring %lld holds %lld keys, more than desc->mlen = %lld", (long long)n,
+                        (long long)rings[n].len, (long long)desc->mlen);
+        if ((st = check_decoder(desc, d_inner, eps, &w[n])) != XL_OK) return st;
+        const size_t rb = (size_t)(desc->batch * desc->n_head * rings[n].cap * desc->d_head) * es;
+        if (overlaps(rings[n].k, rb, rings[n].vt, rb)) return fail(XL_BAD_SHAPE, "ring %lld: k aliases vt", (long long)n);
+        for (const void* p : {rings[n].k, rings[n].vt}) {
+            if (overlaps(p, rb, h, h_bytes) || overlaps(p, rb, out, out_bytes) || overlaps(p, rb, ws, ws_bytes))
+                return fail(XL_BAD_SHAPE, "ring %lld aliases h, out or the workspace", (long long)n);
+            for (int64_t k = 0; k < n; ++k) {
+                const size_t rk = (size_t)(desc->batch * desc->n_head * rings[k].cap * desc->d_head) * es;
+                if (overlaps(p, rb, rings[k].k, rk) || overlaps(p, rb, rings[k].vt, rk))
+                    return fail(XL_BAD_SHAPE, "the rings of layers %lld and %lld overlap", (long long)k, (long long)n);
+            }
+        }
+    }
+    if (overlaps(out, out_bytes, h, h_bytes) || overlaps(out, out_bytes, ws, ws_bytes))
+        return fail(XL_BAD_SHAPE, "out aliases h or the workspace");
+    DecLayout L;
+    dec_layout(desc, desc->mlen, d_inner, true, &L, true);
+    if (ws_bytes < L.total)
+        return fail(XL_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", ws_bytes, L.total);
+    hipStream_t s = (hipStream_t)stream;
+    char* W = (char*)ws;
+    // layer n reads the output of layer n-1; its ring takes that input's
+    // projected keys and values
+    const void* x = h;
+    for (int64_t n = 0; n < n_layer; ++n) {
+        const bool last = n == n_layer - 1;
+        void* y = last ? out : (void*)(W + ((n & 1) ? L.buf1 : L.buf0));
+        xl_attn_desc d = *desc;
+        d.mlen = rings[n].len;
+        if (!last) d.out_dtype = desc->dtype;
+        st = decoder_forward(&d, d_inner, eps, &w[n], x, nullptr, rings[n].len, 0, 0, y, W, L.buf0, s, nullptr,
+                             &rings[n]);
+        if (st != XL_OK) return st;
+        kv_advance(desc, &rings[n]);
         x = y;
     }
     return XL_OK;
