@@ -177,3 +177,31 @@ def test_decoder_stack_kv_matches_fifo(T, qlen, n_seg, mlen_max, cap, n_layer, h
     for s in range(n_seg):
         assert np.array_equal(kouts[s], outs[s]), f"segment {s}: key-ring stack differs from the state-FIFO stack"
         gu.compare(f"key-ring stack segment {s}", kouts[s], routs[s], dtype=w.dtype)
+
+
+def _random_layer(idx):
+    # a seeded random bf16 decoder layer: widths in multiples of 32 (half-width last K
+    # stages when 32 mod 64), several heads, ragged segment and memory lengths, any FFN
+    # width, bias kinds; the GEMM launches land on the 64 x 64 and both 128 x 128 tiles
+    rng = np.random.default_rng(5100 + idx)
+    n_head = int(rng.integers(1, 5))
+    d_model = 32 * int(rng.integers(2, 33))
+    d_inner = 32 * int(rng.integers(1, 65))
+    batch, qlen = int(rng.integers(1, 4)), int(rng.integers(1, 301))
+    mlen = 0 if idx % 4 == 0 else int(rng.integers(1, 401))
+    bias = -1 if rng.random() < 0.5 else int(rng.integers(0, 65))
+    kind = int(rng.integers(0, 2)) if bias >= 0 else 0
+    return n_head, d_model, d_inner, batch, qlen, mlen, bias, kind
+
+
+@pytest.mark.parametrize("idx", range(8))
+def test_decoder_layer_random(T, idx):
+    n_head, d_model, d_inner, batch, qlen, mlen, bias, kind = _random_layer(idx)
+    print(f"decoder random {idx}: H{n_head} D{d_model} di{d_inner} B{batch} q{qlen} m{mlen} bias {bias} kind {kind}",
+          flush=True)
+    w = dataclasses.replace(W["base_bf16"], d_model=d_model, n_head=n_head, bias_clamp=bias, bias_kind=kind,
+                            seed=700 + idx)
+    t = xl_inputs.decoder_inputs(w, d_inner=d_inner, n_layer=1, batch=batch, qlen=qlen, mlen=mlen)
+    got = _run_layer(T, w, t, batch=batch, qlen=qlen, mlen=mlen, d_inner=d_inner)
+    ref = _oracle_layer(t, w, t["layers"][0], t["h"].f64, t["mem"].f64)
+    gu.compare(f"decoder random {idx}", got, ref, dtype="bf16")
