@@ -162,7 +162,8 @@ int run_core(const xl::AttnArgs& a, bool bf16, int dh, hipStream_t s) {
 // keys from it (mem, ring_len, ring_head unused).
 int layer_forward(const xl_attn_desc* d, const xl_attn_weights* w, const void* h, const void* mem, int64_t mlen,
                   int64_t ring_len, int64_t ring_head, void* out, void* ws, size_t ws_bytes, hipStream_t s,
-                  const xl::RowCopy* fifo_write, const xl_kv_fifo* kv = nullptr, const void* residual = nullptr) {
+                  const xl::RowCopy* fifo_write, const xl_kv_fifo* kv = nullptr, const void* residual = nullptr,
+                  bool table_ready = false) {
     xl_ws_layout L;
     fill_layout(d, mlen, &L, kv != nullptr);
     if (ws_bytes < L.total)
@@ -178,8 +179,10 @@ int layer_forward(const xl_attn_desc* d, const xl_attn_weights* w, const void* h
 
     // 1. sinusoid rows R_n, n < n_rel (a distance uses row min(delta, n_rel-1)),
     // unless the caller vouches that the workspace holds this table already
+    // (XL_REUSE_TABLE: then r as well), or the previous layer of a stack step
+    // wrote it for the same key count (table_ready: r is still projected)
     const bool reuse = (d->flags & XL_REUSE_TABLE) != 0;
-    if (!reuse) {
+    if (!reuse && !table_ready) {
         e = xl::launch_relpos(0, L.n_rel, D, -1, base, bf ? 1 : 0, W + L.rel, s);
         if (e != hipSuccess) return hip_fail(e, "relpos launch");
     }
@@ -343,7 +346,8 @@ int check_decoder(const xl_attn_desc* d, int64_t d_inner, float eps, const xl_de
 // into out however small out is after that sum.
 int decoder_forward(const xl_attn_desc* d, int64_t d_inner, float eps, const xl_decoder_weights* w, const void* h,
                     const void* mem, int64_t mlen, int64_t ring_len, int64_t ring_head, void* out, void* ws,
-                    size_t ws_bytes, hipStream_t s, const xl::RowCopy* fifo_write, const xl_kv_fifo* kv = nullptr) {
+                    size_t ws_bytes, hipStream_t s, const xl::RowCopy* fifo_write, const xl_kv_fifo* kv = nullptr,
+                    bool table_ready = false) {
     DecLayout L;
     dec_layout(d, mlen, d_inner, false, &L, kv != nullptr);
     if (ws_bytes < L.total)
@@ -372,7 +376,7 @@ int decoder_forward(const xl_attn_desc* d, int64_t d_inner, float eps, const xl_
     da.mlen = mlen;
     da.out_dtype = XL_F32;
     int st = layer_forward(&da, &w->attn, W + L.xs, kv ? nullptr : W + L.xm, mlen, mlen, 0, W + L.h1, W, L.attn_total,
-                           s, fifo_write, kv, h);
+                           s, fifo_write, kv, h, table_ready);
     if (st != XL_OK) return st;
     // 3. LN2(h1)
     ln.a0 = W + L.h1; ln.a1 = W + L.h1;
@@ -842,17 +846,22 @@ int xl_decoder_stack_step(const xl_attn_desc* desc, int64_t d_inner, float ln_ep
         return fail(XL_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", ws_bytes, L.total);
     hipStream_t s = (hipStream_t)stream;
     char* W = (char*)ws;
-    // layer n reads the output of layer n-1 and keeps that input in its own ring
+    // layer n reads the output of layer n-1 and keeps that input in its own
+    // ring; the sinusoid table in the workspace serves every layer after the
+    // first whose memory length (hence key count) equals the previous one's
     const void* x = h;
+    int64_t prev_len = -1;   // the memory length the previous layer ran with
     for (int64_t n = 0; n < n_layer; ++n) {
         const bool last = n == n_layer - 1;
         void* y = last ? out : (void*)(W + ((n & 1) ? L.buf1 : L.buf0));
         xl_attn_desc d = *desc;
         d.mlen = fifos[n].len;
         if (!last) d.out_dtype = desc->dtype;
+        const bool table_ready = fifos[n].len == prev_len;
+        prev_len = fifos[n].len;
         const xl::RowCopy cp = fifo_copy(desc, &fifos[n], x);
         st = decoder_forward(&d, d_inner, eps, &w[n], x, fifos[n].buf, fifos[n].len, fifos[n].mlen_max, fifos[n].head,
-                             y, W, L.buf0, s, &cp);
+                             y, W, L.buf0, s, &cp, nullptr, table_ready);
         if (st != XL_OK) return st;
         fifo_advance(desc, &fifos[n]);
         x = y;
@@ -912,16 +921,20 @@ int xl_decoder_stack_step_kv(const xl_attn_desc* desc, int64_t d_inner, float ln
     hipStream_t s = (hipStream_t)stream;
     char* W = (char*)ws;
     // layer n reads the output of layer n-1; its ring takes that input's
-    // projected keys and values
+    // projected keys and values. The sinusoid table in the workspace serves
+    // every layer after the first whose memory length equals the previous one's
     const void* x = h;
+    int64_t prev_len = -1;   // the memory length the previous layer ran with
     for (int64_t n = 0; n < n_layer; ++n) {
         const bool last = n == n_layer - 1;
         void* y = last ? out : (void*)(W + ((n & 1) ? L.buf1 : L.buf0));
         xl_attn_desc d = *desc;
         d.mlen = rings[n].len;
         if (!last) d.out_dtype = desc->dtype;
+        const bool table_ready = rings[n].len == prev_len;
+        prev_len = rings[n].len;
         st = decoder_forward(&d, d_inner, eps, &w[n], x, nullptr, rings[n].len, 0, 0, y, W, L.buf0, s, nullptr,
-                             &rings[n]);
+                             &rings[n], table_ready);
         if (st != XL_OK) return st;
         kv_advance(desc, &rings[n]);
         x = y;
