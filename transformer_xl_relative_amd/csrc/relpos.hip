@@ -55,31 +55,40 @@ __device__ __forceinline__ void sincos_f64(double x, double* sp, double* cp) {
     *cp = q == 0 ? cr : q == 1 ? -sr : q == 2 ? -cr : sr;
 }
 
-// A thread owns frequency pair t (blockIdx.x * 256 + threadIdx.x) of RPT
-// consecutive rows: the inverse frequency is evaluated once, then the RPT
-// angles and their sin/cos, which are independent, so their latencies overlap.
+// A workgroup owns 64 frequency pairs t (blockIdx.x * 64 + lane) of 4 * RPT
+// consecutive rows, wave w rows RPT w .. RPT w + RPT - 1. Wave 0 evaluates
+// the 64 inverse frequencies (fp64 pow, the costliest step) into LDS for all
+// four waves; each thread then takes the sin and cos of its RPT angles, which
+// are independent, so their latencies overlap. Lanes run along t: each row's
+// stores are consecutive.
 constexpr int RPT = 2;
+constexpr int RPW = 4 * RPT;   // rows per workgroup
 
 template <bool kBf16>
 __global__ void __launch_bounds__(256) relpos_kernel(int64_t delta0, int64_t n_rows, int64_t d_model,
                                                      int64_t clamp_len, double base, void* out) {
+    __shared__ double inv_freq_s[64];
     const int half = (int)(d_model >> 1);
-    const int t = (int)blockIdx.x * 256 + (int)threadIdx.x;
+    const int lane = (int)threadIdx.x & 63, wave = (int)threadIdx.x >> 6;
+    const int t = (int)blockIdx.x * 64 + lane;
+    if (wave == 0)
+        inv_freq_s[lane] = t < half ? pow(base, -(2.0 * (double)t) / (double)d_model) : 0.0;
+    __syncthreads();
     if (t >= half) return;
-    const double inv_freq = pow(base, -(2.0 * (double)t) / (double)d_model);
-    const int64_t ngroups = (n_rows + RPT - 1) / RPT;
+    const double inv_freq = inv_freq_s[lane];
+    const int64_t ngroups = (n_rows + RPW - 1) / RPW;
     for (int64_t grp = blockIdx.y; grp < ngroups; grp += gridDim.y) {
         double sv[RPT], cv[RPT];
 #pragma unroll
         for (int k = 0; k < RPT; ++k) {
-            const int64_t n = min(grp * RPT + k, n_rows - 1);
+            const int64_t n = min(grp * RPW + RPT * wave + k, n_rows - 1);
             int64_t delta = delta0 + n;
             if (clamp_len >= 0) delta = delta < -clamp_len ? -clamp_len : (delta > clamp_len ? clamp_len : delta);
             sincos_f64((double)delta * inv_freq, &sv[k], &cv[k]);
         }
 #pragma unroll
         for (int k = 0; k < RPT; ++k) {
-            const int64_t n = grp * RPT + k;
+            const int64_t n = grp * RPW + RPT * wave + k;
             if (n < n_rows) {
                 if constexpr (kBf16) {
                     ((uint32_t*)out)[n * half + t] = (uint32_t)d2bf(sv[k]) | ((uint32_t)d2bf(cv[k]) << 16);
@@ -127,8 +136,8 @@ __global__ void __launch_bounds__(256) fifo_kernel(const char* h, int qlen, char
 hipError_t launch_relpos(int64_t delta0, int64_t n_rows, int64_t d_model, int64_t clamp_len, double base,
                          int out_bf16, void* out, hipStream_t s) {
     if (n_rows <= 0 || d_model < 2) return hipSuccess;
-    const int64_t half = d_model / 2, groups = (n_rows + RPT - 1) / RPT;
-    const dim3 grid((unsigned)((half + 255) / 256), (unsigned)(groups < 65535 ? groups : 65535));
+    const int64_t half = d_model / 2, groups = (n_rows + RPW - 1) / RPW;
+    const dim3 grid((unsigned)((half + 63) / 64), (unsigned)(groups < 65535 ? groups : 65535));
     (void)hipGetLastError();   // drop a stale error of an earlier runtime call
     if (out_bf16) hipLaunchKernelGGL(relpos_kernel<true>, grid, dim3(256), 0, s, delta0, n_rows, d_model, clamp_len, base, out);
     else hipLaunchKernelGGL(relpos_kernel<false>, grid, dim3(256), 0, s, delta0, n_rows, d_model, clamp_len, base, out);
