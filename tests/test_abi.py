@@ -154,6 +154,10 @@ def test_workspace_grows_with_memory():
     dec = [xl.xl_decoder_stack_workspace_size(_desc(batch=2, n_head=8, qlen=64, d_model=256, mlen=m), 1024)
            for m in range(1800, 2100, 8)]
     assert all(a <= b for a, b in zip(dec, dec[1:]))
+    # the key-ring stack and step likewise (their memory lengths are the rings' lens)
+    for fn in (lambda d: xl.xl_decoder_stack_kv_workspace_size(d, 1024), xl.xl_segment_step_kv_workspace_size):
+        kv = [fn(_desc(batch=2, n_head=8, qlen=64, d_model=256, mlen=m)) for m in range(0, 2100, 8)]
+        assert all(0 < a <= b for a, b in zip(kv, kv[1:]))
 
 
 def test_core_rejects_bad_arguments():
