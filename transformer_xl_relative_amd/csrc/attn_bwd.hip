@@ -215,26 +215,26 @@ __global__ void __launch_bounds__(64 * BW) bwd_dr_kernel(AttnBwdArgs a) {
     if (c < a.n_rel) {
         const int d_hi = c < a.n_rel - 1 ? c : a.klen - 1;   // distances of row c: [c, d_hi]
         const float vd = ld<T>(a.v, h * DH + lane);
-        for (int b = 0; b < a.B; ++b) {
-            const int64_t rbase = ((int64_t)b * a.H + h) * a.qlen;
-            for (int delta = c; delta <= d_hi; ++delta) {
-                const int i0 = delta > a.mlen ? delta - a.mlen : 0;
-                float pa[ILP] = {};
-                int i = i0;
-                for (; i + ILP <= a.qlen; i += ILP) {
+        for (int delta = c; delta <= d_hi; ++delta) {
+            // the pairs of distance delta: (batch element b, query i0 + k) for
+            // k < rows, taken as one flat range u = b rows + k, so that ILP
+            // independent loads are in flight also when each element has few
+            const int i0 = delta > a.mlen ? delta - a.mlen : 0;
+            const int rows = a.qlen - i0, nu = a.B * rows;
+            auto term = [&](int u) __attribute__((always_inline)) {
+                const int b = u / rows, i = i0 + (u - b * rows);
+                const int64_t row = ((int64_t)b * a.H + h) * a.qlen + i;
+                return ds_at(a, row, a.mlen + i - delta) * (ld<T>(a.q, row * DH + lane) + vd);
+            };
+            float pa[ILP] = {};
+            int u = 0;
+            for (; u + ILP <= nu; u += ILP) {
 #pragma unroll
-                    for (int x = 0; x < ILP; ++x) {
-                        const int64_t row = rbase + i + x;
-                        pa[x] += ds_at(a, row, a.mlen + i + x - delta) * (ld<T>(a.q, row * DH + lane) + vd);
-                    }
-                }
-                for (; i < a.qlen; ++i) {
-                    const int64_t row = rbase + i;
-                    pa[0] += ds_at(a, row, a.mlen + i - delta) * (ld<T>(a.q, row * DH + lane) + vd);
-                }
-#pragma unroll
-                for (int x = 0; x < ILP; ++x) acc += a.scale * pa[x];
+                for (int x = 0; x < ILP; ++x) pa[x] += term(u + x);
             }
+            for (; u < nu; ++u) pa[0] += term(u);
+#pragma unroll
+            for (int x = 0; x < ILP; ++x) acc += a.scale * pa[x];
         }
     }
     a.dr[((int64_t)h * a.r_rows + c) * DH + lane] = acc;
@@ -833,22 +833,41 @@ __global__ void __launch_bounds__(256, MODE == TP_DQ ? 4 : 1) bwd_tile_kernel(At
 }
 
 // du, dv on the tiled path: one workgroup per head adds the dq blocks'
-// partial column sums over the batch elements and query blocks
-__global__ void __launch_bounds__(128) bwd_uv_tiled_kernel(AttnBwdArgs a) {
+// partial column sums (2 x 64 per batch element and 64-query block). Eight
+// groups of 128 threads take every eighth partial, their loads issued
+// together (UVG in flight per thread), then the groups' sums are added in a
+// fixed order through LDS.
+constexpr int UVG = 8;
+
+__global__ void __launch_bounds__(128 * UVG) bwd_uv_tiled_kernel(AttnBwdArgs a) {
     constexpr int DH = 64;
+    __shared__ float part[UVG][2 * DH];
     const int tid = (int)__builtin_amdgcn_workitem_id_x();
+    const int col = tid & (2 * DH - 1), grp = tid >> 7;
     const int h = (int)__builtin_amdgcn_workgroup_id_x();
     const int nmt = (a.qlen + TM - 1) / TM;
     const int n = a.B * nmt;
-    float s4[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int x = 0; x < n; ++x) {
-        const int b = x / nmt, mt = x - b * nmt;
-        s4[x & 3] += a.uvp[(((int64_t)b * a.H + h) * nmt + mt) * 2 * DH + tid];
+    float sum = 0.f;
+    for (int x0 = grp; x0 < n; x0 += UVG * UVG) {
+        float v[UVG];
+#pragma unroll
+        for (int k = 0; k < UVG; ++k) {
+            const int x = x0 + UVG * k;
+            const int b = x / nmt, mt = x - b * nmt;
+            v[k] = x < n ? a.uvp[(((int64_t)b * a.H + h) * nmt + mt) * 2 * DH + col] : 0.f;
+        }
+#pragma unroll
+        for (int k = 0; k < UVG; ++k) sum += v[k];
     }
-    const float sum = (s4[0] + s4[1]) + (s4[2] + s4[3]);
-    float* out = tid < DH ? a.du : a.dvb;
-    out[h * DH + (tid & 63)] = a.scale * sum;
+    part[grp][col] = sum;
+    __syncthreads();
+    if (grp == 0) {
+        float t = 0.f;
+#pragma unroll
+        for (int g = 0; g < UVG; ++g) t += part[g][col];
+        float* out = col < DH ? a.du : a.dvb;
+        out[h * DH + (col & (DH - 1))] = a.scale * t;
+    }
 }
 
 // dr rows c < dr_first: the sum of the batch elements' partial sums, scaled
@@ -966,7 +985,7 @@ hipError_t launch_t(const AttnBwdArgs& a, hipStream_t s) {
     }
     const int64_t nr = a.r_rows - a.dr_first;   // the last table row in use and the unused rows
     hipLaunchKernelGGL((bwd_dr_kernel<T, DH>), dim3((unsigned)((a.H * nr + BW - 1) / BW)), dim3(64 * BW), 0, s, f);
-    if constexpr (DH == 64) hipLaunchKernelGGL(bwd_uv_tiled_kernel, dim3((unsigned)a.H), dim3(128), 0, s, f);
+    if constexpr (DH == 64) hipLaunchKernelGGL(bwd_uv_tiled_kernel, dim3((unsigned)a.H), dim3(128 * UVG), 0, s, f);
     else hipLaunchKernelGGL((bwd_uv_kernel<DH>), dim3((unsigned)a.H), dim3(64 * UVW), 0, s, f);
     if (a.bias) hipLaunchKernelGGL(bwd_bias_kernel, dim3((unsigned)(a.bias_rows * a.H)), dim3(64), 0, s, f);
     return hipGetLastError();
