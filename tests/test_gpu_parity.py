@@ -174,6 +174,20 @@ def test_layer_model_width(T, d_model, n_head):
     _check_intermediates(T, L, w, t, 2, 70, 45)
 
 
+def test_layer_projection_tall_tiles(T):
+    # batch 8, qlen 608, mlen 544 at d_model 512: the grouped projection makes
+    # 192 tiles of 256 x 256 and 256 of 192 x 256, so it runs on the latter;
+    # query tiles cross batch boundaries (608 rows is not a multiple of 192)
+    # and the key, transposed value and R epilogues see 192-row tiles
+    w = W["base_bf16"]
+    t = xl_inputs.layer_inputs(w, batch=8, qlen=608, mlen=544)
+    L = _run_layer(T, w, t, batch=8, qlen=608, mlen=544)
+    _check_intermediates(T, L, w, t, 8, 608, 544)
+    bsel = [0, 5, 7]
+    ref = gu.oracle_layer(t, w, t["h"].f64, t["mem"].f64, bsel=bsel)
+    gu.compare(f"tall projection (batches {bsel})", gu.host64(L.out)[bsel], ref, dtype=w.dtype)
+
+
 @pytest.mark.parametrize("base,qlen,mlen,clamp", [("base_bf16", 70, 1000, -1), ("base_bf16", 130, 0, -1),
                                                   ("longmem_bf16", 64, 1600, 1000), ("tiny_f32", 9, 1030, 5)])
 def test_layer_t5_bias(T, base, qlen, mlen, clamp):
