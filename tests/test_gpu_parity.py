@@ -411,6 +411,26 @@ def test_segment_run_kv_ring_t5(T):
         gu.compare(f"t5 key ring segment {s}", gu.host64(ring_outs[s]), routs[s], dtype="bf16")
 
 
+def test_segment_run_kv_ring_tall_tiles(T):
+    # batch 8, qlen 480, 192 memory rows at d_model 1024: the second segment's
+    # grouped projection (R, the queries and the segment's keys and values)
+    # makes 192 tiles of 256 x 256 and 256 of 192 x 256, so its key and value
+    # rows go into the wrapped ring from 192-row tiles that cross batch elements
+    import dataclasses
+    qlen, n_seg, mlen_max, cap, batch = 480, 2, 192, 704, 8
+    w = dataclasses.replace(W["segments_bf16"], qlen=qlen, mlen=mlen_max, segments=n_seg, seed=480)
+    t = xl_inputs.layer_inputs(w, batch=batch, qlen=qlen)
+    ring_outs = _segment_run_kv(T, w, t, batch=batch, qlen=qlen, n_seg=n_seg, mlen_max=mlen_max, cap=cap,
+                                head0=600)
+    bsel = [0, 3, 7]
+    wts = {k: t[k].f64 for k in ("w_q", "w_k", "w_v", "w_r", "w_o", "u", "v", "beta") if k in t}
+    routs, _ = oracle.segment_run(t["h"].f64[bsel], n_seg, qlen, mlen_max, wts, n_head=w.n_head, d_head=w.d_head,
+                                  clamp_len=w.clamp_len, bias_clamp=w.bias_clamp, bias_kind=w.bias_kind)
+    for s in range(n_seg):
+        gu.compare(f"tall key ring segment {s} (batches {bsel})", gu.host64(ring_outs[s])[bsel], routs[s],
+                   dtype="bf16")
+
+
 def test_segment_run_kv_ring_full_size(T):
     # the segmented workload at full size (batch 4, 16 heads, qlen = mlen = 512),
     # key ring against the state FIFO path, bit for bit
