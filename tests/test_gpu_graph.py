@@ -1,0 +1,65 @@
+"""The layer forward captured in a HIP graph.
+
+xl_rel_attn_fwd issues only kernel launches on the caller's stream (no
+allocation, copy, fill or synchronisation), so a caller can capture it. Every
+replay must give the bits of the eager call; the replays are separated by
+eager work of the program and a synchronisation, and the output buffer is
+overwritten before each one, so that a replay that skipped a node or read a
+stale argument shows.
+"""
+import numpy as np
+import pytest
+
+import xl_inputs
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+W = xl_inputs.WORKLOADS
+
+
+@pytest.fixture(scope="module")
+def T():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import transformer_xl_relative_amd as xl
+    xl.lib()
+    return torch
+
+
+# large_bf16 at batch 2 (one attention launch), longmem_bf16 at batch 2 (its
+# keys split: the attention and the merge kernel)
+@pytest.mark.parametrize("name,batch,qlen,mlen", [("large_bf16", 2, 384, 384), ("longmem_bf16", 2, 64, 1600)])
+def test_layer_graph_replay(T, name, batch, qlen, mlen):
+    import transformer_xl_relative_amd as xl
+    w = W[name]
+    t = xl_inputs.layer_inputs(w, batch=batch, qlen=qlen, mlen=mlen)
+    L = gu.Layer(w, t, batch=batch, qlen=qlen, mlen=mlen, out_f32=True)
+    h = gu.dev(t["h"])
+    mem = gu.dev(t["mem"])
+    print(f"graph replay: {name} batch {batch} qlen {qlen} mlen {mlen}", flush=True)
+    xl.xl_rel_attn_fwd(L.desc, L.weights, h, mem, L.out, L.ws)
+    T.cuda.synchronize()
+    eager = L.out.clone()
+    ref = gu.oracle_layer(t, w, t["h"].f64, t["mem"].f64, bsel=[0])
+    gu.compare(f"{name} eager", gu.host64(eager)[:1], ref, dtype=w.dtype)
+
+    out = T.empty_like(L.out)
+    side = T.cuda.Stream()
+    graph = T.cuda.CUDAGraph()
+    with T.cuda.graph(graph, stream=side):
+        xl.xl_rel_attn_fwd(L.desc, L.weights, h, mem, out, L.ws)
+    scratch = T.empty(1 << 20, dtype=T.float32, device="cuda")
+    for rep in range(4):
+        out.fill_(float("nan"))
+        scratch.normal_()                      # eager work between the replays
+        _ = scratch.sum().item()
+        graph.replay()
+        T.cuda.synchronize()
+        assert T.equal(out, eager), f"replay {rep}: differs from the eager call"
+    # and the eager call after the replays still gives the same bits
+    L.out.fill_(float("nan"))
+    xl.xl_rel_attn_fwd(L.desc, L.weights, h, mem, L.out, L.ws)
+    T.cuda.synchronize()
+    assert np.array_equal(gu.host64(L.out), gu.host64(eager))
