@@ -63,3 +63,43 @@ def test_layer_graph_replay(T, name, batch, qlen, mlen):
     xl.xl_rel_attn_fwd(L.desc, L.weights, h, mem, L.out, L.ws)
     T.cuda.synchronize()
     assert np.array_equal(gu.host64(L.out), gu.host64(eager))
+
+
+def test_decoder_layer_graph_replay(T):
+    # the pre-LN decoder layer (layer norms, attention, feed-forward network
+    # with its residuals) at the large workload's width with a long memory
+    # (its keys split), captured and replayed
+    import transformer_xl_relative_amd as xl
+    w = W["large_bf16"]
+    batch, qlen, mlen, d_inner = 2, 64, 1200, 4096
+    t = xl_inputs.decoder_inputs(w, d_inner=d_inner, n_layer=1, batch=batch, qlen=qlen, mlen=mlen)
+    desc = xl.make_desc(batch=batch, d_model=w.d_model, n_head=w.n_head, d_head=w.d_head, qlen=qlen, mlen=mlen,
+                        clamp_len=w.clamp_len, bias_clamp=w.bias_clamp, bias_kind=w.bias_kind, dtype=xl.XL_BF16,
+                        out_dtype=xl.XL_F32)
+    ws = T.empty(xl.xl_decoder_layer_workspace_size(desc, d_inner), dtype=T.uint8, device="cuda")
+    weights = gu.dec_weights(t["layers"][0])
+    h = gu.dev(t["h"])
+    mem = gu.dev(t["mem"])
+    eager = T.empty((batch, qlen, w.d_model), dtype=T.float32, device="cuda")
+    print(f"graph replay: decoder layer batch {batch} qlen {qlen} mlen {mlen} d_inner {d_inner}", flush=True)
+    xl.xl_decoder_layer_fwd(desc, d_inner, 0.0, weights, h, mem, eager, ws)
+    T.cuda.synchronize()
+    import oracle
+    ref = oracle.decoder_layer_fwd(t["h"].f64[:1], t["mem"].f64[:1], gu.oracle_dec_weights(t["layers"][0]),
+                                   n_head=w.n_head, d_head=w.d_head, clamp_len=w.clamp_len,
+                                   bias_clamp=w.bias_clamp, bias_kind=w.bias_kind)
+    gu.compare("decoder layer eager", gu.host64(eager)[:1], ref, dtype="bf16")
+
+    out = T.empty_like(eager)
+    side = T.cuda.Stream()
+    graph = T.cuda.CUDAGraph()
+    with T.cuda.graph(graph, stream=side):
+        xl.xl_decoder_layer_fwd(desc, d_inner, 0.0, weights, h, mem, out, ws)
+    scratch = T.empty(1 << 20, dtype=T.float32, device="cuda")
+    for rep in range(4):
+        out.fill_(float("nan"))
+        scratch.normal_()
+        _ = scratch.sum().item()
+        graph.replay()
+        T.cuda.synchronize()
+        assert T.equal(out, eager), f"replay {rep}: differs from the eager call"
