@@ -103,3 +103,51 @@ def test_decoder_layer_graph_replay(T):
         graph.replay()
         T.cuda.synchronize()
         assert T.equal(out, eager), f"replay {rep}: differs from the eager call"
+
+
+def test_core_backward_graph_replay(T):
+    # the attention-core gradients (every output written by one thread, no
+    # atomics) with a bias table, captured and replayed: each replay rewrites
+    # every gradient with the eager bits
+    import transformer_xl_relative_amd as xl
+    B, H, qlen, mlen, dh, bias = 2, 3, 200, 75, 64, 40
+    klen = qlen + mlen
+    n_rel = klen
+    ci = xl_inputs.core_inputs(batch=B, n_head=H, d_head=dh, qlen=qlen, mlen=mlen, n_rows=n_rel, dtype="bf16",
+                               seed=11, bias_clamp=bias, bias_kind=0)
+    rng = np.random.default_rng(12)
+    dout = xl_inputs.Tensor(rng.standard_normal((B, qlen, H * dh)).astype(np.float32), "bf16")
+    ldv = (klen + 7) // 8 * 8 + 8
+    vt = np.zeros((B, H, dh, ldv), np.float32)
+    vt[..., :klen] = ci["v"].f32.transpose(0, 1, 3, 2)
+    vt = xl_inputs.Tensor(vt, "bf16")
+    desc = xl.make_desc(batch=B, d_model=2, n_head=H, d_head=dh, qlen=qlen, mlen=mlen, clamp_len=-1,
+                        bias_clamp=bias, bias_kind=0, dtype=xl.XL_BF16)
+    shapes = {"dq": (B, H, qlen, dh), "dk": (B, H, klen, dh), "dv": (B, H, klen, dh), "dr": (H, n_rel, dh),
+              "du": (H, dh), "dv_bias": (H, dh), "dbias": tuple(ci["beta"].shape)}
+    grads = lambda: {k: T.full(s, float("nan"), dtype=T.float32, device="cuda") for k, s in shapes.items()}
+    ops = (gu.dev(ci["q"]), gu.dev(ci["k"]), gu.dev(vt), ldv, gu.dev(ci["r"]), n_rel, gu.dev(ci["u"]),
+           gu.dev(ci["vb"]), gu.dev(ci["beta"]), gu.dev(dout))
+    ws = T.empty(xl.xl_rel_attn_core_bwd_workspace_size(desc), dtype=T.uint8, device="cuda")
+    print(f"graph replay: core backward B {B} H {H} qlen {qlen} mlen {mlen} bias {bias}", flush=True)
+    eager = grads()
+    xl.xl_rel_attn_core_bwd(desc, *ops, eager, ws)
+    T.cuda.synchronize()
+    for k, g in eager.items():
+        assert bool(T.isfinite(g).all()), k
+
+    out = grads()
+    side = T.cuda.Stream()
+    graph = T.cuda.CUDAGraph()
+    with T.cuda.graph(graph, stream=side):
+        xl.xl_rel_attn_core_bwd(desc, *ops, out, ws)
+    scratch = T.empty(1 << 20, dtype=T.float32, device="cuda")
+    for rep in range(4):
+        for g in out.values():
+            g.fill_(float("nan"))
+        scratch.normal_()
+        _ = scratch.sum().item()
+        graph.replay()
+        T.cuda.synchronize()
+        for k in shapes:
+            assert T.equal(out[k], eager[k]), f"replay {rep}: {k} differs from the eager call"
