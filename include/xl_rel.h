@@ -37,6 +37,11 @@
  *    error nothing is launched and a status code is returned, with a
  *    human-readable reason available from xl_last_error() (per thread).
  *  - No output may alias an input.
+ *  - A call enqueues kernel launches only (no allocation, copy, fill or
+ *    synchronisation), so a caller may capture it in a HIP graph; a replay
+ *    recomputes from the buffers' contents at replay time. The segment steps
+ *    advance their FIFO or ring positions on the host when called, so a
+ *    captured step keeps the positions it was captured with.
  *  - Weight layout is nn.Linear's [out_features, in_features]: a projection
  *    is y = x W^T.
  */
