@@ -71,8 +71,8 @@ ATTN_SOURCES = ("transformer_xl_relative_amd/csrc/attn_bf16.hip", "transformer_x
 # HBM bytes per launch of the fused attention kernel (calibrated FETCH_SIZE and
 # WRITE_SIZE, see profiles/attn_bf16_kernel_<workload>_pmc_traffic.md).
 TRAFFIC = {
-    "large_bf16": {"sha256": "407d58b72e062c773fd1d98ba5d345757d7fd95be84802a9f606d2629b38de06",
-                   "bytes": 39651350, "fetch_bytes": 33359894, "write_bytes": 6291456},
+    "large_bf16": {"sha256": "db195e5eb6ab7cb1535eed1060ff7fd41d77c01d824cc560574d1227235bfc8f",
+                   "bytes": 39642961, "fetch_bytes": 33351505, "write_bytes": 6291456},
 }
 
 

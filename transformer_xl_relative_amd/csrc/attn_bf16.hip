@@ -505,6 +505,9 @@ __global__ void __launch_bounds__(NT, 2) attn_bf16_kernel(AttnArgs a) {
             // (the scheduler keeps the reads ahead of the products, so that their
             // latencies overlap instead of adding up)
             __builtin_amdgcn_sched_barrier(0);
+            // the wave issues its products and softmax at raised priority, so
+            // that a second wave on the SIMD does not delay the matrix burst
+            __builtin_amdgcn_s_setprio(1);
             // content product of step s+1 on top of its position terms, and block s+3
 #pragma unroll
             for (int kc = 0; kc < 4; ++kc) {
@@ -541,6 +544,7 @@ __global__ void __launch_bounds__(NT, 2) attn_bf16_kernel(AttnArgs a) {
                 __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_setprio(0);
             ring_write(g, FLIP);               // block s+3 replaces block s+1, read above
             // O^T += V^T P^T
 #pragma unroll
